@@ -1,0 +1,329 @@
+// C ABI of libsgdn.so (declared in include/sgdn.h): argument validation,
+// workspace carve-up and the launch sequence of the dense and sparse
+// GDN-core prefill.  Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/sgdn.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace sgdn;
+
+constexpr int NP_SPARSE = 16;
+
+struct Plan {
+  int B, T, Nq, Nv, C, G, esz, bf16, solve;
+  int kL, kM, kH;
+  int Emax;        // event capacity per sequence inside prefill_sparse
+  int snap_cap;    // snapshot slots per sequence (sparse) or per head (dense)
+  size_t off[24];
+  size_t total;
+};
+
+enum Buf { B_G, B_GAMMA, B_P, B_U, B_W, B_CB, B_KT, B_SNAP, B_S0T, B_SCORE, B_ETA, B_RANK,
+           B_TINFO, B_MASK, B_TIER, B_ROWPAIR, B_ROWPTR, B_COL, B_PRED, B_GSLOT, B_ESLOT,
+           B_WPK, B_STATS, B_COUNT };
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// k = clip(round(rho C), 2, C) in exact integer arithmetic, round half up.
+void tier_counts(int C, int bp, int k[3]) {
+  static const int pct[3] = {8, 30, 95};
+  for (int i = 0; i < 3; ++i) {
+    if (C == 1) { k[i] = 1; continue; }
+    long long num, den;
+    if (bp <= 2900) {
+      num = (long long)pct[i] * bp * C;
+      den = 290000;
+    } else {
+      num = (long long)C * (710000LL - (long long)(100 - pct[i]) * (10000 - bp));
+      den = 710000;
+    }
+    long long kk = (2 * num + den) / (2 * den);
+    if (kk < 2) kk = 2;
+    if (kk > C) kk = C;
+    k[i] = (int)kk;
+  }
+}
+
+int budget_bp(float b) { return (int)floor((double)b * 10000.0 + 0.5); }
+
+int check_problem(const sgdn_problem* pr) {
+  if (pr == nullptr) return SGDN_EINVAL;
+  if (pr->batch < 1 || pr->seqlen < 1 || pr->n_qk < 1 || pr->n_v < 1) return SGDN_EINVAL;
+  if (pr->dtype != SGDN_F32 && pr->dtype != SGDN_BF16) return SGDN_EINVAL;
+  if (pr->solve != SGDN_SOLVE_EXACT && pr->solve != SGDN_SOLVE_BLOCKADJ) return SGDN_EINVAL;
+  if (pr->o_dtype != SGDN_F32 && pr->o_dtype != SGDN_BF16) return SGDN_EINVAL;
+  if (pr->d_k != 128 || pr->d_v != 128) return SGDN_EUNSUPPORTED;
+  if (pr->n_v != 2 * pr->n_qk) return SGDN_EUNSUPPORTED;
+  // grid dimensions and 32-bit in-kernel offsets
+  if ((long long)pr->batch * pr->seqlen > (1LL << 31) / 4 / pr->n_v) return SGDN_EUNSUPPORTED;
+  return SGDN_OK;
+}
+
+int check_params(const sgdn_problem* pr, const sgdn_sparse_params* sp) {
+  if (sp == nullptr) return SGDN_EINVAL;
+  const int bp = budget_bp(sp->keep_budget);
+  if (!(sp->keep_budget > 0.f) || bp < 1 || bp > 10000) return SGDN_EINVAL;
+  if (sp->tail != 16 || sp->r_window != 16) return SGDN_EUNSUPPORTED;
+  if (pr->n_v != 2 * NP_SPARSE) return SGDN_EUNSUPPORTED;
+  const int C = (pr->seqlen + 63) / 64;
+  if (C > 8192) return SGDN_EUNSUPPORTED;
+  return SGDN_OK;
+}
+
+void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp, Plan& p) {
+  p.B = pr->batch; p.T = pr->seqlen; p.Nq = pr->n_qk; p.Nv = pr->n_v;
+  p.C = (p.T + 63) / 64; p.G = (p.C + 1) / 2;
+  p.bf16 = pr->dtype == SGDN_BF16; p.esz = p.bf16 ? 2 : 4; p.solve = pr->solve;
+  int k[3] = {p.C, p.C, p.C};
+  if (sparse) tier_counts(p.C, budget_bp(sp->keep_budget), k);
+  p.kL = k[0]; p.kM = k[1]; p.kH = k[2];
+  const int NP = p.Nv / 2;
+  p.Emax = NP * p.C;
+  p.snap_cap = sparse ? NP * (p.G > 1 ? p.G - 1 : 1) : (p.G > 1 ? p.G - 1 : 1);
+  const size_t B = p.B, Nv = p.Nv, C = p.C, G = p.G, E = p.esz;
+  size_t sz[B_COUNT];
+  memset(sz, 0, sizeof(sz));
+  sz[B_G] = B * Nv * C * L * 4;
+  sz[B_GAMMA] = B * Nv * C * 4;
+  sz[B_P] = B * Nv * (C + 1) * 8;
+  sz[B_U] = B * Nv * C * L * DV * 4;
+  sz[B_KT] = B * p.Nq * C * DK * L * E;
+  sz[B_S0T] = B * Nv * DV * DK * 4;
+  if (!sparse) {
+    sz[B_W] = B * Nv * C * L * DK * E;
+    sz[B_SNAP] = B * Nv * (size_t)p.snap_cap * DV * DK * 4;
+  } else {
+    sz[B_CB] = B * Nv * C * L * L * E;
+    sz[B_SNAP] = B * (size_t)p.snap_cap * 2 * DV * DK * 4;
+    sz[B_SCORE] = B * Nv * C * 4;
+    sz[B_ETA] = B * Nv * 4;
+    sz[B_RANK] = B * NP * C * 4;
+    sz[B_TINFO] = B * 8 * 4;
+    sz[B_MASK] = B * NP * C;
+    sz[B_TIER] = B * NP;
+    sz[B_ROWPAIR] = B * NP * 4;
+    sz[B_ROWPTR] = B * (NP + 1) * 4;
+    sz[B_COL] = B * (size_t)p.Emax * 4;
+    sz[B_PRED] = B * NP * G * 4;
+    sz[B_GSLOT] = B * NP * G * 4;
+    sz[B_ESLOT] = B * (size_t)p.Emax * 4;
+    sz[B_WPK] = B * (size_t)p.Emax * 2 * L * DK * E;
+    sz[B_STATS] = B * 9 * 4;
+  }
+  size_t o = 0;
+  for (int i = 0; i < B_COUNT; ++i) {
+    p.off[i] = o;
+    o += align256(sz[i]);
+  }
+  p.total = o;
+}
+
+template <typename T> T* at(void* ws, const Plan& p, Buf b) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + p.off[b]);
+}
+
+#define SGDN_TRY(expr)                        \
+  do {                                        \
+    if ((expr) != hipSuccess) return SGDN_EHIP; \
+  } while (0)
+
+IntraArgs intra_args(const Plan& pl, void* ws, const void* k, const void* v, const float* a,
+                     const void* beta, int sparse) {
+  IntraArgs ia{};
+  ia.k = k; ia.v = v; ia.a = a; ia.beta = beta;
+  ia.B = pl.B; ia.T = pl.T; ia.Nq = pl.Nq; ia.Nv = pl.Nv; ia.C = pl.C; ia.solve = pl.solve;
+  ia.g = at<float>(ws, pl, B_G);
+  ia.gamma = at<float>(ws, pl, B_GAMMA);
+  ia.U = at<float>(ws, pl, B_U);
+  ia.W = sparse ? nullptr : at<void>(ws, pl, B_W);
+  ia.Cb = sparse ? at<void>(ws, pl, B_CB) : nullptr;
+  ia.KT = at<void>(ws, pl, B_KT);
+  ia.score = sparse ? at<float>(ws, pl, B_SCORE) : nullptr;
+  return ia;
+}
+
+int debug_copies(const Plan& pl, void* ws, sgdn_debug* dbg, hipStream_t st, int with_prefix) {
+  if (dbg == nullptr) return SGDN_OK;
+  const size_t nhc = (size_t)pl.B * pl.Nv * pl.C;
+  if (dbg->g) SGDN_TRY(hipMemcpyAsync(dbg->g, at<void>(ws, pl, B_G), nhc * L * 4, hipMemcpyDeviceToDevice, st));
+  if (dbg->gamma) SGDN_TRY(hipMemcpyAsync(dbg->gamma, at<void>(ws, pl, B_GAMMA), nhc * 4, hipMemcpyDeviceToDevice, st));
+  if (dbg->prefix) {
+    if (!with_prefix) {
+      PrefixArgs pa{at<float>(ws, pl, B_GAMMA), at<double>(ws, pl, B_P), pl.B, pl.Nv, pl.C};
+      SGDN_TRY(launch_prefix(pa, st));
+    }
+    SGDN_TRY(hipMemcpyAsync(dbg->prefix, at<void>(ws, pl, B_P), (size_t)pl.B * pl.Nv * (pl.C + 1) * 8,
+                            hipMemcpyDeviceToDevice, st));
+  }
+  if (dbg->U) SGDN_TRY(launch_debug_u(at<float>(ws, pl, B_U), static_cast<float*>(dbg->U), pl.B, pl.Nv, pl.C, st));
+  return SGDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sgdn_status_string(int status) {
+  switch (status) {
+    case SGDN_OK: return "ok";
+    case SGDN_EINVAL: return "invalid argument";
+    case SGDN_EUNSUPPORTED: return "unsupported problem";
+    case SGDN_EWORKSPACE: return "workspace too small";
+    case SGDN_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t sgdn_workspace_bytes(const sgdn_problem* prob, int sparse, const sgdn_sparse_params* params) {
+  if (check_problem(prob) != SGDN_OK) return 0;
+  if (sparse && check_params(prob, params) != SGDN_OK) return 0;
+  Plan pl;
+  make_plan(prob, sparse, params, pl);
+  return pl.total;
+}
+
+int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, const void* v,
+                       const float* a, const void* beta, const float* s0, void* o,
+                       float* s_final, void* ws, size_t ws_bytes, void* stream, sgdn_debug* dbg) {
+  int st = check_problem(prob);
+  if (st != SGDN_OK) return st;
+  if (!q || !k || !v || !a || !beta || !o || !ws) return SGDN_EINVAL;
+  Plan pl;
+  make_plan(prob, 0, nullptr, pl);
+  if (ws_bytes < pl.total) return SGDN_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  SGDN_TRY(launch_intra(intra_args(pl, ws, k, v, a, beta, 0), pl.bf16, s));
+  if ((st = debug_copies(pl, ws, dbg, s, 0)) != SGDN_OK) return st;
+  if (s0 != nullptr) {
+    S0PrepArgs sa{s0, at<float>(ws, pl, B_S0T), pl.B, pl.Nv};
+    SGDN_TRY(launch_s0prep(sa, s));
+  }
+  HScanArgs ha{};
+  ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, B_W); ha.U = at<float>(ws, pl, B_U);
+  ha.g = at<float>(ws, pl, B_G); ha.gamma = at<float>(ws, pl, B_GAMMA); ha.P = nullptr;
+  ha.s0 = s0; ha.s_final = s_final; ha.snap = at<float>(ws, pl, B_SNAP);
+  ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 0;
+  SGDN_TRY(launch_hscan(ha, pl.bf16, s));
+  OChunkArgs oa{};
+  oa.q = q; oa.k = k; oa.U = at<float>(ws, pl, B_U); oa.snap = at<float>(ws, pl, B_SNAP);
+  oa.s0T = s0 ? at<float>(ws, pl, B_S0T) : nullptr;
+  oa.o_bf16 = prob->o_dtype == SGDN_BF16;
+  oa.g = at<float>(ws, pl, B_G); oa.gamma = at<float>(ws, pl, B_GAMMA); oa.P = nullptr;
+  oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
+  oa.sparse = 0;
+  SGDN_TRY(launch_ochunk(oa, pl.bf16, s));
+  return SGDN_OK;
+}
+
+int sgdn_select(const sgdn_problem* prob, const float* score, const float* gamma, const float* eta,
+                const sgdn_sparse_params* params, uint8_t* mask, uint8_t* tier, int32_t* row_pair,
+                int32_t* row_ptr, int32_t* col, int32_t* pred, int32_t* group_slot,
+                sgdn_stats* stats, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_problem(prob);
+  if (st != SGDN_OK) return st;
+  if ((st = check_params(prob, params)) != SGDN_OK) return st;
+  if (!score || !gamma || !eta || !mask || !tier || !row_pair || !row_ptr || !col || !pred ||
+      !group_slot || !ws)
+    return SGDN_EINVAL;
+  Plan pl;
+  make_plan(prob, 1, params, pl);
+  if (ws_bytes < pl.total) return SGDN_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SelectArgs sa{};
+  sa.score = score; sa.gamma = gamma; sa.eta = eta;
+  sa.B = pl.B; sa.C = pl.C; sa.keep_bp = budget_bp(params->keep_budget);
+  sa.rank = at<int32_t>(ws, pl, B_RANK); sa.tierinfo = at<int32_t>(ws, pl, B_TINFO);
+  sa.mask = mask; sa.tier = tier; sa.row_pair = row_pair; sa.row_ptr = row_ptr; sa.col = col;
+  sa.pred = pred; sa.group_slot = group_slot; sa.event_slot = at<int32_t>(ws, pl, B_ESLOT);
+  sa.Emax = NP_SPARSE * pl.kH; sa.G = pl.G;
+  sa.stats = stats; sa.mask_in = nullptr;
+  SGDN_TRY(launch_select_full(sa, pl.kL, pl.kM, pl.kH, s));
+  return SGDN_OK;
+}
+
+int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, const void* v,
+                        const float* a, const void* beta, const void* z,
+                        const sgdn_sparse_params* params, const uint8_t* mask_override,
+                        const float* s0, void* o, float* s_final, sgdn_stats* stats, void* ws,
+                        size_t ws_bytes, void* stream, sgdn_debug* dbg) {
+  int st = check_problem(prob);
+  if (st != SGDN_OK) return st;
+  if ((st = check_params(prob, params)) != SGDN_OK) return st;
+  if (!q || !k || !v || !a || !beta || !o || !ws) return SGDN_EINVAL;
+  if (z == nullptr && mask_override == nullptr) return SGDN_EINVAL;
+  Plan pl;
+  make_plan(prob, 1, params, pl);
+  if (ws_bytes < pl.total) return SGDN_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int NP = pl.Nv / 2;
+
+  // intra: local solve, U, staged Cb, tail score, gamma
+  SGDN_TRY(launch_intra(intra_args(pl, ws, k, v, a, beta, 1), pl.bf16, s));
+  PrefixArgs pa{at<float>(ws, pl, B_GAMMA), at<double>(ws, pl, B_P), pl.B, pl.Nv, pl.C};
+  SGDN_TRY(launch_prefix(pa, s));
+  if ((st = debug_copies(pl, ws, dbg, s, 1)) != SGDN_OK) return st;
+
+  // selector and event layout
+  if (mask_override == nullptr) {
+    GateArgs ga{z, params->norm_weight, at<float>(ws, pl, B_ETA), pl.B, pl.T, pl.Nv, pl.C};
+    SGDN_TRY(launch_gate(ga, pl.bf16, s));
+  }
+  const int Emax = mask_override ? NP * pl.C : NP * pl.kH;
+  SelectArgs sa{};
+  sa.score = at<float>(ws, pl, B_SCORE); sa.gamma = at<float>(ws, pl, B_GAMMA);
+  sa.eta = at<float>(ws, pl, B_ETA);
+  sa.B = pl.B; sa.C = pl.C; sa.keep_bp = budget_bp(params->keep_budget);
+  sa.rank = at<int32_t>(ws, pl, B_RANK); sa.tierinfo = at<int32_t>(ws, pl, B_TINFO);
+  sa.mask = at<uint8_t>(ws, pl, B_MASK); sa.tier = at<uint8_t>(ws, pl, B_TIER);
+  sa.row_pair = at<int32_t>(ws, pl, B_ROWPAIR); sa.row_ptr = at<int32_t>(ws, pl, B_ROWPTR);
+  sa.col = at<int32_t>(ws, pl, B_COL); sa.pred = at<int32_t>(ws, pl, B_PRED);
+  sa.group_slot = at<int32_t>(ws, pl, B_GSLOT); sa.event_slot = at<int32_t>(ws, pl, B_ESLOT);
+  sa.Emax = Emax; sa.G = pl.G;
+  sa.stats = stats ? static_cast<void*>(stats) : at<void>(ws, pl, B_STATS);
+  sa.mask_in = mask_override;
+  SGDN_TRY(launch_select_full(sa, pl.kL, pl.kM, pl.kH, s));
+  if (dbg != nullptr) {
+    if (dbg->score) SGDN_TRY(hipMemcpyAsync(dbg->score, sa.score, (size_t)pl.B * pl.Nv * pl.C * 4, hipMemcpyDeviceToDevice, s));
+    if (dbg->eta && !mask_override) SGDN_TRY(hipMemcpyAsync(dbg->eta, sa.eta, (size_t)pl.B * pl.Nv * 4, hipMemcpyDeviceToDevice, s));
+    if (dbg->mask) SGDN_TRY(hipMemcpyAsync(dbg->mask, sa.mask, (size_t)pl.B * NP * pl.C, hipMemcpyDeviceToDevice, s));
+    if (dbg->tier) SGDN_TRY(hipMemcpyAsync(dbg->tier, sa.tier, (size_t)pl.B * NP, hipMemcpyDeviceToDevice, s));
+  }
+
+  // deferred W of the kept events
+  DeferredWArgs da{};
+  da.KT = at<void>(ws, pl, B_KT); da.Cb = at<void>(ws, pl, B_CB); da.Wpk = at<void>(ws, pl, B_WPK);
+  da.row_pair = sa.row_pair; da.row_ptr = sa.row_ptr; da.col = sa.col;
+  da.B = pl.B; da.Nv = pl.Nv; da.Nq = pl.Nq; da.C = pl.C; da.Emax = Emax; da.solve = pl.solve;
+  SGDN_TRY(launch_deferred_w(da, pl.bf16, s));
+
+  if (s0 != nullptr) {
+    S0PrepArgs s0a{s0, at<float>(ws, pl, B_S0T), pl.B, pl.Nv};
+    SGDN_TRY(launch_s0prep(s0a, s));
+  }
+  HScanArgs ha{};
+  ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, B_WPK); ha.U = at<float>(ws, pl, B_U);
+  ha.g = at<float>(ws, pl, B_G); ha.gamma = at<float>(ws, pl, B_GAMMA); ha.P = at<double>(ws, pl, B_P);
+  ha.s0 = s0; ha.s_final = s_final; ha.snap = at<float>(ws, pl, B_SNAP);
+  ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 1;
+  ha.row_pair = sa.row_pair; ha.row_ptr = sa.row_ptr; ha.col = sa.col; ha.event_slot = sa.event_slot;
+  ha.Emax = Emax; ha.snap_cap = pl.snap_cap;
+  SGDN_TRY(launch_hscan(ha, pl.bf16, s));
+
+  OChunkArgs oa{};
+  oa.q = q; oa.k = k; oa.U = at<float>(ws, pl, B_U); oa.snap = at<float>(ws, pl, B_SNAP);
+  oa.s0T = s0 ? at<float>(ws, pl, B_S0T) : nullptr;
+  oa.o_bf16 = prob->o_dtype == SGDN_BF16;
+  oa.g = at<float>(ws, pl, B_G); oa.gamma = at<float>(ws, pl, B_GAMMA); oa.P = at<double>(ws, pl, B_P);
+  oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
+  oa.sparse = 1; oa.pred = sa.pred; oa.group_slot = sa.group_slot; oa.snap_cap = pl.snap_cap;
+  SGDN_TRY(launch_ochunk(oa, pl.bf16, s));
+  return SGDN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+// Shared device helpers for the gfx950 kernels: element types, MFMA
+// fragments and their loads/stores.
+//
+// Matrix-core convention (v_mfma_f32_16x16x32_bf16, 64-lane wavefront):
+//   lane l, n = l % 16, g = l / 16
+//   A fragment (16 x 32, row-major M x K): row n,    k = 8g .. 8g+7
+//   B fragment (32 x 16, K x N):           column n, k = 8g .. 8g+7
+//   C/D tile   (16 x 16):                  column n, rows 4g .. 4g+3
+// The fp32 path keeps the same 8-values-per-lane fragments and issues eight
+// v_mfma_f32_16x16x4_f32: product i takes value i of every lane, i.e. the
+// k-slots {i, 8+i, 16+i, 24+i}; together the eight cover all 32 slots once.
+//
+// "Permuted" fragments: two D tiles stacked along the reduction index (rows
+// r0..r0+15 and r0+16..r0+31) already hold, per lane, the 8 values
+// {r0+4g..r0+4g+3, r0+16+4g..r0+16+4g+3}.  Used as a B (or A) fragment, slot
+// 8g+j stands for row r0+4g+j (j<4) or r0+16+4g+j-4 (j>=4); the other operand
+// is then loaded with the same order (two 4-element runs), so a product's
+// result feeds the next product without leaving the registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgdn {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int L = 64;      // chunk length
+constexpr int DK = 128;    // key dimension
+constexpr int DV = 128;    // value dimension
+
+template <typename E> struct FragOf;
+template <> struct FragOf<bf16> { using T = bf16x8; using H = bf16x4; };
+template <> struct FragOf<float> { using T = f32x8; using H = f32x4; };
+template <typename E> using frag_t = typename FragOf<E>::T;
+template <typename E> using half_t = typename FragOf<E>::H;
+
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+template <typename E> __device__ __forceinline__ E from_f(float x);
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const f32x8& a, const f32x8& b, f32x4 c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+  return c;
+}
+
+// 8 consecutive elements (16 B for bf16, 32 B for fp32; aligned).
+template <typename E> __device__ __forceinline__ frag_t<E> ld8(const E* p) {
+  return *reinterpret_cast<const frag_t<E>*>(p);
+}
+// 4 consecutive elements from p0 followed by 4 from p1 (permuted fragment).
+template <typename E> __device__ __forceinline__ frag_t<E> ld44(const E* p0, const E* p1) {
+  half_t<E> lo = *reinterpret_cast<const half_t<E>*>(p0);
+  half_t<E> hi = *reinterpret_cast<const half_t<E>*>(p1);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// 4 consecutive elements as fp32.
+template <typename E> __device__ __forceinline__ f32x4 ld4f(const E* p) {
+  half_t<E> h = *reinterpret_cast<const half_t<E>*>(p);
+  return f32x4{to_f(h[0]), to_f(h[1]), to_f(h[2]), to_f(h[3])};
+}
+template <typename E> __device__ __forceinline__ void st4(E* p, f32x4 v) {
+  half_t<E> h;
+  h[0] = from_f<E>(v[0]); h[1] = from_f<E>(v[1]);
+  h[2] = from_f<E>(v[2]); h[3] = from_f<E>(v[3]);
+  *reinterpret_cast<half_t<E>*>(p) = h;
+}
+// Two stacked D tiles -> one permuted fragment.
+template <typename E> __device__ __forceinline__ frag_t<E> pack44(f32x4 a, f32x4 b) {
+  frag_t<E> f;
+  f[0] = from_f<E>(a[0]); f[1] = from_f<E>(a[1]); f[2] = from_f<E>(a[2]); f[3] = from_f<E>(a[3]);
+  f[4] = from_f<E>(b[0]); f[5] = from_f<E>(b[1]); f[6] = from_f<E>(b[2]); f[7] = from_f<E>(b[3]);
+  return f;
+}
+template <typename E> __device__ __forceinline__ frag_t<E> zero_frag() {
+  frag_t<E> f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = from_f<E>(0.f);
+  return f;
+}
+
+// fp32 -> bf16 hi/lo split: x ~= hi + lo with |x - hi - lo| <= 2^-16 |x|.
+// Products with an fp32 operand use both halves (two or three MFMAs), so the
+// fp32-grade intermediates keep fp32 accuracy on the bf16 matrix cores.
+__device__ __forceinline__ void split8(const f32x8& x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    hi[i] = (bf16)x[i];
+    lo[i] = (bf16)(x[i] - (float)hi[i]);
+  }
+}
+__device__ __forceinline__ f32x8 ld8f(const float* p) { return *reinterpret_cast<const f32x8*>(p); }
+__device__ __forceinline__ f32x8 cat44(f32x4 a, f32x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void st4f(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+// Accumulate a (fp32 values) x b into acc: one product for fp32 operands, two
+// (hi, lo) for bf16 operands.
+__device__ __forceinline__ f32x4 mma_split_a(const f32x8& a, const bf16x8& b, f32x4 acc) {
+  bf16x8 hi, lo;
+  split8(a, hi, lo);
+  acc = mma(hi, b, acc);
+  return mma(lo, b, acc);
+}
+__device__ __forceinline__ f32x4 mma_split_a(const f32x8& a, const f32x8& b, f32x4 acc) {
+  return mma(a, b, acc);
+}
+__device__ __forceinline__ f32x4 mma_split_b(const bf16x8& a, const f32x8& b, f32x4 acc) {
+  bf16x8 hi, lo;
+  split8(b, hi, lo);
+  acc = mma(a, hi, acc);
+  return mma(a, lo, acc);
+}
+__device__ __forceinline__ f32x4 mma_split_b(const f32x8& a, const f32x8& b, f32x4 acc) {
+  return mma(a, b, acc);
+}
+
+// Output element type (o may be fp32 or bf16 independently of the inputs).
+template <typename O> __device__ __forceinline__ void st4o(O* p, f32x4 v);
+template <> __device__ __forceinline__ void st4o<float>(float* p, f32x4 v) { st4f(p, v); }
+template <> __device__ __forceinline__ void st4o<bf16>(bf16* p, f32x4 v) { st4<bf16>(p, v); }
+
+// 16-byte vector copy helpers (global <-> LDS staging).
+struct alignas(16) V16 { uint32_t w[4]; };
+__device__ __forceinline__ V16 ldv(const void* p) { return *reinterpret_cast<const V16*>(p); }
+__device__ __forceinline__ void stv(void* p, const V16& v) { *reinterpret_cast<V16*>(p) = v; }
+__device__ __forceinline__ V16 zv() { V16 v; v.w[0] = v.w[1] = v.w[2] = v.w[3] = 0u; return v; }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace sgdn

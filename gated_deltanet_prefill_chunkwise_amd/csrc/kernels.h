@@ -1,0 +1,99 @@
+// Launch interfaces of the gfx950 kernels (internal to libsgdn.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sgdn {
+
+// Workspace tensors (all per batch b, head-major):
+//   g      [B][Nv][C][64]      fp32  in-chunk inclusive log2 decay
+//   gamma  [B][Nv][C]          fp32  chunk retention g[63]
+//   P      [B][Nv][C+1]        fp64  prefix of gamma
+//   U      [B][Nv][C][dv][64]  fp32  U (then U' in place), dv-major tiles
+//   W      [B][Nv][C][64][dk]  E     dense W, token-major tiles
+//   Cb     [B][Nv][C][64][64]  E     staged C diag(beta 2^g), row-major
+//   KT     [B][Nq][C][dk][64]  E     transposed key tiles
+//   snap   [..][dv][dk]        fp32  compact state snapshots (transposed)
+//   Wpk    [B][Emax][2][64][dk] E    deferred W of kept events
+
+struct IntraArgs {
+  const void* k; const void* v; const float* a; const void* beta;
+  int B, T, Nq, Nv, C, solve;
+  float* g; float* gamma;
+  float* U; void* W; void* Cb; void* KT;
+  float* score;
+};
+
+struct PrefixArgs {
+  const float* gamma; double* P; int B, Nv, C;
+};
+
+// Chain scan over the events of one value head, one dv slice of 16 columns
+// per workgroup.  Dense: every chunk is an event, W from the intra kernel.
+// Sparse: events from the CSR rows, W packed per event.
+struct HScanArgs {
+  const void* KT; const void* W; float* U;
+  const float* g; const float* gamma; const double* P;
+  const float* s0;          // [B][Nv][dk][dv] or null
+  float* s_final;           // [B][Nv][dk][dv] or null
+  float* snap;              // snapshots
+  int B, Nq, Nv, C;
+  int sparse;
+  // sparse metadata (per batch)
+  const int32_t* row_pair;  // [B][NP]
+  const int32_t* row_ptr;   // [B][NP+1]
+  const int32_t* col;       // [B][Emax]
+  const int32_t* event_slot;// [B][Emax]
+  int Emax;
+  int snap_cap;             // snapshot slots per batch (sparse)
+};
+
+struct OChunkArgs {
+  const void* q; const void* k; const float* U; const float* snap; const float* s0T;
+  const float* g; const float* gamma; const double* P;
+  void* o; int o_bf16;
+  int B, T, Nq, Nv, C, G;
+  int sparse;
+  const int32_t* pred;        // [B][NP][G]
+  const int32_t* group_slot;  // [B][NP][G]
+  int snap_cap;
+};
+
+struct S0PrepArgs { const float* s0; float* s0T; int B, Nv; };
+
+struct GateArgs {
+  const void* z; const float* w; float* eta; int B, T, Nv, C;
+};
+
+struct SelectArgs {
+  const float* score; const float* gamma; const float* eta;
+  int B, C, keep_bp;
+  int32_t* rank;        // [B][16][C]   workspace
+  int32_t* tierinfo;    // [B][8]       workspace: k_L, k_M, k_H, n_H, n_M
+  uint8_t* mask; uint8_t* tier;
+  int32_t* row_pair; int32_t* row_ptr; int32_t* col; int32_t* pred;
+  int32_t* group_slot; int32_t* event_slot; int32_t* col_row;  // col_row: [B][Emax] row of each event
+  int Emax, G;
+  void* stats;          // sgdn_stats* or null
+  const uint8_t* mask_in;  // override mask [B][16][C] or null
+};
+
+struct DeferredWArgs {
+  const void* KT; const void* Cb; void* Wpk;
+  const int32_t* row_pair; const int32_t* row_ptr; const int32_t* col;
+  int B, Nv, Nq, C, Emax, solve;
+};
+
+hipError_t launch_intra(const IntraArgs& a, int bf16, hipStream_t s);
+hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s);
+hipError_t launch_hscan(const HScanArgs& a, int bf16, hipStream_t s);
+hipError_t launch_ochunk(const OChunkArgs& a, int bf16, hipStream_t s);
+hipError_t launch_s0prep(const S0PrepArgs& a, hipStream_t s);
+hipError_t launch_gate(const GateArgs& a, int bf16, hipStream_t s);
+hipError_t launch_select_full(const SelectArgs& a, int kL, int kM, int kH, hipStream_t s);
+hipError_t launch_deferred_w(const DeferredWArgs& a, int bf16, hipStream_t s);
+hipError_t launch_debug_u(const float* Ut, float* U, int B, int Nv, int C, hipStream_t s);
+
+}  // namespace sgdn

@@ -1,0 +1,153 @@
+// Small kernels of the pipeline: log-decay prefix, initial-state transpose,
+// gate energy, deferred W of kept events, debug copy of U.
+#include "common.h"
+#include "kernels.h"
+
+namespace sgdn {
+
+namespace {
+
+// P_0 = 0, P_{c+1} = P_c + gamma_c in fp64 (SparseGDN reading notes,
+// Sec. 2.6, Eqs. (19)-(20)).  One wave per (batch, head): each lane sums a
+// contiguous run of chunks, then an exclusive wave scan joins the runs.
+__global__ __launch_bounds__(64) void prefix_kernel(PrefixArgs p) {
+  const int bh = blockIdx.x, lane = threadIdx.x, C = p.C;
+  const float* gm = p.gamma + (size_t)bh * C;
+  double* P = p.P + (size_t)bh * (C + 1);
+  const int per = (C + 63) / 64;
+  const int lo = lane * per, hi = min(C, lo + per);
+  double run = 0.0;
+  for (int c = lo; c < hi; ++c) run += (double)gm[c];
+  double incl = run;
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  double acc = incl - run;
+  if (lane == 0) P[0] = 0.0;
+  for (int c = lo; c < hi; ++c) {
+    acc += (double)gm[c];
+    P[c + 1] = acc;
+  }
+}
+
+// s0 [dk][dv] -> transposed [dv][dk] (fp32), the "virtual snapshot" that
+// output groups without a predecessor read.
+__global__ __launch_bounds__(256) void s0prep_kernel(S0PrepArgs p) {
+  const size_t bh = blockIdx.x;
+  const float* s = p.s0 + bh * DK * DV;
+  float* o = p.s0T + bh * DV * DK;
+  for (int q = threadIdx.x; q < DK * DV; q += 256) {
+    const int dv = q >> 7, dk = q & 127;
+    o[q] = s[dk * DV + dv];
+  }
+}
+
+// eta_h = mean over the 4C samples of (w_v SiLU(z[64c + 8 + 16a, h, v]))^2,
+// v = 73 (4c + a) mod 128 (SparseGDN reading notes, Sec. 2.4, Eq. (11)).
+template <typename E>
+__global__ __launch_bounds__(256) void gate_kernel(GateArgs p) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const E* z = static_cast<const E*>(p.z);
+  const int ns = 4 * p.C;
+  float acc = 0.f;
+  for (int j = tid; j < ns; j += 256) {
+    const int c = j >> 2, a = j & 3;
+    const int pos = c * L + 8 + 16 * a;
+    const int v = (73 * j) & (DV - 1);
+    if (pos < p.T) {
+      const float x = to_f(z[((size_t)(b * p.T + pos) * p.Nv + h) * DV + v]);
+      const float wv = p.w ? p.w[v] : 1.f;
+      const float s = wv * (x / (1.f + __expf(-x)));
+      acc += s * s;
+    }
+  }
+  __shared__ float red[4];
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) p.eta[(size_t)b * p.Nv + h] = (red[0] + red[1] + red[2] + red[3]) / (float)ns;
+}
+
+// Deferred W of kept events only (SparseGDN reading notes, Sec. 2.5,
+// Eq. (15)): W = Cb K from the staged coefficients, computed as
+// W^T = K^T Cb^T and stored token-major per event (both heads of the pair).
+// The grid is sized to the capacity E_max; blocks past the on-device E exit.
+template <typename E>
+__global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int NP = p.Nv / 2;
+  const int E_ = p.row_ptr[b * (NP + 1) + NP];
+  if (i >= E_) return;
+  int row = 0;
+  while (row + 1 < NP && p.row_ptr[b * (NP + 1) + row + 1] <= i) ++row;
+  const int pr = p.row_pair[b * NP + row];
+  const int c = p.col[(size_t)b * p.Emax + i];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const bool blockadj = p.solve == 1;
+  const E* KT = static_cast<const E*>(p.KT) + (((size_t)b * p.Nq + pr) * p.C + c) * DK * L;
+  const int ks_lo = (blockadj && w == 3) ? 1 : 0;
+  const int ks_hi = (w >= 2) ? 1 : 0;
+  for (int hh = 0; hh < 2; ++hh) {
+    const int h = 2 * pr + hh;
+    const E* Cb = static_cast<const E*>(p.Cb) + (((size_t)b * p.Nv + h) * p.C + c) * L * L;
+    f32x4 acc[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
+    for (int ks = ks_lo; ks <= ks_hi; ++ks) {
+      const frag_t<E> fb = ld8(Cb + (16 * w + n16) * L + 32 * ks + 8 * g4);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        acc[mt] = mma(ld8(KT + (16 * mt + n16) * L + 32 * ks + 8 * g4), fb, acc[mt]);
+    }
+    E* W = static_cast<E*>(p.Wpk) + (((size_t)b * p.Emax + i) * 2 + hh) * L * DK;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) st4(W + (16 * w + n16) * DK + 16 * mt + 4 * g4, acc[mt]);
+  }
+}
+
+// U tiles [dv][t] -> token-major [t][dv] copy for the debug output.
+__global__ __launch_bounds__(256) void debug_u_kernel(const float* Ut, float* U) {
+  const size_t tile = blockIdx.x;
+  for (int q = threadIdx.x; q < L * DV; q += 256) {
+    const int t = q >> 7, dv = q & 127;
+    U[tile * L * DV + q] = Ut[tile * DV * L + dv * L + t];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(prefix_kernel, dim3(a.B * a.Nv), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_s0prep(const S0PrepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(s0prep_kernel, dim3(a.B * a.Nv), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate(const GateArgs& a, int bf16, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(gate_kernel<sgdn::bf16>, dim3(a.Nv, a.B), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(gate_kernel<float>, dim3(a.Nv, a.B), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_deferred_w(const DeferredWArgs& a, int bf16, hipStream_t s) {
+  dim3 grid(a.Emax, a.B);
+  if (bf16)
+    hipLaunchKernelGGL(deferred_w_kernel<sgdn::bf16>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(deferred_w_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_u(const float* Ut, float* U, int B, int Nv, int C, hipStream_t s) {
+  hipLaunchKernelGGL(debug_u_kernel, dim3(B * Nv * C), dim3(256), 0, s, Ut, U);
+  return hipGetLastError();
+}
+
+}  // namespace sgdn

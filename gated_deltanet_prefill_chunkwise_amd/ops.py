@@ -1,0 +1,263 @@
+"""Thin Python binding of libsgdn.so (C ABI in include/sgdn.h).
+
+Argument marshalling only: every step of the prefill runs in the library's HIP
+kernels.  Tensors are torch device tensors (torch provides memory and the
+stream).  The library is loaded on first use; a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsgdn.so")
+
+SGDN_F32, SGDN_BF16 = 0, 1
+SOLVES = {"exact": 0, "blockadj": 1}
+EXPORTS = ("sgdn_workspace_bytes", "sgdn_prefill_dense", "sgdn_select",
+           "sgdn_prefill_sparse", "sgdn_status_string")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "seqlen", "n_qk", "n_v", "d_k", "d_v", "dtype", "solve", "o_dtype")]
+
+
+class SparseParams(ctypes.Structure):
+    _fields_ = [("keep_budget", ctypes.c_float), ("tail", ctypes.c_int32),
+                ("r_window", ctypes.c_int32), ("norm_weight", ctypes.c_void_p)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("E_max", ctypes.c_int32),
+                ("n_tier", ctypes.c_int32 * 3), ("k", ctypes.c_int32 * 3),
+                ("n_snapshots", ctypes.c_int32)]
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("g", "gamma", "prefix", "score", "eta", "U", "mask", "tier")]
+
+
+STATS_INTS = ctypes.sizeof(Stats) // 4
+
+_lib = None
+
+
+class SgdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+        self.status = status
+
+
+def lib():
+    """Load libsgdn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m gated_deltanet_prefill_chunkwise_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        P = ctypes.POINTER(Problem)
+        SP = ctypes.POINTER(SparseParams)
+        L.sgdn_workspace_bytes.argtypes = [P, i32, SP]
+        L.sgdn_workspace_bytes.restype = sz
+        L.sgdn_prefill_dense.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.sgdn_prefill_dense.restype = i32
+        L.sgdn_select.argtypes = [P, vp, vp, vp, SP, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sgdn_select.restype = i32
+        L.sgdn_prefill_sparse.argtypes = [P, vp, vp, vp, vp, vp, vp, SP, vp, vp, vp, vp, vp, vp,
+                                          sz, vp, vp]
+        L.sgdn_prefill_sparse.restype = i32
+        L.sgdn_status_string.argtypes = [i32]
+        L.sgdn_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sgdn_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _code(dtype):
+    import torch
+    return SGDN_BF16 if dtype == torch.bfloat16 else SGDN_F32
+
+
+def problem(q, v, solve="exact", out_dtype=None) -> Problem:
+    B, T, Nq, d = q.shape
+    Nv, dv = v.shape[2], v.shape[3]
+    od = _code(out_dtype) if out_dtype is not None else SGDN_F32
+    return Problem(B, T, Nq, Nv, d, dv, _code(q.dtype), SOLVES[solve], od)
+
+
+def sparse_params(keep_budget=0.29, norm_weight=None, tail=16, r_window=16) -> SparseParams:
+    return SparseParams(float(keep_budget), tail, r_window,
+                        None if norm_weight is None else norm_weight.data_ptr())
+
+
+def workspace_bytes(prob: Problem, sparse: bool, params: SparseParams | None = None) -> int:
+    return int(lib().sgdn_workspace_bytes(ctypes.byref(prob), int(sparse),
+                                          None if params is None else ctypes.byref(params)))
+
+
+def _check(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _workspace(nbytes, device, workspace):
+    import torch
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def debug_struct(**bufs) -> Debug:
+    return Debug(*[None if bufs.get(n) is None else bufs[n].data_ptr() for n, _ in Debug._fields_])
+
+
+def prefill_dense(q, k, v, a, beta, s0=None, solve="exact", want_state=True, o=None,
+                  s_final=None, workspace=None, debug=None, stream=None, out_dtype=None):
+    """Dense GDN-core prefill; returns (o, s_final).
+
+    o is fp32 unless ``out_dtype`` (or a given ``o``) says otherwise.
+    """
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta")):
+        _check(t, n, q.dtype)
+    _check(a, "a", torch.float32)
+    _check(s0, "s0", torch.float32)
+    if o is not None:
+        out_dtype = o.dtype
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    _check(o, "o", out_dtype)
+    prob = problem(q, v, solve, out_dtype)
+    B, Nv, dv = q.shape[0], v.shape[2], v.shape[3]
+    if o is None:
+        o = torch.empty(v.shape, dtype=out_dtype, device=v.device)
+    if want_state and s_final is None:
+        s_final = torch.empty((B, Nv, q.shape[3], dv), dtype=torch.float32, device=q.device)
+    nbytes = workspace_bytes(prob, False)
+    if nbytes == 0:
+        raise SgdnError(-2, "sgdn_workspace_bytes")
+    ws = _workspace(nbytes, q.device, workspace)
+    dbg = None if debug is None else ctypes.byref(debug)
+    st = lib().sgdn_prefill_dense(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                  _ptr(beta), _ptr(s0), _ptr(o), _ptr(s_final), _ptr(ws),
+                                  ws.numel(), _stream(stream), dbg)
+    if st != 0:
+        raise SgdnError(st, "sgdn_prefill_dense")
+    return o, s_final
+
+
+def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None):
+    """Selector + CSR layout on fp32 statistics; returns a dict of device tensors."""
+    import torch
+    B, Nv, C = score.shape
+    for t, n in ((score, "score"), (gamma, "gamma"), (eta, "eta")):
+        _check(t, n, torch.float32)
+    T = C * 64
+    prob = Problem(B, T, Nv // 2, Nv, 128, 128, SGDN_BF16, 1, SGDN_F32)
+    params = sparse_params(keep_budget)
+    nbytes = workspace_bytes(prob, True, params)
+    if nbytes == 0:
+        raise SgdnError(-2, "sgdn_workspace_bytes")
+    ws = _workspace(nbytes, score.device, workspace)
+    NP, G = Nv // 2, (C + 1) // 2
+    dev = score.device
+    kH = tier_counts_host(C, keep_budget)[2]
+    out = dict(
+        mask=torch.empty((B, NP, C), dtype=torch.uint8, device=dev),
+        tier=torch.empty((B, NP), dtype=torch.uint8, device=dev),
+        row_pair=torch.empty((B, NP), dtype=torch.int32, device=dev),
+        row_ptr=torch.empty((B, NP + 1), dtype=torch.int32, device=dev),
+        col=torch.full((B, NP * kH), -1, dtype=torch.int32, device=dev),
+        pred=torch.empty((B, NP, G), dtype=torch.int32, device=dev),
+        group_slot=torch.empty((B, NP, G), dtype=torch.int32, device=dev),
+        stats=torch.zeros((B, STATS_INTS), dtype=torch.int32, device=dev),
+    )
+    st = lib().sgdn_select(ctypes.byref(prob), _ptr(score), _ptr(gamma), _ptr(eta),
+                           ctypes.byref(params), _ptr(out["mask"]), _ptr(out["tier"]),
+                           _ptr(out["row_pair"]), _ptr(out["row_ptr"]), _ptr(out["col"]),
+                           _ptr(out["pred"]), _ptr(out["group_slot"]), _ptr(out["stats"]),
+                           _ptr(ws), ws.numel(), _stream(stream))
+    if st != 0:
+        raise SgdnError(st, "sgdn_select")
+    return out
+
+
+def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
+                   mask_override=None, s0=None, norm_weight=None, want_state=True, o=None,
+                   s_final=None, stats=None, workspace=None, debug=None, stream=None,
+                   out_dtype=None):
+    """SparseGDN prefill; returns (o, s_final, stats[B, 9] int32).
+
+    o is fp32 unless ``out_dtype`` (or a given ``o``) says otherwise.
+    """
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta"), (z, "z")):
+        _check(t, n, q.dtype)
+    _check(a, "a", torch.float32)
+    _check(s0, "s0", torch.float32)
+    _check(mask_override, "mask_override", torch.uint8)
+    _check(norm_weight, "norm_weight", torch.float32)
+    if o is not None:
+        out_dtype = o.dtype
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    _check(o, "o", out_dtype)
+    prob = problem(q, v, solve, out_dtype)
+    params = sparse_params(keep_budget, norm_weight)
+    B, Nv, dv = q.shape[0], v.shape[2], v.shape[3]
+    if o is None:
+        o = torch.empty(v.shape, dtype=out_dtype, device=v.device)
+    if want_state and s_final is None:
+        s_final = torch.empty((B, Nv, q.shape[3], dv), dtype=torch.float32, device=q.device)
+    if stats is None:
+        stats = torch.zeros((B, STATS_INTS), dtype=torch.int32, device=q.device)
+    nbytes = workspace_bytes(prob, True, params)
+    if nbytes == 0:
+        raise SgdnError(-2, "sgdn_workspace_bytes")
+    ws = _workspace(nbytes, q.device, workspace)
+    dbg = None if debug is None else ctypes.byref(debug)
+    st = lib().sgdn_prefill_sparse(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                   _ptr(beta), _ptr(z), ctypes.byref(params), _ptr(mask_override),
+                                   _ptr(s0), _ptr(o), _ptr(s_final), _ptr(stats), _ptr(ws),
+                                   ws.numel(), _stream(stream), dbg)
+    if st != 0:
+        raise SgdnError(st, "sgdn_prefill_sparse")
+    return o, s_final, stats
+
+
+def tier_counts_host(C: int, keep_budget: float = 0.29):
+    """(k_L, k_M, k_H) as the library computes them (sizes of the col array)."""
+    import math
+    bp = int(math.floor(float(ctypes.c_float(keep_budget).value) * 10000.0 + 0.5))
+    if C == 1:
+        return (1, 1, 1)
+    out = []
+    for pct in (8, 30, 95):
+        if bp <= 2900:
+            num, den = pct * bp * C, 290000
+        else:
+            num, den = C * (710000 - (100 - pct) * (10000 - bp)), 710000
+        out.append(min(max((2 * num + den) // (2 * den), 2), C))
+    return tuple(out)

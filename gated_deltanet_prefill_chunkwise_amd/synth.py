@@ -154,3 +154,23 @@ def torch_inputs(seed: int, B: int, T: int, Nq: int, Nv: int, d: int = 128,
     if with_z:
         out["z"] = normal((B, T, Nv, dv)).to(tdt)
     return out
+
+
+def selector_stats(seed: int, B: int, C: int, Nv: int = 32, ties: bool = False):
+    """Synthetic fp32 selection statistics for one batch.
+
+    score [B, Nv, C]: non-negative tail-score-like values with a per-head scale;
+    gamma [B, Nv, C]: chunk log2 retentions (<= 0), per-head rate spread over
+    four decades so that some heads keep memory across chunks; eta [B, Nv]:
+    positive gate energies.  ``ties=True`` puts scores on a coarse grid so that
+    equal values (and equal rank keys) are common.
+    """
+    g = np.random.Generator(np.random.PCG64(seed))
+    scale = g.uniform(0.2, 3.0, (B, Nv, 1))
+    score = np.abs(g.standard_normal((B, Nv, C))) * scale + g.uniform(0.0, 0.5, (B, Nv, C))
+    if ties:
+        score = np.round(score * 4.0) / 4.0
+    rate = np.exp(g.uniform(math.log(1e-4), math.log(4.0), (B, Nv, 1)))
+    gamma = -64.0 * rate * np.abs(1.0 + 0.1 * g.standard_normal((B, Nv, C)))
+    eta = g.uniform(0.05, 2.0, (B, Nv))
+    return (score.astype(np.float32), gamma.astype(np.float32), eta.astype(np.float32))

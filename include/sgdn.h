@@ -1,0 +1,172 @@
+/*
+ * sgdn.h - C ABI of libsgdn.so: chunkwise Gated DeltaNet (GDN) core prefill,
+ * dense and SparseGDN, on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the web page "SparseGDN: Chunk Sparse in Linear
+ * Attention" (reading notes of arXiv 2610.41420v1); citations give the
+ * paper section and equation as that page prints them.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array argument is a DEVICE pointer to memory owned by the caller
+ *   (the library never allocates or frees device memory and never
+ *   synchronises the stream).  Problem / parameter structs are HOST pointers.
+ * - Arrays are dense, row-major, without padding, in the shapes given below.
+ *   B = batch, T = tokens, Nq = query/key heads, Nv = value heads,
+ *   d = d_k, dv = d_v, C = ceil(T / 64) chunks, G = ceil(C / 2) groups,
+ *   NP = Nv / 2 head pairs.
+ * - Value head h reads query/key head h / (Nv / Nq).  Supported: d = dv = 128,
+ *   Nv = 2 * Nq (value heads 2p and 2p+1 share query/key head p; Sec. 2.1).
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *   ordered after prior work on it.  Calls are stateless and reentrant; two
+ *   calls must not share a workspace concurrently.
+ * - Errors: a negative sgdn_status is returned BEFORE anything is enqueued
+ *   when an argument is invalid; SGDN_EHIP reports a failed launch.
+ *   Data-dependent conditions are reported through sgdn_stats.
+ * - Inputs must be finite and the decay must satisfy a <= 0 (a is the log2
+ *   retention; a > 0 is outside the operator's domain).
+ * - T need not be a multiple of 64: the last chunk is padded with tokens
+ *   that have a = 0, beta = 0, q = k = v = 0; their outputs are not written.
+ */
+#ifndef SGDN_H
+#define SGDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SGDN_OK = 0,
+  SGDN_EINVAL = -1,        /* null pointer, bad shape, bad parameter            */
+  SGDN_EUNSUPPORTED = -2,  /* valid but not supported (d != 128, Nv != 2 Nq ...) */
+  SGDN_EWORKSPACE = -3,    /* ws_bytes smaller than sgdn_workspace_bytes()       */
+  SGDN_EHIP = -4           /* a HIP launch failed                                */
+} sgdn_status;
+
+typedef enum { SGDN_F32 = 0, SGDN_BF16 = 1 } sgdn_dtype;
+typedef enum { SGDN_SOLVE_EXACT = 0, SGDN_SOLVE_BLOCKADJ = 1 } sgdn_solve;
+
+/* Problem shape.  dtype applies to q, k, v, beta and z; o_dtype to o (a, s0
+ * and s_final are always fp32).  solve selects the local Delta solve
+ * (Sec. 2.3): SGDN_SOLVE_EXACT = M^{-1}, SGDN_SOLVE_BLOCKADJ = the 7-block
+ * form of Eqs. (7)-(8).
+ * Precision: with bf16 inputs the matrix products run on bf16 MFMA with fp32
+ * accumulation; every fp32-valued operand that the outputs are sensitive to
+ * (U, U', the decayed q.k matrix, the state read by O, the update X) enters
+ * as a bf16 hi + lo pair, so o and s_final carry fp32-grade error.  A bf16 o
+ * adds its own rounding (up to 2^-8 of each element). */
+typedef struct {
+  int32_t batch, seqlen, n_qk, n_v, d_k, d_v;
+  int32_t dtype;    /* sgdn_dtype of q, k, v, beta, z */
+  int32_t solve;    /* sgdn_solve */
+  int32_t o_dtype;  /* sgdn_dtype of o */
+} sgdn_problem;
+
+/* Selector parameters (Sec. 2.4).  keep_budget in (0, 1]: 0.29 gives the
+ * page's tier rates (0.08, 0.30, 0.95); other budgets rescale them
+ * (b <= 0.29: rho * b / 0.29; b > 0.29: 1 - (1 - rho)(1 - b) / 0.71);
+ * 1.0 keeps every event.  tail = 16 rows for the score of Eq. (9),
+ * r_window = 16 chunks for r_h of Eq. (11) (only these values are supported).
+ * norm_weight: DEVICE [dv] fp32 RMSNorm scale used in the gate energy, or
+ * NULL for ones. */
+typedef struct {
+  float keep_budget;
+  int32_t tail;
+  int32_t r_window;
+  const float* norm_weight;
+} sgdn_sparse_params;
+
+/* Per-sequence statistics written on the device. */
+typedef struct {
+  int32_t E;            /* kept events (row_ptr[NP])                          */
+  int32_t E_max;        /* capacity 16 * k_H                                  */
+  int32_t n_tier[3];    /* head pairs per tier: [0] Low, [1] Medium, [2] High */
+  int32_t k[3];         /* events per pair in each tier: k_L, k_M, k_H        */
+  int32_t n_snapshots;  /* compact state snapshots written by the H scan      */
+} sgdn_stats;
+
+/* Optional DEVICE outputs of intermediate stages (tests and diagnostics).
+ * Any member may be NULL; pass NULL for the whole struct in production. */
+typedef struct {
+  float* g;        /* [B, Nv, C, 64]   in-chunk inclusive log2 decay          */
+  float* gamma;    /* [B, Nv, C]       chunk log2 retention                   */
+  double* prefix;  /* [B, Nv, C + 1]   P of Eqs. (19)-(20)                    */
+  float* score;    /* [B, Nv, C]       tail score of Eq. (9) (sparse)         */
+  float* eta;      /* [B, Nv]          gate energy of Eq. (11) (sparse)       */
+  float* U;        /* [B, Nv, C, 64, dv] U before the state correction (fp32) */
+  uint8_t* mask;   /* [B, NP, C]       event mask (sparse)                    */
+  uint8_t* tier;   /* [B, NP]          0 Low, 1 Medium, 2 High (sparse)       */
+} sgdn_debug;
+
+/* Bytes of device workspace a call with this problem needs (256-byte
+ * aligned sub-buffers).  sparse = 0 sizes sgdn_prefill_dense, 1 sizes
+ * sgdn_prefill_sparse and sgdn_select.  Returns 0 for an invalid problem. */
+size_t sgdn_workspace_bytes(const sgdn_problem* prob, int sparse,
+                            const sgdn_sparse_params* params);
+
+/* Dense GDN-core prefill, Sec. 2.1, Eqs. (1)-(4), with the local system of
+ * Sec. 2.3, Eqs. (5)-(6) solved exactly or by the 7-block form.
+ *   q, k    [B, T, Nq, d]   dtype
+ *   v       [B, T, Nv, dv]  dtype
+ *   a       [B, T, Nv]      fp32 log2 retention per token (<= 0)
+ *   beta    [B, T, Nv]      dtype
+ *   s0      [B, Nv, d, dv]  fp32 initial state, or NULL for zero
+ *   o       [B, T, Nv, dv]  o_dtype, output before norm / gate / projection
+ *   s_final [B, Nv, d, dv]  fp32 final state, or NULL
+ *   ws      device workspace of at least sgdn_workspace_bytes(prob, 0, NULL)
+ *   debug   optional stage outputs (may be NULL) */
+int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k,
+                       const void* v, const float* a, const void* beta,
+                       const float* s0, void* o, float* s_final, void* ws,
+                       size_t ws_bytes, void* stream, sgdn_debug* debug);
+
+/* Dynamic event selection and CSR event layout, Sec. 2.4, Eqs. (10)-(14),
+ * Sec. 2.5, Eq. (16), from the fp32 selection statistics of one batch.
+ * Requires Nv = 32 (the tier table is written for 16 head pairs) and
+ * C <= 8192.  Decisions are evaluated in binary64 in a fixed order (see the
+ * selector source), so identical inputs give identical integers.
+ *   score      [B, Nv, C]  fp32 tail scores (Eq. (9))
+ *   gamma      [B, Nv, C]  fp32 chunk log2 retentions
+ *   eta        [B, Nv]     fp32 gate energies (Eq. (11))
+ *   mask       [B, NP, C]  out: 1 = event kept
+ *   tier       [B, NP]     out: 0 Low, 1 Medium, 2 High
+ *   row_pair   [B, NP]     out: head pair of each CSR row (High, Medium, Low;
+ *                          ascending pair index within a tier)
+ *   row_ptr    [B, NP + 1] out: row offsets into col
+ *   col        [B, 16 k_H] out: kept chunk indices, ascending within a row
+ *   pred       [B, NP, G]  out: last kept event before chunk 2r, or -1
+ *   group_slot [B, NP, G]  out: snapshot slot of pred (slots number the
+ *                          distinct predecessor events in CSR order), or -1
+ *   stats      [B]         out (may be NULL) */
+int sgdn_select(const sgdn_problem* prob, const float* score, const float* gamma,
+                const float* eta, const sgdn_sparse_params* params, uint8_t* mask,
+                uint8_t* tier, int32_t* row_pair, int32_t* row_ptr, int32_t* col,
+                int32_t* pred, int32_t* group_slot, sgdn_stats* stats, void* ws,
+                size_t ws_bytes, void* stream);
+
+/* SparseGDN prefill, Secs. 2.2-2.7, Eqs. (5)-(25): local solve with fused
+ * tail score, gate energy, selector, deferred W over CSR events,
+ * event-sparse state propagation with compact snapshots, and two-chunk
+ * mapped output.  Requires Nv = 32.  Arguments as sgdn_prefill_dense, plus
+ *   z             [B, T, Nv, dv] dtype output gate (pre-activation)
+ *   mask_override [B, NP, C] uint8 event mask to use instead of the
+ *                 selector, or NULL (z may then be NULL)
+ *   stats         [B] device statistics, or NULL */
+int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k,
+                        const void* v, const float* a, const void* beta,
+                        const void* z, const sgdn_sparse_params* params,
+                        const uint8_t* mask_override, const float* s0, void* o,
+                        float* s_final, sgdn_stats* stats, void* ws,
+                        size_t ws_bytes, void* stream, sgdn_debug* debug);
+
+/* Static description of a status code. */
+const char* sgdn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGDN_H */
