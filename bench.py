@@ -1,0 +1,275 @@
+"""GDN-core prefill benchmark on one MI355X.
+
+Workload: 24 independently seeded GDN layers run back to back, bf16 inputs,
+batch 1, T = 131072, Nq = 16, Nv = 32, d = dv = 128 (value heads 2p, 2p+1
+share query/key head p), per-value-head output gate z, synthetic inputs drawn
+on the device.  One step = one pass of the 24-layer stack through the whole
+SparseGDN path at the default keep budget (29% of head-pair x chunk events):
+intra (block-adjacent solve, tail score), gate energy, selector and CSR
+layout, deferred W, event-sparse H scan with compact snapshots, grouped O.
+The dense exact path (intra, H, O) is timed the same way beside it.
+
+Prints one JSON line.  value = tokens/s of the 24-layer stack (B*T per step);
+roofline = the dominant kernel's algorithmic bytes per launch over its mean
+launch time (HIP events recorded by the library on the launch stream);
+cpu_baseline = the fp64 numpy oracle on a bounded sample (layer 0's first
+32768 tokens, all heads), in the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+B, T, NQ, NV, D = 1, 131072, 16, 32, 128
+LAYERS = 24
+STAGES = ("intra", "prefix", "gate", "select", "deferred_w", "hscan", "o")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--seqlen", type=int, default=T)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=("both", "sparse", "dense"), default="both")
+    ap.add_argument("--cpu-tokens", type=int, default=32768,
+                    help="tokens of layer 0 the oracle baseline processes")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+class Hip:
+    """Minimal HIP event API through the runtime torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreateWithFlags(ctypes.byref(e), 0) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        f = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return f.value
+
+
+def algorithmic_bytes_per_token(stage: str, mode: str, sigma: float, keep: float) -> float:
+    """Bytes per token of the I/O streams a stage must move (bf16 inputs,
+    fp32 outputs and snapshots); pipeline intermediates are not counted."""
+    k_in = NQ * D * 2           # K (shared by a head pair)
+    q_in = NQ * D * 2
+    v_in = NV * D * 2
+    o_out = NV * D * 4          # fp32 O
+    a_b = NV * 4 + NV * 2       # a (fp32) + beta (bf16)
+    snap = NV * D * D * 4 / 128  # one fp32 128x128 snapshot per head per two chunks
+    if stage == "intra":
+        return k_in + v_in + a_b
+    if stage == "hscan":
+        return k_in * (keep if mode == "sparse" else 1.0) + snap * (sigma if mode == "sparse" else 1.0)
+    if stage == "o":
+        return q_in + o_out + snap * (sigma if mode == "sparse" else 1.0)
+    return 0.0
+
+
+def source_hash(stage: str) -> str:
+    f = {"hscan": "hscan.hip", "o": "ochunk.hip", "intra": "intra.hip"}.get(stage)
+    if f is None:
+        return ""
+    p = os.path.join(ROOT, "gated_deltanet_prefill_chunkwise_amd", "csrc", f)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(stage: str, mode: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+        e = d[f"{mode}:{stage}"]
+        if e.get("source_sha256_16") != source_hash(stage):
+            return None
+        return float(e["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(inputs0, tokens=32768):
+    """The fp64 oracle (as it stands) on layer 0's first `tokens` tokens."""
+    import numpy as np
+    from oracle import sparse
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    host = {k: v[:, :tokens].float().cpu().numpy().astype(np.float64) for k, v in inputs0.items()}
+    t0 = time.perf_counter()
+    sparse.sparse_prefill(host["q"], host["k"], host["v"], host["a"], host["beta"], z=host["z"],
+                          keep_budget=0.29, solve="blockadj")
+    dt = time.perf_counter() - t0
+    return dict(value=tokens / dt / LAYERS, unit="tok/s (24-layer GDN-core stack)", cores=threads,
+                kind="oracle",
+                sample=(f"fp64 numpy oracle, SparseGDN 29% path, layer 0's first {tokens} tokens, "
+                        f"all 32 value heads, one layer timed ({dt:.1f} s) and scaled by 1/24; "
+                        f"BLAS calls use up to {threads} threads, the rest one"))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the GDN-core prefill here runs on a single MI355X "
+              "(no sharding, no collectives); --gpus N > 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_deltanet_prefill_chunkwise_amd import ops, synth
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    if args.copy_calibration:
+        # plain copy kernel of known size: 1 GiB read + 1 GiB written per launch
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_launch": src.numel() * 4,
+                          "copy_bytes_written_per_launch": dst.numel() * 4, "launches": 3}))
+        return
+    hip = Hip()
+    L, Tn = args.layers, args.seqlen
+    C = -(-Tn // 64)
+    layers = []
+    for l in range(L):
+        inp = synth.torch_inputs(synth.seed_for(3, l), B, Tn, NQ, NV, dtype="bf16", with_z=True,
+                                 device=dev)
+        o = torch.empty((B, Tn, NV, D), dtype=torch.float32, device=dev)
+        sf = torch.empty((B, NV, D, D), dtype=torch.float32, device=dev)
+        st = torch.zeros((B, ops.STATS_INTS), dtype=torch.int32, device=dev)
+        layers.append((inp, o, sf, st))
+    prob = ops.problem(layers[0][0]["q"], layers[0][0]["v"], "blockadj", torch.float32)
+    ws_bytes = max(ops.workspace_bytes(prob, True, ops.sparse_params()),
+                   ops.workspace_bytes(prob, False))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def run_mode(mode):
+        nev = len(STAGES) + 1
+        events = [[[hip.event() for _ in range(nev)] for _ in range(L)] for _ in range(args.steps)]
+        dbgs = [[ops.debug_struct(events=events[s][l]) for l in range(L)] for s in range(args.steps)]
+
+        def step(dbg_row):
+            for l, (inp, o, sf, st) in enumerate(layers):
+                dbg = dbg_row[l] if dbg_row is not None else None
+                if mode == "sparse":
+                    ops.prefill_sparse(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"],
+                                       z=inp["z"], keep_budget=0.29, solve="blockadj", o=o,
+                                       s_final=sf, stats=st, workspace=ws, debug=dbg)
+                else:
+                    ops.prefill_dense(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"],
+                                      solve="exact", o=o, s_final=sf, workspace=ws, debug=dbg)
+
+        for _ in range(args.warmup):
+            step(None)
+        torch.cuda.synchronize()
+        t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        t_start.record()
+        for s in range(args.steps):
+            step(dbgs[s])
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms = t_start.elapsed_time(t_end) / args.steps
+        stage_ms = {}
+        for i, name in enumerate(STAGES):
+            tot = sum(hip.elapsed_ms(events[s][l][i], events[s][l][i + 1])
+                      for s in range(args.steps) for l in range(L))
+            stage_ms[name] = tot / (args.steps * L)
+        stats = torch.stack([st for (_, _, _, st) in layers]).cpu()
+        return dict(ms_per_step=ms, wall_s=wall, stage_ms_per_launch=stage_ms, stats=stats)
+
+    res = {}
+    for mode in (("sparse", "dense") if args.mode == "both" else (args.mode,)):
+        res[mode] = run_mode(mode)
+        print(f"[bench] {mode}: {res[mode]['ms_per_step']:.3f} ms per {L}-layer step; stages (ms/launch) "
+              + ", ".join(f"{k} {v:.3f}" for k, v in res[mode]["stage_ms_per_launch"].items()),
+              file=sys.stderr, flush=True)
+
+    head = "sparse" if "sparse" in res else "dense"
+    r = res[head]
+    value = B * Tn / (r["ms_per_step"] / 1e3)
+
+    # keep fraction and snapshot fraction (sparse) from the device statistics
+    keep = sigma = 1.0
+    if "sparse" in res:
+        stt = res["sparse"]["stats"].float()[:, 0, :]          # [layers, 9]
+        keep = float((stt[:, 0] / (16 * C)).mean())
+        G = (C + 1) // 2
+        sigma = float((stt[:, 8] / (16 * max(G - 1, 1))).mean())
+
+    def roofline(mode):
+        st = res[mode]["stage_ms_per_launch"]
+        dom = max(st, key=st.get)
+        bpt = algorithmic_bytes_per_token(dom, mode, sigma, keep)
+        alg = bpt * B * Tn
+        achieved = alg / (st[dom] / 1e3) / 1e9
+        traffic = measured_traffic(dom, mode)
+        return dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                    algorithmic_bytes_per_launch=int(alg), launch_ms=round(st[dom], 4))
+
+    out = {
+        "metric": "GDN-core prefill tokens/s at T=32K/128K, dense vs 29% events; % roofline",
+        "value": round(value, 1),
+        "unit": "tok/s (24-layer GDN-core stack)" if args.layers == LAYERS else f"tok/s ({args.layers}-layer stack)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.layers} independently seeded GDN layers, GDN-core only, "
+                               f"{head} path" + (" (SparseGDN, keep budget 0.29, block-adjacent solve)"
+                                                 if head == "sparse" else " (exact solve)"),
+                   "batch": B, "seq_len": Tn, "n_qk_heads": NQ, "n_v_heads": NV, "d": D,
+                   "layers": args.layers, "o_dtype": "fp32", "parallelism": "none (1 GPU)"},
+        "roofline": roofline(head),
+    }
+    for mode, rr in res.items():
+        out[mode] = {"value_tok_s": round(B * Tn / (rr["ms_per_step"] / 1e3), 1),
+                     "per_layer_tok_s": round(B * Tn / (rr["ms_per_step"] / 1e3 / args.layers), 1),
+                     "ms_per_step": round(rr["ms_per_step"], 4),
+                     "stage_ms_per_launch": {k: round(v, 4) for k, v in rr["stage_ms_per_launch"].items()},
+                     "roofline": roofline(mode)}
+    if "sparse" in res:
+        out["sparse"]["measured_keep"] = round(keep, 5)
+        out["sparse"]["snapshot_fraction"] = round(sigma, 5)
+    if "sparse" in res and "dense" in res:
+        out["sparse_speedup_over_dense"] = round(res["dense"]["ms_per_step"] / res["sparse"]["ms_per_step"], 3)
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(layers[0][0], args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -127,6 +127,15 @@ template <typename T> T* at(void* ws, const Plan& p, Buf b) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + p.off[b]);
 }
 
+void mark(sgdn_debug* dbg, int i, hipStream_t s) {
+  if (dbg != nullptr && dbg->events != nullptr && i < dbg->n_events && dbg->events[i] != nullptr)
+    (void)hipEventRecord(static_cast<hipEvent_t>(dbg->events[i]), s);
+}
+
+void mark_range(sgdn_debug* dbg, int lo, int hi, hipStream_t s) {
+  for (int i = lo; i <= hi; ++i) mark(dbg, i, s);
+}
+
 #define SGDN_TRY(expr)                        \
   do {                                        \
     if ((expr) != hipSuccess) return SGDN_EHIP; \
@@ -198,7 +207,9 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   if (ws_bytes < pl.total) return SGDN_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
+  mark(dbg, SGDN_EV_START, s);
   SGDN_TRY(launch_intra(intra_args(pl, ws, k, v, a, beta, 0), pl.bf16, s));
+  mark_range(dbg, SGDN_EV_INTRA, SGDN_EV_DEFERRED, s);
   if ((st = debug_copies(pl, ws, dbg, s, 0)) != SGDN_OK) return st;
   if (s0 != nullptr) {
     S0PrepArgs sa{s0, at<float>(ws, pl, B_S0T), pl.B, pl.Nv};
@@ -210,6 +221,7 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   ha.s0 = s0; ha.s_final = s_final; ha.snap = at<float>(ws, pl, B_SNAP);
   ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 0;
   SGDN_TRY(launch_hscan(ha, pl.bf16, s));
+  mark(dbg, SGDN_EV_HSCAN, s);
   OChunkArgs oa{};
   oa.q = q; oa.k = k; oa.U = at<float>(ws, pl, B_U); oa.snap = at<float>(ws, pl, B_SNAP);
   oa.s0T = s0 ? at<float>(ws, pl, B_S0T) : nullptr;
@@ -218,6 +230,7 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
   oa.sparse = 0;
   SGDN_TRY(launch_ochunk(oa, pl.bf16, s));
+  mark(dbg, SGDN_EV_O, s);
   return SGDN_OK;
 }
 
@@ -264,9 +277,12 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   const int NP = pl.Nv / 2;
 
   // intra: local solve, U, staged Cb, tail score, gamma
+  mark(dbg, SGDN_EV_START, s);
   SGDN_TRY(launch_intra(intra_args(pl, ws, k, v, a, beta, 1), pl.bf16, s));
+  mark(dbg, SGDN_EV_INTRA, s);
   PrefixArgs pa{at<float>(ws, pl, B_GAMMA), at<double>(ws, pl, B_P), pl.B, pl.Nv, pl.C};
   SGDN_TRY(launch_prefix(pa, s));
+  mark(dbg, SGDN_EV_PREFIX, s);
   if ((st = debug_copies(pl, ws, dbg, s, 1)) != SGDN_OK) return st;
 
   // selector and event layout
@@ -274,6 +290,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
     GateArgs ga{z, params->norm_weight, at<float>(ws, pl, B_ETA), pl.B, pl.T, pl.Nv, pl.C};
     SGDN_TRY(launch_gate(ga, pl.bf16, s));
   }
+  mark(dbg, SGDN_EV_GATE, s);
   const int Emax = mask_override ? NP * pl.C : NP * pl.kH;
   SelectArgs sa{};
   sa.score = at<float>(ws, pl, B_SCORE); sa.gamma = at<float>(ws, pl, B_GAMMA);
@@ -288,6 +305,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   sa.stats = stats ? static_cast<void*>(stats) : at<void>(ws, pl, B_STATS);
   sa.mask_in = mask_override;
   SGDN_TRY(launch_select_full(sa, pl.kL, pl.kM, pl.kH, s));
+  mark(dbg, SGDN_EV_SELECT, s);
   if (dbg != nullptr) {
     if (dbg->score) SGDN_TRY(hipMemcpyAsync(dbg->score, sa.score, (size_t)pl.B * pl.Nv * pl.C * 4, hipMemcpyDeviceToDevice, s));
     if (dbg->eta && !mask_override) SGDN_TRY(hipMemcpyAsync(dbg->eta, sa.eta, (size_t)pl.B * pl.Nv * 4, hipMemcpyDeviceToDevice, s));
@@ -301,6 +319,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   da.row_pair = sa.row_pair; da.row_ptr = sa.row_ptr; da.col = sa.col;
   da.B = pl.B; da.Nv = pl.Nv; da.Nq = pl.Nq; da.C = pl.C; da.Emax = Emax; da.solve = pl.solve;
   SGDN_TRY(launch_deferred_w(da, pl.bf16, s));
+  mark(dbg, SGDN_EV_DEFERRED, s);
 
   if (s0 != nullptr) {
     S0PrepArgs s0a{s0, at<float>(ws, pl, B_S0T), pl.B, pl.Nv};
@@ -314,6 +333,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   ha.row_pair = sa.row_pair; ha.row_ptr = sa.row_ptr; ha.col = sa.col; ha.event_slot = sa.event_slot;
   ha.Emax = Emax; ha.snap_cap = pl.snap_cap;
   SGDN_TRY(launch_hscan(ha, pl.bf16, s));
+  mark(dbg, SGDN_EV_HSCAN, s);
 
   OChunkArgs oa{};
   oa.q = q; oa.k = k; oa.U = at<float>(ws, pl, B_U); oa.snap = at<float>(ws, pl, B_SNAP);
@@ -323,6 +343,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
   oa.sparse = 1; oa.pred = sa.pred; oa.group_slot = sa.group_slot; oa.snap_cap = pl.snap_cap;
   SGDN_TRY(launch_ochunk(oa, pl.bf16, s));
+  mark(dbg, SGDN_EV_O, s);
   return SGDN_OK;
 }
 

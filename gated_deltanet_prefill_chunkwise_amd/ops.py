@@ -36,7 +36,11 @@ class Stats(ctypes.Structure):
 
 class Debug(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("g", "gamma", "prefix", "score", "eta", "U", "mask", "tier")]
+                ("g", "gamma", "prefix", "score", "eta", "U", "mask", "tier")] + \
+               [("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int32)]
+
+
+EV_NAMES = ("start", "intra", "prefix", "gate", "select", "deferred_w", "hscan", "o")
 
 
 STATS_INTS = ctypes.sizeof(Stats) // 4
@@ -131,8 +135,15 @@ def _workspace(nbytes, device, workspace):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def debug_struct(**bufs) -> Debug:
-    return Debug(*[None if bufs.get(n) is None else bufs[n].data_ptr() for n, _ in Debug._fields_])
+def debug_struct(events=None, **bufs) -> Debug:
+    """Debug outputs (torch tensors by field name) and optional hipEvent_t handles."""
+    d = Debug(*[None if bufs.get(n) is None else bufs[n].data_ptr() for n, _ in Debug._fields_[:8]])
+    if events is not None:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        d.events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        d.n_events = len(events)
+        d._keep = arr
+    return d
 
 
 def prefill_dense(q, k, v, a, beta, s0=None, solve="exact", want_state=True, o=None,

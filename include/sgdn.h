@@ -99,7 +99,25 @@ typedef struct {
   float* U;        /* [B, Nv, C, 64, dv] U before the state correction (fp32) */
   uint8_t* mask;   /* [B, NP, C]       event mask (sparse)                    */
   uint8_t* tier;   /* [B, NP]          0 Low, 1 Medium, 2 High (sparse)       */
+  /* Stage timing: caller-created hipEvent_t handles, recorded on the stream
+   * at the stage boundaries SGDN_EV_*; events[i] is used when i < n_events.
+   * Stages a call does not run leave adjacent events at the same point. */
+  void** events;
+  int32_t n_events;
 } sgdn_debug;
+
+/* Stage boundaries recorded into sgdn_debug.events. */
+enum {
+  SGDN_EV_START = 0,     /* before the first kernel                       */
+  SGDN_EV_INTRA = 1,     /* after the intra-chunk kernel                  */
+  SGDN_EV_PREFIX = 2,    /* after the log-decay prefix (sparse)           */
+  SGDN_EV_GATE = 3,      /* after the gate energy (sparse)                */
+  SGDN_EV_SELECT = 4,    /* after selector + CSR layout (sparse)          */
+  SGDN_EV_DEFERRED = 5,  /* after deferred W (sparse)                     */
+  SGDN_EV_HSCAN = 6,     /* after the H scan                              */
+  SGDN_EV_O = 7,         /* after the O kernel                            */
+  SGDN_EV_COUNT = 8
+};
 
 /* Bytes of device workspace a call with this problem needs (256-byte
  * aligned sub-buffers).  sparse = 0 sizes sgdn_prefill_dense, 1 sizes
