@@ -141,4 +141,15 @@ __device__ __forceinline__ V16 zv() { V16 v; v.w[0] = v.w[1] = v.w[2] = v.w[3] =
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also releases
+// global memory, which on gfx9 waits for every outstanding vector-memory
+// operation (loads included), draining software-prefetched loads; kernels
+// whose global writes are not read back by other waves in the same launch use
+// this instead.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace sgdn

@@ -57,6 +57,18 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraArgs p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) sKT[(c8 + j) * TS + r] = val[j];
   }
+  // ---- V tiles of both heads are fetched after the key tile (registers; loads retire in
+  //      order) so their latency overlaps the Gram matrix and the solve
+  frag_t<E> vpre[2][4];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int q = tid + 256 * it;
+      const int r = q >> 4, c8 = (q & 15) * 8, t = t0 + r;
+      vpre[hh][it] = t < T ? ld8(V + ((size_t)(b * T + t) * Nv + 2 * pq + hh) * DV + c8) : zero_frag<E>();
+    }
+
   if (tid < 128) {
     const int hh = tid >> 6, t = t0 + lane, h = 2 * pq + hh;
     float av = 0.f, bv = 0.f;
@@ -171,10 +183,11 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraArgs p) {
       sCC[t * TS + s] = hi;
       if constexpr (kSplit) sCL[t * TS + s] = from_f<E>(ct - to_f(hi));
     }
-    for (int q = tid; q < L * 16; q += 256) {
-      const int r = q >> 4, c8 = (q & 15) * 8, t = t0 + r;
-      frag_t<E> val = zero_frag<E>();
-      if (t < T) val = ld8(V + ((size_t)(b * T + t) * Nv + h) * DV + c8);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int q = tid + 256 * it;
+      const int r = q >> 4, c8 = (q & 15) * 8;
+      const frag_t<E> val = vpre[hh][it];
 #pragma unroll
       for (int j = 0; j < 8; ++j) sKV[(c8 + j) * TS + r] = val[j];
     }

@@ -71,15 +71,43 @@ __global__ __launch_bounds__(512) void ochunk_kernel(OChunkArgs p) {
       Ssrc = p.s0T + bh * DV * DK;
   }
 
-  // ---- stage Q rows of the group and G
+  // ---- global loads of both phases are issued up front so that their
+  //      latencies overlap (one workgroup holds the CU's LDS); the Q rows to
+  //      stage go first, because loads retire in order
   const E* Qin = static_cast<const E*>(p.q);
   const E* Kin = static_cast<const E*>(p.k);
-  for (int q = tid; q < 2 * L * 16; q += 512) {
+  frag_t<E> qst[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int q = tid + 512 * it;
     const int rr = q >> 4, c8 = (q & 15) * 8;
     const int t = c0 * L + rr;
-    frag_t<E> val = zero_frag<E>();
-    if (rr < ntile * 16 && t < T) val = ld8(Qin + ((size_t)(b * T + t) * Nq + pr) * DK + c8);
-    *reinterpret_cast<frag_t<E>*>(&sQ[rr * QSTR + c8]) = val;
+    qst[it] = (rr < ntile * 16 && t < T) ? ld8(Qin + ((size_t)(b * T + t) * Nq + pr) * DK + c8)
+                                         : zero_frag<E>();
+  }
+  frag_t<E> kf[4];
+  {
+    const int ts = c0 * L + 16 * w + n16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kf[ks] = (w < ntile && ts < T) ? ld8(Kin + ((size_t)(b * T + ts) * Nq + pr) * DK + 32 * ks + 8 * g4)
+                                     : zero_frag<E>();
+  }
+  const int dvr = 16 * w + n16;
+  f32x8 sfr[4], ufr[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    sfr[ks] = Ssrc != nullptr ? ld8f(Ssrc + (size_t)dvr * DK + 32 * ks + 8 * g4) : f32x8{};
+    ufr[ks] = (2 * ks < ntile) ? ld8f(p.U + ((bh * C + c0 + (ks >> 1)) * DV + dvr) * L + 32 * (ks & 1) + 8 * g4)
+                               : f32x8{};
+  }
+
+  // ---- stage Q rows of the group and G
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int q = tid + 512 * it;
+    const int rr = q >> 4, c8 = (q & 15) * 8;
+    *reinterpret_cast<frag_t<E>*>(&sQ[rr * QSTR + c8]) = qst[it];
   }
   if (tid < 128) {
     const int cc = tid >> 6;
@@ -95,13 +123,6 @@ __global__ __launch_bounds__(512) void ochunk_kernel(OChunkArgs p) {
 
   // ---- phase 1: A^T blocks of source tile w (s in 16w..16w+15)
   if (w < ntile) {
-    frag_t<E> kf[4];
-    const int s_row = 16 * w + n16;
-    const int ts = c0 * L + s_row;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      kf[ks] = ts < T ? ld8(Kin + ((size_t)(b * T + ts) * Nq + pr) * DK + 32 * ks + 8 * g4)
-                      : zero_frag<E>();
     float gs[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) gs[j] = sG[16 * w + 4 * g4 + j];
@@ -141,12 +162,10 @@ __global__ __launch_bounds__(512) void ochunk_kernel(OChunkArgs p) {
   f32x4 acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = zero4();
-  const int dvr = 16 * w + n16;
   if (Ssrc != nullptr) {
-    const float* Srow = Ssrc + (size_t)dvr * DK;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const f32x8 sf = ld8f(Srow + 32 * ks + 8 * g4);
+      const f32x8 sf = sfr[ks];
       frag_t<E> sh, sl;
       if constexpr (kSplit) split8(sf, sh, sl); else sh = sf;
 #pragma unroll
@@ -166,10 +185,10 @@ __global__ __launch_bounds__(512) void ochunk_kernel(OChunkArgs p) {
     }
   }
   // local terms: U'^T A^T, source 32-blocks ks (chunk c0 + ks / 2)
+#pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     if (2 * ks >= ntile) break;
-    const float* Urow = p.U + ((bh * C + c0 + (ks >> 1)) * DV + dvr) * L + 32 * (ks & 1) + 8 * g4;
-    const f32x8 uf = ld8f(Urow);
+    const f32x8 uf = ufr[ks];
     frag_t<E> uh, ul;
     if constexpr (kSplit) split8(uf, uh, ul); else uh = uf;
 #pragma unroll
