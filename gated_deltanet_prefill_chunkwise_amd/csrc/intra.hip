@@ -7,8 +7,19 @@
 // system, block-adjacent inverse, weighted coefficients), Sec. 2.4 Eq. (9)
 // (tail score from the fp32 U while it is on chip).
 //
-// One workgroup (4 waves) per (chunk, head pair, batch): the pair shares its
-// key tile and Gram matrix; the two value heads are solved one after the other.
+// Persistent kernel: each workgroup (4 waves) walks over (chunk, head pair,
+// batch) items and loads the next item's keys, values and gates into registers
+// while it works on the current one.  The pair shares its key tile and Gram
+// matrix; the two value heads are solved one after the other.
+//
+// Solve of the unit lower triangular 64x64 system (I + M) C = I in 16x16
+// blocks: each wave inverts one diagonal block by forward substitution, then
+// the off-diagonal blocks follow from fp32 matrix-core products (block
+// adjacent: C_i,i-1 = -C_ii M_i,i-1 C_i-1,i-1 only; exact: the same for the
+// two 32x32 halves, then the lower-left 32x32 block -C_hi M_hl C_lo).
+//
+// Key and value tiles stay row-major (token x feature) in LDS; products that
+// contract over tokens read them with the gfx950 transposing LDS load.
 #include "common.h"
 #include "kernels.h"
 
@@ -16,262 +27,440 @@ namespace sgdn {
 
 namespace {
 
-constexpr int PAD = 8;
-constexpr int KRS = DK + PAD;  // row stride of the row-major key tile
-constexpr int TS = L + PAD;    // row stride of token-minor tiles (K^T, V^T, C)
+constexpr int KS = DK + 8;      // row stride (elements) of the key / value tiles
+constexpr int TP = 20;          // column stride (floats) of a stored 16x16 fp32 tile
+constexpr int TILE = 16 * TP;   // floats per stored tile
+constexpr int NT = 11;          // 10 lower-triangle blocks + one all-zero block
+constexpr int ZT = 10;
 
-// 16x16 blocks of the 64x64 lower triangle that the Gram matrix must fill.
-__constant__ int kGramExact[10][2] = {{0, 0}, {1, 1}, {2, 2}, {3, 3}, {1, 0},
-                                      {2, 1}, {3, 2}, {2, 0}, {3, 1}, {3, 0}};
+// Slot of block (i, j) of the 4x4 block grid: the lower triangle, zero above
+// it, and (block-adjacent solve) zero below the first sub-diagonal.
+__device__ __forceinline__ int slot(int i, int j, bool ba) {
+  if (j > i || (ba && i - j > 1)) return ZT;
+  return i * (i + 1) / 2 + j;
+}
+
+// Gram block ti: the diagonal (0..3), the first sub-diagonal (4..6), then
+// (2,0), (3,1), (3,0).
+__device__ __forceinline__ void gram_block(int ti, int& bi, int& bj) {
+  if (ti < 4) { bi = ti; bj = ti; }
+  else if (ti < 7) { bi = ti - 3; bj = ti - 4; }
+  else if (ti < 9) { bi = ti - 5; bj = ti - 7; }
+  else { bi = 3; bj = 0; }
+}
+
+// Stored tiles are column-major: element (r, c) at c * TP + r.
+// D += A B for two stored 16x16 fp32 tiles (v_mfma_f32_16x16x4_f32: lane l
+// gives A[l%16][k] and B[k][l%16] with k = l/16 of the 4-wide step).
+__device__ __forceinline__ f32x4 tile_mma(const float* A, const float* B, f32x4 d, int lane) {
+  const int n = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int k = 4 * kb + q;
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(A[k * TP + n], B[n * TP + k], d, 0, 0, 0);
+  }
+  return d;
+}
+// Store a D tile (lane holds rows 4q..4q+3 of column n).
+__device__ __forceinline__ void tile_st(float* T, f32x4 d, int lane) {
+  *reinterpret_cast<f32x4*>(T + (lane & 15) * TP + 4 * (lane >> 4)) = d;
+}
+
+// Fragment of a row-major tile read along its rows: lane (n, g) receives
+// base[(8g + e) * ld + n], e = 0..7, i.e. the B fragment of a product that
+// contracts over the tile's rows (or the A fragment of the transposed tile).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ bf16x8 ld_tr8(const bf16* base, int ld, int lane) {
+  // ds_read_b64_tr_b16: in each 16-lane group, lane m points at 4 elements
+  // (row m/4, columns 4(m%4)..+3) of a 4x16 block; lane n then holds column
+  // n, rows 0..3.  Two such reads give rows 8g..8g+3 and 8g+4..8g+7.
+  const int m = lane & 15, g = lane >> 4;
+  const bf16* p0 = base + (8 * g + (m >> 2)) * ld + 4 * (m & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 4 * ld));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ f32x8 ld_tr8(const float* base, int ld, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  f32x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = base[(8 * g + e) * ld + n];
+  return f;
+}
+
+// Coefficient fragments of one k-step: C~ = C diag(beta) (hi + lo halves for
+// bf16 operands) and Cb = C diag(beta 2^g).
+template <typename E> struct CoefFrag { frag_t<E> hi, lo, cb; };
 
 template <typename E>
-__global__ __launch_bounds__(256) void intra_kernel(IntraArgs p) {
-  constexpr int KV_ELEMS = (L * KRS > DV * TS) ? L * KRS : DV * TS;
-  __shared__ __align__(32) E sKV[KV_ELEMS];   // key tile row-major, later V^T
-  __shared__ __align__(32) E sKT[DK * TS];    // key tile transposed [dk][t]
-  __shared__ __align__(32) E sCC[L * TS];     // weighted coefficients [t][s]
-  constexpr bool kSplit = sizeof(E) == 2;     // bf16: coefficients as hi + lo
-  __shared__ __align__(32) E sCL[kSplit ? L * TS : 8];
-  __shared__ float sG[L][L + 1];              // Gram <k_t, k_s>
-  __shared__ float sM[L][L + 1];              // strictly lower part of M
-  __shared__ float sC[L][L + 1];              // C ~ M^{-1}
-  __shared__ float sY[3][16][17];
-  __shared__ float sg[2][L], sb[2][L];
+__device__ __forceinline__ CoefFrag<E> coef_frag(const float* sCt, const float* sb, const float* sbe,
+                                                 int w, int ks, bool ba, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  const int jt = 2 * ks + (g >> 1), co = 8 * (g & 1), s0 = 16 * jt + co;
+  const float* T = sCt + slot(w, jt, ba) * TILE + co * TP + n;
+  const f32x8 b8 = ld8f(sb + s0), be8 = ld8f(sbe + s0);
+  CoefFrag<E> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float c = T[e * TP];
+    const float ct = c * b8[e];
+    const E h = from_f<E>(ct);
+    f.hi[e] = h;
+    f.lo[e] = from_f<E>(ct - to_f(h));
+    f.cb[e] = from_f<E>(c * be8[e]);
+  }
+  return f;
+}
 
-  const int c = blockIdx.x, pq = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int n16 = lane & 15, g4 = lane >> 4;
+template <typename E, bool BA, bool SPARSE>
+__global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
+  __shared__ __align__(16) E sK[L * KS];      // key tile, row-major [t][dk]
+  __shared__ __align__(16) E sV[L * KS];      // value tile of the current head [t][dv]
+  __shared__ __align__(16) float sMt[NT * TILE];
+  __shared__ __align__(16) float sCt[NT * TILE];
+  __shared__ __align__(16) float sYt[4 * TILE];
+  __shared__ __align__(32) float sg[2][L], sb[2][L], sbe[2][L];
+
+  // thread index; made opaque again at every item (see the loop head)
+  int tid = threadIdx.x;
+  const int w_uniform = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = p.T, Nq = p.Nq, Nv = p.Nv, C = p.C;
-  const int t0 = c * L;
-  const bool blockadj = p.solve == 1;
+  const int n_items = p.B * C * Nq;
   const E* K = static_cast<const E*>(p.k);
   const E* V = static_cast<const E*>(p.v);
   const E* BETA = static_cast<const E*>(p.beta);
+  constexpr int NGRAM = BA ? 7 : 10;
 
-  // ---- key tile: row-major and transposed copies; a and beta of both heads
-  for (int q = tid; q < L * 16; q += 256) {
-    const int r = q >> 4, c8 = (q & 15) * 8, t = t0 + r;
-    frag_t<E> val = zero_frag<E>();
-    if (t < T) val = ld8(K + ((size_t)(b * T + t) * Nq + pq) * DK + c8);
-    *reinterpret_cast<frag_t<E>*>(&sKV[r * KRS + c8]) = val;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sKT[(c8 + j) * TS + r] = val[j];
-  }
-  // ---- V tiles of both heads are fetched after the key tile (registers; loads retire in
-  //      order) so their latency overlaps the Gram matrix and the solve
-  frag_t<E> vpre[2][4];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
+  for (int q = tid; q < TILE; q += 256) sCt[ZT * TILE + q] = 0.f;
+
+  // ---- operand registers of the item being staged (loaded one item ahead)
+  frag_t<E> kreg[4], v0reg[4], v1reg[4];
+  float areg = 0.f, breg = 0.f;
+  auto load_kv = [&](int item, frag_t<E>* kr, frag_t<E>* vr, int hh, bool with_k) {
+    const int pq = item % Nq, c = (item / Nq) % C, b = item / (Nq * C);
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int q = tid + 256 * it;
-      const int r = q >> 4, c8 = (q & 15) * 8, t = t0 + r;
-      vpre[hh][it] = t < T ? ld8(V + ((size_t)(b * T + t) * Nv + 2 * pq + hh) * DV + c8) : zero_frag<E>();
+      const int q = tid + 256 * it, r = q >> 4, c8 = (q & 15) * 8;
+      const int t = min(c * L + r, T - 1);
+      if (with_k) kr[it] = ld8(K + ((size_t)(b * T + t) * Nq + pq) * DK + c8);
+      vr[it] = ld8(V + ((size_t)(b * T + t) * Nv + 2 * pq + hh) * DV + c8);
     }
-
-  if (tid < 128) {
-    const int hh = tid >> 6, t = t0 + lane, h = 2 * pq + hh;
-    float av = 0.f, bv = 0.f;
-    if (t < T) {
-      av = p.a[(size_t)(b * T + t) * Nv + h];
-      bv = to_f(BETA[(size_t)(b * T + t) * Nv + h]);
-    }
-    // inclusive prefix over the chunk (g, Sec. 2.1)
-    float x = av;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(x, off, 64);
-      if (lane >= off) x += y;
-    }
-    sg[hh][lane] = x;
-    sb[hh][lane] = bv;
-    const size_t hc = (size_t)(b * Nv + h) * C + c;
-    p.g[hc * L + lane] = x;
-    if (lane == 63) p.gamma[hc] = x;
-  }
-  __syncthreads();
-
-  // ---- Gram matrix of the pair's keys (fp32 accumulation of bf16 products)
-  {
-    const int ntiles = blockadj ? 7 : 10;
-    for (int ti = w; ti < ntiles; ti += 4) {
-      const int bi = kGramExact[ti][0], bj = kGramExact[ti][1];
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const frag_t<E> fa = ld8(&sKV[(16 * bi + n16) * KRS + 32 * ks + 8 * g4]);
-        const frag_t<E> fb = ld8(&sKV[(16 * bj + n16) * KRS + 32 * ks + 8 * g4]);
-        acc = mma(fa, fb, acc);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sG[16 * bi + 4 * g4 + j][16 * bj + n16] = acc[j];
-    }
-  }
-  // transposed key tile for the H and deferred-W stages
-  {
-    E* kt = static_cast<E*>(p.KT) + ((size_t)(b * Nq + pq) * C + c) * DK * L;
-    for (int q = tid; q < DK * 8; q += 256) {
-      const int r = q >> 3, c8 = (q & 7) * 8;
-      *reinterpret_cast<frag_t<E>*>(kt + r * L + c8) = ld8(&sKT[r * TS + c8]);
-    }
-  }
-  __syncthreads();
-
-  for (int hh = 0; hh < 2; ++hh) {
-    const int h = 2 * pq + hh;
-    const size_t hc = (size_t)(b * Nv + h) * C + c;
-    // ---- M: beta_t <k_t,k_s> 2^(g_t - g_s) for s < t (Eq. (5)); C cleared
-    for (int idx = tid; idx < L * L; idx += 256) {
-      const int t = idx >> 6, s = idx & 63;
-      const int bt = t >> 4, bs = s >> 4;
-      float m = 0.f;
-      if (s < t && (!blockadj || bt - bs <= 1))
-        m = sb[hh][t] * sG[t][s] * exp2f(sg[hh][t] - sg[hh][s]);
-      sM[t][s] = m;
-      sC[t][s] = 0.f;
-    }
-    __syncthreads();
-    // ---- diagonal blocks: C_ii = M_ii^{-1} by forward substitution, one
-    //      column per thread (Eq. (8))
-    if (tid < 64) {
-      const int blk = tid >> 4, j = tid & 15, o = 16 * blk;
-      float x[16];
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        float sum = (t == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int s = 0; s < t; ++s) sum -= sM[o + t][o + s] * x[s];
-        x[t] = sum;
-      }
-#pragma unroll
-      for (int t = 0; t < 16; ++t) sC[o + t][o + j] = x[t];
-    }
-    __syncthreads();
-    // ---- off-diagonal blocks, by distance d = i - j:
-    //      C_ij = -C_ii sum_{k=j}^{i-1} M_ik C_kj.  Block-adjacent keeps d = 1
-    //      only (C_i,i-1 = -C_ii M_i,i-1 C_i-1,i-1, Eq. (8)); exact adds d = 2, 3.
-    const int dmax = blockadj ? 1 : 3;
-    for (int d = 1; d <= dmax; ++d) {
-      const int nb = 4 - d;
-      const int r = tid >> 4, cc = tid & 15;
-      for (int m = 0; m < nb; ++m) {
-        const int i = d + m, j = i - d;
-        float y = 0.f;
-        for (int kb = j; kb < i; ++kb) {
-#pragma unroll
-          for (int u = 0; u < 16; ++u) y += sM[16 * i + r][16 * kb + u] * sC[16 * kb + u][16 * j + cc];
-        }
-        sY[m][r][cc] = y;
-      }
-      __syncthreads();
-      for (int m = 0; m < nb; ++m) {
-        const int i = d + m, j = i - d;
-        float x = 0.f;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) x -= sC[16 * i + r][16 * i + u] * sY[m][u][cc];
-        sC[16 * i + r][16 * j + cc] = x;
-      }
-      __syncthreads();
-    }
-
-    // ---- U = C diag(beta) V  (Ct = C diag(beta)), and the tail score.
-    //      Ct is applied as hi + lo halves so U keeps fp32 accuracy.
-    for (int idx = tid; idx < L * L; idx += 256) {
-      const int t = idx >> 6, s = idx & 63;
-      const float ct = sC[t][s] * sb[hh][s];
-      const E hi = from_f<E>(ct);
-      sCC[t * TS + s] = hi;
-      if constexpr (kSplit) sCL[t * TS + s] = from_f<E>(ct - to_f(hi));
-    }
+  };
+  auto load_ab = [&](int item) {
+    const int pq = item % Nq, c = (item / Nq) % C, b = item / (Nq * C);
+    const int hh = (tid >> 6) & 1, t = min(c * L + (tid & 63), T - 1);
+    const size_t idx = (size_t)(b * T + t) * Nv + 2 * pq + hh;
+    areg = p.a[idx];
+    breg = to_f(BETA[idx]);
+  };
+  // rows past the sequence end are zero
+  auto mask_rows = [&](int item, frag_t<E>* r) {
+    const int c = (item / Nq) % C;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int q = tid + 256 * it;
-      const int r = q >> 4, c8 = (q & 15) * 8;
-      const frag_t<E> val = vpre[hh][it];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sKV[(c8 + j) * TS + r] = val[j];
+      const int row = (tid + 256 * it) >> 4;
+      if (c * L + row >= T) r[it] = zero_frag<E>();
     }
-    __syncthreads();
+  };
+
+  int item = blockIdx.x;
+  if (item < n_items) {
+    load_kv(item, kreg, v0reg, 0, true);
+    load_ab(item);
+    load_kv(item, kreg, v1reg, 1, false);
+  }
+
+  for (; item < n_items; item += gridDim.x) {
+    // wave and thread index as opaque values per item, so that the addresses
+    // derived from them are formed where they are used instead of being kept
+    // in registers across the whole loop
+    int w = w_uniform;
+    asm volatile("" : "+s"(w), "+v"(tid));
+    const int lane = tid & 63, n16 = lane & 15, g4 = lane >> 4;
+    const int pq = item % Nq, c = (item / Nq) % C, b = item / (Nq * C);
+    const int t0 = c * L;
+    const int next = min(item + (int)gridDim.x, n_items - 1);
+    lds_barrier();  // the previous item's readers of sK, sV, sg are done
+
+    // ---- stage keys and the first head's values; decay prefix of both heads
+    mask_rows(item, kreg);
+    mask_rows(item, v0reg);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int q = tid + 256 * it, r = q >> 4, c8 = (q & 15) * 8;
+      *reinterpret_cast<frag_t<E>*>(&sK[r * KS + c8]) = kreg[it];
+      *reinterpret_cast<frag_t<E>*>(&sV[r * KS + c8]) = v0reg[it];
+    }
+    if (tid < 128) {
+      const int hh = tid >> 6, h = 2 * pq + hh;
+      const bool live = t0 + lane < T;
+      float x = live ? areg : 0.f;
+      const float bv = live ? breg : 0.f;
+      // inclusive prefix over the chunk (g, Sec. 2.1)
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      sg[hh][lane] = x;
+      sb[hh][lane] = bv;
+      sbe[hh][lane] = bv * exp2f(x);
+      const size_t hc = (size_t)(b * Nv + h) * C + c;
+      p.g[hc * L + lane] = x;
+      if (lane == 63) p.gamma[hc] = x;
+    }
+    lds_barrier();
+    // next item's keys, first-head values and gates (registers are free now)
+    load_kv(next, kreg, v0reg, 0, true);
+    load_ab(next);
+
+    // ---- transposed key tile for the H and deferred-W stages
     {
-      // k-steps over s with non-zero coefficients for token tile w
-      const int ks_lo = (blockadj && w == 3) ? 1 : 0;
-      const int ks_hi = (w >= 2) ? 1 : 0;
-      f32x4 acc[8];
+      E* kt = static_cast<E*>(p.KT) + ((size_t)(b * Nq + pq) * C + c) * DK * L;
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) acc[nt] = zero4();
-      for (int ks = ks_lo; ks <= ks_hi; ++ks) {
-        const frag_t<E> fa = ld8(&sCC[(16 * w + n16) * TS + 32 * ks + 8 * g4]);
-        frag_t<E> fl;
-        if constexpr (kSplit) fl = ld8(&sCL[(16 * w + n16) * TS + 32 * ks + 8 * g4]);
+      for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const frag_t<E> fb = ld8(&sKV[(16 * nt + n16) * TS + 32 * ks + 8 * g4]);
-          acc[nt] = mma(fa, fb, acc[nt]);
-          if constexpr (kSplit) acc[nt] = mma(fl, fb, acc[nt]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const int mt = 2 * w + mi;
+          const frag_t<E> f = ld_tr8(&sK[32 * ks * KS + 16 * mt], KS, lane);
+          *reinterpret_cast<frag_t<E>*>(kt + (16 * mt + n16) * L + 32 * ks + 8 * g4) = f;
+        }
+    }
+
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int h = 2 * pq + hh;
+      const size_t hc = (size_t)(b * Nv + h) * C + c;
+      // ---- M = beta_t <k_t, k_s> 2^(g_t - g_s), s < t (Eq. (5)), stored
+      //      blockwise; the Gram blocks of the pair's keys are recomputed per
+      //      head (cheaper than keeping them in registers)
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        const int ti = w + 4 * r;
+        if (ti < NGRAM) {
+          int bi, bj;
+          gram_block(ti, bi, bj);
+          f32x4 gram = zero4();
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const frag_t<E> fa = ld8(&sK[(16 * bi + n16) * KS + 32 * ks + 8 * g4]);
+            const frag_t<E> fb = ld8(&sK[(16 * bj + n16) * KS + 32 * ks + 8 * g4]);
+            gram = mma(fa, fb, gram);
+          }
+          const int s = 16 * bj + n16;
+          const float gs = sg[hh][s];
+          f32x4 m;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = 16 * bi + 4 * g4 + j;
+            const float v = sb[hh][t] * gram[j] * exp2f(sg[hh][t] - gs);
+            m[j] = (s < t) ? v : 0.f;
+          }
+          tile_st(sMt + slot(bi, bj, false) * TILE, m, lane);
         }
       }
-      float* U = p.U + hc * DV * L;
+      lds_barrier();
+      if (hh == 1) {
+        // the first head's products are done: second head's values in, and
+        // the next item's second-head values requested
+        mask_rows(item, v1reg);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) st4f(U + (16 * nt + n16) * L + 16 * w + 4 * g4, acc[nt]);
-      if (p.score != nullptr && w == 3) {
-        // Eq. (9): Frobenius norm of U rows 48..63, from the fp32 accumulators
+        for (int it = 0; it < 4; ++it) {
+          const int q = tid + 256 * it, r = q >> 4, c8 = (q & 15) * 8;
+          *reinterpret_cast<frag_t<E>*>(&sV[r * KS + c8]) = v1reg[it];
+        }
+        load_kv(next, kreg, v1reg, 1, false);
+      }
+      // ---- diagonal blocks: C_ii = (I + M_ii)^{-1}, wave w takes block w,
+      //      lane j column j, forward substitution (Eq. (8))
+      {
+        const float* Mw = sMt + slot(w, w, false) * TILE;
+        const int j = n16;
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) x[t] = (t == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int s = 0; s < 15; ++s) {
+          const float* col = Mw + s * TP;  // M[.][s]
+#pragma unroll
+          for (int t = s + 1; t < 16; ++t) x[t] -= col[t] * x[s];
+        }
+        if (lane < 16) {
+          float* Cw = sCt + slot(w, w, false) * TILE + j * TP;
+#pragma unroll
+          for (int t = 0; t < 16; t += 4) *reinterpret_cast<f32x4*>(Cw + t) = f32x4{x[t], x[t + 1], x[t + 2], x[t + 3]};
+        }
+      }
+      lds_barrier();
+      // ---- first sub-diagonal: C_i,i-1 = -C_ii M_i,i-1 C_i-1,i-1
+      //      (block-adjacent: i = 1, 2, 3; exact: i = 1, 3, the 32x32 halves)
+      {
+        const int i = BA ? w + 1 : 2 * w + 1;
+        if (BA ? (w < 3) : (w < 2)) {
+          const f32x4 y = tile_mma(sMt + slot(i, i - 1, false) * TILE,
+                                   sCt + slot(i - 1, i - 1, false) * TILE, zero4(), lane);
+          tile_st(sYt + w * TILE, y, lane);
+          const f32x4 z = tile_mma(sCt + slot(i, i, false) * TILE, sYt + w * TILE, zero4(), lane);
+          tile_st(sCt + slot(i, i - 1, false) * TILE, -z, lane);
+        }
+      }
+      lds_barrier();
+      if constexpr (!BA) {
+        // ---- lower-left 32x32 block: Y = M_hl C_lo, then -C_hi Y
+        {
+          const float* Mt_ = sMt;
+          const float* Ct_ = sCt;
+          f32x4 y = zero4();
+          if (w == 0) {         // Y20 = M20 C00 + M21 C10
+            y = tile_mma(Mt_ + slot(2, 0, false) * TILE, Ct_ + slot(0, 0, false) * TILE, y, lane);
+            y = tile_mma(Mt_ + slot(2, 1, false) * TILE, Ct_ + slot(1, 0, false) * TILE, y, lane);
+          } else if (w == 1) {  // Y30 = M30 C00 + M31 C10
+            y = tile_mma(Mt_ + slot(3, 0, false) * TILE, Ct_ + slot(0, 0, false) * TILE, y, lane);
+            y = tile_mma(Mt_ + slot(3, 1, false) * TILE, Ct_ + slot(1, 0, false) * TILE, y, lane);
+          } else if (w == 2) {  // Y21 = M21 C11
+            y = tile_mma(Mt_ + slot(2, 1, false) * TILE, Ct_ + slot(1, 1, false) * TILE, y, lane);
+          } else {              // Y31 = M31 C11
+            y = tile_mma(Mt_ + slot(3, 1, false) * TILE, Ct_ + slot(1, 1, false) * TILE, y, lane);
+          }
+          tile_st(sYt + w * TILE, y, lane);
+        }
+        lds_barrier();
+        {
+          // Y tiles: 0 = Y20, 1 = Y30, 2 = Y21, 3 = Y31
+          f32x4 z = zero4();
+          int dst;
+          if (w == 0) {         // C20 = -C22 Y20
+            z = tile_mma(sCt + slot(2, 2, false) * TILE, sYt + 0 * TILE, z, lane);
+            dst = slot(2, 0, false);
+          } else if (w == 1) {  // C30 = -(C32 Y20 + C33 Y30)
+            z = tile_mma(sCt + slot(3, 2, false) * TILE, sYt + 0 * TILE, z, lane);
+            z = tile_mma(sCt + slot(3, 3, false) * TILE, sYt + 1 * TILE, z, lane);
+            dst = slot(3, 0, false);
+          } else if (w == 2) {  // C21 = -C22 Y21
+            z = tile_mma(sCt + slot(2, 2, false) * TILE, sYt + 2 * TILE, z, lane);
+            dst = slot(2, 1, false);
+          } else {              // C31 = -(C32 Y21 + C33 Y31)
+            z = tile_mma(sCt + slot(3, 2, false) * TILE, sYt + 2 * TILE, z, lane);
+            z = tile_mma(sCt + slot(3, 3, false) * TILE, sYt + 3 * TILE, z, lane);
+            dst = slot(3, 1, false);
+          }
+          tile_st(sCt + dst * TILE, -z, lane);
+        }
+        lds_barrier();
+      }
+
+      // ---- U = C diag(beta) V for token tile w (Eq. (6)), the tail score,
+      //      and Cb = C diag(beta 2^g) (Eq. (7)): W^T = K^T Cb^T (dense) or
+      //      Cb itself (sparse, for the deferred W of kept events)
+      const int ks_lo = (BA && w == 3) ? 1 : 0;
+      const int ks_hi = (w >= 2) ? 1 : 0;
+      CoefFrag<E> cf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (ks >= ks_lo && ks <= ks_hi) {
+          cf[ks] = coef_frag<E>(sCt, sb[hh], sbe[hh], w, ks, BA, lane);
+        } else {
+          cf[ks].hi = cf[ks].lo = cf[ks].cb = zero_frag<E>();
+        }
+      }
+      {
+        // two halves of 64 value columns each, to bound the live fragments
+        float* U = p.U + hc * DV * L;
         float ss = 0.f;
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
+        for (int half = 0; half < 2; ++half) {
+          f32x4 acc[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) ss += acc[nt][j] * acc[nt][j];
+          for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-        if (lane == 0) p.score[hc] = sqrtf(ss);
-      }
-    }
-    __syncthreads();
-
-    // ---- Cb = C diag(beta 2^g): W (dense) or staged for deferred W (sparse)
-    for (int idx = tid; idx < L * L; idx += 256) {
-      const int t = idx >> 6, s = idx & 63;
-      sCC[t * TS + s] = from_f<E>(sC[t][s] * sb[hh][s] * exp2f(sg[hh][s]));
-    }
-    __syncthreads();
-    if (p.W != nullptr) {
-      // W^T = K^T Cb^T: rows dk, columns t (so W is stored token-major)
-      const int ks_lo = (blockadj && w == 3) ? 1 : 0;
-      const int ks_hi = (w >= 2) ? 1 : 0;
-      f32x4 acc[8];
+          for (int ks = 0; ks < 2; ++ks) {
+            if (ks >= ks_lo && ks <= ks_hi) {
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
-      for (int ks = ks_lo; ks <= ks_hi; ++ks) {
-        const frag_t<E> fb = ld8(&sCC[(16 * w + n16) * TS + 32 * ks + 8 * g4]);
+              for (int nt = 0; nt < 4; ++nt) {
+                const frag_t<E> fb = ld_tr8(&sV[32 * ks * KS + 16 * (4 * half + nt)], KS, lane);
+                acc[nt] = mma(cf[ks].hi, fb, acc[nt]);
+                if constexpr (sizeof(E) == 2) acc[nt] = mma(cf[ks].lo, fb, acc[nt]);
+              }
+            }
+          }
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          const frag_t<E> fa = ld8(&sKT[(16 * mt + n16) * TS + 32 * ks + 8 * g4]);
-          acc[mt] = mma(fa, fb, acc[mt]);
+          for (int nt = 0; nt < 4; ++nt) {
+            st4f(U + (16 * (4 * half + nt) + n16) * L + 16 * w + 4 * g4, acc[nt]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ss += acc[nt][j] * acc[nt][j];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (SPARSE) {
+          // Eq. (9): Frobenius norm of U rows 48..63, from the fp32 accumulators
+#pragma unroll
+          for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+          if (w == 3 && lane == 0) p.score[hc] = sqrtf(ss);
         }
       }
-      E* W = static_cast<E*>(p.W) + hc * L * DK;
+      // keep the U and W products apart (their accumulators would otherwise
+      // be live at the same time)
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (SPARSE) {
+        E* cb = static_cast<E*>(p.Cb) + hc * L * L;
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) st4(W + (16 * w + n16) * DK + 16 * mt + 4 * g4, acc[mt]);
-    }
-    if (p.Cb != nullptr) {
-      E* cb = static_cast<E*>(p.Cb) + hc * L * L;
-      for (int q = tid; q < L * 8; q += 256) {
-        const int r = q >> 3, c8 = (q & 7) * 8;
-        *reinterpret_cast<frag_t<E>*>(cb + r * L + c8) = ld8(&sCC[r * TS + c8]);
+        for (int ks = 0; ks < 2; ++ks)
+          *reinterpret_cast<frag_t<E>*>(cb + (16 * w + n16) * L + 32 * ks + 8 * g4) = cf[ks].cb;
+      } else {
+        // W^T = K^T Cb^T: rows dk, columns t (W is stored token-major)
+        E* W = static_cast<E*>(p.W) + hc * L * DK;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          f32x4 acc[4];
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) acc[mt] = zero4();
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            if (ks >= ks_lo && ks <= ks_hi) {
+#pragma unroll
+              for (int mt = 0; mt < 4; ++mt) {
+                const frag_t<E> fa = ld_tr8(&sK[32 * ks * KS + 16 * (4 * half + mt)], KS, lane);
+                acc[mt] = mma(fa, cf[ks].cb, acc[mt]);
+              }
+            }
+          }
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) st4(W + (16 * w + n16) * DK + 16 * (4 * half + mt) + 4 * g4, acc[mt]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-    __syncthreads();
   }
+}
+
+template <typename E, bool BA, bool SPARSE>
+hipError_t launch_one(const IntraArgs& a, hipStream_t s) {
+  const auto fn = intra_kernel<E, BA, SPARSE>;
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0);
+  if (e != hipSuccess) return e;
+  const long long items = (long long)a.B * a.C * a.Nq;
+  const long long slots = (long long)cus * (per_cu > 0 ? per_cu : 1);
+  const int grid = (int)(items < slots ? items : slots);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_intra(const IntraArgs& a, int bf16, hipStream_t s) {
-  dim3 grid(a.C, a.Nq, a.B);
-  if (bf16)
-    hipLaunchKernelGGL(intra_kernel<sgdn::bf16>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(intra_kernel<float>, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  const bool ba = a.solve == 1, sparse = a.Cb != nullptr;
+  if (bf16) {
+    if (ba) return sparse ? launch_one<sgdn::bf16, true, true>(a, s) : launch_one<sgdn::bf16, true, false>(a, s);
+    return sparse ? launch_one<sgdn::bf16, false, true>(a, s) : launch_one<sgdn::bf16, false, false>(a, s);
+  }
+  if (ba) return sparse ? launch_one<float, true, true>(a, s) : launch_one<float, true, false>(a, s);
+  return sparse ? launch_one<float, false, true>(a, s) : launch_one<float, false, false>(a, s);
 }
 
 }  // namespace sgdn
