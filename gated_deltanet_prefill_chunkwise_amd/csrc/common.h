@@ -128,6 +128,12 @@ __device__ __forceinline__ f32x4 mma_split_b(const f32x8& a, const f32x8& b, f32
   return mma(a, b, acc);
 }
 
+// Fragment-major chunk tiles (W, KT): 16 blocks of 512 elements, one MFMA
+// operand fragment per block, lane-major; see the workspace notes.
+constexpr int FRAG = 512;
+__device__ __forceinline__ int wblk(int q, int i) { return (q * 4 + i) * FRAG; }
+__device__ __forceinline__ int kblk(int mt, int ks) { return (mt * 2 + ks) * FRAG; }
+
 // Output element type (o may be fp32 or bf16 independently of the inputs).
 template <typename O> __device__ __forceinline__ void st4o(O* p, f32x4 v);
 template <> __device__ __forceinline__ void st4o<float>(float* p, f32x4 v) { st4f(p, v); }

@@ -9,15 +9,19 @@
 // Value columns of S evolve independently (both equations act column-wise),
 // so one workgroup owns one 16-column slice of one head's 128x128 state and
 // walks that head's events in time.  Four waves split each step:
-//   W S    : wave w computes token rows 16w..16w+15 of U' (A = W from global,
-//            B = S from LDS, 4 k-steps over d)
-//   K^T X  : wave w updates state rows 32w..32w+31 (A = K^T tile from global,
-//            B = X = U' * 2^(gamma - g) from LDS, 2 k-steps over tokens)
+//   W S    : wave w computes token rows 16w..16w+15 of U' (A = W blocks,
+//            B = S from its LDS copy, 4 k-steps over d)
+//   K^T X  : wave w updates state rows 32w..32w+31 (A = K^T blocks, B = X from
+//            LDS, 2 k-steps over tokens)
+// W and K^T are fragment-major in memory (one contiguous 1 KB read per
+// operand fragment) in a permuted reduction order; the LDS operands S and X
+// are read in the same order.  The operands of an event do not depend on the
+// state, so they are requested DEPTH events ahead into a ring of registers.
 // The fp32 state stays in registers; a bf16 (or fp32) copy in LDS is the
 // operand of the next step's W S (a single bf16 rounding there costs < 0.3% of
-// the output RMS).  U, U' and X are fp32; X enters K^T X as bf16 hi + lo
-// halves, and snapshots are stored in fp32, because single bf16 roundings of
-// these move the outputs by 1-4% of their RMS.
+// the output RMS).  U, U' and X are fp32; X is stored as bf16 hi + lo halves
+// for K^T X, and snapshots are fp32, because single bf16 roundings of these
+// move the outputs by 1-4% of their RMS.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,19 +32,33 @@ namespace {
 constexpr int PAD = 8;
 constexpr int SSTR = DK + PAD;  // LDS state copy [16 dv][dk]
 constexpr int XSTR = L + PAD;   // LDS X [16 dv][64 tokens]
+constexpr int EVT = 240;        // events per LDS metadata tile
 
-constexpr int EVT = 256;         // sparse: events per LDS metadata tile
+// 2^x for x <= 0 on the hardware exponential (results below 2^-126 flush to
+// zero, far below the fp32 terms they are added to).
+__device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename E, bool SPARSE>
-__global__ __launch_bounds__(256) void hscan_kernel(HScanArgs p) {
-  __shared__ __align__(32) E sS[16 * SSTR];
-  __shared__ __align__(32) float sX[16 * XSTR];
-  // sparse event metadata of the current tile: chunk, snapshot slot, gap factor
-  __shared__ int sEvC[SPARSE ? EVT + 1 : 1];
+__global__ __launch_bounds__(256, 1) void hscan_kernel(HScanArgs p) {
+  // events whose operands are in flight: 10 loads per event and wave, so the
+  // ring plus the stores stays below the 63 vector-memory operations a wave
+  // can count (fp32 fragments are twice as large: a shorter ring)
+  constexpr int DEPTH = sizeof(E) == 2 ? 4 : 2;
+  static_assert(EVT % DEPTH == 0, "buffer ring must align with the tiles");
+  constexpr bool kSplit = sizeof(E) == 2;
+  __shared__ __align__(16) E sS[16 * SSTR];
+  __shared__ __align__(16) E sXh[16 * XSTR];
+  __shared__ __align__(16) E sXl[kSplit ? 16 * XSTR : 8];
+  // event metadata of the current tile: chunk retention gamma; sparse also
+  // chunk, snapshot slot and gap factor (chunk indices also for the DEPTH
+  // events past the tile)
+  __shared__ float sEvGam[EVT];
+  __shared__ int sEvC[SPARSE ? EVT + DEPTH : 1];
   __shared__ int sEvSlot[SPARSE ? EVT : 1];
   __shared__ float sEvF[SPARSE ? EVT : 1];
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g4 = lane >> 4;
   const int Nv = p.Nv, C = p.C, B = p.B;
   const int NP = Nv / 2;
@@ -75,29 +93,35 @@ __global__ __launch_bounds__(256) void hscan_kernel(HScanArgs p) {
   const size_t bh = (size_t)b * Nv + h;
   const double* P = SPARSE ? p.P + bh * (C + 1) : nullptr;
 
-  // Stage the metadata of events [t0, t0 + EVT): chunk index, snapshot slot
-  // and the gap factor 2^(P_next - P_{c+1}) that carries S_{c+1} to the next
-  // event (Eq. (21)); the last event carries it to the end of the sequence.
-  auto stage_meta = [&](int t0) {
-    if constexpr (SPARSE) {
-      for (int e = tid; e <= EVT; e += 256) {
-        const int i = t0 + e;
-        if (i < i1) {
-          const int c = colb[i];
-          sEvC[e] = c;
-          if (e < EVT) {
+  // Stage the metadata of events [t0, t0 + EVT): gamma, and (sparse) chunk
+  // index, snapshot slot and the gap factor 2^(P_next - P_{c+1}) that carries
+  // S_{c+1} to the next event (Eq. (21)); the last event carries it to the end
+  // of the sequence.  Chunk indices are staged DEPTH events further for the
+  // operand requests.  Read from LDS, the per-event scalars stay out of the
+  // vector-memory wait counts.
+  auto stage_meta = [&](int t0) __attribute__((always_inline)) {
+    for (int e = tid; e < EVT + DEPTH; e += 256) {
+      const int i = t0 + e;
+      if (i < i1) {
+        const int c = SPARSE ? colb[i] : i;
+        if (SPARSE) sEvC[e] = c;
+        if (e < EVT) {
+          sEvGam[e] = p.gamma[bh * C + c];
+          if (SPARSE) {
             sEvSlot[e] = slotb[i];
             const int cn = (i + 1 < i1) ? colb[i + 1] : C;
             sEvF[e] = exp2f((float)(P[cn] - P[c + 1]));
           }
         }
       }
-      __syncthreads();
     }
+    __syncthreads();
   };
-  auto chunk_at = [&](int i, int t0) { return SPARSE ? sEvC[i - t0] : i; };
+  int t0 = i0;
+  auto chunk_at = [&](int i) __attribute__((always_inline)) { return SPARSE ? sEvC[i - t0] : i; };
 
-  // ---- initial state: s0 decayed over the chunks before the first event
+  // ---- initial state rows 32w + 16tt + 4g + j of column dv0 + n: s0 decayed
+  //      over the chunks before the first event
   f32x4 S[2];
   {
     float f0 = 1.f;
@@ -111,91 +135,106 @@ __global__ __launch_bounds__(256) void hscan_kernel(HScanArgs p) {
       }
       st4(&sS[n16 * SSTR + 32 * w + 16 * tt + 4 * g4], S[tt]);
     }
+    // the initial state is complete before any operand request, so the loop
+    // never waits on these loads
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  int t0 = i0;
   stage_meta(t0);
-  __syncthreads();
 
   const E* Wbase = static_cast<const E*>(p.W);
   const E* KTbase = static_cast<const E*>(p.KT);
   float* Ubase = p.U;
   float* snap = p.snap;
 
-  // Operands of one event, loaded one event ahead so that the global-memory
-  // latency of event i+1 overlaps the matrix work of event i.
+  // Operands of one event for this wave.
   struct Ops {
-    frag_t<E> wf[4], kf[2][2];
-    f32x4 u, gv;
-    float gam;
+    frag_t<E> wf[4];      // W blocks (dk step q, token tile w)
+    frag_t<E> kf[2][2];   // K^T blocks (dk tile 2w + tt, token step ks)
+    f32x4 u, gv;          // U and g of tokens 16w + 4g .. 16w + 4g + 3
     int c;
   };
-  auto load = [&](int i, int c, Ops& o) {
+  auto load = [&](int i, int c, Ops& o) __attribute__((always_inline)) {
     const size_t hc = bh * C + c;
     const E* Wt = SPARSE ? Wbase + (((size_t)b * p.Emax + i) * 2 + hh) * L * DK
                          : Wbase + hc * L * DK;
     const E* KTt = KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) o.wf[ks] = ld8(Wt + (16 * w + n16) * DK + 32 * ks + 8 * g4);
+    for (int q = 0; q < 4; ++q) o.wf[q] = ld8(Wt + wblk(q, w) + 8 * lane);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) o.kf[tt][ks] = ld8(KTt + (32 * w + 16 * tt + n16) * L + 32 * ks + 8 * g4);
+      for (int ks = 0; ks < 2; ++ks) o.kf[tt][ks] = ld8(KTt + kblk(2 * w + tt, ks) + 8 * lane);
     o.u = *reinterpret_cast<const f32x4*>(Ubase + hc * DV * L + (dv0 + n16) * L + 16 * w + 4 * g4);
     o.gv = *reinterpret_cast<const f32x4*>(p.g + hc * L + 16 * w + 4 * g4);
-    o.gam = p.gamma[hc];
     o.c = c;
   };
+  // Request event i's operands (past the last event: the last event again,
+  // unconditionally, so that no branch merges the wait counts into a drain).
+  // sEvC holds EVT + DEPTH entries, so i - t0 < EVT + DEPTH is always staged.
+  auto request = [&](int i, Ops& o) __attribute__((always_inline)) {
+    const int in = i < i1 ? i : i1 - 1;
+    load(in, chunk_at(in), o);
+  };
 
-  // One event step; `cur` holds this event's operands, `nxt` receives the
-  // next event's.  The loop alternates two buffers (no register copies, so
-  // the wait for `nxt` lands at its first use one step later).
-  auto step = [&](int i, Ops& cur, Ops& nxt) {
-    if constexpr (SPARSE) {
-      // event i opens the next metadata tile; the barrier that ended the
-      // previous step guarantees nobody still reads the old tile
-      if (i - t0 == EVT) {
-        t0 += EVT;
-        stage_meta(t0);
-      }
-    }
-    const bool more = i + 1 < i1;
+  // One event step on the operands in `cur`; ends by requesting event
+  // i + DEPTH into the same buffer.
+  auto step = [&](int i, Ops& cur) __attribute__((always_inline)) {
     const int c = cur.c;
     const size_t hc = bh * C + c;
-    float* Ut = Ubase + hc * DV * L + (dv0 + n16) * L + 16 * w + 4 * g4;
+    const float gam = sEvGam[i - t0];
 
-    // ---- U' = U - W S   (Eq. (1))
+    // ---- U' = U - W S   (Eq. (1)); S read in the blocks' permuted order
     f32x4 acc = zero4();
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc = mma(cur.wf[ks], ld8(&sS[n16 * SSTR + 32 * ks + 8 * g4]), acc);
-    // next event's operands are requested only after this event's are in use,
-    // so waiting for `cur` never waits for `nxt` (loads retire in order).  The
-    // request is unconditional (the last event re-reads its own operands): a
-    // branch here would make the wait counts merge to a full drain.
-    // sEvC holds EVT + 1 entries, so i + 1 - t0 <= EVT is always staged.
-    {
-      const int in = more ? i + 1 : i;
-      load(in, chunk_at(in, t0), nxt);
+    for (int q = 0; q < 4; ++q) {
+      const E* sr = &sS[n16 * SSTR + 32 * q + 4 * g4];
+      acc = mma(cur.wf[q], ld44(sr, sr + 16), acc);
     }
     f32x4 up, x;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       up[j] = cur.u[j] - acc[j];
-      x[j] = up[j] * exp2f(cur.gam - cur.gv[j]);
+      x[j] = up[j] * exp2_neg(gam - cur.gv[j]);
     }
-    st4f(Ut, up);
-    st4f(&sX[n16 * XSTR + 16 * w + 4 * g4], x);
+    st4f(Ubase + hc * DV * L + (dv0 + n16) * L + 16 * w + 4 * g4, up);
+    {
+      E* xh = &sXh[n16 * XSTR + 16 * w + 4 * g4];
+      if constexpr (kSplit) {
+        half_t<E> hi, lo;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          hi[j] = from_f<E>(x[j]);
+          lo[j] = from_f<E>(x[j] - to_f(hi[j]));
+        }
+        *reinterpret_cast<half_t<E>*>(xh) = hi;
+        *reinterpret_cast<half_t<E>*>(&sXl[n16 * XSTR + 16 * w + 4 * g4]) = lo;
+      } else {
+        st4(xh, x);
+      }
+    }
     lds_barrier();
 
-    // ---- S <- 2^gamma S + K^T (U' * 2^(gamma - g))   (Eq. (2))
-    const float dec = exp2f(cur.gam);
+    // ---- S <- 2^gamma S + K^T (U' * 2^(gamma - g))   (Eq. (2)); X read in
+    //      the K^T blocks' permuted token order
+    const float dec = exp2_neg(gam);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      f32x4 d = zero4();
+      f32x4 d = S[tt] * dec;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) d = mma_split_b(cur.kf[tt][ks], ld8f(&sX[n16 * XSTR + 32 * ks + 8 * g4]), d);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) S[tt][j] = dec * S[tt][j] + d[j];
+      for (int ks = 0; ks < 2; ++ks) {
+        const E* xr = &sXh[n16 * XSTR + 32 * ks + 4 * g4];
+        d = mma(cur.kf[tt][ks], ld44(xr, xr + 16), d);
+        if constexpr (kSplit) {
+          const E* lr = &sXl[n16 * XSTR + 32 * ks + 4 * g4];
+          d = mma(cur.kf[tt][ks], ld44(lr, lr + 16), d);
+        }
+      }
+      S[tt] = d;
     }
+    // the request reuses cur's registers: keep it after their last use, so the
+    // buffers stay in place (a copy of an in-flight register forces a drain)
+    __builtin_amdgcn_sched_barrier(0);
+    request(i + DEPTH, cur);
 
     // ---- compact snapshot of S_{c+1} if an output group starts from it
     float* sp = nullptr;
@@ -214,20 +253,48 @@ __global__ __launch_bounds__(256) void hscan_kernel(HScanArgs p) {
     if constexpr (SPARSE) {
       const float f = sEvF[i - t0];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[tt][j] *= f;
+      for (int tt = 0; tt < 2; ++tt) S[tt] *= f;
     }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) st4(&sS[n16 * SSTR + 32 * w + 16 * tt + 4 * g4], S[tt]);
     lds_barrier();
   };
 
-  Ops bufA, bufB;
-  if (i0 < i1) load(i0, chunk_at(i0, t0), bufA);
-  for (int i = i0; i < i1; i += 2) {
-    step(i, bufA, bufB);
-    if (i + 1 < i1) step(i + 1, bufB, bufA);
+  Ops buf[DEPTH];
+  if (i0 < i1) {
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) request(i0 + k, buf[k]);
+  }
+  // One metadata tile of EVT events per outer pass (EVT is a multiple of
+  // DEPTH, so event i0 + k + n DEPTH always sits in buffer k).  The next tile
+  // is staged at the end of a pass (the barrier that ends every step
+  // guarantees nobody still reads the old one).  Only the last tile can end in
+  // a partial group, so the way back to the event loop never follows
+  // remainder steps (whose requests would look like the newest loads to the
+  // wait-count analysis).
+  auto run = [&](int ts, int te, bool last) __attribute__((always_inline)) {
+    // whole groups of DEPTH events: straight-line steps, no guards
+    int i = ts;
+    for (; i + DEPTH <= te; i += DEPTH) {
+#pragma unroll
+      for (int k = 0; k < DEPTH; ++k) step(i + k, buf[k]);
+    }
+    if (last) {
+      // the remaining 0 .. DEPTH-1 events; only the last tile has any
+#pragma unroll
+      for (int k = 0; k < DEPTH - 1; ++k)
+        if (i + k < te) step(i + k, buf[k]);
+    }
+  };
+  // (one call site: a second copy of the event loop would get its own
+  // register assignment and copies of in-flight buffers)
+  for (int ts = i0; ts < i1;) {
+    const int te = (i1 - ts < EVT) ? i1 : ts + EVT;
+    const bool last = te >= i1;
+    run(ts, te, last);
+    if (last) break;
+    t0 = ts = te;
+    stage_meta(t0);
   }
 
   if (p.s_final != nullptr) {
@@ -241,22 +308,18 @@ __global__ __launch_bounds__(256) void hscan_kernel(HScanArgs p) {
   }
 }
 
+template <typename E, bool SPARSE>
+hipError_t launch_one(const HScanArgs& a, hipStream_t s) {
+  const int nblk = a.B * (a.Nv / 2) * 16;
+  hipLaunchKernelGGL((hscan_kernel<E, SPARSE>), dim3(nblk), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_hscan(const HScanArgs& a, int bf16, hipStream_t s) {
-  const int nblk = a.B * (a.Nv / 2) * 16;
-  if (bf16) {
-    if (a.sparse)
-      hipLaunchKernelGGL((hscan_kernel<sgdn::bf16, true>), dim3(nblk), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((hscan_kernel<sgdn::bf16, false>), dim3(nblk), dim3(256), 0, s, a);
-  } else {
-    if (a.sparse)
-      hipLaunchKernelGGL((hscan_kernel<float, true>), dim3(nblk), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((hscan_kernel<float, false>), dim3(nblk), dim3(256), 0, s, a);
-  }
-  return hipGetLastError();
+  if (bf16) return a.sparse ? launch_one<sgdn::bf16, true>(a, s) : launch_one<sgdn::bf16, false>(a, s);
+  return a.sparse ? launch_one<float, true>(a, s) : launch_one<float, false>(a, s);
 }
 
 }  // namespace sgdn

@@ -90,6 +90,24 @@ __device__ __forceinline__ f32x8 ld_tr8(const float* base, int ld, int lane) {
   for (int e = 0; e < 8; ++e) f[e] = base[(8 * g + e) * ld + n];
   return f;
 }
+// The same in the permuted reduction order of the fragment-major tiles: lane
+// (n, g) receives rows 4g .. 4g+3 and 16+4g .. 16+4g+3 of column n.
+__device__ __forceinline__ bf16x8 ld_tr44(const bf16* base, int ld, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+  const bf16* p0 = base + (4 * g + (m >> 2)) * ld + 4 * (m & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * ld));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ f32x8 ld_tr44(const float* base, int ld, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  f32x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = base[((e < 4) ? 4 * g + e : 16 + 4 * g + e - 4) * ld + n];
+  return f;
+}
 
 // Coefficient fragments of one k-step: C~ = C diag(beta) (hi + lo halves for
 // bf16 operands) and Cb = C diag(beta 2^g).
@@ -217,7 +235,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     load_kv(next, kreg, v0reg, 0, true);
     load_ab(next);
 
-    // ---- transposed key tile for the H and deferred-W stages
+    // ---- fragment-major key tile (K^T operand blocks) for the H and
+    //      deferred-W stages
     {
       E* kt = static_cast<E*>(p.KT) + ((size_t)(b * Nq + pq) * C + c) * DK * L;
 #pragma unroll
@@ -225,8 +244,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int mt = 2 * w + mi;
-          const frag_t<E> f = ld_tr8(&sK[32 * ks * KS + 16 * mt], KS, lane);
-          *reinterpret_cast<frag_t<E>*>(kt + (16 * mt + n16) * L + 32 * ks + 8 * g4) = f;
+          const frag_t<E> f = ld_tr44(&sK[32 * ks * KS + 16 * mt], KS, lane);
+          *reinterpret_cast<frag_t<E>*>(kt + kblk(mt, ks) + 8 * lane) = f;
         }
     }
 
@@ -410,7 +429,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
         for (int ks = 0; ks < 2; ++ks)
           *reinterpret_cast<frag_t<E>*>(cb + (16 * w + n16) * L + 32 * ks + 8 * g4) = cf[ks].cb;
       } else {
-        // W^T = K^T Cb^T: rows dk, columns t (W is stored token-major)
+        // W^T = K^T Cb^T: rows dk, columns t
         E* W = static_cast<E*>(p.W) + hc * L * DK;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -427,8 +446,11 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
               }
             }
           }
+          // two stacked W^T tiles form one fragment-major W block
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) st4(W + (16 * w + n16) * DK + 16 * (4 * half + mt) + 4 * g4, acc[mt]);
+          for (int qq = 0; qq < 2; ++qq)
+            *reinterpret_cast<frag_t<E>*>(W + wblk(2 * half + qq, w) + 8 * lane) =
+                pack44<E>(acc[2 * qq], acc[2 * qq + 1]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }

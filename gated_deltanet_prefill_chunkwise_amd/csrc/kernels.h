@@ -12,11 +12,20 @@ namespace sgdn {
 //   gamma  [B][Nv][C]          fp32  chunk retention g[63]
 //   P      [B][Nv][C+1]        fp64  prefix of gamma
 //   U      [B][Nv][C][dv][64]  fp32  U (then U' in place), dv-major tiles
-//   W      [B][Nv][C][64][dk]  E     dense W, token-major tiles
+//   W      [B][Nv][C][8192]    E     dense W tiles, fragment-major (below)
 //   Cb     [B][Nv][C][64][64]  E     staged C diag(beta 2^g), row-major
-//   KT     [B][Nq][C][dk][64]  E     transposed key tiles
+//   KT     [B][Nq][C][8192]    E     key tiles, fragment-major (below)
 //   snap   [..][dv][dk]        fp32  compact state snapshots (transposed)
-//   Wpk    [B][Emax][2][64][dk] E    deferred W of kept events
+//   Wpk    [B][Emax][2][8192]  E     deferred W of kept events, fragment-major
+//
+// Fragment-major tiles: 16 blocks of 512 elements, block = one 64-lane MFMA
+// operand fragment (lane l = 16 g + n holds 8 consecutive elements), so a wave
+// reads one block as one contiguous 1 KB (bf16) request.  Both tiles use the
+// permuted reduction order  r(g, e) = 4g + e (e < 4),  16 + 4g + e - 4 (e >= 4)
+// within each 32-wide step, the order in which two stacked accumulator tiles
+// hold their rows (so results feed the next product from registers):
+//   W  block 4q + i  (dk step q, token tile i):  W[16i + n][32q + r(g, e)]
+//   KT block 2mt + ks (dk tile mt, token step ks): K[32ks + r(g, e)][16mt + n]
 
 struct IntraArgs {
   const void* k; const void* v; const float* a; const void* beta;

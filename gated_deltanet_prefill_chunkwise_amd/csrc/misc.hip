@@ -92,18 +92,22 @@ __global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
   for (int hh = 0; hh < 2; ++hh) {
     const int h = 2 * pr + hh;
     const E* Cb = static_cast<const E*>(p.Cb) + (((size_t)b * p.Nv + h) * p.C + c) * L * L;
+    // W^T = K^T Cb^T (rows dk, columns t).  K^T blocks are fragment-major in
+    // the permuted token order, so Cb is read in the same order.
     f32x4 acc[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
     for (int ks = ks_lo; ks <= ks_hi; ++ks) {
-      const frag_t<E> fb = ld8(Cb + (16 * w + n16) * L + 32 * ks + 8 * g4);
+      const E* cr = Cb + (16 * w + n16) * L + 32 * ks + 4 * g4;
+      const frag_t<E> fb = ld44(cr, cr + 16);
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-        acc[mt] = mma(ld8(KT + (16 * mt + n16) * L + 32 * ks + 8 * g4), fb, acc[mt]);
+      for (int mt = 0; mt < 8; ++mt) acc[mt] = mma(ld8(KT + kblk(mt, ks) + 8 * lane), fb, acc[mt]);
     }
+    // two stacked W^T tiles form one fragment-major W block
     E* W = static_cast<E*>(p.Wpk) + (((size_t)b * p.Emax + i) * 2 + hh) * L * DK;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) st4(W + (16 * w + n16) * DK + 16 * mt + 4 * g4, acc[mt]);
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<frag_t<E>*>(W + wblk(q, w) + 8 * lane) = pack44<E>(acc[2 * q], acc[2 * q + 1]);
   }
 }
 
