@@ -15,7 +15,7 @@ using namespace sgdn;
 constexpr int NP_SPARSE = 16;
 
 struct Plan {
-  int B, T, Nq, Nv, C, G, esz, bf16, solve;
+  int B, T, Nq, Nv, C, G, esz, isz, bf16, solve;
   int kL, kM, kH;
   int Emax;        // event capacity per sequence inside prefill_sparse
   int snap_cap;    // snapshot slots per sequence (sparse) or per head (dense)
@@ -79,27 +79,28 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
   p.B = pr->batch; p.T = pr->seqlen; p.Nq = pr->n_qk; p.Nv = pr->n_v;
   p.C = (p.T + 63) / 64; p.G = (p.C + 1) / 2;
   p.bf16 = pr->dtype == SGDN_BF16; p.esz = p.bf16 ? 2 : 4; p.solve = pr->solve;
+  p.isz = p.bf16 ? 2 : 4;   // intermediates: fp16 for bf16 inputs, fp32 for fp32 inputs
   int k[3] = {p.C, p.C, p.C};
   if (sparse) tier_counts(p.C, budget_bp(sp->keep_budget), k);
   p.kL = k[0]; p.kM = k[1]; p.kH = k[2];
   const int NP = p.Nv / 2;
   p.Emax = NP * p.C;
   p.snap_cap = sparse ? NP * (p.G > 1 ? p.G - 1 : 1) : (p.G > 1 ? p.G - 1 : 1);
-  const size_t B = p.B, Nv = p.Nv, C = p.C, G = p.G, E = p.esz;
+  const size_t B = p.B, Nv = p.Nv, C = p.C, G = p.G, I = p.isz;
   size_t sz[B_COUNT];
   memset(sz, 0, sizeof(sz));
   sz[B_G] = B * Nv * C * L * 4;
   sz[B_GAMMA] = B * Nv * C * 4;
   sz[B_P] = B * Nv * (C + 1) * 8;
-  sz[B_U] = B * Nv * C * L * DV * 4;
-  sz[B_KT] = B * p.Nq * C * DK * L * E;
-  sz[B_S0T] = B * Nv * DV * DK * 4;
+  sz[B_U] = B * Nv * C * L * DV * I;
+  sz[B_KT] = B * p.Nq * C * DK * L * I;
+  sz[B_S0T] = B * Nv * DV * DK * I;
   if (!sparse) {
-    sz[B_W] = B * Nv * C * L * DK * E;
-    sz[B_SNAP] = B * Nv * (size_t)p.snap_cap * DV * DK * 4;
+    sz[B_W] = B * Nv * C * L * DK * I;
+    sz[B_SNAP] = B * Nv * (size_t)p.snap_cap * DV * DK * I;
   } else {
-    sz[B_CB] = B * Nv * C * L * L * E;
-    sz[B_SNAP] = B * (size_t)p.snap_cap * 2 * DV * DK * 4;
+    sz[B_CB] = B * Nv * C * L * L * I;
+    sz[B_SNAP] = B * (size_t)p.snap_cap * 2 * DV * DK * I;
     sz[B_SCORE] = B * Nv * C * 4;
     sz[B_ETA] = B * Nv * 4;
     sz[B_RANK] = B * NP * C * 4;
@@ -112,7 +113,7 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
     sz[B_PRED] = B * NP * G * 4;
     sz[B_GSLOT] = B * NP * G * 4;
     sz[B_ESLOT] = B * (size_t)p.Emax * 4;
-    sz[B_WPK] = B * (size_t)p.Emax * 2 * L * DK * E;
+    sz[B_WPK] = B * (size_t)p.Emax * 2 * L * DK * I;
     sz[B_STATS] = B * 9 * 4;
   }
   size_t o = 0;
@@ -148,7 +149,7 @@ IntraArgs intra_args(const Plan& pl, void* ws, const void* k, const void* v, con
   ia.B = pl.B; ia.T = pl.T; ia.Nq = pl.Nq; ia.Nv = pl.Nv; ia.C = pl.C; ia.solve = pl.solve;
   ia.g = at<float>(ws, pl, B_G);
   ia.gamma = at<float>(ws, pl, B_GAMMA);
-  ia.U = at<float>(ws, pl, B_U);
+  ia.U = at<void>(ws, pl, B_U);
   ia.W = sparse ? nullptr : at<void>(ws, pl, B_W);
   ia.Cb = sparse ? at<void>(ws, pl, B_CB) : nullptr;
   ia.KT = at<void>(ws, pl, B_KT);
@@ -169,7 +170,8 @@ int debug_copies(const Plan& pl, void* ws, sgdn_debug* dbg, hipStream_t st, int 
     SGDN_TRY(hipMemcpyAsync(dbg->prefix, at<void>(ws, pl, B_P), (size_t)pl.B * pl.Nv * (pl.C + 1) * 8,
                             hipMemcpyDeviceToDevice, st));
   }
-  if (dbg->U) SGDN_TRY(launch_debug_u(at<float>(ws, pl, B_U), static_cast<float*>(dbg->U), pl.B, pl.Nv, pl.C, st));
+  if (dbg->U)
+    SGDN_TRY(launch_debug_u(at<void>(ws, pl, B_U), static_cast<float*>(dbg->U), pl.B, pl.Nv, pl.C, pl.bf16, st));
   return SGDN_OK;
 }
 
@@ -212,19 +214,19 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   mark_range(dbg, SGDN_EV_INTRA, SGDN_EV_DEFERRED, s);
   if ((st = debug_copies(pl, ws, dbg, s, 0)) != SGDN_OK) return st;
   if (s0 != nullptr) {
-    S0PrepArgs sa{s0, at<float>(ws, pl, B_S0T), pl.B, pl.Nv};
-    SGDN_TRY(launch_s0prep(sa, s));
+    S0PrepArgs sa{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv};
+    SGDN_TRY(launch_s0prep(sa, pl.bf16, s));
   }
   HScanArgs ha{};
-  ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, B_W); ha.U = at<float>(ws, pl, B_U);
+  ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, B_W); ha.U = at<void>(ws, pl, B_U);
   ha.g = at<float>(ws, pl, B_G); ha.gamma = at<float>(ws, pl, B_GAMMA); ha.P = nullptr;
-  ha.s0 = s0; ha.s_final = s_final; ha.snap = at<float>(ws, pl, B_SNAP);
+  ha.s0 = s0; ha.s_final = s_final; ha.snap = at<void>(ws, pl, B_SNAP);
   ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 0;
   SGDN_TRY(launch_hscan(ha, pl.bf16, s));
   mark(dbg, SGDN_EV_HSCAN, s);
   OChunkArgs oa{};
-  oa.q = q; oa.k = k; oa.U = at<float>(ws, pl, B_U); oa.snap = at<float>(ws, pl, B_SNAP);
-  oa.s0T = s0 ? at<float>(ws, pl, B_S0T) : nullptr;
+  oa.q = q; oa.k = k; oa.U = at<void>(ws, pl, B_U); oa.snap = at<void>(ws, pl, B_SNAP);
+  oa.s0T = s0 ? at<void>(ws, pl, B_S0T) : nullptr;
   oa.o_bf16 = prob->o_dtype == SGDN_BF16;
   oa.g = at<float>(ws, pl, B_G); oa.gamma = at<float>(ws, pl, B_GAMMA); oa.P = nullptr;
   oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
@@ -322,13 +324,13 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   mark(dbg, SGDN_EV_DEFERRED, s);
 
   if (s0 != nullptr) {
-    S0PrepArgs s0a{s0, at<float>(ws, pl, B_S0T), pl.B, pl.Nv};
-    SGDN_TRY(launch_s0prep(s0a, s));
+    S0PrepArgs s0a{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv};
+    SGDN_TRY(launch_s0prep(s0a, pl.bf16, s));
   }
   HScanArgs ha{};
-  ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, B_WPK); ha.U = at<float>(ws, pl, B_U);
+  ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, B_WPK); ha.U = at<void>(ws, pl, B_U);
   ha.g = at<float>(ws, pl, B_G); ha.gamma = at<float>(ws, pl, B_GAMMA); ha.P = at<double>(ws, pl, B_P);
-  ha.s0 = s0; ha.s_final = s_final; ha.snap = at<float>(ws, pl, B_SNAP);
+  ha.s0 = s0; ha.s_final = s_final; ha.snap = at<void>(ws, pl, B_SNAP);
   ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 1;
   ha.row_pair = sa.row_pair; ha.row_ptr = sa.row_ptr; ha.col = sa.col; ha.event_slot = sa.event_slot;
   ha.Emax = Emax; ha.snap_cap = pl.snap_cap;
@@ -336,8 +338,8 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   mark(dbg, SGDN_EV_HSCAN, s);
 
   OChunkArgs oa{};
-  oa.q = q; oa.k = k; oa.U = at<float>(ws, pl, B_U); oa.snap = at<float>(ws, pl, B_SNAP);
-  oa.s0T = s0 ? at<float>(ws, pl, B_S0T) : nullptr;
+  oa.q = q; oa.k = k; oa.U = at<void>(ws, pl, B_U); oa.snap = at<void>(ws, pl, B_SNAP);
+  oa.s0T = s0 ? at<void>(ws, pl, B_S0T) : nullptr;
   oa.o_bf16 = prob->o_dtype == SGDN_BF16;
   oa.g = at<float>(ws, pl, B_G); oa.gamma = at<float>(ws, pl, B_GAMMA); oa.P = at<double>(ws, pl, B_P);
   oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;

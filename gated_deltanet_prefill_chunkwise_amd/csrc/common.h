@@ -26,6 +26,9 @@ namespace sgdn {
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 fp16;
+typedef fp16 fp16x8 __attribute__((ext_vector_type(8)));
+typedef fp16 fp16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
@@ -35,20 +38,43 @@ constexpr int DV = 128;    // value dimension
 
 template <typename E> struct FragOf;
 template <> struct FragOf<bf16> { using T = bf16x8; using H = bf16x4; };
+template <> struct FragOf<fp16> { using T = fp16x8; using H = fp16x4; };
 template <> struct FragOf<float> { using T = f32x8; using H = f32x4; };
 template <typename E> using frag_t = typename FragOf<E>::T;
 template <typename E> using half_t = typename FragOf<E>::H;
 
+// Element type of the stage-to-stage intermediates (U, U', W, K^T, Cb,
+// snapshots and the in-LDS state / X operands): fp16 when the inputs are
+// bf16 (11-bit significands, so the stored intermediates add about an eighth
+// of a bf16 rounding), fp32 when the inputs are fp32.
+template <typename E> struct InterOf;
+template <> struct InterOf<bf16> { using T = fp16; };
+template <> struct InterOf<float> { using T = float; };
+template <typename E> using inter_t = typename InterOf<E>::T;
+
 __device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(fp16 x) { return (float)x; }
 __device__ __forceinline__ float to_f(float x) { return x; }
 template <typename E> __device__ __forceinline__ E from_f(float x);
 template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ fp16 from_f<fp16>(float x) { return (fp16)x; }
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+
+// Convert a fragment between element types (elementwise, round to nearest).
+template <typename D, typename S> __device__ __forceinline__ frag_t<D> cvt8(const frag_t<S>& x) {
+  frag_t<D> y;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = from_f<D>(to_f(x[i]));
+  return y;
+}
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const fp16x8& a, const fp16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mma(const f32x8& a, const f32x8& b, f32x4 c) {
 #pragma unroll

@@ -17,11 +17,9 @@
 // operand fragment) in a permuted reduction order; the LDS operands S and X
 // are read in the same order.  The operands of an event do not depend on the
 // state, so they are requested DEPTH events ahead into a ring of registers.
-// The fp32 state stays in registers; a bf16 (or fp32) copy in LDS is the
-// operand of the next step's W S (a single bf16 rounding there costs < 0.3% of
-// the output RMS).  U, U' and X are fp32; X is stored as bf16 hi + lo halves
-// for K^T X, and snapshots are fp32, because single bf16 roundings of these
-// move the outputs by 1-4% of their RMS.
+// The fp32 state stays in registers.  Operands and stored intermediates use
+// the intermediate type I (fp16 for bf16 inputs, fp32 for fp32 inputs): the
+// LDS copy of S for the next W S, X for K^T X, U, U' and the snapshots.
 #include "common.h"
 #include "kernels.h"
 
@@ -42,13 +40,12 @@ template <typename E, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void hscan_kernel(HScanArgs p) {
   // events whose operands are in flight: 10 loads per event and wave, so the
   // ring plus the stores stays below the 63 vector-memory operations a wave
-  // can count (fp32 fragments are twice as large: a shorter ring)
+  // can count (fp32 intermediates are twice as large: a shorter ring)
   constexpr int DEPTH = sizeof(E) == 2 ? 4 : 2;
   static_assert(EVT % DEPTH == 0, "buffer ring must align with the tiles");
-  constexpr bool kSplit = sizeof(E) == 2;
-  __shared__ __align__(16) E sS[16 * SSTR];
-  __shared__ __align__(16) E sXh[16 * XSTR];
-  __shared__ __align__(16) E sXl[kSplit ? 16 * XSTR : 8];
+  using I = inter_t<E>;
+  __shared__ __align__(16) I sS[16 * SSTR];
+  __shared__ __align__(16) I sX[16 * XSTR];
   // event metadata of the current tile: chunk retention gamma; sparse also
   // chunk, snapshot slot and gap factor (chunk indices also for the DEPTH
   // events past the tile)
@@ -133,7 +130,7 @@ __global__ __launch_bounds__(256, 1) void hscan_kernel(HScanArgs p) {
         const int dk = 32 * w + 16 * tt + 4 * g4 + j;
         S[tt][j] = p.s0 ? f0 * p.s0[(bh * DK + dk) * DV + dv0 + n16] : 0.f;
       }
-      st4(&sS[n16 * SSTR + 32 * w + 16 * tt + 4 * g4], S[tt]);
+      st4<I>(&sS[n16 * SSTR + 32 * w + 16 * tt + 4 * g4], S[tt]);
     }
     // the initial state is complete before any operand request, so the loop
     // never waits on these loads
@@ -141,30 +138,31 @@ __global__ __launch_bounds__(256, 1) void hscan_kernel(HScanArgs p) {
   }
   stage_meta(t0);
 
-  const E* Wbase = static_cast<const E*>(p.W);
-  const E* KTbase = static_cast<const E*>(p.KT);
-  float* Ubase = p.U;
-  float* snap = p.snap;
+  const I* Wbase = static_cast<const I*>(p.W);
+  const I* KTbase = static_cast<const I*>(p.KT);
+  I* Ubase = static_cast<I*>(p.U);
+  I* snap = static_cast<I*>(p.snap);
 
   // Operands of one event for this wave.
   struct Ops {
-    frag_t<E> wf[4];      // W blocks (dk step q, token tile w)
-    frag_t<E> kf[2][2];   // K^T blocks (dk tile 2w + tt, token step ks)
-    f32x4 u, gv;          // U and g of tokens 16w + 4g .. 16w + 4g + 3
+    frag_t<I> wf[4];      // W blocks (dk step q, token tile w)
+    frag_t<I> kf[2][2];   // K^T blocks (dk tile 2w + tt, token step ks)
+    half_t<I> u;          // U of tokens 16w + 4g .. 16w + 4g + 3
+    f32x4 gv;             // g of the same tokens
     int c;
   };
   auto load = [&](int i, int c, Ops& o) __attribute__((always_inline)) {
     const size_t hc = bh * C + c;
-    const E* Wt = SPARSE ? Wbase + (((size_t)b * p.Emax + i) * 2 + hh) * L * DK
+    const I* Wt = SPARSE ? Wbase + (((size_t)b * p.Emax + i) * 2 + hh) * L * DK
                          : Wbase + hc * L * DK;
-    const E* KTt = KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L;
+    const I* KTt = KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L;
 #pragma unroll
     for (int q = 0; q < 4; ++q) o.wf[q] = ld8(Wt + wblk(q, w) + 8 * lane);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) o.kf[tt][ks] = ld8(KTt + kblk(2 * w + tt, ks) + 8 * lane);
-    o.u = *reinterpret_cast<const f32x4*>(Ubase + hc * DV * L + (dv0 + n16) * L + 16 * w + 4 * g4);
+    o.u = *reinterpret_cast<const half_t<I>*>(Ubase + hc * DV * L + (dv0 + n16) * L + 16 * w + 4 * g4);
     o.gv = *reinterpret_cast<const f32x4*>(p.g + hc * L + 16 * w + 4 * g4);
     o.c = c;
   };
@@ -187,31 +185,17 @@ __global__ __launch_bounds__(256, 1) void hscan_kernel(HScanArgs p) {
     f32x4 acc = zero4();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const E* sr = &sS[n16 * SSTR + 32 * q + 4 * g4];
+      const I* sr = &sS[n16 * SSTR + 32 * q + 4 * g4];
       acc = mma(cur.wf[q], ld44(sr, sr + 16), acc);
     }
     f32x4 up, x;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      up[j] = cur.u[j] - acc[j];
+      up[j] = to_f(cur.u[j]) - acc[j];
       x[j] = up[j] * exp2_neg(gam - cur.gv[j]);
     }
-    st4f(Ubase + hc * DV * L + (dv0 + n16) * L + 16 * w + 4 * g4, up);
-    {
-      E* xh = &sXh[n16 * XSTR + 16 * w + 4 * g4];
-      if constexpr (kSplit) {
-        half_t<E> hi, lo;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          hi[j] = from_f<E>(x[j]);
-          lo[j] = from_f<E>(x[j] - to_f(hi[j]));
-        }
-        *reinterpret_cast<half_t<E>*>(xh) = hi;
-        *reinterpret_cast<half_t<E>*>(&sXl[n16 * XSTR + 16 * w + 4 * g4]) = lo;
-      } else {
-        st4(xh, x);
-      }
-    }
+    st4<I>(Ubase + hc * DV * L + (dv0 + n16) * L + 16 * w + 4 * g4, up);
+    st4<I>(&sX[n16 * XSTR + 16 * w + 4 * g4], x);
     lds_barrier();
 
     // ---- S <- 2^gamma S + K^T (U' * 2^(gamma - g))   (Eq. (2)); X read in
@@ -222,12 +206,8 @@ __global__ __launch_bounds__(256, 1) void hscan_kernel(HScanArgs p) {
       f32x4 d = S[tt] * dec;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const E* xr = &sXh[n16 * XSTR + 32 * ks + 4 * g4];
+        const I* xr = &sX[n16 * XSTR + 32 * ks + 4 * g4];
         d = mma(cur.kf[tt][ks], ld44(xr, xr + 16), d);
-        if constexpr (kSplit) {
-          const E* lr = &sXl[n16 * XSTR + 32 * ks + 4 * g4];
-          d = mma(cur.kf[tt][ks], ld44(lr, lr + 16), d);
-        }
       }
       S[tt] = d;
     }
@@ -237,7 +217,7 @@ __global__ __launch_bounds__(256, 1) void hscan_kernel(HScanArgs p) {
     request(i + DEPTH, cur);
 
     // ---- compact snapshot of S_{c+1} if an output group starts from it
-    float* sp = nullptr;
+    I* sp = nullptr;
     if constexpr (SPARSE) {
       const int es = sEvSlot[i - t0];
       if (es >= 0) sp = snap + (((size_t)b * p.snap_cap + es) * 2 + hh) * DV * DK;
@@ -246,7 +226,7 @@ __global__ __launch_bounds__(256, 1) void hscan_kernel(HScanArgs p) {
     }
     if (sp != nullptr) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) st4f(sp + (dv0 + n16) * DK + 32 * w + 16 * tt + 4 * g4, S[tt]);
+      for (int tt = 0; tt < 2; ++tt) st4<I>(sp + (dv0 + n16) * DK + 32 * w + 16 * tt + 4 * g4, S[tt]);
     }
 
     // ---- gap to the next event (Eq. (21)): S_next = 2^(P_next - P_{c+1}) S
@@ -256,7 +236,7 @@ __global__ __launch_bounds__(256, 1) void hscan_kernel(HScanArgs p) {
       for (int tt = 0; tt < 2; ++tt) S[tt] *= f;
     }
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) st4(&sS[n16 * SSTR + 32 * w + 16 * tt + 4 * g4], S[tt]);
+    for (int tt = 0; tt < 2; ++tt) st4<I>(&sS[n16 * SSTR + 32 * w + 16 * tt + 4 * g4], S[tt]);
     lds_barrier();
   };
 

@@ -110,8 +110,9 @@ __device__ __forceinline__ f32x8 ld_tr44(const float* base, int ld, int lane) {
 }
 
 // Coefficient fragments of one k-step: C~ = C diag(beta) (hi + lo halves for
-// bf16 operands) and Cb = C diag(beta 2^g).
-template <typename E> struct CoefFrag { frag_t<E> hi, lo, cb; };
+// bf16 operands) and Cb = C diag(beta 2^g), as an MFMA operand (cb) and in the
+// stored intermediate type (cbi).
+template <typename E> struct CoefFrag { frag_t<E> hi, lo, cb; frag_t<inter_t<E>> cbi; };
 
 template <typename E>
 __device__ __forceinline__ CoefFrag<E> coef_frag(const float* sCt, const float* sb, const float* sbe,
@@ -128,13 +129,16 @@ __device__ __forceinline__ CoefFrag<E> coef_frag(const float* sCt, const float* 
     const E h = from_f<E>(ct);
     f.hi[e] = h;
     f.lo[e] = from_f<E>(ct - to_f(h));
-    f.cb[e] = from_f<E>(c * be8[e]);
+    const float cbv = c * be8[e];
+    f.cb[e] = from_f<E>(cbv);
+    f.cbi[e] = from_f<inter_t<E>>(cbv);
   }
   return f;
 }
 
 template <typename E, bool BA, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
+  using I = inter_t<E>;
   __shared__ __align__(16) E sK[L * KS];      // key tile, row-major [t][dk]
   __shared__ __align__(16) E sV[L * KS];      // value tile of the current head [t][dv]
   __shared__ __align__(16) float sMt[NT * TILE];
@@ -238,14 +242,14 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     // ---- fragment-major key tile (K^T operand blocks) for the H and
     //      deferred-W stages
     {
-      E* kt = static_cast<E*>(p.KT) + ((size_t)(b * Nq + pq) * C + c) * DK * L;
+      I* kt = static_cast<I*>(p.KT) + ((size_t)(b * Nq + pq) * C + c) * DK * L;
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int mt = 2 * w + mi;
           const frag_t<E> f = ld_tr44(&sK[32 * ks * KS + 16 * mt], KS, lane);
-          *reinterpret_cast<frag_t<E>*>(kt + kblk(mt, ks) + 8 * lane) = f;
+          *reinterpret_cast<frag_t<I>*>(kt + kblk(mt, ks) + 8 * lane) = cvt8<I, E>(f);
         }
     }
 
@@ -383,11 +387,12 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
           cf[ks] = coef_frag<E>(sCt, sb[hh], sbe[hh], w, ks, BA, lane);
         } else {
           cf[ks].hi = cf[ks].lo = cf[ks].cb = zero_frag<E>();
+          cf[ks].cbi = zero_frag<I>();
         }
       }
       {
         // two halves of 64 value columns each, to bound the live fragments
-        float* U = p.U + hc * DV * L;
+        I* U = static_cast<I*>(p.U) + hc * DV * L;
         float ss = 0.f;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -407,7 +412,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
           }
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) {
-            st4f(U + (16 * (4 * half + nt) + n16) * L + 16 * w + 4 * g4, acc[nt]);
+            st4<I>(U + (16 * (4 * half + nt) + n16) * L + 16 * w + 4 * g4, acc[nt]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) ss += acc[nt][j] * acc[nt][j];
           }
@@ -424,13 +429,13 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
       // be live at the same time)
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (SPARSE) {
-        E* cb = static_cast<E*>(p.Cb) + hc * L * L;
+        I* cb = static_cast<I*>(p.Cb) + hc * L * L;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          *reinterpret_cast<frag_t<E>*>(cb + (16 * w + n16) * L + 32 * ks + 8 * g4) = cf[ks].cb;
+          *reinterpret_cast<frag_t<I>*>(cb + (16 * w + n16) * L + 32 * ks + 8 * g4) = cf[ks].cbi;
       } else {
         // W^T = K^T Cb^T: rows dk, columns t
-        E* W = static_cast<E*>(p.W) + hc * L * DK;
+        I* W = static_cast<I*>(p.W) + hc * L * DK;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           f32x4 acc[4];
@@ -449,8 +454,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
           // two stacked W^T tiles form one fragment-major W block
 #pragma unroll
           for (int qq = 0; qq < 2; ++qq)
-            *reinterpret_cast<frag_t<E>*>(W + wblk(2 * half + qq, w) + 8 * lane) =
-                pack44<E>(acc[2 * qq], acc[2 * qq + 1]);
+            *reinterpret_cast<frag_t<I>*>(W + wblk(2 * half + qq, w) + 8 * lane) =
+                pack44<I>(acc[2 * qq], acc[2 * qq + 1]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }

@@ -7,16 +7,18 @@
 
 namespace sgdn {
 
-// Workspace tensors (all per batch b, head-major):
+// Workspace tensors (all per batch b, head-major).  I is the intermediate
+// element type: fp16 for bf16 inputs, fp32 for fp32 inputs.
 //   g      [B][Nv][C][64]      fp32  in-chunk inclusive log2 decay
 //   gamma  [B][Nv][C]          fp32  chunk retention g[63]
 //   P      [B][Nv][C+1]        fp64  prefix of gamma
-//   U      [B][Nv][C][dv][64]  fp32  U (then U' in place), dv-major tiles
-//   W      [B][Nv][C][8192]    E     dense W tiles, fragment-major (below)
-//   Cb     [B][Nv][C][64][64]  E     staged C diag(beta 2^g), row-major
-//   KT     [B][Nq][C][8192]    E     key tiles, fragment-major (below)
-//   snap   [..][dv][dk]        fp32  compact state snapshots (transposed)
-//   Wpk    [B][Emax][2][8192]  E     deferred W of kept events, fragment-major
+//   U      [B][Nv][C][dv][64]  I     U (then U' in place), dv-major tiles
+//   W      [B][Nv][C][8192]    I     dense W tiles, fragment-major (below)
+//   Cb     [B][Nv][C][64][64]  I     staged C diag(beta 2^g), row-major
+//   KT     [B][Nq][C][8192]    I     key tiles, fragment-major (below)
+//   snap   [..][dv][dk]        I     compact state snapshots (transposed)
+//   s0T    [B][Nv][dv][dk]     I     initial state, transposed
+//   Wpk    [B][Emax][2][8192]  I     deferred W of kept events, fragment-major
 //
 // Fragment-major tiles: 16 blocks of 512 elements, block = one 64-lane MFMA
 // operand fragment (lane l = 16 g + n holds 8 consecutive elements), so a wave
@@ -31,7 +33,7 @@ struct IntraArgs {
   const void* k; const void* v; const float* a; const void* beta;
   int B, T, Nq, Nv, C, solve;
   float* g; float* gamma;
-  float* U; void* W; void* Cb; void* KT;
+  void* U; void* W; void* Cb; void* KT;
   float* score;
 };
 
@@ -43,11 +45,11 @@ struct PrefixArgs {
 // per workgroup.  Dense: every chunk is an event, W from the intra kernel.
 // Sparse: events from the CSR rows, W packed per event.
 struct HScanArgs {
-  const void* KT; const void* W; float* U;
+  const void* KT; const void* W; void* U;
   const float* g; const float* gamma; const double* P;
   const float* s0;          // [B][Nv][dk][dv] or null
   float* s_final;           // [B][Nv][dk][dv] or null
-  float* snap;              // snapshots
+  void* snap;               // snapshots
   int B, Nq, Nv, C;
   int sparse;
   // sparse metadata (per batch)
@@ -60,7 +62,7 @@ struct HScanArgs {
 };
 
 struct OChunkArgs {
-  const void* q; const void* k; const float* U; const float* snap; const float* s0T;
+  const void* q; const void* k; const void* U; const void* snap; const void* s0T;
   const float* g; const float* gamma; const double* P;
   void* o; int o_bf16;
   int B, T, Nq, Nv, C, G;
@@ -70,7 +72,7 @@ struct OChunkArgs {
   int snap_cap;
 };
 
-struct S0PrepArgs { const float* s0; float* s0T; int B, Nv; };
+struct S0PrepArgs { const float* s0; void* s0T; int B, Nv; };
 
 struct GateArgs {
   const void* z; const float* w; float* eta; int B, T, Nv, C;
@@ -99,10 +101,10 @@ hipError_t launch_intra(const IntraArgs& a, int bf16, hipStream_t s);
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s);
 hipError_t launch_hscan(const HScanArgs& a, int bf16, hipStream_t s);
 hipError_t launch_ochunk(const OChunkArgs& a, int bf16, hipStream_t s);
-hipError_t launch_s0prep(const S0PrepArgs& a, hipStream_t s);
+hipError_t launch_s0prep(const S0PrepArgs& a, int bf16, hipStream_t s);
 hipError_t launch_gate(const GateArgs& a, int bf16, hipStream_t s);
 hipError_t launch_select_full(const SelectArgs& a, int kL, int kM, int kH, hipStream_t s);
 hipError_t launch_deferred_w(const DeferredWArgs& a, int bf16, hipStream_t s);
-hipError_t launch_debug_u(const float* Ut, float* U, int B, int Nv, int C, hipStream_t s);
+hipError_t launch_debug_u(const void* Ut, float* U, int B, int Nv, int C, int bf16, hipStream_t s);
 
 }  // namespace sgdn

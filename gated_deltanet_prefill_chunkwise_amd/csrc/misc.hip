@@ -31,15 +31,16 @@ __global__ __launch_bounds__(64) void prefix_kernel(PrefixArgs p) {
   }
 }
 
-// s0 [dk][dv] -> transposed [dv][dk] (fp32), the "virtual snapshot" that
-// output groups without a predecessor read.
+// s0 [dk][dv] -> transposed [dv][dk] in the snapshot element type, the
+// "virtual snapshot" that output groups without a predecessor read.
+template <typename I>
 __global__ __launch_bounds__(256) void s0prep_kernel(S0PrepArgs p) {
   const size_t bh = blockIdx.x;
   const float* s = p.s0 + bh * DK * DV;
-  float* o = p.s0T + bh * DV * DK;
+  I* o = static_cast<I*>(p.s0T) + bh * DV * DK;
   for (int q = threadIdx.x; q < DK * DV; q += 256) {
     const int dv = q >> 7, dk = q & 127;
-    o[q] = s[dk * DV + dv];
+    o[q] = from_f<I>(s[dk * DV + dv]);
   }
 }
 
@@ -71,7 +72,8 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs p) {
 
 // Deferred W of kept events only (SparseGDN reading notes, Sec. 2.5,
 // Eq. (15)): W = Cb K from the staged coefficients, computed as
-// W^T = K^T Cb^T and stored token-major per event (both heads of the pair).
+// W^T = K^T Cb^T and stored as fragment-major W tiles per event (both heads of
+// the pair).
 // The grid is sized to the capacity E_max; blocks past the on-device E exit.
 template <typename E>
 __global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
@@ -86,37 +88,41 @@ __global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int n16 = lane & 15, g4 = lane >> 4;
   const bool blockadj = p.solve == 1;
-  const E* KT = static_cast<const E*>(p.KT) + (((size_t)b * p.Nq + pr) * p.C + c) * DK * L;
+  using I = inter_t<E>;
+  const I* KT = static_cast<const I*>(p.KT) + (((size_t)b * p.Nq + pr) * p.C + c) * DK * L;
   const int ks_lo = (blockadj && w == 3) ? 1 : 0;
   const int ks_hi = (w >= 2) ? 1 : 0;
   for (int hh = 0; hh < 2; ++hh) {
     const int h = 2 * pr + hh;
-    const E* Cb = static_cast<const E*>(p.Cb) + (((size_t)b * p.Nv + h) * p.C + c) * L * L;
+    const I* Cb = static_cast<const I*>(p.Cb) + (((size_t)b * p.Nv + h) * p.C + c) * L * L;
     // W^T = K^T Cb^T (rows dk, columns t).  K^T blocks are fragment-major in
     // the permuted token order, so Cb is read in the same order.
     f32x4 acc[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
     for (int ks = ks_lo; ks <= ks_hi; ++ks) {
-      const E* cr = Cb + (16 * w + n16) * L + 32 * ks + 4 * g4;
-      const frag_t<E> fb = ld44(cr, cr + 16);
+      const I* cr = Cb + (16 * w + n16) * L + 32 * ks + 4 * g4;
+      const frag_t<I> fb = ld44(cr, cr + 16);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc[mt] = mma(ld8(KT + kblk(mt, ks) + 8 * lane), fb, acc[mt]);
     }
     // two stacked W^T tiles form one fragment-major W block
-    E* W = static_cast<E*>(p.Wpk) + (((size_t)b * p.Emax + i) * 2 + hh) * L * DK;
+    I* W = static_cast<I*>(p.Wpk) + (((size_t)b * p.Emax + i) * 2 + hh) * L * DK;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<frag_t<E>*>(W + wblk(q, w) + 8 * lane) = pack44<E>(acc[2 * q], acc[2 * q + 1]);
+      *reinterpret_cast<frag_t<I>*>(W + wblk(q, w) + 8 * lane) = pack44<I>(acc[2 * q], acc[2 * q + 1]);
   }
 }
 
-// U tiles [dv][t] -> token-major [t][dv] copy for the debug output.
-__global__ __launch_bounds__(256) void debug_u_kernel(const float* Ut, float* U) {
+// U tiles [dv][t] (intermediate type) -> token-major fp32 [t][dv] copy for
+// the debug output.
+template <typename I>
+__global__ __launch_bounds__(256) void debug_u_kernel(const void* Ut_, float* U) {
+  const I* Ut = static_cast<const I*>(Ut_);
   const size_t tile = blockIdx.x;
   for (int q = threadIdx.x; q < L * DV; q += 256) {
     const int t = q >> 7, dv = q & 127;
-    U[tile * L * DV + q] = Ut[tile * DV * L + dv * L + t];
+    U[tile * L * DV + q] = to_f(Ut[tile * DV * L + dv * L + t]);
   }
 }
 
@@ -127,8 +133,11 @@ hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_s0prep(const S0PrepArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(s0prep_kernel, dim3(a.B * a.Nv), dim3(256), 0, s, a);
+hipError_t launch_s0prep(const S0PrepArgs& a, int bf16, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(s0prep_kernel<fp16>, dim3(a.B * a.Nv), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(s0prep_kernel<float>, dim3(a.B * a.Nv), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -149,8 +158,11 @@ hipError_t launch_deferred_w(const DeferredWArgs& a, int bf16, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_debug_u(const float* Ut, float* U, int B, int Nv, int C, hipStream_t s) {
-  hipLaunchKernelGGL(debug_u_kernel, dim3(B * Nv * C), dim3(256), 0, s, Ut, U);
+hipError_t launch_debug_u(const void* Ut, float* U, int B, int Nv, int C, int bf16, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(debug_u_kernel<fp16>, dim3(B * Nv * C), dim3(256), 0, s, Ut, U);
+  else
+    hipLaunchKernelGGL(debug_u_kernel<float>, dim3(B * Nv * C), dim3(256), 0, s, Ut, U);
   return hipGetLastError();
 }
 

@@ -16,11 +16,12 @@
 // Computed transposed, O^T = S^T Q^T + U'^T A^T:
 //   phase 1: wave i computes the A^T blocks of source tile i (K rows from
 //            global, Q rows from LDS), applies the decay and stores them in
-//            LDS as bf16 hi + lo halves (B operand layout [t][s]);
+//            LDS (B operand layout [t][s]);
 //   phase 2: wave w owns dv rows 16w..16w+15 of O^T for all 128 tokens, so
-//            each row of the fp32 state and of U' is read exactly once.
-// fp32-valued operands (state, U', A) enter the bf16 matrix cores as hi + lo
-// halves (products: S x Q two terms, U' x A three terms).
+//            each row of the state and of U' is read exactly once.
+// All products run in the intermediate type I of the state snapshots and U'
+// (fp16 for bf16 inputs: q and k are unit-norm rows, so their conversion is
+// exact; fp32 for fp32 inputs).
 #include "common.h"
 #include "kernels.h"
 
@@ -32,11 +33,10 @@ constexpr int QSTR = DK + 8;      // Q rows [t][dk]
 constexpr int ASTR = 2 * L + 8;   // A^T rows [t][s], s over the group's 128 tokens
 
 template <typename E, typename OT>
-__global__ __launch_bounds__(512) void ochunk_kernel(OChunkArgs p) {
-  constexpr bool kSplit = sizeof(E) == 2;
-  __shared__ __align__(32) E sQ[2 * L * QSTR];
-  __shared__ __align__(32) E sAh[2 * L * ASTR];
-  __shared__ __align__(32) E sAl[kSplit ? 2 * L * ASTR : 8];
+__global__ __launch_bounds__(512, 2) void ochunk_kernel(OChunkArgs p) {
+  using I = inter_t<E>;
+  __shared__ __align__(32) I sQ[2 * L * QSTR];
+  __shared__ __align__(32) I sA[2 * L * ASTR];
   __shared__ float sG[2 * L];
 
   const int r = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(512) void ochunk_kernel(OChunkArgs p) {
   const size_t bh = (size_t)b * Nv + h;
 
   // ---- group entry state: source and log2 factor
-  const float* Ssrc = nullptr;
+  const I* Ssrc = nullptr;
   float lf = 0.f;
   if (p.sparse) {
     const size_t pg = ((size_t)b * (Nv / 2) + pr) * G + r;
@@ -58,22 +58,22 @@ __global__ __launch_bounds__(512) void ochunk_kernel(OChunkArgs p) {
     const double* P = p.P + bh * (C + 1);
     if (slot >= 0) {
       const int e = p.pred[pg];
-      Ssrc = p.snap + (((size_t)b * p.snap_cap + slot) * 2 + hh) * DV * DK;
+      Ssrc = static_cast<const I*>(p.snap) + (((size_t)b * p.snap_cap + slot) * 2 + hh) * DV * DK;
       lf = (float)(P[c0] - P[e + 1]);
     } else if (p.s0T != nullptr) {
-      Ssrc = p.s0T + bh * DV * DK;
+      Ssrc = static_cast<const I*>(p.s0T) + bh * DV * DK;
       lf = (float)P[c0];
     }
   } else {
     if (r > 0)
-      Ssrc = p.snap + (bh * (G - 1) + r - 1) * DV * DK;
+      Ssrc = static_cast<const I*>(p.snap) + (bh * (G - 1) + r - 1) * DV * DK;
     else if (p.s0T != nullptr)
-      Ssrc = p.s0T + bh * DV * DK;
+      Ssrc = static_cast<const I*>(p.s0T) + bh * DV * DK;
   }
 
   // ---- global loads of both phases are issued up front so that their
-  //      latencies overlap (one workgroup holds the CU's LDS); the Q rows to
-  //      stage go first, because loads retire in order
+  //      latencies overlap; the Q rows to stage go first, because loads
+  //      retire in order
   const E* Qin = static_cast<const E*>(p.q);
   const E* Kin = static_cast<const E*>(p.k);
   frag_t<E> qst[4];
@@ -94,12 +94,13 @@ __global__ __launch_bounds__(512) void ochunk_kernel(OChunkArgs p) {
                                      : zero_frag<E>();
   }
   const int dvr = 16 * w + n16;
-  f32x8 sfr[4], ufr[4];
+  const I* Up = static_cast<const I*>(p.U);
+  frag_t<I> sfr[4], ufr[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    sfr[ks] = Ssrc != nullptr ? ld8f(Ssrc + (size_t)dvr * DK + 32 * ks + 8 * g4) : f32x8{};
-    ufr[ks] = (2 * ks < ntile) ? ld8f(p.U + ((bh * C + c0 + (ks >> 1)) * DV + dvr) * L + 32 * (ks & 1) + 8 * g4)
-                               : f32x8{};
+    sfr[ks] = Ssrc != nullptr ? ld8(Ssrc + (size_t)dvr * DK + 32 * ks + 8 * g4) : zero_frag<I>();
+    ufr[ks] = (2 * ks < ntile) ? ld8(Up + ((bh * C + c0 + (ks >> 1)) * DV + dvr) * L + 32 * (ks & 1) + 8 * g4)
+                               : zero_frag<I>();
   }
 
   // ---- stage Q rows of the group and G
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(512) void ochunk_kernel(OChunkArgs p) {
   for (int it = 0; it < 4; ++it) {
     const int q = tid + 512 * it;
     const int rr = q >> 4, c8 = (q & 15) * 8;
-    *reinterpret_cast<frag_t<E>*>(&sQ[rr * QSTR + c8]) = qst[it];
+    *reinterpret_cast<frag_t<I>*>(&sQ[rr * QSTR + c8]) = cvt8<I, E>(qst[it]);
   }
   if (tid < 128) {
     const int cc = tid >> 6;
@@ -123,6 +124,9 @@ __global__ __launch_bounds__(512) void ochunk_kernel(OChunkArgs p) {
 
   // ---- phase 1: A^T blocks of source tile w (s in 16w..16w+15)
   if (w < ntile) {
+    frag_t<I> kfi[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kfi[ks] = cvt8<I, E>(kf[ks]);
     float gs[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) gs[j] = sG[16 * w + 4 * g4 + j];
@@ -132,28 +136,17 @@ __global__ __launch_bounds__(512) void ochunk_kernel(OChunkArgs p) {
       f32x4 at = zero4();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        at = mma(kf[ks], ld8(&sQ[(16 * jt + n16) * QSTR + 32 * ks + 8 * g4]), at);
+        at = mma(kfi[ks], ld8(&sQ[(16 * jt + n16) * QSTR + 32 * ks + 8 * g4]), at);
       const int t = 16 * jt + n16;
       const float gt = sG[t];
-      f32x4 hi4, lo4;
+      f32x4 a4;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int s = 16 * w + 4 * g4 + j;
         const float v = (s <= t) ? at[j] * exp2f(gt - gs[j]) : 0.f;
-        hi4[j] = v;
+        a4[j] = v;
       }
-      if constexpr (kSplit) {
-        half_t<E> hh4, ll4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          hh4[j] = (bf16)hi4[j];
-          ll4[j] = (bf16)(hi4[j] - (float)hh4[j]);
-        }
-        *reinterpret_cast<half_t<E>*>(&sAh[t * ASTR + 16 * w + 4 * g4]) = hh4;
-        *reinterpret_cast<half_t<E>*>(&sAl[t * ASTR + 16 * w + 4 * g4]) = ll4;
-      } else {
-        st4<E>(&sAh[t * ASTR + 16 * w + 4 * g4], hi4);
-      }
+      st4<I>(&sA[t * ASTR + 16 * w + 4 * g4], a4);
     }
   }
   __syncthreads();
@@ -165,15 +158,11 @@ __global__ __launch_bounds__(512) void ochunk_kernel(OChunkArgs p) {
   if (Ssrc != nullptr) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const f32x8 sf = sfr[ks];
-      frag_t<E> sh, sl;
-      if constexpr (kSplit) split8(sf, sh, sl); else sh = sf;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j < ntile) {
-          const frag_t<E> qf = ld8(&sQ[(16 * j + n16) * QSTR + 32 * ks + 8 * g4]);
-          acc[j] = mma(sh, qf, acc[j]);
-          if constexpr (kSplit) acc[j] = mma(sl, qf, acc[j]);
+          const frag_t<I> qf = ld8(&sQ[(16 * j + n16) * QSTR + 32 * ks + 8 * g4]);
+          acc[j] = mma(sfr[ks], qf, acc[j]);
         }
       }
     }
@@ -188,19 +177,11 @@ __global__ __launch_bounds__(512) void ochunk_kernel(OChunkArgs p) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     if (2 * ks >= ntile) break;
-    const f32x8 uf = ufr[ks];
-    frag_t<E> uh, ul;
-    if constexpr (kSplit) split8(uf, uh, ul); else uh = uf;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j < ntile && ks <= (j >> 1)) {
-        const frag_t<E> ah = ld8(&sAh[(16 * j + n16) * ASTR + 32 * ks + 8 * g4]);
-        acc[j] = mma(uh, ah, acc[j]);
-        if constexpr (kSplit) {
-          const frag_t<E> al = ld8(&sAl[(16 * j + n16) * ASTR + 32 * ks + 8 * g4]);
-          acc[j] = mma(ul, ah, acc[j]);
-          acc[j] = mma(uh, al, acc[j]);
-        }
+        const frag_t<I> af = ld8(&sA[(16 * j + n16) * ASTR + 32 * ks + 8 * g4]);
+        acc[j] = mma(ufr[ks], af, acc[j]);
       }
     }
   }
