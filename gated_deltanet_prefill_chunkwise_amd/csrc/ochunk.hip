@@ -32,18 +32,35 @@ namespace {
 constexpr int QSTR = DK + 8;      // Q rows [t][dk]
 constexpr int ASTR = 2 * L + 8;   // A^T rows [t][s], s over the group's 128 tokens
 
+// Two workgroups per CU (four waves per SIMD: at most 128 registers per lane)
+// so one group's loads
+// overlap the other's products.
 template <typename E, typename OT>
-__global__ __launch_bounds__(512, 2) void ochunk_kernel(OChunkArgs p) {
+__global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   using I = inter_t<E>;
   __shared__ __align__(32) I sQ[2 * L * QSTR];
   __shared__ __align__(32) I sA[2 * L * ASTR];
   __shared__ float sG[2 * L];
 
-  const int r = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int T = p.T, Nq = p.Nq, Nv = p.Nv, C = p.C, G = p.G;
+  // Block -> (group r, head pair pr, batch b; head hh of the pair).  The two
+  // heads of a pair read the same Q and K rows: they are dispatched one after
+  // the other onto the same XCD (workgroups are dealt to the 8 XCDs
+  // round-robin), so the second read hits that XCD's L2.
+  const int id = blockIdx.x, NP = Nv / 2;
+  int unit, hh;
+  if ((gridDim.x & 15) == 0) {
+    const int local = id >> 3;
+    hh = local & 1;
+    unit = (local >> 1) * 8 + (id & 7);
+  } else {
+    hh = id & 1;
+    unit = id >> 1;
+  }
+  const int pr = unit % NP, r = (unit / NP) % G, b = unit / (NP * G);
+  const int h = 2 * pr + hh;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int n16 = lane & 15, g4 = lane >> 4;
-  const int T = p.T, Nq = p.Nq, Nv = p.Nv, C = p.C, G = p.G;
-  const int pr = h >> 1, hh = h & 1;
   const int c0 = 2 * r;
   const bool has1 = c0 + 1 < C;
   const int ntile = has1 ? 8 : 4;           // 16-token tiles in this group
@@ -203,7 +220,7 @@ __global__ __launch_bounds__(512, 2) void ochunk_kernel(OChunkArgs p) {
 }  // namespace
 
 hipError_t launch_ochunk(const OChunkArgs& a, int bf16, hipStream_t s) {
-  dim3 grid(a.G, a.Nv, a.B);
+  dim3 grid(a.G * a.Nv * a.B);
   if (bf16) {
     if (a.o_bf16)
       hipLaunchKernelGGL((ochunk_kernel<sgdn::bf16, sgdn::bf16>), grid, dim3(512), 0, s, a);
