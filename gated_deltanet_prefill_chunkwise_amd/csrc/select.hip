@@ -73,10 +73,14 @@ __device__ double lifetime(double r, int C) {
 
 // Eq. (10): per-head norms of the tail scores, the within-pair rank key q and
 // the rank of every non-anchor chunk (q descending, chunk index ascending).
+// Workgroup (blk, pp, b) ranks chunks 128 blk .. 128 blk + 127 of pair pp:
+// eight threads per chunk count disjoint eighths of the other chunks.  Every
+// workgroup forms the norms and keys itself, with the same operations.
+constexpr int RANK_CHUNKS = 128;
 __global__ __launch_bounds__(1024) void select_rank_kernel(SelectArgs p) {
   extern __shared__ double sq[];
   __shared__ double snorm[2];
-  const int pp = blockIdx.x, b = blockIdx.y;
+  const int blk = blockIdx.x, pp = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int C = p.C;
   const float* s0 = p.score + ((size_t)b * NV + 2 * pp) * C;
@@ -100,18 +104,21 @@ __global__ __launch_bounds__(1024) void select_rank_kernel(SelectArgs p) {
   }
   __syncthreads();
   int32_t* rk = p.rank + ((size_t)b * NP + pp) * C;
-  for (int c = tid; c < C; c += 1024) {
-    int r = -1;
-    if (c >= 1 && c <= C - 2) {
-      const double qc = sq[c];
-      r = 0;
-      for (int c2 = 1; c2 <= C - 2; ++c2) {
-        const double q2 = sq[c2];
-        r += (q2 > qc || (q2 == qc && c2 < c)) ? 1 : 0;
-      }
+  const int c = RANK_CHUNKS * blk + (tid >> 3), part = tid & 7;
+  int r = 0;
+  const bool inner = c >= 1 && c <= C - 2;
+  if (inner) {
+    const double qc = sq[c];
+    for (int c2 = 1 + part; c2 <= C - 2; c2 += 8) {
+      const double q2 = sq[c2];
+      r += (q2 > qc || (q2 == qc && c2 < c)) ? 1 : 0;
     }
-    rk[c] = r;
   }
+  // the eight partial counts of a chunk sit in eight adjacent lanes
+  r += __shfl_xor(r, 1, 64);
+  r += __shfl_xor(r, 2, 64);
+  r += __shfl_xor(r, 4, 64);
+  if (part == 0 && c < C) rk[c] = inner ? r : -1;
 }
 
 // B(x, k) = k (n-k) / n (mean x[:k] - mean x[k:])^2 over the wave-held sorted
@@ -128,36 +135,39 @@ __device__ double split_score(const double* vals, int n, int k, int lane) {
 }
 
 // Eqs. (11)-(14): lifetime, visibility, upgrade gains, dynamic tier counts.
-__global__ __launch_bounds__(64) void select_tier_kernel(SelectArgs p, int kL, int kM, int kH) {
+// Wave w forms the per-head sums of the two heads of pair w (each sum is one
+// wave's lane-interleaved sum, as everywhere in this file); wave 0 then takes
+// the decisions.
+__global__ __launch_bounds__(1024) void select_tier_kernel(SelectArgs p, int kL, int kM, int kH) {
   __shared__ double sL[NV], sGv[NV], slm[NV], smh[NV];
   __shared__ double sxm[NP], sxh[NP], svals[NP];
   __shared__ int sorder[NP], shigh[NP];
-  const int b = blockIdx.x, lane = threadIdx.x, C = p.C;
+  const int b = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, C = p.C;
   const float* sc = p.score + (size_t)b * NV * C;
   const float* gm = p.gamma + (size_t)b * NV * C;
   const float* et = p.eta + (size_t)b * NV;
   const int32_t* rk = p.rank + (size_t)b * NP * C;
 
   const int lo = C > 16 ? C - 16 : 0, nwin = C - lo;
-  for (int h = 0; h < NV; ++h) {
+  for (int h = 2 * wv; h < 2 * wv + 2; ++h) {
     const double x = lane < nwin ? exp2_fixed((double)gm[h * C + lo + lane]) : 0.0;
     const double tot = wave_sum(x);
     if (lane == 0) sL[h] = lifetime(tot / nwin, C);
-  }
-  const double etab = wave_sum(lane < NV ? (double)et[lane] : 0.0) / NV;
-  if (lane < NV) sGv[lane] = etab > 0.0 ? sqrt((double)et[lane] / etab) : 1.0;
-  for (int h = 0; h < NV; ++h) {
     const int pp = h >> 1;
     double alm = 0.0, amh = 0.0;
     for (int c = lane; c < C; c += 64) {
       const int r = rk[pp * C + c];
-      const double x = (double)sc[h * C + c];
-      alm = alm + ((r >= kL - 2 && r < kM - 2) ? x : 0.0);
-      amh = amh + ((r >= kM - 2 && r < kH - 2) ? x : 0.0);
+      const double xs = (double)sc[h * C + c];
+      alm = alm + ((r >= kL - 2 && r < kM - 2) ? xs : 0.0);
+      amh = amh + ((r >= kM - 2 && r < kH - 2) ? xs : 0.0);
     }
     const double tl = wave_sum(alm), th = wave_sum(amh);
     if (lane == 0) { slm[h] = tl; smh[h] = th; }
   }
+  __syncthreads();
+  if (wv != 0) return;
+  const double etab = wave_sum(lane < NV ? (double)et[lane] : 0.0) / NV;
+  if (lane < NV) sGv[lane] = etab > 0.0 ? sqrt((double)et[lane] / etab) : 1.0;
   __syncthreads();
   double glm = 0.0, gmh = 0.0;
   if (lane < NP) {
@@ -338,19 +348,23 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p, int kL, int 
   }
   __syncthreads();
   {
-    // predecessor of each group of pair w: last kept chunk < 2r
+    // predecessor of each group r of pair w: the last kept chunk < 2r, i.e.
+    // CSR entry beg + (number of kept chunks before 2r) - 1
     const int pp = w, row = s_rowof[pp];
-    const int beg = s_rowptr[row], end = s_rowptr[row + 1];
-    for (int r = lane; r < G; r += 64) {
-      int lo = beg, hi = end;   // first index with col >= 2r
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (col[mid] < 2 * r) lo = mid + 1; else hi = mid;
+    const int beg = s_rowptr[row];
+    int run = 0;   // kept chunks before c0
+    for (int c0 = 0; c0 < C; c0 += 64) {
+      const int c = c0 + lane;
+      const bool z = c < C && mask[(size_t)pp * C + c];
+      const unsigned long long bal = __ballot(z);
+      const int before = run + __popcll(bal & ((1ull << lane) - 1ull));
+      if ((c & 1) == 0 && c < C && (c >> 1) < G) {
+        const int r = c >> 1, i = beg + before - 1;
+        const size_t o = ((size_t)b * NP + pp) * G + r;
+        p.pred[o] = before > 0 ? col[i] : -1;
+        p.group_slot[o] = before > 0 ? eslot[i] : -1;
       }
-      const int i = lo - 1;
-      const size_t o = ((size_t)b * NP + pp) * G + r;
-      p.pred[o] = i >= beg ? col[i] : -1;
-      p.group_slot[o] = i >= beg ? eslot[i] : -1;
+      run += __popcll(bal);
     }
   }
   if (tid == 0 && p.stats != nullptr) {
@@ -369,10 +383,11 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p, int kL, int 
 
 hipError_t launch_select_full(const SelectArgs& a, int kL, int kM, int kH, hipStream_t s) {
   if (a.mask_in == nullptr) {
-    hipLaunchKernelGGL(select_rank_kernel, dim3(NP, a.B), dim3(1024), (size_t)a.C * sizeof(double), s, a);
+    const int nblk = (a.C + RANK_CHUNKS - 1) / RANK_CHUNKS;
+    hipLaunchKernelGGL(select_rank_kernel, dim3(nblk, NP, a.B), dim3(1024), (size_t)a.C * sizeof(double), s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(select_tier_kernel, dim3(a.B), dim3(64), 0, s, a, kL, kM, kH);
+    hipLaunchKernelGGL(select_tier_kernel, dim3(a.B), dim3(1024), 0, s, a, kL, kM, kH);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
