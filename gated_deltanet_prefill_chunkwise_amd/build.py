@@ -22,7 +22,10 @@ OUT = os.path.join(HERE, "libsgdn.so")
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.hip", "intra.hip", "hscan.hip", "ochunk.hip", "misc.hip", "select.hip"]
-EXTRA = {"select.hip": ["-ffp-contract=off"]}
+# hscan: products accumulate in ordinary vector registers (its state tiles are
+# also scaled and converted by vector instructions every event)
+EXTRA = {"select.hip": ["-ffp-contract=off"],
+         "hscan.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:

@@ -19,13 +19,15 @@ struct Plan {
   int kL, kM, kH;
   int Emax;        // event capacity per sequence inside prefill_sparse
   int snap_cap;    // snapshot slots per sequence (sparse) or per head (dense)
-  size_t off[24];
+  size_t off[32];
   size_t total;
 };
 
 enum Buf { B_G, B_GAMMA, B_P, B_U, B_W, B_CB, B_KT, B_SNAP, B_S0T, B_SCORE, B_ETA, B_RANK,
            B_TINFO, B_MASK, B_TIER, B_ROWPAIR, B_ROWPTR, B_COL, B_PRED, B_GSLOT, B_ESLOT,
-           B_WPK, B_STATS, B_COUNT };
+           B_WPK, B_STATS, B_FAC, B_REC, B_COUNT };
+
+static_assert(B_COUNT <= (int)(sizeof(Plan::off) / sizeof(size_t)), "workspace table too small");
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -91,6 +93,8 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
   memset(sz, 0, sizeof(sz));
   sz[B_G] = B * Nv * C * L * 4;
   sz[B_GAMMA] = B * Nv * C * 4;
+  sz[B_FAC] = B * Nv * C * L * 4;
+  sz[B_REC] = B * Nv * C * 16;   // sparse: B * Emax * 2 records, Emax <= NP * C
   sz[B_P] = B * Nv * (C + 1) * 8;
   sz[B_U] = B * Nv * C * L * DV * I;
   sz[B_KT] = B * p.Nq * C * DK * L * I;
@@ -149,6 +153,7 @@ IntraArgs intra_args(const Plan& pl, void* ws, const void* k, const void* v, con
   ia.B = pl.B; ia.T = pl.T; ia.Nq = pl.Nq; ia.Nv = pl.Nv; ia.C = pl.C; ia.solve = pl.solve;
   ia.g = at<float>(ws, pl, B_G);
   ia.gamma = at<float>(ws, pl, B_GAMMA);
+  ia.fac = at<float>(ws, pl, B_FAC);
   ia.U = at<void>(ws, pl, B_U);
   ia.W = sparse ? nullptr : at<void>(ws, pl, B_W);
   ia.Cb = sparse ? at<void>(ws, pl, B_CB) : nullptr;
@@ -217,9 +222,13 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
     S0PrepArgs sa{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv};
     SGDN_TRY(launch_s0prep(sa, pl.bf16, s));
   }
+  EvRecArgs ea{};
+  ea.gamma = at<float>(ws, pl, B_GAMMA); ea.rec = at<int32_t>(ws, pl, B_REC);
+  ea.B = pl.B; ea.Nv = pl.Nv; ea.C = pl.C; ea.sparse = 0;
+  SGDN_TRY(launch_evrec(ea, s));
   HScanArgs ha{};
   ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, B_W); ha.U = at<void>(ws, pl, B_U);
-  ha.g = at<float>(ws, pl, B_G); ha.gamma = at<float>(ws, pl, B_GAMMA); ha.P = nullptr;
+  ha.fac = at<float>(ws, pl, B_FAC); ha.rec = ea.rec; ha.P = nullptr;
   ha.s0 = s0; ha.s_final = s_final; ha.snap = at<void>(ws, pl, B_SNAP);
   ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 0;
   SGDN_TRY(launch_hscan(ha, pl.bf16, s));
@@ -327,9 +336,15 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
     S0PrepArgs s0a{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv};
     SGDN_TRY(launch_s0prep(s0a, pl.bf16, s));
   }
+  EvRecArgs ea{};
+  ea.gamma = at<float>(ws, pl, B_GAMMA); ea.P = at<double>(ws, pl, B_P);
+  ea.row_pair = sa.row_pair; ea.row_ptr = sa.row_ptr; ea.col = sa.col; ea.event_slot = sa.event_slot;
+  ea.rec = at<int32_t>(ws, pl, B_REC);
+  ea.B = pl.B; ea.Nv = pl.Nv; ea.C = pl.C; ea.Emax = Emax; ea.sparse = 1;
+  SGDN_TRY(launch_evrec(ea, s));
   HScanArgs ha{};
   ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, B_WPK); ha.U = at<void>(ws, pl, B_U);
-  ha.g = at<float>(ws, pl, B_G); ha.gamma = at<float>(ws, pl, B_GAMMA); ha.P = at<double>(ws, pl, B_P);
+  ha.fac = at<float>(ws, pl, B_FAC); ha.rec = ea.rec; ha.P = at<double>(ws, pl, B_P);
   ha.s0 = s0; ha.s_final = s_final; ha.snap = at<void>(ws, pl, B_SNAP);
   ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 1;
   ha.row_pair = sa.row_pair; ha.row_ptr = sa.row_ptr; ha.col = sa.col; ha.event_slot = sa.event_slot;

@@ -178,8 +178,11 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // operation (loads included), draining software-prefetched loads; kernels
 // whose global writes are not read back by other waves in the same launch use
 // this instead.
+// The explicit wait for this wave's outstanding LDS operations does not rely
+// on the fence's lowering, which can omit it for a barrier at a loop header.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt unconstrained
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }

@@ -8,51 +8,145 @@
 //
 // Value columns of S evolve independently (both equations act column-wise),
 // so one workgroup owns one 16-column slice of one head's 128x128 state and
-// walks that head's events in time.  Four waves split each step:
-//   W S    : wave w computes token rows 16w..16w+15 of U' (A = W blocks,
-//            B = S from its LDS copy, 4 k-steps over d)
-//   K^T X  : wave w updates state rows 32w..32w+31 (A = K^T blocks, B = X from
-//            LDS, 2 k-steps over tokens)
-// W and K^T are fragment-major in memory (one contiguous 1 KB read per
-// operand fragment) in a permuted reduction order; the LDS operands S and X
-// are read in the same order.  The operands of an event do not depend on the
-// state, so they are requested DEPTH events ahead into a ring of registers.
-// The fp32 state stays in registers.  Operands and stored intermediates use
-// the intermediate type I (fp16 for bf16 inputs, fp32 for fp32 inputs): the
-// LDS copy of S for the next W S, X for K^T X, U, U' and the snapshots.
+// walks that head's events in time.  Its compute wave holds the slice (eight
+// 16x16 fp32 tiles over the key rows) in registers, so both products feed
+// each other without leaving the wave:
+//   W S    : A = W blocks, B = the state tiles stacked in pairs (permuted
+//            reduction order, converted to the intermediate type)
+//   K^T X  : A = K^T blocks, B = the U' tiles stacked in pairs, scaled
+// The other waves keep the compute wave's instruction stream free of global
+// memory operations, which would queue behind the operand requests of the
+// CU:
+//   two loader waves stream each event's operands (W, K^T, the U slice, the
+//     per-token factors 2^(gamma - g) and a 16-byte event record) straight
+//     from global memory into a ring of LDS slots with the direct
+//     global-to-LDS loads of gfx950, DEPTH events ahead;
+//   a storer wave copies U' and the snapshots, which the compute wave leaves
+//     in a two-entry LDS staging ring, to global memory one event later.
+// One workgroup barrier per event hands a filled slot to the compute wave and
+// an emptied one back to the loaders.
+//
+// The gap factor that carries S to the next event is kept out of the state
+// registers: with S_true = F_in * S, the step forms U' = U - F_in (W S) and
+// S <- (2^gamma F_in) S + K^T X, so S is the true state after every update
+// (the snapshot) and one scaling per event remains.
 #include "common.h"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace sgdn {
 
 namespace {
 
-constexpr int PAD = 8;
-constexpr int SSTR = DK + PAD;  // LDS state copy [16 dv][dk]
-constexpr int XSTR = L + PAD;   // LDS X [16 dv][64 tokens]
-constexpr int EVT = 240;        // events per LDS metadata tile
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+typedef const __attribute__((address_space(4))) int32_t cint32;
 
-// 2^x for x <= 0 on the hardware exponential (results below 2^-126 flush to
-// zero, far below the fp32 terms they are added to).
-__device__ __forceinline__ float exp2_neg(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr int NLD = 2;          // loader waves
+constexpr int W_COMPUTE = 0;    // wave roles
+constexpr int W_STORER = 1 + NLD;
+constexpr int NWAVE = 2 + NLD;
 
+// One ring slot per event: W blocks, K^T blocks, the U slice [16 dv][64 t]
+// (rearranged for conflict-free reads), 64 factors 2^(gamma - g_t), and the
+// event record {F_in, 2^gamma F_in, snapshot index, chunk} (repeated).
+// Staging entry: U' (same arrangement as U), the snapshot [16 dv][128 dk] in
+// 16-byte units (8 keys of one value row), and {chunk, snapshot index}.
+template <typename I, bool PFON> struct Ring {
+  static constexpr int FB = 512 * (int)sizeof(I);   // one fragment block
+  static constexpr int W_OFF = 0;
+  static constexpr int K_OFF = 16 * FB;
+  static constexpr int U_OFF = 32 * FB;
+  static constexpr int U_BYTES = 16 * L * (int)sizeof(I);
+  static constexpr int F_OFF = U_OFF + U_BYTES;
+  static constexpr int R_OFF = F_OFF + 256;
+  static constexpr int BYTES = R_OFF + 256;
+  static constexpr int DEPTH = sizeof(I) == 2 ? 3 : 1;  // events requested ahead
+  static constexpr int NS = DEPTH + 1;
+  // copy units of one event: 1 KB pieces (16 bytes per lane), then the
+  // factors and the record (4 bytes per lane)
+  static constexpr int NW = 16 * FB / 1024;          // pieces of W (and of K^T)
+  static constexpr int NUS = U_BYTES / 1024;         // pieces of the U slice
+  static constexpr int NX4 = 2 * NW + NUS;
+  // L2 prefetch (fp16 operands): one scattered 4-byte request per
+  // event that touches this workgroup's share of the pair's W and K^T lines
+  // and its own U lines PF_AHEAD events before they are copied (its data lands
+  // in a scratch row).  The 16 workgroups of a pair request each line once
+  // between them, so the copies of the others hit in L2.
+  static constexpr bool PF = PFON;
+  static constexpr int PF_AHEAD = 6;
+  static constexpr int NU = NX4 + 2 + (PF ? 1 : 0);
+  static constexpr int PER = (NU + NLD - 1) / NLD;   // units per loader wave
+  // staging (the fp32 ring leaves no room: there the compute wave stores)
+  static constexpr bool STAGE = sizeof(I) == 2;
+  static constexpr int SN_BYTES = 16 * DK * (int)sizeof(I);
+  static constexpr int ST_SN = U_BYTES;
+  static constexpr int ST_HDR = ST_SN + SN_BYTES;
+  static constexpr int ST_BYTES = STAGE ? ST_HDR + 16 : 16;
+};
+
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Barrier of the loader waves: they write LDS only through the direct loads,
+// whose completion they have waited for, so no fence (which could also wait
+// for the requests still in flight) is needed.
+__device__ __forceinline__ void loader_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Barrier of the storer wave: its LDS reads are complete (so the compute wave
+// may refill the entry), while its global stores stay in flight (nothing in
+// this kernel reads them; a fence would wait for them and hold the compute
+// wave up).
+__device__ __forceinline__ void storer_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// direct global-to-LDS loads: lane l's 16 (4) bytes land at lds + 16 l (4 l)
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)lds, 4, 0, 0);
+}
+
+// Byte offset of lane (n, g)'s 4 values of token tile i in a U slice
+// [16 dv][64 t] as the ring holds it.  fp16: 16-byte unit 32 i + 16 (g >> 1)
+// + n holds tokens 16 i + 8 (g >> 1) .. + 7 of row n; fp32: unit
+// 64 i + 16 g + n holds tokens 16 i + 4 g .. + 3 of row n.
+template <typename I> __device__ __forceinline__ int u_off(int i, int n, int g) {
+  if constexpr (sizeof(I) == 2) return (32 * i + 16 * (g >> 1) + n) * 16 + 8 * (g & 1);
+  else return (64 * i + 16 * g + n) * 16;
+}
+// Element offset (within the [16 dv][64 t] slice in global memory) of the
+// 16-byte unit P of that arrangement.
+template <typename I> __device__ __forceinline__ int u_unit(int P) {
+  if constexpr (sizeof(I) == 2) return (P & 15) * L + 16 * (P >> 5) + 8 * ((P >> 4) & 1);
+  else return (P & 15) * L + 16 * (P >> 6) + 4 * ((P >> 4) & 3);
+}
+
+// (two waves per SIMD for the register budget: at most 256 registers per
+// lane, so the products accumulate in ordinary vector registers; the LDS ring
+// keeps one workgroup per CU)
 template <typename E, bool SPARSE>
-__global__ __launch_bounds__(256, 1) void hscan_kernel(HScanArgs p) {
-  // events whose operands are in flight: 10 loads per event and wave, so the
-  // ring plus the stores stays below the 63 vector-memory operations a wave
-  // can count (fp32 intermediates are twice as large: a shorter ring)
-  constexpr int DEPTH = sizeof(E) == 2 ? 4 : 2;
-  static_assert(EVT % DEPTH == 0, "buffer ring must align with the tiles");
+__global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
   using I = inter_t<E>;
-  __shared__ __align__(16) I sS[16 * SSTR];
-  __shared__ __align__(16) I sX[16 * XSTR];
-  // event metadata of the current tile: chunk retention gamma; sparse also
-  // chunk, snapshot slot and gap factor (chunk indices also for the DEPTH
-  // events past the tile)
-  __shared__ float sEvGam[EVT];
-  __shared__ int sEvC[SPARSE ? EVT + DEPTH : 1];
-  __shared__ int sEvSlot[SPARSE ? EVT : 1];
-  __shared__ float sEvF[SPARSE ? EVT : 1];
+  using R = Ring<I, sizeof(I) == 2>;
+  constexpr int D = R::DEPTH, NS = R::NS;
+  __shared__ __align__(16) char ring[NS * R::BYTES];
+  __shared__ __align__(16) char stage[2 * R::ST_BYTES];
+  __shared__ __align__(16) char pf_sink[256];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -62,9 +156,10 @@ __global__ __launch_bounds__(256, 1) void hscan_kernel(HScanArgs p) {
   const int G = (C + 1) / 2;
 
   // Block -> (row, batch, head-in-pair, slice).  The 16 workgroups of one
-  // head pair (2 heads x 8 slices) share K^T and W tiles, so they are placed
-  // on one XCD (workgroups are dealt to the 8 XCDs round-robin); rows are
-  // dispatched in order, so the longest (High-tier) chains start first.
+  // head pair (2 heads x 8 slices) share K^T tiles and each head's 8 share W,
+  // so they are placed on one XCD (workgroups are dealt to the 8 XCDs
+  // round-robin); rows are dispatched in order, so the longest (High-tier)
+  // chains start first.
   const int id = blockIdx.x, nblk = gridDim.x;
   int pg, local;
   if ((nblk & 127) == 0) {
@@ -86,204 +181,264 @@ __global__ __launch_bounds__(256, 1) void hscan_kernel(HScanArgs p) {
     i1 = p.row_ptr[b * (NP + 1) + row + 1];
   }
   const int32_t* colb = SPARSE ? p.col + (size_t)b * p.Emax : nullptr;
-  const int32_t* slotb = SPARSE ? p.event_slot + (size_t)b * p.Emax : nullptr;
   const size_t bh = (size_t)b * Nv + h;
-  const double* P = SPARSE ? p.P + bh * (C + 1) : nullptr;
+  I* Ubase = static_cast<I*>(p.U);
+  I* snap = static_cast<I*>(p.snap);
+  const int snap_cap = SPARSE ? p.snap_cap : G - 1;
+  auto snap_at = [&](int si) __attribute__((always_inline)) {
+    return SPARSE ? snap + (((size_t)b * p.snap_cap + si) * 2 + hh) * DV * DK
+                  : snap + (bh * (G - 1) + si) * DV * DK;
+  };
 
-  // Stage the metadata of events [t0, t0 + EVT): gamma, and (sparse) chunk
-  // index, snapshot slot and the gap factor 2^(P_next - P_{c+1}) that carries
-  // S_{c+1} to the next event (Eq. (21)); the last event carries it to the end
-  // of the sequence.  Chunk indices are staged DEPTH events further for the
-  // operand requests.  Read from LDS, the per-event scalars stay out of the
-  // vector-memory wait counts.
-  auto stage_meta = [&](int t0) __attribute__((always_inline)) {
-    for (int e = tid; e < EVT + DEPTH; e += 256) {
-      const int i = t0 + e;
-      if (i < i1) {
-        const int c = SPARSE ? colb[i] : i;
-        if (SPARSE) sEvC[e] = c;
-        if (e < EVT) {
-          sEvGam[e] = p.gamma[bh * C + c];
-          if (SPARSE) {
-            sEvSlot[e] = slotb[i];
-            const int cn = (i + 1 < i1) ? colb[i + 1] : C;
-            sEvF[e] = exp2f((float)(P[cn] - P[c + 1]));
-          }
+  if (w == W_STORER) {
+    // ======================= storer wave =======================
+    // copy staging entry e (U' and the snapshot of one event) to global memory
+    auto copy_out = [&](int e) __attribute__((always_inline)) {
+      const char* st = stage + e * R::ST_BYTES;
+      const int2 hd = *reinterpret_cast<const int2*>(st + R::ST_HDR);
+      // (clamped like the compute wave's record fields: no staging content
+      // can address memory outside U and the snapshots)
+      const int c = min(max(__builtin_amdgcn_readfirstlane(hd.x), 0), C - 1);
+      const int sn = __builtin_amdgcn_readfirstlane(hd.y);
+      const int si = (sn >= 0 && sn < snap_cap) ? sn : -1;
+      I* Ug = Ubase + (bh * C + c) * DV * L + dv0 * L;
+#pragma unroll
+      for (int r = 0; r < R::U_BYTES / 1024; ++r) {
+        const int P = 64 * r + lane;
+        stv(Ug + u_unit<I>(P), ldv(st + P * 16));
+      }
+      if (si >= 0) {
+        I* sp = snap_at(si) + dv0 * DK;
+#pragma unroll
+        for (int r = 0; r < R::SN_BYTES / 1024; ++r) {
+          const int P = 64 * r + lane;   // unit (8 keys c8 = P >> 4, row n = P & 15)
+          stv(sp + (P & 15) * DK + 8 * (P >> 4), ldv(st + R::ST_SN + P * 16));
         }
       }
+    };
+    for (int j = i0; j < i1; ++j) {
+      storer_barrier();   // the compute wave has left event j - 1 in staging
+      if (R::STAGE && j > i0) copy_out((j - 1 - i0) & 1);
     }
-    __syncthreads();
-  };
-  int t0 = i0;
-  auto chunk_at = [&](int i) __attribute__((always_inline)) { return SPARSE ? sEvC[i - t0] : i; };
+    storer_barrier();     // the compute wave is done
+    if (R::STAGE && i1 > i0) copy_out((i1 - 1 - i0) & 1);
+    return;
+  }
 
-  // ---- initial state rows 32w + 16tt + 4g + j of column dv0 + n: s0 decayed
-  //      over the chunks before the first event
-  f32x4 S[2];
+  if (w != W_COMPUTE) {
+    // ======================= loader waves =======================
+    const int k = w - 1;
+    // event chunks are read through the scalar cache (constant address space:
+    // the event list is not written during the kernel), so their waits never
+    // mix with the counted direct loads
+    const cint32* colc = (const cint32*)(colb);
+    auto col_at = [&](int e) __attribute__((always_inline)) {
+      return SPARSE ? colc[__builtin_amdgcn_readfirstlane(e)] : e;
+    };
+    const I* Wbase = static_cast<const I*>(p.W);
+    const I* KTbase = static_cast<const I*>(p.KT);
+    // L2 prefetch of event e (clamped to the row): lanes 0-15 the 16 W lines
+    // of this slice's share of the head's tile, 16-23 this workgroup's 8 of
+    // the pair's 128 K^T lines, 24-39 the 16 lines of its U slice, 40-41 the
+    // factors, the rest repeat lane 0
+    auto prefetch = [&](int e) __attribute__((always_inline)) {
+      e = e < i1 ? e : i1 - 1;
+      const int c = col_at(e);
+      const size_t hc = bh * C + c;
+      const char* Wt = reinterpret_cast<const char*>(
+          SPARSE ? Wbase + (((size_t)b * p.Emax + e) * 2 + hh) * L * DK : Wbase + hc * L * DK);
+      const char* Kt = reinterpret_cast<const char*>(KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L);
+      const char* Ut = reinterpret_cast<const char*>(Ubase + hc * DV * L + dv0 * L);
+      const char* src = Wt + slice * 16 * 128;
+      if (lane < 16) src = Wt + (slice * 16 + lane) * 128;
+      else if (lane < 24) src = Kt + ((hh * 8 + slice) * 8 + lane - 16) * 128;
+      else if (lane < 40) src = Ut + (lane - 24) * 128;
+      else if (lane < 42) src = reinterpret_cast<const char*>(p.fac + hc * L) + (lane - 40) * 128;
+      dma4(src, pf_sink);
+    };
+    // copy units [u0, u1) of event j (chunk c) into slot s
+    auto issue = [&](int j, int c, int s, int u0, int u1) __attribute__((always_inline)) {
+      const size_t hc = bh * C + c;
+      const char* Wt = reinterpret_cast<const char*>(
+          SPARSE ? Wbase + (((size_t)b * p.Emax + j) * 2 + hh) * L * DK : Wbase + hc * L * DK);
+      const char* Kt = reinterpret_cast<const char*>(KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L);
+      const I* Ut = Ubase + hc * DV * L + dv0 * L;
+      const int32_t* rec = SPARSE ? p.rec + (((size_t)b * p.Emax + j) * 2 + hh) * 4 : p.rec + hc * 4;
+      char* sl = ring + s * R::BYTES;
+#pragma unroll
+      for (int u = u0; u < u1; ++u) {
+        if (u < R::NW) {
+          dma16(Wt + u * 1024 + lane * 16, sl + R::W_OFF + u * 1024);
+        } else if (u < 2 * R::NW) {
+          dma16(Kt + (u - R::NW) * 1024 + lane * 16, sl + R::K_OFF + (u - R::NW) * 1024);
+        } else if (u < R::NX4) {
+          const int r = u - 2 * R::NW;
+          dma16(Ut + u_unit<I>(64 * r + lane), sl + R::U_OFF + r * 1024);
+        } else if (u == R::NX4) {
+          dma4(p.fac + hc * L + lane, sl + R::F_OFF);
+        } else if (u == R::NX4 + 1) {
+          dma4(rec + (lane & 3), sl + R::R_OFF);
+        } else {
+          prefetch(j + R::PF_AHEAD);
+        }
+      }
+    };
+    // per-loader unit ranges are compile-time constants, so every loop above
+    // unrolls into straight-line requests
+    auto run = [&](auto kc) __attribute__((always_inline)) {
+      constexpr int K = decltype(kc)::value;
+      constexpr int U0 = K * R::PER;
+      constexpr int U1 = (K + 1) * R::PER < R::NU ? (K + 1) * R::PER : R::NU;
+      constexpr int CNT = U1 - U0;
+      if (i0 < i1) {
+        const int npro = (i1 - i0 < D) ? i1 - i0 : D;
+#pragma unroll
+        for (int e = 0; e < D; ++e)
+          if (e < npro) issue(i0 + e, col_at(i0 + e), e, U0, U1);
+        if (npro == D) wait_vm<CNT * (D - 1)>();
+        else wait_vm<0>();
+      }
+      // sparse: the chunk of the next request is read one event early, so
+      // that its load latency is not paid between barrier and request
+      const int jlast = i1 > i0 ? i1 - 1 : i0;
+      int cnext = col_at(min(i0 + D, jlast));
+      int s = D;   // slot of event j + D
+      for (int j = i0; j < i1; ++j) {
+        loader_barrier();   // event j handed over; slot of j - 1 emptied
+        if (j + D < i1) {
+          const int c = cnext;
+          cnext = col_at(min(j + D + 1, jlast));
+          issue(j + D, c, s, U0, U1);
+          wait_vm<CNT * (D - 1)>();   // event j + 1 complete
+        } else {
+          wait_vm<0>();
+        }
+        s = (s + 1 == NS) ? 0 : s + 1;
+      }
+      loader_barrier();
+    };
+    static_assert(NLD == 2, "one branch per loader wave");
+    if (k == 0) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+    return;
+  }
+
+  // ======================= compute wave =======================
+  const double* P = SPARSE ? p.P + bh * (C + 1) : nullptr;
+
+  // initial state rows 16 mt + 4 g + j of column dv0 + n: s0 decayed over the
+  // chunks before the first event
+  f32x4 S[8];
   {
     float f0 = 1.f;
     if constexpr (SPARSE) f0 = exp2f((float)P[(i0 < i1) ? colb[i0] : C]);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int dk = 32 * w + 16 * tt + 4 * g4 + j;
-        S[tt][j] = p.s0 ? f0 * p.s0[(bh * DK + dk) * DV + dv0 + n16] : 0.f;
+        const int dk = 16 * mt + 4 * g4 + j;
+        S[mt][j] = p.s0 ? f0 * p.s0[(bh * DK + dk) * DV + dv0 + n16] : 0.f;
       }
-      st4<I>(&sS[n16 * SSTR + 32 * w + 16 * tt + 4 * g4], S[tt]);
-    }
-    // the initial state is complete before any operand request, so the loop
-    // never waits on these loads
-    __builtin_amdgcn_s_waitcnt(0);
   }
-  stage_meta(t0);
+  frag_t<I> Sf[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) Sf[q] = pack44<I>(S[2 * q], S[2 * q + 1]);
 
-  const I* Wbase = static_cast<const I*>(p.W);
-  const I* KTbase = static_cast<const I*>(p.KT);
-  I* Ubase = static_cast<I*>(p.U);
-  I* snap = static_cast<I*>(p.snap);
+  int s = 0;
+  for (int j = i0; j < i1; ++j) {
+    lds_barrier();   // the slot of event j is filled; staging entry free
+    const char* sl = ring + s * R::BYTES;
+    char* st = stage + ((j - i0) & 1) * R::ST_BYTES;
+    const int4 rc = *reinterpret_cast<const int4*>(sl + R::R_OFF);
+    const float fin = __int_as_float(__builtin_amdgcn_readfirstlane(rc.x));
+    const float decf = __int_as_float(__builtin_amdgcn_readfirstlane(rc.y));
+    // (chunk and snapshot index are clamped to their ranges, so that no
+    // record content can address memory outside U and the snapshots)
+    const int sn = __builtin_amdgcn_readfirstlane(rc.z);
+    const int snapi = (sn >= 0 && sn < snap_cap) ? sn : -1;
+    const int c = min(max(__builtin_amdgcn_readfirstlane(rc.w), 0), C - 1);
+    const I* Ws = reinterpret_cast<const I*>(sl + R::W_OFF);
+    const I* Ks = reinterpret_cast<const I*>(sl + R::K_OFF);
 
-  // Operands of one event for this wave.
-  struct Ops {
-    frag_t<I> wf[4];      // W blocks (dk step q, token tile w)
-    frag_t<I> kf[2][2];   // K^T blocks (dk tile 2w + tt, token step ks)
-    half_t<I> u;          // U of tokens 16w + 4g .. 16w + 4g + 3
-    f32x4 gv;             // g of the same tokens
-    int c;
-  };
-  auto load = [&](int i, int c, Ops& o) __attribute__((always_inline)) {
-    const size_t hc = bh * C + c;
-    const I* Wt = SPARSE ? Wbase + (((size_t)b * p.Emax + i) * 2 + hh) * L * DK
-                         : Wbase + hc * L * DK;
-    const I* KTt = KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L;
+    // ---- U' = U - F_in W S   (Eq. (1)) and
+    //      S <- 2^gamma F_in S + K^T (U' 2^(gamma - g))   (Eq. (2)),
+    // in token halves so that each half's vector work overlaps the products
+    // of the next: W S of tiles 2-3 runs beside U' and X of tiles 0-1, K^T X
+    // over tokens 0-31 beside U' and X of tiles 2-3
+    auto ws_pair = [&](int i, f32x4& a0, f32x4& a1) __attribute__((always_inline)) {
+      a0 = zero4();
+      a1 = zero4();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) o.wf[q] = ld8(Wt + wblk(q, w) + 8 * lane);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) o.kf[tt][ks] = ld8(KTt + kblk(2 * w + tt, ks) + 8 * lane);
-    o.u = *reinterpret_cast<const half_t<I>*>(Ubase + hc * DV * L + (dv0 + n16) * L + 16 * w + 4 * g4);
-    o.gv = *reinterpret_cast<const f32x4*>(p.g + hc * L + 16 * w + 4 * g4);
-    o.c = c;
-  };
-  // Request event i's operands (past the last event: the last event again,
-  // unconditionally, so that no branch merges the wait counts into a drain).
-  // sEvC holds EVT + DEPTH entries, so i - t0 < EVT + DEPTH is always staged.
-  auto request = [&](int i, Ops& o) __attribute__((always_inline)) {
-    const int in = i < i1 ? i : i1 - 1;
-    load(in, chunk_at(in), o);
-  };
-
-  // One event step on the operands in `cur`; ends by requesting event
-  // i + DEPTH into the same buffer.
-  auto step = [&](int i, Ops& cur) __attribute__((always_inline)) {
-    const int c = cur.c;
-    const size_t hc = bh * C + c;
-    const float gam = sEvGam[i - t0];
-
-    // ---- U' = U - W S   (Eq. (1)); S read in the blocks' permuted order
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const I* sr = &sS[n16 * SSTR + 32 * q + 4 * g4];
-      acc = mma(cur.wf[q], ld44(sr, sr + 16), acc);
-    }
-    f32x4 up, x;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      up[j] = to_f(cur.u[j]) - acc[j];
-      x[j] = up[j] * exp2_neg(gam - cur.gv[j]);
-    }
-    st4<I>(Ubase + hc * DV * L + (dv0 + n16) * L + 16 * w + 4 * g4, up);
-    st4<I>(&sX[n16 * XSTR + 16 * w + 4 * g4], x);
-    lds_barrier();
-
-    // ---- S <- 2^gamma S + K^T (U' * 2^(gamma - g))   (Eq. (2)); X read in
-    //      the K^T blocks' permuted token order
-    const float dec = exp2_neg(gam);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      f32x4 d = S[tt] * dec;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const I* xr = &sX[n16 * XSTR + 32 * ks + 4 * g4];
-        d = mma(cur.kf[tt][ks], ld44(xr, xr + 16), d);
+      for (int q = 0; q < 4; ++q) {
+        a0 = mma(ld8(Ws + wblk(q, i) + 8 * lane), Sf[q], a0);
+        a1 = mma(ld8(Ws + wblk(q, i + 1) + 8 * lane), Sf[q], a1);
       }
-      S[tt] = d;
-    }
-    // the request reuses cur's registers: keep it after their last use, so the
-    // buffers stay in place (a copy of an in-flight register forces a drain)
-    __builtin_amdgcn_sched_barrier(0);
-    request(i + DEPTH, cur);
+    };
+    auto ux = [&](int i, const f32x4& a) __attribute__((always_inline)) {
+      const half_t<I> u = *reinterpret_cast<const half_t<I>*>(sl + R::U_OFF + u_off<I>(i, n16, g4));
+      const f32x4 fc = *reinterpret_cast<const f32x4*>(sl + R::F_OFF + (16 * i + 4 * g4) * 4);
+      f32x4 up, x;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        up[jj] = to_f(u[jj]) - fin * a[jj];
+        x[jj] = up[jj] * fc[jj];
+      }
+      if constexpr (R::STAGE)
+        st4<I>(reinterpret_cast<I*>(st + u_off<I>(i, n16, g4)), up);
+      else
+        st4<I>(Ubase + (bh * C + c) * DV * L + (dv0 + n16) * L + 16 * i + 4 * g4, up);
+      return x;
+    };
+    f32x4 a0, a1, a2, a3;
+    ws_pair(0, a0, a1);
+    ws_pair(2, a2, a3);
+    const frag_t<I> X0 = pack44<I>(ux(0, a0), ux(1, a1));
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) S[mt] = mma(ld8(Ks + kblk(mt, 0) + 8 * lane), X0, S[mt] * decf);
+    const frag_t<I> X1 = pack44<I>(ux(2, a2), ux(3, a3));
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) S[mt] = mma(ld8(Ks + kblk(mt, 1) + 8 * lane), X1, S[mt]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Sf[q] = pack44<I>(S[2 * q], S[2 * q + 1]);
 
-    // ---- compact snapshot of S_{c+1} if an output group starts from it
-    I* sp = nullptr;
-    if constexpr (SPARSE) {
-      const int es = sEvSlot[i - t0];
-      if (es >= 0) sp = snap + (((size_t)b * p.snap_cap + es) * 2 + hh) * DV * DK;
-    } else {
-      if ((c & 1) && c + 1 < C) sp = snap + (bh * (G - 1) + (c + 1) / 2 - 1) * DV * DK;
+    // ---- compact snapshot of S_{c+1} if an output group starts from it:
+    //      lane (n, g) holds keys 32 q + 4 g .. + 3 and 32 q + 16 + 4 g .. + 3
+    if constexpr (R::STAGE) {
+      if (snapi >= 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int hi = 0; hi < 2; ++hi) {
+            const int c8 = 4 * q + 2 * hi + (g4 >> 1);
+            const half_t<I> v = hi ? __builtin_shufflevector(Sf[q], Sf[q], 4, 5, 6, 7)
+                                   : __builtin_shufflevector(Sf[q], Sf[q], 0, 1, 2, 3);
+            *reinterpret_cast<half_t<I>*>(st + R::ST_SN + (c8 * 16 + n16) * 16 + 8 * (g4 & 1)) = v;
+          }
+      }
+      if (lane == 0) *reinterpret_cast<int2*>(st + R::ST_HDR) = make_int2(c, snapi);
+    } else if (snapi >= 0) {
+      I* sp = snap_at(snapi) + (dv0 + n16) * DK + 4 * g4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        *reinterpret_cast<half_t<I>*>(sp + 32 * q) = __builtin_shufflevector(Sf[q], Sf[q], 0, 1, 2, 3);
+        *reinterpret_cast<half_t<I>*>(sp + 32 * q + 16) = __builtin_shufflevector(Sf[q], Sf[q], 4, 5, 6, 7);
+      }
     }
-    if (sp != nullptr) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) st4<I>(sp + (dv0 + n16) * DK + 32 * w + 16 * tt + 4 * g4, S[tt]);
-    }
-
-    // ---- gap to the next event (Eq. (21)): S_next = 2^(P_next - P_{c+1}) S
-    if constexpr (SPARSE) {
-      const float f = sEvF[i - t0];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) S[tt] *= f;
-    }
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) st4<I>(&sS[n16 * SSTR + 32 * w + 16 * tt + 4 * g4], S[tt]);
-    lds_barrier();
-  };
-
-  Ops buf[DEPTH];
-  if (i0 < i1) {
-#pragma unroll
-    for (int k = 0; k < DEPTH; ++k) request(i0 + k, buf[k]);
+    s = (s + 1 == NS) ? 0 : s + 1;
   }
-  // One metadata tile of EVT events per outer pass (EVT is a multiple of
-  // DEPTH, so event i0 + k + n DEPTH always sits in buffer k).  The next tile
-  // is staged at the end of a pass (the barrier that ends every step
-  // guarantees nobody still reads the old one).  Only the last tile can end in
-  // a partial group, so the way back to the event loop never follows
-  // remainder steps (whose requests would look like the newest loads to the
-  // wait-count analysis).
-  auto run = [&](int ts, int te, bool last) __attribute__((always_inline)) {
-    // whole groups of DEPTH events: straight-line steps, no guards
-    int i = ts;
-    for (; i + DEPTH <= te; i += DEPTH) {
-#pragma unroll
-      for (int k = 0; k < DEPTH; ++k) step(i + k, buf[k]);
-    }
-    if (last) {
-      // the remaining 0 .. DEPTH-1 events; only the last tile has any
-#pragma unroll
-      for (int k = 0; k < DEPTH - 1; ++k)
-        if (i + k < te) step(i + k, buf[k]);
-    }
-  };
-  // (one call site: a second copy of the event loop would get its own
-  // register assignment and copies of in-flight buffers)
-  for (int ts = i0; ts < i1;) {
-    const int te = (i1 - ts < EVT) ? i1 : ts + EVT;
-    const bool last = te >= i1;
-    run(ts, te, last);
-    if (last) break;
-    t0 = ts = te;
-    stage_meta(t0);
-  }
+  lds_barrier();   // the last staging entry is complete
 
   if (p.s_final != nullptr) {
+    // gap from the last event to the end of the sequence
+    float fl = 1.f;
+    if constexpr (SPARSE)
+      if (i1 > i0) fl = exp2f((float)(P[C] - P[colb[i1 - 1] + 1]));
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int dk = 32 * w + 16 * tt + 4 * g4 + j;
-        p.s_final[(bh * DK + dk) * DV + dv0 + n16] = S[tt][j];
+        const int dk = 16 * mt + 4 * g4 + j;
+        p.s_final[(bh * DK + dk) * DV + dv0 + n16] = fl * S[mt][j];
       }
   }
 }
@@ -291,7 +446,7 @@ __global__ __launch_bounds__(256, 1) void hscan_kernel(HScanArgs p) {
 template <typename E, bool SPARSE>
 hipError_t launch_one(const HScanArgs& a, hipStream_t s) {
   const int nblk = a.B * (a.Nv / 2) * 16;
-  hipLaunchKernelGGL((hscan_kernel<E, SPARSE>), dim3(nblk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((hscan_kernel<E, SPARSE>), dim3(nblk), dim3(64 * NWAVE), 0, s, a);
   return hipGetLastError();
 }
 

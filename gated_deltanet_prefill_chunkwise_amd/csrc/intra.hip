@@ -233,6 +233,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
       const size_t hc = (size_t)(b * Nv + h) * C + c;
       p.g[hc * L + lane] = x;
       if (lane == 63) p.gamma[hc] = x;
+      // row factors 2^(gamma - g_t) of the H scan's K^T X
+      p.fac[hc * L + lane] = exp2f(__shfl(x, 63, 64) - x);
     }
     lds_barrier();
     // next item's keys, first-head values and gates (registers are free now)

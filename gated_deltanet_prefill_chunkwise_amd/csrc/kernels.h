@@ -10,6 +10,7 @@ namespace sgdn {
 // Workspace tensors (all per batch b, head-major).  I is the intermediate
 // element type: fp16 for bf16 inputs, fp32 for fp32 inputs.
 //   g      [B][Nv][C][64]      fp32  in-chunk inclusive log2 decay
+//   fac    [B][Nv][C][64]      fp32  2^(gamma - g_t), the K^T X row factors
 //   gamma  [B][Nv][C]          fp32  chunk retention g[63]
 //   P      [B][Nv][C+1]        fp64  prefix of gamma
 //   U      [B][Nv][C][dv][64]  I     U (then U' in place), dv-major tiles
@@ -19,6 +20,8 @@ namespace sgdn {
 //   snap   [..][dv][dk]        I     compact state snapshots (transposed)
 //   s0T    [B][Nv][dv][dk]     I     initial state, transposed
 //   Wpk    [B][Emax][2][8192]  I     deferred W of kept events, fragment-major
+//   rec    dense [B][Nv][C], sparse [B][Emax][2]: int4 event records
+//          {F_in, 2^gamma F_in (fp32 bits), snapshot index or -1, chunk}
 //
 // Fragment-major tiles: 16 blocks of 512 elements, block = one 64-lane MFMA
 // operand fragment (lane l = 16 g + n holds 8 consecutive elements), so a wave
@@ -32,7 +35,7 @@ namespace sgdn {
 struct IntraArgs {
   const void* k; const void* v; const float* a; const void* beta;
   int B, T, Nq, Nv, C, solve;
-  float* g; float* gamma;
+  float* g; float* gamma; float* fac;
   void* U; void* W; void* Cb; void* KT;
   float* score;
 };
@@ -46,7 +49,7 @@ struct PrefixArgs {
 // Sparse: events from the CSR rows, W packed per event.
 struct HScanArgs {
   const void* KT; const void* W; void* U;
-  const float* g; const float* gamma; const double* P;
+  const float* fac; const int32_t* rec; const double* P;
   const float* s0;          // [B][Nv][dk][dv] or null
   float* s_final;           // [B][Nv][dk][dv] or null
   void* snap;               // snapshots
@@ -70,6 +73,16 @@ struct OChunkArgs {
   const int32_t* pred;        // [B][NP][G]
   const int32_t* group_slot;  // [B][NP][G]
   int snap_cap;
+};
+
+// Per-event records of the H scan: the gap factor F_in that carries the state
+// from the previous event of the row to this one, the step factor
+// 2^gamma F_in, the snapshot index and the chunk.
+struct EvRecArgs {
+  const float* gamma; const double* P;
+  const int32_t* row_pair; const int32_t* row_ptr; const int32_t* col; const int32_t* event_slot;
+  int32_t* rec;
+  int B, Nv, C, Emax, sparse;
 };
 
 struct S0PrepArgs { const float* s0; void* s0T; int B, Nv; };
@@ -101,6 +114,7 @@ hipError_t launch_intra(const IntraArgs& a, int bf16, hipStream_t s);
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s);
 hipError_t launch_hscan(const HScanArgs& a, int bf16, hipStream_t s);
 hipError_t launch_ochunk(const OChunkArgs& a, int bf16, hipStream_t s);
+hipError_t launch_evrec(const EvRecArgs& a, hipStream_t s);
 hipError_t launch_s0prep(const S0PrepArgs& a, int bf16, hipStream_t s);
 hipError_t launch_gate(const GateArgs& a, int bf16, hipStream_t s);
 hipError_t launch_select_full(const SelectArgs& a, int kL, int kM, int kH, hipStream_t s);

@@ -114,6 +114,47 @@ __global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
   }
 }
 
+// Event records of the H scan (SparseGDN reading notes, Sec. 2.1 Eq. (2) and
+// Sec. 2.6 Eq. (21)).  Dense: every chunk is an event, F_in = 1, and the state
+// after odd chunk c (c + 1 < C) is the snapshot (c + 1) / 2 - 1 of the group
+// that starts at chunk c + 1.  Sparse: one record per kept event and head of
+// the pair; F_in = 2^(P_c - P_{e+1}) joins the previous kept event e of the
+// row (1 for the first event, whose gap the initial state already carries).
+__global__ __launch_bounds__(256) void evrec_dense_kernel(EvRecArgs p) {
+  const size_t n = (size_t)p.B * p.Nv * p.C;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int c = (int)(i % p.C);
+  int4 r;
+  r.x = __float_as_int(1.f);
+  r.y = __float_as_int(exp2f(p.gamma[i]));
+  r.z = ((c & 1) && c + 1 < p.C) ? (c + 1) / 2 - 1 : -1;
+  r.w = c;
+  reinterpret_cast<int4*>(p.rec)[i] = r;
+}
+
+__global__ __launch_bounds__(256) void evrec_sparse_kernel(EvRecArgs p) {
+  const int row = blockIdx.x, b = blockIdx.y, NP = p.Nv / 2;
+  const int beg = p.row_ptr[b * (NP + 1) + row], end = p.row_ptr[b * (NP + 1) + row + 1];
+  const int pr = p.row_pair[b * NP + row];
+  const int32_t* col = p.col + (size_t)b * p.Emax;
+  for (int i = beg + (int)threadIdx.x; i < end; i += 256) {
+    const int c = col[i];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const size_t bh = (size_t)b * p.Nv + 2 * pr + hh;
+      const double* P = p.P + bh * (p.C + 1);
+      const float fin = (i > beg) ? exp2f((float)(P[c] - P[col[i - 1] + 1])) : 1.f;
+      int4 r;
+      r.x = __float_as_int(fin);
+      r.y = __float_as_int(exp2f(p.gamma[bh * p.C + c]) * fin);
+      r.z = p.event_slot[(size_t)b * p.Emax + i];
+      r.w = c;
+      reinterpret_cast<int4*>(p.rec)[((size_t)b * p.Emax + i) * 2 + hh] = r;
+    }
+  }
+}
+
 // U tiles [dv][t] (intermediate type) -> token-major fp32 [t][dv] copy for
 // the debug output.
 template <typename I>
@@ -130,6 +171,16 @@ __global__ __launch_bounds__(256) void debug_u_kernel(const void* Ut_, float* U)
 
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(prefix_kernel, dim3(a.B * a.Nv), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_evrec(const EvRecArgs& a, hipStream_t s) {
+  if (a.sparse) {
+    hipLaunchKernelGGL(evrec_sparse_kernel, dim3(a.Nv / 2, a.B), dim3(256), 0, s, a);
+  } else {
+    const size_t n = (size_t)a.B * a.Nv * a.C;
+    hipLaunchKernelGGL(evrec_dense_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
