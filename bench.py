@@ -73,20 +73,24 @@ class Hip:
 
 
 def algorithmic_bytes_per_token(stage: str, mode: str, sigma: float, keep: float) -> float:
-    """Bytes per token of the I/O streams a stage must move (bf16 inputs,
-    fp32 outputs and snapshots); pipeline intermediates are not counted."""
+    """Bytes per token of the I/O streams a stage must move: bf16 Q, K, V, a
+    (fp32) and beta, fp32 O, and the fp16 group snapshots (one 128x128 state
+    per head per two chunks, written by the H scan and read by O); pipeline
+    intermediates (U, U', W or Cb, K^T tiles) are not counted."""
     k_in = NQ * D * 2           # K (shared by a head pair)
     q_in = NQ * D * 2
     v_in = NV * D * 2
     o_out = NV * D * 4          # fp32 O
     a_b = NV * 4 + NV * 2       # a (fp32) + beta (bf16)
-    snap = NV * D * D * 4 / 128  # one fp32 128x128 snapshot per head per two chunks
+    snap = NV * D * D * 2 / 128 * (sigma if mode == "sparse" else 1.0)   # one direction
     if stage == "intra":
         return k_in + v_in + a_b
     if stage == "hscan":
-        return k_in * (keep if mode == "sparse" else 1.0) + snap * (sigma if mode == "sparse" else 1.0)
+        return k_in * (keep if mode == "sparse" else 1.0) + snap
     if stage == "o":
-        return q_in + o_out + snap * (sigma if mode == "sparse" else 1.0)
+        return q_in + k_in + o_out + snap
+    if stage == "path":
+        return q_in + k_in + v_in + a_b + o_out + 2 * snap
     return 0.0
 
 
@@ -241,6 +245,17 @@ def main():
                     unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     algorithmic_bytes_per_launch=int(alg), launch_ms=round(st[dom], 4))
 
+    def path_roofline(mode):
+        """The whole layer against HBM: I/O streams plus snapshots over the
+        measured time per layer."""
+        per_layer_ms = res[mode]["ms_per_step"] / args.layers
+        alg = algorithmic_bytes_per_token("path", mode, sigma, keep) * B * Tn
+        achieved = alg / (per_layer_ms / 1e3) / 1e9
+        return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), algorithmic_bytes_per_layer=int(alg),
+                    ms_per_layer=round(per_layer_ms, 4),
+                    roofline_ms_per_layer=round(alg / (HBM_PEAK_GBS * 1e9) * 1e3, 4))
+
     out = {
         "metric": "GDN-core prefill tokens/s at T=32K/128K, dense vs 29% events; % roofline",
         "value": round(value, 1),
@@ -261,7 +276,7 @@ def main():
                      "per_layer_tok_s": round(B * Tn / (rr["ms_per_step"] / 1e3 / args.layers), 1),
                      "ms_per_step": round(rr["ms_per_step"], 4),
                      "stage_ms_per_launch": {k: round(v, 4) for k, v in rr["stage_ms_per_launch"].items()},
-                     "roofline": roofline(mode)}
+                     "roofline": roofline(mode), "path_roofline": path_roofline(mode)}
     if "sparse" in res:
         out["sparse"]["measured_keep"] = round(keep, 5)
         out["sparse"]["snapshot_fraction"] = round(sigma, 5)
