@@ -31,6 +31,7 @@ namespace {
 
 constexpr int QSTR = DK + 8;      // Q rows [t][dk]
 constexpr int ASTR = 2 * L + 8;   // A^T rows [t][s], s over the group's 128 tokens
+constexpr int OSTR = DV + 4;      // O staging rows [t][dv] (fp32)
 
 // Two workgroups per CU (four waves per SIMD: at most 128 registers per lane)
 // so one group's loads
@@ -38,8 +39,15 @@ constexpr int ASTR = 2 * L + 8;   // A^T rows [t][s], s over the group's 128 tok
 template <typename E, typename OT>
 __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   using I = inter_t<E>;
-  __shared__ __align__(32) I sQ[2 * L * QSTR];
-  __shared__ __align__(32) I sA[2 * L * ASTR];
+  // Q and A^T during the products; afterwards the same bytes hold the
+  // group's O rows, so that each store writes whole rows (a wave's own O^T
+  // tile covers only 16 of a row's 128 values)
+  constexpr int QA_BYTES = (int)sizeof(I) * 2 * L * (QSTR + ASTR);
+  static_assert(2 * L * OSTR * 4 <= QA_BYTES, "O staging fits in the Q and A^T space");
+  __shared__ __align__(32) char sQA[QA_BYTES];
+  I* sQ = reinterpret_cast<I*>(sQA);
+  I* sA = sQ + 2 * L * QSTR;
+  float* sO = reinterpret_cast<float*>(sQA);
   __shared__ float sG[2 * L];
 
   const int T = p.T, Nq = p.Nq, Nv = p.Nv, C = p.C, G = p.G;
@@ -63,7 +71,9 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   const int n16 = lane & 15, g4 = lane >> 4;
   const int c0 = 2 * r;
   const bool has1 = c0 + 1 < C;
-  const int ntile = has1 ? 8 : 4;           // 16-token tiles in this group
+  // Every group is computed as two chunks (straight-line code); a group
+  // without a second chunk reads zeros for its Q, K, U' and decays there,
+  // so those products vanish, and its rows are not stored.
   const size_t bh = (size_t)b * Nv + h;
 
   // ---- group entry state: source and log2 factor
@@ -99,26 +109,22 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
     const int q = tid + 512 * it;
     const int rr = q >> 4, c8 = (q & 15) * 8;
     const int t = c0 * L + rr;
-    qst[it] = (rr < ntile * 16 && t < T) ? ld8(Qin + ((size_t)(b * T + t) * Nq + pr) * DK + c8)
-                                         : zero_frag<E>();
+    qst[it] = (t < T) ? ld8(Qin + ((size_t)(b * T + t) * Nq + pr) * DK + c8) : zero_frag<E>();
   }
   frag_t<E> kf[4];
   {
     const int ts = c0 * L + 16 * w + n16;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      kf[ks] = (w < ntile && ts < T) ? ld8(Kin + ((size_t)(b * T + ts) * Nq + pr) * DK + 32 * ks + 8 * g4)
-                                     : zero_frag<E>();
+      kf[ks] = (ts < T) ? ld8(Kin + ((size_t)(b * T + ts) * Nq + pr) * DK + 32 * ks + 8 * g4)
+                        : zero_frag<E>();
   }
   const int dvr = 16 * w + n16;
   const I* Up = static_cast<const I*>(p.U);
   frag_t<I> sfr[4], ufr[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < 4; ++ks)
     sfr[ks] = Ssrc != nullptr ? ld8(Ssrc + (size_t)dvr * DK + 32 * ks + 8 * g4) : zero_frag<I>();
-    ufr[ks] = (2 * ks < ntile) ? ld8(Up + ((bh * C + c0 + (ks >> 1)) * DV + dvr) * L + 32 * (ks & 1) + 8 * g4)
-                               : zero_frag<I>();
-  }
 
   // ---- stage Q rows of the group and G
 #pragma unroll
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   __syncthreads();
 
   // ---- phase 1: A^T blocks of source tile w (s in 16w..16w+15)
-  if (w < ntile) {
+  {
     frag_t<I> kfi[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) kfi[ks] = cvt8<I, E>(kf[ks]);
@@ -149,7 +155,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
     for (int j = 0; j < 4; ++j) gs[j] = sG[16 * w + 4 * g4 + j];
     // the block just above the diagonal (source tile w, token tile w - 1) is
     // read by the 32-wide k-steps of phase 2; the causal mask makes it zero
-    for (int jt = (w > 0 ? w - 1 : 0); jt < ntile; ++jt) {
+    for (int jt = (w > 0 ? w - 1 : 0); jt < 8; ++jt) {
       f32x4 at = zero4();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
@@ -166,6 +172,12 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
       st4<I>(&sA[t * ASTR + 16 * w + 4 * g4], a4);
     }
   }
+  // U' rows for phase 2 (requested here, not with the other loads, so that
+  // they are not live across phase 1; their latency overlaps S^T Q^T)
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    ufr[ks] = (c0 + (ks >> 1) < C) ? ld8(Up + ((bh * C + c0 + (ks >> 1)) * DV + dvr) * L + 32 * (ks & 1) + 8 * g4)
+                                   : zero_frag<I>();
   __syncthreads();
 
   // ---- phase 2: dv rows 16w..16w+15 of O^T for every token tile
@@ -177,10 +189,8 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if (j < ntile) {
-          const frag_t<I> qf = ld8(&sQ[(16 * j + n16) * QSTR + 32 * ks + 8 * g4]);
-          acc[j] = mma(sfr[ks], qf, acc[j]);
-        }
+        const frag_t<I> qf = ld8(&sQ[(16 * j + n16) * QSTR + 32 * ks + 8 * g4]);
+        acc[j] = mma(sfr[ks], qf, acc[j]);
       }
     }
 #pragma unroll
@@ -193,10 +203,9 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   // local terms: U'^T A^T, source 32-blocks ks (chunk c0 + ks / 2)
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    if (2 * ks >= ntile) break;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (j < ntile && ks <= (j >> 1)) {
+      if (ks <= (j >> 1)) {
         const frag_t<I> af = ld8(&sA[(16 * j + n16) * ASTR + 32 * ks + 8 * g4]);
         acc[j] = mma(ufr[ks], af, acc[j]);
       }
@@ -204,16 +213,24 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   }
 
   const float scale = 0.08838834764831845f;   // 128^-1/2
-  OT* O = static_cast<OT*>(p.o);
+  __syncthreads();   // Q and A^T are no longer read
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int tok = c0 * L + 16 * j + n16;
-    if (j < ntile && tok < T) {
-      f32x4 v = acc[j];
+    f32x4 v = acc[j];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) v[jj] *= scale;
-      st4o<OT>(O + ((size_t)(b * T + tok) * Nv + h) * DV + 16 * w + 4 * g4, v);
-    }
+    for (int jj = 0; jj < 4; ++jj) v[jj] *= scale;
+    *reinterpret_cast<f32x4*>(&sO[(16 * j + n16) * OSTR + 16 * w + 4 * g4]) = v;
+  }
+  __syncthreads();
+  // rows of 128 values: 32 consecutive lanes write one token's row
+  OT* O = static_cast<OT*>(p.o);
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int q = tid + 512 * it;
+    const int t = q >> 5, c4 = (q & 31) * 4;
+    const int tok = c0 * L + t;
+    if (tok < T)
+      st4o<OT>(O + ((size_t)(b * T + tok) * Nv + h) * DV + c4, *reinterpret_cast<const f32x4*>(&sO[t * OSTR + c4]));
   }
 }
 
