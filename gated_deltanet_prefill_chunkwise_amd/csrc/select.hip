@@ -252,30 +252,51 @@ __global__ __launch_bounds__(1024) void select_tier_kernel(SelectArgs p, int kL,
 // compact-snapshot slots numbered over the referenced events in CSR order.
 // One block of 16 waves per sequence; wave w works on pair w or row w.
 __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p, int kL, int kM, int kH) {
+  // Wave w handles head pair w.  Each pair's kept chunks are held as 64-bit
+  // words (bit l of word i: chunk 64 i + l), and so are its referenced events,
+  // so the CSR columns, the snapshot slots and the group predecessors follow
+  // from bit counts without reading back what this kernel writes.
+  constexpr int NWMAX = 128;   // 64-chunk words per pair (C <= 8192)
   __shared__ int s_tier[NP], s_cnt[NP], s_rowpair[NP], s_rowof[NP], s_rowptr[NP + 1];
   __shared__ int s_ref[NP], s_refbase[NP + 1];
+  __shared__ unsigned long long s_kept[NP][NWMAX], s_refd[NP][NWMAX];
   const int b = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int C = p.C, G = p.G;
+  const int C = p.C, G = p.G, NW = (C + 63) / 64;
+  const unsigned long long below = (1ull << lane) - 1ull;
   uint8_t* mask = p.mask + (size_t)b * NP * C;
   const bool ovr = p.mask_in != nullptr;
   if (tid < NP) s_tier[tid] = ovr ? 0 : p.tier[b * NP + tid];
   __syncthreads();
+  const int pp = w;
   {
-    const int pp = w;
+    // mask of pair w (the rank loads of a batch of words are issued together)
     const int t = s_tier[pp];
     const int k = t == 2 ? kH : (t == 1 ? kM : kL);
     int cnt = 0;
-    for (int c = lane; c < C; c += 64) {
-      const size_t idx = (size_t)pp * C + c;
-      uint8_t z;
-      if (ovr) {
-        z = p.mask_in[(size_t)b * NP * C + idx] ? 1 : 0;
-      } else {
-        const int r = p.rank[(size_t)b * NP * C + idx];
-        z = (c == 0 || c == C - 1 || (r >= 0 && r < k - 2)) ? 1 : 0;
+    for (int i0 = 0; i0 < NW; i0 += 8) {
+      int val[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = 64 * (i0 + u) + lane;
+        const size_t idx = (size_t)b * NP * C + (size_t)pp * C + c;
+        val[u] = 0;
+        if (i0 + u < NW && c < C) val[u] = ovr ? (int)p.mask_in[idx] : p.rank[idx];
       }
-      mask[idx] = z;
-      cnt += z;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u;
+        if (i < NW) {
+          const int c = 64 * i + lane;
+          int z = 0;
+          if (c < C) {
+            z = ovr ? (val[u] ? 1 : 0) : ((c == 0 || c == C - 1 || (val[u] >= 0 && val[u] < k - 2)) ? 1 : 0);
+            mask[(size_t)pp * C + c] = (uint8_t)z;
+          }
+          const unsigned long long bal = __ballot(z);
+          if (lane == 0) s_kept[pp][i] = bal;
+          cnt += z;
+        }
+      }
     }
     for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
     if (lane == 0) s_cnt[pp] = cnt;
@@ -285,11 +306,11 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p, int kL, int 
     int r = 0;
     s_rowptr[0] = 0;
     for (int t = 2; t >= 0; --t)
-      for (int pp = 0; pp < NP; ++pp)
-        if (s_tier[pp] == t) {
-          s_rowpair[r] = pp;
-          s_rowof[pp] = r;
-          s_rowptr[r + 1] = s_rowptr[r] + s_cnt[pp];
+      for (int q = 0; q < NP; ++q)
+        if (s_tier[q] == t) {
+          s_rowpair[r] = q;
+          s_rowof[q] = r;
+          s_rowptr[r + 1] = s_rowptr[r] + s_cnt[q];
           ++r;
         }
   }
@@ -297,35 +318,34 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p, int kL, int 
   if (tid < NP) p.row_pair[b * NP + tid] = s_rowpair[tid];
   if (tid <= NP) p.row_ptr[b * (NP + 1) + tid] = s_rowptr[tid];
   int32_t* col = p.col + (size_t)b * p.Emax;
+  const int row = s_rowof[pp], base = s_rowptr[row];
   {
     // kept chunks of pair w, ascending, at its row's offset
-    const int pp = w, base = s_rowptr[s_rowof[pp]];
     int run = 0;
-    for (int c0 = 0; c0 < C; c0 += 64) {
-      const int c = c0 + lane;
-      const bool z = c < C && mask[(size_t)pp * C + c];
-      const unsigned long long bal = __ballot(z);
-      const int before = __popcll(bal & ((1ull << lane) - 1ull));
-      if (z) col[base + run + before] = c;
+    for (int i = 0; i < NW; ++i) {
+      const unsigned long long bal = s_kept[pp][i];
+      if ((bal >> lane) & 1ull) col[base + run + __popcll(bal & below)] = 64 * i + lane;
       run += __popcll(bal);
     }
   }
-  __syncthreads();
-  // referenced events: e is the predecessor of some group r (2r <= 2(G-1))
-  // iff there is an even number in [e+1, min(next kept, 2(G-1))]
-  auto referenced = [&](int i, int end) {
-    const int c = col[i];
-    const int nxt = (i + 1 < end) ? col[i + 1] : C + 1;
-    const int lo = c + 1, lo_e = lo + (lo & 1);
-    const int hi = min(nxt, 2 * (G - 1));
-    return lo_e <= hi;
-  };
   {
-    const int beg = s_rowptr[w], end = s_rowptr[w + 1];
-    int cnt = 0;
-    for (int i = beg + lane; i < end; i += 64) cnt += referenced(i, end) ? 1 : 0;
-    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
-    if (lane == 0) s_ref[w] = cnt;
+    // referenced events: e is the predecessor of some group r (2r <= 2(G-1))
+    // iff there is an even number in [e+1, min(next kept, 2(G-1))]; the
+    // next kept chunk is found from the words, walking backwards
+    int nextfirst = C + 1, refcnt = 0;
+    for (int i = NW - 1; i >= 0; --i) {
+      const unsigned long long bal = s_kept[pp][i];
+      const int c = 64 * i + lane;
+      const unsigned long long above = lane == 63 ? 0ull : (bal >> (lane + 1));
+      const int nxt = above ? c + 1 + (int)__builtin_ctzll(above) : nextfirst;
+      const int lo = c + 1, lo_e = lo + (lo & 1), hi = min(nxt, 2 * (G - 1));
+      const bool ref = ((bal >> lane) & 1ull) && lo_e <= hi;
+      const unsigned long long rb = __ballot(ref);
+      if (lane == 0) s_refd[pp][i] = rb;
+      refcnt += __popcll(rb);
+      if (bal) nextfirst = 64 * i + (int)__builtin_ctzll(bal);
+    }
+    if (lane == 0) s_ref[row] = refcnt;
   }
   __syncthreads();
   if (tid == 0) {
@@ -335,42 +355,40 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p, int kL, int 
   __syncthreads();
   int32_t* eslot = p.event_slot + (size_t)b * p.Emax;
   {
-    const int beg = s_rowptr[w], end = s_rowptr[w + 1];
-    int run = s_refbase[w];
-    for (int i0 = beg; i0 < end; i0 += 64) {
-      const int i = i0 + lane;
-      const bool ref = i < end && referenced(i, end);
-      const unsigned long long bal = __ballot(ref);
-      const int before = __popcll(bal & ((1ull << lane) - 1ull));
-      if (i < end) eslot[i] = ref ? run + before : -1;
-      run += __popcll(bal);
-    }
-  }
-  __syncthreads();
-  {
-    // predecessor of each group r of pair w: the last kept chunk < 2r, i.e.
-    // CSR entry beg + (number of kept chunks before 2r) - 1
-    const int pp = w, row = s_rowof[pp];
-    const int beg = s_rowptr[row];
-    int run = 0;   // kept chunks before c0
-    for (int c0 = 0; c0 < C; c0 += 64) {
-      const int c = c0 + lane;
-      const bool z = c < C && mask[(size_t)pp * C + c];
-      const unsigned long long bal = __ballot(z);
-      const int before = run + __popcll(bal & ((1ull << lane) - 1ull));
-      if ((c & 1) == 0 && c < C && (c >> 1) < G) {
-        const int r = c >> 1, i = beg + before - 1;
-        const size_t o = ((size_t)b * NP + pp) * G + r;
-        p.pred[o] = before > 0 ? col[i] : -1;
-        p.group_slot[o] = before > 0 ? eslot[i] : -1;
+    // snapshot slot of each event (rank among the referenced ones, rows in
+    // CSR order) and, per group r, the last kept chunk before 2r with its slot
+    const int rbase = s_refbase[row];
+    int run = 0, rrun = 0, lastc = -1, lasts = -1;
+    for (int i = 0; i < NW; ++i) {
+      const unsigned long long bal = s_kept[pp][i], rb = s_refd[pp][i];
+      const int c = 64 * i + lane;
+      if ((bal >> lane) & 1ull)
+        eslot[base + run + __popcll(bal & below)] = ((rb >> lane) & 1ull) ? rbase + rrun + __popcll(rb & below) : -1;
+      if ((c & 1) == 0 && c < C) {
+        const unsigned long long m = bal & below;
+        int pc = lastc, ps = lasts;
+        if (m) {
+          const int el = 63 - (int)__builtin_clzll(m);
+          pc = 64 * i + el;
+          ps = rbase + rrun + __popcll(rb & ((1ull << el) - 1ull));
+        }
+        const size_t o = ((size_t)b * NP + pp) * G + (c >> 1);
+        p.pred[o] = pc;
+        p.group_slot[o] = pc >= 0 ? ps : -1;
+      }
+      if (bal) {
+        const int el = 63 - (int)__builtin_clzll(bal);
+        lastc = 64 * i + el;
+        lasts = rbase + rrun + __popcll(rb & ((1ull << el) - 1ull));
       }
       run += __popcll(bal);
+      rrun += __popcll(rb);
     }
   }
   if (tid == 0 && p.stats != nullptr) {
     int32_t* st = static_cast<int32_t*>(p.stats) + b * 9;
     int nt[3] = {0, 0, 0};
-    for (int pp = 0; pp < NP; ++pp) nt[s_tier[pp]]++;
+    for (int q = 0; q < NP; ++q) nt[s_tier[q]]++;
     st[0] = s_rowptr[NP];
     st[1] = p.Emax;
     st[2] = nt[0]; st[3] = nt[1]; st[4] = nt[2];
