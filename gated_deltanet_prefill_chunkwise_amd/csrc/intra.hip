@@ -194,6 +194,11 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     load_ab(item);
     load_kv(item, kreg, v1reg, 1, false);
   }
+  // The first item's operands are complete before the loop: otherwise the
+  // wait counts at the loop head, merged over this path (few requests after
+  // the gate loads) and the loop's back edge, would make every item wait for
+  // the previous item's stores before it reads its prefetched gates.
+  __builtin_amdgcn_s_waitcnt(0);
 
   for (; item < n_items; item += gridDim.x) {
     // wave and thread index as opaque values per item, so that the addresses
