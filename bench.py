@@ -7,7 +7,9 @@ on the device.  One step = one pass of the 24-layer stack through the whole
 SparseGDN path at the default keep budget (29% of head-pair x chunk events):
 intra (block-adjacent solve, tail score), gate energy, selector and CSR
 layout, deferred W, event-sparse H scan with compact snapshots, grouped O.
-The dense exact path (intra, H, O) is timed the same way beside it.
+The dense exact path (intra, H, O) is timed the same way beside it, and so is
+the single-token decode step that continues from the final states (a batch
+of 128 sequences through the same 24 layers, states updated in place).
 
 Prints one JSON line.  value = tokens/s of the 24-layer stack (B*T per step);
 roofline = the dominant kernel's algorithmic bytes per launch over its mean
@@ -46,6 +48,8 @@ def parse():
     ap.add_argument("--mode", choices=("both", "sparse", "dense"), default="both")
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of layer 0 the oracle baseline processes")
+    ap.add_argument("--decode-batch", type=int, default=128,
+                    help="sequences of the decode-step leg (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -95,7 +99,8 @@ def algorithmic_bytes_per_token(stage: str, mode: str, sigma: float, keep: float
 
 
 def source_hash(stage: str) -> str:
-    f = {"hscan": "hscan.hip", "o": "ochunk.hip", "intra": "intra.hip"}.get(stage)
+    f = {"hscan": "hscan.hip", "o": "ochunk.hip", "intra": "intra.hip",
+         "decode": "decode.hip"}.get(stage)
     if f is None:
         return ""
     p = os.path.join(ROOT, "gated_deltanet_prefill_chunkwise_amd", "csrc", f)
@@ -137,6 +142,66 @@ def cpu_baseline(inputs0, tokens=32768):
                 sample=(f"fp64 numpy oracle, SparseGDN 29% path, layer 0's first {tokens} tokens, "
                         f"all 32 value heads, one layer timed ({dt:.1f} s) and scaled by 1/24; "
                         f"BLAS calls use up to {threads} threads, the rest one"))
+
+
+def decode_bytes_per_launch(Bd: int) -> int:
+    """One decode launch: every head's fp32 state read and written once, plus
+    the token's bf16 q, k, v, beta, fp32 a and the fp32 output."""
+    state = Bd * NV * D * D * 4 * 2
+    tok = Bd * (2 * NQ * D * 2 + NV * D * 2 + NV * 4 + NV * 2) + Bd * NV * D * 4
+    return state + tok
+
+
+def decode_leg(args, hip, dev):
+    """Single-token decode step through the layer stack: Bd sequences, one
+    in-place state per layer; HIP events around every launch."""
+    import torch
+    from gated_deltanet_prefill_chunkwise_amd import ops, synth
+    Bd, L = args.decode_batch, args.layers
+    lay = []
+    for l in range(L):
+        t = synth.torch_inputs(synth.seed_for(5, l), Bd, 1, NQ, NV, dtype="bf16", device=dev)
+        t = {k: v[:, 0].contiguous() for k, v in t.items()}
+        g = torch.Generator(device=dev)
+        g.manual_seed(synth.seed_for(6, l))
+        st = torch.randn((Bd, NV, D, D), generator=g, device=dev) * 0.3
+        o = torch.empty((Bd, NV, D), dtype=torch.float32, device=dev)
+        lay.append((t, st, o))
+    stream = torch.cuda.current_stream()
+
+    def step(evs):
+        for l, (t, st, o) in enumerate(lay):
+            if evs is not None:
+                hip.lib.hipEventRecord(ctypes.c_void_p(evs[l]), ctypes.c_void_p(stream.cuda_stream))
+            ops.decode_step(t["q"], t["k"], t["v"], t["a"], t["beta"], st, s_out=st, o=o)
+        if evs is not None:
+            hip.lib.hipEventRecord(ctypes.c_void_p(evs[L]), ctypes.c_void_p(stream.cuda_stream))
+
+    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    evs = [[hip.event() for _ in range(L + 1)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(args.steps):
+        step(evs[s])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    launch_ms = sum(hip.elapsed_ms(evs[s][l], evs[s][l + 1])
+                    for s in range(args.steps) for l in range(L)) / (args.steps * L)
+    alg = decode_bytes_per_launch(Bd)
+    achieved = alg / (launch_ms / 1e3) / 1e9
+    print(f"[bench] decode: {ms:.3f} ms per {L}-layer step at batch {Bd}; "
+          f"{launch_ms * 1e3:.1f} us per launch", file=sys.stderr, flush=True)
+    return {"value_tok_s": round(Bd / (ms / 1e3), 1), "unit": f"tok/s ({L}-layer stack, batch {Bd})",
+            "ms_per_step": round(ms, 4), "batch": Bd, "layers": L, "state_dtype": "fp32",
+            "roofline": dict(bound="hbm", kernel="decode", achieved=round(achieved, 1),
+                             peak=HBM_PEAK_GBS, unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                             traffic=measured_traffic("decode", "decode"),
+                             algorithmic_bytes_per_launch=alg,
+                             launch_ms=round(launch_ms, 5))}
 
 
 def main():
@@ -282,6 +347,8 @@ def main():
         out["sparse"]["snapshot_fraction"] = round(sigma, 5)
     if "sparse" in res and "dense" in res:
         out["sparse_speedup_over_dense"] = round(res["dense"]["ms_per_step"] / res["sparse"]["ms_per_step"], 3)
+    if args.decode_batch > 0:
+        out["decode"] = decode_leg(args, hip, dev)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(layers[0][0], args.cpu_tokens)
     print(json.dumps(out), flush=True)
 

@@ -21,7 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libsgdn.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.hip", "intra.hip", "hscan.hip", "ochunk.hip", "misc.hip", "select.hip"]
+SOURCES = ["api.hip", "intra.hip", "hscan.hip", "ochunk.hip", "misc.hip", "select.hip",
+           "decode.hip"]
 # hscan: products accumulate in ordinary vector registers (its state tiles are
 # also scaled and converted by vector instructions every event)
 EXTRA = {"select.hip": ["-ffp-contract=off"],

@@ -245,6 +245,28 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   return SGDN_OK;
 }
 
+int sgdn_decode_step(const sgdn_problem* prob, const void* q, const void* k, const void* v,
+                     const float* a, const void* beta, const float* s_in, float* s_out, void* o,
+                     void* stream) {
+  if (prob == nullptr) return SGDN_EINVAL;
+  const sgdn_problem& pr = *prob;
+  if (pr.batch < 1 || pr.seqlen != 1 || pr.n_qk < 1 || pr.n_v < 1) return SGDN_EINVAL;
+  if (pr.dtype != SGDN_F32 && pr.dtype != SGDN_BF16) return SGDN_EINVAL;
+  if (pr.o_dtype != SGDN_F32 && pr.o_dtype != SGDN_BF16) return SGDN_EINVAL;
+  if (pr.d_k != 128 || pr.d_v != 128 || pr.n_v % pr.n_qk != 0) return SGDN_EUNSUPPORTED;
+  if ((long long)pr.batch * pr.n_v > (1LL << 29)) return SGDN_EUNSUPPORTED;
+  if (!q || !k || !v || !a || !beta || !s_in || !s_out || !o) return SGDN_EINVAL;
+  const size_t sbytes = (size_t)pr.batch * pr.n_v * DK * DV * sizeof(float);
+  const char* i0 = reinterpret_cast<const char*>(s_in);
+  const char* o0 = reinterpret_cast<const char*>(s_out);
+  if (i0 != o0 && i0 < o0 + sbytes && o0 < i0 + sbytes) return SGDN_EINVAL;
+  if (((uintptr_t)s_in | (uintptr_t)s_out) & 15) return SGDN_EINVAL;   // 16-byte vector access
+  DecodeArgs da{q, k, v, a, beta, s_in, s_out, o, pr.batch, pr.n_qk, pr.n_v,
+                pr.o_dtype == SGDN_BF16};
+  SGDN_TRY(launch_decode(da, pr.dtype == SGDN_BF16, static_cast<hipStream_t>(stream)));
+  return SGDN_OK;
+}
+
 int sgdn_select(const sgdn_problem* prob, const float* score, const float* gamma, const float* eta,
                 const sgdn_sparse_params* params, uint8_t* mask, uint8_t* tier, int32_t* row_pair,
                 int32_t* row_ptr, int32_t* col, int32_t* pred, int32_t* group_slot,

@@ -110,6 +110,14 @@ struct DeferredWArgs {
   int B, Nv, Nq, C, Emax, solve;
 };
 
+// Single-token decode step (decode.hip).  q, k [B][Nq][128], v [B][Nv][128],
+// a [B][Nv] fp32, beta [B][Nv], s_in / s_out [B][Nv][128][128] fp32.
+struct DecodeArgs {
+  const void* q; const void* k; const void* v; const float* a; const void* beta;
+  const float* s_in; float* s_out; void* o;
+  int B, Nq, Nv, o_bf16;
+};
+
 hipError_t launch_intra(const IntraArgs& a, int bf16, hipStream_t s);
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s);
 hipError_t launch_hscan(const HScanArgs& a, int bf16, hipStream_t s);
@@ -119,6 +127,7 @@ hipError_t launch_s0prep(const S0PrepArgs& a, int bf16, hipStream_t s);
 hipError_t launch_gate(const GateArgs& a, int bf16, hipStream_t s);
 hipError_t launch_select_full(const SelectArgs& a, int kL, int kM, int kH, hipStream_t s);
 hipError_t launch_deferred_w(const DeferredWArgs& a, int bf16, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int bf16, hipStream_t s);
 hipError_t launch_debug_u(const void* Ut, float* U, int B, int Nv, int C, int bf16, hipStream_t s);
 
 }  // namespace sgdn

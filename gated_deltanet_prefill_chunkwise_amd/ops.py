@@ -75,6 +75,8 @@ def lib():
         L.sgdn_prefill_sparse.argtypes = [P, vp, vp, vp, vp, vp, vp, SP, vp, vp, vp, vp, vp, vp,
                                           sz, vp, vp]
         L.sgdn_prefill_sparse.restype = i32
+        L.sgdn_decode_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.sgdn_decode_step.restype = i32
         L.sgdn_status_string.argtypes = [i32]
         L.sgdn_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -178,6 +180,41 @@ def prefill_dense(q, k, v, a, beta, s0=None, solve="exact", want_state=True, o=N
     if st != 0:
         raise SgdnError(st, "sgdn_prefill_dense")
     return o, s_final
+
+
+def decode_step(q, k, v, a, beta, state, s_out=None, o=None, out_dtype=None, stream=None):
+    """One-token decode step from ``state`` [B, Nv, d, dv] fp32; returns (o, s_out).
+
+    q, k [B, Nq, d], v [B, Nv, dv], a [B, Nv] fp32, beta [B, Nv].  ``s_out``
+    may be ``state`` itself (updated in place); by default a new tensor.
+    """
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta")):
+        _check(t, n, q.dtype)
+    _check(a, "a", torch.float32)
+    _check(state, "state", torch.float32)
+    if o is not None:
+        out_dtype = o.dtype
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    _check(o, "o", out_dtype)
+    B, Nq, d = q.shape
+    Nv, dv = v.shape[1], v.shape[2]
+    if o is None:
+        o = torch.empty(v.shape, dtype=out_dtype, device=v.device)
+    if s_out is None:
+        s_out = torch.empty_like(state)
+    _check(s_out, "s_out", torch.float32)
+    for t, shape, n in ((k, (B, Nq, d), "k"), (a, (B, Nv), "a"), (beta, (B, Nv), "beta"),
+                        (state, (B, Nv, d, dv), "state"), (s_out, (B, Nv, d, dv), "s_out"),
+                        (o, (B, Nv, dv), "o")):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{n} must have shape {shape}, got {tuple(t.shape)}")
+    prob = Problem(B, 1, Nq, Nv, d, dv, _code(q.dtype), 0, _code(out_dtype))
+    st = lib().sgdn_decode_step(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                _ptr(beta), _ptr(state), _ptr(s_out), _ptr(o), _stream(stream))
+    if st != 0:
+        raise SgdnError(st, "sgdn_decode_step")
+    return o, s_out
 
 
 def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None):

@@ -180,6 +180,30 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k,
                         float* s_final, sgdn_stats* stats, void* ws,
                         size_t ws_bytes, void* stream, sgdn_debug* debug);
 
+/* Single-token decode step: the gated delta rule applied to one new token of
+ * each sequence, continuing from the final state a prefill returned (Sec. 2.6
+ * hands S_{C,h} to autoregressive decoding; the step is the per-token form of
+ * Sec. 2.1).  For value head h, with alpha = 2^a and query/key head
+ * h / (Nv / Nq):
+ *     S' = alpha S + k u^T,  u = beta (v - alpha S^T k),  o = S'^T q / sqrt(d)
+ * prob: batch = B sequences, seqlen must be 1, Nv a multiple of Nq,
+ * d = dv = 128; dtype applies to q, k, v, beta, o_dtype to o; solve is
+ * ignored.
+ *   q, k   [B, Nq, d]       dtype
+ *   v      [B, Nv, dv]      dtype
+ *   a      [B, Nv]          fp32 log2 retention (<= 0)
+ *   beta   [B, Nv]          dtype
+ *   s_in   [B, Nv, d, dv]   fp32 state before the token
+ *   s_out  [B, Nv, d, dv]   fp32 state after the token; may be s_in itself
+ *                           (updated in place), must not overlap it otherwise
+ *   o      [B, Nv, dv]      o_dtype output of the token
+ * s_in and s_out must be 16-byte aligned.  Needs no workspace.  SGDN_EINVAL
+ * for a null pointer, seqlen != 1, a misaligned state or partially
+ * overlapping states. */
+int sgdn_decode_step(const sgdn_problem* prob, const void* q, const void* k,
+                     const void* v, const float* a, const void* beta,
+                     const float* s_in, float* s_out, void* o, void* stream);
+
 /* Static description of a status code. */
 const char* sgdn_status_string(int status);
 

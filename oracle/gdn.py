@@ -57,6 +57,19 @@ def recurrence(q, k, v, a, beta, s0=None):
     return o, S
 
 
+def decode_step(q, k, v, a, beta, s):
+    """One token of the recurrence per sequence: the decode step that follows a
+    prefill, whose final state S_{C,h} is handed to autoregressive decoding
+    (Sec. 2.6); the step is the per-token rule of `recurrence`.
+
+    q, k [B, Nq, d]; v [B, Nv, dv]; a, beta [B, Nv]; s [B, Nv, d, dv].
+    Returns o [B, Nv, dv] and the new state.
+    """
+    o, S = recurrence(np.asarray(q)[:, None], np.asarray(k)[:, None], np.asarray(v)[:, None],
+                      np.asarray(a)[:, None], np.asarray(beta)[:, None], s)
+    return o[:, 0], S
+
+
 # ---------------------------------------------------------------------------
 # chunk form
 # ---------------------------------------------------------------------------

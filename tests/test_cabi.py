@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["sgdn_workspace_bytes", "sgdn_prefill_dense", "sgdn_select", "sgdn_prefill_sparse",
-         "sgdn_status_string"])
+         "sgdn_status_string", "sgdn_decode_step"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -113,3 +113,22 @@ def test_sparse_and_select_argument_errors(L):
     assert sel(_prob(), good, score=None) == -1
     assert sel(_prob(n_qk=4, n_v=8), good) == -2
     assert sel(_prob(), ops.sparse_params(r_window=8)) == -2
+
+
+def test_decode_argument_errors(L):
+    def call(p, s_in=FAKE, s_out=FAKE, q=FAKE):
+        return L.sgdn_decode_step(ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, s_in, s_out, FAKE,
+                                  None)
+    one = dict(seqlen=1)
+    assert call(_prob(seqlen=2)) == -1                     # one token per sequence
+    assert call(_prob(d_k=64, **one)) == -2
+    assert call(_prob(n_qk=3, n_v=32, **one)) == -2        # Nv not a multiple of Nq
+    assert call(_prob(dtype=4, **one)) == -1
+    assert call(_prob(o_dtype=4, **one)) == -1
+    assert call(_prob(batch=0, **one)) == -1
+    assert call(_prob(**one), q=None) == -1
+    assert call(_prob(**one), s_out=None) == -1
+    # states that overlap without being the same buffer
+    assert call(_prob(**one), s_out=ctypes.c_void_p(0x1000 + 4096)) == -1
+    assert call(_prob(**one), s_in=ctypes.c_void_p(0x1004), s_out=ctypes.c_void_p(0x1004)) == -1
+    assert L.sgdn_decode_step(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1

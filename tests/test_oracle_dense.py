@@ -75,6 +75,40 @@ def test_orthonormal_keys_store_and_overwrite():
     assert np.abs(S[0, :, 5, :]).max() == 0.0                     # never written
 
 
+def test_decode_step_reads_back_and_leaves_the_complement():
+    """One decode step with a unit key and beta = 1 stores v exactly under k
+    whatever the decay and old state: S'^T k = v, so q = k reads v / sqrt(d);
+    every direction x orthogonal to k only decays: S'^T x = 2^a S^T x."""
+    g = np.random.default_rng(21)
+    B, Nq, Nv, d = 2, 2, 4, 16
+    k = g.standard_normal((B, Nq, d)); k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = g.standard_normal((B, Nv, d))
+    a = -g.uniform(0.1, 3.0, (B, Nv))
+    s = g.standard_normal((B, Nv, d, d))
+    o, S = gdn.decode_step(k, k, v, a, np.ones((B, Nv)), s)
+    hq = np.arange(Nv) // (Nv // Nq)
+    kh = k[:, hq]                                            # [B, Nv, d]
+    np.testing.assert_allclose(np.einsum("bhd,bhde->bhe", kh, S), v, atol=1e-12)
+    np.testing.assert_allclose(o, v / math.sqrt(d), atol=1e-12)
+    x = g.standard_normal((B, Nv, d))
+    x -= np.sum(x * kh, axis=-1, keepdims=True) * kh         # x orthogonal to k
+    np.testing.assert_allclose(np.einsum("bhd,bhde->bhe", x, S),
+                               np.exp2(a)[..., None] * np.einsum("bhd,bhde->bhe", x, s),
+                               atol=1e-12)
+
+
+def test_decode_step_continues_a_chunk_prefill():
+    """Chunk prefill of T tokens then one decode step equals the token
+    recurrence over T + 1 tokens (last output and final state)."""
+    q, k, v, a, beta = rand_inputs(22, 1, 131, 2, 4, 16, 16)
+    o_ref, S_ref = gdn.recurrence(q, k, v, a, beta)
+    _, S = gdn.chunk_prefill(q[:, :-1], k[:, :-1], v[:, :-1], a[:, :-1], beta[:, :-1], None,
+                             "exact")
+    o, S2 = gdn.decode_step(q[:, -1], k[:, -1], v[:, -1], a[:, -1], beta[:, -1], S)
+    assert relerr(o, o_ref[:, -1]) < 1e-11
+    assert relerr(S2, S_ref) < 1e-11
+
+
 def test_value_columns_are_independent():
     """Permuting the value columns (and s0's) permutes O and S the same way."""
     q, k, v, a, beta = rand_inputs(4, 1, 100, 1, 2, 16, 16)
