@@ -9,7 +9,9 @@ intra (block-adjacent solve, tail score), gate energy, selector and CSR
 layout, deferred W, event-sparse H scan with compact snapshots, grouped O.
 The dense exact path (intra, H, O) is timed the same way beside it, and so is
 the single-token decode step that continues from the final states (a batch
-of 128 sequences through the same 24 layers, states updated in place).
+of 128 sequences through the same 24 layers, states updated in place).  A
+packed variable-length leg reads the same tokens as 16 sequences of mixed
+lengths (cu_seqlens) and times both paths again.
 
 Prints one JSON line.  value = tokens/s of the 24-layer stack (B*T per step);
 roofline = the dominant kernel's algorithmic bytes per launch over its mean
@@ -48,6 +50,8 @@ def parse():
     ap.add_argument("--mode", choices=("both", "sparse", "dense"), default="both")
     ap.add_argument("--cpu-tokens", type=int, default=32768,
                     help="tokens of layer 0 the oracle baseline processes")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the packed variable-length leg")
     ap.add_argument("--decode-batch", type=int, default=128,
                     help="sequences of the decode-step leg (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -142,6 +146,74 @@ def cpu_baseline(inputs0, tokens=32768):
                 sample=(f"fp64 numpy oracle, SparseGDN 29% path, layer 0's first {tokens} tokens, "
                         f"all 32 value heads, one layer timed ({dt:.1f} s) and scaled by 1/24; "
                         f"BLAS calls use up to {threads} threads, the rest one"))
+
+
+def varlen_lengths(total: int, n: int = 16, seed: int = 7):
+    """n ragged lengths, log-uniform between 1/16 and 1x of total/n*4, summing to total."""
+    import numpy as np
+    g = np.random.default_rng(seed)
+    x = np.exp(g.uniform(np.log(total / n / 4), np.log(total / n * 4), n))
+    lens = np.maximum(1, np.floor(x / x.sum() * total)).astype(np.int64)
+    lens[-1] += total - lens.sum()
+    assert lens.min() >= 1 and lens.sum() == total
+    return [int(v) for v in lens]
+
+
+def varlen_leg(args, layers, hip):
+    """Both paths over the same 24 layers' tokens read as packed sequences."""
+    import torch
+    from gated_deltanet_prefill_chunkwise_amd import ops
+    Tn = args.seqlen
+    lens = varlen_lengths(B * Tn)
+    cu = torch.tensor([0] + list(__import__("itertools").accumulate(lens)), dtype=torch.int32,
+                      device="cuda")
+    Tm = max(lens)
+    inp0 = layers[0][0]
+    prob = ops.problem(inp0["q"], inp0["v"], "blockadj", torch.float32, cu, Tm)
+    wsb = max(ops.workspace_bytes(prob, True, ops.sparse_params()), ops.workspace_bytes(prob, False))
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    nseq = len(lens)
+    sf = torch.empty((nseq, NV, D, D), dtype=torch.float32, device="cuda")
+    st = torch.zeros((nseq, ops.STATS_INTS), dtype=torch.int32, device="cuda")
+    out = {}
+    L = len(layers)
+    nev = len(STAGES) + 1
+    for mode in ("sparse", "dense"):
+        events = [[[hip.event() for _ in range(nev)] for _ in range(L)] for _ in range(args.steps)]
+        dbgs = [[ops.debug_struct(events=events[s][l]) for l in range(L)] for s in range(args.steps)]
+
+        def step(dbg_row):
+            for l, (inp, o, _, _) in enumerate(layers):
+                dbg = dbg_row[l] if dbg_row is not None else None
+                if mode == "sparse":
+                    ops.prefill_sparse(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"],
+                                       z=inp["z"], keep_budget=0.29, solve="blockadj", o=o,
+                                       s_final=sf, stats=st, workspace=ws, cu_seqlens=cu,
+                                       max_seqlen=Tm, debug=dbg)
+                else:
+                    ops.prefill_dense(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"],
+                                      solve="exact", o=o, s_final=sf, workspace=ws,
+                                      cu_seqlens=cu, max_seqlen=Tm, debug=dbg)
+        for _ in range(args.warmup):
+            step(None)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for s_ in range(args.steps):
+            step(dbgs[s_])
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        stage = {name: round(sum(hip.elapsed_ms(events[s_][l][i], events[s_][l][i + 1])
+                                 for s_ in range(args.steps) for l in range(L)) / (args.steps * L), 4)
+                 for i, name in enumerate(STAGES)}
+        out[mode] = {"value_tok_s": round(B * Tn / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+                     "stage_ms_per_launch": stage}
+        print(f"[bench] varlen {mode}: {ms:.3f} ms per {args.layers}-layer step "
+              f"({nseq} packed sequences); stages (ms/launch) "
+              + ", ".join(f"{k} {v:.3f}" for k, v in stage.items()), file=sys.stderr, flush=True)
+    out["lengths"] = lens
+    return out
 
 
 def decode_bytes_per_launch(Bd: int) -> int:
@@ -347,6 +419,8 @@ def main():
         out["sparse"]["snapshot_fraction"] = round(sigma, 5)
     if "sparse" in res and "dense" in res:
         out["sparse_speedup_over_dense"] = round(res["dense"]["ms_per_step"] / res["sparse"]["ms_per_step"], 3)
+    if not args.no_varlen and args.mode == "both":
+        out["varlen"] = varlen_leg(args, layers, hip)
     if args.decode_batch > 0:
         out["decode"] = decode_leg(args, hip, dev)
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(layers[0][0], args.cpu_tokens)

@@ -16,6 +16,7 @@ constexpr int NP_SPARSE = 16;
 
 struct Plan {
   int B, T, Nq, Nv, C, G, esz, isz, bf16, solve;
+  const int32_t* cu;   // packed sequence offsets or null
   int kL, kM, kH;
   int Emax;        // event capacity per sequence inside prefill_sparse
   int snap_cap;    // snapshot slots per sequence (sparse) or per head (dense)
@@ -25,7 +26,7 @@ struct Plan {
 
 enum Buf { B_G, B_GAMMA, B_P, B_U, B_W, B_CB, B_KT, B_SNAP, B_S0T, B_SCORE, B_ETA, B_RANK,
            B_TINFO, B_MASK, B_TIER, B_ROWPAIR, B_ROWPTR, B_COL, B_PRED, B_GSLOT, B_ESLOT,
-           B_WPK, B_STATS, B_FAC, B_REC, B_COUNT };
+           B_WPK, B_STATS, B_FAC, B_REC, B_CHUNKS, B_COUNT };
 
 static_assert(B_COUNT <= (int)(sizeof(Plan::off) / sizeof(size_t)), "workspace table too small");
 
@@ -78,7 +79,7 @@ int check_params(const sgdn_problem* pr, const sgdn_sparse_params* sp) {
 }
 
 void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp, Plan& p) {
-  p.B = pr->batch; p.T = pr->seqlen; p.Nq = pr->n_qk; p.Nv = pr->n_v;
+  p.B = pr->batch; p.T = pr->seqlen; p.Nq = pr->n_qk; p.Nv = pr->n_v; p.cu = pr->cu_seqlens;
   p.C = (p.T + 63) / 64; p.G = (p.C + 1) / 2;
   p.bf16 = pr->dtype == SGDN_BF16; p.esz = p.bf16 ? 2 : 4; p.solve = pr->solve;
   p.isz = p.bf16 ? 2 : 4;   // intermediates: fp16 for bf16 inputs, fp32 for fp32 inputs
@@ -99,6 +100,7 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
   sz[B_U] = B * Nv * C * L * DV * I;
   sz[B_KT] = B * p.Nq * C * DK * L * I;
   sz[B_S0T] = B * Nv * DV * DK * I;
+  if (p.cu != nullptr) sz[B_CHUNKS] = (B * C + 1 + B + 1) * 4;   // valid-chunk table
   if (!sparse) {
     sz[B_W] = B * Nv * C * L * DK * I;
     sz[B_SNAP] = B * Nv * (size_t)p.snap_cap * DV * DK * I;
@@ -151,6 +153,8 @@ IntraArgs intra_args(const Plan& pl, void* ws, const void* k, const void* v, con
   IntraArgs ia{};
   ia.k = k; ia.v = v; ia.a = a; ia.beta = beta;
   ia.B = pl.B; ia.T = pl.T; ia.Nq = pl.Nq; ia.Nv = pl.Nv; ia.C = pl.C; ia.solve = pl.solve;
+  ia.cu = pl.cu;
+  ia.chunks = pl.cu ? at<int32_t>(ws, pl, B_CHUNKS) : nullptr;
   ia.g = at<float>(ws, pl, B_G);
   ia.gamma = at<float>(ws, pl, B_GAMMA);
   ia.fac = at<float>(ws, pl, B_FAC);
@@ -162,6 +166,14 @@ IntraArgs intra_args(const Plan& pl, void* ws, const void* k, const void* v, con
   return ia;
 }
 
+// Packed sequences: the table of valid chunks the intra kernel walks.
+int chunk_table(const Plan& pl, void* ws, hipStream_t s) {
+  if (pl.cu == nullptr) return SGDN_OK;
+  ChunkTableArgs ca{pl.cu, at<int32_t>(ws, pl, B_CHUNKS), pl.B, pl.T, pl.C};
+  SGDN_TRY(launch_chunk_table(ca, s));
+  return SGDN_OK;
+}
+
 int debug_copies(const Plan& pl, void* ws, sgdn_debug* dbg, hipStream_t st, int with_prefix) {
   if (dbg == nullptr) return SGDN_OK;
   const size_t nhc = (size_t)pl.B * pl.Nv * pl.C;
@@ -169,7 +181,8 @@ int debug_copies(const Plan& pl, void* ws, sgdn_debug* dbg, hipStream_t st, int 
   if (dbg->gamma) SGDN_TRY(hipMemcpyAsync(dbg->gamma, at<void>(ws, pl, B_GAMMA), nhc * 4, hipMemcpyDeviceToDevice, st));
   if (dbg->prefix) {
     if (!with_prefix) {
-      PrefixArgs pa{at<float>(ws, pl, B_GAMMA), at<double>(ws, pl, B_P), pl.B, pl.Nv, pl.C};
+      PrefixArgs pa{at<float>(ws, pl, B_GAMMA), at<double>(ws, pl, B_P), pl.B, pl.Nv, pl.C,
+                    pl.cu, pl.T};
       SGDN_TRY(launch_prefix(pa, st));
     }
     SGDN_TRY(hipMemcpyAsync(dbg->prefix, at<void>(ws, pl, B_P), (size_t)pl.B * pl.Nv * (pl.C + 1) * 8,
@@ -215,6 +228,7 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   mark(dbg, SGDN_EV_START, s);
+  if ((st = chunk_table(pl, ws, s)) != SGDN_OK) return st;
   SGDN_TRY(launch_intra(intra_args(pl, ws, k, v, a, beta, 0), pl.bf16, s));
   mark_range(dbg, SGDN_EV_INTRA, SGDN_EV_DEFERRED, s);
   if ((st = debug_copies(pl, ws, dbg, s, 0)) != SGDN_OK) return st;
@@ -231,6 +245,7 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   ha.fac = at<float>(ws, pl, B_FAC); ha.rec = ea.rec; ha.P = nullptr;
   ha.s0 = s0; ha.s_final = s_final; ha.snap = at<void>(ws, pl, B_SNAP);
   ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 0;
+  ha.cu = pl.cu; ha.T = pl.T;
   SGDN_TRY(launch_hscan(ha, pl.bf16, s));
   mark(dbg, SGDN_EV_HSCAN, s);
   OChunkArgs oa{};
@@ -239,6 +254,7 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   oa.o_bf16 = prob->o_dtype == SGDN_BF16;
   oa.g = at<float>(ws, pl, B_G); oa.gamma = at<float>(ws, pl, B_GAMMA); oa.P = nullptr;
   oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
+  oa.cu = pl.cu;
   oa.sparse = 0;
   SGDN_TRY(launch_ochunk(oa, pl.bf16, s));
   mark(dbg, SGDN_EV_O, s);
@@ -251,6 +267,7 @@ int sgdn_decode_step(const sgdn_problem* prob, const void* q, const void* k, con
   if (prob == nullptr) return SGDN_EINVAL;
   const sgdn_problem& pr = *prob;
   if (pr.batch < 1 || pr.seqlen != 1 || pr.n_qk < 1 || pr.n_v < 1) return SGDN_EINVAL;
+  if (pr.cu_seqlens != nullptr) return SGDN_EINVAL;
   if (pr.dtype != SGDN_F32 && pr.dtype != SGDN_BF16) return SGDN_EINVAL;
   if (pr.o_dtype != SGDN_F32 && pr.o_dtype != SGDN_BF16) return SGDN_EINVAL;
   if (pr.d_k != 128 || pr.d_v != 128 || pr.n_v % pr.n_qk != 0) return SGDN_EUNSUPPORTED;
@@ -284,12 +301,13 @@ int sgdn_select(const sgdn_problem* prob, const float* score, const float* gamma
   SelectArgs sa{};
   sa.score = score; sa.gamma = gamma; sa.eta = eta;
   sa.B = pl.B; sa.C = pl.C; sa.keep_bp = budget_bp(params->keep_budget);
+  sa.cu = pl.cu; sa.T = pl.T;
   sa.rank = at<int32_t>(ws, pl, B_RANK); sa.tierinfo = at<int32_t>(ws, pl, B_TINFO);
   sa.mask = mask; sa.tier = tier; sa.row_pair = row_pair; sa.row_ptr = row_ptr; sa.col = col;
   sa.pred = pred; sa.group_slot = group_slot; sa.event_slot = at<int32_t>(ws, pl, B_ESLOT);
   sa.Emax = NP_SPARSE * pl.kH; sa.G = pl.G;
   sa.stats = stats; sa.mask_in = nullptr;
-  SGDN_TRY(launch_select_full(sa, pl.kL, pl.kM, pl.kH, s));
+  SGDN_TRY(launch_select_full(sa, s));
   return SGDN_OK;
 }
 
@@ -311,16 +329,18 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
 
   // intra: local solve, U, staged Cb, tail score, gamma
   mark(dbg, SGDN_EV_START, s);
+  if ((st = chunk_table(pl, ws, s)) != SGDN_OK) return st;
   SGDN_TRY(launch_intra(intra_args(pl, ws, k, v, a, beta, 1), pl.bf16, s));
   mark(dbg, SGDN_EV_INTRA, s);
-  PrefixArgs pa{at<float>(ws, pl, B_GAMMA), at<double>(ws, pl, B_P), pl.B, pl.Nv, pl.C};
+  PrefixArgs pa{at<float>(ws, pl, B_GAMMA), at<double>(ws, pl, B_P), pl.B, pl.Nv, pl.C,
+                pl.cu, pl.T};
   SGDN_TRY(launch_prefix(pa, s));
   mark(dbg, SGDN_EV_PREFIX, s);
   if ((st = debug_copies(pl, ws, dbg, s, 1)) != SGDN_OK) return st;
 
   // selector and event layout
   if (mask_override == nullptr) {
-    GateArgs ga{z, params->norm_weight, at<float>(ws, pl, B_ETA), pl.B, pl.T, pl.Nv, pl.C};
+    GateArgs ga{z, params->norm_weight, at<float>(ws, pl, B_ETA), pl.B, pl.T, pl.Nv, pl.C, pl.cu};
     SGDN_TRY(launch_gate(ga, pl.bf16, s));
   }
   mark(dbg, SGDN_EV_GATE, s);
@@ -329,6 +349,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   sa.score = at<float>(ws, pl, B_SCORE); sa.gamma = at<float>(ws, pl, B_GAMMA);
   sa.eta = at<float>(ws, pl, B_ETA);
   sa.B = pl.B; sa.C = pl.C; sa.keep_bp = budget_bp(params->keep_budget);
+  sa.cu = pl.cu; sa.T = pl.T;
   sa.rank = at<int32_t>(ws, pl, B_RANK); sa.tierinfo = at<int32_t>(ws, pl, B_TINFO);
   sa.mask = at<uint8_t>(ws, pl, B_MASK); sa.tier = at<uint8_t>(ws, pl, B_TIER);
   sa.row_pair = at<int32_t>(ws, pl, B_ROWPAIR); sa.row_ptr = at<int32_t>(ws, pl, B_ROWPTR);
@@ -337,7 +358,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   sa.Emax = Emax; sa.G = pl.G;
   sa.stats = stats ? static_cast<void*>(stats) : at<void>(ws, pl, B_STATS);
   sa.mask_in = mask_override;
-  SGDN_TRY(launch_select_full(sa, pl.kL, pl.kM, pl.kH, s));
+  SGDN_TRY(launch_select_full(sa, s));
   mark(dbg, SGDN_EV_SELECT, s);
   if (dbg != nullptr) {
     if (dbg->score) SGDN_TRY(hipMemcpyAsync(dbg->score, sa.score, (size_t)pl.B * pl.Nv * pl.C * 4, hipMemcpyDeviceToDevice, s));
@@ -369,6 +390,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   ha.fac = at<float>(ws, pl, B_FAC); ha.rec = ea.rec; ha.P = at<double>(ws, pl, B_P);
   ha.s0 = s0; ha.s_final = s_final; ha.snap = at<void>(ws, pl, B_SNAP);
   ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 1;
+  ha.cu = nullptr; ha.T = pl.T;
   ha.row_pair = sa.row_pair; ha.row_ptr = sa.row_ptr; ha.col = sa.col; ha.event_slot = sa.event_slot;
   ha.Emax = Emax; ha.snap_cap = pl.snap_cap;
   SGDN_TRY(launch_hscan(ha, pl.bf16, s));
@@ -380,6 +402,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   oa.o_bf16 = prob->o_dtype == SGDN_BF16;
   oa.g = at<float>(ws, pl, B_G); oa.gamma = at<float>(ws, pl, B_GAMMA); oa.P = at<double>(ws, pl, B_P);
   oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
+  oa.cu = pl.cu;
   oa.sparse = 1; oa.pred = sa.pred; oa.group_slot = sa.group_slot; oa.snap_cap = pl.snap_cap;
   SGDN_TRY(launch_ochunk(oa, pl.bf16, s));
   mark(dbg, SGDN_EV_O, s);

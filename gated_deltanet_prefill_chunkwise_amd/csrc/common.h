@@ -187,4 +187,21 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Tokens of sequence b.  Packed variable-length batches give offsets cu
+// [B + 1] (sequence b is tokens cu[b] .. cu[b+1] - 1, its length clamped to
+// [0, T]); without them sequence b is tokens b T .. b T + T - 1.  The offsets
+// are read through the scalar cache (they are written before the launch), so
+// reading them adds no wait on the vector memory counter.
+typedef const __attribute__((address_space(4))) int32_t cint32;   // scalar-cache reads
+
+struct SeqSpan { int tok0, len; };
+__device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, int b, int T) {
+  if (cu == nullptr) return SeqSpan{b * T, T};
+  const int bb = __builtin_amdgcn_readfirstlane(b);
+  const cint32* c = (const cint32*)cu;
+  const int s = c[bb], e = c[bb + 1];
+  return SeqSpan{s, min(max(e - s, 0), T)};
+}
+__device__ __forceinline__ int chunks_of(int len) { return (len + L - 1) / L; }
+
 }  // namespace sgdn

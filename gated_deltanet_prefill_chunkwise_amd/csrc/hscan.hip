@@ -41,7 +41,6 @@ namespace {
 
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
-typedef const __attribute__((address_space(4))) int32_t cint32;
 
 constexpr int NLD = 2;          // loader waves
 constexpr int W_COMPUTE = 0;    // wave roles
@@ -169,13 +168,18 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
     pg = id >> 4;
     local = id & 15;
   }
-  const int row = pg / B, b = pg % B;
+  // Packed sequences (dense): sequence-major, so the pair groups dispatched
+  // together belong to one sequence and their chains are equally long (they
+  // start and finish together and keep sharing the pair's lines in L2).
+  const bool seq_major = !SPARSE && p.cu != nullptr;
+  const int row = seq_major ? pg % NP : pg / B, b = seq_major ? pg / NP : pg % B;
   const int hh = local >> 3, slice = local & 7;
   const int pr = SPARSE ? p.row_pair[b * NP + row] : row;
   const int h = 2 * pr + hh;
   const int dv0 = 16 * slice;
 
-  int i0 = 0, i1 = C;
+  // dense: every chunk is an event (a packed sequence's valid chunks only)
+  int i0 = 0, i1 = p.cu == nullptr ? C : chunks_of(seq_span(p.cu, b, p.T).len);
   if constexpr (SPARSE) {
     i0 = p.row_ptr[b * (NP + 1) + row];
     i1 = p.row_ptr[b * (NP + 1) + row + 1];

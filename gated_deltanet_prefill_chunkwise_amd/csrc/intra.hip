@@ -136,7 +136,9 @@ __device__ __forceinline__ CoefFrag<E> coef_frag(const float* sCt, const float* 
   return f;
 }
 
-template <typename E, bool BA, bool SPARSE>
+// VARLEN: packed sequences (offsets in p.cu); the dense-layout instance has
+// no offset reads at all.
+template <typename E, bool BA, bool SPARSE, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
   using I = inter_t<E>;
   __shared__ __align__(16) E sK[L * KS];      // key tile, row-major [t][dk]
@@ -150,7 +152,28 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
   int tid = threadIdx.x;
   const int w_uniform = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = p.T, Nq = p.Nq, Nv = p.Nv, C = p.C;
-  const int n_items = p.B * C * Nq;
+  const int32_t* const cu = VARLEN ? p.cu : nullptr;
+  // items are (chunk, head pair); packed sequences enumerate their valid
+  // chunks from the chunk table, the dense layout every (b, c)
+  const int n_items = VARLEN ? ((const cint32*)p.chunks)[(size_t)p.B * C] * Nq : p.B * C * Nq;
+  // item -> (sequence b, chunk c, head pair pq) and the sequence's tokens
+  struct Item { int b, c, pq, tok0, len; };
+  auto locate = [&](int item) __attribute__((always_inline)) {
+    Item x;
+    x.pq = item % Nq;
+    if constexpr (VARLEN) {
+      const int v = ((const cint32*)p.chunks)[__builtin_amdgcn_readfirstlane(item / Nq)];
+      x.b = v / C;
+      x.c = v - x.b * C;
+    } else {
+      x.c = (item / Nq) % C;
+      x.b = item / (Nq * C);
+    }
+    const SeqSpan sp = seq_span(cu, x.b, T);
+    x.tok0 = sp.tok0;
+    x.len = sp.len;
+    return x;
+  };
   const E* K = static_cast<const E*>(p.k);
   const E* V = static_cast<const E*>(p.v);
   const E* BETA = static_cast<const E*>(p.beta);
@@ -161,38 +184,52 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
   // ---- operand registers of the item being staged (loaded one item ahead)
   frag_t<E> kreg[4], v0reg[4], v1reg[4];
   float areg = 0.f, breg = 0.f;
-  auto load_kv = [&](int item, frag_t<E>* kr, frag_t<E>* vr, int hh, bool with_k) {
-    const int pq = item % Nq, c = (item / Nq) % C, b = item / (Nq * C);
+  // Rows past the end of the item's sequence read its last token and are
+  // zeroed when staged (a = beta = 0 there, so they neither decay nor write
+  // the state).  A chunk wholly past the end of a shorter packed sequence
+  // loads nothing (its rows may lie past the end of the arrays).
+  auto load_kv = [&](const Item& x, frag_t<E>* kr, frag_t<E>* vr, int hh, bool with_k) {
+    if (!VARLEN || x.c * L < x.len) {   // always true for the dense layout
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int q = tid + 256 * it, r = q >> 4, c8 = (q & 15) * 8;
-      const int t = min(c * L + r, T - 1);
-      if (with_k) kr[it] = ld8(K + ((size_t)(b * T + t) * Nq + pq) * DK + c8);
-      vr[it] = ld8(V + ((size_t)(b * T + t) * Nv + 2 * pq + hh) * DV + c8);
+      for (int it = 0; it < 4; ++it) {
+        const int q = tid + 256 * it, r = q >> 4, c8 = (q & 15) * 8;
+        const size_t tok = (size_t)(x.tok0 + min(x.c * L + r, x.len - 1));
+        if (with_k) kr[it] = ld8(K + (tok * Nq + x.pq) * DK + c8);
+        vr[it] = ld8(V + (tok * Nv + 2 * x.pq + hh) * DV + c8);
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        if (with_k) kr[it] = zero_frag<E>();
+        vr[it] = zero_frag<E>();
+      }
     }
   };
-  auto load_ab = [&](int item) {
-    const int pq = item % Nq, c = (item / Nq) % C, b = item / (Nq * C);
-    const int hh = (tid >> 6) & 1, t = min(c * L + (tid & 63), T - 1);
-    const size_t idx = (size_t)(b * T + t) * Nv + 2 * pq + hh;
-    areg = p.a[idx];
-    breg = to_f(BETA[idx]);
+  auto load_ab = [&](const Item& x) {
+    areg = 0.f;
+    breg = 0.f;
+    if (!VARLEN || x.c * L < x.len) {
+      const int hh = (tid >> 6) & 1, t = min(x.c * L + (tid & 63), x.len - 1);
+      const size_t idx = (size_t)(x.tok0 + t) * Nv + 2 * x.pq + hh;
+      areg = p.a[idx];
+      breg = to_f(BETA[idx]);
+    }
   };
   // rows past the sequence end are zero
-  auto mask_rows = [&](int item, frag_t<E>* r) {
-    const int c = (item / Nq) % C;
+  auto mask_rows = [&](const Item& x, frag_t<E>* r) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int row = (tid + 256 * it) >> 4;
-      if (c * L + row >= T) r[it] = zero_frag<E>();
+      if (x.c * L + row >= x.len) r[it] = zero_frag<E>();
     }
   };
 
   int item = blockIdx.x;
   if (item < n_items) {
-    load_kv(item, kreg, v0reg, 0, true);
-    load_ab(item);
-    load_kv(item, kreg, v1reg, 1, false);
+    const Item x = locate(item);
+    load_kv(x, kreg, v0reg, 0, true);
+    load_ab(x);
+    load_kv(x, kreg, v1reg, 1, false);
   }
   // The first item's operands are complete before the loop: otherwise the
   // wait counts at the loop head, merged over this path (few requests after
@@ -207,14 +244,14 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     int w = w_uniform;
     asm volatile("" : "+s"(w), "+v"(tid));
     const int lane = tid & 63, n16 = lane & 15, g4 = lane >> 4;
-    const int pq = item % Nq, c = (item / Nq) % C, b = item / (Nq * C);
-    const int t0 = c * L;
-    const int next = min(item + (int)gridDim.x, n_items - 1);
+    const Item cur = locate(item);
+    const Item nxt = locate(min(item + (int)gridDim.x, n_items - 1));
+    const int b = cur.b, c = cur.c, pq = cur.pq, len = cur.len;
     lds_barrier();  // the previous item's readers of sK, sV, sg are done
 
     // ---- stage keys and the first head's values; decay prefix of both heads
-    mask_rows(item, kreg);
-    mask_rows(item, v0reg);
+    mask_rows(cur, kreg);
+    mask_rows(cur, v0reg);
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int q = tid + 256 * it, r = q >> 4, c8 = (q & 15) * 8;
@@ -223,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     }
     if (tid < 128) {
       const int hh = tid >> 6, h = 2 * pq + hh;
-      const bool live = t0 + lane < T;
+      const bool live = c * L + lane < len;
       float x = live ? areg : 0.f;
       const float bv = live ? breg : 0.f;
       // inclusive prefix over the chunk (g, Sec. 2.1)
@@ -243,8 +280,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     }
     lds_barrier();
     // next item's keys, first-head values and gates (registers are free now)
-    load_kv(next, kreg, v0reg, 0, true);
-    load_ab(next);
+    load_kv(nxt, kreg, v0reg, 0, true);
+    load_ab(nxt);
 
     // ---- fragment-major key tile (K^T operand blocks) for the H and
     //      deferred-W stages
@@ -296,13 +333,13 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
       if (hh == 1) {
         // the first head's products are done: second head's values in, and
         // the next item's second-head values requested
-        mask_rows(item, v1reg);
+        mask_rows(cur, v1reg);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
           const int q = tid + 256 * it, r = q >> 4, c8 = (q & 15) * 8;
           *reinterpret_cast<frag_t<E>*>(&sV[r * KS + c8]) = v1reg[it];
         }
-        load_kv(next, kreg, v1reg, 1, false);
+        load_kv(nxt, kreg, v1reg, 1, false);
       }
       // ---- diagonal blocks: C_ii = (I + M_ii)^{-1}, wave w takes block w,
       //      lane j column j, forward substitution (Eq. (8))
@@ -470,9 +507,9 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
   }
 }
 
-template <typename E, bool BA, bool SPARSE>
+template <typename E, bool BA, bool SPARSE, bool VARLEN>
 hipError_t launch_one(const IntraArgs& a, hipStream_t s) {
-  const auto fn = intra_kernel<E, BA, SPARSE>;
+  const auto fn = intra_kernel<E, BA, SPARSE, VARLEN>;
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -487,14 +524,19 @@ hipError_t launch_one(const IntraArgs& a, hipStream_t s) {
 
 }  // namespace
 
+template <typename E, bool BA, bool SPARSE>
+hipError_t launch_vl(const IntraArgs& a, hipStream_t s) {
+  return a.cu != nullptr ? launch_one<E, BA, SPARSE, true>(a, s) : launch_one<E, BA, SPARSE, false>(a, s);
+}
+
 hipError_t launch_intra(const IntraArgs& a, int bf16, hipStream_t s) {
   const bool ba = a.solve == 1, sparse = a.Cb != nullptr;
   if (bf16) {
-    if (ba) return sparse ? launch_one<sgdn::bf16, true, true>(a, s) : launch_one<sgdn::bf16, true, false>(a, s);
-    return sparse ? launch_one<sgdn::bf16, false, true>(a, s) : launch_one<sgdn::bf16, false, false>(a, s);
+    if (ba) return sparse ? launch_vl<sgdn::bf16, true, true>(a, s) : launch_vl<sgdn::bf16, true, false>(a, s);
+    return sparse ? launch_vl<sgdn::bf16, false, true>(a, s) : launch_vl<sgdn::bf16, false, false>(a, s);
   }
-  if (ba) return sparse ? launch_one<float, true, true>(a, s) : launch_one<float, true, false>(a, s);
-  return sparse ? launch_one<float, false, true>(a, s) : launch_one<float, false, false>(a, s);
+  if (ba) return sparse ? launch_vl<float, true, true>(a, s) : launch_vl<float, true, false>(a, s);
+  return sparse ? launch_vl<float, false, true>(a, s) : launch_vl<float, false, false>(a, s);
 }
 
 }  // namespace sgdn

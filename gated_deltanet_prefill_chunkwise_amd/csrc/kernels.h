@@ -35,6 +35,10 @@ namespace sgdn {
 struct IntraArgs {
   const void* k; const void* v; const float* a; const void* beta;
   int B, T, Nq, Nv, C, solve;
+  const int32_t* cu;        // packed sequence offsets [B+1] or null
+  // packed sequences: entry i = b C + c of the i-th valid chunk, the number
+  // of valid chunks at index B C (written by the chunk-table kernel)
+  const int32_t* chunks;
   float* g; float* gamma; float* fac;
   void* U; void* W; void* Cb; void* KT;
   float* score;
@@ -42,7 +46,13 @@ struct IntraArgs {
 
 struct PrefixArgs {
   const float* gamma; double* P; int B, Nv, C;
+  const int32_t* cu; int T;   // packed sequences: gamma is read for valid chunks only
 };
+
+// Valid chunks of packed sequences, in (sequence, chunk) order.
+//   table [B*C + 1 + B + 1]: entries b C + c, the count at index B C, then
+//   the per-sequence offsets into the entries
+struct ChunkTableArgs { const int32_t* cu; int32_t* table; int B, T, C; };
 
 // Chain scan over the events of one value head, one dv slice of 16 columns
 // per workgroup.  Dense: every chunk is an event, W from the intra kernel.
@@ -55,6 +65,7 @@ struct HScanArgs {
   void* snap;               // snapshots
   int B, Nq, Nv, C;
   int sparse;
+  const int32_t* cu; int T;  // packed sequences: a dense chain stops at its valid chunks
   // sparse metadata (per batch)
   const int32_t* row_pair;  // [B][NP]
   const int32_t* row_ptr;   // [B][NP+1]
@@ -69,6 +80,7 @@ struct OChunkArgs {
   const float* g; const float* gamma; const double* P;
   void* o; int o_bf16;
   int B, T, Nq, Nv, C, G;
+  const int32_t* cu;          // packed sequence offsets [B+1] or null
   int sparse;
   const int32_t* pred;        // [B][NP][G]
   const int32_t* group_slot;  // [B][NP][G]
@@ -89,11 +101,15 @@ struct S0PrepArgs { const float* s0; void* s0T; int B, Nv; };
 
 struct GateArgs {
   const void* z; const float* w; float* eta; int B, T, Nv, C;
+  const int32_t* cu;        // packed sequence offsets [B+1] or null
 };
 
 struct SelectArgs {
   const float* score; const float* gamma; const float* eta;
   int B, C, keep_bp;
+  // packed sequence offsets [B+1] or null: sequence b has ceil(len_b / 64)
+  // valid chunks (arrays keep the stride C); T bounds every length
+  const int32_t* cu; int T;
   int32_t* rank;        // [B][16][C]   workspace
   int32_t* tierinfo;    // [B][8]       workspace: k_L, k_M, k_H, n_H, n_M
   uint8_t* mask; uint8_t* tier;
@@ -120,12 +136,13 @@ struct DecodeArgs {
 
 hipError_t launch_intra(const IntraArgs& a, int bf16, hipStream_t s);
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s);
+hipError_t launch_chunk_table(const ChunkTableArgs& a, hipStream_t s);
 hipError_t launch_hscan(const HScanArgs& a, int bf16, hipStream_t s);
 hipError_t launch_ochunk(const OChunkArgs& a, int bf16, hipStream_t s);
 hipError_t launch_evrec(const EvRecArgs& a, hipStream_t s);
 hipError_t launch_s0prep(const S0PrepArgs& a, int bf16, hipStream_t s);
 hipError_t launch_gate(const GateArgs& a, int bf16, hipStream_t s);
-hipError_t launch_select_full(const SelectArgs& a, int kL, int kM, int kH, hipStream_t s);
+hipError_t launch_select_full(const SelectArgs& a, hipStream_t s);
 hipError_t launch_deferred_w(const DeferredWArgs& a, int bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int bf16, hipStream_t s);
 hipError_t launch_debug_u(const void* Ut, float* U, int B, int Nv, int C, int bf16, hipStream_t s);

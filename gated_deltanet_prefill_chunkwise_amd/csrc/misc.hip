@@ -10,14 +10,18 @@ namespace {
 // P_0 = 0, P_{c+1} = P_c + gamma_c in fp64 (SparseGDN reading notes,
 // Sec. 2.6, Eqs. (19)-(20)).  One wave per (batch, head): each lane sums a
 // contiguous run of chunks, then an exclusive wave scan joins the runs.
+// Chunks past the end of a shorter packed sequence retain everything
+// (gamma = 0 there; their gamma entries are not read).
 __global__ __launch_bounds__(64) void prefix_kernel(PrefixArgs p) {
   const int bh = blockIdx.x, lane = threadIdx.x, C = p.C;
+  const int Cv = p.cu == nullptr ? C : chunks_of(seq_span(p.cu, bh / p.Nv, p.T).len);
   const float* gm = p.gamma + (size_t)bh * C;
   double* P = p.P + (size_t)bh * (C + 1);
   const int per = (C + 63) / 64;
   const int lo = lane * per, hi = min(C, lo + per);
+  auto gam = [&](int c) { return c < Cv ? (double)gm[c] : 0.0; };
   double run = 0.0;
-  for (int c = lo; c < hi; ++c) run += (double)gm[c];
+  for (int c = lo; c < hi; ++c) run += gam(c);
   double incl = run;
   for (int off = 1; off < 64; off <<= 1) {
     const double y = __shfl_up(incl, off, 64);
@@ -26,8 +30,54 @@ __global__ __launch_bounds__(64) void prefix_kernel(PrefixArgs p) {
   double acc = incl - run;
   if (lane == 0) P[0] = 0.0;
   for (int c = lo; c < hi; ++c) {
-    acc += (double)gm[c];
+    acc += gam(c);
     P[c + 1] = acc;
+  }
+}
+
+// Table of the valid chunks of packed sequences (one workgroup): per-thread
+// runs of sequences are counted, scanned in LDS, their offsets stored, and
+// the entries b C + c then written by all threads, each finding its
+// sequence by binary search over the offsets.
+__global__ __launch_bounds__(1024) void chunk_table_kernel(ChunkTableArgs p) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x, B = p.B;
+  const size_t BC = (size_t)B * p.C;
+  int32_t* off = p.table + BC + 1;   // [B + 1]
+  auto nchunks = [&](int b) {
+    const int n = min(max(p.cu[b + 1] - p.cu[b], 0), p.T);
+    return chunks_of(n);
+  };
+  const int per = (B + 1023) / 1024;
+  const int lo = min(tid * per, B), hi = min(lo + per, B);
+  int sum = 0;
+  for (int b = lo; b < hi; ++b) sum += nchunks(b);
+  part[tid] = sum;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int v = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int base = part[tid] - sum;
+  for (int b = lo; b < hi; ++b) {
+    off[b] = base;
+    base += nchunks(b);
+  }
+  const int total = part[1023];
+  if (tid == 0) {
+    off[B] = total;
+    p.table[BC] = total;
+  }
+  __syncthreads();
+  for (int i = tid; i < total; i += 1024) {
+    int l = 0, r = B - 1;            // last b with off[b] <= i
+    while (l < r) {
+      const int m = (l + r + 1) >> 1;
+      if (off[m] <= i) l = m; else r = m - 1;
+    }
+    p.table[i] = l * p.C + (i - off[l]);
   }
 }
 
@@ -45,19 +95,21 @@ __global__ __launch_bounds__(256) void s0prep_kernel(S0PrepArgs p) {
 }
 
 // eta_h = mean over the 4C samples of (w_v SiLU(z[64c + 8 + 16a, h, v]))^2,
-// v = 73 (4c + a) mod 128 (SparseGDN reading notes, Sec. 2.4, Eq. (11)).
+// v = 73 (4c + a) mod 128 (SparseGDN reading notes, Sec. 2.4, Eq. (11)), C the
+// sequence's own (valid) chunks; 0 for an empty sequence.
 template <typename E>
 __global__ __launch_bounds__(256) void gate_kernel(GateArgs p) {
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const E* z = static_cast<const E*>(p.z);
-  const int ns = 4 * p.C;
+  const SeqSpan sp = seq_span(p.cu, b, p.T);
+  const int ns = 4 * chunks_of(sp.len);
   float acc = 0.f;
   for (int j = tid; j < ns; j += 256) {
     const int c = j >> 2, a = j & 3;
     const int pos = c * L + 8 + 16 * a;
     const int v = (73 * j) & (DV - 1);
-    if (pos < p.T) {
-      const float x = to_f(z[((size_t)(b * p.T + pos) * p.Nv + h) * DV + v]);
+    if (pos < sp.len) {
+      const float x = to_f(z[((size_t)(sp.tok0 + pos) * p.Nv + h) * DV + v]);
       const float wv = p.w ? p.w[v] : 1.f;
       const float s = wv * (x / (1.f + __expf(-x)));
       acc += s * s;
@@ -67,7 +119,7 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs p) {
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if ((tid & 63) == 0) red[tid >> 6] = acc;
   __syncthreads();
-  if (tid == 0) p.eta[(size_t)b * p.Nv + h] = (red[0] + red[1] + red[2] + red[3]) / (float)ns;
+  if (tid == 0) p.eta[(size_t)b * p.Nv + h] = ns ? (red[0] + red[1] + red[2] + red[3]) / (float)ns : 0.f;
 }
 
 // Deferred W of kept events only (SparseGDN reading notes, Sec. 2.5,
@@ -171,6 +223,11 @@ __global__ __launch_bounds__(256) void debug_u_kernel(const void* Ut_, float* U)
 
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(prefix_kernel, dim3(a.B * a.Nv), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_table(const ChunkTableArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

@@ -70,7 +70,11 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int n16 = lane & 15, g4 = lane >> 4;
   const int c0 = 2 * r;
-  const bool has1 = c0 + 1 < C;
+  // a group past the end of its (shorter, packed) sequence has no outputs;
+  // the whole workgroup leaves before any load or barrier
+  const SeqSpan sp = seq_span(p.cu, b, T);
+  if (c0 * L >= sp.len) return;
+  const bool has1 = c0 + 1 < chunks_of(sp.len);
   // Every group is computed as two chunks (straight-line code); a group
   // without a second chunk reads zeros for its Q, K, U' and decays there,
   // so those products vanish, and its rows are not stored.
@@ -109,14 +113,14 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
     const int q = tid + 512 * it;
     const int rr = q >> 4, c8 = (q & 15) * 8;
     const int t = c0 * L + rr;
-    qst[it] = (t < T) ? ld8(Qin + ((size_t)(b * T + t) * Nq + pr) * DK + c8) : zero_frag<E>();
+    qst[it] = (t < sp.len) ? ld8(Qin + ((size_t)(sp.tok0 + t) * Nq + pr) * DK + c8) : zero_frag<E>();
   }
   frag_t<E> kf[4];
   {
     const int ts = c0 * L + 16 * w + n16;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      kf[ks] = (ts < T) ? ld8(Kin + ((size_t)(b * T + ts) * Nq + pr) * DK + 32 * ks + 8 * g4)
+      kf[ks] = (ts < sp.len) ? ld8(Kin + ((size_t)(sp.tok0 + ts) * Nq + pr) * DK + 32 * ks + 8 * g4)
                         : zero_frag<E>();
   }
   const int dvr = 16 * w + n16;
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   // they are not live across phase 1; their latency overlaps S^T Q^T)
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    ufr[ks] = (c0 + (ks >> 1) < C) ? ld8(Up + ((bh * C + c0 + (ks >> 1)) * DV + dvr) * L + 32 * (ks & 1) + 8 * g4)
+    ufr[ks] = ((ks >> 1) == 0 || has1) ? ld8(Up + ((bh * C + c0 + (ks >> 1)) * DV + dvr) * L + 32 * (ks & 1) + 8 * g4)
                                    : zero_frag<I>();
   __syncthreads();
 
@@ -229,8 +233,8 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
     const int q = tid + 512 * it;
     const int t = q >> 5, c4 = (q & 31) * 4;
     const int tok = c0 * L + t;
-    if (tok < T)
-      st4o<OT>(O + ((size_t)(b * T + tok) * Nv + h) * DV + c4, *reinterpret_cast<const f32x4*>(&sO[t * OSTR + c4]));
+    if (tok < sp.len)
+      st4o<OT>(O + ((size_t)(sp.tok0 + tok) * Nv + h) * DV + c4, *reinterpret_cast<const f32x4*>(&sO[t * OSTR + c4]));
   }
 }
 

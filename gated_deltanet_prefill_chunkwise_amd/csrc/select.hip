@@ -63,6 +63,36 @@ __device__ double powi_fixed(double r, int n) {
   return res;
 }
 
+// Valid chunks of sequence b (Sec. 2.4 counts, ranks and anchors them per
+// sequence); arrays keep the stride p.C.
+__device__ int valid_chunks(const SelectArgs& p, int b) {
+  return p.cu == nullptr ? p.C : chunks_of(seq_span(p.cu, b, p.T).len);
+}
+
+// k = clip(round(rho C), 2, C) (Sec. 2.4.3) for the budget in basis points,
+// in exact integer arithmetic with halves rounded up; rho = (0.08, 0.30, 0.95)
+// at 2900 bp, scaled linearly below it and towards 1 above it.  k = 1 when
+// C = 1 and 0 for an empty sequence.
+__device__ void tier_counts(int C, int bp, int k[3]) {
+  const int pct[3] = {8, 30, 95};
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    if (C == 1) { k[i] = 1; continue; }
+    long long num, den;
+    if (bp <= 2900) {
+      num = (long long)pct[i] * bp * C;
+      den = 290000;
+    } else {
+      num = (long long)C * (710000LL - (long long)(100 - pct[i]) * (10000 - bp));
+      den = 710000;
+    }
+    long long kk = (2 * num + den) / (2 * den);
+    if (kk < 2) kk = 2;
+    if (kk > C) kk = C;
+    k[i] = (int)kk;
+  }
+}
+
 // L_h = sum_{j=1}^{C-2} r^j in closed form (Eq. (11)).
 __device__ double lifetime(double r, int C) {
   const int n = C - 2;
@@ -82,9 +112,9 @@ __global__ __launch_bounds__(1024) void select_rank_kernel(SelectArgs p) {
   __shared__ double snorm[2];
   const int blk = blockIdx.x, pp = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int C = p.C;
-  const float* s0 = p.score + ((size_t)b * NV + 2 * pp) * C;
-  const float* s1 = s0 + C;
+  const int CS = p.C, C = valid_chunks(p, b);
+  const float* s0 = p.score + ((size_t)b * NV + 2 * pp) * CS;
+  const float* s1 = s0 + CS;
   if (w < 2) {
     const float* s = w ? s1 : s0;
     double acc = 0.0;
@@ -103,7 +133,7 @@ __global__ __launch_bounds__(1024) void select_rank_kernel(SelectArgs p) {
     sq[c] = 0.5 * (t0 + t1);
   }
   __syncthreads();
-  int32_t* rk = p.rank + ((size_t)b * NP + pp) * C;
+  int32_t* rk = p.rank + ((size_t)b * NP + pp) * CS;
   const int c = RANK_CHUNKS * blk + (tid >> 3), part = tid & 7;
   int r = 0;
   const bool inner = c >= 1 && c <= C - 2;
@@ -138,26 +168,30 @@ __device__ double split_score(const double* vals, int n, int k, int lane) {
 // Wave w forms the per-head sums of the two heads of pair w (each sum is one
 // wave's lane-interleaved sum, as everywhere in this file); wave 0 then takes
 // the decisions.
-__global__ __launch_bounds__(1024) void select_tier_kernel(SelectArgs p, int kL, int kM, int kH) {
+__global__ __launch_bounds__(1024) void select_tier_kernel(SelectArgs p) {
   __shared__ double sL[NV], sGv[NV], slm[NV], smh[NV];
   __shared__ double sxm[NP], sxh[NP], svals[NP];
   __shared__ int sorder[NP], shigh[NP];
-  const int b = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, C = p.C;
-  const float* sc = p.score + (size_t)b * NV * C;
-  const float* gm = p.gamma + (size_t)b * NV * C;
+  const int b = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int CS = p.C, C = valid_chunks(p, b);
+  int kk[3];
+  tier_counts(C, p.keep_bp, kk);
+  const int kL = kk[0], kM = kk[1], kH = kk[2];
+  const float* sc = p.score + (size_t)b * NV * CS;
+  const float* gm = p.gamma + (size_t)b * NV * CS;
   const float* et = p.eta + (size_t)b * NV;
-  const int32_t* rk = p.rank + (size_t)b * NP * C;
+  const int32_t* rk = p.rank + (size_t)b * NP * CS;
 
   const int lo = C > 16 ? C - 16 : 0, nwin = C - lo;
   for (int h = 2 * wv; h < 2 * wv + 2; ++h) {
-    const double x = lane < nwin ? exp2_fixed((double)gm[h * C + lo + lane]) : 0.0;
+    const double x = lane < nwin ? exp2_fixed((double)gm[h * CS + lo + lane]) : 0.0;
     const double tot = wave_sum(x);
     if (lane == 0) sL[h] = lifetime(tot / nwin, C);
     const int pp = h >> 1;
     double alm = 0.0, amh = 0.0;
     for (int c = lane; c < C; c += 64) {
-      const int r = rk[pp * C + c];
-      const double xs = (double)sc[h * C + c];
+      const int r = rk[pp * CS + c];
+      const double xs = (double)sc[h * CS + c];
       alm = alm + ((r >= kL - 2 && r < kM - 2) ? xs : 0.0);
       amh = amh + ((r >= kM - 2 && r < kH - 2) ? xs : 0.0);
     }
@@ -251,7 +285,7 @@ __global__ __launch_bounds__(1024) void select_tier_kernel(SelectArgs p, int kL,
 // tier), kept chunks ascending, predecessor of every output group and
 // compact-snapshot slots numbered over the referenced events in CSR order.
 // One block of 16 waves per sequence; wave w works on pair w or row w.
-__global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p, int kL, int kM, int kH) {
+__global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
   // Wave w handles head pair w.  Each pair's kept chunks are held as 64-bit
   // words (bit l of word i: chunk 64 i + l), and so are its referenced events,
   // so the CSR columns, the snapshot slots and the group predecessors follow
@@ -261,9 +295,16 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p, int kL, int 
   __shared__ int s_ref[NP], s_refbase[NP + 1];
   __shared__ unsigned long long s_kept[NP][NWMAX], s_refd[NP][NWMAX];
   const int b = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int C = p.C, G = p.G, NW = (C + 63) / 64;
+  // CS, GS: strides of the per-chunk and per-group arrays; C, G: this
+  // sequence's valid chunks and groups.  Chunks past C are not kept (their
+  // mask bytes are written as 0) and groups past G have no predecessor.
+  const int CS = p.C, GS = p.G, NW = (CS + 63) / 64;
+  const int C = valid_chunks(p, b), G = (C + 1) / 2;
+  int kk[3];
+  tier_counts(C, p.keep_bp, kk);
+  const int kL = kk[0], kM = kk[1], kH = kk[2];
   const unsigned long long below = (1ull << lane) - 1ull;
-  uint8_t* mask = p.mask + (size_t)b * NP * C;
+  uint8_t* mask = p.mask + (size_t)b * NP * CS;
   const bool ovr = p.mask_in != nullptr;
   if (tid < NP) s_tier[tid] = ovr ? 0 : p.tier[b * NP + tid];
   __syncthreads();
@@ -278,7 +319,7 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p, int kL, int 
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int c = 64 * (i0 + u) + lane;
-        const size_t idx = (size_t)b * NP * C + (size_t)pp * C + c;
+        const size_t idx = (size_t)b * NP * CS + (size_t)pp * CS + c;
         val[u] = 0;
         if (i0 + u < NW && c < C) val[u] = ovr ? (int)p.mask_in[idx] : p.rank[idx];
       }
@@ -288,10 +329,9 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p, int kL, int 
         if (i < NW) {
           const int c = 64 * i + lane;
           int z = 0;
-          if (c < C) {
+          if (c < C)
             z = ovr ? (val[u] ? 1 : 0) : ((c == 0 || c == C - 1 || (val[u] >= 0 && val[u] < k - 2)) ? 1 : 0);
-            mask[(size_t)pp * C + c] = (uint8_t)z;
-          }
+          if (c < CS) mask[(size_t)pp * CS + c] = (uint8_t)z;
           const unsigned long long bal = __ballot(z);
           if (lane == 0) s_kept[pp][i] = bal;
           cnt += z;
@@ -364,7 +404,7 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p, int kL, int 
       const int c = 64 * i + lane;
       if ((bal >> lane) & 1ull)
         eslot[base + run + __popcll(bal & below)] = ((rb >> lane) & 1ull) ? rbase + rrun + __popcll(rb & below) : -1;
-      if ((c & 1) == 0 && c < C) {
+      if ((c & 1) == 0 && c < CS) {
         const unsigned long long m = bal & below;
         int pc = lastc, ps = lasts;
         if (m) {
@@ -372,7 +412,8 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p, int kL, int 
           pc = 64 * i + el;
           ps = rbase + rrun + __popcll(rb & ((1ull << el) - 1ull));
         }
-        const size_t o = ((size_t)b * NP + pp) * G + (c >> 1);
+        if (c >= C) pc = -1;   // group past the sequence's end
+        const size_t o = ((size_t)b * NP + pp) * GS + (c >> 1);
         p.pred[o] = pc;
         p.group_slot[o] = pc >= 0 ? ps : -1;
       }
@@ -399,17 +440,17 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p, int kL, int 
 
 }  // namespace
 
-hipError_t launch_select_full(const SelectArgs& a, int kL, int kM, int kH, hipStream_t s) {
+hipError_t launch_select_full(const SelectArgs& a, hipStream_t s) {
   if (a.mask_in == nullptr) {
     const int nblk = (a.C + RANK_CHUNKS - 1) / RANK_CHUNKS;
     hipLaunchKernelGGL(select_rank_kernel, dim3(nblk, NP, a.B), dim3(1024), (size_t)a.C * sizeof(double), s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(select_tier_kernel, dim3(a.B), dim3(1024), 0, s, a, kL, kM, kH);
+    hipLaunchKernelGGL(select_tier_kernel, dim3(a.B), dim3(1024), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(layout_kernel, dim3(a.B), dim3(1024), 0, s, a, kL, kM, kH);
+  hipLaunchKernelGGL(layout_kernel, dim3(a.B), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

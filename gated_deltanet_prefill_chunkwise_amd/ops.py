@@ -15,12 +15,13 @@ LIB_PATH = os.path.join(HERE, "libsgdn.so")
 SGDN_F32, SGDN_BF16 = 0, 1
 SOLVES = {"exact": 0, "blockadj": 1}
 EXPORTS = ("sgdn_workspace_bytes", "sgdn_prefill_dense", "sgdn_select",
-           "sgdn_prefill_sparse", "sgdn_status_string")
+           "sgdn_prefill_sparse", "sgdn_decode_step", "sgdn_status_string")
 
 
 class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("batch", "seqlen", "n_qk", "n_v", "d_k", "d_v", "dtype", "solve", "o_dtype")]
+                ("batch", "seqlen", "n_qk", "n_v", "d_k", "d_v", "dtype", "solve", "o_dtype")] + \
+               [("cu_seqlens", ctypes.c_void_p)]
 
 
 class SparseParams(ctypes.Structure):
@@ -102,11 +103,31 @@ def _code(dtype):
     return SGDN_BF16 if dtype == torch.bfloat16 else SGDN_F32
 
 
-def problem(q, v, solve="exact", out_dtype=None) -> Problem:
-    B, T, Nq, d = q.shape
+def batch_shape(q, cu_seqlens=None, max_seqlen=None):
+    """(B, T) of a call.  Packed sequences (``cu_seqlens`` int32 [B + 1] on the
+    device, q [1, N_tok, Nq, d]): B = len(cu_seqlens) - 1 and T = the longest
+    sequence (read back from the device unless ``max_seqlen`` is given)."""
+    if cu_seqlens is None:
+        return q.shape[0], q.shape[1]
+    import torch
+    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    if q.shape[0] != 1:
+        raise ValueError("packed sequences take q, k, v, a, beta, z of batch 1 [1, N_tok, ...]")
+    B = cu_seqlens.numel() - 1
+    if B < 1:
+        raise ValueError("cu_seqlens needs at least two offsets")
+    if max_seqlen is None:
+        max_seqlen = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item())
+    return B, max(int(max_seqlen), 1)
+
+
+def problem(q, v, solve="exact", out_dtype=None, cu_seqlens=None, max_seqlen=None) -> Problem:
+    B, T = batch_shape(q, cu_seqlens, max_seqlen)
+    Nq, d = q.shape[2], q.shape[3]
     Nv, dv = v.shape[2], v.shape[3]
     od = _code(out_dtype) if out_dtype is not None else SGDN_F32
-    return Problem(B, T, Nq, Nv, d, dv, _code(q.dtype), SOLVES[solve], od)
+    return Problem(B, T, Nq, Nv, d, dv, _code(q.dtype), SOLVES[solve], od,
+                   None if cu_seqlens is None else cu_seqlens.data_ptr())
 
 
 def sparse_params(keep_budget=0.29, norm_weight=None, tail=16, r_window=16) -> SparseParams:
@@ -149,10 +170,12 @@ def debug_struct(events=None, **bufs) -> Debug:
 
 
 def prefill_dense(q, k, v, a, beta, s0=None, solve="exact", want_state=True, o=None,
-                  s_final=None, workspace=None, debug=None, stream=None, out_dtype=None):
+                  s_final=None, workspace=None, debug=None, stream=None, out_dtype=None,
+                  cu_seqlens=None, max_seqlen=None):
     """Dense GDN-core prefill; returns (o, s_final).
 
-    o is fp32 unless ``out_dtype`` (or a given ``o``) says otherwise.
+    o is fp32 unless ``out_dtype`` (or a given ``o``) says otherwise.  With
+    ``cu_seqlens`` the inputs hold packed sequences (see ``batch_shape``).
     """
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta")):
@@ -163,8 +186,8 @@ def prefill_dense(q, k, v, a, beta, s0=None, solve="exact", want_state=True, o=N
         out_dtype = o.dtype
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     _check(o, "o", out_dtype)
-    prob = problem(q, v, solve, out_dtype)
-    B, Nv, dv = q.shape[0], v.shape[2], v.shape[3]
+    prob = problem(q, v, solve, out_dtype, cu_seqlens, max_seqlen)
+    B, Nv, dv = prob.batch, v.shape[2], v.shape[3]
     if o is None:
         o = torch.empty(v.shape, dtype=out_dtype, device=v.device)
     if want_state and s_final is None:
@@ -217,14 +240,22 @@ def decode_step(q, k, v, a, beta, state, s_out=None, o=None, out_dtype=None, str
     return o, s_out
 
 
-def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None):
-    """Selector + CSR layout on fp32 statistics; returns a dict of device tensors."""
+def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None, cu_seqlens=None):
+    """Selector + CSR layout on fp32 statistics; returns a dict of device tensors.
+
+    With ``cu_seqlens`` (int32 [B + 1] token offsets) sequence b has only its
+    ceil(len_b / 64) valid chunks; the arrays keep the stride C.
+    """
     import torch
     B, Nv, C = score.shape
     for t, n in ((score, "score"), (gamma, "gamma"), (eta, "eta")):
         _check(t, n, torch.float32)
+    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    if cu_seqlens is not None and cu_seqlens.numel() != B + 1:
+        raise ValueError("cu_seqlens must hold B + 1 offsets")
     T = C * 64
-    prob = Problem(B, T, Nv // 2, Nv, 128, 128, SGDN_BF16, 1, SGDN_F32)
+    prob = Problem(B, T, Nv // 2, Nv, 128, 128, SGDN_BF16, 1, SGDN_F32,
+                   None if cu_seqlens is None else cu_seqlens.data_ptr())
     params = sparse_params(keep_budget)
     nbytes = workspace_bytes(prob, True, params)
     if nbytes == 0:
@@ -256,10 +287,11 @@ def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None):
 def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
                    mask_override=None, s0=None, norm_weight=None, want_state=True, o=None,
                    s_final=None, stats=None, workspace=None, debug=None, stream=None,
-                   out_dtype=None):
+                   out_dtype=None, cu_seqlens=None, max_seqlen=None):
     """SparseGDN prefill; returns (o, s_final, stats[B, 9] int32).
 
-    o is fp32 unless ``out_dtype`` (or a given ``o``) says otherwise.
+    o is fp32 unless ``out_dtype`` (or a given ``o``) says otherwise.  With
+    ``cu_seqlens`` the inputs hold packed sequences (see ``batch_shape``).
     """
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta"), (z, "z")):
@@ -272,9 +304,9 @@ def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
         out_dtype = o.dtype
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     _check(o, "o", out_dtype)
-    prob = problem(q, v, solve, out_dtype)
+    prob = problem(q, v, solve, out_dtype, cu_seqlens, max_seqlen)
     params = sparse_params(keep_budget, norm_weight)
-    B, Nv, dv = q.shape[0], v.shape[2], v.shape[3]
+    B, Nv, dv = prob.batch, v.shape[2], v.shape[3]
     if o is None:
         o = torch.empty(v.shape, dtype=out_dtype, device=v.device)
     if want_state and s_final is None:

@@ -27,6 +27,17 @@
  *   retention; a > 0 is outside the operator's domain).
  * - T need not be a multiple of 64: the last chunk is padded with tokens
  *   that have a = 0, beta = 0, q = k = v = 0; their outputs are not written.
+ * - Packed variable-length batches: with sgdn_problem.cu_seqlens set, the B
+ *   sequences are packed along one token axis (below, "[B, T" then reads
+ *   "[N_tok"): sequence b is tokens cu_seqlens[b] .. cu_seqlens[b+1] - 1 of
+ *   q, k, v, a, beta, z and o, and seqlen is an upper bound on every length
+ *   (longer sequences are cut to seqlen tokens).  Each sequence is computed
+ *   exactly as if it were passed alone: its own chunks (padded at its own
+ *   end), its own s0 / s_final row, and in the sparse path its own valid
+ *   chunks for the selector (Sec. 2.4 ranks, anchors and counts the valid
+ *   chunks of a sequence).  Empty sequences are allowed (s_final = s0).
+ *   Per-chunk workspace arrays and debug outputs keep the stride
+ *   C = ceil(seqlen / 64) per sequence.
  */
 #ifndef SGDN_H
 #define SGDN_H
@@ -63,6 +74,10 @@ typedef struct {
   int32_t dtype;    /* sgdn_dtype of q, k, v, beta, z */
   int32_t solve;    /* sgdn_solve */
   int32_t o_dtype;  /* sgdn_dtype of o */
+  /* DEVICE [batch + 1] int32 token offsets of packed sequences (non-
+   * decreasing, cu_seqlens[0] = 0, cu_seqlens[batch] < 2^31 - seqlen), or
+   * NULL for the dense [B, T] layout.  Read by the kernels, not the host. */
+  const int32_t* cu_seqlens;
 } sgdn_problem;
 
 /* Selector parameters (Sec. 2.4).  keep_budget in (0, 1]: 0.29 gives the
@@ -187,8 +202,8 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k,
  * h / (Nv / Nq):
  *     S' = alpha S + k u^T,  u = beta (v - alpha S^T k),  o = S'^T q / sqrt(d)
  * prob: batch = B sequences, seqlen must be 1, Nv a multiple of Nq,
- * d = dv = 128; dtype applies to q, k, v, beta, o_dtype to o; solve is
- * ignored.
+ * d = dv = 128, cu_seqlens NULL; dtype applies to q, k, v, beta, o_dtype to
+ * o; solve is ignored.
  *   q, k   [B, Nq, d]       dtype
  *   v      [B, Nv, dv]      dtype
  *   a      [B, Nv]          fp32 log2 retention (<= 0)
@@ -198,8 +213,8 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k,
  *                           (updated in place), must not overlap it otherwise
  *   o      [B, Nv, dv]      o_dtype output of the token
  * s_in and s_out must be 16-byte aligned.  Needs no workspace.  SGDN_EINVAL
- * for a null pointer, seqlen != 1, a misaligned state or partially
- * overlapping states. */
+ * for a null pointer, seqlen != 1, cu_seqlens set, a misaligned state or
+ * partially overlapping states. */
 int sgdn_decode_step(const sgdn_problem* prob, const void* q, const void* k,
                      const void* v, const float* a, const void* beta,
                      const float* s_in, float* s_out, void* o, void* stream);

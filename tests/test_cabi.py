@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(L):
 def _prob(**kw):
     from gated_deltanet_prefill_chunkwise_amd import ops
     base = dict(batch=1, seqlen=4096, n_qk=16, n_v=32, d_k=128, d_v=128, dtype=1, solve=0,
-                o_dtype=0)
+                o_dtype=0, cu_seqlens=None)
     base.update(kw)
     return ops.Problem(*[base[n] for n, _ in ops.Problem._fields_])
 
@@ -132,3 +132,4 @@ def test_decode_argument_errors(L):
     assert call(_prob(**one), s_out=ctypes.c_void_p(0x1000 + 4096)) == -1
     assert call(_prob(**one), s_in=ctypes.c_void_p(0x1004), s_out=ctypes.c_void_p(0x1004)) == -1
     assert L.sgdn_decode_step(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert call(_prob(cu_seqlens=0x2000, **one)) == -1      # packed offsets do not apply
