@@ -230,7 +230,7 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   mark(dbg, SGDN_EV_START, s);
   if ((st = chunk_table(pl, ws, s)) != SGDN_OK) return st;
   SGDN_TRY(launch_intra(intra_args(pl, ws, k, v, a, beta, 0), pl.bf16, s));
-  mark_range(dbg, SGDN_EV_INTRA, SGDN_EV_DEFERRED, s);
+  mark(dbg, SGDN_EV_INTRA, s);
   if ((st = debug_copies(pl, ws, dbg, s, 0)) != SGDN_OK) return st;
   if (s0 != nullptr) {
     S0PrepArgs sa{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv};
@@ -240,6 +240,7 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   ea.gamma = at<float>(ws, pl, B_GAMMA); ea.rec = at<int32_t>(ws, pl, B_REC);
   ea.B = pl.B; ea.Nv = pl.Nv; ea.C = pl.C; ea.sparse = 0;
   SGDN_TRY(launch_evrec(ea, s));
+  mark_range(dbg, SGDN_EV_PREFIX, SGDN_EV_DEFERRED, s);
   HScanArgs ha{};
   ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, B_W); ha.U = at<void>(ws, pl, B_U);
   ha.fac = at<float>(ws, pl, B_FAC); ha.rec = ea.rec; ha.P = nullptr;
@@ -373,7 +374,6 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   da.row_pair = sa.row_pair; da.row_ptr = sa.row_ptr; da.col = sa.col;
   da.B = pl.B; da.Nv = pl.Nv; da.Nq = pl.Nq; da.C = pl.C; da.Emax = Emax; da.solve = pl.solve;
   SGDN_TRY(launch_deferred_w(da, pl.bf16, s));
-  mark(dbg, SGDN_EV_DEFERRED, s);
 
   if (s0 != nullptr) {
     S0PrepArgs s0a{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv};
@@ -385,6 +385,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   ea.rec = at<int32_t>(ws, pl, B_REC);
   ea.B = pl.B; ea.Nv = pl.Nv; ea.C = pl.C; ea.Emax = Emax; ea.sparse = 1;
   SGDN_TRY(launch_evrec(ea, s));
+  mark(dbg, SGDN_EV_DEFERRED, s);
   HScanArgs ha{};
   ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, B_WPK); ha.U = at<void>(ws, pl, B_U);
   ha.fac = at<float>(ws, pl, B_FAC); ha.rec = ea.rec; ha.P = at<double>(ws, pl, B_P);

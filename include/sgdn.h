@@ -125,11 +125,12 @@ typedef struct {
 enum {
   SGDN_EV_START = 0,     /* before the first kernel                       */
   SGDN_EV_INTRA = 1,     /* after the intra-chunk kernel                  */
-  SGDN_EV_PREFIX = 2,    /* after the log-decay prefix (sparse)           */
+  SGDN_EV_PREFIX = 2,    /* after the log-decay prefix (sparse); dense:
+                            after the event records                       */
   SGDN_EV_GATE = 3,      /* after the gate energy (sparse)                */
   SGDN_EV_SELECT = 4,    /* after selector + CSR layout (sparse)          */
-  SGDN_EV_DEFERRED = 5,  /* after deferred W (sparse)                     */
-  SGDN_EV_HSCAN = 6,     /* after the H scan                              */
+  SGDN_EV_DEFERRED = 5,  /* after deferred W and the event records        */
+  SGDN_EV_HSCAN = 6,     /* after the H-scan kernel alone                 */
   SGDN_EV_O = 7,         /* after the O kernel                            */
   SGDN_EV_COUNT = 8
 };
