@@ -21,6 +21,7 @@ RATES_PCT = (8, 30, 95)                 # (rho_L, rho_M, rho_H), Sec. 2.4.3, Eq.
 DEFAULT_BUDGET_BP = 2900                # the page's default: about 29% of events
 MEDIUM_CHOICES = {1: (11, 12, 13), 2: (7, 8, 9), 3: (3, 4, 5), 4: (0,)}   # Sec. 2.4.3 table
 HIGH_CHOICES = (1, 2, 3, 4)
+FIXED_HIGH, FIXED_MEDIUM = 3, 4   # the fixed 9 Low / 4 Medium / 3 High split of Table 5
 LOW, MEDIUM, HIGH = 0, 1, 2
 
 
@@ -149,7 +150,8 @@ def _normalise(d):
     return [x / mu if mu > 0.0 else 0.0 for x in d]
 
 
-def select(score, gamma, eta, keep_budget: float = 0.29, window: int = 16):
+def select(score, gamma, eta, keep_budget: float = 0.29, window: int = 16,
+           fixed_tiers: bool = False, unit_visibility: bool = False, rank_key=None):
     """Dynamic event selection for one sequence.  Sec. 2.4, Eqs. (10)-(14).
 
     score, gamma: [Nv, C] (fp32 values); eta: [Nv].  Nv = 32 (16 head pairs;
@@ -157,6 +159,17 @@ def select(score, gamma, eta, keep_budget: float = 0.29, window: int = 16):
     mask [16, C] (uint8), tier [16] (0 Low, 1 Medium, 2 High), k (k_L, k_M, k_H),
     n_high, n_medium, rank [16, C] (-1 for anchors), and the intermediate
     statistics (norms, r, L, G, gains, x).
+
+    Selector ablations (Sec. 3.5, Table 5; the speed side of each):
+      fixed_tiers      3 High / 4 Medium / 9 Low pairs in every layer instead of
+                       the split-score counts of Eqs. (13)-(14); which pairs get
+                       which tier still follows x_H, then x_M.
+      unit_visibility  G_h = 1 for every head (the gate energy is ignored).
+      rank_key [16, C] the non-anchor chunks kept in each pair are the ones with
+                       the largest keys (ties: lower chunk first) instead of the
+                       largest q_c; the tiers and the keep counts are still the
+                       adaptive ones (random keys give the random selection at
+                       matched budget).
     """
     s = np.asarray(score, np.float32).astype(np.float64)
     gm = np.asarray(gamma, np.float32).astype(np.float64)
@@ -187,6 +200,8 @@ def select(score, gamma, eta, keep_budget: float = 0.29, window: int = 16):
     L_h = [lifetime(r, C) for r in r_h]
     eta_bar = csum(et.tolist()) / Nv
     G_h = [math.sqrt(et[h] / eta_bar) if eta_bar > 0.0 else 1.0 for h in range(Nv)]
+    if unit_visibility:
+        G_h = [1.0] * Nv
 
     # Eq. (12): upgrade gains L->M and M->H, unnormalised s.
     def band_sum(h, p, lo_k, hi_k):
@@ -205,23 +220,37 @@ def select(score, gamma, eta, keep_budget: float = 0.29, window: int = 16):
     xM, xH = _normalise(gain_lm), _normalise(gain_mh)
     order_h = sorted(range(Np), key=lambda p: (-xH[p], p))
     vals_h = [xH[p] for p in order_h]
-    n_high = HIGH_CHOICES[_argmax_first([split_score(vals_h, k) for k in HIGH_CHOICES])]
+    if fixed_tiers:
+        n_high = FIXED_HIGH
+    else:
+        n_high = HIGH_CHOICES[_argmax_first([split_score(vals_h, k) for k in HIGH_CHOICES])]
     high = set(order_h[:n_high])
     rest = [p for p in range(Np) if p not in high]
     order_m = sorted(rest, key=lambda p: (-xM[p], p))
     vals_m = [xM[p] for p in order_m]
-    choices = MEDIUM_CHOICES[n_high]
-    n_medium = choices[_argmax_first([split_score(vals_m, k) for k in choices])]
+    if fixed_tiers:
+        n_medium = FIXED_MEDIUM
+    else:
+        choices = MEDIUM_CHOICES[n_high]
+        n_medium = choices[_argmax_first([split_score(vals_m, k) for k in choices])]
     medium = set(order_m[:n_medium])
 
     tier = np.array([HIGH if p in high else MEDIUM if p in medium else LOW
                      for p in range(Np)], dtype=np.uint8)
     kk = {LOW: kL, MEDIUM: kM, HIGH: kH}
+    keep_rank = rank
+    if rank_key is not None:
+        key = np.asarray(rank_key, np.float32).astype(np.float64)
+        keep_rank = np.full((Np, C), -1, dtype=np.int64)
+        for p in range(Np):
+            cand = sorted(range(1, C - 1), key=lambda c: (-key[p, c], c))
+            for r, c in enumerate(cand):
+                keep_rank[p, c] = r
     mask = np.zeros((Np, C), dtype=np.uint8)
     for p in range(Np):
         k = kk[int(tier[p])]
         for c in range(C):
-            if c == 0 or c == C - 1 or (0 <= rank[p, c] < k - 2):
+            if c == 0 or c == C - 1 or (0 <= keep_rank[p, c] < k - 2):
                 mask[p, c] = 1
     return dict(mask=mask, tier=tier, k=(kL, kM, kH), n_high=n_high,
                 n_medium=n_medium, rank=rank, norms=norms, r=r_h, L=L_h, G=G_h,

@@ -41,7 +41,8 @@ def deferred_w(Cb, kc, solve: str = "blockadj"):
 
 
 def sparse_prefill(q, k, v, a, beta, z=None, norm_weight=None, keep_budget=0.29,
-                   solve="blockadj", s0=None, mask=None, return_all=False):
+                   solve="blockadj", s0=None, mask=None, return_all=False, tail=16,
+                   fixed_tiers=False, unit_visibility=False, rank_key=None):
     """End-to-end SparseGDN prefill for a batch of sequences.
 
     Steps (Sec. 2.2 pipeline, Fig. 3): intra (local solve, U, staged Cb,
@@ -49,6 +50,9 @@ def sparse_prefill(q, k, v, a, beta, z=None, norm_weight=None, keep_budget=0.29,
     propagation) -> O (two-chunk groups).  The statistics handed to the
     selector are rounded to fp32, the precision the page keeps them in.
     ``mask`` [B, Nv/2, C] overrides the selector (then z is not needed).
+    ``tail`` is the Tail window of Eq. (9) (8, 16, 32 or 64 rows); the
+    selector ablations (``fixed_tiers``, ``unit_visibility``, ``rank_key``
+    [B, Nv/2, C]) are those of ``selector.select``.
 
     H, per value head h in pair p (Eqs. (17)-(18) with Eqs. (1)-(2)):
         S_in(c) = S
@@ -72,7 +76,7 @@ def sparse_prefill(q, k, v, a, beta, z=None, norm_weight=None, keep_budget=0.29,
     g, gamma, P = gdn.decay_prefix(a)
     C = g.shape[2]
     U, _, Ct, Cb, _ = gdn.intra(kc, vc, bc, g, solve)
-    score = tail_score(U).astype(np.float32)
+    score = tail_score(U, tail).astype(np.float32)
     gamma32 = gamma.astype(np.float32)
     eta = None
     sel = []
@@ -80,7 +84,9 @@ def sparse_prefill(q, k, v, a, beta, z=None, norm_weight=None, keep_budget=0.29,
         if z is None:
             raise ValueError("the selector needs the output gate z")
         eta = gate_energy(z, norm_weight).astype(np.float32)
-        sel = [select(score[b], gamma32[b], eta[b], keep_budget) for b in range(B)]
+        sel = [select(score[b], gamma32[b], eta[b], keep_budget, fixed_tiers=fixed_tiers,
+                      unit_visibility=unit_visibility,
+                      rank_key=None if rank_key is None else rank_key[b]) for b in range(B)]
         mask = np.stack([s["mask"] for s in sel])
     mask = np.asarray(mask).astype(bool)
     zh = np.repeat(mask, 2, axis=1)                      # [B, Nv, C] per value head

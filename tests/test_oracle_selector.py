@@ -117,6 +117,16 @@ def test_tail_score_reads_only_the_last_16_rows():
     np.testing.assert_array_equal(s, [0.0, 2.5, 4.0])
 
 
+@pytest.mark.parametrize("tail", [8, 16, 32, 64])
+def test_tail_score_windows(tail):
+    """Tail-8/32/64 ablation windows (Fig. 10): row r of the chunk holds r + 1
+    in one column, so the score is sqrt(sum of (r + 1)^2 over the last rows)."""
+    U = np.zeros((1, 64, 128))
+    U[0, :, 5] = np.arange(1, 65)
+    expect = math.sqrt(sum((r + 1) ** 2 for r in range(64 - tail, 64)))
+    assert selector.tail_score(U, tail)[0] == pytest.approx(expect, rel=1e-15)
+
+
 def _silu(x):
     return x / (1 + math.exp(-x))
 
@@ -252,6 +262,96 @@ def test_high_tier_takes_largest_gains():
     low = np.flatnonzero(out["tier"] == 0)
     if len(med) and len(low):
         assert xm[med].min() >= xm[low].max()
+
+
+# ---------------------------------------------------------- selector ablations
+
+def _single_high(C=64):
+    """Like the crafted case, but one pair's M->H gain stands far above the
+    rest, so the split score picks n_H = 1 (the dynamic count differs from
+    the fixed 3 / 4 / 9 split).  Gains: x_H order 0, then 1, 2, 3 (B = 2.0,
+    1.9, 1.8), the rest tied; x_M order 4, 5, 6, 7 (A = 9, 8, 7, 6) after the
+    High pairs."""
+    kL, kM, kH = selector.tier_counts(C)
+    A = [1.0] * 4 + [9.0, 8.0, 7.0, 6.0] + [1.0] * 8
+    Bv = [40.0, 2.0, 1.9, 1.8] + [0.5] * 12
+    s = np.zeros((32, C), np.float32)
+    for p in range(16):
+        for h in (2 * p, 2 * p + 1):
+            s[h, :kM - 1] = max(A[p], Bv[p] + 1.0)
+            s[h, kM - 1:] = Bv[p]
+    return s, np.full((32, C), -1.0, np.float32), np.ones(32, np.float32), (kL, kM, kH)
+
+
+def test_fixed_tiers_assign_3_high_4_medium_9_low():
+    s, gamma, eta, (kL, kM, kH) = _single_high()
+    dyn = selector.select(s, gamma, eta)
+    assert dyn["n_high"] == 1                       # the dynamic count differs
+    out = selector.select(s, gamma, eta, fixed_tiers=True)
+    assert out["n_high"] == 3 and out["n_medium"] == 4
+    tiers = out["tier"]
+    xh, xm = np.array(out["x_h"]), np.array(out["x_m"])
+    high = np.flatnonzero(tiers == 2)
+    assert sorted(high.tolist()) == sorted(np.argsort(-xh, kind="stable")[:3].tolist())
+    rest = [p for p in range(16) if p not in high]
+    med = sorted(rest, key=lambda p: (-xm[p], p))[:4]
+    assert sorted(np.flatnonzero(tiers == 1).tolist()) == sorted(med)
+    counts = out["mask"].sum(axis=1)
+    for p in range(16):
+        assert counts[p] == {2: kH, 1: kM, 0: kL}[int(tiers[p])]
+    # the same ranking as the dynamic selector (only the counts are fixed)
+    assert np.array_equal(out["rank"], dyn["rank"])
+
+
+def test_unit_visibility_equals_equal_gate_energies():
+    """G_h = sqrt(eta_h / mean eta) is 1 for equal energies, so G = 1 is the
+    selector run with every eta equal; skewed energies do change it."""
+    rng = np.random.default_rng(31)
+    C = 96
+    s = rng.gamma(2.0, 1.0, (32, C)).astype(np.float32)
+    gamma = (-rng.uniform(0.05, 5, (32, 1)) * np.ones((1, C))).astype(np.float32)
+    eta = np.exp(rng.uniform(-4, 4, 32)).astype(np.float32)
+    a = selector.select(s, gamma, eta, unit_visibility=True)
+    b = selector.select(s, gamma, np.full(32, 0.7, np.float32))
+    c = selector.select(s, gamma, eta)
+    assert np.array_equal(a["mask"], b["mask"]) and np.array_equal(a["tier"], b["tier"])
+    assert a["G"] == [1.0] * 32
+    assert not (np.array_equal(a["mask"], c["mask"]) and np.array_equal(a["tier"], c["tier"]))
+
+
+def test_rank_key_of_eq10_reproduces_the_selector():
+    """Keys equal to the Eq. (10) rank key q_c (formed here from the scores)
+    give the default mask; any keys keep the adaptive tiers, the keep counts
+    and the anchors, and keep the chunks with the largest keys."""
+    rng = np.random.default_rng(33)
+    C = 80
+    s = rng.gamma(2.0, 1.0, (32, C)).astype(np.float32)
+    gamma = (-rng.uniform(0.05, 5, (32, 1)) * np.ones((1, C))).astype(np.float32)
+    eta = rng.uniform(0.5, 2, 32).astype(np.float32)
+    ref = selector.select(s, gamma, eta)
+    s64 = s.astype(np.float64)
+    q = np.empty((16, C))
+    for p in range(16):
+        n0 = math.sqrt(math.fsum(s64[2 * p] ** 2)); n1 = math.sqrt(math.fsum(s64[2 * p + 1] ** 2))
+        q[p] = 0.5 * (s64[2 * p] / n0 + s64[2 * p + 1] / n1)
+    q32 = q.astype(np.float32)
+    for p in range(16):         # fp32 keys keep this draw's order of q exactly
+        assert (sorted(range(1, C - 1), key=lambda c: (-q32[p, c], c))
+                == sorted(range(1, C - 1), key=lambda c: (-q[p, c], c)))
+    same = selector.select(s, gamma, eta, rank_key=q32)
+    assert np.array_equal(same["tier"], ref["tier"])
+    assert np.array_equal(same["mask"], ref["mask"])
+    key = rng.uniform(size=(16, C)).astype(np.float32)
+    rnd = selector.select(s, gamma, eta, rank_key=key)
+    assert np.array_equal(rnd["tier"], ref["tier"])
+    assert np.array_equal(rnd["mask"].sum(axis=1), ref["mask"].sum(axis=1))
+    assert np.all(rnd["mask"][:, 0] == 1) and np.all(rnd["mask"][:, C - 1] == 1)
+    for p in range(16):
+        kept = [c for c in range(1, C - 1) if rnd["mask"][p, c]]
+        dropped = [c for c in range(1, C - 1) if not rnd["mask"][p, c]]
+        if kept and dropped:
+            assert key[p, kept].min() > key[p, dropped].max()
+    assert not np.array_equal(rnd["mask"], ref["mask"])
 
 
 # ---------------------------------------------------------------- CSR layout
