@@ -11,7 +11,9 @@ The dense exact path (intra, H, O) is timed the same way beside it, and so is
 the single-token decode step that continues from the final states (a batch
 of 128 sequences through the same 24 layers, states updated in place).  A
 packed variable-length leg reads the same tokens as 16 sequences of mixed
-lengths (cu_seqlens) and times both paths again.
+lengths (cu_seqlens) and times both paths again.  A selector-ablation leg
+times the sparse step with each switch of Sec. 3.5 (fixed 3/4/9 tiers,
+G_h = 1, random keys at matched budget, Tail-8/32/64 windows).
 
 Prints one JSON line.  value = tokens/s of the 24-layer stack (B*T per step);
 roofline = the dominant kernel's algorithmic bytes per launch over its mean
@@ -52,6 +54,8 @@ def parse():
                     help="tokens of layer 0 the oracle baseline processes")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed variable-length leg")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the selector-ablation leg")
     ap.add_argument("--decode-batch", type=int, default=128,
                     help="sequences of the decode-step leg (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -213,6 +217,48 @@ def varlen_leg(args, layers, hip):
               f"({nseq} packed sequences); stages (ms/launch) "
               + ", ".join(f"{k} {v:.3f}" for k, v in stage.items()), file=sys.stderr, flush=True)
     out["lengths"] = lens
+    return out
+
+
+def variants_leg(args, layers, ws, C):
+    """The sparse 24-layer step under each selector ablation; keep from the
+    device statistics."""
+    import torch
+    from gated_deltanet_prefill_chunkwise_amd import ops, synth
+    st = [torch.zeros((B, ops.STATS_INTS), dtype=torch.int32, device="cuda") for _ in layers]
+    keys = []
+    for l in range(len(layers)):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(synth.seed_for(7, l))
+        keys.append(torch.rand((B, NV // 2, C), generator=g, device="cuda"))
+    variants = {"fixed_tiers_3_4_9": dict(fixed_tiers=True), "unit_visibility": dict(unit_visibility=True),
+                "random_keys": dict(rank_key=True), "tail8": dict(tail=8), "tail32": dict(tail=32),
+                "tail64": dict(tail=64)}
+    out = {}
+    for name, var in variants.items():
+        def step():
+            for l, (inp, o, sf, _) in enumerate(layers):
+                kw = dict(var)
+                if kw.pop("rank_key", False):
+                    kw["rank_key"] = keys[l]
+                ops.prefill_sparse(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], z=inp["z"],
+                                   keep_budget=0.29, solve="blockadj", o=o, s_final=sf, stats=st[l],
+                                   workspace=ws, **kw)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            step()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        keep = float(torch.stack(st).float()[:, 0, 0].mean()) / (16 * C)
+        out[name] = {"ms_per_step": round(ms, 4), "value_tok_s": round(B * args.seqlen / (ms / 1e3), 1),
+                     "measured_keep": round(keep, 5)}
+        print(f"[bench] sparse {name}: {ms:.3f} ms per {args.layers}-layer step, keep {keep:.4f}",
+              file=sys.stderr, flush=True)
     return out
 
 
@@ -419,6 +465,13 @@ def main():
         out["sparse"]["snapshot_fraction"] = round(sigma, 5)
     if "sparse" in res and "dense" in res:
         out["sparse_speedup_over_dense"] = round(res["dense"]["ms_per_step"] / res["sparse"]["ms_per_step"], 3)
+    if not args.no_variants and "sparse" in res:
+        # the rank-key variant needs one more rank table in the workspace
+        key_shape = torch.empty((B, NV // 2, C), device=dev)
+        vws = torch.empty(ops.workspace_bytes(prob, True, ops.sparse_params(rank_key=key_shape)),
+                          dtype=torch.uint8, device=dev)
+        out["selector_variants"] = variants_leg(args, layers, vws, C)
+        del vws
     if not args.no_varlen and args.mode == "both":
         out["varlen"] = varlen_leg(args, layers, hip)
     if args.decode_batch > 0:

@@ -26,7 +26,7 @@ struct Plan {
 
 enum Buf { B_G, B_GAMMA, B_P, B_U, B_W, B_CB, B_KT, B_SNAP, B_S0T, B_SCORE, B_ETA, B_RANK,
            B_TINFO, B_MASK, B_TIER, B_ROWPAIR, B_ROWPTR, B_COL, B_PRED, B_GSLOT, B_ESLOT,
-           B_WPK, B_STATS, B_FAC, B_REC, B_CHUNKS, B_COUNT };
+           B_WPK, B_STATS, B_FAC, B_REC, B_CHUNKS, B_SPART, B_RANK2, B_COUNT };
 
 static_assert(B_COUNT <= (int)(sizeof(Plan::off) / sizeof(size_t)), "workspace table too small");
 
@@ -71,7 +71,11 @@ int check_params(const sgdn_problem* pr, const sgdn_sparse_params* sp) {
   if (sp == nullptr) return SGDN_EINVAL;
   const int bp = budget_bp(sp->keep_budget);
   if (!(sp->keep_budget > 0.f) || bp < 1 || bp > 10000) return SGDN_EINVAL;
-  if (sp->tail != 16 || sp->r_window != 16) return SGDN_EUNSUPPORTED;
+  if (sp->tail != 8 && sp->tail != 16 && sp->tail != 32 && sp->tail != 64) return SGDN_EUNSUPPORTED;
+  if (sp->r_window != 16) return SGDN_EUNSUPPORTED;
+  if ((sp->fixed_tiers != 0 && sp->fixed_tiers != 1) ||
+      (sp->unit_visibility != 0 && sp->unit_visibility != 1))
+    return SGDN_EINVAL;
   if (pr->n_v != 2 * NP_SPARSE) return SGDN_EUNSUPPORTED;
   const int C = (pr->seqlen + 63) / 64;
   if (C > 8192) return SGDN_EUNSUPPORTED;
@@ -108,6 +112,8 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
     sz[B_CB] = B * Nv * C * L * L * I;
     sz[B_SNAP] = B * (size_t)p.snap_cap * 2 * DV * DK * I;
     sz[B_SCORE] = B * Nv * C * 4;
+    sz[B_SPART] = B * Nv * C * 8 * 4;
+    if (sp->rank_key != nullptr) sz[B_RANK2] = B * NP * C * 4;
     sz[B_ETA] = B * Nv * 4;
     sz[B_RANK] = B * NP * C * 4;
     sz[B_TINFO] = B * 8 * 4;
@@ -162,7 +168,7 @@ IntraArgs intra_args(const Plan& pl, void* ws, const void* k, const void* v, con
   ia.W = sparse ? nullptr : at<void>(ws, pl, B_W);
   ia.Cb = sparse ? at<void>(ws, pl, B_CB) : nullptr;
   ia.KT = at<void>(ws, pl, B_KT);
-  ia.score = sparse ? at<float>(ws, pl, B_SCORE) : nullptr;
+  ia.score_part = sparse ? at<float>(ws, pl, B_SPART) : nullptr;
   return ia;
 }
 
@@ -303,6 +309,9 @@ int sgdn_select(const sgdn_problem* prob, const float* score, const float* gamma
   sa.score = score; sa.gamma = gamma; sa.eta = eta;
   sa.B = pl.B; sa.C = pl.C; sa.keep_bp = budget_bp(params->keep_budget);
   sa.cu = pl.cu; sa.T = pl.T;
+  sa.fixed_tiers = params->fixed_tiers; sa.unit_visibility = params->unit_visibility;
+  sa.rank_key = params->rank_key;
+  sa.rank_alt = params->rank_key ? at<int32_t>(ws, pl, B_RANK2) : nullptr;
   sa.rank = at<int32_t>(ws, pl, B_RANK); sa.tierinfo = at<int32_t>(ws, pl, B_TINFO);
   sa.mask = mask; sa.tier = tier; sa.row_pair = row_pair; sa.row_ptr = row_ptr; sa.col = col;
   sa.pred = pred; sa.group_slot = group_slot; sa.event_slot = at<int32_t>(ws, pl, B_ESLOT);
@@ -332,6 +341,9 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   mark(dbg, SGDN_EV_START, s);
   if ((st = chunk_table(pl, ws, s)) != SGDN_OK) return st;
   SGDN_TRY(launch_intra(intra_args(pl, ws, k, v, a, beta, 1), pl.bf16, s));
+  ScoreArgs sca{at<float>(ws, pl, B_SPART), at<float>(ws, pl, B_SCORE),
+                (long long)pl.B * pl.Nv * pl.C, params->tail};
+  SGDN_TRY(launch_score(sca, s));
   mark(dbg, SGDN_EV_INTRA, s);
   PrefixArgs pa{at<float>(ws, pl, B_GAMMA), at<double>(ws, pl, B_P), pl.B, pl.Nv, pl.C,
                 pl.cu, pl.T};
@@ -351,6 +363,9 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   sa.eta = at<float>(ws, pl, B_ETA);
   sa.B = pl.B; sa.C = pl.C; sa.keep_bp = budget_bp(params->keep_budget);
   sa.cu = pl.cu; sa.T = pl.T;
+  sa.fixed_tiers = params->fixed_tiers; sa.unit_visibility = params->unit_visibility;
+  sa.rank_key = params->rank_key;
+  sa.rank_alt = params->rank_key ? at<int32_t>(ws, pl, B_RANK2) : nullptr;
   sa.rank = at<int32_t>(ws, pl, B_RANK); sa.tierinfo = at<int32_t>(ws, pl, B_TINFO);
   sa.mask = at<uint8_t>(ws, pl, B_MASK); sa.tier = at<uint8_t>(ws, pl, B_TIER);
   sa.row_pair = at<int32_t>(ws, pl, B_ROWPAIR); sa.row_ptr = at<int32_t>(ws, pl, B_ROWPTR);

@@ -1,11 +1,12 @@
 // Intra-chunk kernel: decay prefix, gated Gram matrix, local Delta solve
 // (exact or block-adjacent), U = C diag(beta) V, W = C diag(beta 2^g) K (dense)
-// or the staged coefficients C diag(beta 2^g) (sparse), the Tail-16 score, and
-// transposed key tiles for the later stages.
+// or the staged coefficients C diag(beta 2^g) (sparse), the parts of the tail
+// score, and transposed key tiles for the later stages.
 //
 // SparseGDN reading notes: Sec. 2.1 (g, gamma), Sec. 2.3 Eqs. (5)-(8) (local
 // system, block-adjacent inverse, weighted coefficients), Sec. 2.4 Eq. (9)
-// (tail score from the fp32 U while it is on chip).
+// (sums of squares of U over 8-row blocks, from the fp32 U while it is on
+// chip, for the tail score of any window).
 //
 // Persistent kernel: each workgroup (4 waves) walks over (chunk, head pair,
 // batch) items and loads the next item's keys, values and gates into registers
@@ -463,10 +464,12 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
           __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (SPARSE) {
-          // Eq. (9): Frobenius norm of U rows 48..63, from the fp32 accumulators
+          // Eq. (9) in parts: sums of squares of U over 8-row blocks, from the
+          // fp32 accumulators (lanes 0-31 hold rows 16w..16w+7, lanes 32-63
+          // rows 16w+8..16w+15); the tail score sums the blocks of its window
 #pragma unroll
-          for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-          if (w == 3 && lane == 0) p.score[hc] = sqrtf(ss);
+          for (int off = 1; off < 32; off <<= 1) ss += __shfl_xor(ss, off, 64);
+          if ((lane & 31) == 0) p.score_part[hc * 8 + 2 * w + (lane >> 5)] = ss;
         }
       }
       // keep the U and W products apart (their accumulators would otherwise

@@ -41,8 +41,12 @@ struct IntraArgs {
   const int32_t* chunks;
   float* g; float* gamma; float* fac;
   void* U; void* W; void* Cb; void* KT;
-  float* score;
+  float* score_part;        // sparse: [B][Nv][C][8] sums of squares of U per 8-row block
 };
+
+// Tail score of Eq. (9) over the last `tail` rows (8, 16, 32 or 64) from the
+// 8-row parts: score = sqrt(sum of the parts of the window, in row order).
+struct ScoreArgs { const float* part; float* score; long long n; int tail; };
 
 struct PrefixArgs {
   const float* gamma; double* P; int B, Nv, C;
@@ -110,6 +114,11 @@ struct SelectArgs {
   // packed sequence offsets [B+1] or null: sequence b has ceil(len_b / 64)
   // valid chunks (arrays keep the stride C); T bounds every length
   const int32_t* cu; int T;
+  // ablations: 3 High / 4 Medium / 9 Low pairs; G_h = 1; caller rank keys
+  // [B][16][C] that choose the kept chunks (the tiers still follow Eq. (10))
+  int fixed_tiers, unit_visibility;
+  const float* rank_key;
+  int32_t* rank_alt;    // [B][16][C]   workspace: ranks by rank_key
   int32_t* rank;        // [B][16][C]   workspace
   int32_t* tierinfo;    // [B][8]       workspace: k_L, k_M, k_H, n_H, n_M
   uint8_t* mask; uint8_t* tier;
@@ -136,6 +145,7 @@ struct DecodeArgs {
 
 hipError_t launch_intra(const IntraArgs& a, int bf16, hipStream_t s);
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s);
+hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_chunk_table(const ChunkTableArgs& a, hipStream_t s);
 hipError_t launch_hscan(const HScanArgs& a, int bf16, hipStream_t s);
 hipError_t launch_ochunk(const OChunkArgs& a, int bf16, hipStream_t s);

@@ -81,6 +81,17 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(ChunkTableArgs p) {
   }
 }
 
+// s_{c,h} = ||U_{c,h}[64 - tail : 64]||_F (SparseGDN reading notes, Sec. 2.4,
+// Eq. (9); Tail-8/32/64 are the window ablations of Fig. 10).
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs p) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.n) return;
+  const float* q = p.part + i * 8;
+  float s = 0.f;
+  for (int k = 8 - p.tail / 8; k < 8; ++k) s += q[k];
+  p.score[i] = sqrtf(s);
+}
+
 // s0 [dk][dv] -> transposed [dv][dk] in the snapshot element type, the
 // "virtual snapshot" that output groups without a predecessor read.
 template <typename I>
@@ -223,6 +234,11 @@ __global__ __launch_bounds__(256) void debug_u_kernel(const void* Ut_, float* U)
 
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(prefix_kernel, dim3(a.B * a.Nv), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const ScoreArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(score_kernel, dim3((unsigned)((a.n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

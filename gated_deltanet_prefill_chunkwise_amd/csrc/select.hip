@@ -106,7 +106,10 @@ __device__ double lifetime(double r, int C) {
 // Workgroup (blk, pp, b) ranks chunks 128 blk .. 128 blk + 127 of pair pp:
 // eight threads per chunk count disjoint eighths of the other chunks.  Every
 // workgroup forms the norms and keys itself, with the same operations.
+// KEY: rank by the caller's keys instead (the random-selection ablation),
+// into rank_alt.
 constexpr int RANK_CHUNKS = 128;
+template <bool KEY>
 __global__ __launch_bounds__(1024) void select_rank_kernel(SelectArgs p) {
   extern __shared__ double sq[];
   __shared__ double snorm[2];
@@ -115,7 +118,8 @@ __global__ __launch_bounds__(1024) void select_rank_kernel(SelectArgs p) {
   const int CS = p.C, C = valid_chunks(p, b);
   const float* s0 = p.score + ((size_t)b * NV + 2 * pp) * CS;
   const float* s1 = s0 + CS;
-  if (w < 2) {
+  const float* key = KEY ? p.rank_key + ((size_t)b * NP + pp) * CS : nullptr;
+  if (!KEY && w < 2) {
     const float* s = w ? s1 : s0;
     double acc = 0.0;
     for (int c = lane; c < C; c += 64) {
@@ -128,12 +132,16 @@ __global__ __launch_bounds__(1024) void select_rank_kernel(SelectArgs p) {
   __syncthreads();
   const double n0 = snorm[0], n1 = snorm[1];
   for (int c = tid; c < C; c += 1024) {
-    const double t0 = n0 > 0.0 ? (double)s0[c] / n0 : 0.0;
-    const double t1 = n1 > 0.0 ? (double)s1[c] / n1 : 0.0;
-    sq[c] = 0.5 * (t0 + t1);
+    if (KEY) {
+      sq[c] = (double)key[c];
+    } else {
+      const double t0 = n0 > 0.0 ? (double)s0[c] / n0 : 0.0;
+      const double t1 = n1 > 0.0 ? (double)s1[c] / n1 : 0.0;
+      sq[c] = 0.5 * (t0 + t1);
+    }
   }
   __syncthreads();
-  int32_t* rk = p.rank + ((size_t)b * NP + pp) * CS;
+  int32_t* rk = (KEY ? p.rank_alt : p.rank) + ((size_t)b * NP + pp) * CS;
   const int c = RANK_CHUNKS * blk + (tid >> 3), part = tid & 7;
   int r = 0;
   const bool inner = c >= 1 && c <= C - 2;
@@ -201,7 +209,7 @@ __global__ __launch_bounds__(1024) void select_tier_kernel(SelectArgs p) {
   __syncthreads();
   if (wv != 0) return;
   const double etab = wave_sum(lane < NV ? (double)et[lane] : 0.0) / NV;
-  if (lane < NV) sGv[lane] = etab > 0.0 ? sqrt((double)et[lane] / etab) : 1.0;
+  if (lane < NV) sGv[lane] = (etab > 0.0 && !p.unit_visibility) ? sqrt((double)et[lane] / etab) : 1.0;
   __syncthreads();
   double glm = 0.0, gmh = 0.0;
   if (lane < NP) {
@@ -228,7 +236,9 @@ __global__ __launch_bounds__(1024) void select_tier_kernel(SelectArgs p) {
   if (lane < NP) svals[lane] = sxh[sorder[lane]];
   __syncthreads();
   int nH = 1;
-  {
+  if (p.fixed_tiers) {
+    nH = 3;                 // the fixed 9 Low / 4 Medium / 3 High split
+  } else {
     double best = 0.0;
     for (int k = 1; k <= 4; ++k) {
       const double v = split_score(svals, NP, k, lane);
@@ -257,7 +267,9 @@ __global__ __launch_bounds__(1024) void select_tier_kernel(SelectArgs p) {
   else if (nH == 3) { cand[0] = 3; cand[1] = 4; cand[2] = 5; ncand = 3; }
   else { cand[0] = 0; ncand = 1; }
   int nM = cand[0];
-  {
+  if (p.fixed_tiers) {
+    nM = 4;
+  } else {
     double best = 0.0;
     for (int i = 0; i < ncand; ++i) {
       const double v = split_score(svals, nrest, cand[i], lane);
@@ -306,6 +318,7 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
   const unsigned long long below = (1ull << lane) - 1ull;
   uint8_t* mask = p.mask + (size_t)b * NP * CS;
   const bool ovr = p.mask_in != nullptr;
+  const int32_t* rank_src = p.rank_key != nullptr ? p.rank_alt : p.rank;
   if (tid < NP) s_tier[tid] = ovr ? 0 : p.tier[b * NP + tid];
   __syncthreads();
   const int pp = w;
@@ -321,7 +334,7 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
         const int c = 64 * (i0 + u) + lane;
         const size_t idx = (size_t)b * NP * CS + (size_t)pp * CS + c;
         val[u] = 0;
-        if (i0 + u < NW && c < C) val[u] = ovr ? (int)p.mask_in[idx] : p.rank[idx];
+        if (i0 + u < NW && c < C) val[u] = ovr ? (int)p.mask_in[idx] : rank_src[idx];
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -443,9 +456,14 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
 hipError_t launch_select_full(const SelectArgs& a, hipStream_t s) {
   if (a.mask_in == nullptr) {
     const int nblk = (a.C + RANK_CHUNKS - 1) / RANK_CHUNKS;
-    hipLaunchKernelGGL(select_rank_kernel, dim3(nblk, NP, a.B), dim3(1024), (size_t)a.C * sizeof(double), s, a);
+    hipLaunchKernelGGL(select_rank_kernel<false>, dim3(nblk, NP, a.B), dim3(1024), (size_t)a.C * sizeof(double), s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.rank_key != nullptr) {
+      hipLaunchKernelGGL(select_rank_kernel<true>, dim3(nblk, NP, a.B), dim3(1024), (size_t)a.C * sizeof(double), s, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(select_tier_kernel, dim3(a.B), dim3(1024), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

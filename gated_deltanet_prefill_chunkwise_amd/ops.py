@@ -26,7 +26,9 @@ class Problem(ctypes.Structure):
 
 class SparseParams(ctypes.Structure):
     _fields_ = [("keep_budget", ctypes.c_float), ("tail", ctypes.c_int32),
-                ("r_window", ctypes.c_int32), ("norm_weight", ctypes.c_void_p)]
+                ("r_window", ctypes.c_int32), ("norm_weight", ctypes.c_void_p),
+                ("fixed_tiers", ctypes.c_int32), ("unit_visibility", ctypes.c_int32),
+                ("rank_key", ctypes.c_void_p)]
 
 
 class Stats(ctypes.Structure):
@@ -130,9 +132,14 @@ def problem(q, v, solve="exact", out_dtype=None, cu_seqlens=None, max_seqlen=Non
                    None if cu_seqlens is None else cu_seqlens.data_ptr())
 
 
-def sparse_params(keep_budget=0.29, norm_weight=None, tail=16, r_window=16) -> SparseParams:
+def sparse_params(keep_budget=0.29, norm_weight=None, tail=16, r_window=16, fixed_tiers=False,
+                  unit_visibility=False, rank_key=None) -> SparseParams:
+    """Selector parameters; ``rank_key`` (device fp32 [B, Nv/2, C]) and the
+    flags are the selector ablations described in include/sgdn.h."""
     return SparseParams(float(keep_budget), tail, r_window,
-                        None if norm_weight is None else norm_weight.data_ptr())
+                        None if norm_weight is None else norm_weight.data_ptr(),
+                        int(bool(fixed_tiers)), int(bool(unit_visibility)),
+                        None if rank_key is None else rank_key.data_ptr())
 
 
 def workspace_bytes(prob: Problem, sparse: bool, params: SparseParams | None = None) -> int:
@@ -240,7 +247,8 @@ def decode_step(q, k, v, a, beta, state, s_out=None, o=None, out_dtype=None, str
     return o, s_out
 
 
-def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None, cu_seqlens=None):
+def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None, cu_seqlens=None,
+           fixed_tiers=False, unit_visibility=False, rank_key=None):
     """Selector + CSR layout on fp32 statistics; returns a dict of device tensors.
 
     With ``cu_seqlens`` (int32 [B + 1] token offsets) sequence b has only its
@@ -251,12 +259,16 @@ def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None, cu_
     for t, n in ((score, "score"), (gamma, "gamma"), (eta, "eta")):
         _check(t, n, torch.float32)
     _check(cu_seqlens, "cu_seqlens", torch.int32)
+    _check(rank_key, "rank_key", torch.float32)
+    if rank_key is not None and tuple(rank_key.shape) != (B, Nv // 2, C):
+        raise ValueError("rank_key must be [B, Nv/2, C]")
     if cu_seqlens is not None and cu_seqlens.numel() != B + 1:
         raise ValueError("cu_seqlens must hold B + 1 offsets")
     T = C * 64
     prob = Problem(B, T, Nv // 2, Nv, 128, 128, SGDN_BF16, 1, SGDN_F32,
                    None if cu_seqlens is None else cu_seqlens.data_ptr())
-    params = sparse_params(keep_budget)
+    params = sparse_params(keep_budget, fixed_tiers=fixed_tiers, unit_visibility=unit_visibility,
+                           rank_key=rank_key)
     nbytes = workspace_bytes(prob, True, params)
     if nbytes == 0:
         raise SgdnError(-2, "sgdn_workspace_bytes")
@@ -287,7 +299,8 @@ def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None, cu_
 def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
                    mask_override=None, s0=None, norm_weight=None, want_state=True, o=None,
                    s_final=None, stats=None, workspace=None, debug=None, stream=None,
-                   out_dtype=None, cu_seqlens=None, max_seqlen=None):
+                   out_dtype=None, cu_seqlens=None, max_seqlen=None, tail=16, fixed_tiers=False,
+                   unit_visibility=False, rank_key=None):
     """SparseGDN prefill; returns (o, s_final, stats[B, 9] int32).
 
     o is fp32 unless ``out_dtype`` (or a given ``o``) says otherwise.  With
@@ -305,7 +318,12 @@ def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     _check(o, "o", out_dtype)
     prob = problem(q, v, solve, out_dtype, cu_seqlens, max_seqlen)
-    params = sparse_params(keep_budget, norm_weight)
+    _check(rank_key, "rank_key", torch.float32)
+    if rank_key is not None and tuple(rank_key.shape) != (prob.batch, v.shape[2] // 2,
+                                                         -(-prob.seqlen // 64)):
+        raise ValueError("rank_key must be [B, Nv/2, C]")
+    params = sparse_params(keep_budget, norm_weight, tail=tail, fixed_tiers=fixed_tiers,
+                           unit_visibility=unit_visibility, rank_key=rank_key)
     B, Nv, dv = prob.batch, v.shape[2], v.shape[3]
     if o is None:
         o = torch.empty(v.shape, dtype=out_dtype, device=v.device)

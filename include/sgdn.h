@@ -83,15 +83,28 @@ typedef struct {
 /* Selector parameters (Sec. 2.4).  keep_budget in (0, 1]: 0.29 gives the
  * page's tier rates (0.08, 0.30, 0.95); other budgets rescale them
  * (b <= 0.29: rho * b / 0.29; b > 0.29: 1 - (1 - rho)(1 - b) / 0.71);
- * 1.0 keeps every event.  tail = 16 rows for the score of Eq. (9),
- * r_window = 16 chunks for r_h of Eq. (11) (only these values are supported).
- * norm_weight: DEVICE [dv] fp32 RMSNorm scale used in the gate energy, or
- * NULL for ones. */
+ * 1.0 keeps every event.  tail: rows of the score of Eq. (9), 16 by default;
+ * 8, 32 and 64 are the window ablations of Fig. 10.  r_window = 16 chunks for
+ * r_h of Eq. (11) (the only supported value).  norm_weight: DEVICE [dv] fp32
+ * RMSNorm scale used in the gate energy, or NULL for ones.
+ * Selector ablations of Sec. 3.5 (0 = the method as defined):
+ *   fixed_tiers = 1      3 High / 4 Medium / 9 Low head pairs in every layer
+ *                        (Table 5) instead of the counts of Eqs. (13)-(14);
+ *                        pairs are still assigned by x_H, then x_M.
+ *   unit_visibility = 1  G_h = 1 for every head (gate energy not used).
+ *   rank_key             DEVICE [B, NP, C] fp32 keys, or NULL: the kept
+ *                        non-anchor chunks of a pair are those with the
+ *                        largest keys (ties: lower chunk) instead of the
+ *                        largest q_c; tiers and keep counts stay adaptive
+ *                        (random keys = random selection at matched budget). */
 typedef struct {
   float keep_budget;
   int32_t tail;
   int32_t r_window;
   const float* norm_weight;
+  int32_t fixed_tiers;
+  int32_t unit_visibility;
+  const float* rank_key;
 } sgdn_sparse_params;
 
 /* Per-sequence statistics written on the device. */

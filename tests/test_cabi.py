@@ -102,7 +102,11 @@ def test_sparse_and_select_argument_errors(L):
     assert sparse(_prob(), None) == -1
     assert sparse(_prob(n_qk=8, n_v=16), good) == -2
     assert sparse(_prob(), ops.sparse_params(keep_budget=0.0)) == -1
-    assert sparse(_prob(), ops.sparse_params(tail=8)) == -2
+    assert sparse(_prob(), ops.sparse_params(tail=12)) == -2
+    assert sparse(_prob(), ops.sparse_params(tail=128)) == -2
+    bad = ops.sparse_params()
+    bad.fixed_tiers = 2
+    assert sparse(_prob(), bad) == -1
     assert sparse(_prob(), good, z=None) == -1               # no gate and no mask
     assert sparse(_prob(seqlen=64 * 8193), good) == -2       # C > 8192
     assert sparse(_prob(), good, ws_bytes=4096) == -3
