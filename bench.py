@@ -13,7 +13,9 @@ of 128 sequences through the same 24 layers, states updated in place).  A
 packed variable-length leg reads the same tokens as 16 sequences of mixed
 lengths (cu_seqlens) and times both paths again.  A selector-ablation leg
 times the sparse step with each switch of Sec. 3.5 (fixed 3/4/9 tiers,
-G_h = 1, random keys at matched budget, Tail-8/32/64 windows).
+G_h = 1, random keys at matched budget, Tail-8/32/64 windows), and a
+kernel-pipeline ablation leg times it with deferred W and compact states
+undone (Table 6), reporting each mechanism's speedup over its stages.
 
 Prints one JSON line.  value = tokens/s of the 24-layer stack (B*T per step);
 roofline = the dominant kernel's algorithmic bytes per launch over its mean
@@ -54,6 +56,8 @@ def parse():
                     help="tokens of layer 0 the oracle baseline processes")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed variable-length leg")
+    ap.add_argument("--no-ablations", action="store_true",
+                    help="skip the kernel-pipeline ablation leg")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the selector-ablation leg")
     ap.add_argument("--decode-batch", type=int, default=128,
@@ -150,6 +154,65 @@ def cpu_baseline(inputs0, tokens=32768):
                 sample=(f"fp64 numpy oracle, SparseGDN 29% path, layer 0's first {tokens} tokens, "
                         f"all 32 value heads, one layer timed ({dt:.1f} s) and scaled by 1/24; "
                         f"BLAS calls use up to {threads} threads, the rest one"))
+
+
+def time_stack(args, hip, L, call):
+    """Warm-up then args.steps timed passes of call(l, dbg) over L layers;
+    returns (ms per step, mean ms per launch of every stage)."""
+    import torch
+    from gated_deltanet_prefill_chunkwise_amd import ops
+    nev = len(STAGES) + 1
+    events = [[[hip.event() for _ in range(nev)] for _ in range(L)] for _ in range(args.steps)]
+    dbgs = [[ops.debug_struct(events=events[s][l]) for l in range(L)] for s in range(args.steps)]
+    for _ in range(args.warmup):
+        for l in range(L):
+            call(l, None)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s_ in range(args.steps):
+        for l in range(L):
+            call(l, dbgs[s_][l])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    stage = {name: round(sum(hip.elapsed_ms(events[s_][l][i], events[s_][l][i + 1])
+                             for s_ in range(args.steps) for l in range(L)) / (args.steps * L), 4)
+             for i, name in enumerate(STAGES)}
+    return ms, stage
+
+
+def ablation_leg(args, layers, hip, prob, dev):
+    """The sparse step with each kernel-pipeline ablation of Table 6 (the
+    mechanism undone), beside the default; speedup = ablated / default time
+    over the stages of the row's scope."""
+    import torch
+    from gated_deltanet_prefill_chunkwise_amd import ops
+    out = {}
+    scope = {"deferred_w": ("intra", "deferred_w", "hscan", "o"),
+             "compact_states": ("hscan",), "deferred_w+compact_states": ("intra", "deferred_w", "hscan", "o")}
+    runs = {"default": (), "deferred_w": ("deferred_w",), "compact_states": ("compact_states",),
+            "deferred_w+compact_states": ("deferred_w", "compact_states")}
+    for name, ab in runs.items():
+        ws = torch.empty(ops.workspace_bytes(prob, True, ops.sparse_params(ablate=ab)),
+                         dtype=torch.uint8, device=dev)
+
+        def call(l, dbg, ab=ab, ws=ws):
+            inp, o, sf, st = layers[l]
+            ops.prefill_sparse(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"], z=inp["z"],
+                               keep_budget=0.29, solve="blockadj", o=o, s_final=sf, stats=st,
+                               workspace=ws, debug=dbg, ablate=ab)
+        ms, stage = time_stack(args, hip, len(layers), call)
+        del ws
+        out[name] = {"ms_per_step": round(ms, 4), "stage_ms_per_launch": stage}
+        print(f"[bench] ablation {name}: {ms:.3f} ms per {args.layers}-layer step; stages "
+              + ", ".join(f"{k} {v:.3f}" for k, v in stage.items()), file=sys.stderr, flush=True)
+    base = out["default"]["stage_ms_per_launch"]
+    for name, sc in scope.items():
+        st = out[name]["stage_ms_per_launch"]
+        out[name]["scope"] = "+".join(sc)
+        out[name]["speedup_of_mechanism"] = round(sum(st[k] for k in sc) / sum(base[k] for k in sc), 3)
+    return out
 
 
 def varlen_lengths(total: int, n: int = 16, seed: int = 7):
@@ -465,6 +528,8 @@ def main():
         out["sparse"]["snapshot_fraction"] = round(sigma, 5)
     if "sparse" in res and "dense" in res:
         out["sparse_speedup_over_dense"] = round(res["dense"]["ms_per_step"] / res["sparse"]["ms_per_step"], 3)
+    if not args.no_ablations and "sparse" in res:
+        out["pipeline_ablations"] = ablation_leg(args, layers, hip, prob, dev)
     if not args.no_variants and "sparse" in res:
         # the rank-key variant needs one more rank table in the workspace
         key_shape = torch.empty((B, NV // 2, C), device=dev)

@@ -18,6 +18,7 @@ struct Plan {
   int B, T, Nq, Nv, C, G, esz, isz, bf16, solve;
   const int32_t* cu;   // packed sequence offsets or null
   int kL, kM, kH;
+  int ablate;      // SGDN_ABLATE_* bits (sparse)
   int Emax;        // event capacity per sequence inside prefill_sparse
   int snap_cap;    // snapshot slots per sequence (sparse) or per head (dense)
   size_t off[32];
@@ -26,7 +27,7 @@ struct Plan {
 
 enum Buf { B_G, B_GAMMA, B_P, B_U, B_W, B_CB, B_KT, B_SNAP, B_S0T, B_SCORE, B_ETA, B_RANK,
            B_TINFO, B_MASK, B_TIER, B_ROWPAIR, B_ROWPTR, B_COL, B_PRED, B_GSLOT, B_ESLOT,
-           B_WPK, B_STATS, B_FAC, B_REC, B_CHUNKS, B_SPART, B_RANK2, B_COUNT };
+           B_WPK, B_STATS, B_FAC, B_REC, B_CHUNKS, B_SPART, B_RANK2, B_ENTRY, B_COUNT };
 
 static_assert(B_COUNT <= (int)(sizeof(Plan::off) / sizeof(size_t)), "workspace table too small");
 
@@ -76,6 +77,8 @@ int check_params(const sgdn_problem* pr, const sgdn_sparse_params* sp) {
   if ((sp->fixed_tiers != 0 && sp->fixed_tiers != 1) ||
       (sp->unit_visibility != 0 && sp->unit_visibility != 1))
     return SGDN_EINVAL;
+  if (sp->ablate & ~(SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_COMPACT_STATES)) return SGDN_EINVAL;
+  if ((sp->ablate & SGDN_ABLATE_DEFERRED_W) && pr->cu_seqlens != nullptr) return SGDN_EUNSUPPORTED;
   if (pr->n_v != 2 * NP_SPARSE) return SGDN_EUNSUPPORTED;
   const int C = (pr->seqlen + 63) / 64;
   if (C > 8192) return SGDN_EUNSUPPORTED;
@@ -89,6 +92,7 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
   p.isz = p.bf16 ? 2 : 4;   // intermediates: fp16 for bf16 inputs, fp32 for fp32 inputs
   int k[3] = {p.C, p.C, p.C};
   if (sparse) tier_counts(p.C, budget_bp(sp->keep_budget), k);
+  p.ablate = sparse ? sp->ablate : 0;
   p.kL = k[0]; p.kM = k[1]; p.kH = k[2];
   const int NP = p.Nv / 2;
   p.Emax = NP * p.C;
@@ -109,7 +113,9 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
     sz[B_W] = B * Nv * C * L * DK * I;
     sz[B_SNAP] = B * Nv * (size_t)p.snap_cap * DV * DK * I;
   } else {
-    sz[B_CB] = B * Nv * C * L * L * I;
+    if (p.ablate & SGDN_ABLATE_DEFERRED_W) sz[B_W] = B * Nv * C * L * DK * I;   // W of every chunk
+    else sz[B_CB] = B * Nv * C * L * L * I;
+    if (p.ablate & SGDN_ABLATE_COMPACT_STATES) sz[B_ENTRY] = B * Nv * G * DV * DK * I;
     sz[B_SNAP] = B * (size_t)p.snap_cap * 2 * DV * DK * I;
     sz[B_SCORE] = B * Nv * C * 4;
     sz[B_SPART] = B * Nv * C * 8 * 4;
@@ -125,7 +131,7 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
     sz[B_PRED] = B * NP * G * 4;
     sz[B_GSLOT] = B * NP * G * 4;
     sz[B_ESLOT] = B * (size_t)p.Emax * 4;
-    sz[B_WPK] = B * (size_t)p.Emax * 2 * L * DK * I;
+    if (!(p.ablate & SGDN_ABLATE_DEFERRED_W)) sz[B_WPK] = B * (size_t)p.Emax * 2 * L * DK * I;
     sz[B_STATS] = B * 9 * 4;
   }
   size_t o = 0;
@@ -165,8 +171,9 @@ IntraArgs intra_args(const Plan& pl, void* ws, const void* k, const void* v, con
   ia.gamma = at<float>(ws, pl, B_GAMMA);
   ia.fac = at<float>(ws, pl, B_FAC);
   ia.U = at<void>(ws, pl, B_U);
-  ia.W = sparse ? nullptr : at<void>(ws, pl, B_W);
-  ia.Cb = sparse ? at<void>(ws, pl, B_CB) : nullptr;
+  const bool wall = sparse && (pl.ablate & SGDN_ABLATE_DEFERRED_W);
+  ia.W = (sparse && !wall) ? nullptr : at<void>(ws, pl, B_W);
+  ia.Cb = (sparse && !wall) ? at<void>(ws, pl, B_CB) : nullptr;
   ia.KT = at<void>(ws, pl, B_KT);
   ia.score_part = sparse ? at<float>(ws, pl, B_SPART) : nullptr;
   return ia;
@@ -383,12 +390,16 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
     if (dbg->tier) SGDN_TRY(hipMemcpyAsync(dbg->tier, sa.tier, (size_t)pl.B * NP, hipMemcpyDeviceToDevice, s));
   }
 
-  // deferred W of the kept events
-  DeferredWArgs da{};
-  da.KT = at<void>(ws, pl, B_KT); da.Cb = at<void>(ws, pl, B_CB); da.Wpk = at<void>(ws, pl, B_WPK);
-  da.row_pair = sa.row_pair; da.row_ptr = sa.row_ptr; da.col = sa.col;
-  da.B = pl.B; da.Nv = pl.Nv; da.Nq = pl.Nq; da.C = pl.C; da.Emax = Emax; da.solve = pl.solve;
-  SGDN_TRY(launch_deferred_w(da, pl.bf16, s));
+  // deferred W of the kept events (the deferred-W ablation has W of every
+  // chunk from the intra stage instead)
+  const bool wall = (pl.ablate & SGDN_ABLATE_DEFERRED_W) != 0;
+  if (!wall) {
+    DeferredWArgs da{};
+    da.KT = at<void>(ws, pl, B_KT); da.Cb = at<void>(ws, pl, B_CB); da.Wpk = at<void>(ws, pl, B_WPK);
+    da.row_pair = sa.row_pair; da.row_ptr = sa.row_ptr; da.col = sa.col;
+    da.B = pl.B; da.Nv = pl.Nv; da.Nq = pl.Nq; da.C = pl.C; da.Emax = Emax; da.solve = pl.solve;
+    SGDN_TRY(launch_deferred_w(da, pl.bf16, s));
+  }
 
   if (s0 != nullptr) {
     S0PrepArgs s0a{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv};
@@ -402,7 +413,8 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   SGDN_TRY(launch_evrec(ea, s));
   mark(dbg, SGDN_EV_DEFERRED, s);
   HScanArgs ha{};
-  ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, B_WPK); ha.U = at<void>(ws, pl, B_U);
+  ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, wall ? B_W : B_WPK); ha.U = at<void>(ws, pl, B_U);
+  ha.w_by_chunk = wall;
   ha.fac = at<float>(ws, pl, B_FAC); ha.rec = ea.rec; ha.P = at<double>(ws, pl, B_P);
   ha.s0 = s0; ha.s_final = s_final; ha.snap = at<void>(ws, pl, B_SNAP);
   ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 1;
@@ -410,6 +422,15 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   ha.row_pair = sa.row_pair; ha.row_ptr = sa.row_ptr; ha.col = sa.col; ha.event_slot = sa.event_slot;
   ha.Emax = Emax; ha.snap_cap = pl.snap_cap;
   SGDN_TRY(launch_hscan(ha, pl.bf16, s));
+  void* entry = nullptr;
+  if (pl.ablate & SGDN_ABLATE_COMPACT_STATES) {
+    // compact-states ablation: dense group-entry states for O
+    entry = at<void>(ws, pl, B_ENTRY);
+    ExpandArgs xa{at<void>(ws, pl, B_SNAP), s0 ? at<void>(ws, pl, B_S0T) : nullptr,
+                  at<double>(ws, pl, B_P), sa.pred, sa.group_slot, entry,
+                  pl.B, pl.Nv, pl.C, pl.G, pl.snap_cap, pl.T, pl.cu};
+    SGDN_TRY(launch_expand(xa, pl.bf16, s));
+  }
   mark(dbg, SGDN_EV_HSCAN, s);
 
   OChunkArgs oa{};
@@ -418,7 +439,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   oa.o_bf16 = prob->o_dtype == SGDN_BF16;
   oa.g = at<float>(ws, pl, B_G); oa.gamma = at<float>(ws, pl, B_GAMMA); oa.P = at<double>(ws, pl, B_P);
   oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
-  oa.cu = pl.cu;
+  oa.cu = pl.cu; oa.entry = entry;
   oa.sparse = 1; oa.pred = sa.pred; oa.group_slot = sa.group_slot; oa.snap_cap = pl.snap_cap;
   SGDN_TRY(launch_ochunk(oa, pl.bf16, s));
   mark(dbg, SGDN_EV_O, s);

@@ -240,6 +240,9 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
       return SPARSE ? colc[__builtin_amdgcn_readfirstlane(e)] : e;
     };
     const I* Wbase = static_cast<const I*>(p.W);
+    // W packed per kept event (deferred W), or per chunk (dense, and the
+    // deferred-W ablation of the sparse path)
+    const bool w_ev = SPARSE && !p.w_by_chunk;
     const I* KTbase = static_cast<const I*>(p.KT);
     // L2 prefetch of event e (clamped to the row): lanes 0-15 the 16 W lines
     // of this slice's share of the head's tile, 16-23 this workgroup's 8 of
@@ -250,7 +253,7 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
       const int c = col_at(e);
       const size_t hc = bh * C + c;
       const char* Wt = reinterpret_cast<const char*>(
-          SPARSE ? Wbase + (((size_t)b * p.Emax + e) * 2 + hh) * L * DK : Wbase + hc * L * DK);
+          w_ev ? Wbase + (((size_t)b * p.Emax + e) * 2 + hh) * L * DK : Wbase + hc * L * DK);
       const char* Kt = reinterpret_cast<const char*>(KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L);
       const char* Ut = reinterpret_cast<const char*>(Ubase + hc * DV * L + dv0 * L);
       const char* src = Wt + slice * 16 * 128;
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
     auto issue = [&](int j, int c, int s, int u0, int u1) __attribute__((always_inline)) {
       const size_t hc = bh * C + c;
       const char* Wt = reinterpret_cast<const char*>(
-          SPARSE ? Wbase + (((size_t)b * p.Emax + j) * 2 + hh) * L * DK : Wbase + hc * L * DK);
+          w_ev ? Wbase + (((size_t)b * p.Emax + j) * 2 + hh) * L * DK : Wbase + hc * L * DK);
       const char* Kt = reinterpret_cast<const char*>(KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L);
       const I* Ut = Ubase + hc * DV * L + dv0 * L;
       const int32_t* rec = SPARSE ? p.rec + (((size_t)b * p.Emax + j) * 2 + hh) * 4 : p.rec + hc * 4;

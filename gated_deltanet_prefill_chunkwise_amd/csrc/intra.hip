@@ -137,9 +137,11 @@ __device__ __forceinline__ CoefFrag<E> coef_frag(const float* sCt, const float* 
   return f;
 }
 
-// VARLEN: packed sequences (offsets in p.cu); the dense-layout instance has
-// no offset reads at all.
-template <typename E, bool BA, bool SPARSE, bool VARLEN>
+// MODE 0: dense (W); 1: sparse (staged Cb and the tail-score parts; W is
+// deferred to the kept events); 2: the deferred-W ablation (W of every chunk
+// and the tail-score parts).  VARLEN: packed sequences (offsets in p.cu); the
+// dense-layout instances have no offset reads at all.
+template <typename E, bool BA, int MODE, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
   using I = inter_t<E>;
   __shared__ __align__(16) E sK[L * KS];      // key tile, row-major [t][dk]
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (SPARSE) {
+        if constexpr (MODE != 0) {
           // Eq. (9) in parts: sums of squares of U over 8-row blocks, from the
           // fp32 accumulators (lanes 0-31 hold rows 16w..16w+7, lanes 32-63
           // rows 16w+8..16w+15); the tail score sums the blocks of its window
@@ -475,7 +477,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
       // keep the U and W products apart (their accumulators would otherwise
       // be live at the same time)
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (SPARSE) {
+      if constexpr (MODE == 1) {
         I* cb = static_cast<I*>(p.Cb) + hc * L * L;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -510,9 +512,9 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
   }
 }
 
-template <typename E, bool BA, bool SPARSE, bool VARLEN>
+template <typename E, bool BA, int MODE, bool VARLEN>
 hipError_t launch_one(const IntraArgs& a, hipStream_t s) {
-  const auto fn = intra_kernel<E, BA, SPARSE, VARLEN>;
+  const auto fn = intra_kernel<E, BA, MODE, VARLEN>;
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -527,19 +529,23 @@ hipError_t launch_one(const IntraArgs& a, hipStream_t s) {
 
 }  // namespace
 
-template <typename E, bool BA, bool SPARSE>
+template <typename E, bool BA, int MODE>
 hipError_t launch_vl(const IntraArgs& a, hipStream_t s) {
-  return a.cu != nullptr ? launch_one<E, BA, SPARSE, true>(a, s) : launch_one<E, BA, SPARSE, false>(a, s);
+  return a.cu != nullptr ? launch_one<E, BA, MODE, true>(a, s) : launch_one<E, BA, MODE, false>(a, s);
+}
+
+template <typename E, bool BA>
+hipError_t launch_mode(const IntraArgs& a, hipStream_t s) {
+  if (a.score_part == nullptr) return launch_vl<E, BA, 0>(a, s);
+  if (a.Cb != nullptr) return launch_vl<E, BA, 1>(a, s);
+  // deferred-W ablation: dense layout only
+  return a.cu == nullptr ? launch_one<E, BA, 2, false>(a, s) : hipErrorInvalidValue;
 }
 
 hipError_t launch_intra(const IntraArgs& a, int bf16, hipStream_t s) {
-  const bool ba = a.solve == 1, sparse = a.Cb != nullptr;
-  if (bf16) {
-    if (ba) return sparse ? launch_vl<sgdn::bf16, true, true>(a, s) : launch_vl<sgdn::bf16, true, false>(a, s);
-    return sparse ? launch_vl<sgdn::bf16, false, true>(a, s) : launch_vl<sgdn::bf16, false, false>(a, s);
-  }
-  if (ba) return sparse ? launch_vl<float, true, true>(a, s) : launch_vl<float, true, false>(a, s);
-  return sparse ? launch_vl<float, false, true>(a, s) : launch_vl<float, false, false>(a, s);
+  const bool ba = a.solve == 1;
+  if (bf16) return ba ? launch_mode<sgdn::bf16, true>(a, s) : launch_mode<sgdn::bf16, false>(a, s);
+  return ba ? launch_mode<float, true>(a, s) : launch_mode<float, false>(a, s);
 }
 
 }  // namespace sgdn

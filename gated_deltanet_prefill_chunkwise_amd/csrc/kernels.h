@@ -70,6 +70,7 @@ struct HScanArgs {
   int B, Nq, Nv, C;
   int sparse;
   const int32_t* cu; int T;  // packed sequences: a dense chain stops at its valid chunks
+  int w_by_chunk;           // sparse: W [B][Nv][C][8192] per chunk (deferred-W ablation)
   // sparse metadata (per batch)
   const int32_t* row_pair;  // [B][NP]
   const int32_t* row_ptr;   // [B][NP+1]
@@ -89,6 +90,19 @@ struct OChunkArgs {
   const int32_t* pred;        // [B][NP][G]
   const int32_t* group_slot;  // [B][NP][G]
   int snap_cap;
+  // compact-states ablation: dense group-entry states [B][Nv][G][dv][dk]
+  // (already decayed), read instead of the compact snapshots; or null
+  const void* entry;
+};
+
+// Compact-states ablation: every group's entry state S_2r written out densely
+// from the compact snapshots (or s0), decayed by 2^(P_2r - P_e+1).
+struct ExpandArgs {
+  const void* snap; const void* s0T; const double* P;
+  const int32_t* pred; const int32_t* group_slot;
+  void* entry;
+  int B, Nv, C, G, snap_cap, T;
+  const int32_t* cu;
 };
 
 // Per-event records of the H scan: the gap factor F_in that carries the state
@@ -146,6 +160,7 @@ struct DecodeArgs {
 hipError_t launch_intra(const IntraArgs& a, int bf16, hipStream_t s);
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_expand(const ExpandArgs& a, int bf16, hipStream_t s);
 hipError_t launch_chunk_table(const ChunkTableArgs& a, hipStream_t s);
 hipError_t launch_hscan(const HScanArgs& a, int bf16, hipStream_t s);
 hipError_t launch_ochunk(const OChunkArgs& a, int bf16, hipStream_t s);

@@ -92,6 +92,43 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs p) {
   p.score[i] = sqrtf(s);
 }
 
+// Compact-states ablation (SparseGDN reading notes, Sec. 3.6, Table 6): the
+// entry state of every output group r, S_2r = 2^(P_2r - P_e+1) S_e+1 from the
+// snapshot of its predecessor event e (Sec. 2.6, Eq. (21)), or 2^P_2r s0, or
+// zero, written densely.  One workgroup per (group, head); groups past a
+// packed sequence's end are skipped (nothing reads them).
+template <typename I>
+__global__ __launch_bounds__(256) void expand_kernel(ExpandArgs p) {
+  const int r = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / p.Nv, h = bh - b * p.Nv, pr = h >> 1, hh = h & 1;
+  if (p.cu != nullptr && 2 * r * L >= seq_span(p.cu, b, p.T).len) return;
+  const size_t pg = ((size_t)b * (p.Nv / 2) + pr) * p.G + r;
+  const int slot = p.group_slot[pg];
+  const double* P = p.P + (size_t)bh * (p.C + 1);
+  const I* src = nullptr;
+  float f = 0.f;
+  if (slot >= 0) {
+    src = static_cast<const I*>(p.snap) + (((size_t)b * p.snap_cap + slot) * 2 + hh) * DV * DK;
+    f = exp2f((float)(P[2 * r] - P[p.pred[pg] + 1]));
+  } else if (p.s0T != nullptr) {
+    src = static_cast<const I*>(p.s0T) + (size_t)bh * DV * DK;
+    f = exp2f((float)P[2 * r]);
+  }
+  I* dst = static_cast<I*>(p.entry) + ((size_t)bh * p.G + r) * DV * DK;
+  for (int i = threadIdx.x * 8; i < DV * DK; i += 256 * 8) {
+    frag_t<I> y;
+    if (src != nullptr) {
+      const frag_t<I> x = *reinterpret_cast<const frag_t<I>*>(src + i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = from_f<I>(f * to_f(x[j]));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = from_f<I>(0.f);
+    }
+    *reinterpret_cast<frag_t<I>*>(dst + i) = y;
+  }
+}
+
 // s0 [dk][dv] -> transposed [dv][dk] in the snapshot element type, the
 // "virtual snapshot" that output groups without a predecessor read.
 template <typename I>
@@ -234,6 +271,15 @@ __global__ __launch_bounds__(256) void debug_u_kernel(const void* Ut_, float* U)
 
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(prefix_kernel, dim3(a.B * a.Nv), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand(const ExpandArgs& a, int bf16, hipStream_t s) {
+  const dim3 grid(a.G, a.B * a.Nv);
+  if (bf16)
+    hipLaunchKernelGGL(expand_kernel<fp16>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(expand_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

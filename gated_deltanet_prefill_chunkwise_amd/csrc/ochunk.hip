@@ -83,7 +83,9 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   // ---- group entry state: source and log2 factor
   const I* Ssrc = nullptr;
   float lf = 0.f;
-  if (p.sparse) {
+  if (p.entry != nullptr) {
+    Ssrc = static_cast<const I*>(p.entry) + (bh * G + r) * DV * DK;
+  } else if (p.sparse) {
     const size_t pg = ((size_t)b * (Nv / 2) + pr) * G + r;
     const int slot = p.group_slot[pg];
     const double* P = p.P + bh * (C + 1);

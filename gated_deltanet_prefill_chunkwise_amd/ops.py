@@ -28,7 +28,10 @@ class SparseParams(ctypes.Structure):
     _fields_ = [("keep_budget", ctypes.c_float), ("tail", ctypes.c_int32),
                 ("r_window", ctypes.c_int32), ("norm_weight", ctypes.c_void_p),
                 ("fixed_tiers", ctypes.c_int32), ("unit_visibility", ctypes.c_int32),
-                ("rank_key", ctypes.c_void_p)]
+                ("rank_key", ctypes.c_void_p), ("ablate", ctypes.c_int32)]
+
+
+ABLATE = {"deferred_w": 1, "compact_states": 2}   # SGDN_ABLATE_* bits
 
 
 class Stats(ctypes.Structure):
@@ -133,13 +136,17 @@ def problem(q, v, solve="exact", out_dtype=None, cu_seqlens=None, max_seqlen=Non
 
 
 def sparse_params(keep_budget=0.29, norm_weight=None, tail=16, r_window=16, fixed_tiers=False,
-                  unit_visibility=False, rank_key=None) -> SparseParams:
+                  unit_visibility=False, rank_key=None, ablate=()) -> SparseParams:
     """Selector parameters; ``rank_key`` (device fp32 [B, Nv/2, C]) and the
-    flags are the selector ablations described in include/sgdn.h."""
+    flags are the selector ablations, ``ablate`` names kernel-pipeline
+    ablations (keys of ABLATE), all described in include/sgdn.h."""
+    bits = 0
+    for name in ablate:
+        bits |= ABLATE[name]
     return SparseParams(float(keep_budget), tail, r_window,
                         None if norm_weight is None else norm_weight.data_ptr(),
                         int(bool(fixed_tiers)), int(bool(unit_visibility)),
-                        None if rank_key is None else rank_key.data_ptr())
+                        None if rank_key is None else rank_key.data_ptr(), bits)
 
 
 def workspace_bytes(prob: Problem, sparse: bool, params: SparseParams | None = None) -> int:
@@ -300,7 +307,7 @@ def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
                    mask_override=None, s0=None, norm_weight=None, want_state=True, o=None,
                    s_final=None, stats=None, workspace=None, debug=None, stream=None,
                    out_dtype=None, cu_seqlens=None, max_seqlen=None, tail=16, fixed_tiers=False,
-                   unit_visibility=False, rank_key=None):
+                   unit_visibility=False, rank_key=None, ablate=()):
     """SparseGDN prefill; returns (o, s_final, stats[B, 9] int32).
 
     o is fp32 unless ``out_dtype`` (or a given ``o``) says otherwise.  With
@@ -323,7 +330,7 @@ def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
                                                          -(-prob.seqlen // 64)):
         raise ValueError("rank_key must be [B, Nv/2, C]")
     params = sparse_params(keep_budget, norm_weight, tail=tail, fixed_tiers=fixed_tiers,
-                           unit_visibility=unit_visibility, rank_key=rank_key)
+                           unit_visibility=unit_visibility, rank_key=rank_key, ablate=ablate)
     B, Nv, dv = prob.batch, v.shape[2], v.shape[3]
     if o is None:
         o = torch.empty(v.shape, dtype=out_dtype, device=v.device)

@@ -105,7 +105,22 @@ typedef struct {
   int32_t fixed_tiers;
   int32_t unit_visibility;
   const float* rank_key;
+  int32_t ablate;   /* SGDN_ABLATE_* bits, 0 for the method as defined */
 } sgdn_sparse_params;
+
+/* Kernel-pipeline ablations (Sec. 3.6, Table 6): reference paths that undo
+ * one mechanism each, for measuring what it buys; outputs agree with the
+ * default path within rounding.
+ *   SGDN_ABLATE_DEFERRED_W      W of every chunk is formed in the intra stage
+ *                               and read by chunk in the H scan (the packed-W
+ *                               path), instead of W of the kept events after
+ *                               selection (Eq. (15)).  Not with cu_seqlens.
+ *   SGDN_ABLATE_COMPACT_STATES  the entry state of every output group is
+ *                               written out densely (decayed from the compact
+ *                               snapshots) and O reads it, instead of O
+ *                               reading the compact snapshots with the gap
+ *                               factor (Eq. (21)). */
+enum { SGDN_ABLATE_DEFERRED_W = 1, SGDN_ABLATE_COMPACT_STATES = 2 };
 
 /* Per-sequence statistics written on the device. */
 typedef struct {

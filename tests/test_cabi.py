@@ -107,6 +107,11 @@ def test_sparse_and_select_argument_errors(L):
     bad = ops.sparse_params()
     bad.fixed_tiers = 2
     assert sparse(_prob(), bad) == -1
+    bad = ops.sparse_params()
+    bad.ablate = 4
+    assert sparse(_prob(), bad) == -1
+    # the packed-W ablation is defined for the dense layout only
+    assert sparse(_prob(cu_seqlens=0x2000), ops.sparse_params(ablate=("deferred_w",))) == -2
     assert sparse(_prob(), good, z=None) == -1               # no gate and no mask
     assert sparse(_prob(seqlen=64 * 8193), good) == -2       # C > 8192
     assert sparse(_prob(), good, ws_bytes=4096) == -3
