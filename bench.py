@@ -18,8 +18,11 @@ kernel-pipeline ablation leg times it with deferred W and compact states
 undone (Table 6), reporting each mechanism's speedup over its stages.
 
 Prints one JSON line.  value = tokens/s of the 24-layer stack (B*T per step);
-roofline = the dominant kernel's algorithmic bytes per launch over its mean
-launch time (HIP events recorded by the library on the launch stream);
+roofline = the dominant kernel's algorithmic bytes per layer over its mean
+time per layer (HIP events recorded by the library on the caller's stream;
+in the sparse path the H scan of CSR rows 4-15 runs on a second stream
+during the launch for rows 0-3, which the events bracket, so the bytes of
+both count over that time; traffic likewise sums both launches);
 cpu_baseline = the fp64 numpy oracle on a bounded sample (layer 0's first
 32768 tokens, all heads), in the same unit.
 """

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/sgdn.h"
 #include "common.h"
 #include "kernels.h"
@@ -179,6 +181,39 @@ IntraArgs intra_args(const Plan& pl, void* ws, const void* k, const void* v, con
   return ia;
 }
 
+// Second stream of the sparse path with its fork / join events, one set per
+// device, created on first use and kept for the life of the process.  The
+// mutex keeps the events of concurrent calls on one device apart.
+constexpr int SPLIT_ROWS = 4;   // most High-tier pairs of a sequence
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+constexpr int MAX_DEVICES = 64;
+Side g_side[MAX_DEVICES];
+std::mutex g_side_init;
+
+int side_stream(Side** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return SGDN_EHIP;
+  Side& sd = g_side[dev];
+  std::lock_guard<std::mutex> lk(g_side_init);
+  if (sd.s == nullptr) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess ||
+        hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess)
+      return SGDN_EHIP;
+    sd.fork = f;
+    sd.join = j;
+    sd.s = st;
+  }
+  *out = &sd;
+  return SGDN_OK;
+}
+
 // Packed sequences: the table of valid chunks the intra kernel walks.
 int chunk_table(const Plan& pl, void* ws, hipStream_t s) {
   if (pl.cu == nullptr) return SGDN_OK;
@@ -260,6 +295,7 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   ha.s0 = s0; ha.s_final = s_final; ha.snap = at<void>(ws, pl, B_SNAP);
   ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 0;
   ha.cu = pl.cu; ha.T = pl.T;
+  ha.row_lo = 0; ha.nrows = pl.Nv / 2; ha.xcd_shift = 0;
   SGDN_TRY(launch_hscan(ha, pl.bf16, s));
   mark(dbg, SGDN_EV_HSCAN, s);
   OChunkArgs oa{};
@@ -269,6 +305,7 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   oa.g = at<float>(ws, pl, B_G); oa.gamma = at<float>(ws, pl, B_GAMMA); oa.P = nullptr;
   oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
   oa.cu = pl.cu;
+  oa.row_lo = 0; oa.nrows = pl.Nv / 2;
   oa.sparse = 0;
   SGDN_TRY(launch_ochunk(oa, pl.bf16, s));
   mark(dbg, SGDN_EV_O, s);
@@ -421,6 +458,42 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   ha.cu = nullptr; ha.T = pl.T;
   ha.row_pair = sa.row_pair; ha.row_ptr = sa.row_ptr; ha.col = sa.col; ha.event_slot = sa.event_slot;
   ha.Emax = Emax; ha.snap_cap = pl.snap_cap;
+  OChunkArgs oa{};
+  oa.q = q; oa.k = k; oa.U = at<void>(ws, pl, B_U); oa.snap = at<void>(ws, pl, B_SNAP);
+  oa.s0T = s0 ? at<void>(ws, pl, B_S0T) : nullptr;
+  oa.o_bf16 = prob->o_dtype == SGDN_BF16;
+  oa.g = at<float>(ws, pl, B_G); oa.gamma = at<float>(ws, pl, B_GAMMA); oa.P = at<double>(ws, pl, B_P);
+  oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
+  oa.cu = pl.cu; oa.row_pair = sa.row_pair;
+  oa.sparse = 1; oa.pred = sa.pred; oa.group_slot = sa.group_slot; oa.snap_cap = pl.snap_cap;
+
+  if (pl.B == 1 && !(pl.ablate & SGDN_ABLATE_COMPACT_STATES)) {
+    // CSR rows 0-3 hold every High-tier pair (at most 4), whose chains are
+    // the longest and bound the H scan.  The H scan and O of rows 4-15 run on
+    // a second stream beside them, so O of the shorter chains overlaps the
+    // long ones; rows 4-15 start at XCD 4, rows 0-3 at XCD 0, which keeps
+    // 32 workgroups on every XCD.
+    Side* sd = nullptr;
+    if ((st = side_stream(&sd)) != SGDN_OK) return st;
+    std::lock_guard<std::mutex> lk(sd->mu);
+    SGDN_TRY(hipEventRecord(sd->fork, s));
+    SGDN_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0));
+    ha.row_lo = SPLIT_ROWS; ha.nrows = NP - SPLIT_ROWS; ha.xcd_shift = SPLIT_ROWS;
+    SGDN_TRY(launch_hscan(ha, pl.bf16, sd->s));
+    oa.row_lo = SPLIT_ROWS; oa.nrows = NP - SPLIT_ROWS;
+    SGDN_TRY(launch_ochunk(oa, pl.bf16, sd->s));
+    SGDN_TRY(hipEventRecord(sd->join, sd->s));
+    ha.row_lo = 0; ha.nrows = SPLIT_ROWS; ha.xcd_shift = 0;
+    SGDN_TRY(launch_hscan(ha, pl.bf16, s));
+    mark(dbg, SGDN_EV_HSCAN, s);
+    oa.row_lo = 0; oa.nrows = SPLIT_ROWS;
+    SGDN_TRY(launch_ochunk(oa, pl.bf16, s));
+    SGDN_TRY(hipStreamWaitEvent(s, sd->join, 0));
+    mark(dbg, SGDN_EV_O, s);
+    return SGDN_OK;
+  }
+
+  ha.row_lo = 0; ha.nrows = NP; ha.xcd_shift = 0;
   SGDN_TRY(launch_hscan(ha, pl.bf16, s));
   void* entry = nullptr;
   if (pl.ablate & SGDN_ABLATE_COMPACT_STATES) {
@@ -432,15 +505,8 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
     SGDN_TRY(launch_expand(xa, pl.bf16, s));
   }
   mark(dbg, SGDN_EV_HSCAN, s);
-
-  OChunkArgs oa{};
-  oa.q = q; oa.k = k; oa.U = at<void>(ws, pl, B_U); oa.snap = at<void>(ws, pl, B_SNAP);
-  oa.s0T = s0 ? at<void>(ws, pl, B_S0T) : nullptr;
-  oa.o_bf16 = prob->o_dtype == SGDN_BF16;
-  oa.g = at<float>(ws, pl, B_G); oa.gamma = at<float>(ws, pl, B_GAMMA); oa.P = at<double>(ws, pl, B_P);
-  oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
-  oa.cu = pl.cu; oa.entry = entry;
-  oa.sparse = 1; oa.pred = sa.pred; oa.group_slot = sa.group_slot; oa.snap_cap = pl.snap_cap;
+  oa.entry = entry;
+  oa.row_lo = 0; oa.nrows = NP;
   SGDN_TRY(launch_ochunk(oa, pl.bf16, s));
   mark(dbg, SGDN_EV_O, s);
   return SGDN_OK;

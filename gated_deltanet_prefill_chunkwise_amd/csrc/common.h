@@ -204,4 +204,5 @@ __device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, int b, int T) {
 }
 __device__ __forceinline__ int chunks_of(int len) { return (len + L - 1) / L; }
 
+
 }  // namespace sgdn

@@ -157,22 +157,20 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
   // Block -> (row, batch, head-in-pair, slice).  The 16 workgroups of one
   // head pair (2 heads x 8 slices) share K^T tiles and each head's 8 share W,
   // so they are placed on one XCD (workgroups are dealt to the 8 XCDs
-  // round-robin); rows are dispatched in order, so the longest (High-tier)
-  // chains start first.
-  const int id = blockIdx.x, nblk = gridDim.x;
-  int pg, local;
-  if ((nblk & 127) == 0) {
-    pg = (id >> 7) * 8 + (id & 7);
-    local = (id >> 3) & 15;
-  } else {
-    pg = id >> 4;
-    local = id & 15;
-  }
+  // round-robin): a window of 128 workgroups holds 8 pair groups, group k on
+  // XCD (k + xcd_shift) mod 8.  A launch covers rows row_lo .. row_lo +
+  // nrows - 1 of every sequence; its grid is padded to whole windows and the
+  // padding leaves at once.  Rows are dispatched in order, so the longest
+  // (High-tier) chains start first.
+  const int id = blockIdx.x, nr = p.nrows;
+  const int pg = (id >> 7) * 8 + (((id & 7) - p.xcd_shift) & 7);
+  if (pg >= B * nr) return;
+  const int local = (id >> 3) & 15;
   // Packed sequences (dense): sequence-major, so the pair groups dispatched
   // together belong to one sequence and their chains are equally long (they
   // start and finish together and keep sharing the pair's lines in L2).
   const bool seq_major = !SPARSE && p.cu != nullptr;
-  const int row = seq_major ? pg % NP : pg / B, b = seq_major ? pg / NP : pg % B;
+  const int row = p.row_lo + (seq_major ? pg % nr : pg / B), b = seq_major ? pg / nr : pg % B;
   const int hh = local >> 3, slice = local & 7;
   const int pr = SPARSE ? p.row_pair[b * NP + row] : row;
   const int h = 2 * pr + hh;
@@ -452,7 +450,7 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
 
 template <typename E, bool SPARSE>
 hipError_t launch_one(const HScanArgs& a, hipStream_t s) {
-  const int nblk = a.B * (a.Nv / 2) * 16;
+  const int nblk = 128 * ((a.B * a.nrows + 7) / 8);
   hipLaunchKernelGGL((hscan_kernel<E, SPARSE>), dim3(nblk), dim3(64 * NWAVE), 0, s, a);
   return hipGetLastError();
 }

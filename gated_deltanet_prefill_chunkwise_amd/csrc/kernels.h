@@ -71,6 +71,9 @@ struct HScanArgs {
   int sparse;
   const int32_t* cu; int T;  // packed sequences: a dense chain stops at its valid chunks
   int w_by_chunk;           // sparse: W [B][Nv][C][8192] per chunk (deferred-W ablation)
+  // rows row_lo .. row_lo + nrows - 1 of every sequence (CSR rows, sparse;
+  // head pairs, dense); pair groups start at XCD xcd_shift
+  int row_lo, nrows, xcd_shift;
   // sparse metadata (per batch)
   const int32_t* row_pair;  // [B][NP]
   const int32_t* row_ptr;   // [B][NP+1]
@@ -93,6 +96,8 @@ struct OChunkArgs {
   // compact-states ablation: dense group-entry states [B][Nv][G][dv][dk]
   // (already decayed), read instead of the compact snapshots; or null
   const void* entry;
+  const int32_t* row_pair;    // sparse: [B][NP] head pair of each CSR row
+  int row_lo, nrows;          // rows covered by this launch
 };
 
 // Compact-states ablation: every group's entry state S_2r written out densely

@@ -51,10 +51,12 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   __shared__ float sG[2 * L];
 
   const int T = p.T, Nq = p.Nq, Nv = p.Nv, C = p.C, G = p.G;
-  // Block -> (group r, head pair pr, batch b; head hh of the pair).  The two
-  // heads of a pair read the same Q and K rows: they are dispatched one after
-  // the other onto the same XCD (workgroups are dealt to the 8 XCDs
-  // round-robin), so the second read hits that XCD's L2.
+  // Block -> (group r, row, batch b; head hh of the pair).  The two heads of
+  // a pair read the same Q and K rows: they are dispatched one after the
+  // other onto the same XCD (workgroups are dealt to the 8 XCDs
+  // round-robin), so the second read hits that XCD's L2.  A launch covers
+  // rows row_lo .. row_lo + nrows - 1: head pairs (dense) or CSR rows, whose
+  // pair is row_pair (sparse).
   const int id = blockIdx.x, NP = Nv / 2;
   int unit, hh;
   if ((gridDim.x & 15) == 0) {
@@ -65,7 +67,9 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
     hh = id & 1;
     unit = id >> 1;
   }
-  const int pr = unit % NP, r = (unit / NP) % G, b = unit / (NP * G);
+  const int nr = p.nrows;
+  const int row = p.row_lo + unit % nr, r = (unit / nr) % G, b = unit / (nr * G);
+  const int pr = p.sparse ? ((const cint32*)p.row_pair)[__builtin_amdgcn_readfirstlane(b * NP + row)] : row;
   const int h = 2 * pr + hh;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int n16 = lane & 15, g4 = lane >> 4;
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
 }  // namespace
 
 hipError_t launch_ochunk(const OChunkArgs& a, int bf16, hipStream_t s) {
-  dim3 grid(a.G * a.Nv * a.B);
+  dim3 grid(a.G * 2 * a.nrows * a.B);
   if (bf16) {
     if (a.o_bf16)
       hipLaunchKernelGGL((ochunk_kernel<sgdn::bf16, sgdn::bf16>), grid, dim3(512), 0, s, a);
