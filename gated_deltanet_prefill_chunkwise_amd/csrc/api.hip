@@ -428,27 +428,30 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   }
 
   // deferred W of the kept events (the deferred-W ablation has W of every
-  // chunk from the intra stage instead)
+  // chunk from the intra stage instead) and event records
   const bool wall = (pl.ablate & SGDN_ABLATE_DEFERRED_W) != 0;
-  if (!wall) {
-    DeferredWArgs da{};
-    da.KT = at<void>(ws, pl, B_KT); da.Cb = at<void>(ws, pl, B_CB); da.Wpk = at<void>(ws, pl, B_WPK);
-    da.row_pair = sa.row_pair; da.row_ptr = sa.row_ptr; da.col = sa.col;
-    da.B = pl.B; da.Nv = pl.Nv; da.Nq = pl.Nq; da.C = pl.C; da.Emax = Emax; da.solve = pl.solve;
-    SGDN_TRY(launch_deferred_w(da, pl.bf16, s));
-  }
-
-  if (s0 != nullptr) {
-    S0PrepArgs s0a{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv};
-    SGDN_TRY(launch_s0prep(s0a, pl.bf16, s));
-  }
+  DeferredWArgs da{};
+  da.KT = at<void>(ws, pl, B_KT); da.Cb = at<void>(ws, pl, B_CB); da.Wpk = at<void>(ws, pl, B_WPK);
+  da.row_pair = sa.row_pair; da.row_ptr = sa.row_ptr; da.col = sa.col;
+  da.B = pl.B; da.Nv = pl.Nv; da.Nq = pl.Nq; da.C = pl.C; da.Emax = Emax; da.solve = pl.solve;
   EvRecArgs ea{};
   ea.gamma = at<float>(ws, pl, B_GAMMA); ea.P = at<double>(ws, pl, B_P);
   ea.row_pair = sa.row_pair; ea.row_ptr = sa.row_ptr; ea.col = sa.col; ea.event_slot = sa.event_slot;
   ea.rec = at<int32_t>(ws, pl, B_REC);
   ea.B = pl.B; ea.Nv = pl.Nv; ea.C = pl.C; ea.Emax = Emax; ea.sparse = 1;
-  SGDN_TRY(launch_evrec(ea, s));
-  mark(dbg, SGDN_EV_DEFERRED, s);
+  auto events = [&](int lo, int hi, hipStream_t q) -> hipError_t {
+    hipError_t e = hipSuccess;
+    if (!wall) {
+      da.row_lo = lo; da.row_hi = hi;
+      if ((e = launch_deferred_w(da, pl.bf16, q)) != hipSuccess) return e;
+    }
+    ea.row_lo = lo; ea.row_hi = hi;
+    return launch_evrec(ea, q);
+  };
+  if (s0 != nullptr) {
+    S0PrepArgs s0a{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv};
+    SGDN_TRY(launch_s0prep(s0a, pl.bf16, s));
+  }
   HScanArgs ha{};
   ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, wall ? B_W : B_WPK); ha.U = at<void>(ws, pl, B_U);
   ha.w_by_chunk = wall;
@@ -467,12 +470,18 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   oa.cu = pl.cu; oa.row_pair = sa.row_pair;
   oa.sparse = 1; oa.pred = sa.pred; oa.group_slot = sa.group_slot; oa.snap_cap = pl.snap_cap;
 
+  SGDN_TRY(events(0, NP, s));
+  mark(dbg, SGDN_EV_DEFERRED, s);
+
   if (pl.B == 1 && !(pl.ablate & SGDN_ABLATE_COMPACT_STATES)) {
     // CSR rows 0-3 hold every High-tier pair (at most 4), whose chains are
-    // the longest and bound the H scan.  The H scan and O of rows 4-15 run on
-    // a second stream beside them, so O of the shorter chains overlaps the
-    // long ones; rows 4-15 start at XCD 4, rows 0-3 at XCD 0, which keeps
-    // 32 workgroups on every XCD.
+    // the longest and bound the H scan.  The H scan and O of rows 4-15 run
+    // on a second stream beside those of rows 0-3, so O of the shorter
+    // chains overlaps the long ones; rows 4-15 start at XCD 4, rows 0-3 at
+    // XCD 0, which keeps 32 H-scan workgroups on every XCD.  (Splitting
+    // deferred W and the event records the same way, or moving the gate
+    // energy beside the intra kernel, measured no faster: the GPU is busy
+    // in those phases.)
     Side* sd = nullptr;
     if ((st = side_stream(&sd)) != SGDN_OK) return st;
     std::lock_guard<std::mutex> lk(sd->mu);

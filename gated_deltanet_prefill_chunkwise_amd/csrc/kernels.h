@@ -118,6 +118,7 @@ struct EvRecArgs {
   const int32_t* row_pair; const int32_t* row_ptr; const int32_t* col; const int32_t* event_slot;
   int32_t* rec;
   int B, Nv, C, Emax, sparse;
+  int row_lo, row_hi;   // sparse: CSR rows row_lo .. row_hi - 1
 };
 
 struct S0PrepArgs { const float* s0; void* s0T; int B, Nv; };
@@ -152,6 +153,7 @@ struct DeferredWArgs {
   const void* KT; const void* Cb; void* Wpk;
   const int32_t* row_pair; const int32_t* row_ptr; const int32_t* col;
   int B, Nv, Nq, C, Emax, solve;
+  int row_lo, row_hi;   // the events of CSR rows row_lo .. row_hi - 1
 };
 
 // Single-token decode step (decode.hip).  q, k [B][Nq][128], v [B][Nv][128],

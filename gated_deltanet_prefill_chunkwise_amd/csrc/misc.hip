@@ -20,8 +20,16 @@ __global__ __launch_bounds__(64) void prefix_kernel(PrefixArgs p) {
   const int per = (C + 63) / 64;
   const int lo = lane * per, hi = min(C, lo + per);
   auto gam = [&](int c) { return c < Cv ? (double)gm[c] : 0.0; };
+  // the run's loads are issued eight at a time; sums keep chunk order
   double run = 0.0;
-  for (int c = lo; c < hi; ++c) run += gam(c);
+  for (int c0 = lo; c0 < hi; c0 += 8) {
+    double x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = c0 + u < hi ? gam(c0 + u) : 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c0 + u < hi) run += x[u];
+  }
   double incl = run;
   for (int off = 1; off < 64; off <<= 1) {
     const double y = __shfl_up(incl, off, 64);
@@ -29,9 +37,16 @@ __global__ __launch_bounds__(64) void prefix_kernel(PrefixArgs p) {
   }
   double acc = incl - run;
   if (lane == 0) P[0] = 0.0;
-  for (int c = lo; c < hi; ++c) {
-    acc += gam(c);
-    P[c + 1] = acc;
+  for (int c0 = lo; c0 < hi; c0 += 8) {
+    double x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = c0 + u < hi ? gam(c0 + u) : 0.0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c0 + u < hi) {
+        acc += x[u];
+        P[c0 + u + 1] = acc;
+      }
   }
 }
 
@@ -152,15 +167,28 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs p) {
   const SeqSpan sp = seq_span(p.cu, b, p.T);
   const int ns = 4 * chunks_of(sp.len);
   float acc = 0.f;
-  for (int j = tid; j < ns; j += 256) {
-    const int c = j >> 2, a = j & 3;
-    const int pos = c * L + 8 + 16 * a;
-    const int v = (73 * j) & (DV - 1);
-    if (pos < sp.len) {
-      const float x = to_f(z[((size_t)(sp.tok0 + pos) * p.Nv + h) * DV + v]);
-      const float wv = p.w ? p.w[v] : 1.f;
-      const float s = wv * (x / (1.f + __expf(-x)));
-      acc += s * s;
+  // eight samples' loads are issued together; the sum keeps sample order
+  for (int j0 = tid; j0 < ns; j0 += 256 * 8) {
+    float xv[8], wvv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + 256 * u;
+      const int c = j >> 2, a = j & 3;
+      const int pos = c * L + 8 + 16 * a;
+      const int v = (73 * j) & (DV - 1);
+      const bool ok = j < ns && pos < sp.len;
+      xv[u] = ok ? to_f(z[((size_t)(sp.tok0 + pos) * p.Nv + h) * DV + v]) : 0.f;
+      wvv[u] = (ok && p.w) ? p.w[v] : 1.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + 256 * u;
+      const int pos = (j >> 2) * L + 8 + 16 * (j & 3);
+      if (j < ns && pos < sp.len) {
+        const float x = xv[u];
+        const float s = wvv[u] * (x / (1.f + __expf(-x)));
+        acc += s * s;
+      }
     }
   }
   __shared__ float red[4];
@@ -177,12 +205,12 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs p) {
 // The grid is sized to the capacity E_max; blocks past the on-device E exit.
 template <typename E>
 __global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
-  const int i = blockIdx.x, b = blockIdx.y;
+  const int b = blockIdx.y;
   const int NP = p.Nv / 2;
-  const int E_ = p.row_ptr[b * (NP + 1) + NP];
-  if (i >= E_) return;
-  int row = 0;
-  while (row + 1 < NP && p.row_ptr[b * (NP + 1) + row + 1] <= i) ++row;
+  const int i = p.row_ptr[b * (NP + 1) + p.row_lo] + (int)blockIdx.x;
+  if (i >= p.row_ptr[b * (NP + 1) + p.row_hi]) return;
+  int row = p.row_lo;
+  while (row + 1 < p.row_hi && p.row_ptr[b * (NP + 1) + row + 1] <= i) ++row;
   const int pr = p.row_pair[b * NP + row];
   const int c = p.col[(size_t)b * p.Emax + i];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -233,12 +261,12 @@ __global__ __launch_bounds__(256) void evrec_dense_kernel(EvRecArgs p) {
   reinterpret_cast<int4*>(p.rec)[i] = r;
 }
 
-__global__ __launch_bounds__(256) void evrec_sparse_kernel(EvRecArgs p) {
-  const int row = blockIdx.x, b = blockIdx.y, NP = p.Nv / 2;
+__global__ __launch_bounds__(1024) void evrec_sparse_kernel(EvRecArgs p) {
+  const int row = p.row_lo + (int)blockIdx.x, b = blockIdx.y, NP = p.Nv / 2;
   const int beg = p.row_ptr[b * (NP + 1) + row], end = p.row_ptr[b * (NP + 1) + row + 1];
   const int pr = p.row_pair[b * NP + row];
   const int32_t* col = p.col + (size_t)b * p.Emax;
-  for (int i = beg + (int)threadIdx.x; i < end; i += 256) {
+  for (int i = beg + (int)threadIdx.x; i < end; i += 1024) {
     const int c = col[i];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -295,7 +323,7 @@ hipError_t launch_chunk_table(const ChunkTableArgs& a, hipStream_t s) {
 
 hipError_t launch_evrec(const EvRecArgs& a, hipStream_t s) {
   if (a.sparse) {
-    hipLaunchKernelGGL(evrec_sparse_kernel, dim3(a.Nv / 2, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(evrec_sparse_kernel, dim3(a.row_hi - a.row_lo, a.B), dim3(1024), 0, s, a);
   } else {
     const size_t n = (size_t)a.B * a.Nv * a.C;
     hipLaunchKernelGGL(evrec_dense_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);

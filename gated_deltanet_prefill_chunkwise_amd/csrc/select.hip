@@ -122,9 +122,18 @@ __global__ __launch_bounds__(1024) void select_rank_kernel(SelectArgs p) {
   if (!KEY && w < 2) {
     const float* s = w ? s1 : s0;
     double acc = 0.0;
-    for (int c = lane; c < C; c += 64) {
-      const double x = (double)s[c];
-      acc = acc + x * x;
+    // loads of eight chunks are issued together; the sum keeps the lane's
+    // chunk order
+    for (int c0 = lane; c0 < C; c0 += 64 * 8) {
+      float xs[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) xs[u] = c0 + 64 * u < C ? s[c0 + 64 * u] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + 64 * u < C) {
+          const double x = (double)xs[u];
+          acc = acc + x * x;
+        }
     }
     const double tot = wave_sum(acc);
     if (lane == 0) snorm[w] = sqrt(tot);
@@ -197,11 +206,23 @@ __global__ __launch_bounds__(1024) void select_tier_kernel(SelectArgs p) {
     if (lane == 0) sL[h] = lifetime(tot / nwin, C);
     const int pp = h >> 1;
     double alm = 0.0, amh = 0.0;
-    for (int c = lane; c < C; c += 64) {
-      const int r = rk[pp * CS + c];
-      const double xs = (double)sc[h * CS + c];
-      alm = alm + ((r >= kL - 2 && r < kM - 2) ? xs : 0.0);
-      amh = amh + ((r >= kM - 2 && r < kH - 2) ? xs : 0.0);
+    for (int c0 = lane; c0 < C; c0 += 64 * 8) {
+      int rr[8];
+      float xx[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + 64 * u;
+        rr[u] = c < C ? rk[pp * CS + c] : -1;
+        xx[u] = c < C ? sc[h * CS + c] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (c0 + 64 * u < C) {
+          const int r = rr[u];
+          const double xs = (double)xx[u];
+          alm = alm + ((r >= kL - 2 && r < kM - 2) ? xs : 0.0);
+          amh = amh + ((r >= kM - 2 && r < kH - 2) ? xs : 0.0);
+        }
     }
     const double tl = wave_sum(alm), th = wave_sum(amh);
     if (lane == 0) { slm[h] = tl; smh[h] = th; }
