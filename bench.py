@@ -192,10 +192,15 @@ def ablation_leg(args, layers, hip, prob, dev):
     import torch
     from gated_deltanet_prefill_chunkwise_amd import ops
     out = {}
+    # CSR-off also forms W of every chunk, so it is set against the packed-W
+    # run; its scope is the H scan and O stages (with one sequence the O
+    # stage holds the wait for the rows 4-15 scan)
     scope = {"deferred_w": ("intra", "deferred_w", "hscan", "o"),
-             "compact_states": ("hscan",), "deferred_w+compact_states": ("intra", "deferred_w", "hscan", "o")}
+             "compact_states": ("hscan",), "deferred_w+compact_states": ("intra", "deferred_w", "hscan", "o"),
+             "csr": ("hscan", "o")}
+    base_of = {"csr": "deferred_w"}
     runs = {"default": (), "deferred_w": ("deferred_w",), "compact_states": ("compact_states",),
-            "deferred_w+compact_states": ("deferred_w", "compact_states")}
+            "deferred_w+compact_states": ("deferred_w", "compact_states"), "csr": ("csr",)}
     for name, ab in runs.items():
         ws = torch.empty(ops.workspace_bytes(prob, True, ops.sparse_params(ablate=ab)),
                          dtype=torch.uint8, device=dev)
@@ -210,10 +215,11 @@ def ablation_leg(args, layers, hip, prob, dev):
         out[name] = {"ms_per_step": round(ms, 4), "stage_ms_per_launch": stage}
         print(f"[bench] ablation {name}: {ms:.3f} ms per {args.layers}-layer step; stages "
               + ", ".join(f"{k} {v:.3f}" for k, v in stage.items()), file=sys.stderr, flush=True)
-    base = out["default"]["stage_ms_per_launch"]
     for name, sc in scope.items():
+        base = out[base_of.get(name, "default")]["stage_ms_per_launch"]
         st = out[name]["stage_ms_per_launch"]
         out[name]["scope"] = "+".join(sc)
+        out[name]["reference"] = base_of.get(name, "default")
         out[name]["speedup_of_mechanism"] = round(sum(st[k] for k in sc) / sum(base[k] for k in sc), 3)
     return out
 

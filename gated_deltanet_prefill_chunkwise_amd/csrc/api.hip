@@ -29,7 +29,8 @@ struct Plan {
 
 enum Buf { B_G, B_GAMMA, B_P, B_U, B_W, B_CB, B_KT, B_SNAP, B_S0T, B_SCORE, B_ETA, B_RANK,
            B_TINFO, B_MASK, B_TIER, B_ROWPAIR, B_ROWPTR, B_COL, B_PRED, B_GSLOT, B_ESLOT,
-           B_WPK, B_STATS, B_FAC, B_REC, B_CHUNKS, B_SPART, B_RANK2, B_ENTRY, B_COUNT };
+           B_WPK, B_STATS, B_FAC, B_REC, B_CHUNKS, B_SPART, B_RANK2, B_ENTRY, B_COLALL,
+           B_RPALL, B_COUNT };
 
 static_assert(B_COUNT <= (int)(sizeof(Plan::off) / sizeof(size_t)), "workspace table too small");
 
@@ -79,8 +80,10 @@ int check_params(const sgdn_problem* pr, const sgdn_sparse_params* sp) {
   if ((sp->fixed_tiers != 0 && sp->fixed_tiers != 1) ||
       (sp->unit_visibility != 0 && sp->unit_visibility != 1))
     return SGDN_EINVAL;
-  if (sp->ablate & ~(SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_COMPACT_STATES)) return SGDN_EINVAL;
-  if ((sp->ablate & SGDN_ABLATE_DEFERRED_W) && pr->cu_seqlens != nullptr) return SGDN_EUNSUPPORTED;
+  constexpr int ALL = SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_COMPACT_STATES | SGDN_ABLATE_CSR;
+  if (sp->ablate & ~ALL) return SGDN_EINVAL;
+  if ((sp->ablate & (SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_CSR)) && pr->cu_seqlens != nullptr)
+    return SGDN_EUNSUPPORTED;
   if (pr->n_v != 2 * NP_SPARSE) return SGDN_EUNSUPPORTED;
   const int C = (pr->seqlen + 63) / 64;
   if (C > 8192) return SGDN_EUNSUPPORTED;
@@ -115,8 +118,13 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
     sz[B_W] = B * Nv * C * L * DK * I;
     sz[B_SNAP] = B * Nv * (size_t)p.snap_cap * DV * DK * I;
   } else {
-    if (p.ablate & SGDN_ABLATE_DEFERRED_W) sz[B_W] = B * Nv * C * L * DK * I;   // W of every chunk
+    const bool wall = (p.ablate & (SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_CSR)) != 0;
+    if (wall) sz[B_W] = B * Nv * C * L * DK * I;   // W of every chunk
     else sz[B_CB] = B * Nv * C * L * L * I;
+    if (p.ablate & SGDN_ABLATE_CSR) {                 // all-chunk event lists
+      sz[B_COLALL] = B * NP * C * 4;
+      sz[B_RPALL] = B * (NP + 1) * 4;
+    }
     if (p.ablate & SGDN_ABLATE_COMPACT_STATES) sz[B_ENTRY] = B * Nv * G * DV * DK * I;
     sz[B_SNAP] = B * (size_t)p.snap_cap * 2 * DV * DK * I;
     sz[B_SCORE] = B * Nv * C * 4;
@@ -133,7 +141,7 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
     sz[B_PRED] = B * NP * G * 4;
     sz[B_GSLOT] = B * NP * G * 4;
     sz[B_ESLOT] = B * (size_t)p.Emax * 4;
-    if (!(p.ablate & SGDN_ABLATE_DEFERRED_W)) sz[B_WPK] = B * (size_t)p.Emax * 2 * L * DK * I;
+    if (!wall) sz[B_WPK] = B * (size_t)p.Emax * 2 * L * DK * I;
     sz[B_STATS] = B * 9 * 4;
   }
   size_t o = 0;
@@ -173,7 +181,7 @@ IntraArgs intra_args(const Plan& pl, void* ws, const void* k, const void* v, con
   ia.gamma = at<float>(ws, pl, B_GAMMA);
   ia.fac = at<float>(ws, pl, B_FAC);
   ia.U = at<void>(ws, pl, B_U);
-  const bool wall = sparse && (pl.ablate & SGDN_ABLATE_DEFERRED_W);
+  const bool wall = sparse && (pl.ablate & (SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_CSR));
   ia.W = (sparse && !wall) ? nullptr : at<void>(ws, pl, B_W);
   ia.Cb = (sparse && !wall) ? at<void>(ws, pl, B_CB) : nullptr;
   ia.KT = at<void>(ws, pl, B_KT);
@@ -429,7 +437,8 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
 
   // deferred W of the kept events (the deferred-W ablation has W of every
   // chunk from the intra stage instead) and event records
-  const bool wall = (pl.ablate & SGDN_ABLATE_DEFERRED_W) != 0;
+  const bool wall = (pl.ablate & (SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_CSR)) != 0;
+  const bool csr_off = (pl.ablate & SGDN_ABLATE_CSR) != 0;
   DeferredWArgs da{};
   da.KT = at<void>(ws, pl, B_KT); da.Cb = at<void>(ws, pl, B_CB); da.Wpk = at<void>(ws, pl, B_WPK);
   da.row_pair = sa.row_pair; da.row_ptr = sa.row_ptr; da.col = sa.col;
@@ -439,7 +448,11 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   ea.row_pair = sa.row_pair; ea.row_ptr = sa.row_ptr; ea.col = sa.col; ea.event_slot = sa.event_slot;
   ea.rec = at<int32_t>(ws, pl, B_REC);
   ea.B = pl.B; ea.Nv = pl.Nv; ea.C = pl.C; ea.Emax = Emax; ea.sparse = 1;
+  EvAllArgs xa_all{ea.gamma, ea.P, sa.mask, sa.row_pair, sa.row_ptr, sa.event_slot, ea.rec,
+                    at<int32_t>(ws, pl, B_COLALL), at<int32_t>(ws, pl, B_RPALL),
+                    pl.B, pl.Nv, pl.C, Emax};
   auto events = [&](int lo, int hi, hipStream_t q) -> hipError_t {
+    if (csr_off) return launch_evrec_all(xa_all, q);   // every chunk an event
     hipError_t e = hipSuccess;
     if (!wall) {
       da.row_lo = lo; da.row_hi = hi;
@@ -461,6 +474,9 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   ha.cu = nullptr; ha.T = pl.T;
   ha.row_pair = sa.row_pair; ha.row_ptr = sa.row_ptr; ha.col = sa.col; ha.event_slot = sa.event_slot;
   ha.Emax = Emax; ha.snap_cap = pl.snap_cap;
+  if (csr_off) {
+    ha.row_ptr = xa_all.row_ptr_all; ha.col = xa_all.col_all; ha.Emax = NP * pl.C;
+  }
   OChunkArgs oa{};
   oa.q = q; oa.k = k; oa.U = at<void>(ws, pl, B_U); oa.snap = at<void>(ws, pl, B_SNAP);
   oa.s0T = s0 ? at<void>(ws, pl, B_S0T) : nullptr;

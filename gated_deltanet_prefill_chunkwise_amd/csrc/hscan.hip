@@ -204,10 +204,12 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
       const int sn = __builtin_amdgcn_readfirstlane(hd.y);
       const int si = (sn >= 0 && sn < snap_cap) ? sn : -1;
       I* Ug = Ubase + (bh * C + c) * DV * L + dv0 * L;
+      if (sn != NULL_EVENT) {   // a null event keeps U
 #pragma unroll
-      for (int r = 0; r < R::U_BYTES / 1024; ++r) {
-        const int P = 64 * r + lane;
-        stv(Ug + u_unit<I>(P), ldv(st + P * 16));
+        for (int r = 0; r < R::U_BYTES / 1024; ++r) {
+          const int P = 64 * r + lane;
+          stv(Ug + u_unit<I>(P), ldv(st + P * 16));
+        }
       }
       if (si >= 0) {
         I* sp = snap_at(si) + dv0 * DK;
@@ -350,6 +352,7 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
   for (int q = 0; q < 4; ++q) Sf[q] = pack44<I>(S[2 * q], S[2 * q + 1]);
 
   int s = 0;
+  int last_c = -1;   // chunk of the last event that updated the state
   for (int j = i0; j < i1; ++j) {
     lds_barrier();   // the slot of event j is filled; staging entry free
     const char* sl = ring + s * R::BYTES;
@@ -362,6 +365,11 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
     const int sn = __builtin_amdgcn_readfirstlane(rc.z);
     const int snapi = (sn >= 0 && sn < snap_cap) ? sn : -1;
     const int c = min(max(__builtin_amdgcn_readfirstlane(rc.w), 0), C - 1);
+    // a null event (the CSR-off control) computes the products but leaves the
+    // state and U as they are: X = 0, decay 1
+    const bool null_ev = sn == NULL_EVENT;
+    const float xsc = null_ev ? 0.f : 1.f;
+    if (!null_ev) last_c = c;
     const I* Ws = reinterpret_cast<const I*>(sl + R::W_OFF);
     const I* Ks = reinterpret_cast<const I*>(sl + R::K_OFF);
 
@@ -386,11 +394,11 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         up[jj] = to_f(u[jj]) - fin * a[jj];
-        x[jj] = up[jj] * fc[jj];
+        x[jj] = up[jj] * (fc[jj] * xsc);
       }
       if constexpr (R::STAGE)
         st4<I>(reinterpret_cast<I*>(st + u_off<I>(i, n16, g4)), up);
-      else
+      else if (!null_ev)
         st4<I>(Ubase + (bh * C + c) * DV * L + (dv0 + n16) * L + 16 * i + 4 * g4, up);
       return x;
     };
@@ -420,7 +428,7 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
             *reinterpret_cast<half_t<I>*>(st + R::ST_SN + (c8 * 16 + n16) * 16 + 8 * (g4 & 1)) = v;
           }
       }
-      if (lane == 0) *reinterpret_cast<int2*>(st + R::ST_HDR) = make_int2(c, snapi);
+      if (lane == 0) *reinterpret_cast<int2*>(st + R::ST_HDR) = make_int2(c, null_ev ? NULL_EVENT : snapi);
     } else if (snapi >= 0) {
       I* sp = snap_at(snapi) + (dv0 + n16) * DK + 4 * g4;
 #pragma unroll
@@ -437,7 +445,7 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
     // gap from the last event to the end of the sequence
     float fl = 1.f;
     if constexpr (SPARSE)
-      if (i1 > i0) fl = exp2f((float)(P[C] - P[colb[i1 - 1] + 1]));
+      if (i1 > i0) fl = exp2f((float)(P[C] - P[last_c + 1]));
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll

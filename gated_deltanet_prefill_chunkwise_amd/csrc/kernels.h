@@ -121,6 +121,20 @@ struct EvRecArgs {
   int row_lo, row_hi;   // sparse: CSR rows row_lo .. row_hi - 1
 };
 
+// Snapshot field of a null event in a record: the H scan forms its products
+// and drops them (the CSR-off control of the sparse path).
+constexpr int NULL_EVENT = -2;
+
+// CSR-off control: every chunk of a CSR row is an event of the H scan, the
+// chunks outside the mask null events.  Writes the all-chunk event lists
+// (row_ptr_all [B][NP+1], col_all [B][NP*C]) and records [B][NP*C][2].
+struct EvAllArgs {
+  const float* gamma; const double* P; const uint8_t* mask;
+  const int32_t* row_pair; const int32_t* row_ptr; const int32_t* event_slot;
+  int32_t* rec; int32_t* col_all; int32_t* row_ptr_all;
+  int B, Nv, C, Emax;
+};
+
 struct S0PrepArgs { const float* s0; void* s0T; int B, Nv; };
 
 struct GateArgs {
@@ -172,6 +186,7 @@ hipError_t launch_chunk_table(const ChunkTableArgs& a, hipStream_t s);
 hipError_t launch_hscan(const HScanArgs& a, int bf16, hipStream_t s);
 hipError_t launch_ochunk(const OChunkArgs& a, int bf16, hipStream_t s);
 hipError_t launch_evrec(const EvRecArgs& a, hipStream_t s);
+hipError_t launch_evrec_all(const EvAllArgs& a, hipStream_t s);
 hipError_t launch_s0prep(const S0PrepArgs& a, int bf16, hipStream_t s);
 hipError_t launch_gate(const GateArgs& a, int bf16, hipStream_t s);
 hipError_t launch_select_full(const SelectArgs& a, hipStream_t s);

@@ -283,6 +283,71 @@ __global__ __launch_bounds__(1024) void evrec_sparse_kernel(EvRecArgs p) {
   }
 }
 
+// CSR-off control (SparseGDN reading notes, Sec. 3.6, Table 6): the H scan
+// steps through every chunk of a row with the same mask and decay arithmetic.
+// A kept chunk's record is the CSR one (gap factor from the previous kept
+// chunk, or from the start of the sequence, whose decay the event-list scan
+// then carries instead of the initial state); a chunk outside the mask is a
+// null event.  One workgroup per (row, sequence); chunks in tiles of 1024
+// with block scans for the kept count and the last kept chunk.
+__global__ __launch_bounds__(1024) void evrec_all_kernel(EvAllArgs p) {
+  __shared__ int s_cnt[1024], s_last[1024];
+  const int row = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int NP = p.Nv / 2, C = p.C;
+  const int pr = p.row_pair[b * NP + row];
+  const int beg = p.row_ptr[b * (NP + 1) + row];
+  const uint8_t* m = p.mask + ((size_t)b * NP + pr) * C;
+  const size_t ebase = ((size_t)b * NP + row) * C;   // event index of chunk 0 of this row
+  if (tid == 0) {
+    p.row_ptr_all[b * (NP + 1) + row] = row * C;
+    if (row == NP - 1) p.row_ptr_all[b * (NP + 1) + NP] = NP * C;
+  }
+  int carry_cnt = 0, carry_last = -1;
+  for (int c0 = 0; c0 < C; c0 += 1024) {
+    const int c = c0 + tid;
+    const int kept = (c < C && m[c]) ? 1 : 0;
+    s_cnt[tid] = kept;
+    s_last[tid] = kept ? c : -1;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+      const int a = tid >= d ? s_cnt[tid - d] : 0;
+      const int l = tid >= d ? s_last[tid - d] : -1;
+      __syncthreads();
+      s_cnt[tid] += a;
+      s_last[tid] = max(s_last[tid], l);
+      __syncthreads();
+    }
+    const int cnt = carry_cnt + s_cnt[tid];                      // kept in [0, c]
+    const int prev = max(carry_last, tid > 0 ? s_last[tid - 1] : -1);   // last kept before c
+    if (c < C) {
+      const size_t j = ebase + c;
+      p.col_all[j] = c;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const size_t bh = (size_t)b * p.Nv + 2 * pr + hh;
+        int4 r;
+        if (kept) {
+          const double* P = p.P + bh * (C + 1);
+          const float fin = exp2f((float)(P[c] - P[prev + 1]));
+          r.x = __float_as_int(fin);
+          r.y = __float_as_int(exp2f(p.gamma[bh * C + c]) * fin);
+          r.z = p.event_slot[(size_t)b * p.Emax + beg + cnt - 1];
+        } else {
+          r.x = __float_as_int(1.f);
+          r.y = __float_as_int(1.f);
+          r.z = NULL_EVENT;
+        }
+        r.w = c;
+        reinterpret_cast<int4*>(p.rec)[j * 2 + hh] = r;
+      }
+    }
+    const int tile_cnt = s_cnt[1023], tile_last = s_last[1023];
+    __syncthreads();
+    carry_cnt += tile_cnt;
+    carry_last = max(carry_last, tile_last);
+  }
+}
+
 // U tiles [dv][t] (intermediate type) -> token-major fp32 [t][dv] copy for
 // the debug output.
 template <typename I>
@@ -328,6 +393,11 @@ hipError_t launch_evrec(const EvRecArgs& a, hipStream_t s) {
     const size_t n = (size_t)a.B * a.Nv * a.C;
     hipLaunchKernelGGL(evrec_dense_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_evrec_all(const EvAllArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(evrec_all_kernel, dim3(a.Nv / 2, a.B), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

@@ -119,8 +119,14 @@ typedef struct {
  *                               written out densely (decayed from the compact
  *                               snapshots) and O reads it, instead of O
  *                               reading the compact snapshots with the gap
- *                               factor (Eq. (21)). */
-enum { SGDN_ABLATE_DEFERRED_W = 1, SGDN_ABLATE_COMPACT_STATES = 2 };
+ *                               factor (Eq. (21)).
+ *   SGDN_ABLATE_CSR             the H scan steps through every chunk of each
+ *                               head pair, forming the products of the
+ *                               chunks outside the mask and dropping them,
+ *                               instead of walking the CSR event list
+ *                               (Eq. (16)); W of every chunk as with
+ *                               SGDN_ABLATE_DEFERRED_W.  Not with cu_seqlens. */
+enum { SGDN_ABLATE_DEFERRED_W = 1, SGDN_ABLATE_COMPACT_STATES = 2, SGDN_ABLATE_CSR = 4 };
 
 /* Per-sequence statistics written on the device. */
 typedef struct {

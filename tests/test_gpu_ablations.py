@@ -1,6 +1,7 @@
 """Kernel-pipeline ablations of the sparse path (Sec. 3.6, Table 6): the
-packed-W path (W of every chunk formed in the intra stage) and dense
-group-entry states (expanded from the compact snapshots, read by O).
+packed-W path (W of every chunk formed in the intra stage), dense
+group-entry states (expanded from the compact snapshots, read by O) and the
+CSR-off scan (every chunk an event, those outside the mask dropped).
 
 Each ablated run must select the same events as the default run (the
 selector statistics do not depend on the ablation), match the oracle given
@@ -16,7 +17,8 @@ from helpers import TOL, host, rel_max_err, to_device
 
 pytestmark = pytest.mark.gpu
 
-ABLATIONS = [("deferred_w",), ("compact_states",), ("deferred_w", "compact_states")]
+ABLATIONS = [("deferred_w",), ("compact_states",), ("deferred_w", "compact_states"), ("csr",),
+             ("csr", "compact_states")]
 
 
 def _run(d, C, B, ablate=(), s0=None, **kw):
@@ -52,7 +54,7 @@ def test_ablation_matches_default_and_oracle(ablate, dtype, solve):
     print(f"{ablate} {dtype}: err O {eo:.3e} S {es:.3e}; vs default O {do:.3e} S {ds:.3e}")
     assert eo <= TOL[dtype] and es <= TOL[dtype]
     assert do <= TOL[dtype] and ds <= TOL[dtype]
-    if "deferred_w" not in ablate:
+    if not {"deferred_w", "csr"} & set(ablate):
         # same W and the same H scan: the final state is bit-identical
         assert np.array_equal(S1, S0)
 
