@@ -196,7 +196,7 @@ def ablation_leg(args, layers, hip, prob, dev):
     # run; its scope is the H scan and O stages (with one sequence the O
     # stage holds the wait for the rows 4-15 scan)
     scope = {"deferred_w": ("intra", "deferred_w", "hscan", "o"),
-             "compact_states": ("hscan",), "deferred_w+compact_states": ("intra", "deferred_w", "hscan", "o"),
+             "compact_states": ("hscan", "o"), "deferred_w+compact_states": ("intra", "deferred_w", "hscan", "o"),
              "csr": ("hscan", "o")}
     base_of = {"csr": "deferred_w"}
     runs = {"default": (), "deferred_w": ("deferred_w",), "compact_states": ("compact_states",),

@@ -489,7 +489,20 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   SGDN_TRY(events(0, NP, s));
   mark(dbg, SGDN_EV_DEFERRED, s);
 
-  if (pl.B == 1 && !(pl.ablate & SGDN_ABLATE_COMPACT_STATES)) {
+  // compact-states ablation: dense group-entry states for O, per row range
+  const bool dense_entry = (pl.ablate & SGDN_ABLATE_COMPACT_STATES) != 0;
+  ExpandArgs xa{at<void>(ws, pl, B_SNAP), s0 ? at<void>(ws, pl, B_S0T) : nullptr,
+                at<double>(ws, pl, B_P), sa.pred, sa.group_slot,
+                dense_entry ? at<void>(ws, pl, B_ENTRY) : nullptr,
+                pl.B, pl.Nv, pl.C, pl.G, pl.snap_cap, pl.T, pl.cu, sa.row_pair, 0, NP};
+  oa.entry = xa.entry;
+  auto expand = [&](int lo, int n, hipStream_t q) -> hipError_t {
+    if (!dense_entry) return hipSuccess;
+    xa.row_lo = lo; xa.nrows = n;
+    return launch_expand(xa, pl.bf16, q);
+  };
+
+  if (pl.B == 1) {
     // CSR rows 0-3 hold every High-tier pair (at most 4), whose chains are
     // the longest and bound the H scan.  The H scan and O of rows 4-15 run
     // on a second stream beside those of rows 0-3, so O of the shorter
@@ -505,11 +518,13 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
     SGDN_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0));
     ha.row_lo = SPLIT_ROWS; ha.nrows = NP - SPLIT_ROWS; ha.xcd_shift = SPLIT_ROWS;
     SGDN_TRY(launch_hscan(ha, pl.bf16, sd->s));
+    SGDN_TRY(expand(SPLIT_ROWS, NP - SPLIT_ROWS, sd->s));
     oa.row_lo = SPLIT_ROWS; oa.nrows = NP - SPLIT_ROWS;
     SGDN_TRY(launch_ochunk(oa, pl.bf16, sd->s));
     SGDN_TRY(hipEventRecord(sd->join, sd->s));
     ha.row_lo = 0; ha.nrows = SPLIT_ROWS; ha.xcd_shift = 0;
     SGDN_TRY(launch_hscan(ha, pl.bf16, s));
+    SGDN_TRY(expand(0, SPLIT_ROWS, s));
     mark(dbg, SGDN_EV_HSCAN, s);
     oa.row_lo = 0; oa.nrows = SPLIT_ROWS;
     SGDN_TRY(launch_ochunk(oa, pl.bf16, s));
@@ -520,17 +535,8 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
 
   ha.row_lo = 0; ha.nrows = NP; ha.xcd_shift = 0;
   SGDN_TRY(launch_hscan(ha, pl.bf16, s));
-  void* entry = nullptr;
-  if (pl.ablate & SGDN_ABLATE_COMPACT_STATES) {
-    // compact-states ablation: dense group-entry states for O
-    entry = at<void>(ws, pl, B_ENTRY);
-    ExpandArgs xa{at<void>(ws, pl, B_SNAP), s0 ? at<void>(ws, pl, B_S0T) : nullptr,
-                  at<double>(ws, pl, B_P), sa.pred, sa.group_slot, entry,
-                  pl.B, pl.Nv, pl.C, pl.G, pl.snap_cap, pl.T, pl.cu};
-    SGDN_TRY(launch_expand(xa, pl.bf16, s));
-  }
+  SGDN_TRY(expand(0, NP, s));
   mark(dbg, SGDN_EV_HSCAN, s);
-  oa.entry = entry;
   oa.row_lo = 0; oa.nrows = NP;
   SGDN_TRY(launch_ochunk(oa, pl.bf16, s));
   mark(dbg, SGDN_EV_O, s);

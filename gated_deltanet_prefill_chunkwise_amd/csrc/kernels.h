@@ -108,6 +108,8 @@ struct ExpandArgs {
   void* entry;
   int B, Nv, C, G, snap_cap, T;
   const int32_t* cu;
+  const int32_t* row_pair;   // [B][NP] head pair of each CSR row
+  int row_lo, nrows;         // CSR rows covered by this launch
 };
 
 // Per-event records of the H scan: the gap factor F_in that carries the state

@@ -110,12 +110,14 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs p) {
 // Compact-states ablation (SparseGDN reading notes, Sec. 3.6, Table 6): the
 // entry state of every output group r, S_2r = 2^(P_2r - P_e+1) S_e+1 from the
 // snapshot of its predecessor event e (Sec. 2.6, Eq. (21)), or 2^P_2r s0, or
-// zero, written densely.  One workgroup per (group, head); groups past a
-// packed sequence's end are skipped (nothing reads them).
+// zero, written densely.  One workgroup per (group, head of a pair in CSR
+// rows row_lo .. row_lo + nrows - 1); groups past a packed sequence's end
+// are skipped (nothing reads them).
 template <typename I>
 __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs p) {
-  const int r = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / p.Nv, h = bh - b * p.Nv, pr = h >> 1, hh = h & 1;
+  const int r = blockIdx.x, y = blockIdx.y, NP = p.Nv / 2;
+  const int hh = y & 1, row = p.row_lo + (y >> 1) % p.nrows, b = (y >> 1) / p.nrows;
+  const int pr = p.row_pair[b * NP + row], h = 2 * pr + hh, bh = b * p.Nv + h;
   if (p.cu != nullptr && 2 * r * L >= seq_span(p.cu, b, p.T).len) return;
   const size_t pg = ((size_t)b * (p.Nv / 2) + pr) * p.G + r;
   const int slot = p.group_slot[pg];
@@ -368,7 +370,7 @@ hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_expand(const ExpandArgs& a, int bf16, hipStream_t s) {
-  const dim3 grid(a.G, a.B * a.Nv);
+  const dim3 grid(a.G, a.B * a.nrows * 2);
   if (bf16)
     hipLaunchKernelGGL(expand_kernel<fp16>, grid, dim3(256), 0, s, a);
   else

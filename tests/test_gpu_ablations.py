@@ -34,10 +34,12 @@ def _run(d, C, B, ablate=(), s0=None, **kw):
 
 
 @pytest.mark.parametrize("ablate", ABLATIONS)
-@pytest.mark.parametrize("dtype,solve", [("bf16", "blockadj"), ("f32", "exact")])
-def test_ablation_matches_default_and_oracle(ablate, dtype, solve):
+@pytest.mark.parametrize("dtype,solve,B", [("bf16", "blockadj", 1), ("f32", "exact", 2)])
+def test_ablation_matches_default_and_oracle(ablate, dtype, solve, B):
+    """B = 1 takes the two-stream schedule (CSR rows 0-3 and 4-15), B = 2 one
+    launch per stage."""
     import torch
-    B, T = 2, 64 * 11 + 19
+    T = 64 * 11 + 19
     inp = synth.numpy_inputs(3100 + len(ablate), B, T, 16, 32, dtype=dtype, with_z=True,
                              decay_scale=1 / 16)
     C = -(-T // 64)
