@@ -20,6 +20,12 @@
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *   ordered after prior work on it.  Calls are stateless and reentrant; two
  *   calls must not share a workspace concurrently.
+ * - sgdn_prefill_sparse with batch 1 runs part of its work on a second
+ *   stream of the library's (one per device, created by the first such call
+ *   and kept until the process ends), forked from and joined back to
+ *   `stream` with events: later work on `stream` still sees every output.
+ *   To capture such a call in a HIP graph, make one call before capturing,
+ *   so that the stream exists.
  * - Errors: a negative sgdn_status is returned BEFORE anything is enqueued
  *   when an argument is invalid; SGDN_EHIP reports a failed launch.
  *   Data-dependent conditions are reported through sgdn_stats.
