@@ -14,8 +14,9 @@ packed variable-length leg reads the same tokens as 16 sequences of mixed
 lengths (cu_seqlens) and times both paths again.  A selector-ablation leg
 times the sparse step with each switch of Sec. 3.5 (fixed 3/4/9 tiers,
 G_h = 1, random keys at matched budget, Tail-8/32/64 windows), and a
-kernel-pipeline ablation leg times it with deferred W and compact states
-undone (Table 6), reporting each mechanism's speedup over its stages.
+kernel-pipeline ablation leg times it with deferred W, compact states, the
+CSR event walk and the two-chunk O mapping undone (Table 6), reporting each
+mechanism's speedup over its stages.
 
 Prints one JSON line.  value = tokens/s of the 24-layer stack (B*T per step);
 roofline = the dominant kernel's algorithmic bytes per layer over its mean
@@ -186,21 +187,29 @@ def time_stack(args, hip, L, call):
 
 
 def ablation_leg(args, layers, hip, prob, dev):
-    """The sparse step with each kernel-pipeline ablation of Table 6 (the
-    mechanism undone), beside the default; speedup = ablated / default time
-    over the stages of the row's scope."""
+    """The sparse step with kernel-pipeline mechanisms undone (Table 6),
+    beside the default.  Each row sets one run against its matched
+    reference run: speedup = run / reference time over the row's stages."""
     import torch
     from gated_deltanet_prefill_chunkwise_amd import ops
-    out = {}
-    # CSR-off also forms W of every chunk, so it is set against the packed-W
-    # run; its scope is the H scan and O stages (with one sequence the O
-    # stage holds the wait for the rows 4-15 scan)
-    scope = {"deferred_w": ("intra", "deferred_w", "hscan", "o"),
-             "compact_states": ("hscan", "o"), "deferred_w+compact_states": ("intra", "deferred_w", "hscan", "o"),
-             "csr": ("hscan", "o")}
-    base_of = {"csr": "deferred_w"}
-    runs = {"default": (), "deferred_w": ("deferred_w",), "compact_states": ("compact_states",),
-            "deferred_w+compact_states": ("deferred_w", "compact_states"), "csr": ("csr",)}
+    runs = {"default": (), "deferred_w": ("deferred_w",), "csr": ("csr",),
+            "compact_states": ("compact_states",), "tier_schedule": ("tier_schedule",),
+            "compact_states+mapped_o": ("compact_states", "mapped_o"), "mapped_o": ("mapped_o",)}
+    # (mechanism, run with it undone, reference run, stages).  CSR-off also
+    # forms W of every chunk, so it is set against the packed-W run; mapped-O
+    # off is set against the run with the same dense group-entry states, so
+    # that only O's reads differ; compact+mapped undoes both.  With one
+    # sequence the O stage holds the wait for the second stream's H scan and
+    # O, so the H-side rows take the H scan and O stages together.
+    full = ("intra", "deferred_w", "hscan", "o")
+    rows = [("deferred_w", "deferred_w", "default", full),
+            ("csr_event_scan", "csr", "deferred_w", ("hscan", "o")),
+            ("compact_states", "compact_states", "default", ("hscan", "o")),
+            ("tier_schedule", "tier_schedule", "default", ("hscan", "o")),
+            ("mapped_o", "compact_states+mapped_o", "compact_states", ("hscan", "o")),
+            ("compact_states+mapped_o", "compact_states+mapped_o", "default", full),
+            ("mapped_o_over_compact_snapshots", "mapped_o", "default", ("hscan", "o"))]
+    out = {"runs": {}, "rows": []}
     for name, ab in runs.items():
         ws = torch.empty(ops.workspace_bytes(prob, True, ops.sparse_params(ablate=ab)),
                          dtype=torch.uint8, device=dev)
@@ -212,15 +221,15 @@ def ablation_leg(args, layers, hip, prob, dev):
                                workspace=ws, debug=dbg, ablate=ab)
         ms, stage = time_stack(args, hip, len(layers), call)
         del ws
-        out[name] = {"ms_per_step": round(ms, 4), "stage_ms_per_launch": stage}
+        out["runs"][name] = {"undone": list(ab), "ms_per_step": round(ms, 4),
+                             "stage_ms_per_launch": stage}
         print(f"[bench] ablation {name}: {ms:.3f} ms per {args.layers}-layer step; stages "
               + ", ".join(f"{k} {v:.3f}" for k, v in stage.items()), file=sys.stderr, flush=True)
-    for name, sc in scope.items():
-        base = out[base_of.get(name, "default")]["stage_ms_per_launch"]
-        st = out[name]["stage_ms_per_launch"]
-        out[name]["scope"] = "+".join(sc)
-        out[name]["reference"] = base_of.get(name, "default")
-        out[name]["speedup_of_mechanism"] = round(sum(st[k] for k in sc) / sum(base[k] for k in sc), 3)
+    for mech, run, ref, sc in rows:
+        st = out["runs"][run]["stage_ms_per_launch"]
+        base = out["runs"][ref]["stage_ms_per_launch"]
+        out["rows"].append({"mechanism": mech, "run": run, "reference": ref, "scope": "+".join(sc),
+                            "speedup": round(sum(st[k] for k in sc) / sum(base[k] for k in sc), 3)})
     return out
 
 

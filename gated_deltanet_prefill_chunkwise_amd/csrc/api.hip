@@ -80,7 +80,8 @@ int check_params(const sgdn_problem* pr, const sgdn_sparse_params* sp) {
   if ((sp->fixed_tiers != 0 && sp->fixed_tiers != 1) ||
       (sp->unit_visibility != 0 && sp->unit_visibility != 1))
     return SGDN_EINVAL;
-  constexpr int ALL = SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_COMPACT_STATES | SGDN_ABLATE_CSR;
+  constexpr int ALL = SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_COMPACT_STATES | SGDN_ABLATE_CSR |
+                      SGDN_ABLATE_MAPPED_O | SGDN_ABLATE_TIER_SCHEDULE;
   if (sp->ablate & ~ALL) return SGDN_EINVAL;
   if ((sp->ablate & (SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_CSR)) && pr->cu_seqlens != nullptr)
     return SGDN_EUNSUPPORTED;
@@ -416,6 +417,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   sa.B = pl.B; sa.C = pl.C; sa.keep_bp = budget_bp(params->keep_budget);
   sa.cu = pl.cu; sa.T = pl.T;
   sa.fixed_tiers = params->fixed_tiers; sa.unit_visibility = params->unit_visibility;
+  sa.pair_order = (pl.ablate & SGDN_ABLATE_TIER_SCHEDULE) != 0;
   sa.rank_key = params->rank_key;
   sa.rank_alt = params->rank_key ? at<int32_t>(ws, pl, B_RANK2) : nullptr;
   sa.rank = at<int32_t>(ws, pl, B_RANK); sa.tierinfo = at<int32_t>(ws, pl, B_TINFO);
@@ -496,13 +498,14 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
                 dense_entry ? at<void>(ws, pl, B_ENTRY) : nullptr,
                 pl.B, pl.Nv, pl.C, pl.G, pl.snap_cap, pl.T, pl.cu, sa.row_pair, 0, NP};
   oa.entry = xa.entry;
+  oa.per_chunk = (pl.ablate & SGDN_ABLATE_MAPPED_O) != 0;
   auto expand = [&](int lo, int n, hipStream_t q) -> hipError_t {
     if (!dense_entry) return hipSuccess;
     xa.row_lo = lo; xa.nrows = n;
     return launch_expand(xa, pl.bf16, q);
   };
 
-  if (pl.B == 1) {
+  if (pl.B == 1 && !(pl.ablate & SGDN_ABLATE_TIER_SCHEDULE)) {
     // CSR rows 0-3 hold every High-tier pair (at most 4), whose chains are
     // the longest and bound the H scan.  The H scan and O of rows 4-15 run
     // on a second stream beside those of rows 0-3, so O of the shorter

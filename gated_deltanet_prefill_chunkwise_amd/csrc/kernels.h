@@ -98,6 +98,7 @@ struct OChunkArgs {
   const void* entry;
   const int32_t* row_pair;    // sparse: [B][NP] head pair of each CSR row
   int row_lo, nrows;          // rows covered by this launch
+  int per_chunk;              // mapped-O ablation: one chunk per workgroup
 };
 
 // Compact-states ablation: every group's entry state S_2r written out densely
@@ -153,6 +154,7 @@ struct SelectArgs {
   // ablations: 3 High / 4 Medium / 9 Low pairs; G_h = 1; caller rank keys
   // [B][16][C] that choose the kept chunks (the tiers still follow Eq. (10))
   int fixed_tiers, unit_visibility;
+  int pair_order;       // tier-schedule ablation: CSR rows in head-pair order
   const float* rank_key;
   int32_t* rank_alt;    // [B][16][C]   workspace: ranks by rank_key
   int32_t* rank;        // [B][16][C]   workspace

@@ -36,17 +36,24 @@ constexpr int OSTR = DV + 4;      // O staging rows [t][dv] (fp32)
 // Two workgroups per CU (four waves per SIMD: at most 128 registers per lane)
 // so one group's loads
 // overlap the other's products.
-template <typename E, typename OT>
+//
+// ONE (the mapped-O ablation): one chunk per workgroup.  Block 2r + half
+// computes the 64 output rows of chunk 2r + half of group r: half 0 with
+// the sources of the first chunk, half 1 with all 128 sources (the cross
+// term A_{c+1,c} U'_c included); both restore the group entry state, so the
+// outputs are those of the two-chunk form.
+template <typename E, typename OT, bool ONE>
 __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
+  constexpr int NT = ONE ? 4 : 8;   // 16-token tiles computed
   using I = inter_t<E>;
   // Q and A^T during the products; afterwards the same bytes hold the
   // group's O rows, so that each store writes whole rows (a wave's own O^T
   // tile covers only 16 of a row's 128 values)
-  constexpr int QA_BYTES = (int)sizeof(I) * 2 * L * (QSTR + ASTR);
-  static_assert(2 * L * OSTR * 4 <= QA_BYTES, "O staging fits in the Q and A^T space");
+  constexpr int QA_MIN = (int)sizeof(I) * NT * 16 * (QSTR + ASTR), O_MIN = NT * 16 * OSTR * 4;
+  constexpr int QA_BYTES = QA_MIN > O_MIN ? QA_MIN : O_MIN;
   __shared__ __align__(32) char sQA[QA_BYTES];
   I* sQ = reinterpret_cast<I*>(sQA);
-  I* sA = sQ + 2 * L * QSTR;
+  I* sA = sQ + NT * 16 * QSTR;
   float* sO = reinterpret_cast<float*>(sQA);
   __shared__ float sG[2 * L];
 
@@ -67,18 +74,21 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
     hh = id & 1;
     unit = id >> 1;
   }
-  const int nr = p.nrows;
-  const int row = p.row_lo + unit % nr, r = (unit / nr) % G, b = unit / (nr * G);
+  const int nr = p.nrows, NU = ONE ? 2 * G : G;   // blocks per row of a sequence
+  const int row = p.row_lo + unit % nr, rb = (unit / nr) % NU, b = unit / (nr * NU);
+  const int r = ONE ? rb >> 1 : rb, half = ONE ? rb & 1 : 0;
   const int pr = p.sparse ? ((const cint32*)p.row_pair)[__builtin_amdgcn_readfirstlane(b * NP + row)] : row;
   const int h = 2 * pr + hh;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int n16 = lane & 15, g4 = lane >> 4;
-  const int c0 = 2 * r;
-  // a group past the end of its (shorter, packed) sequence has no outputs;
-  // the whole workgroup leaves before any load or barrier
+  const int c0 = 2 * r, j0 = 4 * half;   // j0: first token tile computed
+  // a group (chunk, with ONE) past the end of its (shorter, packed) sequence
+  // has no outputs; the whole workgroup leaves before any load or barrier
   const SeqSpan sp = seq_span(p.cu, b, T);
-  if (c0 * L >= sp.len) return;
+  if ((c0 + half) * L >= sp.len) return;
   const bool has1 = c0 + 1 < chunks_of(sp.len);
+  // the sources include the second chunk (not for the first half with ONE)
+  const bool need1 = has1 && (!ONE || half == 1);
   // Every group is computed as two chunks (straight-line code); a group
   // without a second chunk reads zeros for its Q, K, U' and decays there,
   // so those products vanish, and its rows are not stored.
@@ -113,12 +123,12 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   //      retire in order
   const E* Qin = static_cast<const E*>(p.q);
   const E* Kin = static_cast<const E*>(p.k);
-  frag_t<E> qst[4];
+  frag_t<E> qst[NT / 2];
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
+  for (int it = 0; it < NT / 2; ++it) {
     const int q = tid + 512 * it;
     const int rr = q >> 4, c8 = (q & 15) * 8;
-    const int t = c0 * L + rr;
+    const int t = c0 * L + 16 * j0 + rr;
     qst[it] = (t < sp.len) ? ld8(Qin + ((size_t)(sp.tok0 + t) * Nq + pr) * DK + c8) : zero_frag<E>();
   }
   frag_t<E> kf[4];
@@ -126,7 +136,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
     const int ts = c0 * L + 16 * w + n16;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      kf[ks] = (ts < sp.len) ? ld8(Kin + ((size_t)(sp.tok0 + ts) * Nq + pr) * DK + 32 * ks + 8 * g4)
+      kf[ks] = (ts < sp.len && (!ONE || w < 4 || need1)) ? ld8(Kin + ((size_t)(sp.tok0 + ts) * Nq + pr) * DK + 32 * ks + 8 * g4)
                         : zero_frag<E>();
   }
   const int dvr = 16 * w + n16;
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
 
   // ---- stage Q rows of the group and G
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
+  for (int it = 0; it < NT / 2; ++it) {
     const int q = tid + 512 * it;
     const int rr = q >> 4, c8 = (q & 15) * 8;
     *reinterpret_cast<frag_t<I>*>(&sQ[rr * QSTR + c8]) = cvt8<I, E>(qst[it]);
@@ -148,7 +158,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
     float gv = 0.f;
     if (cc == 0) {
       gv = p.g[(bh * C + c0) * L + lane];
-    } else if (has1) {
+    } else if (need1) {
       gv = p.gamma[bh * C + c0] + p.g[(bh * C + c0 + 1) * L + lane];
     }
     sG[tid] = gv;
@@ -156,7 +166,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   __syncthreads();
 
   // ---- phase 1: A^T blocks of source tile w (s in 16w..16w+15)
-  {
+  if (!ONE || half == 1 || w < 4) {
     frag_t<I> kfi[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) kfi[ks] = cvt8<I, E>(kf[ks]);
@@ -165,11 +175,11 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
     for (int j = 0; j < 4; ++j) gs[j] = sG[16 * w + 4 * g4 + j];
     // the block just above the diagonal (source tile w, token tile w - 1) is
     // read by the 32-wide k-steps of phase 2; the causal mask makes it zero
-    for (int jt = (w > 0 ? w - 1 : 0); jt < 8; ++jt) {
+    for (int jt = max(w - 1, j0); jt < j0 + NT; ++jt) {
       f32x4 at = zero4();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        at = mma(kfi[ks], ld8(&sQ[(16 * jt + n16) * QSTR + 32 * ks + 8 * g4]), at);
+        at = mma(kfi[ks], ld8(&sQ[(16 * (jt - j0) + n16) * QSTR + 32 * ks + 8 * g4]), at);
       const int t = 16 * jt + n16;
       const float gt = sG[t];
       f32x4 a4;
@@ -179,33 +189,33 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
         const float v = (s <= t) ? at[j] * exp2f(gt - gs[j]) : 0.f;
         a4[j] = v;
       }
-      st4<I>(&sA[t * ASTR + 16 * w + 4 * g4], a4);
+      st4<I>(&sA[(t - 16 * j0) * ASTR + 16 * w + 4 * g4], a4);
     }
   }
   // U' rows for phase 2 (requested here, not with the other loads, so that
   // they are not live across phase 1; their latency overlaps S^T Q^T)
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    ufr[ks] = ((ks >> 1) == 0 || has1) ? ld8(Up + ((bh * C + c0 + (ks >> 1)) * DV + dvr) * L + 32 * (ks & 1) + 8 * g4)
+    ufr[ks] = ((ks >> 1) == 0 || need1) ? ld8(Up + ((bh * C + c0 + (ks >> 1)) * DV + dvr) * L + 32 * (ks & 1) + 8 * g4)
                                    : zero_frag<I>();
   __syncthreads();
 
   // ---- phase 2: dv rows 16w..16w+15 of O^T for every token tile
-  f32x4 acc[8];
+  f32x4 acc[NT];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = zero4();
+  for (int j = 0; j < NT; ++j) acc[j] = zero4();
   if (Ssrc != nullptr) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < NT; ++j) {
         const frag_t<I> qf = ld8(&sQ[(16 * j + n16) * QSTR + 32 * ks + 8 * g4]);
         acc[j] = mma(sfr[ks], qf, acc[j]);
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float fac = exp2f(sG[16 * j + n16] + lf);
+    for (int j = 0; j < NT; ++j) {
+      const float fac = exp2f(sG[16 * (j0 + j) + n16] + lf);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) acc[j][jj] *= fac;
     }
@@ -214,8 +224,8 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (ks <= (j >> 1)) {
+    for (int j = 0; j < NT; ++j) {
+      if (ks <= ((j0 + j) >> 1)) {
         const frag_t<I> af = ld8(&sA[(16 * j + n16) * ASTR + 32 * ks + 8 * g4]);
         acc[j] = mma(ufr[ks], af, acc[j]);
       }
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   const float scale = 0.08838834764831845f;   // 128^-1/2
   __syncthreads();   // Q and A^T are no longer read
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < NT; ++j) {
     f32x4 v = acc[j];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) v[jj] *= scale;
@@ -235,30 +245,38 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   // rows of 128 values: 32 consecutive lanes write one token's row
   OT* O = static_cast<OT*>(p.o);
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
+  for (int it = 0; it < NT; ++it) {
     const int q = tid + 512 * it;
     const int t = q >> 5, c4 = (q & 31) * 4;
-    const int tok = c0 * L + t;
+    const int tok = c0 * L + 16 * j0 + t;
     if (tok < sp.len)
       st4o<OT>(O + ((size_t)(sp.tok0 + tok) * Nv + h) * DV + c4, *reinterpret_cast<const f32x4*>(&sO[t * OSTR + c4]));
+  }
+}
+
+template <bool ONE>
+void launch_one(const OChunkArgs& a, int bf16, dim3 grid, hipStream_t s) {
+  if (bf16) {
+    if (a.o_bf16)
+      hipLaunchKernelGGL((ochunk_kernel<sgdn::bf16, sgdn::bf16, ONE>), grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((ochunk_kernel<sgdn::bf16, float, ONE>), grid, dim3(512), 0, s, a);
+  } else {
+    if (a.o_bf16)
+      hipLaunchKernelGGL((ochunk_kernel<float, sgdn::bf16, ONE>), grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((ochunk_kernel<float, float, ONE>), grid, dim3(512), 0, s, a);
   }
 }
 
 }  // namespace
 
 hipError_t launch_ochunk(const OChunkArgs& a, int bf16, hipStream_t s) {
-  dim3 grid(a.G * 2 * a.nrows * a.B);
-  if (bf16) {
-    if (a.o_bf16)
-      hipLaunchKernelGGL((ochunk_kernel<sgdn::bf16, sgdn::bf16>), grid, dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((ochunk_kernel<sgdn::bf16, float>), grid, dim3(512), 0, s, a);
-  } else {
-    if (a.o_bf16)
-      hipLaunchKernelGGL((ochunk_kernel<float, sgdn::bf16>), grid, dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((ochunk_kernel<float, float>), grid, dim3(512), 0, s, a);
-  }
+  dim3 grid(a.G * (a.per_chunk ? 2 : 1) * 2 * a.nrows * a.B);
+  if (a.per_chunk)
+    launch_one<true>(a, bf16, grid, s);
+  else
+    launch_one<false>(a, bf16, grid, s);
   return hipGetLastError();
 }
 

@@ -377,11 +377,12 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
   }
   __syncthreads();
   if (tid == 0) {
+    // CSR rows by tier, High first (in head-pair order with pair_order)
     int r = 0;
     s_rowptr[0] = 0;
     for (int t = 2; t >= 0; --t)
       for (int q = 0; q < NP; ++q)
-        if (s_tier[q] == t) {
+        if (p.pair_order ? t == 2 : s_tier[q] == t) {
           s_rowpair[r] = q;
           s_rowof[q] = r;
           s_rowptr[r + 1] = s_rowptr[r] + s_cnt[q];

@@ -31,7 +31,8 @@ class SparseParams(ctypes.Structure):
                 ("rank_key", ctypes.c_void_p), ("ablate", ctypes.c_int32)]
 
 
-ABLATE = {"deferred_w": 1, "compact_states": 2, "csr": 4}   # SGDN_ABLATE_* bits
+ABLATE = {"deferred_w": 1, "compact_states": 2, "csr": 4, "mapped_o": 8,
+          "tier_schedule": 16}   # SGDN_ABLATE_* bits
 
 
 class Stats(ctypes.Structure):

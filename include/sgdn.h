@@ -131,8 +131,26 @@ typedef struct {
  *                               chunks outside the mask and dropping them,
  *                               instead of walking the CSR event list
  *                               (Eq. (16)); W of every chunk as with
- *                               SGDN_ABLATE_DEFERRED_W.  Not with cu_seqlens. */
-enum { SGDN_ABLATE_DEFERRED_W = 1, SGDN_ABLATE_COMPACT_STATES = 2, SGDN_ABLATE_CSR = 4 };
+ *                               SGDN_ABLATE_DEFERRED_W.  Not with cu_seqlens.
+ *   SGDN_ABLATE_MAPPED_O        O runs one chunk per workgroup instead of
+ *                               one two-chunk group (Eqs. (22)-(24)): both
+ *                               workgroups of a group restore its entry
+ *                               state, and the second also forms the cross
+ *                               term A_{c+1,c} U'_c from the first chunk's
+ *                               K and U'.  Same outputs; combined with
+ *                               COMPACT_STATES it isolates the O mapping.
+ *   SGDN_ABLATE_TIER_SCHEDULE   the CSR rows are laid out in head-pair order
+ *                               instead of by tier (High first), and each
+ *                               stage is one launch on `stream` (the
+ *                               second-stream schedule relies on the High
+ *                               tier in the first rows).  Same outputs. */
+enum {
+  SGDN_ABLATE_DEFERRED_W = 1,
+  SGDN_ABLATE_COMPACT_STATES = 2,
+  SGDN_ABLATE_CSR = 4,
+  SGDN_ABLATE_MAPPED_O = 8,
+  SGDN_ABLATE_TIER_SCHEDULE = 16
+};
 
 /* Per-sequence statistics written on the device. */
 typedef struct {

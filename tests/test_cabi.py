@@ -108,7 +108,7 @@ def test_sparse_and_select_argument_errors(L):
     bad.fixed_tiers = 2
     assert sparse(_prob(), bad) == -1
     bad = ops.sparse_params()
-    bad.ablate = 8
+    bad.ablate = 32
     assert sparse(_prob(), bad) == -1
     assert sparse(_prob(cu_seqlens=0x2000), ops.sparse_params(ablate=("csr",))) == -2
     # the packed-W ablation is defined for the dense layout only

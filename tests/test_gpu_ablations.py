@@ -1,7 +1,9 @@
 """Kernel-pipeline ablations of the sparse path (Sec. 3.6, Table 6): the
 packed-W path (W of every chunk formed in the intra stage), dense
-group-entry states (expanded from the compact snapshots, read by O) and the
-CSR-off scan (every chunk an event, those outside the mask dropped).
+group-entry states (expanded from the compact snapshots, read by O), the
+CSR-off scan (every chunk an event, those outside the mask dropped), the
+mapped-O-off control (O one chunk per workgroup, the group output rule
+kept) and CSR rows in head-pair order instead of by tier.
 
 Each ablated run must select the same events as the default run (the
 selector statistics do not depend on the ablation), match the oracle given
@@ -18,7 +20,8 @@ from helpers import TOL, host, rel_max_err, to_device
 pytestmark = pytest.mark.gpu
 
 ABLATIONS = [("deferred_w",), ("compact_states",), ("deferred_w", "compact_states"), ("csr",),
-             ("csr", "compact_states")]
+             ("csr", "compact_states"), ("mapped_o",), ("compact_states", "mapped_o"),
+             ("tier_schedule",)]
 
 
 def _run(d, C, B, ablate=(), s0=None, **kw):
@@ -61,7 +64,8 @@ def test_ablation_matches_default_and_oracle(ablate, dtype, solve, B):
         assert np.array_equal(S1, S0)
 
 
-def test_compact_states_ablation_packed_sequences():
+@pytest.mark.parametrize("ablate", [("compact_states",), ("mapped_o",), ("compact_states", "mapped_o")])
+def test_state_ablations_packed_sequences(ablate):
     import torch
     lens = [64 * 5 + 3, 1, 0, 64 * 8]
     seqs = [synth.numpy_inputs(3200 + i, 1, max(n, 1), 16, 32, dtype="bf16", with_z=True,
@@ -73,7 +77,7 @@ def test_compact_states_ablation_packed_sequences():
     cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), device="cuda")
     C = -(-max(lens) // 64)
     r0 = _run(d, C, len(lens), cu_seqlens=cu)
-    r1 = _run(d, C, len(lens), ablate=("compact_states",), cu_seqlens=cu)
-    assert np.array_equal(r0[3], r1[3])
+    r1 = _run(d, C, len(lens), ablate=ablate, cu_seqlens=cu)
+    assert np.array_equal(r0[3], r1[3]) and np.array_equal(r0[2], r1[2])
     assert rel_max_err(r1[0], r0[0]) <= TOL["bf16"]
     assert np.array_equal(r1[1], r0[1])
