@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/sgdn.h"
@@ -112,7 +113,9 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
   sz[B_REC] = B * Nv * C * 16;   // sparse: B * Emax * 2 records, Emax <= NP * C
   sz[B_P] = B * Nv * (C + 1) * 8;
   sz[B_U] = B * Nv * C * L * DV * I;
-  sz[B_KT] = B * p.Nq * C * DK * L * I;
+  // K^T blocks per chunk (dense, and the sparse ablations with W of every
+  // chunk) or per kept event (sparse: at most E_max = NP C per sequence)
+  sz[B_KT] = B * (size_t)std::max(p.Nq * p.C, sparse ? p.Emax : 0) * DK * L * I;
   sz[B_S0T] = B * Nv * DV * DK * I;
   if (p.cu != nullptr) sz[B_CHUNKS] = (B * C + 1 + B + 1) * 4;   // valid-chunk table
   if (!sparse) {
@@ -442,7 +445,8 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   const bool wall = (pl.ablate & (SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_CSR)) != 0;
   const bool csr_off = (pl.ablate & SGDN_ABLATE_CSR) != 0;
   DeferredWArgs da{};
-  da.KT = at<void>(ws, pl, B_KT); da.Cb = at<void>(ws, pl, B_CB); da.Wpk = at<void>(ws, pl, B_WPK);
+  da.k = k; da.Cb = at<void>(ws, pl, B_CB); da.Wpk = at<void>(ws, pl, B_WPK);
+  da.KTpk = at<void>(ws, pl, B_KT); da.cu = pl.cu; da.T = pl.T;
   da.row_pair = sa.row_pair; da.row_ptr = sa.row_ptr; da.col = sa.col;
   da.B = pl.B; da.Nv = pl.Nv; da.Nq = pl.Nq; da.C = pl.C; da.Emax = Emax; da.solve = pl.solve;
   EvRecArgs ea{};

@@ -110,6 +110,31 @@ template <typename E> __device__ __forceinline__ frag_t<E> pack44(f32x4 a, f32x4
   f[4] = from_f<E>(b[0]); f[5] = from_f<E>(b[1]); f[6] = from_f<E>(b[2]); f[7] = from_f<E>(b[3]);
   return f;
 }
+// Fragment of a row-major LDS tile read along its rows, in the permuted
+// reduction order of the fragment-major tiles: lane (n, g) receives rows
+// 4g .. 4g+3 and 16+4g .. 16+4g+3 of column n (the A fragment of the
+// transposed tile).  bf16: ds_read_b64_tr_b16, where in each 16-lane group
+// lane m points at 4 elements (row m/4, columns 4(m%4)..+3) of a 4x16 block
+// and lane n then holds column n, rows 0..3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ bf16x8 ld_tr44(const bf16* base, int ld, int lane) {
+  const int m = lane & 15, g = lane >> 4;
+  const bf16* p0 = base + (4 * g + (m >> 2)) * ld + 4 * (m & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * ld));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ f32x8 ld_tr44(const float* base, int ld, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  f32x8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = base[((e < 4) ? 4 * g + e : 16 + 4 * g + e - 4) * ld + n];
+  return f;
+}
+
 template <typename E> __device__ __forceinline__ frag_t<E> zero_frag() {
   frag_t<E> f;
 #pragma unroll

@@ -240,8 +240,8 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
       return SPARSE ? colc[__builtin_amdgcn_readfirstlane(e)] : e;
     };
     const I* Wbase = static_cast<const I*>(p.W);
-    // W packed per kept event (deferred W), or per chunk (dense, and the
-    // deferred-W ablation of the sparse path)
+    // W and K^T packed per kept event (deferred W), or per chunk (dense, and
+    // the deferred-W ablation of the sparse path)
     const bool w_ev = SPARSE && !p.w_by_chunk;
     const I* KTbase = static_cast<const I*>(p.KT);
     // L2 prefetch of event e (clamped to the row): lanes 0-15 the 16 W lines
@@ -254,7 +254,8 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
       const size_t hc = bh * C + c;
       const char* Wt = reinterpret_cast<const char*>(
           w_ev ? Wbase + (((size_t)b * p.Emax + e) * 2 + hh) * L * DK : Wbase + hc * L * DK);
-      const char* Kt = reinterpret_cast<const char*>(KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L);
+      const char* Kt = reinterpret_cast<const char*>(
+          w_ev ? KTbase + ((size_t)b * p.Emax + e) * DK * L : KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L);
       const char* Ut = reinterpret_cast<const char*>(Ubase + hc * DV * L + dv0 * L);
       const char* src = Wt + slice * 16 * 128;
       if (lane < 16) src = Wt + (slice * 16 + lane) * 128;
@@ -268,7 +269,8 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
       const size_t hc = bh * C + c;
       const char* Wt = reinterpret_cast<const char*>(
           w_ev ? Wbase + (((size_t)b * p.Emax + j) * 2 + hh) * L * DK : Wbase + hc * L * DK);
-      const char* Kt = reinterpret_cast<const char*>(KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L);
+      const char* Kt = reinterpret_cast<const char*>(
+          w_ev ? KTbase + ((size_t)b * p.Emax + j) * DK * L : KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L);
       const I* Ut = Ubase + hc * DV * L + dv0 * L;
       const int32_t* rec = SPARSE ? p.rec + (((size_t)b * p.Emax + j) * 2 + hh) * 4 : p.rec + hc * 4;
       char* sl = ring + s * R::BYTES;

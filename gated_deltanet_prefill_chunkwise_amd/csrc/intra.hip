@@ -70,8 +70,6 @@ __device__ __forceinline__ void tile_st(float* T, f32x4 d, int lane) {
 // Fragment of a row-major tile read along its rows: lane (n, g) receives
 // base[(8g + e) * ld + n], e = 0..7, i.e. the B fragment of a product that
 // contracts over the tile's rows (or the A fragment of the transposed tile).
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ bf16x8 ld_tr8(const bf16* base, int ld, int lane) {
   // ds_read_b64_tr_b16: in each 16-lane group, lane m points at 4 elements
   // (row m/4, columns 4(m%4)..+3) of a 4x16 block; lane n then holds column
@@ -89,24 +87,6 @@ __device__ __forceinline__ f32x8 ld_tr8(const float* base, int ld, int lane) {
   f32x8 f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) f[e] = base[(8 * g + e) * ld + n];
-  return f;
-}
-// The same in the permuted reduction order of the fragment-major tiles: lane
-// (n, g) receives rows 4g .. 4g+3 and 16+4g .. 16+4g+3 of column n.
-__device__ __forceinline__ bf16x8 ld_tr44(const bf16* base, int ld, int lane) {
-  const int m = lane & 15, g = lane >> 4;
-  const bf16* p0 = base + (4 * g + (m >> 2)) * ld + 4 * (m & 3);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * ld));
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
-__device__ __forceinline__ f32x8 ld_tr44(const float* base, int ld, int lane) {
-  const int n = lane & 15, g = lane >> 4;
-  f32x8 f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = base[((e < 4) ? 4 * g + e : 16 + 4 * g + e - 4) * ld + n];
   return f;
 }
 
@@ -286,9 +266,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     load_kv(nxt, kreg, v0reg, 0, true);
     load_ab(nxt);
 
-    // ---- fragment-major key tile (K^T operand blocks) for the H and
-    //      deferred-W stages
-    {
+    // ---- fragment-major key tile (K^T operand blocks) for the H scan; the
+    //      sparse path forms them for the kept events only, in the
+    //      deferred-W stage
+    if constexpr (MODE != 1) {
       I* kt = static_cast<I*>(p.KT) + ((size_t)(b * Nq + pq) * C + c) * DK * L;
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
@@ -478,10 +459,13 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
       // be live at the same time)
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (MODE == 1) {
+        // only the 32-column blocks the deferred-W stage reads (the others
+        // are zero by the causal or block-adjacent structure)
         I* cb = static_cast<I*>(p.Cb) + hc * L * L;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          *reinterpret_cast<frag_t<I>*>(cb + (16 * w + n16) * L + 32 * ks + 8 * g4) = cf[ks].cbi;
+          if (ks >= ks_lo && ks <= ks_hi)
+            *reinterpret_cast<frag_t<I>*>(cb + (16 * w + n16) * L + 32 * ks + 8 * g4) = cf[ks].cbi;
       } else {
         // W^T = K^T Cb^T: rows dk, columns t
         I* W = static_cast<I*>(p.W) + hc * L * DK;

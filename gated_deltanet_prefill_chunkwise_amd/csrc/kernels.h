@@ -168,9 +168,13 @@ struct SelectArgs {
 };
 
 struct DeferredWArgs {
-  const void* KT; const void* Cb; void* Wpk;
+  const void* k;        // keys [tokens][Nq][dk] (the input)
+  const void* Cb;
+  void* Wpk;            // [B][Emax][2][64 * 128] W per kept event and head
+  void* KTpk;           // [B][Emax][128 * 64] K^T blocks per kept event
   const int32_t* row_pair; const int32_t* row_ptr; const int32_t* col;
   int B, Nv, Nq, C, Emax, solve;
+  const int32_t* cu; int T;   // packed sequences
   int row_lo, row_hi;   // the events of CSR rows row_lo .. row_hi - 1
 };
 

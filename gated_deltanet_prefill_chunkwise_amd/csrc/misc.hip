@@ -203,10 +203,16 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs p) {
 // Deferred W of kept events only (SparseGDN reading notes, Sec. 2.5,
 // Eq. (15)): W = Cb K from the staged coefficients, computed as
 // W^T = K^T Cb^T and stored as fragment-major W tiles per event (both heads of
-// the pair).
+// the pair).  The event's key rows are staged in LDS (zero past the end of
+// the sequence) and turned into the fragment-major K^T blocks the H scan
+// reads, which are stored per event as well: only kept chunks get them.
 // The grid is sized to the capacity E_max; blocks past the on-device E exit.
+constexpr int DW_KS = DK + 8;   // row stride (elements) of the staged key rows
+
 template <typename E>
 __global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
+  using I = inter_t<E>;
+  __shared__ __align__(16) E sK[L * DW_KS];
   const int b = blockIdx.y;
   const int NP = p.Nv / 2;
   const int i = p.row_ptr[b * (NP + 1) + p.row_lo] + (int)blockIdx.x;
@@ -218,8 +224,31 @@ __global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int n16 = lane & 15, g4 = lane >> 4;
   const bool blockadj = p.solve == 1;
-  using I = inter_t<E>;
-  const I* KT = static_cast<const I*>(p.KT) + (((size_t)b * p.Nq + pr) * p.C + c) * DK * L;
+  const SeqSpan sp = seq_span(p.cu, b, p.T);
+  {
+    // key rows c*64 .. c*64+63 in 16-byte pieces
+    constexpr int PV = 16 / (int)sizeof(E), PR = DK / PV;
+    const E* K = static_cast<const E*>(p.k);
+#pragma unroll
+    for (int it = 0; it < L * PR / 256; ++it) {
+      const int q = tid + 256 * it;
+      const int t = q / PR, e0 = (q % PR) * PV, tok = c * L + t;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (tok < sp.len) v = *reinterpret_cast<const uint4*>(K + ((size_t)(sp.tok0 + tok) * p.Nq + pr) * DK + e0);
+      *reinterpret_cast<uint4*>(&sK[t * DW_KS + e0]) = v;
+    }
+  }
+  __syncthreads();
+  // K^T blocks of the event: wave w forms key tiles 2w and 2w+1
+  I* KT = static_cast<I*>(p.KTpk) + ((size_t)b * p.Emax + i) * DK * L;
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int mt = 2 * w + mi;
+      *reinterpret_cast<frag_t<I>*>(KT + kblk(mt, ks) + 8 * lane) =
+          cvt8<I, E>(ld_tr44(&sK[32 * ks * DW_KS + 16 * mt], DW_KS, lane));
+    }
   const int ks_lo = (blockadj && w == 3) ? 1 : 0;
   const int ks_hi = (w >= 2) ? 1 : 0;
   for (int hh = 0; hh < 2; ++hh) {
@@ -234,7 +263,8 @@ __global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
       const I* cr = Cb + (16 * w + n16) * L + 32 * ks + 4 * g4;
       const frag_t<I> fb = ld44(cr, cr + 16);
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) acc[mt] = mma(ld8(KT + kblk(mt, ks) + 8 * lane), fb, acc[mt]);
+      for (int mt = 0; mt < 8; ++mt)
+        acc[mt] = mma(cvt8<I, E>(ld_tr44(&sK[32 * ks * DW_KS + 16 * mt], DW_KS, lane)), fb, acc[mt]);
     }
     // two stacked W^T tiles form one fragment-major W block
     I* W = static_cast<I*>(p.Wpk) + (((size_t)b * p.Emax + i) * 2 + hh) * L * DK;
