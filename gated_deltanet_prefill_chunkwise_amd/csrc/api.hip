@@ -31,7 +31,7 @@ struct Plan {
 enum Buf { B_G, B_GAMMA, B_P, B_U, B_W, B_CB, B_KT, B_SNAP, B_S0T, B_SCORE, B_ETA, B_RANK,
            B_TINFO, B_MASK, B_TIER, B_ROWPAIR, B_ROWPTR, B_COL, B_PRED, B_GSLOT, B_ESLOT,
            B_WPK, B_STATS, B_FAC, B_REC, B_CHUNKS, B_SPART, B_RANK2, B_ENTRY, B_COLALL,
-           B_RPALL, B_COUNT };
+           B_RPALL, B_ETAP, B_COUNT };
 
 static_assert(B_COUNT <= (int)(sizeof(Plan::off) / sizeof(size_t)), "workspace table too small");
 
@@ -135,6 +135,7 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
     sz[B_SPART] = B * Nv * C * 8 * 4;
     if (sp->rank_key != nullptr) sz[B_RANK2] = B * NP * C * 4;
     sz[B_ETA] = B * Nv * 4;
+    sz[B_ETAP] = B * Nv * GATE_SPLIT * 4;
     sz[B_RANK] = B * NP * C * 4;
     sz[B_TINFO] = B * 8 * 4;
     sz[B_MASK] = B * NP * C;
@@ -409,7 +410,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
 
   // selector and event layout
   if (mask_override == nullptr) {
-    GateArgs ga{z, params->norm_weight, at<float>(ws, pl, B_ETA), pl.B, pl.T, pl.Nv, pl.C, pl.cu};
+    GateArgs ga{z, params->norm_weight, at<float>(ws, pl, B_ETAP), pl.B, pl.T, pl.Nv, pl.C, pl.cu};
     SGDN_TRY(launch_gate(ga, pl.bf16, s));
   }
   mark(dbg, SGDN_EV_GATE, s);
@@ -417,6 +418,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   SelectArgs sa{};
   sa.score = at<float>(ws, pl, B_SCORE); sa.gamma = at<float>(ws, pl, B_GAMMA);
   sa.eta = at<float>(ws, pl, B_ETA);
+  sa.eta_part = at<float>(ws, pl, B_ETAP); sa.eta_out = at<float>(ws, pl, B_ETA);
   sa.B = pl.B; sa.C = pl.C; sa.keep_bp = budget_bp(params->keep_budget);
   sa.cu = pl.cu; sa.T = pl.T;
   sa.fixed_tiers = params->fixed_tiers; sa.unit_visibility = params->unit_visibility;

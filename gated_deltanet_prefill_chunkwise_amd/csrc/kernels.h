@@ -140,13 +140,19 @@ struct EvAllArgs {
 
 struct S0PrepArgs { const float* s0; void* s0T; int B, Nv; };
 
+// The samples of a head are split over GATE_SPLIT workgroups, each writing
+// its sum of squares to eta_part [B][Nv][GATE_SPLIT]; the tier kernel adds
+// the parts in order and divides by the sample count.
+constexpr int GATE_SPLIT = 8;
 struct GateArgs {
-  const void* z; const float* w; float* eta; int B, T, Nv, C;
+  const void* z; const float* w; float* eta_part; int B, T, Nv, C;
   const int32_t* cu;        // packed sequence offsets [B+1] or null
 };
 
 struct SelectArgs {
   const float* score; const float* gamma; const float* eta;
+  // (prefill) eta from the gate kernel's parts, written to eta_out
+  const float* eta_part; float* eta_out;
   int B, C, keep_bp;
   // packed sequence offsets [B+1] or null: sequence b has ceil(len_b / 64)
   // valid chunks (arrays keep the stride C); T bounds every length

@@ -161,43 +161,38 @@ __global__ __launch_bounds__(256) void s0prep_kernel(S0PrepArgs p) {
 
 // eta_h = mean over the 4C samples of (w_v SiLU(z[64c + 8 + 16a, h, v]))^2,
 // v = 73 (4c + a) mod 128 (SparseGDN reading notes, Sec. 2.4, Eq. (11)), C the
-// sequence's own (valid) chunks; 0 for an empty sequence.
+// sequence's own (valid) chunks; 0 for an empty sequence.  Workgroup
+// (h, b, z) sums the squares of the samples in batches z, z + GATE_SPLIT, ...
+// of 1024 (one sample per thread and batch): spread over many CUs, the
+// scattered sample reads are not held up by one CU's outstanding misses.
+constexpr int GATE_THREADS = 1024;
 template <typename E>
-__global__ __launch_bounds__(256) void gate_kernel(GateArgs p) {
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+__global__ __launch_bounds__(GATE_THREADS) void gate_kernel(GateArgs p) {
+  const int h = blockIdx.x, b = blockIdx.y, zb = blockIdx.z, tid = threadIdx.x;
   const E* z = static_cast<const E*>(p.z);
   const SeqSpan sp = seq_span(p.cu, b, p.T);
   const int ns = 4 * chunks_of(sp.len);
   float acc = 0.f;
-  // eight samples' loads are issued together; the sum keeps sample order
-  for (int j0 = tid; j0 < ns; j0 += 256 * 8) {
-    float xv[8], wvv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = j0 + 256 * u;
-      const int c = j >> 2, a = j & 3;
-      const int pos = c * L + 8 + 16 * a;
-      const int v = (73 * j) & (DV - 1);
-      const bool ok = j < ns && pos < sp.len;
-      xv[u] = ok ? to_f(z[((size_t)(sp.tok0 + pos) * p.Nv + h) * DV + v]) : 0.f;
-      wvv[u] = (ok && p.w) ? p.w[v] : 1.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = j0 + 256 * u;
-      const int pos = (j >> 2) * L + 8 + 16 * (j & 3);
-      if (j < ns && pos < sp.len) {
-        const float x = xv[u];
-        const float s = wvv[u] * (x / (1.f + __expf(-x)));
-        acc += s * s;
-      }
+  for (int j = zb * GATE_THREADS + tid; j < ns; j += GATE_SPLIT * GATE_THREADS) {
+    const int c = j >> 2, a = j & 3;
+    const int pos = c * L + 8 + 16 * a;
+    const int v = (73 * j) & (DV - 1);
+    if (pos < sp.len) {
+      const float x = to_f(z[((size_t)(sp.tok0 + pos) * p.Nv + h) * DV + v]);
+      const float s = (p.w ? p.w[v] : 1.f) * (x / (1.f + __expf(-x)));
+      acc += s * s;
     }
   }
-  __shared__ float red[4];
+  constexpr int NWV = GATE_THREADS / 64;
+  __shared__ float red[NWV];
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if ((tid & 63) == 0) red[tid >> 6] = acc;
   __syncthreads();
-  if (tid == 0) p.eta[(size_t)b * p.Nv + h] = ns ? (red[0] + red[1] + red[2] + red[3]) / (float)ns : 0.f;
+  if (tid == 0) {
+    float t = 0.f;
+    for (int i = 0; i < NWV; ++i) t += red[i];
+    p.eta_part[((size_t)b * p.Nv + h) * GATE_SPLIT + zb] = t;
+  }
 }
 
 // Deferred W of kept events only (SparseGDN reading notes, Sec. 2.5,
@@ -443,9 +438,9 @@ hipError_t launch_s0prep(const S0PrepArgs& a, int bf16, hipStream_t s) {
 
 hipError_t launch_gate(const GateArgs& a, int bf16, hipStream_t s) {
   if (bf16)
-    hipLaunchKernelGGL(gate_kernel<sgdn::bf16>, dim3(a.Nv, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(gate_kernel<sgdn::bf16>, dim3(a.Nv, a.B, GATE_SPLIT), dim3(GATE_THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL(gate_kernel<float>, dim3(a.Nv, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(gate_kernel<float>, dim3(a.Nv, a.B, GATE_SPLIT), dim3(GATE_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

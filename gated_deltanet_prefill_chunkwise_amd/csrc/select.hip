@@ -199,38 +199,67 @@ __global__ __launch_bounds__(1024) void select_tier_kernel(SelectArgs p) {
   const float* et = p.eta + (size_t)b * NV;
   const int32_t* rk = p.rank + (size_t)b * NP * CS;
 
+  // wave wv: pair wv, both heads in one pass over the pair's ranks (16
+  // chunks per lane and batch, each lane summing its chunks in ascending order)
   const int lo = C > 16 ? C - 16 : 0, nwin = C - lo;
-  for (int h = 2 * wv; h < 2 * wv + 2; ++h) {
-    const double x = lane < nwin ? exp2_fixed((double)gm[h * CS + lo + lane]) : 0.0;
-    const double tot = wave_sum(x);
-    if (lane == 0) sL[h] = lifetime(tot / nwin, C);
-    const int pp = h >> 1;
-    double alm = 0.0, amh = 0.0;
-    for (int c0 = lane; c0 < C; c0 += 64 * 8) {
-      int rr[8];
-      float xx[8];
+  {
+    const int pp = wv, h0 = 2 * pp;
+    double xw[2];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+    for (int hh = 0; hh < 2; ++hh)
+      xw[hh] = lane < nwin ? exp2_fixed((double)gm[(h0 + hh) * CS + lo + lane]) : 0.0;
+    double alm[2] = {0.0, 0.0}, amh[2] = {0.0, 0.0};
+    for (int c0 = lane; c0 < C; c0 += 64 * 16) {
+      int rr[16];
+      float xx[2][16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
         const int c = c0 + 64 * u;
         rr[u] = c < C ? rk[pp * CS + c] : -1;
-        xx[u] = c < C ? sc[h * CS + c] : 0.f;
+        xx[0][u] = c < C ? sc[h0 * CS + c] : 0.f;
+        xx[1][u] = c < C ? sc[(h0 + 1) * CS + c] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 16; ++u)
         if (c0 + 64 * u < C) {
           const int r = rr[u];
-          const double xs = (double)xx[u];
-          alm = alm + ((r >= kL - 2 && r < kM - 2) ? xs : 0.0);
-          amh = amh + ((r >= kM - 2 && r < kH - 2) ? xs : 0.0);
+          const bool inm = r >= kL - 2 && r < kM - 2, inh = r >= kM - 2 && r < kH - 2;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const double xs = (double)xx[hh][u];
+            alm[hh] = alm[hh] + (inm ? xs : 0.0);
+            amh[hh] = amh[hh] + (inh ? xs : 0.0);
+          }
         }
     }
-    const double tl = wave_sum(alm), th = wave_sum(amh);
-    if (lane == 0) { slm[h] = tl; smh[h] = th; }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const double tot = wave_sum(xw[hh]);
+      const double tl = wave_sum(alm[hh]), th = wave_sum(amh[hh]);
+      if (lane == 0) {
+        sL[h0 + hh] = lifetime(tot / nwin, C);
+        slm[h0 + hh] = tl;
+        smh[h0 + hh] = th;
+      }
+    }
   }
   __syncthreads();
   if (wv != 0) return;
-  const double etab = wave_sum(lane < NV ? (double)et[lane] : 0.0) / NV;
-  if (lane < NV) sGv[lane] = (etab > 0.0 && !p.unit_visibility) ? sqrt((double)et[lane] / etab) : 1.0;
+  // eta of head `lane`: given, or the mean from the gate kernel's parts
+  float eh = 0.f;
+  if (lane < NV) {
+    if (p.eta_part != nullptr) {
+      const float* ep = p.eta_part + ((size_t)b * NV + lane) * GATE_SPLIT;
+      float t = 0.f;
+      for (int i = 0; i < GATE_SPLIT; ++i) t += ep[i];
+      eh = C > 0 ? t / (float)(4 * C) : 0.f;
+      p.eta_out[(size_t)b * NV + lane] = eh;
+    } else {
+      eh = et[lane];
+    }
+  }
+  const double etab = wave_sum(lane < NV ? (double)eh : 0.0) / NV;
+  if (lane < NV) sGv[lane] = (etab > 0.0 && !p.unit_visibility) ? sqrt((double)eh / etab) : 1.0;
   __syncthreads();
   double glm = 0.0, gmh = 0.0;
   if (lane < NP) {
@@ -348,17 +377,17 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
     const int t = s_tier[pp];
     const int k = t == 2 ? kH : (t == 1 ? kM : kL);
     int cnt = 0;
-    for (int i0 = 0; i0 < NW; i0 += 8) {
-      int val[8];
+    for (int i0 = 0; i0 < NW; i0 += 16) {
+      int val[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         const int c = 64 * (i0 + u) + lane;
         const size_t idx = (size_t)b * NP * CS + (size_t)pp * CS + c;
         val[u] = 0;
         if (i0 + u < NW && c < C) val[u] = ovr ? (int)p.mask_in[idx] : rank_src[idx];
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
         const int i = i0 + u;
         if (i < NW) {
           const int c = 64 * i + lane;
