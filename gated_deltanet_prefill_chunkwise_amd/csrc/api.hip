@@ -124,7 +124,7 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
   } else {
     const bool wall = (p.ablate & (SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_CSR)) != 0;
     if (wall) sz[B_W] = B * Nv * C * L * DK * I;   // W of every chunk
-    else sz[B_CB] = B * Nv * C * L * L * I;
+    else sz[B_CB] = B * Nv * C * (I == 2 ? CB_BLOCKS * 512 : L * L) * I;
     if (p.ablate & SGDN_ABLATE_CSR) {                 // all-chunk event lists
       sz[B_COLALL] = B * NP * C * 4;
       sz[B_RPALL] = B * (NP + 1) * 4;
@@ -146,7 +146,7 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
     sz[B_PRED] = B * NP * G * 4;
     sz[B_GSLOT] = B * NP * G * 4;
     sz[B_ESLOT] = B * (size_t)p.Emax * 4;
-    if (!wall) sz[B_WPK] = B * (size_t)p.Emax * 2 * L * DK * I;
+    if (!wall && I == 4) sz[B_WPK] = B * (size_t)p.Emax * 2 * L * DK * I;   // fp32: W per event
     sz[B_STATS] = B * 9 * 4;
   }
   size_t o = 0;
@@ -447,7 +447,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   const bool wall = (pl.ablate & (SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_CSR)) != 0;
   const bool csr_off = (pl.ablate & SGDN_ABLATE_CSR) != 0;
   DeferredWArgs da{};
-  da.k = k; da.Cb = at<void>(ws, pl, B_CB); da.Wpk = at<void>(ws, pl, B_WPK);
+  da.k = k; da.Cb = at<void>(ws, pl, B_CB); da.Wpk = pl.bf16 ? nullptr : at<void>(ws, pl, B_WPK);
   da.KTpk = at<void>(ws, pl, B_KT); da.cu = pl.cu; da.T = pl.T;
   da.row_pair = sa.row_pair; da.row_ptr = sa.row_ptr; da.col = sa.col;
   da.B = pl.B; da.Nv = pl.Nv; da.Nq = pl.Nq; da.C = pl.C; da.Emax = Emax; da.solve = pl.solve;
@@ -476,6 +476,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   HScanArgs ha{};
   ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, wall ? B_W : B_WPK); ha.U = at<void>(ws, pl, B_U);
   ha.w_by_chunk = wall;
+  ha.Cb = at<void>(ws, pl, B_CB); ha.blockadj = pl.solve == SGDN_SOLVE_BLOCKADJ;
   ha.fac = at<float>(ws, pl, B_FAC); ha.rec = ea.rec; ha.P = at<double>(ws, pl, B_P);
   ha.s0 = s0; ha.s_final = s_final; ha.snap = at<void>(ws, pl, B_SNAP);
   ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 1;

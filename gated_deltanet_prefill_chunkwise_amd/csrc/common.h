@@ -110,6 +110,21 @@ template <typename E> __device__ __forceinline__ frag_t<E> pack44(f32x4 a, f32x4
   f[4] = from_f<E>(b[0]); f[5] = from_f<E>(b[1]); f[6] = from_f<E>(b[2]); f[7] = from_f<E>(b[3]);
   return f;
 }
+// Staged Cb of the sparse path with fp16 intermediates: per (chunk, head) six
+// fragment-major blocks of 512 elements, block cb_block(i, ks) the MFMA A
+// operand of token tile i over source tokens 32 ks .. 32 ks + 31 (lane
+// (n, g): row 16 i + n, sources in the permuted order 4g + e, 16 + 4g + e - 4).
+// Blocks (0,1) and (1,1) are zero by causality and not stored; (3,0) is zero
+// with the block-adjacent solve and not written then.
+constexpr int CB_BLOCKS = 6;
+// Position of lane l's 16-byte unit inside a K^T block of the sparse path
+// with fp16 intermediates: unit n + 16 g is stored at 16 g + (n ^ 4 g), so
+// that the transposed reads of four consecutive tokens of one key by lanes
+// with different g fall into different LDS banks (a permutation: the plain
+// per-lane reads stay conflict-free).
+__device__ __forceinline__ int kswz(int l) { return (l & 48) | ((l & 15) ^ ((l >> 2) & 12)); }
+__device__ __forceinline__ int cb_block(int i, int ks) { return i < 2 ? i : 2 * i - 2 + ks; }
+
 // Fragment of a row-major LDS tile read along its rows, in the permuted
 // reduction order of the fragment-major tiles: lane (n, g) receives rows
 // 4g .. 4g+3 and 16+4g .. 16+4g+3 of column n (the A fragment of the

@@ -47,16 +47,18 @@ constexpr int W_COMPUTE = 0;    // wave roles
 constexpr int W_STORER = 1 + NLD;
 constexpr int NWAVE = 2 + NLD;
 
-// One ring slot per event: W blocks, K^T blocks, the U slice [16 dv][64 t]
-// (rearranged for conflict-free reads), 64 factors 2^(gamma - g_t), and the
-// event record {F_in, 2^gamma F_in, snapshot index, chunk} (repeated).
+// One ring slot per event: W blocks (or, CBP, the six Cb blocks of the head),
+// K^T blocks, the U slice [16 dv][64 t] (rearranged for conflict-free reads),
+// 64 factors 2^(gamma - g_t), and the event record {F_in, 2^gamma F_in,
+// snapshot index, chunk} (repeated).
 // Staging entry: U' (same arrangement as U), the snapshot [16 dv][128 dk] in
 // 16-byte units (8 keys of one value row), and {chunk, snapshot index}.
-template <typename I, bool PFON> struct Ring {
+template <typename I, bool PFON, bool CBP> struct Ring {
   static constexpr int FB = 512 * (int)sizeof(I);   // one fragment block
+  static constexpr int NWB = CBP ? CB_BLOCKS : 16;   // blocks of W (of Cb)
   static constexpr int W_OFF = 0;
-  static constexpr int K_OFF = 16 * FB;
-  static constexpr int U_OFF = 32 * FB;
+  static constexpr int K_OFF = NWB * FB;
+  static constexpr int U_OFF = (NWB + 16) * FB;
   static constexpr int U_BYTES = 16 * L * (int)sizeof(I);
   static constexpr int F_OFF = U_OFF + U_BYTES;
   static constexpr int R_OFF = F_OFF + 256;
@@ -65,9 +67,10 @@ template <typename I, bool PFON> struct Ring {
   static constexpr int NS = DEPTH + 1;
   // copy units of one event: 1 KB pieces (16 bytes per lane), then the
   // factors and the record (4 bytes per lane)
-  static constexpr int NW = 16 * FB / 1024;          // pieces of W (and of K^T)
+  static constexpr int NWA = NWB * FB / 1024;       // pieces of W (of Cb)
+  static constexpr int NW = 16 * FB / 1024;          // pieces of K^T
   static constexpr int NUS = U_BYTES / 1024;         // pieces of the U slice
-  static constexpr int NX4 = 2 * NW + NUS;
+  static constexpr int NX4 = NWA + NW + NUS;
   // L2 prefetch (fp16 operands): one scattered 4-byte request per
   // event that touches this workgroup's share of the pair's W and K^T lines
   // and its own U lines PF_AHEAD events before they are copied (its data lands
@@ -112,6 +115,16 @@ __device__ __forceinline__ void storer_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Two transposed LDS reads (ds_read_b64_tr_b16) forming one 8-element MFMA
+// operand: in each 16-lane group lane m supplies the address of 4 contiguous
+// elements (row m / 4, columns 4 (m % 4) .. + 3 of a 4 x 16 block) and lane n
+// receives column n, rows 0 .. 3.
+__device__ __forceinline__ fp16x8 ld_tr_pair(const fp16* p0, const fp16* p1) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+  return __builtin_bit_cast(fp16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // direct global-to-LDS loads: lane l's 16 (4) bytes land at lds + 16 l (4 l)
 __device__ __forceinline__ void dma16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)lds, 16, 0, 0);
@@ -138,10 +151,17 @@ template <typename I> __device__ __forceinline__ int u_unit(int P) {
 // (two waves per SIMD for the register budget: at most 256 registers per
 // lane, so the products accumulate in ordinary vector registers; the LDS ring
 // keeps one workgroup per CU)
-template <typename E, bool SPARSE>
+// CBP (sparse, fp16 intermediates): the ring holds the head's Cb blocks
+// instead of W, and the compute wave forms W S = Cb (K S): Y = K S from the
+// K^T blocks read transposed (gfx950's ds_read_b64_tr_b16: four consecutive
+// tokens of one key are 8 contiguous bytes of a K^T block), then Cb Y from Y
+// converted to the intermediate type.  The operand stream per event drops
+// from 34 KiB (W, K^T, U) to 24 KiB (Cb, K^T, U).
+template <typename E, bool SPARSE, bool CBP>
 __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
   using I = inter_t<E>;
-  using R = Ring<I, sizeof(I) == 2>;
+  static_assert(!CBP || (SPARSE && sizeof(I) == 2), "Cb operand: sparse, fp16 only");
+  using R = Ring<I, sizeof(I) == 2, CBP>;
   constexpr int D = R::DEPTH, NS = R::NS;
   __shared__ __align__(16) char ring[NS * R::BYTES];
   __shared__ __align__(16) char stage[2 * R::ST_BYTES];
@@ -244,8 +264,10 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
     // the deferred-W ablation of the sparse path)
     const bool w_ev = SPARSE && !p.w_by_chunk;
     const I* KTbase = static_cast<const I*>(p.KT);
+    const I* Cbase = static_cast<const I*>(p.Cb);
     // L2 prefetch of event e (clamped to the row): lanes 0-15 the 16 W lines
-    // of this slice's share of the head's tile, 16-23 this workgroup's 8 of
+    // of this slice's share of the head's tile (CBP: lanes 0-5 the 6 of the
+    // head's 48 Cb lines, 6-15 repeat lane 0), 16-23 this workgroup's 8 of
     // the pair's 128 K^T lines, 24-39 the 16 lines of its U slice, 40-41 the
     // factors, the rest repeat lane 0
     auto prefetch = [&](int e) __attribute__((always_inline)) {
@@ -257,9 +279,12 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
       const char* Kt = reinterpret_cast<const char*>(
           w_ev ? KTbase + ((size_t)b * p.Emax + e) * DK * L : KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L);
       const char* Ut = reinterpret_cast<const char*>(Ubase + hc * DV * L + dv0 * L);
-      const char* src = Wt + slice * 16 * 128;
-      if (lane < 16) src = Wt + (slice * 16 + lane) * 128;
-      else if (lane < 24) src = Kt + ((hh * 8 + slice) * 8 + lane - 16) * 128;
+      const char* Ct = reinterpret_cast<const char*>(Cbase + hc * (CB_BLOCKS * 512));
+      const char* src = CBP ? Ct + slice * 6 * 128 : Wt + slice * 16 * 128;
+      if (lane < 16) {
+        if (!CBP) src = Wt + (slice * 16 + lane) * 128;
+        else if (lane < 6) src = Ct + (slice * 6 + lane) * 128;
+      } else if (lane < 24) src = Kt + ((hh * 8 + slice) * 8 + lane - 16) * 128;
       else if (lane < 40) src = Ut + (lane - 24) * 128;
       else if (lane < 42) src = reinterpret_cast<const char*>(p.fac + hc * L) + (lane - 40) * 128;
       dma4(src, pf_sink);
@@ -276,12 +301,16 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
       char* sl = ring + s * R::BYTES;
 #pragma unroll
       for (int u = u0; u < u1; ++u) {
-        if (u < R::NW) {
-          dma16(Wt + u * 1024 + lane * 16, sl + R::W_OFF + u * 1024);
-        } else if (u < 2 * R::NW) {
-          dma16(Kt + (u - R::NW) * 1024 + lane * 16, sl + R::K_OFF + (u - R::NW) * 1024);
+        if (u < R::NWA) {
+          if constexpr (CBP)
+            dma16(reinterpret_cast<const char*>(Cbase + hc * (CB_BLOCKS * 512)) + u * 1024 + lane * 16,
+                  sl + R::W_OFF + u * 1024);
+          else
+            dma16(Wt + u * 1024 + lane * 16, sl + R::W_OFF + u * 1024);
+        } else if (u < R::NWA + R::NW) {
+          dma16(Kt + (u - R::NWA) * 1024 + lane * 16, sl + R::K_OFF + (u - R::NWA) * 1024);
         } else if (u < R::NX4) {
-          const int r = u - 2 * R::NW;
+          const int r = u - R::NWA - R::NW;
           dma16(Ut + u_unit<I>(64 * r + lane), sl + R::U_OFF + r * 1024);
         } else if (u == R::NX4) {
           dma4(p.fac + hc * L + lane, sl + R::F_OFF);
@@ -405,14 +434,45 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
       return x;
     };
     f32x4 a0, a1, a2, a3;
-    ws_pair(0, a0, a1);
-    ws_pair(2, a2, a3);
+    if constexpr (CBP) {
+      // A fragment of K over key step q (keys 32 q + 4 g + e, 32 q + 16 +
+      // 4 g + e) for token tile i: lane m of group g points at key 32 q +
+      // 4 g + m / 4 (+ 16), tokens 16 i + 4 (m % 4) .. + 3, which are 8
+      // contiguous bytes of K^T block (key tile, token step i / 2)
+      const int koff = 8 * kswz(4 * g4 + (n16 >> 2) + 16 * (n16 & 3));
+      auto kfrag = [&](int q, int i) __attribute__((always_inline)) {
+        const int o = koff + 4 * (i & 1);
+        return ld_tr_pair(Ks + kblk(2 * q, i >> 1) + o, Ks + kblk(2 * q + 1, i >> 1) + o);
+      };
+      f32x4 y[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[i] = zero4();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) y[i] = mma(kfrag(q, i), Sf[q], y[i]);
+      }
+      // W S = Cb Y over source steps 0 (tokens 0-31) and 1 (32-63)
+      const frag_t<I> Y0 = pack44<I>(y[0], y[1]), Y1 = pack44<I>(y[2], y[3]);
+      auto cbf = [&](int i, int ks) __attribute__((always_inline)) {
+        return ld8(Ws + cb_block(i, ks) * 512 + 8 * lane);
+      };
+      a0 = mma(cbf(0, 0), Y0, zero4());
+      a1 = mma(cbf(1, 0), Y0, zero4());
+      a2 = mma(cbf(2, 1), Y1, mma(cbf(2, 0), Y0, zero4()));
+      a3 = mma(cbf(3, 1), Y1, zero4());
+      if (!p.blockadj) a3 = mma(cbf(3, 0), Y0, a3);
+    } else {
+      ws_pair(0, a0, a1);
+      ws_pair(2, a2, a3);
+    }
+    // (CBP: the K^T units are stored in the order kswz)
+    const int kl = CBP ? kswz(lane) : lane;
     const frag_t<I> X0 = pack44<I>(ux(0, a0), ux(1, a1));
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) S[mt] = mma(ld8(Ks + kblk(mt, 0) + 8 * lane), X0, S[mt] * decf);
+    for (int mt = 0; mt < 8; ++mt) S[mt] = mma(ld8(Ks + kblk(mt, 0) + 8 * kl), X0, S[mt] * decf);
     const frag_t<I> X1 = pack44<I>(ux(2, a2), ux(3, a3));
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) S[mt] = mma(ld8(Ks + kblk(mt, 1) + 8 * lane), X1, S[mt]);
+    for (int mt = 0; mt < 8; ++mt) S[mt] = mma(ld8(Ks + kblk(mt, 1) + 8 * kl), X1, S[mt]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) Sf[q] = pack44<I>(S[2 * q], S[2 * q + 1]);
 
@@ -458,18 +518,22 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
   }
 }
 
-template <typename E, bool SPARSE>
+template <typename E, bool SPARSE, bool CBP>
 hipError_t launch_one(const HScanArgs& a, hipStream_t s) {
   const int nblk = 128 * ((a.B * a.nrows + 7) / 8);
-  hipLaunchKernelGGL((hscan_kernel<E, SPARSE>), dim3(nblk), dim3(64 * NWAVE), 0, s, a);
+  hipLaunchKernelGGL((hscan_kernel<E, SPARSE, CBP>), dim3(nblk), dim3(64 * NWAVE), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_hscan(const HScanArgs& a, int bf16, hipStream_t s) {
-  if (bf16) return a.sparse ? launch_one<sgdn::bf16, true>(a, s) : launch_one<sgdn::bf16, false>(a, s);
-  return a.sparse ? launch_one<float, true>(a, s) : launch_one<float, false>(a, s);
+  if (bf16) {
+    if (!a.sparse) return launch_one<sgdn::bf16, false, false>(a, s);
+    // W of every chunk (the deferred-W and CSR-off controls) or W S from Cb
+    return a.w_by_chunk ? launch_one<sgdn::bf16, true, false>(a, s) : launch_one<sgdn::bf16, true, true>(a, s);
+  }
+  return a.sparse ? launch_one<float, true, false>(a, s) : launch_one<float, false, false>(a, s);
 }
 
 }  // namespace sgdn

@@ -458,7 +458,20 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
       // keep the U and W products apart (their accumulators would otherwise
       // be live at the same time)
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (MODE == 1) {
+      if constexpr (MODE == 1 && sizeof(I) == 2) {
+        // fragment-major blocks for the H scan (W S = Cb (K S)): lane
+        // (n, g) holds sources 8g .. 8g+7, which are positions 4 (g >> 1) ..
+        // + 3 of lanes n + 16 (2 (g & 1)) and n + 16 (2 (g & 1) + 1) there
+        I* cb = static_cast<I*>(p.Cb) + hc * CB_BLOCKS * 512;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          if (ks >= ks_lo && ks <= ks_hi) {
+            I* blk = cb + cb_block(w, ks) * 512 + 4 * (g4 >> 1);
+            const int l0 = n16 + 32 * (g4 & 1);
+            *reinterpret_cast<half_t<I>*>(blk + 8 * l0) = __builtin_shufflevector(cf[ks].cbi, cf[ks].cbi, 0, 1, 2, 3);
+            *reinterpret_cast<half_t<I>*>(blk + 8 * (l0 + 16)) = __builtin_shufflevector(cf[ks].cbi, cf[ks].cbi, 4, 5, 6, 7);
+          }
+      } else if constexpr (MODE == 1) {
         // only the 32-column blocks the deferred-W stage reads (the others
         // are zero by the causal or block-adjacent structure)
         I* cb = static_cast<I*>(p.Cb) + hc * L * L;

@@ -81,6 +81,10 @@ struct HScanArgs {
   const int32_t* event_slot;// [B][Emax]
   int Emax;
   int snap_cap;             // snapshot slots per batch (sparse)
+  // sparse, fp16 intermediates: staged Cb [B][Nv][C][6][512] (fragment-major
+  // blocks); W S is formed as Cb (K S) from it and the K^T tile
+  const void* Cb;
+  int blockadj;             // Cb block (3,0) is zero (block-adjacent solve)
 };
 
 struct OChunkArgs {

@@ -196,11 +196,14 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_kernel(GateArgs p) {
 }
 
 // Deferred W of kept events only (SparseGDN reading notes, Sec. 2.5,
-// Eq. (15)): W = Cb K from the staged coefficients, computed as
-// W^T = K^T Cb^T and stored as fragment-major W tiles per event (both heads of
-// the pair).  The event's key rows are staged in LDS (zero past the end of
+// Eq. (15)).  The event's key rows are staged in LDS (zero past the end of
 // the sequence) and turned into the fragment-major K^T blocks the H scan
-// reads, which are stored per event as well: only kept chunks get them.
+// reads, stored per event: only kept chunks get them (with fp16
+// intermediates in the bank-spread unit order kswz).  With fp32
+// intermediates W = Cb K is formed here as well, as W^T = K^T Cb^T, and stored
+// as fragment-major W tiles per event (both heads of the pair); with fp16
+// intermediates (Wpk null) the H scan forms W S = Cb (K S) from Cb and K^T
+// itself, so W is never written.
 // The grid is sized to the capacity E_max; blocks past the on-device E exit.
 constexpr int DW_KS = DK + 8;   // row stride (elements) of the staged key rows
 
@@ -241,9 +244,11 @@ __global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int mt = 2 * w + mi;
-      *reinterpret_cast<frag_t<I>*>(KT + kblk(mt, ks) + 8 * lane) =
+      *reinterpret_cast<frag_t<I>*>(KT + kblk(mt, ks) + 8 * (sizeof(I) == 2 ? kswz(lane) : lane)) =
           cvt8<I, E>(ld_tr44(&sK[32 * ks * DW_KS + 16 * mt], DW_KS, lane));
     }
+  // (fp16 intermediates: the H scan forms W S as Cb (K S) itself)
+  if (p.Wpk == nullptr) return;
   const int ks_lo = (blockadj && w == 3) ? 1 : 0;
   const int ks_hi = (w >= 2) ? 1 : 0;
   for (int hh = 0; hh < 2; ++hh) {
