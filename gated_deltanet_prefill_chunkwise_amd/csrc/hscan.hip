@@ -43,8 +43,7 @@ typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
 
 constexpr int NLD = 2;          // loader waves
-constexpr int W_COMPUTE = 0;    // wave roles
-constexpr int W_STORER = 1 + NLD;
+// waves: compute (one; two with the Cb operand), loaders, storer
 constexpr int NWAVE = 2 + NLD;
 
 // One ring slot per event: W blocks (or, CBP, the six Cb blocks of the head),
@@ -63,7 +62,9 @@ template <typename I, bool PFON, bool CBP> struct Ring {
   static constexpr int F_OFF = U_OFF + U_BYTES;
   static constexpr int R_OFF = F_OFF + 256;
   static constexpr int BYTES = R_OFF + 256;
-  static constexpr int DEPTH = sizeof(I) == 2 ? 3 : 1;  // events requested ahead
+  // events requested ahead (CBP: the compute waves also read the slot of the
+  // next event, so one more is in the ring)
+  static constexpr int DEPTH = CBP ? 4 : (sizeof(I) == 2 ? 3 : 1);
   static constexpr int NS = DEPTH + 1;
   // copy units of one event: 1 KB pieces (16 bytes per lane), then the
   // factors and the record (4 bytes per lane)
@@ -157,15 +158,28 @@ template <typename I> __device__ __forceinline__ int u_unit(int P) {
 // tokens of one key are 8 contiguous bytes of a K^T block), then Cb Y from Y
 // converted to the intermediate type.  The operand stream per event drops
 // from 34 KiB (W, K^T, U) to 24 KiB (Cb, K^T, U).
+//
+// CBP also splits the compute over two waves (on two SIMDs): compute wave cw
+// owns key rows 64 cw .. 64 cw + 63 of the slice's state.  Each forms its
+// half of the next event's Y = K S from that event's slot at the end of the
+// current step and leaves it in LDS; after the event barrier both add the
+// two halves (in the same order) and form Cb Y, U' and X identically; each
+// then updates its own state rows with K^T X.  The loaders keep two events
+// complete at every barrier (the current and the next).
 template <typename E, bool SPARSE, bool CBP>
-__global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
+__global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanArgs p) {
   using I = inter_t<E>;
   static_assert(!CBP || (SPARSE && sizeof(I) == 2), "Cb operand: sparse, fp16 only");
   using R = Ring<I, sizeof(I) == 2, CBP>;
   constexpr int D = R::DEPTH, NS = R::NS;
+  constexpr int NCW = CBP ? 2 : 1;         // compute waves 0 .. NCW - 1
+  constexpr int WST = NCW + NLD;           // storer wave (loaders in between)
+  static_assert(!CBP || D >= 2, "two events complete at each barrier");
   __shared__ __align__(16) char ring[NS * R::BYTES];
   __shared__ __align__(16) char stage[2 * R::ST_BYTES];
   __shared__ __align__(16) char pf_sink[256];
+  // CBP: halves of the next event's Y, [parity][compute wave][token tile][lane]
+  __shared__ __align__(16) f32x4 ych[CBP ? 2 * 2 * 4 * 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -212,7 +226,7 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
                   : snap + (bh * (G - 1) + si) * DV * DK;
   };
 
-  if (w == W_STORER) {
+  if (w == WST) {
     // ======================= storer wave =======================
     // copy staging entry e (U' and the snapshot of one event) to global memory
     auto copy_out = [&](int e) __attribute__((always_inline)) {
@@ -249,9 +263,9 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
     return;
   }
 
-  if (w != W_COMPUTE) {
+  if (w >= NCW) {
     // ======================= loader waves =======================
-    const int k = w - 1;
+    const int k = w - NCW;
     // event chunks are read through the scalar cache (constant address space:
     // the event list is not written during the kernel), so their waits never
     // mix with the counted direct loads
@@ -333,7 +347,7 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
 #pragma unroll
         for (int e = 0; e < D; ++e)
           if (e < npro) issue(i0 + e, col_at(i0 + e), e, U0, U1);
-        if (npro == D) wait_vm<CNT * (D - 1)>();
+        if (npro == D) wait_vm<CNT * (D - (CBP ? 2 : 1))>();   // first (two) events complete
         else wait_vm<0>();
       }
       // sparse: the chunk of the next request is read one event early, so
@@ -347,7 +361,7 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
           const int c = cnext;
           cnext = col_at(min(j + D + 1, jlast));
           issue(j + D, c, s, U0, U1);
-          wait_vm<CNT * (D - 1)>();   // event j + 1 complete
+          wait_vm<CNT * (D - (CBP ? 2 : 1))>();   // event j + 1 (CBP: and j + 2) complete
         } else {
           wait_vm<0>();
         }
@@ -358,6 +372,169 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
     static_assert(NLD == 2, "one branch per loader wave");
     if (k == 0) run(std::integral_constant<int, 0>{});
     else run(std::integral_constant<int, 1>{});
+    return;
+  }
+
+  if constexpr (CBP) {
+    // =================== compute waves (Cb operand) ===================
+    const int cw = w;
+    const double* P = p.P + bh * (C + 1);
+    // initial state (all rows: the first event's Y is formed from it in
+    // full by both waves), s0 decayed over the chunks before the first event
+    f32x4 S[8];
+    {
+      const float f0 = exp2f((float)P[(i0 < i1) ? colb[i0] : C]);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int dk = 16 * mt + 4 * g4 + j;
+          S[mt][j] = p.s0 ? f0 * p.s0[(bh * DK + dk) * DV + dv0 + n16] : 0.f;
+        }
+    }
+    // own rows: tiles 4 cw .. 4 cw + 3 (key steps 2 cw, 2 cw + 1), read
+    // again rather than picked from S (a runtime pick would index S)
+    f32x4 So[4];
+    {
+      const float f0 = exp2f((float)P[(i0 < i1) ? colb[i0] : C]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int dk = 16 * (4 * cw + t) + 4 * g4 + j;
+          So[t][j] = p.s0 ? f0 * p.s0[(bh * DK + dk) * DV + dv0 + n16] : 0.f;
+        }
+    }
+    frag_t<I> Sfo[2];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) Sfo[qq] = pack44<I>(So[2 * qq], So[2 * qq + 1]);
+
+    // A fragment of K over key step q (keys 32 q + 4 g + e, 32 q + 16 + 4 g +
+    // e) for token tile i: lane m of group g points at key 32 q + 4 g + m / 4
+    // (+ 16), tokens 16 i + 4 (m % 4) .. + 3: 8 contiguous bytes of the K^T
+    // block (key tile, token step i / 2), unit kswz(key % 16 + 16 (m % 4))
+    const int koff = 8 * kswz(4 * g4 + (n16 >> 2) + 16 * (n16 & 3));
+    auto kfrag = [&](const I* Kb, int q, int i) __attribute__((always_inline)) {
+      const int o = koff + 4 * (i & 1);
+      return ld_tr_pair(Kb + kblk(2 * q, i >> 1) + o, Kb + kblk(2 * q + 1, i >> 1) + o);
+    };
+    const int kl = kswz(lane);
+
+    f32x4 y[4], ym[4];
+    int s = 0;
+    int last_c = -1;   // chunk of the last event that updated the state
+    if (i0 < i1) {
+      lds_barrier();   // events i0 and i0 + 1 are in the ring
+      const I* Ks = reinterpret_cast<const I*>(ring + R::K_OFF);
+      frag_t<I> Sf[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Sf[q] = pack44<I>(S[2 * q], S[2 * q + 1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[i] = zero4();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) y[i] = mma(kfrag(Ks, q, i), Sf[q], y[i]);
+      }
+    }
+    for (int j = i0; j < i1; ++j) {
+      if (j > i0) {
+        lds_barrier();   // event j + 1 in the ring; halves of Y(j) in LDS
+        const f32x4* yo = ych + ((j & 1) * 2 + (1 - cw)) * 4 * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 o = yo[i * 64 + lane];
+          y[i] = cw == 0 ? ym[i] + o : o + ym[i];   // both: half 0 + half 1
+        }
+      }
+      const char* sl = ring + s * R::BYTES;
+      char* st = stage + ((j - i0) & 1) * R::ST_BYTES;
+      const int4 rc = *reinterpret_cast<const int4*>(sl + R::R_OFF);
+      const float fin = __int_as_float(__builtin_amdgcn_readfirstlane(rc.x));
+      const float decf = __int_as_float(__builtin_amdgcn_readfirstlane(rc.y));
+      // (chunk and snapshot index are clamped to their ranges, so that no
+      // record content can address memory outside U and the snapshots)
+      const int sn = __builtin_amdgcn_readfirstlane(rc.z);
+      const int snapi = (sn >= 0 && sn < snap_cap) ? sn : -1;
+      const int c = min(max(__builtin_amdgcn_readfirstlane(rc.w), 0), C - 1);
+      last_c = c;
+      const I* Cs = reinterpret_cast<const I*>(sl + R::W_OFF);
+      const I* Ks = reinterpret_cast<const I*>(sl + R::K_OFF);
+
+      // ---- W S = Cb Y over source steps 0 (tokens 0-31) and 1 (32-63)
+      const frag_t<I> Y0 = pack44<I>(y[0], y[1]), Y1 = pack44<I>(y[2], y[3]);
+      auto cbf = [&](int i, int ks) __attribute__((always_inline)) {
+        return ld8(Cs + cb_block(i, ks) * 512 + 8 * lane);
+      };
+      const f32x4 a0 = mma(cbf(0, 0), Y0, zero4());
+      const f32x4 a1 = mma(cbf(1, 0), Y0, zero4());
+      const f32x4 a2 = mma(cbf(2, 1), Y1, mma(cbf(2, 0), Y0, zero4()));
+      f32x4 a3 = mma(cbf(3, 1), Y1, zero4());
+      if (!p.blockadj) a3 = mma(cbf(3, 0), Y0, a3);
+
+      // ---- U' = U - F_in W S (Eq. (1)); X = U' 2^(gamma - g); wave 0
+      //      stages U'
+      auto ux = [&](int i, const f32x4& ai) __attribute__((always_inline)) {
+        const half_t<I> u = *reinterpret_cast<const half_t<I>*>(sl + R::U_OFF + u_off<I>(i, n16, g4));
+        const f32x4 fc = *reinterpret_cast<const f32x4*>(sl + R::F_OFF + (16 * i + 4 * g4) * 4);
+        f32x4 up, x;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          up[jj] = to_f(u[jj]) - fin * ai[jj];
+          x[jj] = up[jj] * fc[jj];
+        }
+        if (cw == 0) st4<I>(reinterpret_cast<I*>(st + u_off<I>(i, n16, g4)), up);
+        return x;
+      };
+      const frag_t<I> X0 = pack44<I>(ux(0, a0), ux(1, a1));
+      const frag_t<I> X1 = pack44<I>(ux(2, a2), ux(3, a3));
+      // ---- own rows: S <- 2^gamma F_in S + K^T X (Eq. (2))
+#pragma unroll
+      for (int t = 0; t < 4; ++t) So[t] = mma(ld8(Ks + kblk(4 * cw + t, 0) + 8 * kl), X0, So[t] * decf);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) So[t] = mma(ld8(Ks + kblk(4 * cw + t, 1) + 8 * kl), X1, So[t]);
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) Sfo[qq] = pack44<I>(So[2 * qq], So[2 * qq + 1]);
+
+      // ---- compact snapshot of S_{c+1}, own key rows (key steps 2 cw + qq)
+      if (snapi >= 0) {
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+          for (int hi = 0; hi < 2; ++hi) {
+            const int c8 = 4 * (2 * cw + qq) + 2 * hi + (g4 >> 1);
+            const half_t<I> v = hi ? __builtin_shufflevector(Sfo[qq], Sfo[qq], 4, 5, 6, 7)
+                                   : __builtin_shufflevector(Sfo[qq], Sfo[qq], 0, 1, 2, 3);
+            *reinterpret_cast<half_t<I>*>(st + R::ST_SN + (c8 * 16 + n16) * 16 + 8 * (g4 & 1)) = v;
+          }
+      }
+      if (cw == 0 && lane == 0) *reinterpret_cast<int2*>(st + R::ST_HDR) = make_int2(c, snapi);
+
+      // ---- own half of the next event's Y from its slot
+      const int s1 = (s + 1 == NS) ? 0 : s + 1;
+      if (j + 1 < i1) {
+        const I* Kn = reinterpret_cast<const I*>(ring + s1 * R::BYTES + R::K_OFF);
+        f32x4* yw = ych + (((j + 1) & 1) * 2 + cw) * 4 * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ym[i] = mma(kfrag(Kn, 2 * cw + 1, i), Sfo[1], mma(kfrag(Kn, 2 * cw, i), Sfo[0], zero4()));
+          yw[i * 64 + lane] = ym[i];
+        }
+      }
+      s = s1;
+    }
+    lds_barrier();   // the last staging entry is complete
+
+    if (p.s_final != nullptr) {
+      // gap from the last event to the end of the sequence
+      const float fl = (i1 > i0) ? exp2f((float)(P[C] - P[last_c + 1])) : 1.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int dk = 16 * (4 * cw + t) + 4 * g4 + j;
+          p.s_final[(bh * DK + dk) * DV + dv0 + n16] = fl * So[t][j];
+        }
+    }
     return;
   }
 
@@ -434,39 +611,9 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
       return x;
     };
     f32x4 a0, a1, a2, a3;
-    if constexpr (CBP) {
-      // A fragment of K over key step q (keys 32 q + 4 g + e, 32 q + 16 +
-      // 4 g + e) for token tile i: lane m of group g points at key 32 q +
-      // 4 g + m / 4 (+ 16), tokens 16 i + 4 (m % 4) .. + 3, which are 8
-      // contiguous bytes of K^T block (key tile, token step i / 2)
-      const int koff = 8 * kswz(4 * g4 + (n16 >> 2) + 16 * (n16 & 3));
-      auto kfrag = [&](int q, int i) __attribute__((always_inline)) {
-        const int o = koff + 4 * (i & 1);
-        return ld_tr_pair(Ks + kblk(2 * q, i >> 1) + o, Ks + kblk(2 * q + 1, i >> 1) + o);
-      };
-      f32x4 y[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        y[i] = zero4();
-#pragma unroll
-        for (int q = 0; q < 4; ++q) y[i] = mma(kfrag(q, i), Sf[q], y[i]);
-      }
-      // W S = Cb Y over source steps 0 (tokens 0-31) and 1 (32-63)
-      const frag_t<I> Y0 = pack44<I>(y[0], y[1]), Y1 = pack44<I>(y[2], y[3]);
-      auto cbf = [&](int i, int ks) __attribute__((always_inline)) {
-        return ld8(Ws + cb_block(i, ks) * 512 + 8 * lane);
-      };
-      a0 = mma(cbf(0, 0), Y0, zero4());
-      a1 = mma(cbf(1, 0), Y0, zero4());
-      a2 = mma(cbf(2, 1), Y1, mma(cbf(2, 0), Y0, zero4()));
-      a3 = mma(cbf(3, 1), Y1, zero4());
-      if (!p.blockadj) a3 = mma(cbf(3, 0), Y0, a3);
-    } else {
-      ws_pair(0, a0, a1);
-      ws_pair(2, a2, a3);
-    }
-    // (CBP: the K^T units are stored in the order kswz)
-    const int kl = CBP ? kswz(lane) : lane;
+    ws_pair(0, a0, a1);
+    ws_pair(2, a2, a3);
+    const int kl = lane;
     const frag_t<I> X0 = pack44<I>(ux(0, a0), ux(1, a1));
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) S[mt] = mma(ld8(Ks + kblk(mt, 0) + 8 * kl), X0, S[mt] * decf);
@@ -521,7 +668,7 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void hscan_kernel(HScanArgs p) {
 template <typename E, bool SPARSE, bool CBP>
 hipError_t launch_one(const HScanArgs& a, hipStream_t s) {
   const int nblk = 128 * ((a.B * a.nrows + 7) / 8);
-  hipLaunchKernelGGL((hscan_kernel<E, SPARSE, CBP>), dim3(nblk), dim3(64 * NWAVE), 0, s, a);
+  hipLaunchKernelGGL((hscan_kernel<E, SPARSE, CBP>), dim3(nblk), dim3(64 * (CBP ? 5 : NWAVE)), 0, s, a);
   return hipGetLastError();
 }
 
