@@ -378,6 +378,9 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
   if constexpr (CBP) {
     // =================== compute waves (Cb operand) ===================
     const int cw = w;
+    // the compute waves' chain bounds the step: they win issue arbitration
+    // against the storer wave that shares a SIMD with compute wave 0
+    __builtin_amdgcn_s_setprio(3);
     const double* P = p.P + bh * (C + 1);
     // initial state (all rows: the first event's Y is formed from it in
     // full by both waves), s0 decayed over the chunks before the first event
