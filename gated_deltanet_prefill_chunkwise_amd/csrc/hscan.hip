@@ -26,6 +26,12 @@
 // One workgroup barrier per event hands a filled slot to the compute wave and
 // an emptied one back to the loaders.
 //
+// Two operand forms (template CBP): the W operand above (dense path, fp32
+// inputs, and the sparse controls with W of every chunk), and for the sparse
+// path with fp16 intermediates the Cb operand, where W = Cb K is never formed
+// (W S = Cb (K S)) and the state rows are split over two compute waves; see
+// the comment at the kernel.
+//
 // The gap factor that carries S to the next event is kept out of the state
 // registers: with S_true = F_in * S, the step forms U' = U - F_in (W S) and
 // S <- (2^gamma F_in) S + K^T X, so S is the true state after every update
