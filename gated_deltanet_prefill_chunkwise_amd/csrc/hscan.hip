@@ -468,6 +468,20 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
       last_c = c;
       const I* Cs = reinterpret_cast<const I*>(sl + R::W_OFF);
       const I* Ks = reinterpret_cast<const I*>(sl + R::K_OFF);
+      // the next event's K fragments of this wave's key steps, requested now
+      // (its slot is complete at this barrier) so that their latency overlaps
+      // this step; for the row's last event they read a stale slot and the
+      // result goes unused.  The step below has no branches, so the loads of
+      // all its operands can be issued ahead of their products.
+      const int s1 = (s + 1 == NS) ? 0 : s + 1;
+      frag_t<I> kn[2][4];
+      {
+        const I* Kn = reinterpret_cast<const I*>(ring + s1 * R::BYTES + R::K_OFF);
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kn[qq][i] = kfrag(Kn, 2 * cw + qq, i);
+      }
 
       // ---- W S = Cb Y over source steps 0 (tokens 0-31) and 1 (32-63)
       const frag_t<I> Y0 = pack44<I>(y[0], y[1]), Y1 = pack44<I>(y[2], y[3]);
@@ -477,11 +491,14 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
       const f32x4 a0 = mma(cbf(0, 0), Y0, zero4());
       const f32x4 a1 = mma(cbf(1, 0), Y0, zero4());
       const f32x4 a2 = mma(cbf(2, 1), Y1, mma(cbf(2, 0), Y0, zero4()));
-      f32x4 a3 = mma(cbf(3, 1), Y1, zero4());
-      if (!p.blockadj) a3 = mma(cbf(3, 0), Y0, a3);
+      const f32x4 a3b = mma(cbf(3, 1), Y1, zero4());
+      // (the block-adjacent solve stores no block (3,0): the product of
+      // whatever its slot holds is formed and dropped)
+      const f32x4 a3x = mma(cbf(3, 0), Y0, a3b);
+      const f32x4 a3 = p.blockadj ? a3b : a3x;
 
-      // ---- U' = U - F_in W S (Eq. (1)); X = U' 2^(gamma - g); wave 0
-      //      stages U'
+      // ---- U' = U - F_in W S (Eq. (1)); X = U' 2^(gamma - g); both waves
+      //      stage the same U' values
       auto ux = [&](int i, const f32x4& ai) __attribute__((always_inline)) {
         const half_t<I> u = *reinterpret_cast<const half_t<I>*>(sl + R::U_OFF + u_off<I>(i, n16, g4));
         const f32x4 fc = *reinterpret_cast<const f32x4*>(sl + R::F_OFF + (16 * i + 4 * g4) * 4);
@@ -491,7 +508,7 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
           up[jj] = to_f(u[jj]) - fin * ai[jj];
           x[jj] = up[jj] * fc[jj];
         }
-        if (cw == 0) st4<I>(reinterpret_cast<I*>(st + u_off<I>(i, n16, g4)), up);
+        st4<I>(reinterpret_cast<I*>(st + u_off<I>(i, n16, g4)), up);
         return x;
       };
       const frag_t<I> X0 = pack44<I>(ux(0, a0), ux(1, a1));
@@ -504,30 +521,25 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) Sfo[qq] = pack44<I>(So[2 * qq], So[2 * qq + 1]);
 
-      // ---- compact snapshot of S_{c+1}, own key rows (key steps 2 cw + qq)
-      if (snapi >= 0) {
+      // ---- compact snapshot of S_{c+1}, own key rows (key steps 2 cw + qq);
+      //      staged for every event, copied only where referenced
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq)
+      for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-          for (int hi = 0; hi < 2; ++hi) {
-            const int c8 = 4 * (2 * cw + qq) + 2 * hi + (g4 >> 1);
-            const half_t<I> v = hi ? __builtin_shufflevector(Sfo[qq], Sfo[qq], 4, 5, 6, 7)
-                                   : __builtin_shufflevector(Sfo[qq], Sfo[qq], 0, 1, 2, 3);
-            *reinterpret_cast<half_t<I>*>(st + R::ST_SN + (c8 * 16 + n16) * 16 + 8 * (g4 & 1)) = v;
-          }
-      }
-      if (cw == 0 && lane == 0) *reinterpret_cast<int2*>(st + R::ST_HDR) = make_int2(c, snapi);
-
-      // ---- own half of the next event's Y from its slot
-      const int s1 = (s + 1 == NS) ? 0 : s + 1;
-      if (j + 1 < i1) {
-        const I* Kn = reinterpret_cast<const I*>(ring + s1 * R::BYTES + R::K_OFF);
-        f32x4* yw = ych + (((j + 1) & 1) * 2 + cw) * 4 * 64;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ym[i] = mma(kfrag(Kn, 2 * cw + 1, i), Sfo[1], mma(kfrag(Kn, 2 * cw, i), Sfo[0], zero4()));
-          yw[i * 64 + lane] = ym[i];
+        for (int hi = 0; hi < 2; ++hi) {
+          const int c8 = 4 * (2 * cw + qq) + 2 * hi + (g4 >> 1);
+          const half_t<I> v = hi ? __builtin_shufflevector(Sfo[qq], Sfo[qq], 4, 5, 6, 7)
+                                 : __builtin_shufflevector(Sfo[qq], Sfo[qq], 0, 1, 2, 3);
+          *reinterpret_cast<half_t<I>*>(st + R::ST_SN + (c8 * 16 + n16) * 16 + 8 * (g4 & 1)) = v;
         }
+      if (lane == 0) *reinterpret_cast<int2*>(st + R::ST_HDR) = make_int2(c, snapi);
+
+      // ---- own half of the next event's Y
+      f32x4* yw = ych + (((j + 1) & 1) * 2 + cw) * 4 * 64;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ym[i] = mma(kn[1][i], Sfo[1], mma(kn[0][i], Sfo[0], zero4()));
+        yw[i * 64 + lane] = ym[i];
       }
       s = s1;
     }
@@ -622,13 +634,12 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
     f32x4 a0, a1, a2, a3;
     ws_pair(0, a0, a1);
     ws_pair(2, a2, a3);
-    const int kl = lane;
     const frag_t<I> X0 = pack44<I>(ux(0, a0), ux(1, a1));
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) S[mt] = mma(ld8(Ks + kblk(mt, 0) + 8 * kl), X0, S[mt] * decf);
+    for (int mt = 0; mt < 8; ++mt) S[mt] = mma(ld8(Ks + kblk(mt, 0) + 8 * lane), X0, S[mt] * decf);
     const frag_t<I> X1 = pack44<I>(ux(2, a2), ux(3, a3));
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) S[mt] = mma(ld8(Ks + kblk(mt, 1) + 8 * kl), X1, S[mt]);
+    for (int mt = 0; mt < 8; ++mt) S[mt] = mma(ld8(Ks + kblk(mt, 1) + 8 * lane), X1, S[mt]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) Sf[q] = pack44<I>(S[2 * q], S[2 * q + 1]);
 
