@@ -429,7 +429,40 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
     };
     const int kl = kswz(lane);
 
+    // Operands of one event, read from its slot one step ahead: the event
+    // after the current one is complete at every barrier, so its record, Cb
+    // blocks, U slice, factors and this wave's K^T blocks are requested at the
+    // end of the current step and their latency overlaps the barrier.  (For
+    // the row's last event the read slot is stale and the values unused.)
+    struct Ops {
+      int4 rc;
+      frag_t<I> cb[CB_BLOCKS];
+      half_t<I> u[4];
+      f32x4 fc[4];
+      frag_t<I> kt[4][2];
+    };
+    auto load_ops = [&](int slot) __attribute__((always_inline)) {
+      Ops o;
+      const char* sl = ring + slot * R::BYTES;
+      const I* Cs = reinterpret_cast<const I*>(sl + R::W_OFF);
+      const I* Ks = reinterpret_cast<const I*>(sl + R::K_OFF);
+      o.rc = *reinterpret_cast<const int4*>(sl + R::R_OFF);
+#pragma unroll
+      for (int b = 0; b < CB_BLOCKS; ++b) o.cb[b] = ld8(Cs + b * 512 + 8 * lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o.u[i] = *reinterpret_cast<const half_t<I>*>(sl + R::U_OFF + u_off<I>(i, n16, g4));
+        o.fc[i] = *reinterpret_cast<const f32x4*>(sl + R::F_OFF + (16 * i + 4 * g4) * 4);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) o.kt[t][ks] = ld8(Ks + kblk(4 * cw + t, ks) + 8 * kl);
+      return o;
+    };
+
     f32x4 y[4], ym[4];
+    Ops op;
     int s = 0;
     int last_c = -1;   // chunk of the last event that updated the state
     if (i0 < i1) {
@@ -444,6 +477,7 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
 #pragma unroll
         for (int q = 0; q < 4; ++q) y[i] = mma(kfrag(Ks, q, i), Sf[q], y[i]);
       }
+      op = load_ops(0);
     }
     for (int j = i0; j < i1; ++j) {
       if (j > i0) {
@@ -455,24 +489,19 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
           y[i] = cw == 0 ? ym[i] + o : o + ym[i];   // both: half 0 + half 1
         }
       }
-      const char* sl = ring + s * R::BYTES;
       char* st = stage + ((j - i0) & 1) * R::ST_BYTES;
-      const int4 rc = *reinterpret_cast<const int4*>(sl + R::R_OFF);
-      const float fin = __int_as_float(__builtin_amdgcn_readfirstlane(rc.x));
-      const float decf = __int_as_float(__builtin_amdgcn_readfirstlane(rc.y));
+      const float fin = __int_as_float(__builtin_amdgcn_readfirstlane(op.rc.x));
+      const float decf = __int_as_float(__builtin_amdgcn_readfirstlane(op.rc.y));
       // (chunk and snapshot index are clamped to their ranges, so that no
       // record content can address memory outside U and the snapshots)
-      const int sn = __builtin_amdgcn_readfirstlane(rc.z);
+      const int sn = __builtin_amdgcn_readfirstlane(op.rc.z);
       const int snapi = (sn >= 0 && sn < snap_cap) ? sn : -1;
-      const int c = min(max(__builtin_amdgcn_readfirstlane(rc.w), 0), C - 1);
+      const int c = min(max(__builtin_amdgcn_readfirstlane(op.rc.w), 0), C - 1);
       last_c = c;
-      const I* Cs = reinterpret_cast<const I*>(sl + R::W_OFF);
-      const I* Ks = reinterpret_cast<const I*>(sl + R::K_OFF);
       // the next event's K fragments of this wave's key steps, requested now
       // (its slot is complete at this barrier) so that their latency overlaps
-      // this step; for the row's last event they read a stale slot and the
-      // result goes unused.  The step below has no branches, so the loads of
-      // all its operands can be issued ahead of their products.
+      // this step.  The step below has no branches, so the loads of all its
+      // operands can be issued ahead of their products.
       const int s1 = (s + 1 == NS) ? 0 : s + 1;
       frag_t<I> kn[2][4];
       {
@@ -485,9 +514,7 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
 
       // ---- W S = Cb Y over source steps 0 (tokens 0-31) and 1 (32-63)
       const frag_t<I> Y0 = pack44<I>(y[0], y[1]), Y1 = pack44<I>(y[2], y[3]);
-      auto cbf = [&](int i, int ks) __attribute__((always_inline)) {
-        return ld8(Cs + cb_block(i, ks) * 512 + 8 * lane);
-      };
+      auto cbf = [&](int i, int ks) __attribute__((always_inline)) { return op.cb[cb_block(i, ks)]; };
       const f32x4 a0 = mma(cbf(0, 0), Y0, zero4());
       const f32x4 a1 = mma(cbf(1, 0), Y0, zero4());
       const f32x4 a2 = mma(cbf(2, 1), Y1, mma(cbf(2, 0), Y0, zero4()));
@@ -500,13 +527,11 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
       // ---- U' = U - F_in W S (Eq. (1)); X = U' 2^(gamma - g); both waves
       //      stage the same U' values
       auto ux = [&](int i, const f32x4& ai) __attribute__((always_inline)) {
-        const half_t<I> u = *reinterpret_cast<const half_t<I>*>(sl + R::U_OFF + u_off<I>(i, n16, g4));
-        const f32x4 fc = *reinterpret_cast<const f32x4*>(sl + R::F_OFF + (16 * i + 4 * g4) * 4);
         f32x4 up, x;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          up[jj] = to_f(u[jj]) - fin * ai[jj];
-          x[jj] = up[jj] * fc[jj];
+          up[jj] = to_f(op.u[i][jj]) - fin * ai[jj];
+          x[jj] = up[jj] * op.fc[i][jj];
         }
         st4<I>(reinterpret_cast<I*>(st + u_off<I>(i, n16, g4)), up);
         return x;
@@ -515,9 +540,9 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
       const frag_t<I> X1 = pack44<I>(ux(2, a2), ux(3, a3));
       // ---- own rows: S <- 2^gamma F_in S + K^T X (Eq. (2))
 #pragma unroll
-      for (int t = 0; t < 4; ++t) So[t] = mma(ld8(Ks + kblk(4 * cw + t, 0) + 8 * kl), X0, So[t] * decf);
+      for (int t = 0; t < 4; ++t) So[t] = mma(op.kt[t][0], X0, So[t] * decf);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) So[t] = mma(ld8(Ks + kblk(4 * cw + t, 1) + 8 * kl), X1, So[t]);
+      for (int t = 0; t < 4; ++t) So[t] = mma(op.kt[t][1], X1, So[t]);
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) Sfo[qq] = pack44<I>(So[2 * qq], So[2 * qq + 1]);
 
@@ -541,6 +566,7 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
         ym[i] = mma(kn[1][i], Sfo[1], mma(kn[0][i], Sfo[0], zero4()));
         yw[i * 64 + lane] = ym[i];
       }
+      op = load_ops(s1);
       s = s1;
     }
     lds_barrier();   // the last staging entry is complete
