@@ -181,7 +181,10 @@ struct DeferredWArgs {
   const void* k;        // keys [tokens][Nq][dk] (the input)
   const void* Cb;
   void* Wpk;            // [B][Emax][2][64 * 128] W per kept event and head
+                        // (fp32 intermediates; null with fp16, where the H
+                        // scan forms W S from Cb)
   void* KTpk;           // [B][Emax][128 * 64] K^T blocks per kept event
+                        // (fp16: 16-byte units in the order kswz)
   const int32_t* row_pair; const int32_t* row_ptr; const int32_t* col;
   int B, Nv, Nq, C, Emax, solve;
   const int32_t* cu; int T;   // packed sequences
