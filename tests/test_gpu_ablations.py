@@ -37,10 +37,11 @@ def _run(d, C, B, ablate=(), s0=None, **kw):
 
 
 @pytest.mark.parametrize("ablate", ABLATIONS)
-@pytest.mark.parametrize("dtype,solve,B", [("bf16", "blockadj", 1), ("f32", "exact", 2)])
+@pytest.mark.parametrize("dtype,solve,B", [("bf16", "blockadj", 1), ("f32", "exact", 2), ("bf16", "exact", 2)])
 def test_ablation_matches_default_and_oracle(ablate, dtype, solve, B):
     """B = 1 takes the two-stream schedule (CSR rows 0-3 and 4-15), B = 2 one
-    launch per stage."""
+    launch per stage; bf16 runs the Cb-operand H scan (with the exact solve:
+    Cb block (3,0) in use), fp32 the W operand."""
     import torch
     T = 64 * 11 + 19
     inp = synth.numpy_inputs(3100 + len(ablate), B, T, 16, 32, dtype=dtype, with_z=True,
