@@ -119,7 +119,9 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
   sz[B_S0T] = B * Nv * DV * DK * I;
   if (p.cu != nullptr) sz[B_CHUNKS] = (B * C + 1 + B + 1) * 4;   // valid-chunk table
   if (!sparse) {
-    sz[B_W] = B * Nv * C * L * DK * I;
+    // fp16: Cb blocks for the Cb-operand H scan; fp32: W
+    if (I == 2) sz[B_CB] = B * Nv * C * CB_BLOCKS * 512 * I;
+    else sz[B_W] = B * Nv * C * L * DK * I;
     sz[B_SNAP] = B * Nv * (size_t)p.snap_cap * DV * DK * I;
   } else {
     const bool wall = (p.ablate & (SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_CSR)) != 0;
@@ -187,8 +189,11 @@ IntraArgs intra_args(const Plan& pl, void* ws, const void* k, const void* v, con
   ia.fac = at<float>(ws, pl, B_FAC);
   ia.U = at<void>(ws, pl, B_U);
   const bool wall = sparse && (pl.ablate & (SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_CSR));
-  ia.W = (sparse && !wall) ? nullptr : at<void>(ws, pl, B_W);
-  ia.Cb = (sparse && !wall) ? at<void>(ws, pl, B_CB) : nullptr;
+  // sparse: staged Cb (W of every chunk for the W controls); dense: W, or
+  // with fp16 intermediates Cb for the Cb-operand H scan
+  const bool cb = sparse ? !wall : pl.bf16 != 0;
+  ia.W = cb ? nullptr : at<void>(ws, pl, B_W);
+  ia.Cb = cb ? at<void>(ws, pl, B_CB) : nullptr;
   ia.KT = at<void>(ws, pl, B_KT);
   ia.score_part = sparse ? at<float>(ws, pl, B_SPART) : nullptr;
   return ia;
@@ -308,6 +313,7 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   ha.s0 = s0; ha.s_final = s_final; ha.snap = at<void>(ws, pl, B_SNAP);
   ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 0;
   ha.cu = pl.cu; ha.T = pl.T;
+  ha.Cb = at<void>(ws, pl, B_CB); ha.blockadj = pl.solve == SGDN_SOLVE_BLOCKADJ;
   ha.row_lo = 0; ha.nrows = pl.Nv / 2; ha.xcd_shift = 0;
   SGDN_TRY(launch_hscan(ha, pl.bf16, s));
   mark(dbg, SGDN_EV_HSCAN, s);

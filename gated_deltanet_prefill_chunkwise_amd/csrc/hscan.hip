@@ -175,7 +175,7 @@ template <typename I> __device__ __forceinline__ int u_unit(int P) {
 template <typename E, bool SPARSE, bool CBP>
 __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanArgs p) {
   using I = inter_t<E>;
-  static_assert(!CBP || (SPARSE && sizeof(I) == 2), "Cb operand: sparse, fp16 only");
+  static_assert(!CBP || sizeof(I) == 2, "Cb operand: fp16 intermediates only");
   using R = Ring<I, sizeof(I) == 2, CBP>;
   constexpr int D = R::DEPTH, NS = R::NS;
   constexpr int NCW = CBP ? 2 : 1;         // compute waves 0 .. NCW - 1
@@ -387,12 +387,12 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
     // the compute waves' chain bounds the step: they win issue arbitration
     // against the storer wave that shares a SIMD with compute wave 0
     __builtin_amdgcn_s_setprio(3);
-    const double* P = p.P + bh * (C + 1);
+    const double* P = SPARSE ? p.P + bh * (C + 1) : nullptr;
     // initial state (all rows: the first event's Y is formed from it in
     // full by both waves), s0 decayed over the chunks before the first event
     f32x4 S[8];
     {
-      const float f0 = exp2f((float)P[(i0 < i1) ? colb[i0] : C]);
+      const float f0 = SPARSE ? exp2f((float)P[(i0 < i1) ? colb[i0] : C]) : 1.f;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
     // again rather than picked from S (a runtime pick would index S)
     f32x4 So[4];
     {
-      const float f0 = exp2f((float)P[(i0 < i1) ? colb[i0] : C]);
+      const float f0 = SPARSE ? exp2f((float)P[(i0 < i1) ? colb[i0] : C]) : 1.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
 
     if (p.s_final != nullptr) {
       // gap from the last event to the end of the sequence
-      const float fl = (i1 > i0) ? exp2f((float)(P[C] - P[last_c + 1])) : 1.f;
+      const float fl = (SPARSE && i1 > i0) ? exp2f((float)(P[C] - P[last_c + 1])) : 1.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -722,7 +722,7 @@ hipError_t launch_one(const HScanArgs& a, hipStream_t s) {
 
 hipError_t launch_hscan(const HScanArgs& a, int bf16, hipStream_t s) {
   if (bf16) {
-    if (!a.sparse) return launch_one<sgdn::bf16, false, false>(a, s);
+    if (!a.sparse) return launch_one<sgdn::bf16, false, true>(a, s);
     // W of every chunk (the deferred-W and CSR-off controls) or W S from Cb
     return a.w_by_chunk ? launch_one<sgdn::bf16, true, false>(a, s) : launch_one<sgdn::bf16, true, true>(a, s);
   }

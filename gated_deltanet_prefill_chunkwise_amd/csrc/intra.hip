@@ -277,7 +277,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
         for (int ks = 0; ks < 2; ++ks) {
           const int mt = 2 * w + mi;
           const frag_t<E> f = ld_tr44(&sK[32 * ks * KS + 16 * mt], KS, lane);
-          *reinterpret_cast<frag_t<I>*>(kt + kblk(mt, ks) + 8 * lane) = cvt8<I, E>(f);
+          // (dense with fp16 intermediates: the Cb-operand H scan reads the
+          // units in the order kswz)
+          *reinterpret_cast<frag_t<I>*>(kt + kblk(mt, ks) + 8 * (MODE == 0 && sizeof(I) == 2 ? kswz(lane) : lane)) =
+              cvt8<I, E>(f);
         }
     }
 
@@ -458,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
       // keep the U and W products apart (their accumulators would otherwise
       // be live at the same time)
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (MODE == 1 && sizeof(I) == 2) {
+      if constexpr (MODE != 2 && sizeof(I) == 2) {
         // fragment-major blocks for the H scan (W S = Cb (K S)): lane
         // (n, g) holds sources 8g .. 8g+7, which are positions 4 (g >> 1) ..
         // + 3 of lanes n + 16 (2 (g & 1)) and n + 16 (2 (g & 1) + 1) there
