@@ -120,7 +120,9 @@ typedef struct {
  *   SGDN_ABLATE_DEFERRED_W      W of every chunk is formed in the intra stage
  *                               and read by chunk in the H scan (the packed-W
  *                               path), instead of W of the kept events after
- *                               selection (Eq. (15)).  Not with cu_seqlens.
+ *                               selection (Eq. (15); with bf16 inputs the H
+ *                               scan then forms W S as Cb (K S) and W is
+ *                               never stored).  Not with cu_seqlens.
  *   SGDN_ABLATE_COMPACT_STATES  the entry state of every output group is
  *                               written out densely (decayed from the compact
  *                               snapshots) and O reads it, instead of O
@@ -240,7 +242,8 @@ int sgdn_select(const sgdn_problem* prob, const float* score, const float* gamma
                 size_t ws_bytes, void* stream);
 
 /* SparseGDN prefill, Secs. 2.2-2.7, Eqs. (5)-(25): local solve with fused
- * tail score, gate energy, selector, deferred W over CSR events,
+ * tail score, gate energy, selector, deferred W over CSR events (with bf16
+ * inputs formed inside the H scan as W S = Cb (K S)),
  * event-sparse state propagation with compact snapshots, and two-chunk
  * mapped output.  Requires Nv = 32.  Arguments as sgdn_prefill_dense, plus
  *   z             [B, T, Nv, dv] dtype output gate (pre-activation)
