@@ -8,9 +8,9 @@ for all 32 heads, as the benchmark launches it.  The fp64 oracle then checks:
   pairs are independent, so the pair's oracle run is the full problem
   restricted to those heads;
 * sparse: the selector from the GPU's own fp32 statistics (score, gamma, eta),
-  mask and tiers bit-exact, and the pair with the most events over the whole
-  sequence given the GPU's mask (pairs are independent once the mask is
-  fixed).
+  mask and tiers bit-exact, and the pairs with the most and the fewest events
+  over the whole sequence given the GPU's mask (pairs are independent once
+  the mask is fixed).
 
 Each oracle pass takes tens of seconds on the host.
 """
@@ -79,12 +79,16 @@ def test_full_size_sparse_selector_and_pair():
     assert np.array_equal(m_gpu, ref["mask"]), "mask"
     assert np.array_equal(tier.cpu().numpy()[0], ref["tier"]), "tier"
     assert int(st.cpu().numpy()[0, 0]) == int(m_gpu.sum())
-    # the pair with the most events, given the GPU's mask
-    p = int(np.argmax(m_gpu.sum(axis=1)))
-    x = _pair_inputs(d, p)
-    o_ref, S_ref = sparse.sparse_prefill(x.q, x.k, x.v, x.a, x.beta, solve="blockadj",
-                                         mask=m_gpu[None, p:p + 1])
-    eo = rel_max_err(host(o[:, :, 2 * p:2 * p + 2]), o_ref)
-    es = rel_max_err(host(S[:, 2 * p:2 * p + 2]), S_ref)
-    print(f"pair {p} ({int(m_gpu[p].sum())} events): err O {eo:.3e}  S {es:.3e}")
-    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    # the pair with the most events (a High-tier pair: its CSR row is among
+    # rows 0-3, whose H scan and O run on the caller's stream) and the pair
+    # with the fewest (a Low-tier pair: CSR rows 4-15, on the library's second
+    # stream), each given the GPU's mask
+    counts = m_gpu.sum(axis=1)
+    for p in (int(np.argmax(counts)), int(np.argmin(counts))):
+        x = _pair_inputs(d, p)
+        o_ref, S_ref = sparse.sparse_prefill(x.q, x.k, x.v, x.a, x.beta, solve="blockadj",
+                                             mask=m_gpu[None, p:p + 1])
+        eo = rel_max_err(host(o[:, :, 2 * p:2 * p + 2]), o_ref)
+        es = rel_max_err(host(S[:, 2 * p:2 * p + 2]), S_ref)
+        print(f"pair {p} ({int(counts[p])} events): err O {eo:.3e}  S {es:.3e}")
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
