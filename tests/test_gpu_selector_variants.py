@@ -106,3 +106,12 @@ def test_tail_windows_end_to_end(tail):
 @pytest.mark.parametrize("vi", range(len(VARIANTS)))
 def test_selector_variants_end_to_end(vi):
     _end_to_end(64 * 12 + 33, **VARIANTS[vi])
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 130])
+def test_tiny_sequences_end_to_end(T):
+    """One sequence of one to three chunks (ragged or whole) through the
+    single-sequence schedule (CSR rows 0-3 and 4-15 on two streams): the
+    first and last chunk are the same or adjacent anchors, every pair keeps
+    them, and the tail window may lie wholly in the zero padding."""
+    _end_to_end(T)
