@@ -147,10 +147,12 @@ def test_select_varlen_bit_exact():
         assert out["stats"][b, 5:8].tolist() == [kL, kM, kH], b
 
 
-def test_sparse_varlen_matches_each_sequence():
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_sparse_varlen_matches_each_sequence(with_s0):
     """End to end with the on-device selector: each sequence's mask is the
     oracle selector's on the GPU's own fp32 statistics for that sequence, and
-    O and the final state match the oracle given that mask."""
+    O and the final state match the oracle given that mask; with an initial
+    state per sequence, an empty sequence hands its s0 back unchanged."""
     import torch
     from gated_deltanet_prefill_chunkwise_amd import ops
     lens = SPARSE_LENS
@@ -165,8 +167,11 @@ def test_sparse_varlen_matches_each_sequence():
     mask = torch.empty((B, 16, C), dtype=torch.uint8, device="cuda")
     tier = torch.empty((B, 16), dtype=torch.uint8, device="cuda")
     dbg = ops.debug_struct(score=score, gamma=gam, eta=eta, mask=mask, tier=tier)
+    s0 = (np.random.default_rng(531).standard_normal((B, 32, 128, 128)) * 0.05).astype(np.float32) \
+        if with_s0 else None
     o, S, st = ops.prefill_sparse(d["q"], d["k"], d["v"], d["a"], d["beta"], z=d["z"],
                                   keep_budget=0.29, solve="blockadj", debug=dbg,
+                                  s0=None if s0 is None else torch.from_numpy(s0).cuda(),
                                   cu_seqlens=_cu(lens))
     torch.cuda.synchronize()
     o, S, st = host(o), host(S), st.cpu().numpy()
@@ -176,14 +181,16 @@ def test_sparse_varlen_matches_each_sequence():
         Cb = -(-n // 64)
         assert not m_gpu[i, :, Cb:].any()
         if n == 0:
-            assert st[i, 0] == 0 and not S[i].any()
+            assert st[i, 0] == 0
+            assert np.array_equal(S[i], s0[i]) if with_s0 else not S[i].any()
             continue
         ref = selector.select(sc[i, :, :Cb], gm[i, :, :Cb], et[i], keep_budget=0.29)
         assert np.array_equal(m_gpu[i, :, :Cb], ref["mask"]), i
         assert np.array_equal(t_gpu[i], ref["tier"]), i
         assert st[i, 0] == int(ref["mask"].sum())
         o_ref, S_ref = sparse.sparse_prefill(x["q"], x["k"], x["v"], x["a"], x["beta"],
-                                             solve="blockadj", mask=ref["mask"][None])
+                                             solve="blockadj", mask=ref["mask"][None],
+                                             s0=None if s0 is None else s0[i:i + 1].astype(np.float64))
         eo, es = rel_max_err(_rows(o, lens, i), o_ref), rel_max_err(S[i:i + 1], S_ref)
         print(f"seq {i} (T={n}, {st[i, 0]} events): err O {eo:.3e} S {es:.3e}")
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
