@@ -83,7 +83,7 @@ def oracle_sparse(inp, budget=0.29, solve="blockadj", mask=None, s0=None):
                                  solve=solve, mask=mask, s0=s0, return_all=True)
 
 
-def run_sparse(inp, budget=0.29, solve="blockadj", mask=None, s0=None, debug=None):
+def run_sparse(inp, budget=0.29, solve="blockadj", mask=None, s0=None, debug=None, out_dtype=None):
     import torch
     from gated_deltanet_prefill_chunkwise_amd import ops
     d = to_device(inp)
@@ -91,7 +91,9 @@ def run_sparse(inp, budget=0.29, solve="blockadj", mask=None, s0=None, debug=Non
     s0d = None if s0 is None else _t(s0.astype(np.float32))
     o, S, st = ops.prefill_sparse(d["q"], d["k"], d["v"], d["a"], d["beta"], z=d["z"],
                                   keep_budget=budget, solve=solve, mask_override=m, s0=s0d,
-                                  debug=debug)
+                                  debug=debug, out_dtype=out_dtype)
+    if out_dtype is not None:
+        assert o.dtype == out_dtype
     torch.cuda.synchronize()
     return host(o), host(S), st.cpu().numpy()
 
@@ -107,6 +109,26 @@ def test_sparse_given_mask(dtype, T, decay):
     print(f"err O {eo:.3e} S {es:.3e}  E {st[0, 0]}")
     assert eo <= TOL[dtype] and es <= TOL[dtype]
     assert st[0, 0] == int(info["mask"].sum())
+
+
+@pytest.mark.parametrize("solve", ["exact", "blockadj"])
+def test_sparse_bf16_output(solve):
+    """O in bf16 on the sparse path (the O kernel's bf16-output instance on
+    both streams of the single-sequence schedule): the bar is the fp32-output
+    bar plus the output's own rounding (at most 2^-8 of the element)."""
+    import torch
+    T = 64 * 30 + 21
+    inp = synth.numpy_inputs(synth.seed_for(2) + 11, 1, T, 16, 32, dtype="bf16", with_z=True,
+                             decay_scale=1 / 16)
+    _, _, info = oracle_sparse(inp, solve=solve)
+    o, S, _ = run_sparse(inp, solve=solve, mask=info["mask"], out_dtype=torch.bfloat16)
+    o_ref, S_ref = sparse.sparse_prefill(inp.q, inp.k, inp.v, inp.a, inp.beta, solve=solve,
+                                         mask=info["mask"])
+    rms = np.sqrt(np.mean(o_ref ** 2))
+    excess = np.abs(o - o_ref) - 2.0 ** -8 * np.abs(o_ref)
+    print(f"max excess over the output rounding {excess.max() / rms:.3e}; err S {rel_max_err(S, S_ref):.3e}")
+    assert excess.max() <= TOL["bf16"] * rms
+    assert rel_max_err(S, S_ref) <= TOL["bf16"]
 
 
 def test_sparse_random_mask_with_initial_state():
