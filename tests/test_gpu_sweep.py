@@ -1,0 +1,73 @@
+"""Parity over the keep-budget and batch sweep: one layer, bf16, T = 32768,
+Nq = 16, Nv = 32, batch 2 / 4 / 8, keep budget 0.15 / 0.29 / 0.5 / 1.0, and
+the wide spread of per-head decay scales (u_h ~ U(0, ln 16)).  The pages
+time this sweep (batch scaling and the keep-budget trade-off, Sec. 3); here
+it is a parity case at its full size, in one launch per stage as a batch
+runs.
+
+For every (batch, budget): the selector of every sequence is bit-exact
+against the oracle selector on the GPU's own fp32 statistics, the event
+count per sequence matches the mask, and in the last sequence the pair with
+the most events has O and S_final within the bar given the GPU's mask.
+"""
+import functools
+import math
+import types
+
+import numpy as np
+import pytest
+
+from gated_deltanet_prefill_chunkwise_amd import synth
+from oracle import selector, sparse
+
+from helpers import TOL, host, rel_max_err
+
+pytestmark = pytest.mark.gpu
+
+T = 32768
+NQ, NV = 16, 32
+
+
+@functools.lru_cache(maxsize=1)
+def _inputs(B):
+    return synth.torch_inputs(synth.seed_for(4, 0) + B, B, T, NQ, NV, dtype="bf16", with_z=True,
+                              u_max=math.log(16.0), device="cuda")
+
+
+@pytest.mark.parametrize("B", [2, 4, 8])
+@pytest.mark.parametrize("keep", [0.15, 0.29, 0.5, 1.0])
+def test_sweep_selector_and_pair(B, keep):
+    import torch
+    from gated_deltanet_prefill_chunkwise_amd import ops
+    d = _inputs(B)
+    C = T // 64
+    score = torch.empty((B, NV, C), device="cuda")
+    gam = torch.empty((B, NV, C), device="cuda")
+    eta = torch.empty((B, NV), device="cuda")
+    mask = torch.empty((B, NV // 2, C), dtype=torch.uint8, device="cuda")
+    tier = torch.empty((B, NV // 2), dtype=torch.uint8, device="cuda")
+    dbg = ops.debug_struct(score=score, gamma=gam, eta=eta, mask=mask, tier=tier)
+    o, S, st = ops.prefill_sparse(d["q"], d["k"], d["v"], d["a"], d["beta"], z=d["z"],
+                                  keep_budget=keep, solve="blockadj", debug=dbg)
+    torch.cuda.synchronize()
+    sc, gm, et = score.cpu().numpy(), gam.cpu().numpy(), eta.cpu().numpy()
+    m_gpu, t_gpu, st = mask.cpu().numpy(), tier.cpu().numpy(), st.cpu().numpy()
+    for b in range(B):
+        ref = selector.select(sc[b], gm[b], et[b], keep_budget=keep)
+        assert np.array_equal(m_gpu[b], ref["mask"]), f"mask of sequence {b}"
+        assert np.array_equal(t_gpu[b], ref["tier"]), f"tiers of sequence {b}"
+        assert int(st[b, 0]) == int(m_gpu[b].sum())
+    b = B - 1
+    p = int(np.argmax(m_gpu[b].sum(axis=1)))
+    f = lambda t: t[b:b + 1].float().cpu().numpy().astype(np.float64)
+    x = types.SimpleNamespace(q=f(d["q"][:, :, p:p + 1]), k=f(d["k"][:, :, p:p + 1]),
+                              v=f(d["v"][:, :, 2 * p:2 * p + 2]), a=f(d["a"][:, :, 2 * p:2 * p + 2]),
+                              beta=f(d["beta"][:, :, 2 * p:2 * p + 2]))
+    o_ref, S_ref = sparse.sparse_prefill(x.q, x.k, x.v, x.a, x.beta, solve="blockadj",
+                                         mask=m_gpu[b:b + 1, p:p + 1])
+    eo = rel_max_err(host(o[b:b + 1, :, 2 * p:2 * p + 2]), o_ref)
+    es = rel_max_err(host(S[b:b + 1, 2 * p:2 * p + 2]), S_ref)
+    keep_meas = float(m_gpu.mean())
+    print(f"B {B} keep {keep}: measured keep {keep_meas:.4f}; pair {p} of sequence {b} "
+          f"({int(m_gpu[b, p].sum())} events): err O {eo:.3e} S {es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
