@@ -3,7 +3,8 @@ Nq = 16, Nv = 32, batch 2 / 4 / 8, keep budget 0.15 / 0.29 / 0.5 / 1.0, and
 the wide spread of per-head decay scales (u_h ~ U(0, ln 16)).  The pages
 time this sweep (batch scaling and the keep-budget trade-off, Sec. 3); here
 it is a parity case at its full size, in one launch per stage as a batch
-runs.
+runs; the single 32768-token layer (keep 0.29, u_h ~ U(0, ln 4)) runs beside
+it.
 
 For every (batch, budget): the selector of every sequence is bit-exact
 against the oracle selector on the GPU's own fp32 statistics, the event
@@ -29,17 +30,22 @@ NQ, NV = 16, 32
 
 
 @functools.lru_cache(maxsize=1)
-def _inputs(B):
-    return synth.torch_inputs(synth.seed_for(4, 0) + B, B, T, NQ, NV, dtype="bf16", with_z=True,
-                              u_max=math.log(16.0), device="cuda")
+def _inputs(B, u_max):
+    return synth.torch_inputs(synth.seed_for(4 if B > 1 else 2, 0) + B, B, T, NQ, NV, dtype="bf16",
+                              with_z=True, u_max=u_max, device="cuda")
 
 
-@pytest.mark.parametrize("B", [2, 4, 8])
-@pytest.mark.parametrize("keep", [0.15, 0.29, 0.5, 1.0])
-def test_sweep_selector_and_pair(B, keep):
+# the sweep, then the single 32768-token layer at the default budget and the
+# default decay spread (one sequence: CSR rows 0-3 and 4-15 on two streams)
+CASES = [(B, keep, math.log(16.0)) for keep in (0.15, 0.29, 0.5, 1.0) for B in (2, 4, 8)] + \
+        [(1, 0.29, math.log(4.0))]
+
+
+@pytest.mark.parametrize("B,keep,u_max", CASES)
+def test_sweep_selector_and_pair(B, keep, u_max):
     import torch
     from gated_deltanet_prefill_chunkwise_amd import ops
-    d = _inputs(B)
+    d = _inputs(B, u_max)
     C = T // 64
     score = torch.empty((B, NV, C), device="cuda")
     gam = torch.empty((B, NV, C), device="cuda")
