@@ -5,7 +5,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <mutex>
 
 #include "../../include/sgdn.h"
 #include "common.h"
@@ -78,6 +77,9 @@ int check_params(const sgdn_problem* pr, const sgdn_sparse_params* sp) {
   if (!(sp->keep_budget > 0.f) || bp < 1 || bp > 10000) return SGDN_EINVAL;
   if (sp->tail != 8 && sp->tail != 16 && sp->tail != 32 && sp->tail != 64) return SGDN_EUNSUPPORTED;
   if (sp->r_window != 16) return SGDN_EUNSUPPORTED;
+  if (sp->aux_stream != nullptr && (sp->aux_events[0] == nullptr || sp->aux_events[1] == nullptr ||
+                                    sp->aux_events[0] == sp->aux_events[1]))
+    return SGDN_EINVAL;
   if ((sp->fixed_tiers != 0 && sp->fixed_tiers != 1) ||
       (sp->unit_visibility != 0 && sp->unit_visibility != 1))
     return SGDN_EINVAL;
@@ -149,8 +151,8 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
     sz[B_GSLOT] = B * NP * G * 4;
     sz[B_ESLOT] = B * (size_t)p.Emax * 4;
     if (!wall && I == 4) sz[B_WPK] = B * (size_t)p.Emax * 2 * L * DK * I;   // fp32: W per event
-    sz[B_STATS] = B * 9 * 4;
   }
+  sz[B_STATS] = B * STATS_INTS * 4;   // used when the caller passes no stats array
   size_t o = 0;
   for (int i = 0; i < B_COUNT; ++i) {
     p.off[i] = o;
@@ -199,38 +201,14 @@ IntraArgs intra_args(const Plan& pl, void* ws, const void* k, const void* v, con
   return ia;
 }
 
-// Second stream of the sparse path with its fork / join events, one set per
-// device, created on first use and kept for the life of the process.  The
-// mutex keeps the events of concurrent calls on one device apart.
-constexpr int SPLIT_ROWS = 4;   // most High-tier pairs of a sequence
-struct Side {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  std::mutex mu;
-};
-constexpr int MAX_DEVICES = 64;
-Side g_side[MAX_DEVICES];
-std::mutex g_side_init;
-
-int side_stream(Side** out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return SGDN_EHIP;
-  Side& sd = g_side[dev];
-  std::lock_guard<std::mutex> lk(g_side_init);
-  if (sd.s == nullptr) {
-    hipStream_t st = nullptr;
-    hipEvent_t f = nullptr, j = nullptr;
-    if (hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess ||
-        hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess)
-      return SGDN_EHIP;
-    sd.fork = f;
-    sd.join = j;
-    sd.s = st;
-  }
-  *out = &sd;
-  return SGDN_OK;
+// The statistics words of a call: the caller's array or the workspace's.
+int32_t* stats_words(const Plan& pl, void* ws, sgdn_stats* st) {
+  return st != nullptr ? reinterpret_cast<int32_t*>(st) : at<int32_t>(ws, pl, B_STATS);
 }
+static_assert(sizeof(sgdn_stats) == STATS_INTS * sizeof(int32_t), "stats layout");
+
+// CSR rows 0-3 hold every High-tier pair (at most 4) of a sequence.
+constexpr int SPLIT_ROWS = 4;
 
 // Packed sequences: the table of valid chunks the intra kernel walks.
 int chunk_table(const Plan& pl, void* ws, hipStream_t s) {
@@ -282,9 +260,33 @@ size_t sgdn_workspace_bytes(const sgdn_problem* prob, int sparse, const sgdn_spa
   return pl.total;
 }
 
+int sgdn_event_capacity(const sgdn_problem* prob, const sgdn_sparse_params* params, int32_t* k,
+                        int32_t* e_max) {
+  int st = check_problem(prob);
+  if (st != SGDN_OK) return st;
+  if ((st = check_params(prob, params)) != SGDN_OK) return st;
+  if (e_max == nullptr) return SGDN_EINVAL;
+  Plan pl;
+  make_plan(prob, 1, params, pl);
+  if (k != nullptr) {
+    k[0] = pl.kL; k[1] = pl.kM; k[2] = pl.kH;
+  }
+  *e_max = NP_SPARSE * pl.kH;
+  return SGDN_OK;
+}
+
+int sgdn_fp64_selftest(const double* x, const double* y, double* quot, double* root, int64_t n,
+                       void* stream) {
+  if (n < 0) return SGDN_EINVAL;
+  if (n > 0 && (!x || !y || !quot || !root)) return SGDN_EINVAL;
+  SGDN_TRY(launch_fp64_selftest(x, y, quot, root, (long long)n, static_cast<hipStream_t>(stream)));
+  return SGDN_OK;
+}
+
 int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, const void* v,
                        const float* a, const void* beta, const float* s0, void* o,
-                       float* s_final, void* ws, size_t ws_bytes, void* stream, sgdn_debug* dbg) {
+                       float* s_final, sgdn_stats* stats, void* ws, size_t ws_bytes, void* stream,
+                       sgdn_debug* dbg) {
   int st = check_problem(prob);
   if (st != SGDN_OK) return st;
   if (!q || !k || !v || !a || !beta || !o || !ws) return SGDN_EINVAL;
@@ -292,14 +294,18 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   make_plan(prob, 0, nullptr, pl);
   if (ws_bytes < pl.total) return SGDN_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* stw = stats_words(pl, ws, stats);
 
   mark(dbg, SGDN_EV_START, s);
+  SGDN_TRY(launch_stats_init(StatsInitArgs{stw, pl.B, pl.Nv, pl.C, pl.T, pl.cu, 1}, s));
   if ((st = chunk_table(pl, ws, s)) != SGDN_OK) return st;
-  SGDN_TRY(launch_intra(intra_args(pl, ws, k, v, a, beta, 0), pl.bf16, s));
+  IntraArgs ia = intra_args(pl, ws, k, v, a, beta, 0);
+  ia.stats = stw;
+  SGDN_TRY(launch_intra(ia, pl.bf16, s));
   mark(dbg, SGDN_EV_INTRA, s);
   if ((st = debug_copies(pl, ws, dbg, s, 0)) != SGDN_OK) return st;
   if (s0 != nullptr) {
-    S0PrepArgs sa{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv};
+    S0PrepArgs sa{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv, stw};
     SGDN_TRY(launch_s0prep(sa, pl.bf16, s));
   }
   EvRecArgs ea{};
@@ -315,9 +321,11 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   ha.cu = pl.cu; ha.T = pl.T;
   ha.Cb = at<void>(ws, pl, B_CB); ha.blockadj = pl.solve == SGDN_SOLVE_BLOCKADJ;
   ha.row_lo = 0; ha.nrows = pl.Nv / 2; ha.xcd_shift = 0;
+  ha.stats = stw;
   SGDN_TRY(launch_hscan(ha, pl.bf16, s));
   mark(dbg, SGDN_EV_HSCAN, s);
   OChunkArgs oa{};
+  oa.stats = stw;
   oa.q = q; oa.k = k; oa.U = at<void>(ws, pl, B_U); oa.snap = at<void>(ws, pl, B_SNAP);
   oa.s0T = s0 ? at<void>(ws, pl, B_S0T) : nullptr;
   oa.o_bf16 = prob->o_dtype == SGDN_BF16;
@@ -379,7 +387,7 @@ int sgdn_select(const sgdn_problem* prob, const float* score, const float* gamma
   sa.mask = mask; sa.tier = tier; sa.row_pair = row_pair; sa.row_ptr = row_ptr; sa.col = col;
   sa.pred = pred; sa.group_slot = group_slot; sa.event_slot = at<int32_t>(ws, pl, B_ESLOT);
   sa.Emax = NP_SPARSE * pl.kH; sa.G = pl.G;
-  sa.stats = stats; sa.mask_in = nullptr;
+  sa.stats = stats; sa.nf_clear = 1; sa.mask_in = nullptr;
   SGDN_TRY(launch_select_full(sa, s));
   return SGDN_OK;
 }
@@ -399,11 +407,15 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   if (ws_bytes < pl.total) return SGDN_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int NP = pl.Nv / 2;
+  int32_t* stw = stats_words(pl, ws, stats);
 
   // intra: local solve, U, staged Cb, tail score, gamma
   mark(dbg, SGDN_EV_START, s);
+  SGDN_TRY(launch_stats_init(StatsInitArgs{stw, pl.B, pl.Nv, pl.C, pl.T, pl.cu, 0}, s));
   if ((st = chunk_table(pl, ws, s)) != SGDN_OK) return st;
-  SGDN_TRY(launch_intra(intra_args(pl, ws, k, v, a, beta, 1), pl.bf16, s));
+  IntraArgs ia = intra_args(pl, ws, k, v, a, beta, 1);
+  ia.stats = stw;
+  SGDN_TRY(launch_intra(ia, pl.bf16, s));
   ScoreArgs sca{at<float>(ws, pl, B_SPART), at<float>(ws, pl, B_SCORE),
                 (long long)pl.B * pl.Nv * pl.C, params->tail};
   SGDN_TRY(launch_score(sca, s));
@@ -416,7 +428,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
 
   // selector and event layout
   if (mask_override == nullptr) {
-    GateArgs ga{z, params->norm_weight, at<float>(ws, pl, B_ETAP), pl.B, pl.T, pl.Nv, pl.C, pl.cu};
+    GateArgs ga{z, params->norm_weight, at<float>(ws, pl, B_ETAP), pl.B, pl.T, pl.Nv, pl.C, pl.cu, stw};
     SGDN_TRY(launch_gate(ga, pl.bf16, s));
   }
   mark(dbg, SGDN_EV_GATE, s);
@@ -437,7 +449,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   sa.col = at<int32_t>(ws, pl, B_COL); sa.pred = at<int32_t>(ws, pl, B_PRED);
   sa.group_slot = at<int32_t>(ws, pl, B_GSLOT); sa.event_slot = at<int32_t>(ws, pl, B_ESLOT);
   sa.Emax = Emax; sa.G = pl.G;
-  sa.stats = stats ? static_cast<void*>(stats) : at<void>(ws, pl, B_STATS);
+  sa.stats = stw; sa.nf_clear = 0;
   sa.mask_in = mask_override;
   SGDN_TRY(launch_select_full(sa, s));
   mark(dbg, SGDN_EV_SELECT, s);
@@ -476,7 +488,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
     return launch_evrec(ea, q);
   };
   if (s0 != nullptr) {
-    S0PrepArgs s0a{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv};
+    S0PrepArgs s0a{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv, stw};
     SGDN_TRY(launch_s0prep(s0a, pl.bf16, s));
   }
   HScanArgs ha{};
@@ -489,6 +501,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   ha.cu = nullptr; ha.T = pl.T;
   ha.row_pair = sa.row_pair; ha.row_ptr = sa.row_ptr; ha.col = sa.col; ha.event_slot = sa.event_slot;
   ha.Emax = Emax; ha.snap_cap = pl.snap_cap;
+  ha.stats = stw;
   if (csr_off) {
     ha.row_ptr = xa_all.row_ptr_all; ha.col = xa_all.col_all; ha.Emax = NP * pl.C;
   }
@@ -500,6 +513,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
   oa.cu = pl.cu; oa.row_pair = sa.row_pair;
   oa.sparse = 1; oa.pred = sa.pred; oa.group_slot = sa.group_slot; oa.snap_cap = pl.snap_cap;
+  oa.stats = stw;
 
   SGDN_TRY(events(0, NP, s));
   mark(dbg, SGDN_EV_DEFERRED, s);
@@ -518,33 +532,33 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
     return launch_expand(xa, pl.bf16, q);
   };
 
-  if (pl.B == 1 && !(pl.ablate & SGDN_ABLATE_TIER_SCHEDULE)) {
+  if (pl.B == 1 && !(pl.ablate & SGDN_ABLATE_TIER_SCHEDULE) && params->aux_stream != nullptr) {
     // CSR rows 0-3 hold every High-tier pair (at most 4), whose chains are
     // the longest and bound the H scan.  The H scan and O of rows 4-15 run
-    // on a second stream beside those of rows 0-3, so O of the shorter
-    // chains overlaps the long ones; rows 4-15 start at XCD 4, rows 0-3 at
-    // XCD 0, which keeps 32 H-scan workgroups on every XCD.  (Splitting
-    // deferred W and the event records the same way, or moving the gate
-    // energy beside the intra kernel, measured no faster: the GPU is busy
-    // in those phases.)
-    Side* sd = nullptr;
-    if ((st = side_stream(&sd)) != SGDN_OK) return st;
-    std::lock_guard<std::mutex> lk(sd->mu);
-    SGDN_TRY(hipEventRecord(sd->fork, s));
-    SGDN_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0));
+    // on the caller's second stream beside those of rows 0-3, so O of the
+    // shorter chains overlaps the long ones; rows 4-15 start at XCD 4, rows
+    // 0-3 at XCD 0, which keeps 32 H-scan workgroups on every XCD.
+    // (Splitting deferred W and the event records the same way, or moving
+    // the gate energy beside the intra kernel, measured no faster: the GPU
+    // is busy in those phases.)
+    hipStream_t aux = static_cast<hipStream_t>(params->aux_stream);
+    hipEvent_t fork = static_cast<hipEvent_t>(params->aux_events[0]);
+    hipEvent_t join = static_cast<hipEvent_t>(params->aux_events[1]);
+    SGDN_TRY(hipEventRecord(fork, s));
+    SGDN_TRY(hipStreamWaitEvent(aux, fork, 0));
     ha.row_lo = SPLIT_ROWS; ha.nrows = NP - SPLIT_ROWS; ha.xcd_shift = SPLIT_ROWS;
-    SGDN_TRY(launch_hscan(ha, pl.bf16, sd->s));
-    SGDN_TRY(expand(SPLIT_ROWS, NP - SPLIT_ROWS, sd->s));
+    SGDN_TRY(launch_hscan(ha, pl.bf16, aux));
+    SGDN_TRY(expand(SPLIT_ROWS, NP - SPLIT_ROWS, aux));
     oa.row_lo = SPLIT_ROWS; oa.nrows = NP - SPLIT_ROWS;
-    SGDN_TRY(launch_ochunk(oa, pl.bf16, sd->s));
-    SGDN_TRY(hipEventRecord(sd->join, sd->s));
+    SGDN_TRY(launch_ochunk(oa, pl.bf16, aux));
+    SGDN_TRY(hipEventRecord(join, aux));
     ha.row_lo = 0; ha.nrows = SPLIT_ROWS; ha.xcd_shift = 0;
     SGDN_TRY(launch_hscan(ha, pl.bf16, s));
     SGDN_TRY(expand(0, SPLIT_ROWS, s));
     mark(dbg, SGDN_EV_HSCAN, s);
     oa.row_lo = 0; oa.nrows = SPLIT_ROWS;
     SGDN_TRY(launch_ochunk(oa, pl.bf16, s));
-    SGDN_TRY(hipStreamWaitEvent(s, sd->join, 0));
+    SGDN_TRY(hipStreamWaitEvent(s, join, 0));
     mark(dbg, SGDN_EV_O, s);
     return SGDN_OK;
   }

@@ -244,5 +244,39 @@ __device__ __forceinline__ SeqSpan seq_span(const int32_t* cu, int b, int T) {
 }
 __device__ __forceinline__ int chunks_of(int len) { return (len + L - 1) / L; }
 
+// sgdn_stats as int32 words per sequence: E, E_max, n_tier[3], k[3],
+// n_snapshots, nonfinite_input, nonfinite_output.
+constexpr int STATS_INTS = 11;
+constexpr int ST_NF_IN = 9, ST_NF_OUT = 10;
+// nonfinite_input / nonfinite_output bits (the SGDN_NF_* values)
+constexpr int NF_Q = 1, NF_K = 2, NF_V = 4, NF_A = 8, NF_BETA = 16, NF_Z = 32, NF_S0 = 64;
+constexpr int NF_O = 1, NF_SFINAL = 2;
+
+// Nonzero iff an element of the fragment is infinite or NaN.  bf16: an
+// exponent field of all ones; with x = w & 0x7F807F80 per 32-bit word, adding
+// 0x00800080 sets bit 15 (31) exactly for such a half (no carry crosses
+// halves), so two integer operations test two elements.
+__device__ __forceinline__ uint32_t nonfinite8(const bf16x8& f) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 u = __builtin_bit_cast(u32x4, f);
+  const uint32_t m = 0x7F807F80u, o = 0x00800080u;
+  return (((u[0] & m) + o) | ((u[1] & m) + o) | ((u[2] & m) + o) | ((u[3] & m) + o)) & 0x80008000u;
+}
+__device__ __forceinline__ uint32_t nonfinite8(const f32x8& f) {
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bad |= !__builtin_isfinite(f[i]);
+  return bad ? 1u : 0u;
+}
+__device__ __forceinline__ uint32_t nonfinite1(float x) { return __builtin_isfinite(x) ? 0u : 1u; }
+
+// OR `bits` into word `field` of sequence b's statistics (vector atomics;
+// the wave-uniform test keeps the clean path to one ballot).
+__device__ __forceinline__ void flag_or(int32_t* stats, int b, int field, int bits) {
+  if (stats == nullptr) return;
+  if (__ballot(bits != 0) == 0ull) return;
+  if (bits != 0) atomicOr(stats + (size_t)b * STATS_INTS + field, bits);
+}
+
 
 }  // namespace sgdn

@@ -574,13 +574,17 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
     if (p.s_final != nullptr) {
       // gap from the last event to the end of the sequence
       const float fl = (SPARSE && i1 > i0) ? exp2f((float)(P[C] - P[last_c + 1])) : 1.f;
+      bool nfs = false;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int dk = 16 * (4 * cw + t) + 4 * g4 + j;
-          p.s_final[(bh * DK + dk) * DV + dv0 + n16] = fl * So[t][j];
+          const float x = fl * So[t][j];
+          nfs |= !__builtin_isfinite(x);
+          p.s_final[(bh * DK + dk) * DV + dv0 + n16] = x;
         }
+      flag_or(p.stats, b, ST_NF_OUT, nfs ? NF_SFINAL : 0);
     }
     return;
   }
@@ -701,13 +705,17 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
     float fl = 1.f;
     if constexpr (SPARSE)
       if (i1 > i0) fl = exp2f((float)(P[C] - P[last_c + 1]));
+    bool nfs = false;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int dk = 16 * mt + 4 * g4 + j;
-        p.s_final[(bh * DK + dk) * DV + dv0 + n16] = fl * S[mt][j];
+        const float x = fl * S[mt][j];
+        nfs |= !__builtin_isfinite(x);
+        p.s_final[(bh * DK + dk) * DV + dv0 + n16] = x;
       }
+    flag_or(p.stats, b, ST_NF_OUT, nfs ? NF_SFINAL : 0);
   }
 }
 

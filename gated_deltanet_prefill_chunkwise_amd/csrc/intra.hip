@@ -232,18 +232,25 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     const int b = cur.b, c = cur.c, pq = cur.pq, len = cur.len;
     lds_barrier();  // the previous item's readers of sK, sV, sg are done
 
-    // ---- stage keys and the first head's values; decay prefix of both heads
+    // ---- stage keys and the first head's values; decay prefix of both heads.
+    //      Inputs outside the operator's domain (non-finite k, v, beta; a
+    //      non-finite or positive) are flagged for the sequence's statistics.
     mask_rows(cur, kreg);
     mask_rows(cur, v0reg);
+    int nfbits = 0;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int q = tid + 256 * it, r = q >> 4, c8 = (q & 15) * 8;
+      if (nonfinite8(kreg[it])) nfbits |= NF_K;
+      if (nonfinite8(v0reg[it])) nfbits |= NF_V;
       *reinterpret_cast<frag_t<E>*>(&sK[r * KS + c8]) = kreg[it];
       *reinterpret_cast<frag_t<E>*>(&sV[r * KS + c8]) = v0reg[it];
     }
     if (tid < 128) {
       const int hh = tid >> 6, h = 2 * pq + hh;
       const bool live = c * L + lane < len;
+      if (live && (nonfinite1(areg) || areg > 0.f)) nfbits |= NF_A;
+      if (live && nonfinite1(breg)) nfbits |= NF_BETA;
       float x = live ? areg : 0.f;
       const float bv = live ? breg : 0.f;
       // inclusive prefix over the chunk (g, Sec. 2.1)
@@ -261,6 +268,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
       // row factors 2^(gamma - g_t) of the H scan's K^T X
       p.fac[hc * L + lane] = exp2f(__shfl(x, 63, 64) - x);
     }
+    flag_or(p.stats, b, ST_NF_IN, nfbits);
     lds_barrier();
     // next item's keys, first-head values and gates (registers are free now)
     load_kv(nxt, kreg, v0reg, 0, true);
@@ -321,11 +329,14 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
         // the first head's products are done: second head's values in, and
         // the next item's second-head values requested
         mask_rows(cur, v1reg);
+        uint32_t nfv = 0;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
           const int q = tid + 256 * it, r = q >> 4, c8 = (q & 15) * 8;
+          nfv |= nonfinite8(v1reg[it]);
           *reinterpret_cast<frag_t<E>*>(&sV[r * KS + c8]) = v1reg[it];
         }
+        flag_or(p.stats, b, ST_NF_IN, nfv ? NF_V : 0);
         load_kv(nxt, kreg, v1reg, 1, false);
       }
       // ---- diagonal blocks: C_ii = (I + M_ii)^{-1}, wave w takes block w,

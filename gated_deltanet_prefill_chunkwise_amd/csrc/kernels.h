@@ -42,6 +42,7 @@ struct IntraArgs {
   float* g; float* gamma; float* fac;
   void* U; void* W; void* Cb; void* KT;
   float* score_part;        // sparse: [B][Nv][C][8] sums of squares of U per 8-row block
+  int32_t* stats;           // [B][STATS_INTS] nonfinite_input bits K, V, A, BETA are ORed in
 };
 
 // Tail score of Eq. (9) over the last `tail` rows (8, 16, 32 or 64) from the
@@ -85,6 +86,7 @@ struct HScanArgs {
   // blocks); W S is formed as Cb (K S) from it and the K^T tile
   const void* Cb;
   int blockadj;             // Cb block (3,0) is zero (block-adjacent solve)
+  int32_t* stats;           // [B][STATS_INTS]: NF_SFINAL of nonfinite_output
 };
 
 struct OChunkArgs {
@@ -103,6 +105,7 @@ struct OChunkArgs {
   const int32_t* row_pair;    // sparse: [B][NP] head pair of each CSR row
   int row_lo, nrows;          // rows covered by this launch
   int per_chunk;              // mapped-O ablation: one chunk per workgroup
+  int32_t* stats;             // [B][STATS_INTS]: NF_Q of nonfinite_input, NF_O of nonfinite_output
 };
 
 // Compact-states ablation: every group's entry state S_2r written out densely
@@ -142,7 +145,13 @@ struct EvAllArgs {
   int B, Nv, C, Emax;
 };
 
-struct S0PrepArgs { const float* s0; void* s0T; int B, Nv; };
+struct S0PrepArgs { const float* s0; void* s0T; int B, Nv; int32_t* stats; };
+
+// Statistics words at the start of a call: the nonfinite fields cleared
+// (sparse: the selector's layout kernel writes the others); dense: every
+// field, with each chunk of each pair an event and Nv (G_b - 1) group-entry
+// states.
+struct StatsInitArgs { int32_t* stats; int B, Nv, C, T; const int32_t* cu; int dense; };
 
 // The samples of a head are split over GATE_SPLIT workgroups, each writing
 // its sum of squares to eta_part [B][Nv][GATE_SPLIT]; the tier kernel adds
@@ -151,6 +160,7 @@ constexpr int GATE_SPLIT = 8;
 struct GateArgs {
   const void* z; const float* w; float* eta_part; int B, T, Nv, C;
   const int32_t* cu;        // packed sequence offsets [B+1] or null
+  int32_t* stats;           // NF_Z of nonfinite_input (the sampled gates)
 };
 
 struct SelectArgs {
@@ -174,6 +184,7 @@ struct SelectArgs {
   int32_t* group_slot; int32_t* event_slot; int32_t* col_row;  // col_row: [B][Emax] row of each event
   int Emax, G;
   void* stats;          // sgdn_stats* or null
+  int nf_clear;         // also zero the nonfinite fields (sgdn_select)
   const uint8_t* mask_in;  // override mask [B][16][C] or null
 };
 
@@ -213,6 +224,9 @@ hipError_t launch_gate(const GateArgs& a, int bf16, hipStream_t s);
 hipError_t launch_select_full(const SelectArgs& a, hipStream_t s);
 hipError_t launch_deferred_w(const DeferredWArgs& a, int bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int bf16, hipStream_t s);
+hipError_t launch_stats_init(const StatsInitArgs& a, hipStream_t s);
+hipError_t launch_fp64_selftest(const double* x, const double* y, double* q, double* r, long long n,
+                                hipStream_t s);
 hipError_t launch_debug_u(const void* Ut, float* U, int B, int Nv, int C, int bf16, hipStream_t s);
 
 }  // namespace sgdn

@@ -153,10 +153,32 @@ __global__ __launch_bounds__(256) void s0prep_kernel(S0PrepArgs p) {
   const size_t bh = blockIdx.x;
   const float* s = p.s0 + bh * DK * DV;
   I* o = static_cast<I*>(p.s0T) + bh * DV * DK;
+  uint32_t bad = 0;
   for (int q = threadIdx.x; q < DK * DV; q += 256) {
     const int dv = q >> 7, dk = q & 127;
-    o[q] = from_f<I>(s[dk * DV + dv]);
+    const float x = s[dk * DV + dv];
+    bad |= nonfinite1(x);
+    o[q] = from_f<I>(x);
   }
+  flag_or(p.stats, (int)(bh / p.Nv), ST_NF_IN, bad ? NF_S0 : 0);
+}
+
+// Statistics at the start of a prefill call (one thread per sequence).
+__global__ __launch_bounds__(256) void stats_init_kernel(StatsInitArgs p) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= p.B) return;
+  int32_t* st = p.stats + (size_t)b * STATS_INTS;
+  if (p.dense) {
+    const int NP = p.Nv / 2;
+    const int Cb = p.cu == nullptr ? p.C : chunks_of(seq_span(p.cu, b, p.T).len);
+    const int Gb = (Cb + 1) / 2;
+    st[0] = NP * Cb;
+    st[1] = NP * p.C;
+    for (int i = 2; i < 8; ++i) st[i] = 0;
+    st[8] = p.Nv * (Gb > 1 ? Gb - 1 : 0);
+  }
+  st[ST_NF_IN] = 0;
+  st[ST_NF_OUT] = 0;
 }
 
 // eta_h = mean over the 4C samples of (w_v SiLU(z[64c + 8 + 16a, h, v]))^2,
@@ -173,16 +195,19 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_kernel(GateArgs p) {
   const SeqSpan sp = seq_span(p.cu, b, p.T);
   const int ns = 4 * chunks_of(sp.len);
   float acc = 0.f;
+  uint32_t bad = 0;
   for (int j = zb * GATE_THREADS + tid; j < ns; j += GATE_SPLIT * GATE_THREADS) {
     const int c = j >> 2, a = j & 3;
     const int pos = c * L + 8 + 16 * a;
     const int v = (73 * j) & (DV - 1);
     if (pos < sp.len) {
       const float x = to_f(z[((size_t)(sp.tok0 + pos) * p.Nv + h) * DV + v]);
+      bad |= nonfinite1(x);
       const float s = (p.w ? p.w[v] : 1.f) * (x / (1.f + __expf(-x)));
       acc += s * s;
     }
   }
+  flag_or(p.stats, b, ST_NF_IN, bad ? NF_Z : 0);
   constexpr int NWV = GATE_THREADS / 64;
   __shared__ float red[NWV];
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -393,6 +418,11 @@ __global__ __launch_bounds__(256) void debug_u_kernel(const void* Ut_, float* U)
 }
 
 }  // namespace
+
+hipError_t launch_stats_init(const StatsInitArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(stats_init_kernel, dim3((a.B + 255) / 256), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefix(const PrefixArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(prefix_kernel, dim3(a.B * a.Nv), dim3(64), 0, s, a);

@@ -146,13 +146,16 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   for (int ks = 0; ks < 4; ++ks)
     sfr[ks] = Ssrc != nullptr ? ld8(Ssrc + (size_t)dvr * DK + 32 * ks + 8 * g4) : zero_frag<I>();
 
-  // ---- stage Q rows of the group and G
+  // ---- stage Q rows of the group and G (a non-finite q is flagged)
+  uint32_t nfq = 0;
 #pragma unroll
   for (int it = 0; it < NT / 2; ++it) {
     const int q = tid + 512 * it;
     const int rr = q >> 4, c8 = (q & 15) * 8;
+    nfq |= nonfinite8(qst[it]);
     *reinterpret_cast<frag_t<I>*>(&sQ[rr * QSTR + c8]) = cvt8<I, E>(qst[it]);
   }
+  flag_or(p.stats, b, ST_NF_IN, nfq ? NF_Q : 0);
   if (tid < 128) {
     const int cc = tid >> 6;
     float gv = 0.f;
@@ -234,13 +237,20 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
 
   const float scale = 0.08838834764831845f;   // 128^-1/2
   __syncthreads();   // Q and A^T are no longer read
+  // (rows past the end of a sequence hold zeros, so the check covers only
+  // what is stored)
+  bool nfo = false;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     f32x4 v = acc[j];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) v[jj] *= scale;
+    for (int jj = 0; jj < 4; ++jj) {
+      v[jj] *= scale;
+      nfo |= !__builtin_isfinite(v[jj]);
+    }
     *reinterpret_cast<f32x4*>(&sO[(16 * j + n16) * OSTR + 16 * w + 4 * g4]) = v;
   }
+  flag_or(p.stats, b, ST_NF_OUT, nfo ? NF_O : 0);
   __syncthreads();
   // rows of 128 values: 32 consecutive lanes write one token's row
   OT* O = static_cast<OT*>(p.o);

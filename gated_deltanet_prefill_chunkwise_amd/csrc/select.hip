@@ -12,7 +12,10 @@
 //  * 2^x: x clamped to [-2000, 1000], n = rint(x), f = x - n,
 //    y = f * ln2 (binary64 nearest), Taylor sum_{i<=14} y^i / i! by Horner
 //    from i = 14 down, then ldexp(., n);
-//  * r^n for integer n: binary powering from the least significant bit.
+//  * r^n for integer n: binary powering from the least significant bit;
+//  * orderings (rank keys, pair gains) treat NaN as -infinity, so that they
+//    stay total orders (a rank is a permutation, each tier gets its count)
+//    even when non-finite inputs reach the statistics.
 #pragma clang fp contract(off)
 
 #include "common.h"
@@ -52,6 +55,8 @@ __device__ double exp2_fixed(double x) {
   for (int i = 13; i >= 0; --i) pp = pp * y + kInvFact[i];
   return ldexp(pp, (int)n);
 }
+
+__device__ __forceinline__ double ord_key(double x) { return x != x ? -__builtin_inf() : x; }
 
 __device__ double powi_fixed(double r, int n) {
   double res = 1.0, base = r;
@@ -142,11 +147,11 @@ __global__ __launch_bounds__(1024) void select_rank_kernel(SelectArgs p) {
   const double n0 = snorm[0], n1 = snorm[1];
   for (int c = tid; c < C; c += 1024) {
     if (KEY) {
-      sq[c] = (double)key[c];
+      sq[c] = ord_key((double)key[c]);
     } else {
       const double t0 = n0 > 0.0 ? (double)s0[c] / n0 : 0.0;
       const double t1 = n1 > 0.0 ? (double)s1[c] / n1 : 0.0;
-      sq[c] = 0.5 * (t0 + t1);
+      sq[c] = ord_key(0.5 * (t0 + t1));
     }
   }
   __syncthreads();
@@ -270,8 +275,8 @@ __global__ __launch_bounds__(1024) void select_tier_kernel(SelectArgs p) {
   const double mum = wave_sum(glm) / NP;
   const double muh = wave_sum(gmh) / NP;
   if (lane < NP) {
-    sxm[lane] = mum > 0.0 ? glm / mum : 0.0;
-    sxh[lane] = muh > 0.0 ? gmh / muh : 0.0;
+    sxm[lane] = ord_key(mum > 0.0 ? glm / mum : 0.0);
+    sxh[lane] = ord_key(muh > 0.0 ? gmh / muh : 0.0);
   }
   __syncthreads();
 
@@ -491,7 +496,8 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
     }
   }
   if (tid == 0 && p.stats != nullptr) {
-    int32_t* st = static_cast<int32_t*>(p.stats) + b * 9;
+    int32_t* st = static_cast<int32_t*>(p.stats) + (size_t)b * STATS_INTS;
+    if (p.nf_clear) st[ST_NF_IN] = st[ST_NF_OUT] = 0;
     int nt[3] = {0, 0, 0};
     for (int q = 0; q < NP; ++q) nt[s_tier[q]]++;
     st[0] = s_rowptr[NP];
@@ -502,7 +508,27 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
   }
 }
 
+// Diagnostic: this file's binary64 division and square root (the forms the
+// selector's decisions are computed with), element by element.
+__global__ __launch_bounds__(256) void fp64_selftest_kernel(const double* x, const double* y, double* q,
+                                                            double* r, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const double a = x[i];
+    q[i] = a / y[i];
+    r[i] = sqrt(a);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_fp64_selftest(const double* x, const double* y, double* q, double* r, long long n,
+                                hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const long long blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(fp64_selftest_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0,
+                     s, x, y, q, r, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_select_full(const SelectArgs& a, hipStream_t s) {
   if (a.mask_in == nullptr) {

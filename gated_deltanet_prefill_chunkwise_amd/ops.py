@@ -14,8 +14,8 @@ LIB_PATH = os.path.join(HERE, "libsgdn.so")
 
 SGDN_F32, SGDN_BF16 = 0, 1
 SOLVES = {"exact": 0, "blockadj": 1}
-EXPORTS = ("sgdn_workspace_bytes", "sgdn_prefill_dense", "sgdn_select",
-           "sgdn_prefill_sparse", "sgdn_decode_step", "sgdn_status_string")
+EXPORTS = ("sgdn_workspace_bytes", "sgdn_event_capacity", "sgdn_prefill_dense", "sgdn_select",
+           "sgdn_prefill_sparse", "sgdn_decode_step", "sgdn_status_string", "sgdn_fp64_selftest")
 
 
 class Problem(ctypes.Structure):
@@ -28,7 +28,8 @@ class SparseParams(ctypes.Structure):
     _fields_ = [("keep_budget", ctypes.c_float), ("tail", ctypes.c_int32),
                 ("r_window", ctypes.c_int32), ("norm_weight", ctypes.c_void_p),
                 ("fixed_tiers", ctypes.c_int32), ("unit_visibility", ctypes.c_int32),
-                ("rank_key", ctypes.c_void_p), ("ablate", ctypes.c_int32)]
+                ("rank_key", ctypes.c_void_p), ("ablate", ctypes.c_int32),
+                ("aux_stream", ctypes.c_void_p), ("aux_events", ctypes.c_void_p * 2)]
 
 
 ABLATE = {"deferred_w": 1, "compact_states": 2, "csr": 4, "mapped_o": 8,
@@ -38,7 +39,15 @@ ABLATE = {"deferred_w": 1, "compact_states": 2, "csr": 4, "mapped_o": 8,
 class Stats(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int32), ("E_max", ctypes.c_int32),
                 ("n_tier", ctypes.c_int32 * 3), ("k", ctypes.c_int32 * 3),
-                ("n_snapshots", ctypes.c_int32)]
+                ("n_snapshots", ctypes.c_int32), ("nonfinite_input", ctypes.c_int32),
+                ("nonfinite_output", ctypes.c_int32)]
+
+
+# bits of Stats.nonfinite_input / nonfinite_output (SGDN_NF_*)
+NF_INPUT = {"q": 1, "k": 2, "v": 4, "a": 8, "beta": 16, "z": 32, "s0": 64}
+NF_OUTPUT = {"o": 1, "s_final": 2}
+STAT_FIELDS = ("E", "E_max", "n_low", "n_medium", "n_high", "k_low", "k_medium", "k_high",
+               "n_snapshots", "nonfinite_input", "nonfinite_output")
 
 
 class Debug(ctypes.Structure):
@@ -75,7 +84,12 @@ def lib():
         SP = ctypes.POINTER(SparseParams)
         L.sgdn_workspace_bytes.argtypes = [P, i32, SP]
         L.sgdn_workspace_bytes.restype = sz
-        L.sgdn_prefill_dense.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.sgdn_event_capacity.argtypes = [P, SP, ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_int32)]
+        L.sgdn_event_capacity.restype = i32
+        L.sgdn_fp64_selftest.argtypes = [vp, vp, vp, vp, ctypes.c_int64, vp]
+        L.sgdn_fp64_selftest.restype = i32
+        L.sgdn_prefill_dense.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.sgdn_prefill_dense.restype = i32
         L.sgdn_select.argtypes = [P, vp, vp, vp, SP, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sgdn_select.restype = i32
@@ -137,17 +151,73 @@ def problem(q, v, solve="exact", out_dtype=None, cu_seqlens=None, max_seqlen=Non
 
 
 def sparse_params(keep_budget=0.29, norm_weight=None, tail=16, r_window=16, fixed_tiers=False,
-                  unit_visibility=False, rank_key=None, ablate=()) -> SparseParams:
+                  unit_visibility=False, rank_key=None, ablate=(), aux=None) -> SparseParams:
     """Selector parameters; ``rank_key`` (device fp32 [B, Nv/2, C]) and the
     flags are the selector ablations, ``ablate`` names kernel-pipeline
-    ablations (keys of ABLATE), all described in include/sgdn.h."""
+    ablations (keys of ABLATE), all described in include/sgdn.h.  ``aux`` is
+    an (aux stream, fork event, join event) triple of torch objects, or None
+    for the one-stream schedule."""
     bits = 0
     for name in ablate:
         bits |= ABLATE[name]
-    return SparseParams(float(keep_budget), tail, r_window,
-                        None if norm_weight is None else norm_weight.data_ptr(),
-                        int(bool(fixed_tiers)), int(bool(unit_visibility)),
-                        None if rank_key is None else rank_key.data_ptr(), bits)
+    p = SparseParams(float(keep_budget), tail, r_window,
+                     None if norm_weight is None else norm_weight.data_ptr(),
+                     int(bool(fixed_tiers)), int(bool(unit_visibility)),
+                     None if rank_key is None else rank_key.data_ptr(), bits)
+    if aux is not None:
+        stream, ev0, ev1 = aux
+        p.aux_stream = stream.cuda_stream
+        p.aux_events[0] = ev0.cuda_event
+        p.aux_events[1] = ev1.cuda_event
+    return p
+
+
+_aux = {}
+
+
+def aux_stream(device=None):
+    """The binding's second stream and fork / join events for ``device``
+    (created once per device and kept; the library itself holds none).  The
+    stream has the default priority; the events are recorded once so that
+    their handles exist."""
+    import torch
+    idx = None if device is None else torch.device(device).index
+    dev = torch.device("cuda", torch.cuda.current_device() if idx is None else idx)
+    if dev not in _aux:
+        with torch.cuda.device(dev):
+            st = torch.cuda.Stream(device=dev)
+            evs = (torch.cuda.Event(enable_timing=False), torch.cuda.Event(enable_timing=False))
+            for e in evs:
+                e.record(st)
+            st.synchronize()
+        _aux[dev] = (st, *evs)
+    return _aux[dev]
+
+
+def event_capacity(prob: Problem, params: SparseParams):
+    """((k_L, k_M, k_H), E_max per sequence) as the library sizes them."""
+    k = (ctypes.c_int32 * 3)()
+    e = ctypes.c_int32()
+    st = lib().sgdn_event_capacity(ctypes.byref(prob), ctypes.byref(params), k, ctypes.byref(e))
+    if st != 0:
+        raise SgdnError(st, "sgdn_event_capacity")
+    return tuple(k), int(e.value)
+
+
+def fp64_selftest(x, y, stream=None):
+    """Run the selector's compiled binary64 division and square root on device
+    fp64 tensors; returns (x / y, sqrt(x)) as device tensors."""
+    import torch
+    _check(x, "x", torch.float64)
+    _check(y, "y", torch.float64)
+    if x.shape != y.shape:
+        raise ValueError("x and y must have the same shape")
+    q = torch.empty_like(x)
+    r = torch.empty_like(x)
+    st = lib().sgdn_fp64_selftest(_ptr(x), _ptr(y), _ptr(q), _ptr(r), x.numel(), _stream(stream))
+    if st != 0:
+        raise SgdnError(st, "sgdn_fp64_selftest")
+    return q, r
 
 
 def workspace_bytes(prob: Problem, sparse: bool, params: SparseParams | None = None) -> int:
@@ -164,6 +234,13 @@ def _check(t, name, dtype=None):
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stats_check(stats, B):
+    import torch
+    _check(stats, "stats", torch.int32)
+    if stats is not None and tuple(stats.shape) != (B, STATS_INTS):
+        raise ValueError(f"stats must be int32 [{B}, {STATS_INTS}]")
 
 
 def _workspace(nbytes, device, workspace):
@@ -186,11 +263,13 @@ def debug_struct(events=None, **bufs) -> Debug:
 
 def prefill_dense(q, k, v, a, beta, s0=None, solve="exact", want_state=True, o=None,
                   s_final=None, workspace=None, debug=None, stream=None, out_dtype=None,
-                  cu_seqlens=None, max_seqlen=None):
+                  cu_seqlens=None, max_seqlen=None, stats=None):
     """Dense GDN-core prefill; returns (o, s_final).
 
     o is fp32 unless ``out_dtype`` (or a given ``o``) says otherwise.  With
     ``cu_seqlens`` the inputs hold packed sequences (see ``batch_shape``).
+    ``stats`` (int32 [B, STATS_INTS] on the device) receives the per-sequence
+    statistics, including the non-finite flags.
     """
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta")):
@@ -207,14 +286,15 @@ def prefill_dense(q, k, v, a, beta, s0=None, solve="exact", want_state=True, o=N
         o = torch.empty(v.shape, dtype=out_dtype, device=v.device)
     if want_state and s_final is None:
         s_final = torch.empty((B, Nv, q.shape[3], dv), dtype=torch.float32, device=q.device)
+    _stats_check(stats, B)
     nbytes = workspace_bytes(prob, False)
     if nbytes == 0:
         raise SgdnError(-2, "sgdn_workspace_bytes")
     ws = _workspace(nbytes, q.device, workspace)
     dbg = None if debug is None else ctypes.byref(debug)
     st = lib().sgdn_prefill_dense(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
-                                  _ptr(beta), _ptr(s0), _ptr(o), _ptr(s_final), _ptr(ws),
-                                  ws.numel(), _stream(stream), dbg)
+                                  _ptr(beta), _ptr(s0), _ptr(o), _ptr(s_final), _ptr(stats),
+                                  _ptr(ws), ws.numel(), _stream(stream), dbg)
     if st != 0:
         raise SgdnError(st, "sgdn_prefill_dense")
     return o, s_final
@@ -283,13 +363,13 @@ def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None, cu_
     ws = _workspace(nbytes, score.device, workspace)
     NP, G = Nv // 2, (C + 1) // 2
     dev = score.device
-    kH = tier_counts_host(C, keep_budget)[2]
+    _, e_max = event_capacity(prob, params)
     out = dict(
         mask=torch.empty((B, NP, C), dtype=torch.uint8, device=dev),
         tier=torch.empty((B, NP), dtype=torch.uint8, device=dev),
         row_pair=torch.empty((B, NP), dtype=torch.int32, device=dev),
         row_ptr=torch.empty((B, NP + 1), dtype=torch.int32, device=dev),
-        col=torch.full((B, NP * kH), -1, dtype=torch.int32, device=dev),
+        col=torch.full((B, e_max), -1, dtype=torch.int32, device=dev),
         pred=torch.empty((B, NP, G), dtype=torch.int32, device=dev),
         group_slot=torch.empty((B, NP, G), dtype=torch.int32, device=dev),
         stats=torch.zeros((B, STATS_INTS), dtype=torch.int32, device=dev),
@@ -308,11 +388,14 @@ def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
                    mask_override=None, s0=None, norm_weight=None, want_state=True, o=None,
                    s_final=None, stats=None, workspace=None, debug=None, stream=None,
                    out_dtype=None, cu_seqlens=None, max_seqlen=None, tail=16, fixed_tiers=False,
-                   unit_visibility=False, rank_key=None, ablate=()):
-    """SparseGDN prefill; returns (o, s_final, stats[B, 9] int32).
+                   unit_visibility=False, rank_key=None, ablate=(), aux=True):
+    """SparseGDN prefill; returns (o, s_final, stats[B, STATS_INTS] int32).
 
     o is fp32 unless ``out_dtype`` (or a given ``o``) says otherwise.  With
     ``cu_seqlens`` the inputs hold packed sequences (see ``batch_shape``).
+    ``aux``: True uses the binding's second stream for the batch-1 schedule
+    (``aux_stream``), False runs every kernel on ``stream``, or a (stream,
+    event, event) triple of the caller's.
     """
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta"), (z, "z")):
@@ -330,8 +413,13 @@ def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
     if rank_key is not None and tuple(rank_key.shape) != (prob.batch, v.shape[2] // 2,
                                                          -(-prob.seqlen // 64)):
         raise ValueError("rank_key must be [B, Nv/2, C]")
+    if aux is True:
+        aux = aux_stream(q.device) if prob.batch == 1 else None
+    elif aux is False:
+        aux = None
     params = sparse_params(keep_budget, norm_weight, tail=tail, fixed_tiers=fixed_tiers,
-                           unit_visibility=unit_visibility, rank_key=rank_key, ablate=ablate)
+                           unit_visibility=unit_visibility, rank_key=rank_key, ablate=ablate,
+                           aux=aux)
     B, Nv, dv = prob.batch, v.shape[2], v.shape[3]
     if o is None:
         o = torch.empty(v.shape, dtype=out_dtype, device=v.device)
@@ -339,6 +427,7 @@ def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
         s_final = torch.empty((B, Nv, q.shape[3], dv), dtype=torch.float32, device=q.device)
     if stats is None:
         stats = torch.zeros((B, STATS_INTS), dtype=torch.int32, device=q.device)
+    _stats_check(stats, B)
     nbytes = workspace_bytes(prob, True, params)
     if nbytes == 0:
         raise SgdnError(-2, "sgdn_workspace_bytes")
@@ -352,18 +441,3 @@ def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
         raise SgdnError(st, "sgdn_prefill_sparse")
     return o, s_final, stats
 
-
-def tier_counts_host(C: int, keep_budget: float = 0.29):
-    """(k_L, k_M, k_H) as the library computes them (sizes of the col array)."""
-    import math
-    bp = int(math.floor(float(ctypes.c_float(keep_budget).value) * 10000.0 + 0.5))
-    if C == 1:
-        return (1, 1, 1)
-    out = []
-    for pct in (8, 30, 95):
-        if bp <= 2900:
-            num, den = pct * bp * C, 290000
-        else:
-            num, den = C * (710000 - (100 - pct) * (10000 - bp)), 710000
-        out.append(min(max((2 * num + den) // (2 * den), 2), C))
-    return tuple(out)

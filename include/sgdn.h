@@ -18,19 +18,39 @@
  * - Value head h reads query/key head h / (Nv / Nq).  Supported: d = dv = 128,
  *   Nv = 2 * Nq (value heads 2p and 2p+1 share query/key head p; Sec. 2.1).
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
- *   ordered after prior work on it.  Calls are stateless and reentrant; two
- *   calls must not share a workspace concurrently.
- * - sgdn_prefill_sparse with batch 1 runs part of its work on a second
- *   stream of the library's (one per device, created by the first such call
- *   and kept until the process ends), forked from and joined back to
- *   `stream` with events: later work on `stream` still sees every output.
- *   To capture such a call in a HIP graph, make one call before capturing,
- *   so that the stream exists.
+ *   ordered after prior work on it.  The library keeps no state between
+ *   calls (no streams, events or buffers of its own): calls are reentrant,
+ *   except that two calls must not share a workspace, a stats array or the
+ *   auxiliary events of sgdn_sparse_params concurrently.
+ * - sgdn_prefill_sparse with batch 1 can run part of its work on a second,
+ *   caller-owned stream (sgdn_sparse_params.aux_stream, forked from and
+ *   joined back to `stream` with the caller's two events): later work on
+ *   `stream` still sees every output.  Without it, every kernel runs on
+ *   `stream`.  Both forms can be captured in a HIP graph.
  * - Errors: a negative sgdn_status is returned BEFORE anything is enqueued
  *   when an argument is invalid; SGDN_EHIP reports a failed launch.
- *   Data-dependent conditions are reported through sgdn_stats.
- * - Inputs must be finite and the decay must satisfy a <= 0 (a is the log2
- *   retention; a > 0 is outside the operator's domain).
+ *   Data-dependent conditions are reported through sgdn_stats (below),
+ *   including inputs outside the operator's domain.
+ * - Domain (Sec. 2.1): the decay must satisfy a <= 0 (a is the log2
+ *   retention; a > 0 is outside the operator's domain), every input must be
+ *   finite, and q and k are expected to be L2-normalised rows (the
+ *   operator's convention; the kernels do not normalise them, and their
+ *   fp16 operand copies below rely on |q_i|, |k_i| <= 1).  Violations are
+ *   not refused up front (that would need a pass over the inputs); the
+ *   kernels flag them in sgdn_stats.nonfinite_input / nonfinite_output.
+ * - Precision with bf16 inputs: the matrix products run on the fp16 / bf16
+ *   matrix cores with fp32 accumulation, and the stage-to-stage
+ *   intermediates (U, U', the staged coefficients Cb, the key tiles, the
+ *   compact state snapshots, and the state slices fed to the products) are
+ *   stored as fp16: 11-bit significands, so each rounding adds about 2^-12
+ *   relative error; measured end to end, max |o - o_ref| / rms(o_ref) is
+ *   2e-3 to 6e-3 at the workload's decays (fp32 inputs: every intermediate
+ *   is fp32, about 1e-5).  fp16 holds magnitudes up to 65504: an
+ *   intermediate beyond that (for example |v| in the thousands with beta
+ *   near 1, or a state that large) becomes infinite, which surfaces as a
+ *   non-finite o or s_final and sets nonfinite_output.  The state and its
+ *   accumulation are always fp32.  A bf16 o adds its own rounding (up to
+ *   2^-8 of each element).
  * - T need not be a multiple of 64: the last chunk is padded with tokens
  *   that have a = 0, beta = 0, q = k = v = 0; their outputs are not written.
  * - Packed variable-length batches: with sgdn_problem.cu_seqlens set, the B
@@ -69,12 +89,7 @@ typedef enum { SGDN_SOLVE_EXACT = 0, SGDN_SOLVE_BLOCKADJ = 1 } sgdn_solve;
 /* Problem shape.  dtype applies to q, k, v, beta and z; o_dtype to o (a, s0
  * and s_final are always fp32).  solve selects the local Delta solve
  * (Sec. 2.3): SGDN_SOLVE_EXACT = M^{-1}, SGDN_SOLVE_BLOCKADJ = the 7-block
- * form of Eqs. (7)-(8).
- * Precision: with bf16 inputs the matrix products run on bf16 MFMA with fp32
- * accumulation; every fp32-valued operand that the outputs are sensitive to
- * (U, U', the decayed q.k matrix, the state read by O, the update X) enters
- * as a bf16 hi + lo pair, so o and s_final carry fp32-grade error.  A bf16 o
- * adds its own rounding (up to 2^-8 of each element). */
+ * form of Eqs. (7)-(8).  Precision: see the conventions above. */
 typedef struct {
   int32_t batch, seqlen, n_qk, n_v, d_k, d_v;
   int32_t dtype;    /* sgdn_dtype of q, k, v, beta, z */
@@ -112,6 +127,14 @@ typedef struct {
   int32_t unit_visibility;
   const float* rank_key;
   int32_t ablate;   /* SGDN_ABLATE_* bits, 0 for the method as defined */
+  /* Optional second stream for the batch-1 schedule: a hipStream_t of the
+   * caller's (default priority) and two hipEvent_t of the caller's (created
+   * with hipEventDisableTiming is enough), used to fork the H scan and O of
+   * CSR rows 4-15 onto aux_stream beside those of rows 0-3 on `stream` and
+   * to join them back.  NULL aux_stream: one stream (same outputs).  The
+   * events must not be used by another call at the same time. */
+  void* aux_stream;
+  void* aux_events[2];
 } sgdn_sparse_params;
 
 /* Kernel-pipeline ablations (Sec. 3.6, Table 6): reference paths that undo
@@ -154,14 +177,32 @@ enum {
   SGDN_ABLATE_TIER_SCHEDULE = 16
 };
 
-/* Per-sequence statistics written on the device. */
+/* Per-sequence statistics written on the device (every field is written by
+ * each call that is given the array).  The dense path reports every chunk of
+ * every head pair as an event: E = NP C_b (C_b the sequence's chunks),
+ * E_max = NP C, n_tier and k zero, n_snapshots = Nv (G_b - 1) group-entry
+ * states.
+ * nonfinite_input: bits of the inputs in which the kernels met a value
+ *   outside the operator's domain (Sec. 2.1): SGDN_NF_Q, _K, _V, _A (a
+ *   non-finite or a > 0), _BETA, _Z (the gate samples the selector reads),
+ *   _S0.  0 for a clean call.
+ * nonfinite_output: SGDN_NF_O if o holds a non-finite value, SGDN_NF_SFINAL
+ *   if s_final does (with finite inputs: an fp16 intermediate overflowed). */
 typedef struct {
   int32_t E;            /* kept events (row_ptr[NP])                          */
   int32_t E_max;        /* capacity 16 * k_H                                  */
   int32_t n_tier[3];    /* head pairs per tier: [0] Low, [1] Medium, [2] High */
   int32_t k[3];         /* events per pair in each tier: k_L, k_M, k_H        */
   int32_t n_snapshots;  /* compact state snapshots written by the H scan      */
+  int32_t nonfinite_input;
+  int32_t nonfinite_output;
 } sgdn_stats;
+
+enum {
+  SGDN_NF_Q = 1, SGDN_NF_K = 2, SGDN_NF_V = 4, SGDN_NF_A = 8, SGDN_NF_BETA = 16,
+  SGDN_NF_Z = 32, SGDN_NF_S0 = 64,          /* nonfinite_input bits  */
+  SGDN_NF_O = 1, SGDN_NF_SFINAL = 2         /* nonfinite_output bits */
+};
 
 /* Optional DEVICE outputs of intermediate stages (tests and diagnostics).
  * Any member may be NULL; pass NULL for the whole struct in production. */
@@ -201,6 +242,16 @@ enum {
 size_t sgdn_workspace_bytes(const sgdn_problem* prob, int sparse,
                             const sgdn_sparse_params* params);
 
+/* Event capacity of the selector (Sec. 2.4.3, Eq. (13); Sec. 2.5: the CSR
+ * column array holds at most E_max = 16 k_H events per sequence, and the
+ * device-side E never exceeds it).  Writes k = (k_L, k_M, k_H) for C =
+ * ceil(seqlen / 64) chunks at params->keep_budget (host memory, may be NULL)
+ * and *e_max = 16 k_H, the per-sequence length of sgdn_select's col array.
+ * Packed sequences with fewer chunks select fewer events.  Returns a negative
+ * status for an invalid problem or parameters (nothing written). */
+int sgdn_event_capacity(const sgdn_problem* prob, const sgdn_sparse_params* params,
+                        int32_t* k, int32_t* e_max);
+
 /* Dense GDN-core prefill, Sec. 2.1, Eqs. (1)-(4), with the local system of
  * Sec. 2.3, Eqs. (5)-(6) solved exactly or by the 7-block form.
  *   q, k    [B, T, Nq, d]   dtype
@@ -210,12 +261,13 @@ size_t sgdn_workspace_bytes(const sgdn_problem* prob, int sparse,
  *   s0      [B, Nv, d, dv]  fp32 initial state, or NULL for zero
  *   o       [B, T, Nv, dv]  o_dtype, output before norm / gate / projection
  *   s_final [B, Nv, d, dv]  fp32 final state, or NULL
+ *   stats   [B] device statistics (see sgdn_stats), or NULL
  *   ws      device workspace of at least sgdn_workspace_bytes(prob, 0, NULL)
  *   debug   optional stage outputs (may be NULL) */
 int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k,
                        const void* v, const float* a, const void* beta,
-                       const float* s0, void* o, float* s_final, void* ws,
-                       size_t ws_bytes, void* stream, sgdn_debug* debug);
+                       const float* s0, void* o, float* s_final, sgdn_stats* stats,
+                       void* ws, size_t ws_bytes, void* stream, sgdn_debug* debug);
 
 /* Dynamic event selection and CSR event layout, Sec. 2.4, Eqs. (10)-(14),
  * Sec. 2.5, Eq. (16), from the fp32 selection statistics of one batch.
@@ -283,6 +335,16 @@ int sgdn_decode_step(const sgdn_problem* prob, const void* q, const void* k,
 
 /* Static description of a status code. */
 const char* sgdn_status_string(int status);
+
+/* Diagnostic: the selector's decisions are bit-reproducible only if the
+ * device's binary64 division and square root round correctly (Sec. 2.4,
+ * Eqs. (10)-(14) are evaluated with them).  This runs the selector's own
+ * compiled forms of both operations: quot[i] = x[i] / y[i] and
+ * root[i] = sqrt(x[i]) for i < n, so that callers can compare them with a
+ * correctly rounded host.  All arrays DEVICE [n]; n >= 0.  SGDN_EINVAL for
+ * a null pointer with n > 0. */
+int sgdn_fp64_selftest(const double* x, const double* y, double* quot, double* root,
+                       int64_t n, void* stream);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,8 @@ this implementation's reading, stated once and followed on both sides:
   sums p_l = (((0 + x[l]) + x[l+64]) + x[l+128]) + ...  for l < 64, combined
   pairwise: for w = 32, 16, 8, 4, 2, 1: p_l <- p_l + p_{l+w} for l < w;
   the result is p_0.
-* exp2(x): x is first clamped to [-2000, 1000]; n = round-half-even(x),
+* exp2(x): x is first clamped to [-2000, 1000] (a NaN x becomes 1000, as
+  fmin / fmax treat it); n = round-half-even(x),
   f = x - n (exact),
   y = f * LN2 with LN2 the binary64 value nearest ln 2; the Taylor polynomial
   sum_{i=0}^{14} y^i / i! is evaluated by Horner's rule from i = 14 down

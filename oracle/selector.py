@@ -137,6 +137,13 @@ def lifetime(r: float, C: int) -> float:
     return r * (1.0 - powi(r, n)) / (1.0 - r)
 
 
+def _ord(x: float) -> float:
+    """Ordering key of a binary64 value: NaN counts as -infinity (a reading:
+    the page's orderings assume finite statistics; this keeps every ranking a
+    total order when a non-finite input reaches them)."""
+    return -math.inf if x != x else x
+
+
 def _argmax_first(values):
     best, bi = None, 0
     for i, x in enumerate(values):
@@ -189,7 +196,7 @@ def select(score, gamma, eta, keep_budget: float = 0.29, window: int = 16,
         for c in range(C):
             t0 = s[h0, c] / norms[h0] if norms[h0] > 0.0 else 0.0
             t1 = s[h1, c] / norms[h1] if norms[h1] > 0.0 else 0.0
-            qv.append(0.5 * (t0 + t1))
+            qv.append(_ord(0.5 * (t0 + t1)))
         cand = sorted(range(1, C - 1), key=lambda c: (-qv[c], c))
         for r, c in enumerate(cand):
             rank[p, c] = r
@@ -217,7 +224,8 @@ def select(score, gamma, eta, keep_budget: float = 0.29, window: int = 16,
                        + (L_h[h1] * G_h[h1]) * band_sum(h1, p, kM, kH))
 
     # Eqs. (13)-(14): normalised gains, High count first, then Medium.
-    xM, xH = _normalise(gain_lm), _normalise(gain_mh)
+    xM = [_ord(x) for x in _normalise(gain_lm)]
+    xH = [_ord(x) for x in _normalise(gain_mh)]
     order_h = sorted(range(Np), key=lambda p: (-xH[p], p))
     vals_h = [xH[p] for p in order_h]
     if fixed_tiers:
@@ -243,7 +251,7 @@ def select(score, gamma, eta, keep_budget: float = 0.29, window: int = 16,
         key = np.asarray(rank_key, np.float32).astype(np.float64)
         keep_rank = np.full((Np, C), -1, dtype=np.int64)
         for p in range(Np):
-            cand = sorted(range(1, C - 1), key=lambda c: (-key[p, c], c))
+            cand = sorted(range(1, C - 1), key=lambda c: (-_ord(key[p, c]), c))
             for r, c in enumerate(cand):
                 keep_rank[p, c] = r
     mask = np.zeros((Np, C), dtype=np.uint8)

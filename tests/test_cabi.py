@@ -27,8 +27,34 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["sgdn_workspace_bytes", "sgdn_prefill_dense", "sgdn_select", "sgdn_prefill_sparse",
-         "sgdn_status_string", "sgdn_decode_step"])
+        ["sgdn_workspace_bytes", "sgdn_event_capacity", "sgdn_prefill_dense", "sgdn_select",
+         "sgdn_prefill_sparse", "sgdn_status_string", "sgdn_decode_step", "sgdn_fp64_selftest"])
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """The binding's ctypes mirrors of the header's structs have the sizes and
+    field offsets a C compiler gives them (stats: 11 int32 words)."""
+    from gated_deltanet_prefill_chunkwise_amd import ops
+    assert ops.STATS_INTS == 11 and len(ops.STAT_FIELDS) == ops.STATS_INTS
+    structs = {"sgdn_problem": ops.Problem, "sgdn_sparse_params": ops.SparseParams,
+               "sgdn_stats": ops.Stats, "sgdn_debug": ops.Debug}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "sgdn.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True,
+                                                        text=True, check=True).stdout.splitlines())
+    for cname, py in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert int(got[f"{cname}.{f}"]) == getattr(py, f).offset, f"{cname}.{f}"
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -64,6 +90,35 @@ def test_workspace_bytes(L):
     assert ops.workspace_bytes(p, True, ops.sparse_params(keep_budget=1.5)) == 0
 
 
+def test_event_capacity(L):
+    """k_l of Eq. (13) and E_max = 16 k_H come from the library (the binding
+    does none of that arithmetic); values as the oracle pins them."""
+    from gated_deltanet_prefill_chunkwise_amd import ops
+    from oracle import selector
+    for T, budget in ((4096, 0.29), (32768, 0.29), (131072, 0.29), (64 * 35, 0.29),
+                      (32768, 0.15), (32768, 0.5), (32768, 1.0), (64, 0.29), (100, 0.29)):
+        k, e_max = ops.event_capacity(_prob(seqlen=T), ops.sparse_params(keep_budget=budget))
+        C = -(-T // 64)
+        assert k == selector.tier_counts(C, budget), (T, budget)
+        assert e_max == 16 * k[2]
+    assert ops.event_capacity(_prob(seqlen=32768), ops.sparse_params())[0] == (41, 154, 486)
+    with pytest.raises(ops.SgdnError):
+        ops.event_capacity(_prob(n_qk=8, n_v=16), ops.sparse_params())
+    with pytest.raises(ops.SgdnError):
+        ops.event_capacity(_prob(), ops.sparse_params(keep_budget=0.0))
+    e = ctypes.c_int32()
+    assert L.sgdn_event_capacity(ctypes.byref(_prob()), ctypes.byref(ops.sparse_params()), None,
+                                 None) == -1
+    assert L.sgdn_event_capacity(ctypes.byref(_prob()), ctypes.byref(ops.sparse_params()), None,
+                                 ctypes.byref(e)) == 0 and e.value == 16 * 61
+
+
+def test_fp64_selftest_argument_errors(L):
+    assert L.sgdn_fp64_selftest(None, None, None, None, -1, None) == -1
+    assert L.sgdn_fp64_selftest(None, FAKE, FAKE, FAKE, 10, None) == -1
+    assert L.sgdn_fp64_selftest(None, None, None, None, 0, None) == 0   # nothing to do
+
+
 def test_status_strings(L):
     from gated_deltanet_prefill_chunkwise_amd import ops
     assert ops.status_string(0) == "ok"
@@ -77,7 +132,7 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails va
 def test_dense_argument_errors(L):
     def call(p, ws_bytes=1 << 40, q=FAKE, ws=FAKE):
         return L.sgdn_prefill_dense(ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
-                                    ws, ws_bytes, None, None)
+                                    None, ws, ws_bytes, None, None)
     assert call(_prob(d_k=64)) == -2
     assert call(_prob(n_v=33)) == -2
     assert call(_prob(seqlen=0)) == -1
@@ -87,8 +142,8 @@ def test_dense_argument_errors(L):
     assert call(_prob(), q=None) == -1
     assert call(_prob(), ws=None) == -1
     assert call(_prob(), ws_bytes=1024) == -3
-    assert L.sgdn_prefill_dense(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 1,
-                                None, None) == -1
+    assert L.sgdn_prefill_dense(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE,
+                                1, None, None) == -1
 
 
 def test_sparse_and_select_argument_errors(L):
@@ -116,6 +171,14 @@ def test_sparse_and_select_argument_errors(L):
     assert sparse(_prob(), good, z=None) == -1               # no gate and no mask
     assert sparse(_prob(seqlen=64 * 8193), good) == -2       # C > 8192
     assert sparse(_prob(), good, ws_bytes=4096) == -3
+    # a caller's second stream needs its two distinct fork / join events
+    aux = ops.sparse_params()
+    aux.aux_stream = 0x3000
+    assert sparse(_prob(), aux) == -1
+    aux.aux_events[0] = 0x4000
+    assert sparse(_prob(), aux) == -1
+    aux.aux_events[1] = 0x4000
+    assert sparse(_prob(), aux) == -1
 
     def sel(p, params, score=FAKE):
         return L.sgdn_select(ctypes.byref(p), score, FAKE, FAKE, ctypes.byref(params), FAKE, FAKE,

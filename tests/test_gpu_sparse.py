@@ -4,8 +4,10 @@
   on identical seeded fp32 statistics.
 * sgdn_prefill_sparse with a given event mask (the oracle's own selection):
   O and S_final within 2e-2 (bf16) / 1e-4 (fp32) of max error over RMS.
-* end to end with the on-device selector: statistics within tolerance, the
-  mask valid, and equal to the oracle's except at near-ties of the rank key.
+* end to end with the on-device selector: the device statistics (score,
+  gamma, eta) within tolerance of the oracle's, the oracle selector on the
+  device's own fp32 statistics bit-exact with the device mask and tiers, and
+  O, S_final against the oracle given that mask.
 """
 import numpy as np
 import pytest
@@ -47,7 +49,7 @@ def compare_select(score, gamma, eta, budget):
         st = out["stats"][b]
         kL, kM, kH = ref["k"]
         nt = [int((ref["tier"] == t).sum()) for t in (0, 1, 2)]
-        assert st.tolist() == [E, 16 * kH, *nt, kL, kM, kH, lay["n_snap"]], st
+        assert st.tolist() == [E, 16 * kH, *nt, kL, kM, kH, lay["n_snap"], 0, 0], st
 
 
 @pytest.mark.parametrize("C", [1, 2, 3, 4, 5, 33, 64, 200, 512])
@@ -66,6 +68,24 @@ def test_select_bit_exact_budgets(budget):
 def test_select_bit_exact_full_length():
     """C = 2048 (T = 128K)."""
     score, gamma, eta = synth.selector_stats(2048, 1, 2048)
+    compare_select(score, gamma, eta, 0.29)
+
+
+@pytest.mark.parametrize("case", ["nan_scores", "inf_score", "nan_eta", "nan_gamma"])
+def test_select_bit_exact_non_finite(case):
+    """Non-finite statistics (what inputs outside the operator's domain give):
+    both sides order NaN as -infinity, so the selection stays a valid one and
+    bit-exact."""
+    score, gamma, eta = synth.selector_stats(4242, 2, 96)
+    if case == "nan_scores":
+        score[0, 3, ::5] = np.nan
+        score[1, :, 7] = np.nan
+    elif case == "inf_score":
+        score[1, 8, 40] = np.inf
+    elif case == "nan_eta":
+        eta[0, 11] = np.nan
+    else:
+        gamma[1, 20, 90] = np.nan
     compare_select(score, gamma, eta, 0.29)
 
 
@@ -175,15 +195,24 @@ def _mask_valid(mask, tier, C, budget=0.29):
     assert nH in (1, 2, 3, 4) and nM in selector.MEDIUM_CHOICES[nH]
 
 
-@pytest.mark.parametrize("T,decay", [(4096, 1.0), (4096, 1 / 64)])
+@pytest.mark.parametrize("T,decay", [(4096, 1.0), (4096, 1 / 64), (64 * 37 + 19, 1 / 16)])
 def test_selector_end_to_end(T, decay):
-    """Device statistics match the oracle's; the device mask is valid and agrees
-    with the oracle's except where rank keys are within the statistics' error."""
+    """The whole sparse path with the on-device selector (gate energy, tail
+    scores, ranking, tiers, CSR), checked in three parts:
+    * the device statistics against the oracle's own (tolerance: they come
+      from different arithmetic);
+    * the oracle selector run on the device's fp32 statistics reproduces the
+      device's mask and tiers bit for bit (identical inputs, identical
+      integers);
+    * O and S_final against the oracle prefill given the device's mask.
+    The agreement of the device mask with the oracle's own selection (from
+    the oracle's fp64 statistics) is printed as information only: near-ties
+    of the rank key may flip at the top-k boundary."""
     import torch
     from gated_deltanet_prefill_chunkwise_amd import ops
     inp = synth.numpy_inputs(synth.seed_for(2) + T, 1, T, 16, 32, dtype="bf16", with_z=True,
                              decay_scale=decay)
-    C = T // 64
+    C = -(-T // 64)
     score = torch.empty((1, 32, C), device="cuda")
     gam = torch.empty((1, 32, C), device="cuda")
     eta = torch.empty((1, 32), device="cuda")
@@ -191,19 +220,24 @@ def test_selector_end_to_end(T, decay):
     tier = torch.empty((1, 16), dtype=torch.uint8, device="cuda")
     dbg = ops.debug_struct(score=score, gamma=gam, eta=eta, mask=mask, tier=tier)
     o, S, st = run_sparse(inp, debug=dbg)
-    o_ref, S_ref, info = oracle_sparse(inp)
+    o_own, S_own, info = oracle_sparse(inp)
     s_gpu, s_ref = host(score)[0], info["score"][0].astype(np.float64)
     assert np.max(np.abs(s_gpu - s_ref) / np.maximum(s_ref, 1e-6)) < 2e-2
     assert np.max(np.abs(host(eta)[0] - info["eta"][0]) / info["eta"][0]) < 1e-3
     m_gpu, t_gpu = mask.cpu().numpy()[0], tier.cpu().numpy()[0]
+    ref = selector.select(score.cpu().numpy()[0], gam.cpu().numpy()[0], eta.cpu().numpy()[0],
+                          keep_budget=0.29)
+    assert np.array_equal(m_gpu, ref["mask"]), "mask"
+    assert np.array_equal(t_gpu, ref["tier"]), "tier"
     _mask_valid(m_gpu, t_gpu, C)
-    m_ref, t_ref = info["mask"][0], info["sel"][0]["tier"]
-    diff = int((m_gpu != m_ref).sum())
-    print(f"mask differences {diff} of {m_ref.size}; tier differences {(t_gpu != t_ref).sum()}")
-    assert (t_gpu != t_ref).sum() <= 2
-    assert diff <= 0.03 * m_ref.size
-    if diff == 0:
-        assert rel_max_err(o, o_ref) <= TOL["bf16"] and rel_max_err(S, S_ref) <= TOL["bf16"]
+    assert st[0, 0] == int(m_gpu.sum()) and st[0, 9] == 0 and st[0, 10] == 0
+    o_ref, S_ref = sparse.sparse_prefill(inp.q, inp.k, inp.v, inp.a, inp.beta, solve="blockadj",
+                                         mask=m_gpu[None])
+    eo, es = rel_max_err(o, o_ref), rel_max_err(S, S_ref)
+    flips = int((m_gpu != info["mask"][0]).sum())
+    print(f"err O {eo:.3e} S {es:.3e}; mask entries differing from the oracle's own selection "
+          f"(information only): {flips} of {m_gpu.size}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
 def test_sparse_deterministic():
@@ -211,3 +245,20 @@ def test_sparse_deterministic():
     a = run_sparse(inp)
     b = run_sparse(inp)
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_one_stream_schedule_equals_two_streams():
+    """Without a second stream every kernel runs on the caller's stream: the
+    same products in the same order per head, so bit-identical outputs."""
+    import torch
+    from gated_deltanet_prefill_chunkwise_amd import ops
+    inp = synth.numpy_inputs(33, 1, 64 * 23 + 3, 16, 32, dtype="bf16", with_z=True,
+                             decay_scale=1 / 16)
+    d = to_device(inp)
+    outs = []
+    for aux in (True, False):
+        o, S, st = ops.prefill_sparse(d["q"], d["k"], d["v"], d["a"], d["beta"], z=d["z"],
+                                      keep_budget=0.29, solve="blockadj", aux=aux)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), S.cpu(), st.cpu()))
+    assert all(torch.equal(x, y) for x, y in zip(*outs))

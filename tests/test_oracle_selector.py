@@ -246,6 +246,48 @@ def test_selector_structure(C):
         assert 0.28442 <= E / (16 * C) <= 0.31372
 
 
+@pytest.mark.parametrize("case", ["nan_score_head", "nan_everywhere", "inf_score", "nan_eta",
+                                  "nan_gamma", "nan_rank_key"])
+def test_selector_total_orders_with_non_finite_statistics(case):
+    """Non-finite statistics (inputs outside the operator's domain) still give
+    a valid selection: ranks are a permutation of the inner chunks, each tier
+    keeps exactly k_l chunks, n_H and n_M come from the table, and E <= 16 k_H
+    (the capacity the CSR arrays are sized to).  NaN orders as -infinity."""
+    C = 40
+    rng = np.random.default_rng(5)
+    s = rng.gamma(2.0, 1.0, (32, C)).astype(np.float32)
+    gamma = (-rng.uniform(0.5, 30, (32, 1)) * np.ones((1, C))).astype(np.float32)
+    eta = rng.uniform(0.1, 3, 32).astype(np.float32)
+    key = None
+    if case == "nan_score_head":
+        s[5, 7] = np.nan
+    elif case == "nan_everywhere":
+        s[:, ::3] = np.nan
+    elif case == "inf_score":
+        s[9, 3] = np.inf
+    elif case == "nan_eta":
+        eta[4] = np.nan
+    elif case == "nan_gamma":
+        gamma[2, 10] = np.nan
+    else:
+        key = rng.uniform(size=(16, C)).astype(np.float32)
+        key[:, 5:9] = np.nan
+    out = selector.select(s, gamma, eta, rank_key=key)
+    kL, kM, kH = out["k"]
+    nH, nM = out["n_high"], out["n_medium"]
+    assert nH in (1, 2, 3, 4) and nM in selector.MEDIUM_CHOICES[nH]
+    for p in range(16):
+        assert sorted(out["rank"][p, 1:C - 1].tolist()) == list(range(C - 2))
+        assert out["mask"][p].sum() == {2: kH, 1: kM, 0: kL}[int(out["tier"][p])]
+    assert out["mask"].sum() <= 16 * kH
+    if case == "nan_rank_key":
+        # chunks whose key is NaN rank after every chunk with a finite key
+        for p in range(16):
+            k = {2: kH, 1: kM, 0: kL}[int(out["tier"][p])]
+            if k - 2 <= C - 2 - 4:
+                assert not out["mask"][p, 5:9].any()
+
+
 def test_high_tier_takes_largest_gains():
     rng = np.random.default_rng(11)
     C = 64
