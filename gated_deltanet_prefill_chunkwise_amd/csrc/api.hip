@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/sgdn.h"
 #include "common.h"
@@ -237,6 +238,83 @@ int debug_copies(const Plan& pl, void* ws, sgdn_debug* dbg, hipStream_t st, int 
   return SGDN_OK;
 }
 
+// Selector scratch: rank tables (q-ranks; caller-key ranks), tier counts,
+// snapshot slot of every event.
+struct SelectScratch { int32_t *rank, *rank_alt, *tierinfo, *event_slot; };
+
+int check_select(const sgdn_problem* prob, const float* score, const float* gamma, const float* eta,
+                 const sgdn_sparse_params* params, const uint8_t* mask, const uint8_t* tier,
+                 const int32_t* row_pair, const int32_t* row_ptr, const int32_t* col,
+                 const int32_t* pred, const int32_t* group_slot) {
+  int st = check_problem(prob);
+  if (st != SGDN_OK) return st;
+  if ((st = check_params(prob, params)) != SGDN_OK) return st;
+  if (!score || !gamma || !eta || !mask || !tier || !row_pair || !row_ptr || !col || !pred ||
+      !group_slot)
+    return SGDN_EINVAL;
+  return SGDN_OK;
+}
+
+int launch_select_call(const Plan& pl, const float* score, const float* gamma, const float* eta,
+                       const sgdn_sparse_params* params, uint8_t* mask, uint8_t* tier,
+                       int32_t* row_pair, int32_t* row_ptr, int32_t* col, int32_t* pred,
+                       int32_t* group_slot, sgdn_stats* stats, const SelectScratch& sc,
+                       hipStream_t s) {
+  SelectArgs sa{};
+  sa.score = score; sa.gamma = gamma; sa.eta = eta;
+  sa.B = pl.B; sa.C = pl.C; sa.keep_bp = budget_bp(params->keep_budget);
+  sa.cu = pl.cu; sa.T = pl.T;
+  sa.fixed_tiers = params->fixed_tiers; sa.unit_visibility = params->unit_visibility;
+  sa.rank_key = params->rank_key;
+  sa.rank_alt = sc.rank_alt;
+  sa.rank = sc.rank; sa.tierinfo = sc.tierinfo;
+  sa.mask = mask; sa.tier = tier; sa.row_pair = row_pair; sa.row_ptr = row_ptr; sa.col = col;
+  sa.pred = pred; sa.group_slot = group_slot; sa.event_slot = sc.event_slot;
+  sa.Emax = NP_SPARSE * pl.kH; sa.G = pl.G;
+  sa.stats = stats; sa.nf_clear = 1; sa.mask_in = nullptr;
+  SGDN_TRY(launch_select_full(sa, s));
+  return SGDN_OK;
+}
+
+// ---- scratch of sgdn_select_noalloc --------------------------------------
+// A file-scope device array instead of a caller workspace.  Each device
+// the library runs on holds its own copy until the process ends; its address
+// on a device comes from hipGetSymbolAddress, taken once per device (on the
+// first call there, with that device current) and kept.  The array's name
+// itself is a host-side stand-in and is never passed to a kernel or a copy.
+// Every call on a device shares that device's copy: calls that overlap on
+// one device race.  Nothing in it needs to start at zero (every entry the
+// selector reads is written by the same call first).
+__device__ __align__(256) static unsigned char scratch[SGDN_NOALLOC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[MAX_DEVICES] = {};
+
+int noalloc_scratch(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return SGDN_EHIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return SGDN_EHIP;
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return SGDN_OK;
+}
+
+// Offsets of the four selector arrays inside the scratch (256-byte aligned);
+// returns the bytes used.
+size_t noalloc_layout(const Plan& pl, bool with_key, size_t off[4]) {
+  const size_t ranks = align256((size_t)pl.B * NP_SPARSE * pl.C * 4);
+  off[0] = 0;
+  off[1] = ranks;
+  off[2] = off[1] + (with_key ? ranks : 0);
+  off[3] = off[2] + align256((size_t)pl.B * 8 * 4);
+  return off[3] + align256((size_t)pl.B * NP_SPARSE * pl.kH * 4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -366,30 +444,38 @@ int sgdn_select(const sgdn_problem* prob, const float* score, const float* gamma
                 const sgdn_sparse_params* params, uint8_t* mask, uint8_t* tier, int32_t* row_pair,
                 int32_t* row_ptr, int32_t* col, int32_t* pred, int32_t* group_slot,
                 sgdn_stats* stats, void* ws, size_t ws_bytes, void* stream) {
-  int st = check_problem(prob);
+  int st = check_select(prob, score, gamma, eta, params, mask, tier, row_pair, row_ptr, col, pred,
+                        group_slot);
   if (st != SGDN_OK) return st;
-  if ((st = check_params(prob, params)) != SGDN_OK) return st;
-  if (!score || !gamma || !eta || !mask || !tier || !row_pair || !row_ptr || !col || !pred ||
-      !group_slot || !ws)
-    return SGDN_EINVAL;
+  if (!ws) return SGDN_EINVAL;
   Plan pl;
   make_plan(prob, 1, params, pl);
   if (ws_bytes < pl.total) return SGDN_EWORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  SelectArgs sa{};
-  sa.score = score; sa.gamma = gamma; sa.eta = eta;
-  sa.B = pl.B; sa.C = pl.C; sa.keep_bp = budget_bp(params->keep_budget);
-  sa.cu = pl.cu; sa.T = pl.T;
-  sa.fixed_tiers = params->fixed_tiers; sa.unit_visibility = params->unit_visibility;
-  sa.rank_key = params->rank_key;
-  sa.rank_alt = params->rank_key ? at<int32_t>(ws, pl, B_RANK2) : nullptr;
-  sa.rank = at<int32_t>(ws, pl, B_RANK); sa.tierinfo = at<int32_t>(ws, pl, B_TINFO);
-  sa.mask = mask; sa.tier = tier; sa.row_pair = row_pair; sa.row_ptr = row_ptr; sa.col = col;
-  sa.pred = pred; sa.group_slot = group_slot; sa.event_slot = at<int32_t>(ws, pl, B_ESLOT);
-  sa.Emax = NP_SPARSE * pl.kH; sa.G = pl.G;
-  sa.stats = stats; sa.nf_clear = 1; sa.mask_in = nullptr;
-  SGDN_TRY(launch_select_full(sa, s));
-  return SGDN_OK;
+  SelectScratch sc{at<int32_t>(ws, pl, B_RANK), params->rank_key ? at<int32_t>(ws, pl, B_RANK2) : nullptr,
+                   at<int32_t>(ws, pl, B_TINFO), at<int32_t>(ws, pl, B_ESLOT)};
+  return launch_select_call(pl, score, gamma, eta, params, mask, tier, row_pair, row_ptr, col, pred,
+                            group_slot, stats, sc, static_cast<hipStream_t>(stream));
+}
+
+int sgdn_select_noalloc(const sgdn_problem* prob, const float* score, const float* gamma,
+                        const float* eta, const sgdn_sparse_params* params, uint8_t* mask,
+                        uint8_t* tier, int32_t* row_pair, int32_t* row_ptr, int32_t* col,
+                        int32_t* pred, int32_t* group_slot, sgdn_stats* stats, void* stream) {
+  int st = check_select(prob, score, gamma, eta, params, mask, tier, row_pair, row_ptr, col, pred,
+                        group_slot);
+  if (st != SGDN_OK) return st;
+  Plan pl;
+  make_plan(prob, 1, params, pl);
+  size_t off[4];
+  if (noalloc_layout(pl, params->rank_key != nullptr, off) > SGDN_NOALLOC_SCRATCH_BYTES)
+    return SGDN_EWORKSPACE;
+  char* base = nullptr;
+  if ((st = noalloc_scratch(&base)) != SGDN_OK) return st;
+  SelectScratch sc{reinterpret_cast<int32_t*>(base + off[0]),
+                   params->rank_key ? reinterpret_cast<int32_t*>(base + off[1]) : nullptr,
+                   reinterpret_cast<int32_t*>(base + off[2]), reinterpret_cast<int32_t*>(base + off[3])};
+  return launch_select_call(pl, score, gamma, eta, params, mask, tier, row_pair, row_ptr, col, pred,
+                            group_slot, stats, sc, static_cast<hipStream_t>(stream));
 }
 
 int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, const void* v,

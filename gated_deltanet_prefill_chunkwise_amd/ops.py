@@ -15,7 +15,9 @@ LIB_PATH = os.path.join(HERE, "libsgdn.so")
 SGDN_F32, SGDN_BF16 = 0, 1
 SOLVES = {"exact": 0, "blockadj": 1}
 EXPORTS = ("sgdn_workspace_bytes", "sgdn_event_capacity", "sgdn_prefill_dense", "sgdn_select",
-           "sgdn_prefill_sparse", "sgdn_decode_step", "sgdn_status_string", "sgdn_fp64_selftest")
+           "sgdn_prefill_sparse", "sgdn_decode_step", "sgdn_status_string", "sgdn_fp64_selftest",
+           "sgdn_select_noalloc")
+NOALLOC_SCRATCH_BYTES = 4 << 20   # SGDN_NOALLOC_SCRATCH_BYTES
 
 
 class Problem(ctypes.Structure):
@@ -93,6 +95,8 @@ def lib():
         L.sgdn_prefill_dense.restype = i32
         L.sgdn_select.argtypes = [P, vp, vp, vp, SP, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sgdn_select.restype = i32
+        L.sgdn_select_noalloc.argtypes = [P, vp, vp, vp, SP, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.sgdn_select_noalloc.restype = i32
         L.sgdn_prefill_sparse.argtypes = [P, vp, vp, vp, vp, vp, vp, SP, vp, vp, vp, vp, vp, vp,
                                           sz, vp, vp]
         L.sgdn_prefill_sparse.restype = i32
@@ -336,11 +340,13 @@ def decode_step(q, k, v, a, beta, state, s_out=None, o=None, out_dtype=None, str
 
 
 def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None, cu_seqlens=None,
-           fixed_tiers=False, unit_visibility=False, rank_key=None):
+           fixed_tiers=False, unit_visibility=False, rank_key=None, noalloc=False, out=None):
     """Selector + CSR layout on fp32 statistics; returns a dict of device tensors.
 
     With ``cu_seqlens`` (int32 [B + 1] token offsets) sequence b has only its
-    ceil(len_b / 64) valid chunks; the arrays keep the stride C.
+    ceil(len_b / 64) valid chunks; the arrays keep the stride C.  ``noalloc``
+    calls sgdn_select_noalloc (the library's static scratch, no workspace);
+    ``out`` reuses a dict of output tensors from an earlier call.
     """
     import torch
     B, Nv, C = score.shape
@@ -357,28 +363,39 @@ def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None, cu_
                    None if cu_seqlens is None else cu_seqlens.data_ptr())
     params = sparse_params(keep_budget, fixed_tiers=fixed_tiers, unit_visibility=unit_visibility,
                            rank_key=rank_key)
+    NP, G = Nv // 2, (C + 1) // 2
+    dev = score.device
+    _, e_max = event_capacity(prob, params)
+    shapes = dict(mask=((B, NP, C), torch.uint8), tier=((B, NP), torch.uint8),
+                  row_pair=((B, NP), torch.int32), row_ptr=((B, NP + 1), torch.int32),
+                  col=((B, e_max), torch.int32), pred=((B, NP, G), torch.int32),
+                  group_slot=((B, NP, G), torch.int32), stats=((B, STATS_INTS), torch.int32))
+    if out is not None:
+        for name, (shape, dt) in shapes.items():
+            _check(out[name], name, dt)
+            if tuple(out[name].shape) != shape:
+                raise ValueError(f"{name} must have shape {shape}, got {tuple(out[name].shape)}")
+    else:
+        out = {name: torch.empty(shape, dtype=dt, device=dev) for name, (shape, dt) in shapes.items()}
+        out["col"].fill_(-1)
+    return _select_call(prob, params, score, gamma, eta, out, workspace, noalloc, stream)
+
+
+def _select_call(prob, params, score, gamma, eta, out, workspace, noalloc, stream):
+    args = (_ptr(out["mask"]), _ptr(out["tier"]), _ptr(out["row_pair"]), _ptr(out["row_ptr"]),
+            _ptr(out["col"]), _ptr(out["pred"]), _ptr(out["group_slot"]), _ptr(out["stats"]))
+    if noalloc:
+        st = lib().sgdn_select_noalloc(ctypes.byref(prob), _ptr(score), _ptr(gamma), _ptr(eta),
+                                       ctypes.byref(params), *args, _stream(stream))
+        if st != 0:
+            raise SgdnError(st, "sgdn_select_noalloc")
+        return out
     nbytes = workspace_bytes(prob, True, params)
     if nbytes == 0:
         raise SgdnError(-2, "sgdn_workspace_bytes")
     ws = _workspace(nbytes, score.device, workspace)
-    NP, G = Nv // 2, (C + 1) // 2
-    dev = score.device
-    _, e_max = event_capacity(prob, params)
-    out = dict(
-        mask=torch.empty((B, NP, C), dtype=torch.uint8, device=dev),
-        tier=torch.empty((B, NP), dtype=torch.uint8, device=dev),
-        row_pair=torch.empty((B, NP), dtype=torch.int32, device=dev),
-        row_ptr=torch.empty((B, NP + 1), dtype=torch.int32, device=dev),
-        col=torch.full((B, e_max), -1, dtype=torch.int32, device=dev),
-        pred=torch.empty((B, NP, G), dtype=torch.int32, device=dev),
-        group_slot=torch.empty((B, NP, G), dtype=torch.int32, device=dev),
-        stats=torch.zeros((B, STATS_INTS), dtype=torch.int32, device=dev),
-    )
     st = lib().sgdn_select(ctypes.byref(prob), _ptr(score), _ptr(gamma), _ptr(eta),
-                           ctypes.byref(params), _ptr(out["mask"]), _ptr(out["tier"]),
-                           _ptr(out["row_pair"]), _ptr(out["row_ptr"]), _ptr(out["col"]),
-                           _ptr(out["pred"]), _ptr(out["group_slot"]), _ptr(out["stats"]),
-                           _ptr(ws), ws.numel(), _stream(stream))
+                           ctypes.byref(params), *args, _ptr(ws), ws.numel(), _stream(stream))
     if st != 0:
         raise SgdnError(st, "sgdn_select")
     return out

@@ -293,6 +293,25 @@ int sgdn_select(const sgdn_problem* prob, const float* score, const float* gamma
                 int32_t* pred, int32_t* group_slot, sgdn_stats* stats, void* ws,
                 size_t ws_bytes, void* stream);
 
+/* sgdn_select without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and statistics
+ * as sgdn_select; the selector's scratch (rank tables, tier counts, event
+ * slots) lives in a static device array of SGDN_NOALLOC_SCRATCH_BYTES that
+ * every device the library runs on holds until the process ends, located on
+ * the first call on a device (which must be the current device).  It calls
+ * no allocation routine.  Limit: the selector's 64 B C + 32 B + 64 B k_H
+ * bytes (plus 64 B C with rank_key), each rounded up to 256, must fit; about
+ * B * C <= 22,000 sequence-chunks in every case (one sequence of 1.4M
+ * tokens, or 8 sequences of 131,072), SGDN_EWORKSPACE beyond it (nothing
+ * enqueued).  Calls that overlap on one device share the
+ * scratch and race: serialise them (one stream, or events). */
+#define SGDN_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int sgdn_select_noalloc(const sgdn_problem* prob, const float* score, const float* gamma,
+                        const float* eta, const sgdn_sparse_params* params, uint8_t* mask,
+                        uint8_t* tier, int32_t* row_pair, int32_t* row_ptr, int32_t* col,
+                        int32_t* pred, int32_t* group_slot, sgdn_stats* stats, void* stream);
+
 /* SparseGDN prefill, Secs. 2.2-2.7, Eqs. (5)-(25): local solve with fused
  * tail score, gate energy, selector, deferred W over CSR events (with bf16
  * inputs formed inside the H scan as W S = Cb (K S)),

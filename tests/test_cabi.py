@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["sgdn_workspace_bytes", "sgdn_event_capacity", "sgdn_prefill_dense", "sgdn_select",
-         "sgdn_prefill_sparse", "sgdn_status_string", "sgdn_decode_step", "sgdn_fp64_selftest"])
+         "sgdn_prefill_sparse", "sgdn_status_string", "sgdn_decode_step", "sgdn_fp64_selftest",
+         "sgdn_select_noalloc"])
 
 
 def test_struct_layouts_match_header(tmp_path):
@@ -186,6 +187,26 @@ def test_sparse_and_select_argument_errors(L):
     assert sel(_prob(), good, score=None) == -1
     assert sel(_prob(n_qk=4, n_v=8), good) == -2
     assert sel(_prob(), ops.sparse_params(r_window=8)) == -2
+
+
+def test_select_noalloc_argument_errors(L):
+    """Validation and the scratch-capacity refusal happen on the host, before
+    the scratch is located or anything is enqueued."""
+    from gated_deltanet_prefill_chunkwise_amd import ops
+
+    def sel(p, params, score=FAKE):
+        return L.sgdn_select_noalloc(ctypes.byref(p), score, FAKE, FAKE, ctypes.byref(params), FAKE,
+                                     FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    good = ops.sparse_params()
+    assert sel(_prob(), good, score=None) == -1
+    assert sel(_prob(n_qk=4, n_v=8), good) == -2
+    assert sel(_prob(), ops.sparse_params(r_window=8)) == -2
+    # 16 x 131072 tokens with a caller key: 6 MiB of selector scratch > 4 MiB
+    keyed = ops.sparse_params()
+    keyed.rank_key = 0x5000
+    assert sel(_prob(batch=16, seqlen=131072), keyed) == -3
+    assert sel(_prob(batch=17, seqlen=131072), good) == -3      # without a key: 4.35 MB
+    assert ops.NOALLOC_SCRATCH_BYTES == 4 << 20
 
 
 def test_decode_argument_errors(L):
