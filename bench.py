@@ -18,14 +18,26 @@ kernel-pipeline ablation leg times it with deferred W, compact states, the
 CSR event walk and the two-chunk O mapping undone (Table 6), reporting each
 mechanism's speedup over its stages.
 
+Beside the 131072-token stack, the same layers' first 4K ... 64K tokens are
+timed in both modes (the length sweep of Sec. 3.2, Table 1; 32K is the other
+length the metric names), and the keep-budget x batch grid of Sec. 3.3-3.4
+(batch 2 / 4 / 8 of 32768 tokens, keep 0.15 / 0.29 / 0.5 / 1.0, per-head
+decay scale u ~ U(0, ln 16)) is timed against the dense path at each batch.
+
 Prints one JSON line.  value = tokens/s of the 24-layer stack (B*T per step);
+each timed configuration reports the mean and the median over its steps.
 roofline = the dominant kernel's algorithmic bytes per layer over its mean
 time per layer (HIP events recorded by the library on the caller's stream;
 in the sparse path the H scan of CSR rows 4-15 runs on a second stream
 during the launch for rows 0-3, which the events bracket, so the bytes of
-both count over that time; traffic likewise sums both launches);
-cpu_baseline = the fp64 numpy oracle on a bounded sample (layer 0's first
-32768 tokens, all heads), in the same unit.
+both count over that time; traffic likewise sums both launches).
+path_roofline = the whole layer against HBM with the algorithmic bytes of
+the I/O streams (bf16 Q, K, V, O; fp32 a; bf16 beta) plus the compact
+snapshots written and read; mfma = the algorithmic flops of the method over
+the same time against the dense bf16 matrix-core peak.
+cpu_baseline = the fp64 numpy oracle as it stands, one worker process per
+host core (up to 16), each on a different layer's first tokens, in both
+modes, in the same unit.
 """
 from __future__ import annotations
 
@@ -42,6 +54,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 matrix cores, published
 B, T, NQ, NV, D = 1, 131072, 16, 32, 128
 LAYERS = 24
 STAGES = ("intra", "prefix", "gate", "select", "deferred_w", "hscan", "o")
@@ -56,8 +69,14 @@ def parse():
     ap.add_argument("--seqlen", type=int, default=T)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=("both", "sparse", "dense"), default="both")
-    ap.add_argument("--cpu-tokens", type=int, default=32768,
-                    help="tokens of layer 0 the oracle baseline processes")
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="tokens of one layer each oracle worker processes")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="oracle worker processes (at most the host's usable cores)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the 4K-64K length sweep")
+    ap.add_argument("--no-grid", action="store_true",
+                    help="skip the keep-budget x batch grid")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed variable-length leg")
     ap.add_argument("--no-ablations", action="store_true",
@@ -96,13 +115,14 @@ class Hip:
 
 def algorithmic_bytes_per_token(stage: str, mode: str, sigma: float, keep: float) -> float:
     """Bytes per token of the I/O streams a stage must move: bf16 Q, K, V, a
-    (fp32) and beta, fp32 O, and the fp16 group snapshots (one 128x128 state
+    (fp32) and beta, O counted as bf16 (the output stream of the problem
+    statement; this run writes an fp32 O), and the fp16 group snapshots (one 128x128 state
     per head per two chunks, written by the H scan and read by O); pipeline
     intermediates (U, U', W or Cb, K^T tiles) are not counted."""
     k_in = NQ * D * 2           # K (shared by a head pair)
     q_in = NQ * D * 2
     v_in = NV * D * 2
-    o_out = NV * D * 4          # fp32 O
+    o_out = NV * D * 2          # O as the algorithmic byte count has it (bf16)
     a_b = NV * 4 + NV * 2       # a (fp32) + beta (bf16)
     snap = NV * D * D * 2 / 128 * (sigma if mode == "sparse" else 1.0)   # one direction
     if stage == "intra":
@@ -114,6 +134,31 @@ def algorithmic_bytes_per_token(stage: str, mode: str, sigma: float, keep: float
     if stage == "path":
         return q_in + k_in + v_in + a_b + o_out + 2 * snap
     return 0.0
+
+
+def path_bytes_per_token(mode: str, sigma: float, o_bytes: int = 2) -> float:
+    """Algorithmic HBM bytes per token of one layer: the I/O streams (bf16 Q,
+    K, V and O by default, fp32 a, bf16 beta) plus the fp16 group snapshots,
+    one 128x128 state per head per two chunks written once and read once
+    (the fraction sigma of them in the sparse path)."""
+    io = NQ * D * 2 * 2 + NV * D * 2 + NV * D * o_bytes + NV * 4 + NV * 2
+    snap = 2 * NV * D * D * 2 / 128 * (sigma if mode == "sparse" else 1.0)
+    return io + snap
+
+
+def flops_per_token(mode: str, keep: float) -> float:
+    """Algorithmic flops per token of one layer (multiply-adds x 2): per chunk
+    and value head the Gram and Q K^T products of a pair counted once per
+    pair, the causal triangle only, the 7 blocks of the block-adjacent solve,
+    and in the sparse path W, W S and K^T U' on the kept events only:
+      dense exact: Gram 129,024 + inverse 43,680 + U 266,240 + W 266,240
+                   + W S, K^T U', Q S 3 x 1,048,576 + Q K^T 133,120
+                   + A U' 266,240 = 4,250,272 MAC;
+      sparse:      Gram 79,872 + inverse 15,776 + U 167,936 + Q S 1,048,576
+                   + Q K^T 264,192 + A U' 528,384 = 2,104,736 MAC, plus
+                   (W 167,936 + W S + K^T U' 2 x 1,048,576) x keep."""
+    mac = 4250272.0 if mode == "dense" else 2104736.0 + 2265088.0 * keep
+    return mac * 2 * NV / 64
 
 
 def source_hash(stage: str) -> str:
@@ -141,25 +186,126 @@ def measured_traffic(stage: str, mode: str):
         return None
 
 
-def cpu_baseline(inputs0, tokens=32768):
-    """The fp64 oracle (as it stands) on layer 0's first `tokens` tokens."""
-    import numpy as np
-    from oracle import sparse
+def _cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    host = {k: v[:, :tokens].float().cpu().numpy().astype(np.float64) for k, v in inputs0.items()}
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_worker(path: str, mode: str) -> float:
+    """One oracle run (a worker process, one BLAS thread) on a saved layer
+    sample; returns its wall time."""
+    import numpy as np
+    from oracle import gdn, sparse
+    x = np.load(path)
+    f = {k: x[k].astype(np.float64) for k in x.files}
     t0 = time.perf_counter()
-    sparse.sparse_prefill(host["q"], host["k"], host["v"], host["a"], host["beta"], z=host["z"],
-                          keep_budget=0.29, solve="blockadj")
-    dt = time.perf_counter() - t0
-    return dict(value=tokens / dt / LAYERS, unit="tok/s (24-layer GDN-core stack)", cores=threads,
-                kind="oracle",
-                sample=(f"fp64 numpy oracle, SparseGDN 29% path, layer 0's first {tokens} tokens, "
-                        f"all 32 value heads, one layer timed ({dt:.1f} s) and scaled by 1/24; "
-                        f"BLAS calls use up to {threads} threads, the rest one"))
+    if mode == "dense":
+        gdn.chunk_prefill(f["q"], f["k"], f["v"], f["a"], f["beta"], None, "exact")
+    else:
+        sparse.sparse_prefill(f["q"], f["k"], f["v"], f["a"], f["beta"], z=f["z"],
+                              keep_budget=0.29, solve="blockadj")
+    return time.perf_counter() - t0
+
+
+def _worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+    # one tiny run of each path, so that lazy imports and first-call costs
+    # stay outside the timed region
+    import numpy as np
+    from oracle import gdn, sparse
+    g = np.random.default_rng(0)
+    x = {k: g.standard_normal(s) for k, s in (("q", (1, 128, 16, 128)), ("k", (1, 128, 16, 128)),
+                                                ("v", (1, 128, 32, 128)), ("z", (1, 128, 32, 128)))}
+    a, beta = -np.ones((1, 128, 32)), np.full((1, 128, 32), 0.5)
+    gdn.chunk_prefill(x["q"], x["k"], x["v"], a, beta, None, "exact")
+    sparse.sparse_prefill(x["q"], x["k"], x["v"], a, beta, z=x["z"])
+
+
+def _noop(i):
+    time.sleep(0.05)
+    return i
+
+
+def cpu_baseline(layers, tokens, workers):
+    """The fp64 oracle as it stands, on the host's cores: one worker process
+    per core (at most `workers`, at most the cores this process may use), each
+    running the whole oracle on the first `tokens` tokens of a different
+    layer, all 32 value heads; dense (exact) and sparse (29%, block-adjacent,
+    selector included).  Throughput = all workers' tokens over the wall time
+    of the pool, in the headline's unit (per 24-layer stack)."""
+    import multiprocessing as mp
+    import tempfile
+    from concurrent.futures import ProcessPoolExecutor
+    import numpy as np
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    n = max(1, min(workers, usable or 1, len(layers)))
+    # samples go through memory-backed files (removed below)
+    tmp = tempfile.mkdtemp(prefix="sgdn_cpu_", dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    paths = []
+    t0 = time.perf_counter()
+    for l in range(n):
+        inp = layers[l][0]
+        arrs = {k: v[:, :tokens].float().cpu().numpy() for k, v in inp.items()}
+        pth = os.path.join(tmp, f"layer{l}.npz")
+        np.savez(pth, **arrs)
+        paths.append(pth)
+    print(f"[bench] cpu baseline: {n} samples of {tokens} tokens staged in "
+          f"{time.perf_counter() - t0:.1f} s; {n} workers", file=sys.stderr, flush=True)
+    out = {}
+    try:
+        with ProcessPoolExecutor(max_workers=n, mp_context=mp.get_context("spawn"),
+                                 initializer=_worker_init) as ex:
+            list(ex.map(_noop, range(4 * n)))      # every worker started and initialised
+            for mode in ("dense", "sparse"):
+                t0 = time.perf_counter()
+                per = list(ex.map(_oracle_worker, paths, [mode] * n))
+                wall = time.perf_counter() - t0
+                tok_s_layer = n * tokens / wall
+                print(f"[bench] cpu baseline {mode}: {wall:.1f} s for {n} x {tokens} tokens",
+                      file=sys.stderr, flush=True)
+                out[mode] = dict(value=round(tok_s_layer / LAYERS, 2),
+                                 per_layer_tok_s=round(tok_s_layer, 1), wall_s=round(wall, 2),
+                                 worker_s=[round(t, 2) for t in per])
+    finally:
+        for pth in paths:
+            os.remove(pth)
+        os.rmdir(tmp)
+    return dict(value=out["sparse"]["value"], unit="tok/s (24-layer GDN-core stack)", cores=n,
+                kind="oracle", host_cpus=os.cpu_count(), usable_cpus=usable, cpu_model=_cpu_model(),
+                dense=out["dense"], sparse=out["sparse"],
+                sample=(f"fp64 numpy oracle as it stands, {n} worker processes (one BLAS thread "
+                        f"each) on {n} cores, each on the first {tokens} tokens of a different "
+                        f"layer (all 32 value heads): the sparse path (29% budget, block-adjacent "
+                        f"solve, selector included; value) and the dense exact path; tokens of all "
+                        f"workers over the pool's wall time, divided by 24 for the stack"))
+
+
+def timed_steps(args, step):
+    """args.warmup untimed calls of step(i), then args.steps timed ones, each
+    bracketed by events on the current stream; returns (mean ms, median ms)."""
+    import statistics
+    import torch
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return statistics.fmean(ms), statistics.median(ms)
 
 
 def time_stack(args, hip, L, call):
@@ -382,6 +528,102 @@ def bf16_output_leg(args, layers, ws):
     return res
 
 
+def sweep_leg(args, layers, ws):
+    """Both modes over the first T tokens of the same 24 layers, T = 4K ...
+    64K (the 131072-token point is the headline): Sec. 3.2, Table 1 times
+    this sweep (4K, 8K, 16K, 32K, 64K, 128K); 32K is named by the metric."""
+    from gated_deltanet_prefill_chunkwise_amd import ops
+    out = {}
+    for Tn in (4096, 8192, 16384, 32768, 65536):
+        if Tn > args.seqlen:
+            continue
+        row = {}
+        for mode in ("sparse", "dense"):
+            def step(_i, mode=mode, Tn=Tn):
+                for inp, o, sf, st in layers:
+                    x = {k: v[:, :Tn] for k, v in inp.items()}
+                    if mode == "sparse":
+                        ops.prefill_sparse(x["q"], x["k"], x["v"], x["a"], x["beta"], z=x["z"],
+                                           keep_budget=0.29, solve="blockadj", o=o[:, :Tn],
+                                           s_final=sf, stats=st, workspace=ws)
+                    else:
+                        ops.prefill_dense(x["q"], x["k"], x["v"], x["a"], x["beta"], solve="exact",
+                                          o=o[:, :Tn], s_final=sf, workspace=ws)
+            mean, med = timed_steps(args, step)
+            row[mode] = {"ms_per_step": round(mean, 4), "median_ms_per_step": round(med, 4),
+                         "value_tok_s": round(B * Tn / (mean / 1e3), 1),
+                         "per_layer_tok_s": round(B * Tn * len(layers) / (mean / 1e3), 1)}
+            if mode == "sparse":
+                import torch
+                stt = torch.stack([st for (_, _, _, st) in layers]).float().cpu()[:, 0, :]
+                C = Tn // 64
+                keep = float((stt[:, 0] / (16 * C)).mean())
+                sigma = float((stt[:, 8] / (16 * max((C + 1) // 2 - 1, 1))).mean())
+                row[mode]["measured_keep"] = round(keep, 5)
+                row[mode]["snapshot_fraction"] = round(sigma, 5)
+            else:
+                sigma, keep = 1.0, 1.0
+            per_layer_ms = mean / len(layers)
+            alg = path_bytes_per_token(mode, sigma) * B * Tn
+            row[mode]["path_roofline_frac"] = round(alg / (per_layer_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
+            fl = flops_per_token(mode, keep) * B * Tn
+            row[mode]["mfma_frac"] = round(fl / (per_layer_ms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS, 4)
+        row["sparse_speedup_over_dense"] = round(row["dense"]["ms_per_step"] / row["sparse"]["ms_per_step"], 3)
+        out[str(Tn)] = row
+        print(f"[bench] T={Tn}: sparse {row['sparse']['ms_per_step']:.3f} ms, dense "
+              f"{row['dense']['ms_per_step']:.3f} ms per {len(layers)}-layer step "
+              f"({row['sparse_speedup_over_dense']:.2f}x)", file=sys.stderr, flush=True)
+    return out
+
+
+def grid_leg(args, dev):
+    """Sec. 3.3 (batch 2 / 4 / 8, Fig. 8, Table 2) and Sec. 3.4 (keep budgets,
+    Table 3): one layer of 32768 tokens per sequence, bf16, u ~ U(0, ln 16),
+    keep 0.15 / 0.29 / 0.5 / 1.0 and the dense exact path at each batch;
+    a step is 24 calls (the stack of the pages' timings; one input set is
+    reused across the calls and the keep budgets, so that budgets compare on
+    identical data)."""
+    import torch
+    from gated_deltanet_prefill_chunkwise_amd import ops, synth
+    Tg, Bmax = 32768, 8
+    inp = synth.torch_inputs(synth.seed_for(4, 0) + Bmax, Bmax, Tg, NQ, NV, dtype="bf16",
+                             with_z=True, u_max=math.log(16.0), device=dev)
+    o = torch.empty((Bmax, Tg, NV, D), dtype=torch.float32, device=dev)
+    sf = torch.empty((Bmax, NV, D, D), dtype=torch.float32, device=dev)
+    st = torch.zeros((Bmax, ops.STATS_INTS), dtype=torch.int32, device=dev)
+    prob = ops.problem(inp["q"], inp["v"], "blockadj", torch.float32)
+    ws = torch.empty(max(ops.workspace_bytes(prob, True, ops.sparse_params()),
+                         ops.workspace_bytes(prob, False)), dtype=torch.uint8, device=dev)
+    out = {}
+    for Bg in (2, 4, 8):
+        x = {k: v[:Bg] for k, v in inp.items()}
+        row = {}
+        for keep in (0.15, 0.29, 0.5, 1.0, "dense"):
+            def step(_i, keep=keep):
+                for _ in range(LAYERS):
+                    if keep == "dense":
+                        ops.prefill_dense(x["q"], x["k"], x["v"], x["a"], x["beta"], solve="exact",
+                                          o=o[:Bg], s_final=sf[:Bg], workspace=ws)
+                    else:
+                        ops.prefill_sparse(x["q"], x["k"], x["v"], x["a"], x["beta"], z=x["z"],
+                                           keep_budget=keep, solve="blockadj", o=o[:Bg],
+                                           s_final=sf[:Bg], stats=st[:Bg], workspace=ws)
+            mean, med = timed_steps(args, step)
+            r = {"ms_per_step": round(mean, 4), "median_ms_per_step": round(med, 4),
+                 "value_tok_s": round(Bg * Tg / (mean / 1e3), 1)}
+            if keep != "dense":
+                r["measured_keep"] = round(float(st[:Bg, 0].float().mean()) / (16 * Tg // 64), 5)
+            row[str(keep)] = r
+        for keep in (0.15, 0.29, 0.5, 1.0):
+            row[str(keep)]["speedup_over_dense"] = round(row["dense"]["ms_per_step"] / row[str(keep)]["ms_per_step"], 3)
+        out[f"batch{Bg}"] = row
+        print(f"[bench] grid batch {Bg}: " + ", ".join(
+            f"{k} {v['ms_per_step']:.2f} ms" for k, v in row.items()), file=sys.stderr, flush=True)
+    del inp, o, sf, st, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_bytes_per_launch(Bd: int) -> int:
     """One decode launch: every head's fp32 state read and written once, plus
     the token's bf16 q, k, v, beta, fp32 a and the fp32 output."""
@@ -502,21 +744,27 @@ def main():
             step(None)
         torch.cuda.synchronize()
         t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         w0 = time.perf_counter()
         t_start.record()
+        marks[0].record()
         for s in range(args.steps):
             step(dbgs[s])
+            marks[s + 1].record()
         t_end.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
         ms = t_start.elapsed_time(t_end) / args.steps
+        import statistics
+        med = statistics.median(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
         stage_ms = {}
         for i, name in enumerate(STAGES):
             tot = sum(hip.elapsed_ms(events[s][l][i], events[s][l][i + 1])
                       for s in range(args.steps) for l in range(L))
             stage_ms[name] = tot / (args.steps * L)
         stats = torch.stack([st for (_, _, _, st) in layers]).cpu()
-        return dict(ms_per_step=ms, wall_s=wall, stage_ms_per_launch=stage_ms, stats=stats)
+        return dict(ms_per_step=ms, median_ms_per_step=med, wall_s=wall, stage_ms_per_launch=stage_ms,
+                    stats=stats)
 
     res = {}
     for mode in (("sparse", "dense") if args.mode == "both" else (args.mode,)):
@@ -548,16 +796,29 @@ def main():
                     unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     algorithmic_bytes_per_launch=int(alg), launch_ms=round(st[dom], 4))
 
-    def path_roofline(mode):
-        """The whole layer against HBM: I/O streams plus snapshots over the
-        measured time per layer."""
+    def path_roofline(mode, o_bytes=2):
+        """The whole layer against HBM: the I/O streams (bf16 O as the
+        algorithmic byte count; o_bytes=4 gives the figure with the fp32 O
+        this run writes) plus the snapshots, over the measured time per
+        layer."""
         per_layer_ms = res[mode]["ms_per_step"] / args.layers
-        alg = algorithmic_bytes_per_token("path", mode, sigma, keep) * B * Tn
+        alg = path_bytes_per_token(mode, sigma if mode == "sparse" else 1.0, o_bytes) * B * Tn
         achieved = alg / (per_layer_ms / 1e3) / 1e9
         return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), algorithmic_bytes_per_layer=int(alg),
+                    bytes_per_token=round(alg / (B * Tn), 1), o_bytes=o_bytes,
                     ms_per_layer=round(per_layer_ms, 4),
                     roofline_ms_per_layer=round(alg / (HBM_PEAK_GBS * 1e9) * 1e3, 4))
+
+    def mfma_roofline(mode):
+        """The whole layer against the dense bf16 matrix-core peak with the
+        method's algorithmic flops (keep = measured event fraction)."""
+        per_layer_ms = res[mode]["ms_per_step"] / args.layers
+        fl = flops_per_token(mode, keep if mode == "sparse" else 1.0) * B * Tn
+        achieved = fl / (per_layer_ms / 1e3) / 1e12
+        return dict(bound="mfma", achieved=round(achieved, 1), peak=MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(achieved / MFMA_PEAK_TFLOPS, 4), flops_per_layer=int(fl),
+                    roofline_ms_per_layer=round(fl / (MFMA_PEAK_TFLOPS * 1e12) * 1e3, 4))
 
     out = {
         "metric": "GDN-core prefill tokens/s at T=32K/128K, dense vs 29% events; % roofline",
@@ -575,16 +836,26 @@ def main():
         "roofline": roofline(head),
     }
     for mode, rr in res.items():
+        pr, mr = path_roofline(mode), mfma_roofline(mode)
         out[mode] = {"value_tok_s": round(B * Tn / (rr["ms_per_step"] / 1e3), 1),
                      "per_layer_tok_s": round(B * Tn / (rr["ms_per_step"] / 1e3 / args.layers), 1),
                      "ms_per_step": round(rr["ms_per_step"], 4),
+                     "median_ms_per_step": round(rr["median_ms_per_step"], 4),
                      "stage_ms_per_launch": {k: round(v, 4) for k, v in rr["stage_ms_per_launch"].items()},
-                     "roofline": roofline(mode), "path_roofline": path_roofline(mode)}
+                     "roofline": roofline(mode), "path_roofline": pr,
+                     "path_roofline_fp32_o": path_roofline(mode, 4), "mfma_roofline": mr,
+                     "binding_roofline": "hbm" if pr["roofline_ms_per_layer"] >= mr["roofline_ms_per_layer"] else "mfma"}
     if "sparse" in res:
         out["sparse"]["measured_keep"] = round(keep, 5)
         out["sparse"]["snapshot_fraction"] = round(sigma, 5)
     if "sparse" in res and "dense" in res:
         out["sparse_speedup_over_dense"] = round(res["dense"]["ms_per_step"] / res["sparse"]["ms_per_step"], 3)
+    if not args.no_sweep and args.mode == "both":
+        out["length_sweep"] = sweep_leg(args, layers, ws)
+        if "32768" in out["length_sweep"]:
+            out["t32k"] = out["length_sweep"]["32768"]
+    if not args.no_grid and args.mode == "both":
+        out["keep_batch_grid"] = grid_leg(args, dev)
     if not args.no_ablations and "sparse" in res:
         out["pipeline_ablations"] = ablation_leg(args, layers, hip, prob, dev)
     if not args.no_variants and "sparse" in res:
@@ -600,7 +871,12 @@ def main():
         out["varlen"] = varlen_leg(args, layers, hip)
     if args.decode_batch > 0:
         out["decode"] = decode_leg(args, hip, dev)
-    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(layers[0][0], args.cpu_tokens)
+    out["cpu_baseline"] = None
+    if not args.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = cpu_baseline(layers, args.cpu_tokens, args.cpu_workers)
+        except Exception as e:   # the GPU figures above stand without it
+            print(f"[bench] cpu baseline failed: {e!r}", file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 
