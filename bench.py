@@ -24,6 +24,9 @@ length the metric names), and the keep-budget x batch grid of Sec. 3.3-3.4
 (batch 2 / 4 / 8 of 32768 tokens, keep 0.15 / 0.29 / 0.5 / 1.0, per-head
 decay scale u ~ U(0, ln 16)) is timed against the dense path at each batch.
 
+Every timed prefill writes an fp16 O (fp32 a and s_final); an output leg
+repeats both modes with an fp32 and a bf16 O.
+
 Prints one JSON line.  value = tokens/s of the 24-layer stack (B*T per step);
 each timed configuration reports the mean and the median over its steps.
 roofline = the dominant kernel's algorithmic bytes per layer over its mean
@@ -32,7 +35,7 @@ in the sparse path the H scan of CSR rows 4-15 runs on a second stream
 during the launch for rows 0-3, which the events bracket, so the bytes of
 both count over that time; traffic likewise sums both launches).
 path_roofline = the whole layer against HBM with the algorithmic bytes of
-the I/O streams (bf16 Q, K, V, O; fp32 a; bf16 beta) plus the compact
+the I/O streams (bf16 Q, K, V; fp16 O; fp32 a; bf16 beta) plus the compact
 snapshots written and read; mfma = the algorithmic flops of the method over
 the same time against the dense bf16 matrix-core peak.
 cpu_baseline = the fp64 numpy oracle as it stands, one worker process per
@@ -56,6 +59,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 matrix cores, published
 B, T, NQ, NV, D = 1, 131072, 16, 32, 128
+O_DTYPE = "fp16"               # output o of every timed prefill (fp32 and bf16 O: output_leg)
 LAYERS = 24
 STAGES = ("intra", "prefix", "gate", "select", "deferred_w", "hscan", "o")
 
@@ -81,8 +85,8 @@ def parse():
                     help="skip the packed variable-length leg")
     ap.add_argument("--no-ablations", action="store_true",
                     help="skip the kernel-pipeline ablation leg")
-    ap.add_argument("--no-bf16-output", action="store_true",
-                    help="skip the leg that reruns both modes with a bf16 O")
+    ap.add_argument("--no-output-types", action="store_true",
+                    help="skip the leg that reruns both modes with an fp32 and a bf16 O")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the selector-ablation leg")
     ap.add_argument("--decode-batch", type=int, default=128,
@@ -115,14 +119,14 @@ class Hip:
 
 def algorithmic_bytes_per_token(stage: str, mode: str, sigma: float, keep: float) -> float:
     """Bytes per token of the I/O streams a stage must move: bf16 Q, K, V, a
-    (fp32) and beta, O counted as bf16 (the output stream of the problem
-    statement; this run writes an fp32 O), and the fp16 group snapshots (one 128x128 state
+    (fp32) and beta, a 2-byte O (the output stream of the problem statement;
+    this run writes it as fp16), and the fp16 group snapshots (one 128x128 state
     per head per two chunks, written by the H scan and read by O); pipeline
     intermediates (U, U', W or Cb, K^T tiles) are not counted."""
     k_in = NQ * D * 2           # K (shared by a head pair)
     q_in = NQ * D * 2
     v_in = NV * D * 2
-    o_out = NV * D * 2          # O as the algorithmic byte count has it (bf16)
+    o_out = NV * D * 2          # O at 2 bytes (fp16 here)
     a_b = NV * 4 + NV * 2       # a (fp32) + beta (bf16)
     snap = NV * D * D * 2 / 128 * (sigma if mode == "sparse" else 1.0)   # one direction
     if stage == "intra":
@@ -138,7 +142,7 @@ def algorithmic_bytes_per_token(stage: str, mode: str, sigma: float, keep: float
 
 def path_bytes_per_token(mode: str, sigma: float, o_bytes: int = 2) -> float:
     """Algorithmic HBM bytes per token of one layer: the I/O streams (bf16 Q,
-    K, V and O by default, fp32 a, bf16 beta) plus the fp16 group snapshots,
+    K, V, a 2-byte O by default, fp32 a, bf16 beta) plus the fp16 group snapshots,
     one 128x128 state per head per two chunks written once and read once
     (the fraction sigma of them in the sparse path)."""
     io = NQ * D * 2 * 2 + NV * D * 2 + NV * D * o_bytes + NV * 4 + NV * 2
@@ -402,7 +406,7 @@ def varlen_leg(args, layers, hip):
                       device="cuda")
     Tm = max(lens)
     inp0 = layers[0][0]
-    prob = ops.problem(inp0["q"], inp0["v"], "blockadj", torch.float32, cu, Tm)
+    prob = ops.problem(inp0["q"], inp0["v"], "blockadj", torch.float16, cu, Tm)
     wsb = max(ops.workspace_bytes(prob, True, ops.sparse_params()), ops.workspace_bytes(prob, False))
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     nseq = len(lens)
@@ -491,40 +495,36 @@ def variants_leg(args, layers, ws, C):
     return out
 
 
-def bf16_output_leg(args, layers, ws):
-    """Both modes with a bf16 O (the output dtype the pages' problem statement
-    gives).  The headline keeps the fp32 O, the only output that meets the
-    parity bar at these decays (a bf16 rounding of the exact O alone exceeds
-    it); this leg shows what the narrower output stream saves."""
+def output_leg(args, layers, ws):
+    """Both modes with an fp32 O and with a bf16 O beside the headline's fp16
+    O.  fp16 carries an 11-bit significand, so its rounding (at most 2^-11
+    of an element) stays well inside the parity bar; a bf16 O (the pages'
+    model dtype) rounds to 2^-8 of an element, which alone exceeds the bar
+    on the largest outputs; fp32 shows what the wider output stream costs."""
     import torch
     from gated_deltanet_prefill_chunkwise_amd import ops
-    outs = [torch.empty(inp["v"].shape, dtype=torch.bfloat16, device="cuda") for (inp, _, _, _) in layers]
     res = {}
-    for mode in ("sparse", "dense"):
-        def step():
-            for l, (inp, _, sf, st) in enumerate(layers):
-                if mode == "sparse":
-                    ops.prefill_sparse(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"],
-                                       z=inp["z"], keep_budget=0.29, solve="blockadj", o=outs[l],
-                                       s_final=sf, stats=st, workspace=ws)
-                else:
-                    ops.prefill_dense(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"],
-                                      solve="exact", o=outs[l], s_final=sf, workspace=ws)
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(args.steps):
-            step()
-        t1.record()
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / args.steps
-        res[mode] = {"ms_per_step": round(ms, 4), "value_tok_s": round(B * args.seqlen / (ms / 1e3), 1)}
-        print(f"[bench] {mode}, bf16 O: {ms:.3f} ms per {args.layers}-layer step",
-              file=sys.stderr, flush=True)
-    del outs
-    res["sparse_speedup_over_dense"] = round(res["dense"]["ms_per_step"] / res["sparse"]["ms_per_step"], 3)
+    for name, dt in (("fp32", torch.float32), ("bf16", torch.bfloat16)):
+        outs = [torch.empty(inp["v"].shape, dtype=dt, device="cuda") for (inp, _, _, _) in layers]
+        row = {}
+        for mode in ("sparse", "dense"):
+            def step(_i, mode=mode):
+                for l, (inp, _, sf, st) in enumerate(layers):
+                    if mode == "sparse":
+                        ops.prefill_sparse(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"],
+                                           z=inp["z"], keep_budget=0.29, solve="blockadj",
+                                           o=outs[l], s_final=sf, stats=st, workspace=ws)
+                    else:
+                        ops.prefill_dense(inp["q"], inp["k"], inp["v"], inp["a"], inp["beta"],
+                                          solve="exact", o=outs[l], s_final=sf, workspace=ws)
+            mean, med = timed_steps(args, step)
+            row[mode] = {"ms_per_step": round(mean, 4), "median_ms_per_step": round(med, 4),
+                         "value_tok_s": round(B * args.seqlen / (mean / 1e3), 1)}
+            print(f"[bench] {mode}, {name} O: {mean:.3f} ms per {args.layers}-layer step",
+                  file=sys.stderr, flush=True)
+        del outs
+        row["sparse_speedup_over_dense"] = round(row["dense"]["ms_per_step"] / row["sparse"]["ms_per_step"], 3)
+        res[f"{name}_o"] = row
     return res
 
 
@@ -588,10 +588,10 @@ def grid_leg(args, dev):
     Tg, Bmax = 32768, 8
     inp = synth.torch_inputs(synth.seed_for(4, 0) + Bmax, Bmax, Tg, NQ, NV, dtype="bf16",
                              with_z=True, u_max=math.log(16.0), device=dev)
-    o = torch.empty((Bmax, Tg, NV, D), dtype=torch.float32, device=dev)
+    o = torch.empty((Bmax, Tg, NV, D), dtype=torch.float16, device=dev)
     sf = torch.empty((Bmax, NV, D, D), dtype=torch.float32, device=dev)
     st = torch.zeros((Bmax, ops.STATS_INTS), dtype=torch.int32, device=dev)
-    prob = ops.problem(inp["q"], inp["v"], "blockadj", torch.float32)
+    prob = ops.problem(inp["q"], inp["v"], "blockadj", torch.float16)
     ws = torch.empty(max(ops.workspace_bytes(prob, True, ops.sparse_params()),
                          ops.workspace_bytes(prob, False)), dtype=torch.uint8, device=dev)
     out = {}
@@ -714,11 +714,11 @@ def main():
     for l in range(L):
         inp = synth.torch_inputs(synth.seed_for(3, l), B, Tn, NQ, NV, dtype="bf16", with_z=True,
                                  device=dev)
-        o = torch.empty((B, Tn, NV, D), dtype=torch.float32, device=dev)
+        o = torch.empty((B, Tn, NV, D), dtype=torch.float16, device=dev)
         sf = torch.empty((B, NV, D, D), dtype=torch.float32, device=dev)
         st = torch.zeros((B, ops.STATS_INTS), dtype=torch.int32, device=dev)
         layers.append((inp, o, sf, st))
-    prob = ops.problem(layers[0][0]["q"], layers[0][0]["v"], "blockadj", torch.float32)
+    prob = ops.problem(layers[0][0]["q"], layers[0][0]["v"], "blockadj", torch.float16)
     ws_bytes = max(ops.workspace_bytes(prob, True, ops.sparse_params()),
                    ops.workspace_bytes(prob, False))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -797,10 +797,8 @@ def main():
                     algorithmic_bytes_per_launch=int(alg), launch_ms=round(st[dom], 4))
 
     def path_roofline(mode, o_bytes=2):
-        """The whole layer against HBM: the I/O streams (bf16 O as the
-        algorithmic byte count; o_bytes=4 gives the figure with the fp32 O
-        this run writes) plus the snapshots, over the measured time per
-        layer."""
+        """The whole layer against HBM: the I/O streams (the 2-byte O this run
+        writes) plus the snapshots, over the measured time per layer."""
         per_layer_ms = res[mode]["ms_per_step"] / args.layers
         alg = path_bytes_per_token(mode, sigma if mode == "sparse" else 1.0, o_bytes) * B * Tn
         achieved = alg / (per_layer_ms / 1e3) / 1e9
@@ -832,7 +830,7 @@ def main():
                                f"{head} path" + (" (SparseGDN, keep budget 0.29, block-adjacent solve)"
                                                  if head == "sparse" else " (exact solve)"),
                    "batch": B, "seq_len": Tn, "n_qk_heads": NQ, "n_v_heads": NV, "d": D,
-                   "layers": args.layers, "o_dtype": "fp32", "parallelism": "none (1 GPU)"},
+                   "layers": args.layers, "o_dtype": O_DTYPE, "parallelism": "none (1 GPU)"},
         "roofline": roofline(head),
     }
     for mode, rr in res.items():
@@ -842,8 +840,7 @@ def main():
                      "ms_per_step": round(rr["ms_per_step"], 4),
                      "median_ms_per_step": round(rr["median_ms_per_step"], 4),
                      "stage_ms_per_launch": {k: round(v, 4) for k, v in rr["stage_ms_per_launch"].items()},
-                     "roofline": roofline(mode), "path_roofline": pr,
-                     "path_roofline_fp32_o": path_roofline(mode, 4), "mfma_roofline": mr,
+                     "roofline": roofline(mode), "path_roofline": pr, "mfma_roofline": mr,
                      "binding_roofline": "hbm" if pr["roofline_ms_per_layer"] >= mr["roofline_ms_per_layer"] else "mfma"}
     if "sparse" in res:
         out["sparse"]["measured_keep"] = round(keep, 5)
@@ -865,8 +862,8 @@ def main():
                           dtype=torch.uint8, device=dev)
         out["selector_variants"] = variants_leg(args, layers, vws, C)
         del vws
-    if not args.no_bf16_output and args.mode == "both":
-        out["bf16_output"] = bf16_output_leg(args, layers, ws)
+    if not args.no_output_types and args.mode == "both":
+        out["output_types"] = output_leg(args, layers, ws)
     if not args.no_varlen and args.mode == "both":
         out["varlen"] = varlen_leg(args, layers, hip)
     if args.decode_batch > 0:

@@ -16,6 +16,8 @@ namespace {
 using namespace sgdn;
 
 constexpr int NP_SPARSE = 16;
+static_assert(OUT_F32 == SGDN_F32 && OUT_BF16 == SGDN_BF16 && OUT_F16 == SGDN_F16,
+              "output element codes");
 
 struct Plan {
   int B, T, Nq, Nv, C, G, esz, isz, bf16, solve;
@@ -38,12 +40,17 @@ static_assert(B_COUNT <= (int)(sizeof(Plan::off) / sizeof(size_t)), "workspace t
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // k = clip(round(rho C), 2, C) in exact integer arithmetic, round half up.
-void tier_counts(int C, int bp, int k[3]) {
+// rbp: the caller's tier rates in basis points, or rbp[0] = 0 for the rates
+// derived from the budget bp.
+void tier_counts(int C, int bp, const int rbp[3], int k[3]) {
   static const int pct[3] = {8, 30, 95};
   for (int i = 0; i < 3; ++i) {
     if (C == 1) { k[i] = 1; continue; }
     long long num, den;
-    if (bp <= 2900) {
+    if (rbp[0] > 0) {
+      num = (long long)rbp[i] * C;
+      den = 10000;
+    } else if (bp <= 2900) {
       num = (long long)pct[i] * bp * C;
       den = 290000;
     } else {
@@ -59,12 +66,30 @@ void tier_counts(int C, int bp, int k[3]) {
 
 int budget_bp(float b) { return (int)floor((double)b * 10000.0 + 0.5); }
 
+// The caller's tier rates in basis points (floor(rho 10000 + 0.5)), or
+// {0, 0, 0} when all three are zero (rates derived from the keep budget).
+// Returns SGDN_EINVAL for a rate outside (0, 1], a non-finite rate, or rates
+// that decrease from Low to Medium to High.
+int rates_bp(const sgdn_sparse_params* sp, int r[3]) {
+  r[0] = r[1] = r[2] = 0;
+  if (sp->tier_rate[0] == 0.f && sp->tier_rate[1] == 0.f && sp->tier_rate[2] == 0.f) return SGDN_OK;
+  for (int i = 0; i < 3; ++i) {
+    const float x = sp->tier_rate[i];
+    if (!(x > 0.f) || !(x <= 1.f)) return SGDN_EINVAL;
+    r[i] = budget_bp(x);
+    if (r[i] < 1 || r[i] > 10000) return SGDN_EINVAL;
+  }
+  if (r[0] > r[1] || r[1] > r[2]) return SGDN_EINVAL;
+  return SGDN_OK;
+}
+
 int check_problem(const sgdn_problem* pr) {
   if (pr == nullptr) return SGDN_EINVAL;
   if (pr->batch < 1 || pr->seqlen < 1 || pr->n_qk < 1 || pr->n_v < 1) return SGDN_EINVAL;
   if (pr->dtype != SGDN_F32 && pr->dtype != SGDN_BF16) return SGDN_EINVAL;
   if (pr->solve != SGDN_SOLVE_EXACT && pr->solve != SGDN_SOLVE_BLOCKADJ) return SGDN_EINVAL;
-  if (pr->o_dtype != SGDN_F32 && pr->o_dtype != SGDN_BF16) return SGDN_EINVAL;
+  if (pr->o_dtype != SGDN_F32 && pr->o_dtype != SGDN_BF16 && pr->o_dtype != SGDN_F16)
+    return SGDN_EINVAL;
   if (pr->d_k != 128 || pr->d_v != 128) return SGDN_EUNSUPPORTED;
   if (pr->n_v != 2 * pr->n_qk) return SGDN_EUNSUPPORTED;
   // grid dimensions and 32-bit in-kernel offsets
@@ -76,6 +101,8 @@ int check_params(const sgdn_problem* pr, const sgdn_sparse_params* sp) {
   if (sp == nullptr) return SGDN_EINVAL;
   const int bp = budget_bp(sp->keep_budget);
   if (!(sp->keep_budget > 0.f) || bp < 1 || bp > 10000) return SGDN_EINVAL;
+  int rbp[3];
+  if (rates_bp(sp, rbp) != SGDN_OK) return SGDN_EINVAL;
   if (sp->tail != 8 && sp->tail != 16 && sp->tail != 32 && sp->tail != 64) return SGDN_EUNSUPPORTED;
   if (sp->r_window != 16) return SGDN_EUNSUPPORTED;
   if (sp->aux_stream != nullptr && (sp->aux_events[0] == nullptr || sp->aux_events[1] == nullptr ||
@@ -101,7 +128,11 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
   p.bf16 = pr->dtype == SGDN_BF16; p.esz = p.bf16 ? 2 : 4; p.solve = pr->solve;
   p.isz = p.bf16 ? 2 : 4;   // intermediates: fp16 for bf16 inputs, fp32 for fp32 inputs
   int k[3] = {p.C, p.C, p.C};
-  if (sparse) tier_counts(p.C, budget_bp(sp->keep_budget), k);
+  if (sparse) {
+    int rbp[3];
+    rates_bp(sp, rbp);
+    tier_counts(p.C, budget_bp(sp->keep_budget), rbp, k);
+  }
   p.ablate = sparse ? sp->ablate : 0;
   p.kL = k[0]; p.kM = k[1]; p.kH = k[2];
   const int NP = p.Nv / 2;
@@ -263,6 +294,7 @@ int launch_select_call(const Plan& pl, const float* score, const float* gamma, c
   SelectArgs sa{};
   sa.score = score; sa.gamma = gamma; sa.eta = eta;
   sa.B = pl.B; sa.C = pl.C; sa.keep_bp = budget_bp(params->keep_budget);
+  rates_bp(params, sa.rate_bp);
   sa.cu = pl.cu; sa.T = pl.T;
   sa.fixed_tiers = params->fixed_tiers; sa.unit_visibility = params->unit_visibility;
   sa.rank_key = params->rank_key;
@@ -406,7 +438,7 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   oa.stats = stw;
   oa.q = q; oa.k = k; oa.U = at<void>(ws, pl, B_U); oa.snap = at<void>(ws, pl, B_SNAP);
   oa.s0T = s0 ? at<void>(ws, pl, B_S0T) : nullptr;
-  oa.o_bf16 = prob->o_dtype == SGDN_BF16;
+  oa.o_type = prob->o_dtype;
   oa.g = at<float>(ws, pl, B_G); oa.gamma = at<float>(ws, pl, B_GAMMA); oa.P = nullptr;
   oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
   oa.cu = pl.cu;
@@ -425,7 +457,8 @@ int sgdn_decode_step(const sgdn_problem* prob, const void* q, const void* k, con
   if (pr.batch < 1 || pr.seqlen != 1 || pr.n_qk < 1 || pr.n_v < 1) return SGDN_EINVAL;
   if (pr.cu_seqlens != nullptr) return SGDN_EINVAL;
   if (pr.dtype != SGDN_F32 && pr.dtype != SGDN_BF16) return SGDN_EINVAL;
-  if (pr.o_dtype != SGDN_F32 && pr.o_dtype != SGDN_BF16) return SGDN_EINVAL;
+  if (pr.o_dtype != SGDN_F32 && pr.o_dtype != SGDN_BF16 && pr.o_dtype != SGDN_F16)
+    return SGDN_EINVAL;
   if (pr.d_k != 128 || pr.d_v != 128 || pr.n_v % pr.n_qk != 0) return SGDN_EUNSUPPORTED;
   if ((long long)pr.batch * pr.n_v > (1LL << 29)) return SGDN_EUNSUPPORTED;
   if (!q || !k || !v || !a || !beta || !s_in || !s_out || !o) return SGDN_EINVAL;
@@ -434,8 +467,7 @@ int sgdn_decode_step(const sgdn_problem* prob, const void* q, const void* k, con
   const char* o0 = reinterpret_cast<const char*>(s_out);
   if (i0 != o0 && i0 < o0 + sbytes && o0 < i0 + sbytes) return SGDN_EINVAL;
   if (((uintptr_t)s_in | (uintptr_t)s_out) & 15) return SGDN_EINVAL;   // 16-byte vector access
-  DecodeArgs da{q, k, v, a, beta, s_in, s_out, o, pr.batch, pr.n_qk, pr.n_v,
-                pr.o_dtype == SGDN_BF16};
+  DecodeArgs da{q, k, v, a, beta, s_in, s_out, o, pr.batch, pr.n_qk, pr.n_v, pr.o_dtype};
   SGDN_TRY(launch_decode(da, pr.dtype == SGDN_BF16, static_cast<hipStream_t>(stream)));
   return SGDN_OK;
 }
@@ -524,6 +556,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   sa.eta = at<float>(ws, pl, B_ETA);
   sa.eta_part = at<float>(ws, pl, B_ETAP); sa.eta_out = at<float>(ws, pl, B_ETA);
   sa.B = pl.B; sa.C = pl.C; sa.keep_bp = budget_bp(params->keep_budget);
+  rates_bp(params, sa.rate_bp);
   sa.cu = pl.cu; sa.T = pl.T;
   sa.fixed_tiers = params->fixed_tiers; sa.unit_visibility = params->unit_visibility;
   sa.pair_order = (pl.ablate & SGDN_ABLATE_TIER_SCHEDULE) != 0;
@@ -594,7 +627,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   OChunkArgs oa{};
   oa.q = q; oa.k = k; oa.U = at<void>(ws, pl, B_U); oa.snap = at<void>(ws, pl, B_SNAP);
   oa.s0T = s0 ? at<void>(ws, pl, B_S0T) : nullptr;
-  oa.o_bf16 = prob->o_dtype == SGDN_BF16;
+  oa.o_type = prob->o_dtype;
   oa.g = at<float>(ws, pl, B_G); oa.gamma = at<float>(ws, pl, B_GAMMA); oa.P = at<double>(ws, pl, B_P);
   oa.o = o; oa.B = pl.B; oa.T = pl.T; oa.Nq = pl.Nq; oa.Nv = pl.Nv; oa.C = pl.C; oa.G = pl.G;
   oa.cu = pl.cu; oa.row_pair = sa.row_pair;

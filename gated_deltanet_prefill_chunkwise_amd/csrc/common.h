@@ -200,10 +200,12 @@ constexpr int FRAG = 512;
 __device__ __forceinline__ int wblk(int q, int i) { return (q * 4 + i) * FRAG; }
 __device__ __forceinline__ int kblk(int mt, int ks) { return (mt * 2 + ks) * FRAG; }
 
-// Output element type (o may be fp32 or bf16 independently of the inputs).
+// Output element type (o may be fp32, bf16 or fp16 independently of the
+// inputs; the narrow types round to nearest even).
 template <typename O> __device__ __forceinline__ void st4o(O* p, f32x4 v);
 template <> __device__ __forceinline__ void st4o<float>(float* p, f32x4 v) { st4f(p, v); }
 template <> __device__ __forceinline__ void st4o<bf16>(bf16* p, f32x4 v) { st4<bf16>(p, v); }
+template <> __device__ __forceinline__ void st4o<fp16>(fp16* p, f32x4 v) { st4<fp16>(p, v); }
 
 // 16-byte vector copy helpers (global <-> LDS staging).
 struct alignas(16) V16 { uint32_t w[4]; };

@@ -121,8 +121,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs p) {
 template <typename E>
 hipError_t launch_decode_e(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((size_t)a.B * a.Nv * NCB));
-  if (a.o_bf16)
+  if (a.o_type == OUT_BF16)
     hipLaunchKernelGGL((decode_kernel<E, bf16>), grid, dim3(256), 0, s, a);
+  else if (a.o_type == OUT_F16)
+    hipLaunchKernelGGL((decode_kernel<E, fp16>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((decode_kernel<E, float>), grid, dim3(256), 0, s, a);
   return hipGetLastError();

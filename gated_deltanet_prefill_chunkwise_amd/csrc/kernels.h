@@ -7,6 +7,9 @@
 
 namespace sgdn {
 
+// Element type of the output o (the values of the boundary's sgdn_dtype).
+constexpr int OUT_F32 = 0, OUT_BF16 = 1, OUT_F16 = 2;
+
 // Workspace tensors (all per batch b, head-major).  I is the intermediate
 // element type: fp16 for bf16 inputs, fp32 for fp32 inputs.
 //   g      [B][Nv][C][64]      fp32  in-chunk inclusive log2 decay
@@ -92,7 +95,7 @@ struct HScanArgs {
 struct OChunkArgs {
   const void* q; const void* k; const void* U; const void* snap; const void* s0T;
   const float* g; const float* gamma; const double* P;
-  void* o; int o_bf16;
+  void* o; int o_type;   // OUT_* element type of o
   int B, T, Nq, Nv, C, G;
   const int32_t* cu;          // packed sequence offsets [B+1] or null
   int sparse;
@@ -168,6 +171,7 @@ struct SelectArgs {
   // (prefill) eta from the gate kernel's parts, written to eta_out
   const float* eta_part; float* eta_out;
   int B, C, keep_bp;
+  int rate_bp[3];   // caller's tier rates in basis points, or {0, 0, 0}
   // packed sequence offsets [B+1] or null: sequence b has ceil(len_b / 64)
   // valid chunks (arrays keep the stride C); T bounds every length
   const int32_t* cu; int T;
@@ -207,7 +211,7 @@ struct DeferredWArgs {
 struct DecodeArgs {
   const void* q; const void* k; const void* v; const float* a; const void* beta;
   const float* s_in; float* s_out; void* o;
-  int B, Nq, Nv, o_bf16;
+  int B, Nq, Nv, o_type;   // OUT_* element type of o
 };
 
 hipError_t launch_intra(const IntraArgs& a, int bf16, hipStream_t s);

@@ -238,7 +238,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   const float scale = 0.08838834764831845f;   // 128^-1/2
   __syncthreads();   // Q and A^T are no longer read
   // (rows past the end of a sequence hold zeros, so the check covers only
-  // what is stored)
+  // what is stored; a finite value beyond the range of o's type counts too)
   bool nfo = false;
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       v[jj] *= scale;
-      nfo |= !__builtin_isfinite(v[jj]);
+      nfo |= !__builtin_isfinite(to_f(from_f<OT>(v[jj])));   // as stored (range of o's type)
     }
     *reinterpret_cast<f32x4*>(&sO[(16 * j + n16) * OSTR + 16 * w + 4 * g4]) = v;
   }
@@ -264,19 +264,22 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   }
 }
 
+template <typename E, bool ONE>
+void launch_e(const OChunkArgs& a, dim3 grid, hipStream_t s) {
+  if (a.o_type == OUT_BF16)
+    hipLaunchKernelGGL((ochunk_kernel<E, sgdn::bf16, ONE>), grid, dim3(512), 0, s, a);
+  else if (a.o_type == OUT_F16)
+    hipLaunchKernelGGL((ochunk_kernel<E, sgdn::fp16, ONE>), grid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((ochunk_kernel<E, float, ONE>), grid, dim3(512), 0, s, a);
+}
+
 template <bool ONE>
 void launch_one(const OChunkArgs& a, int bf16, dim3 grid, hipStream_t s) {
-  if (bf16) {
-    if (a.o_bf16)
-      hipLaunchKernelGGL((ochunk_kernel<sgdn::bf16, sgdn::bf16, ONE>), grid, dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((ochunk_kernel<sgdn::bf16, float, ONE>), grid, dim3(512), 0, s, a);
-  } else {
-    if (a.o_bf16)
-      hipLaunchKernelGGL((ochunk_kernel<float, sgdn::bf16, ONE>), grid, dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((ochunk_kernel<float, float, ONE>), grid, dim3(512), 0, s, a);
-  }
+  if (bf16)
+    launch_e<sgdn::bf16, ONE>(a, grid, s);
+  else
+    launch_e<float, ONE>(a, grid, s);
 }
 
 }  // namespace

@@ -74,17 +74,21 @@ __device__ int valid_chunks(const SelectArgs& p, int b) {
   return p.cu == nullptr ? p.C : chunks_of(seq_span(p.cu, b, p.T).len);
 }
 
-// k = clip(round(rho C), 2, C) (Sec. 2.4.3) for the budget in basis points,
-// in exact integer arithmetic with halves rounded up; rho = (0.08, 0.30, 0.95)
-// at 2900 bp, scaled linearly below it and towards 1 above it.  k = 1 when
-// C = 1 and 0 for an empty sequence.
-__device__ void tier_counts(int C, int bp, int k[3]) {
+// k = clip(round(rho C), 2, C) (Sec. 2.4.3) in exact integer arithmetic with
+// halves rounded up.  With the caller's rates (rbp[0] > 0, basis points) rho
+// is those; otherwise rho = (0.08, 0.30, 0.95) at a budget of 2900 bp, scaled
+// linearly below it and towards 1 above it.  k = 1 when C = 1 and 0 for an
+// empty sequence.
+__device__ void tier_counts(int C, int bp, const int rbp[3], int k[3]) {
   const int pct[3] = {8, 30, 95};
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
     if (C == 1) { k[i] = 1; continue; }
     long long num, den;
-    if (bp <= 2900) {
+    if (rbp[0] > 0) {
+      num = (long long)rbp[i] * C;
+      den = 10000;
+    } else if (bp <= 2900) {
       num = (long long)pct[i] * bp * C;
       den = 290000;
     } else {
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(1024) void select_tier_kernel(SelectArgs p) {
   const int b = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int CS = p.C, C = valid_chunks(p, b);
   int kk[3];
-  tier_counts(C, p.keep_bp, kk);
+  tier_counts(C, p.keep_bp, p.rate_bp, kk);
   const int kL = kk[0], kM = kk[1], kH = kk[2];
   const float* sc = p.score + (size_t)b * NV * CS;
   const float* gm = p.gamma + (size_t)b * NV * CS;
@@ -368,7 +372,7 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
   const int CS = p.C, GS = p.G, NW = (CS + 63) / 64;
   const int C = valid_chunks(p, b), G = (C + 1) / 2;
   int kk[3];
-  tier_counts(C, p.keep_bp, kk);
+  tier_counts(C, p.keep_bp, p.rate_bp, kk);
   const int kL = kk[0], kM = kk[1], kH = kk[2];
   const unsigned long long below = (1ull << lane) - 1ull;
   uint8_t* mask = p.mask + (size_t)b * NP * CS;

@@ -12,7 +12,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsgdn.so")
 
-SGDN_F32, SGDN_BF16 = 0, 1
+SGDN_F32, SGDN_BF16, SGDN_F16 = 0, 1, 2
 SOLVES = {"exact": 0, "blockadj": 1}
 EXPORTS = ("sgdn_workspace_bytes", "sgdn_event_capacity", "sgdn_prefill_dense", "sgdn_select",
            "sgdn_prefill_sparse", "sgdn_decode_step", "sgdn_status_string", "sgdn_fp64_selftest",
@@ -27,7 +27,8 @@ class Problem(ctypes.Structure):
 
 
 class SparseParams(ctypes.Structure):
-    _fields_ = [("keep_budget", ctypes.c_float), ("tail", ctypes.c_int32),
+    _fields_ = [("keep_budget", ctypes.c_float), ("tier_rate", ctypes.c_float * 3),
+                ("tail", ctypes.c_int32),
                 ("r_window", ctypes.c_int32), ("norm_weight", ctypes.c_void_p),
                 ("fixed_tiers", ctypes.c_int32), ("unit_visibility", ctypes.c_int32),
                 ("rank_key", ctypes.c_void_p), ("ablate", ctypes.c_int32),
@@ -123,8 +124,21 @@ def _stream(stream):
 
 
 def _code(dtype):
+    """sgdn_dtype of an input tensor dtype (fp32 or bf16)."""
     import torch
-    return SGDN_BF16 if dtype == torch.bfloat16 else SGDN_F32
+    codes = {torch.float32: SGDN_F32, torch.bfloat16: SGDN_BF16}
+    if dtype not in codes:
+        raise ValueError(f"inputs must be float32 or bfloat16, got {dtype}")
+    return codes[dtype]
+
+
+def _ocode(dtype):
+    """sgdn_dtype of the output o (fp32, bf16 or fp16)."""
+    import torch
+    codes = {torch.float32: SGDN_F32, torch.bfloat16: SGDN_BF16, torch.float16: SGDN_F16}
+    if dtype not in codes:
+        raise ValueError(f"o must be float32, bfloat16 or float16, got {dtype}")
+    return codes[dtype]
 
 
 def batch_shape(q, cu_seqlens=None, max_seqlen=None):
@@ -149,22 +163,25 @@ def problem(q, v, solve="exact", out_dtype=None, cu_seqlens=None, max_seqlen=Non
     B, T = batch_shape(q, cu_seqlens, max_seqlen)
     Nq, d = q.shape[2], q.shape[3]
     Nv, dv = v.shape[2], v.shape[3]
-    od = _code(out_dtype) if out_dtype is not None else SGDN_F32
+    od = _ocode(out_dtype) if out_dtype is not None else SGDN_F32
     return Problem(B, T, Nq, Nv, d, dv, _code(q.dtype), SOLVES[solve], od,
                    None if cu_seqlens is None else cu_seqlens.data_ptr())
 
 
 def sparse_params(keep_budget=0.29, norm_weight=None, tail=16, r_window=16, fixed_tiers=False,
-                  unit_visibility=False, rank_key=None, ablate=(), aux=None) -> SparseParams:
+                  unit_visibility=False, rank_key=None, ablate=(), aux=None,
+                  tier_rate=None) -> SparseParams:
     """Selector parameters; ``rank_key`` (device fp32 [B, Nv/2, C]) and the
     flags are the selector ablations, ``ablate`` names kernel-pipeline
-    ablations (keys of ABLATE), all described in include/sgdn.h.  ``aux`` is
-    an (aux stream, fork event, join event) triple of torch objects, or None
-    for the one-stream schedule."""
+    ablations (keys of ABLATE), ``tier_rate`` a (rho_L, rho_M, rho_H)
+    override of the budget's tier rates, all described in include/sgdn.h.
+    ``aux`` is an (aux stream, fork event, join event) triple of torch
+    objects, or None for the one-stream schedule."""
     bits = 0
     for name in ablate:
         bits |= ABLATE[name]
-    p = SparseParams(float(keep_budget), tail, r_window,
+    rates = (ctypes.c_float * 3)(*((0.0, 0.0, 0.0) if tier_rate is None else tier_rate))
+    p = SparseParams(float(keep_budget), rates, tail, r_window,
                      None if norm_weight is None else norm_weight.data_ptr(),
                      int(bool(fixed_tiers)), int(bool(unit_visibility)),
                      None if rank_key is None else rank_key.data_ptr(), bits)
@@ -331,7 +348,7 @@ def decode_step(q, k, v, a, beta, state, s_out=None, o=None, out_dtype=None, str
                         (o, (B, Nv, dv), "o")):
         if tuple(t.shape) != shape:
             raise ValueError(f"{n} must have shape {shape}, got {tuple(t.shape)}")
-    prob = Problem(B, 1, Nq, Nv, d, dv, _code(q.dtype), 0, _code(out_dtype))
+    prob = Problem(B, 1, Nq, Nv, d, dv, _code(q.dtype), 0, _ocode(out_dtype))
     st = lib().sgdn_decode_step(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                 _ptr(beta), _ptr(state), _ptr(s_out), _ptr(o), _stream(stream))
     if st != 0:
@@ -340,7 +357,8 @@ def decode_step(q, k, v, a, beta, state, s_out=None, o=None, out_dtype=None, str
 
 
 def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None, cu_seqlens=None,
-           fixed_tiers=False, unit_visibility=False, rank_key=None, noalloc=False, out=None):
+           fixed_tiers=False, unit_visibility=False, rank_key=None, noalloc=False, out=None,
+           tier_rate=None):
     """Selector + CSR layout on fp32 statistics; returns a dict of device tensors.
 
     With ``cu_seqlens`` (int32 [B + 1] token offsets) sequence b has only its
@@ -362,7 +380,7 @@ def select(score, gamma, eta, keep_budget=0.29, workspace=None, stream=None, cu_
     prob = Problem(B, T, Nv // 2, Nv, 128, 128, SGDN_BF16, 1, SGDN_F32,
                    None if cu_seqlens is None else cu_seqlens.data_ptr())
     params = sparse_params(keep_budget, fixed_tiers=fixed_tiers, unit_visibility=unit_visibility,
-                           rank_key=rank_key)
+                           rank_key=rank_key, tier_rate=tier_rate)
     NP, G = Nv // 2, (C + 1) // 2
     dev = score.device
     _, e_max = event_capacity(prob, params)
@@ -405,7 +423,7 @@ def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
                    mask_override=None, s0=None, norm_weight=None, want_state=True, o=None,
                    s_final=None, stats=None, workspace=None, debug=None, stream=None,
                    out_dtype=None, cu_seqlens=None, max_seqlen=None, tail=16, fixed_tiers=False,
-                   unit_visibility=False, rank_key=None, ablate=(), aux=True):
+                   unit_visibility=False, rank_key=None, ablate=(), aux=True, tier_rate=None):
     """SparseGDN prefill; returns (o, s_final, stats[B, STATS_INTS] int32).
 
     o is fp32 unless ``out_dtype`` (or a given ``o``) says otherwise.  With
@@ -436,7 +454,7 @@ def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
         aux = None
     params = sparse_params(keep_budget, norm_weight, tail=tail, fixed_tiers=fixed_tiers,
                            unit_visibility=unit_visibility, rank_key=rank_key, ablate=ablate,
-                           aux=aux)
+                           aux=aux, tier_rate=tier_rate)
     B, Nv, dv = prob.batch, v.shape[2], v.shape[3]
     if o is None:
         o = torch.empty(v.shape, dtype=out_dtype, device=v.device)

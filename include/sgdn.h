@@ -50,7 +50,9 @@
  *   near 1, or a state that large) becomes infinite, which surfaces as a
  *   non-finite o or s_final and sets nonfinite_output.  The state and its
  *   accumulation are always fp32.  A bf16 o adds its own rounding (up to
- *   2^-8 of each element).
+ *   2^-8 of each element), an fp16 o up to 2^-11 of each element (and holds
+ *   magnitudes up to 65504: a larger output element is stored as infinite
+ *   and sets nonfinite_output).
  * - T need not be a multiple of 64: the last chunk is padded with tokens
  *   that have a = 0, beta = 0, q = k = v = 0; their outputs are not written.
  * - Packed variable-length batches: with sgdn_problem.cu_seqlens set, the B
@@ -83,7 +85,8 @@ typedef enum {
   SGDN_EHIP = -4           /* a HIP launch failed                                */
 } sgdn_status;
 
-typedef enum { SGDN_F32 = 0, SGDN_BF16 = 1 } sgdn_dtype;
+/* SGDN_F16 (IEEE binary16) is accepted for o_dtype only. */
+typedef enum { SGDN_F32 = 0, SGDN_BF16 = 1, SGDN_F16 = 2 } sgdn_dtype;
 typedef enum { SGDN_SOLVE_EXACT = 0, SGDN_SOLVE_BLOCKADJ = 1 } sgdn_solve;
 
 /* Problem shape.  dtype applies to q, k, v, beta and z; o_dtype to o (a, s0
@@ -94,7 +97,7 @@ typedef struct {
   int32_t batch, seqlen, n_qk, n_v, d_k, d_v;
   int32_t dtype;    /* sgdn_dtype of q, k, v, beta, z */
   int32_t solve;    /* sgdn_solve */
-  int32_t o_dtype;  /* sgdn_dtype of o */
+  int32_t o_dtype;  /* sgdn_dtype of o: SGDN_F32, SGDN_BF16 or SGDN_F16 */
   /* DEVICE [batch + 1] int32 token offsets of packed sequences (non-
    * decreasing, cu_seqlens[0] = 0, cu_seqlens[batch] < 2^31 - seqlen), or
    * NULL for the dense [B, T] layout.  Read by the kernels, not the host. */
@@ -120,6 +123,13 @@ typedef struct {
  *                        (random keys = random selection at matched budget). */
 typedef struct {
   float keep_budget;
+  /* Tier rates (rho_L, rho_M, rho_H) of Eq. (13) overriding the ones derived
+   * from keep_budget (which is then not used), or all three 0 for the derived
+   * rates.  Each is taken in basis points, floor(rho * 10000 + 0.5), must lie
+   * in (0, 1] and must not decrease from Low to High; otherwise SGDN_EINVAL.
+   * k_l = clip(round(rho_l C), 2, C) with halves rounded up, as for the
+   * derived rates. */
+  float tier_rate[3];
   int32_t tail;
   int32_t r_window;
   const float* norm_weight;
@@ -245,7 +255,8 @@ size_t sgdn_workspace_bytes(const sgdn_problem* prob, int sparse,
 /* Event capacity of the selector (Sec. 2.4.3, Eq. (13); Sec. 2.5: the CSR
  * column array holds at most E_max = 16 k_H events per sequence, and the
  * device-side E never exceeds it).  Writes k = (k_L, k_M, k_H) for C =
- * ceil(seqlen / 64) chunks at params->keep_budget (host memory, may be NULL)
+ * ceil(seqlen / 64) chunks at params->keep_budget or params->tier_rate
+ * (host memory, may be NULL)
  * and *e_max = 16 k_H, the per-sequence length of sgdn_select's col array.
  * Packed sequences with fewer chunks select fewer events.  Returns a negative
  * status for an invalid problem or parameters (nothing written). */

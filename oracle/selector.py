@@ -11,6 +11,7 @@ energies eta [Nv], for one sequence.
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -68,11 +69,12 @@ def gate_energy(z, norm_weight=None):
 # ---------------------------------------------------------------------------
 
 def budget_bp(keep_budget: float) -> int:
-    """Keep budget in basis points: floor(b * 10000 + 0.5) in binary64."""
-    return int(math.floor(float(keep_budget) * 10000.0 + 0.5))
+    """Keep budget in basis points: floor(b * 10000 + 0.5) in binary64, with b
+    first rounded to binary32 (the precision in which a caller hands it over)."""
+    return int(math.floor(float(np.float32(keep_budget)) * 10000.0 + 0.5))
 
 
-def tier_counts(C: int, keep_budget: float = 0.29):
+def tier_counts(C: int, keep_budget: float = 0.29, tier_rate=None):
     """(k_L, k_M, k_H) = clip(round(rho_l C), 2, C).  Sec. 2.4.3, Eq. (13).
 
     round() is half away from zero on the exact rational rho_l * C.  At the
@@ -80,7 +82,26 @@ def tier_counts(C: int, keep_budget: float = 0.29):
     rates (the page re-selects tiers per budget point without giving the map;
     reading used here): b <= 0.29: rho(b) = rho * b / 0.29;
     b > 0.29: rho(b) = 1 - (1 - rho)(1 - b) / 0.71.  C = 1 keeps the only chunk.
+
+    tier_rate = (rho_L, rho_M, rho_H) overrides the budget's rates; each is
+    taken in basis points (floor(rho * 10000 + 0.5)), must lie in (0, 1] and
+    must not decrease from Low to High.
     """
+    if tier_rate is not None:
+        rbp = [budget_bp(r) for r in tier_rate]
+        if len(rbp) != 3 or not all(1 <= r <= 10000 and 0.0 < float(x) <= 1.0
+                                    for r, x in zip(rbp, tier_rate)):
+            raise ValueError("tier rates must lie in (0, 1]")
+        if not rbp[0] <= rbp[1] <= rbp[2]:
+            raise ValueError("tier rates must not decrease from Low to High")
+        if C == 1:
+            return (1, 1, 1)
+        out = []
+        for r in rbp:
+            x = Fraction(r * C, 10000)
+            k = math.floor(x + Fraction(1, 2))
+            out.append(min(max(k, 2), C))
+        return tuple(out)
     bp = budget_bp(keep_budget)
     if not 1 <= bp <= 10000:
         raise ValueError("keep budget must lie in (0, 1]")
@@ -158,7 +179,8 @@ def _normalise(d):
 
 
 def select(score, gamma, eta, keep_budget: float = 0.29, window: int = 16,
-           fixed_tiers: bool = False, unit_visibility: bool = False, rank_key=None):
+           fixed_tiers: bool = False, unit_visibility: bool = False, rank_key=None,
+           tier_rate=None):
     """Dynamic event selection for one sequence.  Sec. 2.4, Eqs. (10)-(14).
 
     score, gamma: [Nv, C] (fp32 values); eta: [Nv].  Nv = 32 (16 head pairs;
@@ -177,6 +199,8 @@ def select(score, gamma, eta, keep_budget: float = 0.29, window: int = 16,
                        largest q_c; the tiers and the keep counts are still the
                        adaptive ones (random keys give the random selection at
                        matched budget).
+    tier_rate          (rho_L, rho_M, rho_H) in place of the budget's rates
+                       (see tier_counts).
     """
     s = np.asarray(score, np.float32).astype(np.float64)
     gm = np.asarray(gamma, np.float32).astype(np.float64)
@@ -185,7 +209,7 @@ def select(score, gamma, eta, keep_budget: float = 0.29, window: int = 16,
     if Nv != 32:
         raise ValueError("the tier table is defined for 16 head pairs (Nv = 32)")
     Np = Nv // 2
-    kL, kM, kH = tier_counts(C, keep_budget)
+    kL, kM, kH = tier_counts(C, keep_budget, tier_rate)
 
     # Eq. (10): per-head chunk norm and within-pair rank key.
     norms = [math.sqrt(csum([x * x for x in s[h].tolist()])) for h in range(Nv)]

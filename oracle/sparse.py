@@ -42,7 +42,7 @@ def deferred_w(Cb, kc, solve: str = "blockadj"):
 
 def sparse_prefill(q, k, v, a, beta, z=None, norm_weight=None, keep_budget=0.29,
                    solve="blockadj", s0=None, mask=None, return_all=False, tail=16,
-                   fixed_tiers=False, unit_visibility=False, rank_key=None):
+                   fixed_tiers=False, unit_visibility=False, rank_key=None, tier_rate=None):
     """End-to-end SparseGDN prefill for a batch of sequences.
 
     Steps (Sec. 2.2 pipeline, Fig. 3): intra (local solve, U, staged Cb,
@@ -52,7 +52,8 @@ def sparse_prefill(q, k, v, a, beta, z=None, norm_weight=None, keep_budget=0.29,
     ``mask`` [B, Nv/2, C] overrides the selector (then z is not needed).
     ``tail`` is the Tail window of Eq. (9) (8, 16, 32 or 64 rows); the
     selector ablations (``fixed_tiers``, ``unit_visibility``, ``rank_key``
-    [B, Nv/2, C]) are those of ``selector.select``.
+    [B, Nv/2, C]) and the ``tier_rate`` override are those of
+    ``selector.select``.
 
     H, per value head h in pair p (Eqs. (17)-(18) with Eqs. (1)-(2)):
         S_in(c) = S
@@ -86,7 +87,8 @@ def sparse_prefill(q, k, v, a, beta, z=None, norm_weight=None, keep_budget=0.29,
         eta = gate_energy(z, norm_weight).astype(np.float32)
         sel = [select(score[b], gamma32[b], eta[b], keep_budget, fixed_tiers=fixed_tiers,
                       unit_visibility=unit_visibility,
-                      rank_key=None if rank_key is None else rank_key[b]) for b in range(B)]
+                      rank_key=None if rank_key is None else rank_key[b],
+                      tier_rate=tier_rate) for b in range(B)]
         mask = np.stack([s["mask"] for s in sel])
     mask = np.asarray(mask).astype(bool)
     zh = np.repeat(mask, 2, axis=1)                      # [B, Nv, C] per value head

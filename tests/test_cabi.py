@@ -107,6 +107,16 @@ def test_event_capacity(L):
         ops.event_capacity(_prob(n_qk=8, n_v=16), ops.sparse_params())
     with pytest.raises(ops.SgdnError):
         ops.event_capacity(_prob(), ops.sparse_params(keep_budget=0.0))
+    # the caller's tier rates replace the budget's (Eq. (13) with rho given)
+    for T, rates in ((64 * 35, (0.1, 0.25, 0.5)), (32768, (0.08, 0.30, 0.95)),
+                     (131072, (0.05, 0.2, 0.6)), (64, (0.01, 0.01, 1.0))):
+        k, e_max = ops.event_capacity(_prob(seqlen=T), ops.sparse_params(0.5, tier_rate=rates))
+        assert k == selector.tier_counts(-(-T // 64), tier_rate=rates), (T, rates)
+        assert e_max == 16 * k[2]
+    for bad in ((0.3, 0.2, 0.9), (0.0, 0.3, 0.9), (0.1, 0.3, 1.5), (float("nan"), 0.3, 0.9),
+                (-0.1, 0.3, 0.9), (0.1, 0.3, float("inf"))):
+        with pytest.raises(ops.SgdnError):
+            ops.event_capacity(_prob(), ops.sparse_params(tier_rate=bad))
     e = ctypes.c_int32()
     assert L.sgdn_event_capacity(ctypes.byref(_prob()), ctypes.byref(ops.sparse_params()), None,
                                  None) == -1

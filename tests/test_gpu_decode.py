@@ -76,6 +76,15 @@ def test_decode_step_bf16_output():
     assert np.all(np.abs(o - o_ref) <= TOL["bf16"] * rms + 2.0 ** -8 * np.abs(o_ref))
 
 
+def test_decode_step_fp16_output():
+    import torch
+    tok = _token(922, 2, 16, 32, "bf16")
+    s = _state(923, 2, 32)
+    o, _ = _run(tok, s, "bf16", out_dtype=torch.float16)
+    o_ref, _ = gdn.decode_step(tok["q"], tok["k"], tok["v"], tok["a"], tok["beta"], s)
+    assert rel_max_err(o, o_ref) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_continues_gpu_prefill(dtype):
     """GPU dense prefill over T tokens, then three GPU decode steps from its

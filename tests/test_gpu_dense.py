@@ -102,6 +102,24 @@ def test_deterministic():
 
 
 @pytest.mark.parametrize("solve", ["exact", "blockadj"])
+def test_fp16_output(solve):
+    """o in fp16 (the benchmark's output type): the plain bf16-input bar, with
+    the output's own rounding (at most 2^-11 of the element) inside it."""
+    import torch
+    from gated_deltanet_prefill_chunkwise_amd import ops
+    inp = synth.numpy_inputs(synth.seed_for(1) + 8, 1, 2048 + 40, 16, 32, dtype="bf16")
+    d = to_device(inp)
+    o, S = ops.prefill_dense(d["q"], d["k"], d["v"], d["a"], d["beta"], solve=solve,
+                             out_dtype=torch.float16)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float16
+    o_ref, S_ref = gdn.chunk_prefill(inp.q, inp.k, inp.v, inp.a, inp.beta, None, solve)
+    eo, es = rel_max_err(host(o), o_ref), rel_max_err(host(S), S_ref)
+    print(f"fp16 o: err O {eo:.3e} S {es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("solve", ["exact", "blockadj"])
 def test_bf16_output(solve):
     """o in bf16: the bar is the fp32 bar plus the output's own rounding
     (half a bf16 ulp, at most 2^-8 of the element)."""

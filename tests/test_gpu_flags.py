@@ -25,18 +25,19 @@ def _inputs(seed=77):
     return synth.numpy_inputs(seed, 2, T, 16, 32, dtype="bf16", with_z=True, decay_scale=1 / 16)
 
 
-def _run(mode, d, s0=None):
+def _run(mode, d, s0=None, out_dtype=None):
     import torch
     from gated_deltanet_prefill_chunkwise_amd import ops
     st = torch.full((2, ops.STATS_INTS), -7, dtype=torch.int32, device="cuda")
     if mode == "dense":
         o, S = ops.prefill_dense(d["q"], d["k"], d["v"], d["a"], d["beta"], s0=s0, solve="exact",
-                                 stats=st)
+                                 stats=st, out_dtype=out_dtype)
     else:
         o, S, _ = ops.prefill_sparse(d["q"], d["k"], d["v"], d["a"], d["beta"], z=d["z"], s0=s0,
-                                     keep_budget=0.29, solve="blockadj", stats=st)
+                                     keep_budget=0.29, solve="blockadj", stats=st,
+                                     out_dtype=out_dtype)
     torch.cuda.synchronize()
-    return o.cpu().numpy(), S.cpu().numpy(), st.cpu().numpy()
+    return o.float().cpu().numpy(), S.cpu().numpy(), st.cpu().numpy()
 
 
 @pytest.mark.parametrize("mode", ["dense", "sparse"])
@@ -107,4 +108,22 @@ def test_fp16_range_overflow_is_flagged(mode):
     assert st[0, 9] == 0 and st[1, 9] == 0
     assert st[0, 10] & NF_O
     assert not np.isfinite(o[0]).all()
+    assert st[1, 10] == 0 and np.isfinite(o[1]).all()
+
+
+@pytest.mark.parametrize("mode", ["dense", "sparse"])
+def test_fp16_output_overflow_is_flagged(mode):
+    """fp32 inputs (fp32 intermediates) with |v| ~ 1e7: every intermediate and
+    the fp32 output are finite, but an fp16 o cannot hold the outputs; the
+    fp16 call flags nonfinite_output, the fp32 call does not."""
+    import torch
+    inp = synth.numpy_inputs(80, 2, T, 16, 32, dtype="f32", with_z=True, decay_scale=1 / 16)
+    d = to_device(inp)
+    d["v"][0] = d["v"][0] * 1e7
+    o, S, st = _run(mode, d)
+    assert (st[:, 9:] == 0).all(), st
+    assert np.isfinite(o).all() and np.abs(o[0]).max() > 1e5
+    o, S, st = _run(mode, d, out_dtype=torch.float16)
+    assert st[0, 9] == 0 and st[1, 9] == 0
+    assert st[0, 10] == NF_O and not np.isfinite(o[0]).all()
     assert st[1, 10] == 0 and np.isfinite(o[1]).all()

@@ -4,7 +4,7 @@ One layer of the benchmark workload (T = 131072, bf16, B = 1, Nq = 16, Nv = 32,
 the benchmark's seed for layer 0, inputs drawn on the device) runs on the GPU
 for all 32 heads, as the benchmark launches it (the sparse path with the
 binding's second stream: CSR rows 0-3 on the caller's stream, 4-15 beside
-them).  The fp64 oracle then checks:
+them; fp16 o).  The fp64 oracle then checks:
 
 * dense: one head pair over the whole sequence (O at every token and S_final);
   pairs are independent, so the pair's oracle run is the full problem
@@ -57,7 +57,8 @@ def test_full_size_dense_pair(decay):
     import torch
     from gated_deltanet_prefill_chunkwise_amd import ops
     d = _device_inputs(decay)
-    o, S = ops.prefill_dense(d["q"], d["k"], d["v"], d["a"], d["beta"], solve="exact")
+    o, S = ops.prefill_dense(d["q"], d["k"], d["v"], d["a"], d["beta"], solve="exact",
+                             out_dtype=torch.float16)
     torch.cuda.synchronize()
     p = 11
     x = _pair_inputs(d, p)
@@ -81,7 +82,8 @@ def test_full_size_sparse_selector_and_tier_pairs(decay):
     tier = torch.empty((1, NV // 2), dtype=torch.uint8, device="cuda")
     dbg = ops.debug_struct(score=score, gamma=gam, eta=eta, mask=mask, tier=tier)
     o, S, st = ops.prefill_sparse(d["q"], d["k"], d["v"], d["a"], d["beta"], z=d["z"],
-                                  keep_budget=0.29, solve="blockadj", debug=dbg)
+                                  keep_budget=0.29, solve="blockadj", debug=dbg,
+                                  out_dtype=torch.float16)
     torch.cuda.synchronize()
     m_gpu, t_gpu = mask.cpu().numpy()[0], tier.cpu().numpy()[0]
     # selector: identical fp32 statistics give identical integers

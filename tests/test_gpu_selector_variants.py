@@ -1,6 +1,7 @@
 """Selector ablations on the GPU (Sec. 3.5, Table 5, Fig. 10): fixed 3/4/9
 tiers, G_h = 1, caller rank keys (random selection at matched budget) and
-the Tail-8/32/64 score windows.
+the Tail-8/32/64 score windows; and the caller's tier rates in place of the
+budget's (Eq. (13) with rho given).
 
 * sgdn_select with each switch: mask, tiers, CSR rows, predecessors and
   snapshot slots bit-exact against the oracle selector with the same switch
@@ -21,7 +22,8 @@ from helpers import TOL, host, rel_max_err, to_device
 pytestmark = pytest.mark.gpu
 
 VARIANTS = [dict(fixed_tiers=True), dict(unit_visibility=True), dict(rank_key="random"),
-            dict(fixed_tiers=True, unit_visibility=True, rank_key="random")]
+            dict(fixed_tiers=True, unit_visibility=True, rank_key="random"),
+            dict(tier_rate=(0.05, 0.2, 0.6)), dict(tier_rate=(0.5, 0.5, 1.0), rank_key="random")]
 
 
 def _keys(seed, B, C):
@@ -46,7 +48,8 @@ def test_select_variants_bit_exact(C, vi):
         ref = selector.select(score[b], gamma[b], eta[b], keep_budget=0.29,
                               fixed_tiers=var.get("fixed_tiers", False),
                               unit_visibility=var.get("unit_visibility", False),
-                              rank_key=None if key is None else key[b])
+                              rank_key=None if key is None else key[b],
+                              tier_rate=var.get("tier_rate"))
         lay = selector.event_layout(ref["mask"], ref["tier"])
         assert np.array_equal(out["mask"][b], ref["mask"]), "mask"
         assert np.array_equal(out["tier"][b], ref["tier"]), "tier"
@@ -77,7 +80,8 @@ def _end_to_end(T, tail=16, **var):
                                   keep_budget=0.29, solve="blockadj", debug=dbg, tail=tail,
                                   fixed_tiers=var.get("fixed_tiers", False),
                                   unit_visibility=var.get("unit_visibility", False),
-                                  rank_key=None if key is None else torch.from_numpy(key).cuda())
+                                  rank_key=None if key is None else torch.from_numpy(key).cuda(),
+                                  tier_rate=var.get("tier_rate"))
     torch.cuda.synchronize()
     o, S = host(o), host(S)
     _, _, info = sparse.sparse_prefill(inp.q, inp.k, inp.v, inp.a, inp.beta, z=inp.z,
@@ -88,7 +92,8 @@ def _end_to_end(T, tail=16, **var):
     ref = selector.select(score.cpu().numpy()[0], gam.cpu().numpy()[0], eta.cpu().numpy()[0],
                           keep_budget=0.29, fixed_tiers=var.get("fixed_tiers", False),
                           unit_visibility=var.get("unit_visibility", False),
-                          rank_key=None if key is None else key[0])
+                          rank_key=None if key is None else key[0],
+                          tier_rate=var.get("tier_rate"))
     assert np.array_equal(mask.cpu().numpy()[0], ref["mask"]), "mask"
     assert np.array_equal(tier.cpu().numpy()[0], ref["tier"]), "tier"
     o_ref, S_ref = sparse.sparse_prefill(inp.q, inp.k, inp.v, inp.a, inp.beta, solve="blockadj",

@@ -132,6 +132,23 @@ def test_sparse_given_mask(dtype, T, decay):
 
 
 @pytest.mark.parametrize("solve", ["exact", "blockadj"])
+def test_sparse_fp16_output(solve):
+    """O in fp16 (the benchmark's output type) on the sparse path, both
+    streams of the single-sequence schedule: the plain bar."""
+    import torch
+    T = 64 * 30 + 21
+    inp = synth.numpy_inputs(synth.seed_for(2) + 12, 1, T, 16, 32, dtype="bf16", with_z=True,
+                             decay_scale=1 / 16)
+    _, _, info = oracle_sparse(inp, solve=solve)
+    o, S, st = run_sparse(inp, solve=solve, mask=info["mask"], out_dtype=torch.float16)
+    o_ref, S_ref = sparse.sparse_prefill(inp.q, inp.k, inp.v, inp.a, inp.beta, solve=solve,
+                                         mask=info["mask"])
+    eo, es = rel_max_err(o, o_ref), rel_max_err(S, S_ref)
+    print(f"fp16 o: err O {eo:.3e} S {es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("solve", ["exact", "blockadj"])
 def test_sparse_bf16_output(solve):
     """O in bf16 on the sparse path (the O kernel's bf16-output instance on
     both streams of the single-sequence schedule): the bar is the fp32-output

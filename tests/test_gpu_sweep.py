@@ -55,7 +55,8 @@ def test_sweep_selector_and_pair(B, keep, u_max):
     tier = torch.empty((B, NV // 2), dtype=torch.uint8, device="cuda")
     dbg = ops.debug_struct(score=score, gamma=gam, eta=eta, mask=mask, tier=tier)
     o, S, st = ops.prefill_sparse(d["q"], d["k"], d["v"], d["a"], d["beta"], z=d["z"],
-                                  keep_budget=keep, solve="blockadj", debug=dbg)
+                                  keep_budget=keep, solve="blockadj", debug=dbg,
+                                  out_dtype=torch.float16)
     torch.cuda.synchronize()
     sc, gm, et = score.cpu().numpy(), gam.cpu().numpy(), eta.cpu().numpy()
     m_gpu, t_gpu, st = mask.cpu().numpy(), tier.cpu().numpy(), st.cpu().numpy()

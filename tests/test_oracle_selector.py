@@ -75,6 +75,44 @@ def test_tier_counts_other_budgets():
         selector.tier_counts(512, 0.0)
 
 
+@pytest.mark.parametrize("C", [1, 2, 4, 35, 64, 512, 2048])
+def test_tier_rate_override_at_page_rates_is_default(C):
+    """Overriding with the page's own rates (0.08, 0.30, 0.95) gives the
+    default budget's counts (Sec. 2.4.3, Eq. (13))."""
+    assert selector.tier_counts(C, 0.5, tier_rate=(0.08, 0.30, 0.95)) == selector.tier_counts(C)
+
+
+def test_tier_rate_override_hand_values():
+    # 0.1 * 35 = 3.5 -> 4, 0.25 * 35 = 8.75 -> 9, 0.5 * 35 = 17.5 -> 18 (halves up)
+    assert selector.tier_counts(35, tier_rate=(0.1, 0.25, 0.5)) == (4, 9, 18)
+    assert selector.tier_counts(100, tier_rate=(0.1, 0.25, 0.5)) == (10, 25, 50)
+    # 0.01 * 64 = 0.64 -> 1, clipped to the two anchors
+    assert selector.tier_counts(64, tier_rate=(0.01, 0.01, 1.0)) == (2, 2, 64)
+    # the keep budget is not used once rates are given
+    assert selector.tier_counts(100, 1.0, tier_rate=(0.1, 0.25, 0.5)) == (10, 25, 50)
+    for bad in [(0.3, 0.2, 0.9), (0.0, 0.3, 0.9), (0.1, 0.3, 1.5), (float("nan"), 0.3, 0.9),
+                (-0.1, 0.3, 0.9)]:
+        with pytest.raises(ValueError):
+            selector.tier_counts(64, tier_rate=bad)
+
+
+def test_select_with_tier_rate_keeps_k_per_tier():
+    """With overridden rates every pair keeps exactly k of its tier, anchors
+    included (Sec. 2.4.3, Eqs. (13)-(14))."""
+    rng = np.random.default_rng(5)
+    C = 96
+    score = rng.gamma(2.0, 1.0, (32, C)).astype(np.float32)
+    gamma = (-rng.uniform(0.1, 3.0, (32, 1)) * np.ones((1, C))).astype(np.float32)
+    eta = rng.uniform(0.5, 2.0, 32).astype(np.float32)
+    rates = (0.05, 0.2, 0.6)
+    out = selector.select(score, gamma, eta, tier_rate=rates)
+    k = selector.tier_counts(C, tier_rate=rates)
+    assert out["k"] == k
+    for p in range(16):
+        assert int(out["mask"][p].sum()) == k[int(out["tier"][p])]
+        assert out["mask"][p, 0] == 1 and out["mask"][p, C - 1] == 1
+
+
 def test_nominal_keep_range_matches_page():
     """The candidate table bounds the nominal mean keep to 28.44%-31.31%."""
     vals = [selector.nominal_keep(h, m) for h, ms in selector.MEDIUM_CHOICES.items() for m in ms]
