@@ -173,7 +173,7 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
     sz[B_ETA] = B * Nv * 4;
     sz[B_ETAP] = B * Nv * GATE_SPLIT * 4;
     sz[B_RANK] = B * NP * C * 4;
-    sz[B_TINFO] = B * 8 * 4;
+    sz[B_TINFO] = B * NP * PAIRREC_BYTES;
     sz[B_MASK] = B * NP * C;
     sz[B_TIER] = B * NP;
     sz[B_ROWPAIR] = B * NP * 4;
@@ -343,7 +343,7 @@ size_t noalloc_layout(const Plan& pl, bool with_key, size_t off[4]) {
   off[0] = 0;
   off[1] = ranks;
   off[2] = off[1] + (with_key ? ranks : 0);
-  off[3] = off[2] + align256((size_t)pl.B * 8 * 4);
+  off[3] = off[2] + align256((size_t)pl.B * NP_SPARSE * PAIRREC_BYTES);
   return off[3] + align256((size_t)pl.B * NP_SPARSE * pl.kH * 4);
 }
 

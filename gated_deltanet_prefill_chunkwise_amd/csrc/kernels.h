@@ -157,7 +157,7 @@ struct S0PrepArgs { const float* s0; void* s0T; int B, Nv; int32_t* stats; };
 struct StatsInitArgs { int32_t* stats; int B, Nv, C, T; const int32_t* cu; int dense; };
 
 // The samples of a head are split over GATE_SPLIT workgroups, each writing
-// its sum of squares to eta_part [B][Nv][GATE_SPLIT]; the tier kernel adds
+// its sum of squares to eta_part [B][Nv][GATE_SPLIT]; the selector adds
 // the parts in order and divides by the sample count.
 constexpr int GATE_SPLIT = 8;
 struct GateArgs {
@@ -165,6 +165,10 @@ struct GateArgs {
   const int32_t* cu;        // packed sequence offsets [B+1] or null
   int32_t* stats;           // NF_Z of nonfinite_input (the sampled gates)
 };
+
+// Bytes of the per-(sequence, head pair) record the selector passes between
+// its kernels.
+constexpr int PAIRREC_BYTES = 32;
 
 struct SelectArgs {
   const float* score; const float* gamma; const float* eta;
@@ -182,7 +186,7 @@ struct SelectArgs {
   const float* rank_key;
   int32_t* rank_alt;    // [B][16][C]   workspace: ranks by rank_key
   int32_t* rank;        // [B][16][C]   workspace
-  int32_t* tierinfo;    // [B][8]       workspace: k_L, k_M, k_H, n_H, n_M
+  int32_t* tierinfo;    // [B][16] pair records of PAIRREC_BYTES (gains, referenced events)
   uint8_t* mask; uint8_t* tier;
   int32_t* row_pair; int32_t* row_ptr; int32_t* col; int32_t* pred;
   int32_t* group_slot; int32_t* event_slot; int32_t* col_row;  // col_row: [B][Emax] row of each event

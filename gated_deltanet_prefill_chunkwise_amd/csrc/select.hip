@@ -114,10 +114,12 @@ __device__ double lifetime(double r, int C) {
 // the rank of every non-anchor chunk (q descending, chunk index ascending).
 // Workgroup (blk, pp, b) ranks chunks 128 blk .. 128 blk + 127 of pair pp:
 // eight threads per chunk count disjoint eighths of the other chunks.  Every
-// workgroup forms the norms and keys itself, with the same operations.
-// KEY: rank by the caller's keys instead (the random-selection ablation),
-// into rank_alt.
+// workgroup stages the pair's scores in LDS and forms the norms and keys
+// itself, with the same operations.  KEY: rank by the caller's keys instead
+// (the random-selection ablation), into rank_alt.
+// Dynamic LDS: C doubles (keys) + 2 C floats (scores).
 constexpr int RANK_CHUNKS = 128;
+constexpr int MAX_C = 8192;
 template <bool KEY>
 __global__ __launch_bounds__(1024) void select_rank_kernel(SelectArgs p) {
   extern __shared__ double sq[];
@@ -125,36 +127,45 @@ __global__ __launch_bounds__(1024) void select_rank_kernel(SelectArgs p) {
   const int blk = blockIdx.x, pp = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int CS = p.C, C = valid_chunks(p, b);
-  const float* s0 = p.score + ((size_t)b * NV + 2 * pp) * CS;
-  const float* s1 = s0 + CS;
-  const float* key = KEY ? p.rank_key + ((size_t)b * NP + pp) * CS : nullptr;
-  if (!KEY && w < 2) {
-    const float* s = w ? s1 : s0;
-    double acc = 0.0;
-    // loads of eight chunks are issued together; the sum keeps the lane's
-    // chunk order
-    for (int c0 = lane; c0 < C; c0 += 64 * 8) {
-      float xs[8];
+  if (KEY) {
+    const float* key = p.rank_key + ((size_t)b * NP + pp) * CS;
+    for (int c = tid; c < C; c += 1024) sq[c] = ord_key((double)key[c]);
+  } else {
+    float* ss = reinterpret_cast<float*>(sq + CS);   // [2][CS] staged scores
+    const float* s0 = p.score + ((size_t)b * NV + 2 * pp) * CS;
+    const float* s1 = s0 + CS;
+    {
+      // every load of a thread is issued before the first store
+      constexpr int U = MAX_C / 1024;
+      float x0[U], x1[U];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) xs[u] = c0 + 64 * u < C ? s[c0 + 64 * u] : 0.f;
+      for (int u = 0; u < U; ++u) {
+        const int c = tid + 1024 * u;
+        x0[u] = c < C ? s0[c] : 0.f;
+        x1[u] = c < C ? s1[c] : 0.f;
+      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (c0 + 64 * u < C) {
-          const double x = (double)xs[u];
-          acc = acc + x * x;
-        }
+      for (int u = 0; u < U; ++u) {
+        const int c = tid + 1024 * u;
+        if (c < C) { ss[c] = x0[u]; ss[CS + c] = x1[u]; }
+      }
     }
-    const double tot = wave_sum(acc);
-    if (lane == 0) snorm[w] = sqrt(tot);
-  }
-  __syncthreads();
-  const double n0 = snorm[0], n1 = snorm[1];
-  for (int c = tid; c < C; c += 1024) {
-    if (KEY) {
-      sq[c] = ord_key((double)key[c]);
-    } else {
-      const double t0 = n0 > 0.0 ? (double)s0[c] / n0 : 0.0;
-      const double t1 = n1 > 0.0 ? (double)s1[c] / n1 : 0.0;
+    __syncthreads();
+    if (w < 2) {
+      const float* s = ss + w * CS;
+      double acc = 0.0;
+      for (int c = lane; c < C; c += 64) {
+        const double x = (double)s[c];
+        acc = acc + x * x;
+      }
+      const double tot = wave_sum(acc);
+      if (lane == 0) snorm[w] = sqrt(tot);
+    }
+    __syncthreads();
+    const double n0 = snorm[0], n1 = snorm[1];
+    for (int c = tid; c < C; c += 1024) {
+      const double t0 = n0 > 0.0 ? (double)ss[c] / n0 : 0.0;
+      const double t1 = n1 > 0.0 ? (double)ss[CS + c] / n1 : 0.0;
       sq[c] = ord_key(0.5 * (t0 + t1));
     }
   }
@@ -162,19 +173,37 @@ __global__ __launch_bounds__(1024) void select_rank_kernel(SelectArgs p) {
   int32_t* rk = (KEY ? p.rank_alt : p.rank) + ((size_t)b * NP + pp) * CS;
   const int c = RANK_CHUNKS * blk + (tid >> 3), part = tid & 7;
   int r = 0;
-  const bool inner = c >= 1 && c <= C - 2;
-  if (inner) {
+  if (c >= 1 && c <= C - 2) {
+    // candidates c2 = 1 + part + 8 j (j < J, c2 <= C - 2): one before c
+    // outranks it when q2 >= qc (ties go to the lower chunk), one after it
+    // when q2 > qc; c2 = c counts neither way
     const double qc = sq[c];
-    for (int c2 = 1 + part; c2 <= C - 2; c2 += 8) {
-      const double q2 = sq[c2];
-      r += (q2 > qc || (q2 == qc && c2 < c)) ? 1 : 0;
+    const double* qb = sq + 1 + part;
+    const int J = C - 3 - part >= 0 ? (C - 3 - part) / 8 + 1 : 0;
+    const int js = min(c - 1 - part > 0 ? (c - 1 - part + 7) / 8 : 0, J);
+    int j = 0;
+    for (; j + 8 <= js; j += 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = qb[8 * (j + u)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += v[u] >= qc ? 1 : 0;
     }
+    for (; j < js; ++j) r += qb[8 * j] >= qc ? 1 : 0;
+    for (; j + 8 <= J; j += 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = qb[8 * (j + u)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += v[u] > qc ? 1 : 0;
+    }
+    for (; j < J; ++j) r += qb[8 * j] > qc ? 1 : 0;
   }
   // the eight partial counts of a chunk sit in eight adjacent lanes
   r += __shfl_xor(r, 1, 64);
   r += __shfl_xor(r, 2, 64);
   r += __shfl_xor(r, 4, 64);
-  if (part == 0 && c < C) rk[c] = inner ? r : -1;
+  if (part == 0 && c < C) rk[c] = (c >= 1 && c <= C - 2) ? r : -1;
 }
 
 // B(x, k) = k (n-k) / n (mean x[:k] - mean x[k:])^2 over the wave-held sorted
@@ -190,172 +219,415 @@ __device__ double split_score(const double* vals, int n, int k, int lane) {
   return f * (dm * dm);
 }
 
-// Eqs. (11)-(14): lifetime, visibility, upgrade gains, dynamic tier counts.
-// Wave w forms the per-head sums of the two heads of pair w (each sum is one
-// wave's lane-interleaved sum, as everywhere in this file); wave 0 then takes
-// the decisions.
-__global__ __launch_bounds__(1024) void select_tier_kernel(SelectArgs p) {
-  __shared__ double sL[NV], sGv[NV], slm[NV], smh[NV];
-  __shared__ double sxm[NP], sxh[NP], svals[NP];
-  __shared__ int sorder[NP], shigh[NP];
-  const int b = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  const int CS = p.C, C = valid_chunks(p, b);
+// Per (sequence, head pair) record handed from select_pair_kernel to
+// select_decide_kernel: the upgrade gains of Eq. (12) and the number of
+// referenced events (group predecessors) the pair would have in each tier.
+struct PairRec {
+  double glm, gmh;
+  int32_t nref[3];
+  int32_t pad;
+};
+static_assert(sizeof(PairRec) == PAIRREC_BYTES, "pair record size");
+
+// Kept chunks of one pair as 64-bit words (bit l of word i: chunk 64 i + l)
+// for keep count k, from its ranks (anchors always kept); lane = bit.
+__device__ __forceinline__ unsigned long long kept_word(const int32_t* rank, int i, int lane, int C,
+                                                        int k) {
+  const int c = 64 * i + lane;
+  bool z = false;
+  if (c < C) {
+    const int r = rank[c];
+    z = c == 0 || c == C - 1 || (r >= 0 && r < k - 2);
+  }
+  return __ballot(z);
+}
+
+// Referenced events of word i: kept chunk e is the predecessor of some group
+// r (2 r <= 2 (G - 1)) iff an even number lies in [e + 1, min(next kept,
+// 2 (G - 1))]; nextfirst is the first kept chunk after word i (C + 1 if none).
+__device__ __forceinline__ unsigned long long ref_word(unsigned long long bal, int i, int lane,
+                                                       int nextfirst, int G) {
+  const int c = 64 * i + lane;
+  const unsigned long long above = lane == 63 ? 0ull : (bal >> (lane + 1));
+  const int nxt = above ? c + 1 + (int)__builtin_ctzll(above) : nextfirst;
+  const int lo = c + 1, lo_e = lo + (lo & 1), hi = min(nxt, 2 * (G - 1));
+  return __ballot(((bal >> lane) & 1ull) && lo_e <= hi);
+}
+
+// Eqs. (11)-(12) for one head pair, and its referenced-event counts: workgroup
+// (pp, b) stages the pair's ranks and scores, then wave 0 forms the band sums
+// of both heads (the ranks of Eq. (10) between k_L - 2 and k_M - 2, and
+// between k_M - 2 and k_H - 2; each sum one wave's lane-interleaved sum),
+// wave 1 the lifetimes of Eq. (11), wave 2 the visibilities (and, in pair 0,
+// eta from the gate kernel's parts), waves 3-5 the referenced events with the
+// keep count of tier 0, 1, 2.  Dynamic LDS: 2 C ints (ranks, keep ranks) and
+// 2 C floats (scores).
+__global__ __launch_bounds__(1024) void select_pair_kernel(SelectArgs p) {
+  extern __shared__ int32_t s_rank[];
+  __shared__ double s_sum[4], s_L[2], s_G[2];
+  __shared__ int s_nref[3];
+  const int pp = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int CS = p.C, C = valid_chunks(p, b), G = (C + 1) / 2, NW = (C + 63) / 64;
+  const bool key = p.rank_key != nullptr;
+  int32_t* s_keep = key ? s_rank + CS : s_rank;
+  float* s_sc = reinterpret_cast<float*>(s_rank + 2 * CS);
   int kk[3];
   tier_counts(C, p.keep_bp, p.rate_bp, kk);
   const int kL = kk[0], kM = kk[1], kH = kk[2];
-  const float* sc = p.score + (size_t)b * NV * CS;
-  const float* gm = p.gamma + (size_t)b * NV * CS;
-  const float* et = p.eta + (size_t)b * NV;
-  const int32_t* rk = p.rank + (size_t)b * NP * CS;
-
-  // wave wv: pair wv, both heads in one pass over the pair's ranks (16
-  // chunks per lane and batch, each lane summing its chunks in ascending order)
-  const int lo = C > 16 ? C - 16 : 0, nwin = C - lo;
+  const int h0 = 2 * pp;
   {
-    const int pp = wv, h0 = 2 * pp;
-    double xw[2];
+    const int32_t* rk = p.rank + ((size_t)b * NP + pp) * CS;
+    const int32_t* ra = key ? p.rank_alt + ((size_t)b * NP + pp) * CS : nullptr;
+    const float* sc = p.score + ((size_t)b * NV + h0) * CS;
+    constexpr int U = MAX_C / 1024;
+    int r0[U], r1[U];
+    float x0[U], x1[U];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-      xw[hh] = lane < nwin ? exp2_fixed((double)gm[(h0 + hh) * CS + lo + lane]) : 0.0;
-    double alm[2] = {0.0, 0.0}, amh[2] = {0.0, 0.0};
-    for (int c0 = lane; c0 < C; c0 += 64 * 16) {
-      int rr[16];
-      float xx[2][16];
+    for (int u = 0; u < U; ++u) {
+      const int c = tid + 1024 * u;
+      r0[u] = c < C ? rk[c] : -1;
+      r1[u] = (key && c < C) ? ra[c] : -1;
+      x0[u] = c < C ? sc[c] : 0.f;
+      x1[u] = c < C ? sc[CS + c] : 0.f;
+    }
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int c = c0 + 64 * u;
-        rr[u] = c < C ? rk[pp * CS + c] : -1;
-        xx[0][u] = c < C ? sc[h0 * CS + c] : 0.f;
-        xx[1][u] = c < C ? sc[(h0 + 1) * CS + c] : 0.f;
+    for (int u = 0; u < U; ++u) {
+      const int c = tid + 1024 * u;
+      if (c < C) {
+        s_rank[c] = r0[u];
+        if (key) s_keep[c] = r1[u];
+        s_sc[c] = x0[u];
+        s_sc[CS + c] = x1[u];
       }
+    }
+  }
+  __syncthreads();
+  if (wv == 0) {
+    double alm[2] = {0.0, 0.0}, amh[2] = {0.0, 0.0};
+    for (int c = lane; c < C; c += 64) {
+      const int r = s_rank[c];
+      const bool inm = r >= kL - 2 && r < kM - 2, inh = r >= kM - 2 && r < kH - 2;
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (c0 + 64 * u < C) {
-          const int r = rr[u];
-          const bool inm = r >= kL - 2 && r < kM - 2, inh = r >= kM - 2 && r < kH - 2;
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const double xs = (double)xx[hh][u];
-            alm[hh] = alm[hh] + (inm ? xs : 0.0);
-            amh[hh] = amh[hh] + (inh ? xs : 0.0);
-          }
-        }
+      for (int hh = 0; hh < 2; ++hh) {
+        const double xs = (double)s_sc[hh * CS + c];
+        alm[hh] = alm[hh] + (inm ? xs : 0.0);
+        amh[hh] = amh[hh] + (inh ? xs : 0.0);
+      }
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const double tot = wave_sum(xw[hh]);
       const double tl = wave_sum(alm[hh]), th = wave_sum(amh[hh]);
-      if (lane == 0) {
-        sL[h0 + hh] = lifetime(tot / nwin, C);
-        slm[h0 + hh] = tl;
-        smh[h0 + hh] = th;
+      if (lane == 0) { s_sum[hh] = tl; s_sum[2 + hh] = th; }
+    }
+  } else if (wv == 1) {
+    const int lo = C > 16 ? C - 16 : 0, nwin = C - lo;
+    const float* gm = p.gamma + ((size_t)b * NV + h0) * CS;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const double xw = lane < nwin ? exp2_fixed((double)gm[hh * CS + lo + lane]) : 0.0;
+      const double tot = wave_sum(xw);
+      if (lane == 0) s_L[hh] = lifetime(tot / nwin, C);
+    }
+  } else if (wv == 2) {
+    // eta of head `lane`: given, or the mean from the gate kernel's parts
+    float eh = 0.f;
+    if (lane < NV) {
+      if (p.eta_part != nullptr) {
+        const float* ep = p.eta_part + ((size_t)b * NV + lane) * GATE_SPLIT;
+        float t = 0.f;
+        for (int i = 0; i < GATE_SPLIT; ++i) t += ep[i];
+        eh = C > 0 ? t / (float)(4 * C) : 0.f;
+        if (pp == 0) p.eta_out[(size_t)b * NV + lane] = eh;
+      } else {
+        eh = p.eta[(size_t)b * NV + lane];
       }
     }
+    const double etab = wave_sum(lane < NV ? (double)eh : 0.0) / NV;
+    if (lane == h0 || lane == h0 + 1)
+      s_G[lane - h0] = (etab > 0.0 && !p.unit_visibility) ? sqrt((double)eh / etab) : 1.0;
+  } else if (wv >= 3 && wv <= 5) {
+    const int k = kk[wv - 3];
+    // words are walked from the last one, carrying the first kept chunk
+    // after the current word
+    int nextfirst = C + 1, cnt = 0;
+    for (int i = NW - 1; i >= 0; --i) {
+      const unsigned long long bal = kept_word(s_keep, i, lane, C, k);
+      cnt += __popcll(ref_word(bal, i, lane, nextfirst, G));
+      if (bal) nextfirst = 64 * i + (int)__builtin_ctzll(bal);
+    }
+    if (lane == 0) s_nref[wv - 3] = cnt;
   }
   __syncthreads();
-  if (wv != 0) return;
-  // eta of head `lane`: given, or the mean from the gate kernel's parts
-  float eh = 0.f;
-  if (lane < NV) {
-    if (p.eta_part != nullptr) {
-      const float* ep = p.eta_part + ((size_t)b * NV + lane) * GATE_SPLIT;
-      float t = 0.f;
-      for (int i = 0; i < GATE_SPLIT; ++i) t += ep[i];
-      eh = C > 0 ? t / (float)(4 * C) : 0.f;
-      p.eta_out[(size_t)b * NV + lane] = eh;
-    } else {
-      eh = et[lane];
+  if (tid == 0) {
+    PairRec* rec = reinterpret_cast<PairRec*>(p.tierinfo) + (size_t)b * NP + pp;
+    PairRec q;
+    q.glm = (s_L[0] * s_G[0]) * s_sum[0] + (s_L[1] * s_G[1]) * s_sum[1];
+    q.gmh = (s_L[0] * s_G[0]) * s_sum[2] + (s_L[1] * s_G[1]) * s_sum[3];
+    q.nref[0] = s_nref[0]; q.nref[1] = s_nref[1]; q.nref[2] = s_nref[2];
+    q.pad = 0;
+    *rec = q;
+  }
+}
+
+// Eqs. (13)-(14) and Eq. (16): every workgroup (pp, b) takes the sequence's
+// tier decision from the pair records (the same operations in every
+// workgroup, so the same tiers), orders the CSR rows (High, Medium, Low;
+// ascending pair within a tier) and numbers the compact snapshots over the
+// rows; then its 16 waves lay out pair pp: mask, kept chunks ascending at
+// the row's offset, the snapshot slot of every event and the predecessor of
+// every output group.  Workgroup 0 writes the sequence's tiers, rows and
+// statistics.  Dynamic LDS: C ints (keep ranks).
+__global__ __launch_bounds__(1024) void select_decide_kernel(SelectArgs p) {
+  extern __shared__ int32_t s_keep[];
+  constexpr int NWMAX = MAX_C / 64;
+  __shared__ double sxm[NP], sxh[NP], svals[NP];
+  __shared__ int sorder[NP], shigh[NP], s_tier[NP], s_rowof[NP], s_rowpair[NP];
+  __shared__ int s_rowptr[NP + 1], s_refbase[NP + 1];
+  __shared__ unsigned long long s_kept[NWMAX], s_refd[NWMAX];
+  __shared__ int s_run[NWMAX], s_rrun[NWMAX], s_next[NWMAX], s_last[NWMAX];
+  const int pp = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int CS = p.C, GS = p.G, C = valid_chunks(p, b), G = (C + 1) / 2;
+  const int NW = (C + 63) / 64, NWS = (CS + 63) / 64;
+  int kk[3];
+  tier_counts(C, p.keep_bp, p.rate_bp, kk);
+  const PairRec* recs = reinterpret_cast<const PairRec*>(p.tierinfo) + (size_t)b * NP;
+  // waves 1-15 stage this pair's keep ranks while wave 0 decides the tiers
+  // (the workgroup barriers below order wave 0's steps; the other waves
+  // pass them)
+  if (wv != 0) {
+    const int32_t* src = (p.rank_key != nullptr ? p.rank_alt : p.rank) + ((size_t)b * NP + pp) * CS;
+    for (int c = tid - 64; c < C; c += 1024 - 64) s_keep[c] = src[c];
+  }
+  const bool w0 = wv == 0;
+  if (w0) {
+    double glm = 0.0, gmh = 0.0;
+    if (lane < NP) { glm = recs[lane].glm; gmh = recs[lane].gmh; }
+    const double mum = wave_sum(glm) / NP;
+    const double muh = wave_sum(gmh) / NP;
+    if (lane < NP) {
+      sxm[lane] = ord_key(mum > 0.0 ? glm / mum : 0.0);
+      sxh[lane] = ord_key(muh > 0.0 ? gmh / muh : 0.0);
     }
   }
-  const double etab = wave_sum(lane < NV ? (double)eh : 0.0) / NV;
-  if (lane < NV) sGv[lane] = (etab > 0.0 && !p.unit_visibility) ? sqrt((double)eh / etab) : 1.0;
   __syncthreads();
-  double glm = 0.0, gmh = 0.0;
-  if (lane < NP) {
-    const int h0 = 2 * lane, h1 = h0 + 1;
-    glm = (sL[h0] * sGv[h0]) * slm[h0] + (sL[h1] * sGv[h1]) * slm[h1];
-    gmh = (sL[h0] * sGv[h0]) * smh[h0] + (sL[h1] * sGv[h1]) * smh[h1];
-  }
-  const double mum = wave_sum(glm) / NP;
-  const double muh = wave_sum(gmh) / NP;
-  if (lane < NP) {
-    sxm[lane] = ord_key(mum > 0.0 ? glm / mum : 0.0);
-    sxh[lane] = ord_key(muh > 0.0 ? gmh / muh : 0.0);
-  }
-  __syncthreads();
-
   // High count: pairs sorted by x_H descending (ties: lower pair first)
-  if (lane < NP) {
+  if (w0 && lane < NP) {
     int pos = 0;
     for (int q = 0; q < NP; ++q)
       pos += (sxh[q] > sxh[lane] || (sxh[q] == sxh[lane] && q < lane)) ? 1 : 0;
     sorder[pos] = lane;
   }
   __syncthreads();
-  if (lane < NP) svals[lane] = sxh[sorder[lane]];
+  if (w0 && lane < NP) svals[lane] = sxh[sorder[lane]];
   __syncthreads();
   int nH = 1;
-  if (p.fixed_tiers) {
-    nH = 3;                 // the fixed 9 Low / 4 Medium / 3 High split
-  } else {
-    double best = 0.0;
-    for (int k = 1; k <= 4; ++k) {
-      const double v = split_score(svals, NP, k, lane);
-      if (k == 1 || v > best) { best = v; nH = k; }
+  if (w0) {
+    if (p.fixed_tiers) {
+      nH = 3;                 // the fixed 9 Low / 4 Medium / 3 High split
+    } else {
+      double best = 0.0;
+      for (int k = 1; k <= 4; ++k) {
+        const double v = split_score(svals, NP, k, lane);
+        if (k == 1 || v > best) { best = v; nH = k; }
+      }
     }
+    if (lane < NP) shigh[lane] = 0;
   }
-  if (lane < NP) shigh[lane] = 0;
   __syncthreads();
-  if (lane < nH) shigh[sorder[lane]] = 1;
+  if (w0 && lane < nH) shigh[sorder[lane]] = 1;
   __syncthreads();
-
   // Medium count among the remaining pairs, sorted by x_M descending
   const int nrest = NP - nH;
-  if (lane < NP && !shigh[lane]) {
+  if (w0 && lane < NP && !shigh[lane]) {
     int pos = 0;
     for (int q = 0; q < NP; ++q)
       if (!shigh[q]) pos += (sxm[q] > sxm[lane] || (sxm[q] == sxm[lane] && q < lane)) ? 1 : 0;
     sorder[pos] = lane;
   }
   __syncthreads();
-  if (lane < nrest) svals[lane] = sxm[sorder[lane]];
+  if (w0 && lane < nrest) svals[lane] = sxm[sorder[lane]];
   __syncthreads();
-  int cand[3], ncand;
-  if (nH == 1) { cand[0] = 11; cand[1] = 12; cand[2] = 13; ncand = 3; }
-  else if (nH == 2) { cand[0] = 7; cand[1] = 8; cand[2] = 9; ncand = 3; }
-  else if (nH == 3) { cand[0] = 3; cand[1] = 4; cand[2] = 5; ncand = 3; }
-  else { cand[0] = 0; ncand = 1; }
-  int nM = cand[0];
-  if (p.fixed_tiers) {
-    nM = 4;
-  } else {
-    double best = 0.0;
-    for (int i = 0; i < ncand; ++i) {
-      const double v = split_score(svals, nrest, cand[i], lane);
-      if (i == 0 || v > best) { best = v; nM = cand[i]; }
+  if (w0) {
+    int cand[3], ncand;
+    if (nH == 1) { cand[0] = 11; cand[1] = 12; cand[2] = 13; ncand = 3; }
+    else if (nH == 2) { cand[0] = 7; cand[1] = 8; cand[2] = 9; ncand = 3; }
+    else if (nH == 3) { cand[0] = 3; cand[1] = 4; cand[2] = 5; ncand = 3; }
+    else { cand[0] = 0; ncand = 1; }
+    int nM = cand[0];
+    if (p.fixed_tiers) {
+      nM = 4;
+    } else {
+      double best = 0.0;
+      for (int i = 0; i < ncand; ++i) {
+        const double v = split_score(svals, nrest, cand[i], lane);
+        if (i == 0 || v > best) { best = v; nM = cand[i]; }
+      }
+    }
+    if (lane < NP) {
+      int t = 2;
+      if (!shigh[lane]) {
+        int pos = 0;   // position among the remaining pairs
+        for (int q = 0; q < nrest; ++q) pos += (sorder[q] == lane) ? q : 0;
+        t = pos < nM ? 1 : 0;
+      }
+      s_tier[lane] = t;
     }
   }
-  if (lane < NP) {
-    int t = 0;
-    if (shigh[lane]) t = 2;
-    else {
-      // position among the remaining pairs
-      int pos = 0;
-      for (int q = 0; q < nrest; ++q) pos += (sorder[q] == lane) ? q : 0;
-      t = pos < nM ? 1 : 0;
+  __syncthreads();
+  // rows: High first, ascending pair within a tier (head-pair order with
+  // pair_order); each row holds the k of its tier events
+  if (w0 && lane < NP) {
+    int row = lane;
+    if (!p.pair_order) {
+      const int t = s_tier[lane];
+      row = 0;
+      for (int q = 0; q < NP; ++q)
+        row += (s_tier[q] > t || (s_tier[q] == t && q < lane)) ? 1 : 0;
     }
-    p.tier[b * NP + lane] = (uint8_t)t;
+    s_rowof[lane] = row;
+    s_rowpair[row] = lane;
   }
-  if (lane == 0) {
-    int32_t* ti = p.tierinfo + b * 8;
-    ti[0] = kL; ti[1] = kM; ti[2] = kH; ti[3] = nH; ti[4] = nM;
+  __syncthreads();
+  if (w0 && lane <= NP) {
+    int e = 0, f = 0;
+    for (int r = 0; r < lane; ++r) {
+      const int q = s_rowpair[r], tq = s_tier[q];
+      e += kk[tq];
+      f += recs[q].nref[tq];
+    }
+    s_rowptr[lane] = e;
+    s_refbase[lane] = f;
+  }
+  __syncthreads();
+  if (w0 && pp == 0) {
+    if (lane < NP) {
+      p.tier[b * NP + lane] = (uint8_t)s_tier[lane];
+      p.row_pair[b * NP + lane] = s_rowpair[lane];
+    }
+    if (lane <= NP) p.row_ptr[b * (NP + 1) + lane] = s_rowptr[lane];
+    if (lane == 0 && p.stats != nullptr) {
+      int32_t* st = static_cast<int32_t*>(p.stats) + (size_t)b * STATS_INTS;
+      if (p.nf_clear) st[ST_NF_IN] = st[ST_NF_OUT] = 0;
+      int nt[3] = {0, 0, 0};
+      for (int q = 0; q < NP; ++q) nt[s_tier[q]]++;
+      st[0] = s_rowptr[NP];
+      st[1] = p.Emax;
+      st[2] = nt[0]; st[3] = nt[1]; st[4] = nt[2];
+      st[5] = kk[0]; st[6] = kk[1]; st[7] = kk[2];
+      st[8] = s_refbase[NP];
+    }
+  }
+  __syncthreads();
+  const int k = kk[s_tier[pp]];
+  const int row = s_rowof[pp], base = s_rowptr[row], rbase = s_refbase[row];
+  // kept words (wave w: words w, w + 16, ...)
+  for (int i = wv; i < NW; i += 16) {
+    const unsigned long long bal = kept_word(s_keep, i, lane, C, k);
+    if (lane == 0) s_kept[i] = bal;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    // per word: kept events before it, the first kept chunk after it and the
+    // last kept chunk before it (lane l: words 2 l and 2 l + 1)
+    int cnt2[2], first2[2], last2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 2 * lane + h;
+      const unsigned long long bal = i < NW ? s_kept[i] : 0ull;
+      cnt2[h] = __popcll(bal);
+      first2[h] = bal ? 64 * i + (int)__builtin_ctzll(bal) : C + 1;
+      last2[h] = bal ? 64 * i + 63 - (int)__builtin_clzll(bal) : -1;
+    }
+    // inclusive scans over lanes of the lane totals
+    int incl = cnt2[0] + cnt2[1];
+    int lastin = max(last2[0], last2[1]);
+    int firstin = min(first2[0], first2[1]);
+    int firstsuf = firstin;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int a = __shfl_up(incl, d, 64), m = __shfl_up(lastin, d, 64);
+      const int f = __shfl_down(firstsuf, d, 64);
+      if (lane >= d) { incl += a; lastin = max(lastin, m); }
+      if (lane + d < 64) firstsuf = min(firstsuf, f);
+    }
+    const int excl = incl - cnt2[0] - cnt2[1];
+    int lastex = __shfl_up(lastin, 1, 64);
+    if (lane == 0) lastex = -1;
+    int firstafter = __shfl_down(firstsuf, 1, 64);
+    if (lane == 63) firstafter = C + 1;
+    if (2 * lane < NW) {
+      s_run[2 * lane] = excl;
+      s_last[2 * lane] = lastex;
+      s_next[2 * lane] = min(first2[1], firstafter);
+    }
+    if (2 * lane + 1 < NW) {
+      s_run[2 * lane + 1] = excl + cnt2[0];
+      s_last[2 * lane + 1] = max(lastex, last2[0]);
+      s_next[2 * lane + 1] = firstafter;
+    }
+  }
+  __syncthreads();
+  for (int i = wv; i < NW; i += 16) {
+    const unsigned long long rb = ref_word(s_kept[i], i, lane, s_next[i], G);
+    if (lane == 0) s_refd[i] = rb;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    int c2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) c2[h] = 2 * lane + h < NW ? __popcll(s_refd[2 * lane + h]) : 0;
+    int incl = c2[0] + c2[1];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int a = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += a;
+    }
+    const int excl = incl - c2[0] - c2[1];
+    if (2 * lane < NW) s_rrun[2 * lane] = excl;
+    if (2 * lane + 1 < NW) s_rrun[2 * lane + 1] = excl + c2[0];
+  }
+  __syncthreads();
+  // outputs of pair pp: words w, w + 16, ... (and the mask bytes and groups
+  // of every word of the stride C, past the sequence's end too)
+  const unsigned long long below = (1ull << lane) - 1ull;
+  uint8_t* mask = p.mask + ((size_t)b * NP + pp) * CS;
+  int32_t* col = p.col + (size_t)b * p.Emax;
+  int32_t* eslot = p.event_slot + (size_t)b * p.Emax;
+  for (int i = wv; i < NWS; i += 16) {
+    const int c = 64 * i + lane;
+    const unsigned long long bal = i < NW ? s_kept[i] : 0ull;
+    const unsigned long long rb = i < NW ? s_refd[i] : 0ull;
+    const bool kept = (bal >> lane) & 1ull;
+    if (c < CS) mask[c] = kept ? 1 : 0;
+    if (kept) {
+      const int e = base + s_run[i] + __popcll(bal & below);
+      col[e] = c;
+      eslot[e] = ((rb >> lane) & 1ull) ? rbase + s_rrun[i] + __popcll(rb & below) : -1;
+    }
+    if ((c & 1) == 0 && c < CS) {
+      // group c / 2: the last kept chunk before c and its snapshot slot
+      int pc = -1, ps = -1;
+      if (c < C) {
+        const unsigned long long m = bal & below;
+        pc = m ? 64 * i + 63 - (int)__builtin_clzll(m) : s_last[i];
+        if (pc >= 0) {
+          const int j = pc >> 6, el = pc & 63;
+          ps = rbase + s_rrun[j] + __popcll(s_refd[j] & ((1ull << el) - 1ull));
+        }
+      }
+      const size_t o = ((size_t)b * NP + pp) * GS + (c >> 1);
+      p.pred[o] = pc;
+      p.group_slot[o] = ps;
+    }
   }
 }
 
-// Eq. (16): event mask, CSR rows (High, Medium, Low; ascending pair within a
-// tier), kept chunks ascending, predecessor of every output group and
-// compact-snapshot slots numbered over the referenced events in CSR order.
-// One block of 16 waves per sequence; wave w works on pair w or row w.
+// Eq. (16) for a caller's mask (mask_in): event mask, CSR rows (every pair a
+// Low row, in pair order), kept chunks ascending, predecessor of every output
+// group and compact-snapshot slots numbered over the referenced events in CSR
+// order.  One block of 16 waves per sequence; wave w works on pair w or row w.
 __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
   // Wave w handles head pair w.  Each pair's kept chunks are held as 64-bit
   // words (bit l of word i: chunk 64 i + l), and so are its referenced events,
@@ -535,21 +807,22 @@ hipError_t launch_fp64_selftest(const double* x, const double* y, double* q, dou
 }
 
 hipError_t launch_select_full(const SelectArgs& a, hipStream_t s) {
-  if (a.mask_in == nullptr) {
-    const int nblk = (a.C + RANK_CHUNKS - 1) / RANK_CHUNKS;
-    hipLaunchKernelGGL(select_rank_kernel<false>, dim3(nblk, NP, a.B), dim3(1024), (size_t)a.C * sizeof(double), s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.rank_key != nullptr) {
-      hipLaunchKernelGGL(select_rank_kernel<true>, dim3(nblk, NP, a.B), dim3(1024), (size_t)a.C * sizeof(double), s, a);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(select_tier_kernel, dim3(a.B), dim3(1024), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  if (a.mask_in != nullptr) {
+    hipLaunchKernelGGL(layout_kernel, dim3(a.B), dim3(1024), 0, s, a);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(layout_kernel, dim3(a.B), dim3(1024), 0, s, a);
+  const int nblk = (a.C + RANK_CHUNKS - 1) / RANK_CHUNKS;
+  const size_t rank_lds = (size_t)a.C * (sizeof(double) + 2 * sizeof(float));
+  hipLaunchKernelGGL(select_rank_kernel<false>, dim3(nblk, NP, a.B), dim3(1024), rank_lds, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.rank_key != nullptr) {
+    hipLaunchKernelGGL(select_rank_kernel<true>, dim3(nblk, NP, a.B), dim3(1024), rank_lds, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(select_pair_kernel, dim3(NP, a.B), dim3(1024), (size_t)a.C * 16, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(select_decide_kernel, dim3(NP, a.B), dim3(1024), (size_t)a.C * 4, s, a);
   return hipGetLastError();
 }
 
