@@ -229,73 +229,81 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_kernel(GateArgs p) {
 // as fragment-major W tiles per event (both heads of the pair); with fp16
 // intermediates (Wpk null) the H scan forms W S = Cb (K S) from Cb and K^T
 // itself, so W is never written.
-// The grid is sized to the capacity E_max; blocks past the on-device E exit.
+// Each workgroup walks events blockIdx.x, blockIdx.x + gridDim.x, ... of the
+// CSR rows row_lo .. row_hi - 1 (the count is on the device; the grid is
+// sized by the host and does not depend on it).
 constexpr int DW_KS = DK + 8;   // row stride (elements) of the staged key rows
+constexpr int DW_BLOCKS = 2048; // workgroups per sequence
 
 template <typename E>
 __global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
   using I = inter_t<E>;
   __shared__ __align__(16) E sK[L * DW_KS];
+  __shared__ int s_ptr[17];
   const int b = blockIdx.y;
   const int NP = p.Nv / 2;
-  const int i = p.row_ptr[b * (NP + 1) + p.row_lo] + (int)blockIdx.x;
-  if (i >= p.row_ptr[b * (NP + 1) + p.row_hi]) return;
-  int row = p.row_lo;
-  while (row + 1 < p.row_hi && p.row_ptr[b * (NP + 1) + row + 1] <= i) ++row;
-  const int pr = p.row_pair[b * NP + row];
-  const int c = p.col[(size_t)b * p.Emax + i];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int n16 = lane & 15, g4 = lane >> 4;
+  if (tid <= NP) s_ptr[tid] = p.row_ptr[b * (NP + 1) + tid];
+  __syncthreads();
   const bool blockadj = p.solve == 1;
   const SeqSpan sp = seq_span(p.cu, b, p.T);
-  {
-    // key rows c*64 .. c*64+63 in 16-byte pieces
-    constexpr int PV = 16 / (int)sizeof(E), PR = DK / PV;
-    const E* K = static_cast<const E*>(p.k);
+  const E* K = static_cast<const E*>(p.k);
+  int row = p.row_lo;
+  for (int i = s_ptr[p.row_lo] + (int)blockIdx.x; i < s_ptr[p.row_hi]; i += (int)gridDim.x) {
+    while (row + 1 < p.row_hi && s_ptr[row + 1] <= i) ++row;
+    const int pr = p.row_pair[b * NP + row];
+    const int c = p.col[(size_t)b * p.Emax + i];
+    {
+      // key rows c*64 .. c*64+63 in 16-byte pieces
+      constexpr int PV = 16 / (int)sizeof(E), PR = DK / PV;
 #pragma unroll
-    for (int it = 0; it < L * PR / 256; ++it) {
-      const int q = tid + 256 * it;
-      const int t = q / PR, e0 = (q % PR) * PV, tok = c * L + t;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (tok < sp.len) v = *reinterpret_cast<const uint4*>(K + ((size_t)(sp.tok0 + tok) * p.Nq + pr) * DK + e0);
-      *reinterpret_cast<uint4*>(&sK[t * DW_KS + e0]) = v;
+      for (int it = 0; it < L * PR / 256; ++it) {
+        const int q = tid + 256 * it;
+        const int t = q / PR, e0 = (q % PR) * PV, tok = c * L + t;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (tok < sp.len) v = *reinterpret_cast<const uint4*>(K + ((size_t)(sp.tok0 + tok) * p.Nq + pr) * DK + e0);
+        *reinterpret_cast<uint4*>(&sK[t * DW_KS + e0]) = v;
+      }
     }
-  }
-  __syncthreads();
-  // K^T blocks of the event: wave w forms key tiles 2w and 2w+1
-  I* KT = static_cast<I*>(p.KTpk) + ((size_t)b * p.Emax + i) * DK * L;
+    __syncthreads();
+    // K^T blocks of the event: wave w forms key tiles 2w and 2w+1
+    I* KT = static_cast<I*>(p.KTpk) + ((size_t)b * p.Emax + i) * DK * L;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+    for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int mt = 2 * w + mi;
-      *reinterpret_cast<frag_t<I>*>(KT + kblk(mt, ks) + 8 * (sizeof(I) == 2 ? kswz(lane) : lane)) =
-          cvt8<I, E>(ld_tr44(&sK[32 * ks * DW_KS + 16 * mt], DW_KS, lane));
+      for (int ks = 0; ks < 2; ++ks) {
+        const int mt = 2 * w + mi;
+        *reinterpret_cast<frag_t<I>*>(KT + kblk(mt, ks) + 8 * (sizeof(I) == 2 ? kswz(lane) : lane)) =
+            cvt8<I, E>(ld_tr44(&sK[32 * ks * DW_KS + 16 * mt], DW_KS, lane));
+      }
+    // (fp16 intermediates: the H scan forms W S as Cb (K S) itself)
+    if (p.Wpk != nullptr) {
+      const int ks_lo = (blockadj && w == 3) ? 1 : 0;
+      const int ks_hi = (w >= 2) ? 1 : 0;
+      for (int hh = 0; hh < 2; ++hh) {
+        const int h = 2 * pr + hh;
+        const I* Cb = static_cast<const I*>(p.Cb) + (((size_t)b * p.Nv + h) * p.C + c) * L * L;
+        // W^T = K^T Cb^T (rows dk, columns t).  K^T blocks are fragment-major in
+        // the permuted token order, so Cb is read in the same order.
+        f32x4 acc[8];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
+        for (int ks = ks_lo; ks <= ks_hi; ++ks) {
+          const I* cr = Cb + (16 * w + n16) * L + 32 * ks + 4 * g4;
+          const frag_t<I> fb = ld44(cr, cr + 16);
+#pragma unroll
+          for (int mt = 0; mt < 8; ++mt)
+            acc[mt] = mma(cvt8<I, E>(ld_tr44(&sK[32 * ks * DW_KS + 16 * mt], DW_KS, lane)), fb, acc[mt]);
+        }
+        // two stacked W^T tiles form one fragment-major W block
+        I* W = static_cast<I*>(p.Wpk) + (((size_t)b * p.Emax + i) * 2 + hh) * L * DK;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<frag_t<I>*>(W + wblk(q, w) + 8 * lane) = pack44<I>(acc[2 * q], acc[2 * q + 1]);
+      }
     }
-  // (fp16 intermediates: the H scan forms W S as Cb (K S) itself)
-  if (p.Wpk == nullptr) return;
-  const int ks_lo = (blockadj && w == 3) ? 1 : 0;
-  const int ks_hi = (w >= 2) ? 1 : 0;
-  for (int hh = 0; hh < 2; ++hh) {
-    const int h = 2 * pr + hh;
-    const I* Cb = static_cast<const I*>(p.Cb) + (((size_t)b * p.Nv + h) * p.C + c) * L * L;
-    // W^T = K^T Cb^T (rows dk, columns t).  K^T blocks are fragment-major in
-    // the permuted token order, so Cb is read in the same order.
-    f32x4 acc[8];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
-    for (int ks = ks_lo; ks <= ks_hi; ++ks) {
-      const I* cr = Cb + (16 * w + n16) * L + 32 * ks + 4 * g4;
-      const frag_t<I> fb = ld44(cr, cr + 16);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-        acc[mt] = mma(cvt8<I, E>(ld_tr44(&sK[32 * ks * DW_KS + 16 * mt], DW_KS, lane)), fb, acc[mt]);
-    }
-    // two stacked W^T tiles form one fragment-major W block
-    I* W = static_cast<I*>(p.Wpk) + (((size_t)b * p.Emax + i) * 2 + hh) * L * DK;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<frag_t<I>*>(W + wblk(q, w) + 8 * lane) = pack44<I>(acc[2 * q], acc[2 * q + 1]);
+    __syncthreads();   // the next event rewrites sK
   }
 }
 
@@ -480,7 +488,7 @@ hipError_t launch_gate(const GateArgs& a, int bf16, hipStream_t s) {
 }
 
 hipError_t launch_deferred_w(const DeferredWArgs& a, int bf16, hipStream_t s) {
-  dim3 grid(a.Emax, a.B);
+  dim3 grid(a.Emax < DW_BLOCKS ? a.Emax : DW_BLOCKS, a.B);
   if (bf16)
     hipLaunchKernelGGL(deferred_w_kernel<sgdn::bf16>, grid, dim3(256), 0, s, a);
   else
