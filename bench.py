@@ -29,6 +29,10 @@ repeats both modes with an fp32 and a bf16 O.
 
 Prints one JSON line.  value = tokens/s of the 24-layer stack (B*T per step);
 each timed configuration reports the mean and the median over its steps.
+The headline modes and the length sweep are also timed as replays of the
+step captured once as a HIP graph (graph_*), which removes the host's
+per-launch cost (it matters at the short lengths, where a layer's kernels
+are short).
 roofline = the dominant kernel's algorithmic bytes per layer over its mean
 time per layer (HIP events recorded by the library on the caller's stream;
 in the sparse path the H scan of CSR rows 4-15 runs on a second stream
@@ -73,7 +77,7 @@ def parse():
     ap.add_argument("--seqlen", type=int, default=T)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=("both", "sparse", "dense"), default="both")
-    ap.add_argument("--cpu-tokens", type=int, default=4096,
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="tokens of one layer each oracle worker processes")
     ap.add_argument("--cpu-workers", type=int, default=16,
                     help="oracle worker processes (at most the host's usable cores)")
@@ -309,6 +313,38 @@ def timed_steps(args, step):
         evs[i][1].record()
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in evs]
+    return statistics.fmean(ms), statistics.median(ms)
+
+
+def graph_steps(args, step):
+    """The same step captured once as a HIP graph (torch.cuda.CUDAGraph over
+    the library's launches on the caller's stream and its second stream),
+    then args.steps timed replays after args.warmup untimed ones; returns
+    (mean, median) ms per replay."""
+    import statistics
+    import torch
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        step(None)
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(None)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record()
+        g.replay()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    del g
     return statistics.fmean(ms), statistics.median(ms)
 
 
@@ -550,9 +586,13 @@ def sweep_leg(args, layers, ws):
                         ops.prefill_dense(x["q"], x["k"], x["v"], x["a"], x["beta"], solve="exact",
                                           o=o[:, :Tn], s_final=sf, workspace=ws)
             mean, med = timed_steps(args, step)
+            gmean, gmed = graph_steps(args, step)
             row[mode] = {"ms_per_step": round(mean, 4), "median_ms_per_step": round(med, 4),
                          "value_tok_s": round(B * Tn / (mean / 1e3), 1),
-                         "per_layer_tok_s": round(B * Tn * len(layers) / (mean / 1e3), 1)}
+                         "per_layer_tok_s": round(B * Tn * len(layers) / (mean / 1e3), 1),
+                         "graph_ms_per_step": round(gmean, 4),
+                         "graph_median_ms_per_step": round(gmed, 4),
+                         "graph_value_tok_s": round(B * Tn / (gmean / 1e3), 1)}
             if mode == "sparse":
                 import torch
                 stt = torch.stack([st for (_, _, _, st) in layers]).float().cpu()[:, 0, :]
@@ -569,10 +609,14 @@ def sweep_leg(args, layers, ws):
             fl = flops_per_token(mode, keep) * B * Tn
             row[mode]["mfma_frac"] = round(fl / (per_layer_ms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS, 4)
         row["sparse_speedup_over_dense"] = round(row["dense"]["ms_per_step"] / row["sparse"]["ms_per_step"], 3)
+        row["graph_sparse_speedup_over_dense"] = round(
+            row["dense"]["graph_ms_per_step"] / row["sparse"]["graph_ms_per_step"], 3)
         out[str(Tn)] = row
         print(f"[bench] T={Tn}: sparse {row['sparse']['ms_per_step']:.3f} ms, dense "
               f"{row['dense']['ms_per_step']:.3f} ms per {len(layers)}-layer step "
-              f"({row['sparse_speedup_over_dense']:.2f}x)", file=sys.stderr, flush=True)
+              f"({row['sparse_speedup_over_dense']:.2f}x); graph replay: sparse "
+              f"{row['sparse']['graph_ms_per_step']:.3f} ms, dense {row['dense']['graph_ms_per_step']:.3f} ms "
+              f"({row['graph_sparse_speedup_over_dense']:.2f}x)", file=sys.stderr, flush=True)
     return out
 
 
@@ -763,13 +807,15 @@ def main():
                       for s in range(args.steps) for l in range(L))
             stage_ms[name] = tot / (args.steps * L)
         stats = torch.stack([st for (_, _, _, st) in layers]).cpu()
+        gmean, gmed = graph_steps(args, step)
         return dict(ms_per_step=ms, median_ms_per_step=med, wall_s=wall, stage_ms_per_launch=stage_ms,
-                    stats=stats)
+                    stats=stats, graph_ms_per_step=gmean, graph_median_ms_per_step=gmed)
 
     res = {}
     for mode in (("sparse", "dense") if args.mode == "both" else (args.mode,)):
         res[mode] = run_mode(mode)
-        print(f"[bench] {mode}: {res[mode]['ms_per_step']:.3f} ms per {L}-layer step; stages (ms/launch) "
+        print(f"[bench] {mode}: {res[mode]['ms_per_step']:.3f} ms per {L}-layer step "
+              f"(graph replay {res[mode]['graph_ms_per_step']:.3f} ms); stages (ms/launch) "
               + ", ".join(f"{k} {v:.3f}" for k, v in res[mode]["stage_ms_per_launch"].items()),
               file=sys.stderr, flush=True)
 
@@ -839,6 +885,8 @@ def main():
                      "per_layer_tok_s": round(B * Tn / (rr["ms_per_step"] / 1e3 / args.layers), 1),
                      "ms_per_step": round(rr["ms_per_step"], 4),
                      "median_ms_per_step": round(rr["median_ms_per_step"], 4),
+                     "graph_ms_per_step": round(rr["graph_ms_per_step"], 4),
+                     "graph_median_ms_per_step": round(rr["graph_median_ms_per_step"], 4),
                      "stage_ms_per_launch": {k: round(v, 4) for k, v in rr["stage_ms_per_launch"].items()},
                      "roofline": roofline(mode), "path_roofline": pr, "mfma_roofline": mr,
                      "binding_roofline": "hbm" if pr["roofline_ms_per_layer"] >= mr["roofline_ms_per_layer"] else "mfma"}
