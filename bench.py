@@ -89,6 +89,8 @@ def parse():
                     help="skip the packed variable-length leg")
     ap.add_argument("--no-ablations", action="store_true",
                     help="skip the kernel-pipeline ablation leg")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replay timings (one call per layer and step)")
     ap.add_argument("--no-output-types", action="store_true",
                     help="skip the leg that reruns both modes with an fp32 and a bf16 O")
     ap.add_argument("--no-variants", action="store_true",
@@ -586,13 +588,14 @@ def sweep_leg(args, layers, ws):
                         ops.prefill_dense(x["q"], x["k"], x["v"], x["a"], x["beta"], solve="exact",
                                           o=o[:, :Tn], s_final=sf, workspace=ws)
             mean, med = timed_steps(args, step)
-            gmean, gmed = graph_steps(args, step)
             row[mode] = {"ms_per_step": round(mean, 4), "median_ms_per_step": round(med, 4),
                          "value_tok_s": round(B * Tn / (mean / 1e3), 1),
-                         "per_layer_tok_s": round(B * Tn * len(layers) / (mean / 1e3), 1),
-                         "graph_ms_per_step": round(gmean, 4),
-                         "graph_median_ms_per_step": round(gmed, 4),
-                         "graph_value_tok_s": round(B * Tn / (gmean / 1e3), 1)}
+                         "per_layer_tok_s": round(B * Tn * len(layers) / (mean / 1e3), 1)}
+            if not args.no_graph:
+                gmean, gmed = graph_steps(args, step)
+                row[mode].update({"graph_ms_per_step": round(gmean, 4),
+                                  "graph_median_ms_per_step": round(gmed, 4),
+                                  "graph_value_tok_s": round(B * Tn / (gmean / 1e3), 1)})
             if mode == "sparse":
                 import torch
                 stt = torch.stack([st for (_, _, _, st) in layers]).float().cpu()[:, 0, :]
@@ -609,14 +612,16 @@ def sweep_leg(args, layers, ws):
             fl = flops_per_token(mode, keep) * B * Tn
             row[mode]["mfma_frac"] = round(fl / (per_layer_ms / 1e3) / 1e12 / MFMA_PEAK_TFLOPS, 4)
         row["sparse_speedup_over_dense"] = round(row["dense"]["ms_per_step"] / row["sparse"]["ms_per_step"], 3)
-        row["graph_sparse_speedup_over_dense"] = round(
-            row["dense"]["graph_ms_per_step"] / row["sparse"]["graph_ms_per_step"], 3)
+        gtxt = ""
+        if not args.no_graph:
+            row["graph_sparse_speedup_over_dense"] = round(
+                row["dense"]["graph_ms_per_step"] / row["sparse"]["graph_ms_per_step"], 3)
+            gtxt = (f"; graph replay: sparse {row['sparse']['graph_ms_per_step']:.3f} ms, dense "
+                    f"{row['dense']['graph_ms_per_step']:.3f} ms ({row['graph_sparse_speedup_over_dense']:.2f}x)")
         out[str(Tn)] = row
         print(f"[bench] T={Tn}: sparse {row['sparse']['ms_per_step']:.3f} ms, dense "
               f"{row['dense']['ms_per_step']:.3f} ms per {len(layers)}-layer step "
-              f"({row['sparse_speedup_over_dense']:.2f}x); graph replay: sparse "
-              f"{row['sparse']['graph_ms_per_step']:.3f} ms, dense {row['dense']['graph_ms_per_step']:.3f} ms "
-              f"({row['graph_sparse_speedup_over_dense']:.2f}x)", file=sys.stderr, flush=True)
+              f"({row['sparse_speedup_over_dense']:.2f}x){gtxt}", file=sys.stderr, flush=True)
     return out
 
 
@@ -807,15 +812,15 @@ def main():
                       for s in range(args.steps) for l in range(L))
             stage_ms[name] = tot / (args.steps * L)
         stats = torch.stack([st for (_, _, _, st) in layers]).cpu()
-        gmean, gmed = graph_steps(args, step)
+        gmean, gmed = (None, None) if args.no_graph else graph_steps(args, step)
         return dict(ms_per_step=ms, median_ms_per_step=med, wall_s=wall, stage_ms_per_launch=stage_ms,
                     stats=stats, graph_ms_per_step=gmean, graph_median_ms_per_step=gmed)
 
     res = {}
     for mode in (("sparse", "dense") if args.mode == "both" else (args.mode,)):
         res[mode] = run_mode(mode)
-        print(f"[bench] {mode}: {res[mode]['ms_per_step']:.3f} ms per {L}-layer step "
-              f"(graph replay {res[mode]['graph_ms_per_step']:.3f} ms); stages (ms/launch) "
+        gtxt = "" if args.no_graph else f" (graph replay {res[mode]['graph_ms_per_step']:.3f} ms)"
+        print(f"[bench] {mode}: {res[mode]['ms_per_step']:.3f} ms per {L}-layer step{gtxt}; stages (ms/launch) "
               + ", ".join(f"{k} {v:.3f}" for k, v in res[mode]["stage_ms_per_launch"].items()),
               file=sys.stderr, flush=True)
 
@@ -885,8 +890,8 @@ def main():
                      "per_layer_tok_s": round(B * Tn / (rr["ms_per_step"] / 1e3 / args.layers), 1),
                      "ms_per_step": round(rr["ms_per_step"], 4),
                      "median_ms_per_step": round(rr["median_ms_per_step"], 4),
-                     "graph_ms_per_step": round(rr["graph_ms_per_step"], 4),
-                     "graph_median_ms_per_step": round(rr["graph_median_ms_per_step"], 4),
+                     "graph_ms_per_step": None if args.no_graph else round(rr["graph_ms_per_step"], 4),
+                     "graph_median_ms_per_step": None if args.no_graph else round(rr["graph_median_ms_per_step"], 4),
                      "stage_ms_per_launch": {k: round(v, 4) for k, v in rr["stage_ms_per_launch"].items()},
                      "roofline": roofline(mode), "path_roofline": pr, "mfma_roofline": mr,
                      "binding_roofline": "hbm" if pr["roofline_ms_per_layer"] >= mr["roofline_ms_per_layer"] else "mfma"}
