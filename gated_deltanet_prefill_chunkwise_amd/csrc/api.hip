@@ -534,22 +534,19 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   IntraArgs ia = intra_args(pl, ws, k, v, a, beta, 1);
   ia.stats = stw;
   SGDN_TRY(launch_intra(ia, pl.bf16, s));
+  mark(dbg, SGDN_EV_INTRA, s);
+  // tail scores, prefix and (with the selector) gate energies in one launch
   ScoreArgs sca{at<float>(ws, pl, B_SPART), at<float>(ws, pl, B_SCORE),
                 (long long)pl.B * pl.Nv * pl.C, params->tail};
-  SGDN_TRY(launch_score(sca, s));
-  mark(dbg, SGDN_EV_INTRA, s);
   PrefixArgs pa{at<float>(ws, pl, B_GAMMA), at<double>(ws, pl, B_P), pl.B, pl.Nv, pl.C,
                 pl.cu, pl.T};
-  SGDN_TRY(launch_prefix(pa, s));
+  GateArgs ga{z, params->norm_weight, at<float>(ws, pl, B_ETAP), pl.B, pl.T, pl.Nv, pl.C, pl.cu, stw};
+  SGDN_TRY(launch_prep(pa, mask_override == nullptr ? &ga : nullptr, sca, pl.bf16, s));
   mark(dbg, SGDN_EV_PREFIX, s);
   if ((st = debug_copies(pl, ws, dbg, s, 1)) != SGDN_OK) return st;
+  mark(dbg, SGDN_EV_GATE, s);
 
   // selector and event layout
-  if (mask_override == nullptr) {
-    GateArgs ga{z, params->norm_weight, at<float>(ws, pl, B_ETAP), pl.B, pl.T, pl.Nv, pl.C, pl.cu, stw};
-    SGDN_TRY(launch_gate(ga, pl.bf16, s));
-  }
-  mark(dbg, SGDN_EV_GATE, s);
   const int Emax = mask_override ? NP * pl.C : NP * pl.kH;
   SelectArgs sa{};
   sa.score = at<float>(ws, pl, B_SCORE); sa.gamma = at<float>(ws, pl, B_GAMMA);
@@ -598,13 +595,10 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
                     pl.B, pl.Nv, pl.C, Emax};
   auto events = [&](int lo, int hi, hipStream_t q) -> hipError_t {
     if (csr_off) return launch_evrec_all(xa_all, q);   // every chunk an event
-    hipError_t e = hipSuccess;
-    if (!wall) {
-      da.row_lo = lo; da.row_hi = hi;
-      if ((e = launch_deferred_w(da, pl.bf16, q)) != hipSuccess) return e;
-    }
     ea.row_lo = lo; ea.row_hi = hi;
-    return launch_evrec(ea, q);
+    if (wall) return launch_evrec(ea, q);
+    da.row_lo = lo; da.row_hi = hi;
+    return launch_events(da, ea, pl.bf16, q);          // deferred W and the records
   };
   if (s0 != nullptr) {
     S0PrepArgs s0a{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv, stw};

@@ -229,6 +229,12 @@ hipError_t launch_evrec(const EvRecArgs& a, hipStream_t s);
 hipError_t launch_evrec_all(const EvAllArgs& a, hipStream_t s);
 hipError_t launch_s0prep(const S0PrepArgs& a, int bf16, hipStream_t s);
 hipError_t launch_gate(const GateArgs& a, int bf16, hipStream_t s);
+// gate energies (ga non-null), prefix and tail scores in one launch (sparse path)
+hipError_t launch_prep(const PrefixArgs& pa, const GateArgs* ga, const ScoreArgs& sc, int bf16,
+                       hipStream_t s);
+// deferred W + sparse event records of rows ea.row_lo .. ea.row_hi - 1 in one
+// launch (da and ea cover the same rows)
+hipError_t launch_events(const DeferredWArgs& da, const EvRecArgs& ea, int bf16, hipStream_t s);
 hipError_t launch_select_full(const SelectArgs& a, hipStream_t s);
 hipError_t launch_deferred_w(const DeferredWArgs& a, int bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int bf16, hipStream_t s);

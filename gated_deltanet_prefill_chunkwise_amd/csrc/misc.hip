@@ -12,8 +12,8 @@ namespace {
 // contiguous run of chunks, then an exclusive wave scan joins the runs.
 // Chunks past the end of a shorter packed sequence retain everything
 // (gamma = 0 there; their gamma entries are not read).
-__global__ __launch_bounds__(64) void prefix_kernel(PrefixArgs p) {
-  const int bh = blockIdx.x, lane = threadIdx.x, C = p.C;
+__device__ __forceinline__ void prefix_body(const PrefixArgs& p, int bh, int lane) {
+  const int C = p.C;
   const int Cv = p.cu == nullptr ? C : chunks_of(seq_span(p.cu, bh / p.Nv, p.T).len);
   const float* gm = p.gamma + (size_t)bh * C;
   double* P = p.P + (size_t)bh * (C + 1);
@@ -48,6 +48,10 @@ __global__ __launch_bounds__(64) void prefix_kernel(PrefixArgs p) {
         P[c0 + u + 1] = acc;
       }
   }
+}
+
+__global__ __launch_bounds__(64) void prefix_kernel(PrefixArgs p) {
+  prefix_body(p, blockIdx.x, threadIdx.x);
 }
 
 // Table of the valid chunks of packed sequences (one workgroup): per-thread
@@ -98,13 +102,16 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(ChunkTableArgs p) {
 
 // s_{c,h} = ||U_{c,h}[64 - tail : 64]||_F (SparseGDN reading notes, Sec. 2.4,
 // Eq. (9); Tail-8/32/64 are the window ablations of Fig. 10).
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs p) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void score_body(const ScoreArgs& p, long long i) {
   if (i >= p.n) return;
   const float* q = p.part + i * 8;
   float s = 0.f;
   for (int k = 8 - p.tail / 8; k < 8; ++k) s += q[k];
   p.score[i] = sqrtf(s);
+}
+
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs p) {
+  score_body(p, (long long)blockIdx.x * 256 + threadIdx.x);
 }
 
 // Compact-states ablation (SparseGDN reading notes, Sec. 3.6, Table 6): the
@@ -189,8 +196,7 @@ __global__ __launch_bounds__(256) void stats_init_kernel(StatsInitArgs p) {
 // scattered sample reads are not held up by one CU's outstanding misses.
 constexpr int GATE_THREADS = 1024;
 template <typename E>
-__global__ __launch_bounds__(GATE_THREADS) void gate_kernel(GateArgs p) {
-  const int h = blockIdx.x, b = blockIdx.y, zb = blockIdx.z, tid = threadIdx.x;
+__device__ __forceinline__ void gate_body(const GateArgs& p, int h, int b, int zb, int tid) {
   const E* z = static_cast<const E*>(p.z);
   const SeqSpan sp = seq_span(p.cu, b, p.T);
   const int ns = 4 * chunks_of(sp.len);
@@ -220,6 +226,30 @@ __global__ __launch_bounds__(GATE_THREADS) void gate_kernel(GateArgs p) {
   }
 }
 
+template <typename E>
+__global__ __launch_bounds__(GATE_THREADS) void gate_kernel(GateArgs p) {
+  gate_body<E>(p, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x);
+}
+
+// The gate energies, the prefix and the tail scores in one launch (each reads
+// only the inputs and what the intra kernel left; two dependent launches
+// fewer): workgroups 0 .. ng - 1 are gate_kernel's (h, b, z) in that order,
+// the next np one prefix wave each (batch-major heads; the other waves leave:
+// a head's strided loads and stores want a CU's address unit of their own,
+// as in prefix_kernel), the rest 1024 scores each.
+template <typename E>
+__global__ __launch_bounds__(GATE_THREADS) void prep_kernel(PrefixArgs pa, GateArgs ga, ScoreArgs sc,
+                                                            int ng, int np) {
+  const int id = blockIdx.x, tid = threadIdx.x;
+  if (id < ng) {
+    gate_body<E>(ga, id % ga.Nv, (id / ga.Nv) % ga.B, id / (ga.Nv * ga.B), tid);
+  } else if (id < ng + np) {
+    if (tid < 64) prefix_body(pa, id - ng, tid);
+  } else {
+    score_body(sc, (long long)(id - ng - np) * GATE_THREADS + tid);
+  }
+}
+
 // Deferred W of kept events only (SparseGDN reading notes, Sec. 2.5,
 // Eq. (15)).  The event's key rows are staged in LDS (zero past the end of
 // the sequence) and turned into the fragment-major K^T blocks the H scan
@@ -236,11 +266,10 @@ constexpr int DW_KS = DK + 8;   // row stride (elements) of the staged key rows
 constexpr int DW_BLOCKS = 2048; // workgroups per sequence
 
 template <typename E>
-__global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
+__device__ __forceinline__ void deferred_w_body(const DeferredWArgs& p, int bx, int nbx, int b) {
   using I = inter_t<E>;
   __shared__ __align__(16) E sK[L * DW_KS];
   __shared__ int s_ptr[17];
-  const int b = blockIdx.y;
   const int NP = p.Nv / 2;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int n16 = lane & 15, g4 = lane >> 4;
@@ -250,7 +279,7 @@ __global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
   const SeqSpan sp = seq_span(p.cu, b, p.T);
   const E* K = static_cast<const E*>(p.k);
   int row = p.row_lo;
-  for (int i = s_ptr[p.row_lo] + (int)blockIdx.x; i < s_ptr[p.row_hi]; i += (int)gridDim.x) {
+  for (int i = s_ptr[p.row_lo] + bx; i < s_ptr[p.row_hi]; i += nbx) {
     while (row + 1 < p.row_hi && s_ptr[row + 1] <= i) ++row;
     const int pr = p.row_pair[b * NP + row];
     const int c = p.col[(size_t)b * p.Emax + i];
@@ -307,6 +336,11 @@ __global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
   }
 }
 
+template <typename E>
+__global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
+  deferred_w_body<E>(p, blockIdx.x, gridDim.x, blockIdx.y);
+}
+
 // Event records of the H scan (SparseGDN reading notes, Sec. 2.1 Eq. (2) and
 // Sec. 2.6 Eq. (21)).  Dense: every chunk is an event, F_in = 1, and the state
 // after odd chunk c (c + 1 < C) is the snapshot (c + 1) / 2 - 1 of the group
@@ -326,12 +360,12 @@ __global__ __launch_bounds__(256) void evrec_dense_kernel(EvRecArgs p) {
   reinterpret_cast<int4*>(p.rec)[i] = r;
 }
 
-__global__ __launch_bounds__(1024) void evrec_sparse_kernel(EvRecArgs p) {
-  const int row = p.row_lo + (int)blockIdx.x, b = blockIdx.y, NP = p.Nv / 2;
+__device__ __forceinline__ void evrec_sparse_body(const EvRecArgs& p, int row, int b, int tid, int nthr) {
+  const int NP = p.Nv / 2;
   const int beg = p.row_ptr[b * (NP + 1) + row], end = p.row_ptr[b * (NP + 1) + row + 1];
   const int pr = p.row_pair[b * NP + row];
   const int32_t* col = p.col + (size_t)b * p.Emax;
-  for (int i = beg + (int)threadIdx.x; i < end; i += 1024) {
+  for (int i = beg + tid; i < end; i += nthr) {
     const int c = col[i];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -346,6 +380,22 @@ __global__ __launch_bounds__(1024) void evrec_sparse_kernel(EvRecArgs p) {
       reinterpret_cast<int4*>(p.rec)[((size_t)b * p.Emax + i) * 2 + hh] = r;
     }
   }
+}
+
+__global__ __launch_bounds__(1024) void evrec_sparse_kernel(EvRecArgs p) {
+  evrec_sparse_body(p, p.row_lo + (int)blockIdx.x, blockIdx.y, threadIdx.x, 1024);
+}
+
+// Deferred W and the event records of the same rows in one launch (both read
+// only the CSR layout and the prefix; one dependent launch fewer):
+// workgroups 0 .. nd - 1 walk the kept events as deferred_w_kernel does, the
+// rest write the records of one row each.
+template <typename E>
+__global__ __launch_bounds__(256) void events_kernel(DeferredWArgs da, EvRecArgs ea, int nd) {
+  if ((int)blockIdx.x < nd)
+    deferred_w_body<E>(da, blockIdx.x, nd, blockIdx.y);
+  else
+    evrec_sparse_body(ea, ea.row_lo + (int)blockIdx.x - nd, blockIdx.y, threadIdx.x, 256);
 }
 
 // CSR-off control (SparseGDN reading notes, Sec. 3.6, Table 6): the H scan
@@ -484,6 +534,30 @@ hipError_t launch_gate(const GateArgs& a, int bf16, hipStream_t s) {
     hipLaunchKernelGGL(gate_kernel<sgdn::bf16>, dim3(a.Nv, a.B, GATE_SPLIT), dim3(GATE_THREADS), 0, s, a);
   else
     hipLaunchKernelGGL(gate_kernel<float>, dim3(a.Nv, a.B, GATE_SPLIT), dim3(GATE_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const PrefixArgs& pa, const GateArgs* ga, const ScoreArgs& sc, int bf16,
+                       hipStream_t s) {
+  const int ng = ga != nullptr ? ga->Nv * ga->B * GATE_SPLIT : 0;
+  const int np = pa.B * pa.Nv;
+  const int ns = (int)((sc.n + GATE_THREADS - 1) / GATE_THREADS);
+  const GateArgs g = ga != nullptr ? *ga : GateArgs{};
+  const dim3 grid(ng + np + ns);
+  if (bf16)
+    hipLaunchKernelGGL(prep_kernel<sgdn::bf16>, grid, dim3(GATE_THREADS), 0, s, pa, g, sc, ng, np);
+  else
+    hipLaunchKernelGGL(prep_kernel<float>, grid, dim3(GATE_THREADS), 0, s, pa, g, sc, ng, np);
+  return hipGetLastError();
+}
+
+hipError_t launch_events(const DeferredWArgs& da, const EvRecArgs& ea, int bf16, hipStream_t s) {
+  const int nd = da.Emax < DW_BLOCKS ? da.Emax : DW_BLOCKS;
+  const dim3 grid(nd + (ea.row_hi - ea.row_lo), da.B);
+  if (bf16)
+    hipLaunchKernelGGL(events_kernel<sgdn::bf16>, grid, dim3(256), 0, s, da, ea, nd);
+  else
+    hipLaunchKernelGGL(events_kernel<float>, grid, dim3(256), 0, s, da, ea, nd);
   return hipGetLastError();
 }
 
