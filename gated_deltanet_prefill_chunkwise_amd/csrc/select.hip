@@ -58,6 +58,13 @@ __device__ double exp2_fixed(double x) {
 
 __device__ __forceinline__ double ord_key(double x) { return x != x ? -__builtin_inf() : x; }
 
+// Orders one wave's LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ double powi_fixed(double r, int n) {
   double res = 1.0, base = r;
   while (n) {
@@ -206,17 +213,42 @@ __global__ __launch_bounds__(1024) void select_rank_kernel(SelectArgs p) {
   if (part == 0 && c < C) rk[c] = (c >= 1 && c <= C - 2) ? r : -1;
 }
 
-// B(x, k) = k (n-k) / n (mean x[:k] - mean x[k:])^2 over the wave-held sorted
-// values vals[0..n) (Eq. (14)).
-__device__ double split_score(const double* vals, int n, int k, int lane) {
-  if (k <= 0 || k >= n) return 0.0;
-  const double a = wave_sum(lane < k ? vals[lane] : 0.0);
-  const double c = wave_sum(lane < n - k ? vals[k + lane] : 0.0);
-  const double m1 = a / k;
-  const double m2 = c / (n - k);
-  const double f = (double)(k * (n - k)) / n;
-  const double dm = m1 - m2;
-  return f * (dm * dm);
+// B(x, k) = k (n-k) / n (mean x[:k] - mean x[k:])^2 (Eq. (14)) over the
+// sorted values vals[0..n) (n <= 16) for the candidate counts k0 .. k0 +
+// ncand - 1 (ncand <= 4) at once; B = 0 for k <= 0 or k >= n.  Candidate s
+// takes lanes 16 s .. 16 s + 15, which form its two sums as the 64-lane
+// interleaved sums of the selector's rules: with at most 16 values the
+// 64-lane tree's first two levels only add +0 (and no partial sum here is
+// -0), so its 16-lane part gives the same results.  Returns the first count
+// with the largest B (ties: the earlier one).
+__device__ int best_split(const double* vals, int n, int k0, int ncand, int lane) {
+  const int sg = lane >> 4, j = lane & 15;
+  const int k = sg < ncand ? k0 + sg : -1;
+  const bool valid = k > 0 && k < n;
+  double a = (valid && j < k) ? vals[j] : 0.0;
+  double c = (valid && j < n - k) ? vals[k + j] : 0.0;
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1) {
+    const double oa = __shfl_down(a, w, 16);
+    const double oc = __shfl_down(c, w, 16);
+    a = a + oa;
+    c = c + oc;
+  }
+  double v = 0.0;
+  if (valid) {
+    const double m1 = a / k;
+    const double m2 = c / (n - k);
+    const double f = (double)(k * (n - k)) / n;
+    const double dm = m1 - m2;
+    v = f * (dm * dm);
+  }
+  int best_i = 0;
+  double best = 0.0;
+  for (int i = 0; i < ncand; ++i) {
+    const double vi = __shfl(v, 16 * i, 64);
+    if (i == 0 || vi > best) { best = vi; best_i = i; }
+  }
+  return k0 + best_i;
 }
 
 // Per (sequence, head pair) record handed from select_pair_kernel to
@@ -254,18 +286,23 @@ __device__ __forceinline__ unsigned long long ref_word(unsigned long long bal, i
   return __ballot(((bal >> lane) & 1ull) && lo_e <= hi);
 }
 
-// Eqs. (11)-(12) for one head pair, and its referenced-event counts: workgroup
-// (pp, b) stages the pair's ranks and scores, then wave 0 forms the band sums
-// of both heads (the ranks of Eq. (10) between k_L - 2 and k_M - 2, and
-// between k_M - 2 and k_H - 2; each sum one wave's lane-interleaved sum),
-// wave 1 the lifetimes of Eq. (11), wave 2 the visibilities (and, in pair 0,
-// eta from the gate kernel's parts), waves 3-5 the referenced events with the
-// keep count of tier 0, 1, 2.  Dynamic LDS: 2 C ints (ranks, keep ranks) and
-// 2 C floats (scores).
+// Eqs. (11)-(12) for one head pair, and its referenced-event counts:
+// workgroup (pp, b) stages the pair's ranks and scores, forms the kept words
+// of the pair for each of the three keep counts (all but waves 0-4), finds
+// the first kept chunk after every word (waves 5-7, one keep count each),
+// then in parallel: waves 0-1 the band sums of head 0 and 1 (the ranks of
+// Eq. (10) between k_L - 2 and k_M - 2, and between k_M - 2 and k_H - 2; each
+// sum one wave's lane-interleaved sum), waves 2-3 their lifetimes (Eq. (11)),
+// wave 4 the visibilities (and, in pair 0, eta from the gate kernel's parts),
+// the others the referenced events with each keep count.  Dynamic LDS: 2 C
+// ints (ranks, keep ranks) and 2 C floats (scores).
 __global__ __launch_bounds__(1024) void select_pair_kernel(SelectArgs p) {
   extern __shared__ int32_t s_rank[];
+  constexpr int NWMAX = MAX_C / 64;
   __shared__ double s_sum[4], s_L[2], s_G[2];
   __shared__ int s_nref[3];
+  __shared__ unsigned long long s_kw[3][NWMAX];
+  __shared__ int s_nf[3][NWMAX];
   const int pp = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int CS = p.C, C = valid_chunks(p, b), G = (C + 1) / 2, NW = (C + 63) / 64;
@@ -276,6 +313,7 @@ __global__ __launch_bounds__(1024) void select_pair_kernel(SelectArgs p) {
   tier_counts(C, p.keep_bp, p.rate_bp, kk);
   const int kL = kk[0], kM = kk[1], kH = kk[2];
   const int h0 = 2 * pp;
+  constexpr int FIRST_REF_WAVE = 5;
   {
     const int32_t* rk = p.rank + ((size_t)b * NP + pp) * CS;
     const int32_t* ra = key ? p.rank_alt + ((size_t)b * NP + pp) * CS : nullptr;
@@ -301,35 +339,73 @@ __global__ __launch_bounds__(1024) void select_pair_kernel(SelectArgs p) {
         s_sc[CS + c] = x1[u];
       }
     }
+    if (tid < 3) s_nref[tid] = 0;
   }
   __syncthreads();
-  if (wv == 0) {
-    double alm[2] = {0.0, 0.0}, amh[2] = {0.0, 0.0};
-    for (int c = lane; c < C; c += 64) {
-      const int r = s_rank[c];
-      const bool inm = r >= kL - 2 && r < kM - 2, inh = r >= kM - 2 && r < kH - 2;
+  // kept words for the three keep counts (word t NW + i over the ref waves)
+  for (int q = wv - FIRST_REF_WAVE; q >= 0 && q < 3 * NW; q += 16 - FIRST_REF_WAVE) {
+    const int t = q / NW, i = q - t * NW;
+    const unsigned long long bal = kept_word(s_keep, i, lane, C, kk[t]);
+    if (lane == 0) s_kw[t][i] = bal;
+  }
+  __syncthreads();
+  if (wv >= FIRST_REF_WAVE && wv < FIRST_REF_WAVE + 3) {
+    // first kept chunk after each word (C + 1 if none): lane l holds words
+    // 2 l and 2 l + 1, suffix minimum over the lanes
+    const int t = wv - FIRST_REF_WAVE;
+    int f2[2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const double xs = (double)s_sc[hh * CS + c];
-        alm[hh] = alm[hh] + (inm ? xs : 0.0);
-        amh[hh] = amh[hh] + (inh ? xs : 0.0);
+    for (int h = 0; h < 2; ++h) {
+      const int i = 2 * lane + h;
+      const unsigned long long bal = i < NW ? s_kw[t][i] : 0ull;
+      f2[h] = bal ? 64 * i + (int)__builtin_ctzll(bal) : C + 1;
+    }
+    int suf = min(f2[0], f2[1]);
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int f = __shfl_down(suf, d, 64);
+      if (lane + d < 64) suf = min(suf, f);
+    }
+    int after = __shfl_down(suf, 1, 64);
+    if (lane == 63) after = C + 1;
+    if (2 * lane < NW) s_nf[t][2 * lane] = min(f2[1], after);
+    if (2 * lane + 1 < NW) s_nf[t][2 * lane + 1] = after;
+  }
+  __syncthreads();
+  if (wv < 2) {
+    // band sums of head wv: each lane sums its chunks in ascending order;
+    // eight chunks' operands are read before their additions
+    const int hh = wv;
+    double alm = 0.0, amh = 0.0;
+    for (int c0 = lane; c0 < C; c0 += 64 * 8) {
+      int rr[8];
+      float xs[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + 64 * u;
+        rr[u] = c < C ? s_rank[c] : -1;
+        xs[u] = c < C ? s_sc[hh * CS + c] : 0.f;
       }
-    }
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const double tl = wave_sum(alm[hh]), th = wave_sum(amh[hh]);
-      if (lane == 0) { s_sum[hh] = tl; s_sum[2 + hh] = th; }
+      for (int u = 0; u < 8; ++u)
+        if (c0 + 64 * u < C) {
+          const int r = rr[u];
+          const bool inm = r >= kL - 2 && r < kM - 2, inh = r >= kM - 2 && r < kH - 2;
+          const double x = (double)xs[u];
+          alm = alm + (inm ? x : 0.0);
+          amh = amh + (inh ? x : 0.0);
+        }
     }
-  } else if (wv == 1) {
+    const double tl = wave_sum(alm), th = wave_sum(amh);
+    if (lane == 0) { s_sum[hh] = tl; s_sum[2 + hh] = th; }
+  } else if (wv < 4) {
+    const int hh = wv - 2;
     const int lo = C > 16 ? C - 16 : 0, nwin = C - lo;
-    const float* gm = p.gamma + ((size_t)b * NV + h0) * CS;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const double xw = lane < nwin ? exp2_fixed((double)gm[hh * CS + lo + lane]) : 0.0;
-      const double tot = wave_sum(xw);
-      if (lane == 0) s_L[hh] = lifetime(tot / nwin, C);
-    }
-  } else if (wv == 2) {
+    const float* gm = p.gamma + ((size_t)b * NV + h0 + hh) * CS;
+    const double xw = lane < nwin ? exp2_fixed((double)gm[lo + lane]) : 0.0;
+    const double tot = wave_sum(xw);
+    if (lane == 0) s_L[hh] = lifetime(tot / nwin, C);
+  } else if (wv == 4) {
     // eta of head `lane`: given, or the mean from the gate kernel's parts
     float eh = 0.f;
     if (lane < NV) {
@@ -346,17 +422,18 @@ __global__ __launch_bounds__(1024) void select_pair_kernel(SelectArgs p) {
     const double etab = wave_sum(lane < NV ? (double)eh : 0.0) / NV;
     if (lane == h0 || lane == h0 + 1)
       s_G[lane - h0] = (etab > 0.0 && !p.unit_visibility) ? sqrt((double)eh / etab) : 1.0;
-  } else if (wv >= 3 && wv <= 5) {
-    const int k = kk[wv - 3];
-    // words are walked from the last one, carrying the first kept chunk
-    // after the current word
-    int nextfirst = C + 1, cnt = 0;
-    for (int i = NW - 1; i >= 0; --i) {
-      const unsigned long long bal = kept_word(s_keep, i, lane, C, k);
-      cnt += __popcll(ref_word(bal, i, lane, nextfirst, G));
-      if (bal) nextfirst = 64 * i + (int)__builtin_ctzll(bal);
+  } else {
+    int cnt[3] = {0, 0, 0};
+    for (int q = wv - FIRST_REF_WAVE; q < 3 * NW; q += 16 - FIRST_REF_WAVE) {
+      const int t = q / NW, i = q - t * NW;
+      const int n = __popcll(ref_word(s_kw[t][i], i, lane, s_nf[t][i], G));
+      cnt[0] += t == 0 ? n : 0;
+      cnt[1] += t == 1 ? n : 0;
+      cnt[2] += t == 2 ? n : 0;
     }
-    if (lane == 0) s_nref[wv - 3] = cnt;
+    if (lane == 0)
+      for (int t = 0; t < 3; ++t)
+        if (cnt[t]) atomicAdd(&s_nref[t], cnt[t]);
   }
   __syncthreads();
   if (tid == 0) {
@@ -383,7 +460,7 @@ __global__ __launch_bounds__(1024) void select_decide_kernel(SelectArgs p) {
   constexpr int NWMAX = MAX_C / 64;
   __shared__ double sxm[NP], sxh[NP], svals[NP];
   __shared__ int sorder[NP], shigh[NP], s_tier[NP], s_rowof[NP], s_rowpair[NP];
-  __shared__ int s_rowptr[NP + 1], s_refbase[NP + 1];
+  __shared__ int s_rowptr[NP + 1], s_refbase[NP + 1], s_nref[NP][3];
   __shared__ unsigned long long s_kept[NWMAX], s_refd[NWMAX];
   __shared__ int s_run[NWMAX], s_rrun[NWMAX], s_next[NWMAX], s_last[NWMAX];
   const int pp = blockIdx.x, b = blockIdx.y;
@@ -394,77 +471,61 @@ __global__ __launch_bounds__(1024) void select_decide_kernel(SelectArgs p) {
   tier_counts(C, p.keep_bp, p.rate_bp, kk);
   const PairRec* recs = reinterpret_cast<const PairRec*>(p.tierinfo) + (size_t)b * NP;
   // waves 1-15 stage this pair's keep ranks while wave 0 decides the tiers
-  // (the workgroup barriers below order wave 0's steps; the other waves
-  // pass them)
+  // (its steps are ordered by wave-level syncs; one workgroup barrier
+  // follows)
   if (wv != 0) {
     const int32_t* src = (p.rank_key != nullptr ? p.rank_alt : p.rank) + ((size_t)b * NP + pp) * CS;
     for (int c = tid - 64; c < C; c += 1024 - 64) s_keep[c] = src[c];
-  }
-  const bool w0 = wv == 0;
-  if (w0) {
-    double glm = 0.0, gmh = 0.0;
-    if (lane < NP) { glm = recs[lane].glm; gmh = recs[lane].gmh; }
-    const double mum = wave_sum(glm) / NP;
-    const double muh = wave_sum(gmh) / NP;
+  } else {
+    // wave 0: the tier decision (Eqs. (13)-(14)); the records are read once
+    {
+      double glm = 0.0, gmh = 0.0;
+      if (lane < NP) {
+        const PairRec r = recs[lane];
+        glm = r.glm;
+        gmh = r.gmh;
+        s_nref[lane][0] = r.nref[0]; s_nref[lane][1] = r.nref[1]; s_nref[lane][2] = r.nref[2];
+      }
+      const double mum = wave_sum(glm) / NP;
+      const double muh = wave_sum(gmh) / NP;
+      if (lane < NP) {
+        sxm[lane] = ord_key(mum > 0.0 ? glm / mum : 0.0);
+        sxh[lane] = ord_key(muh > 0.0 ? gmh / muh : 0.0);
+      }
+    }
+    wave_sync();
+    // High count: pairs sorted by x_H descending (ties: lower pair first)
     if (lane < NP) {
-      sxm[lane] = ord_key(mum > 0.0 ? glm / mum : 0.0);
-      sxh[lane] = ord_key(muh > 0.0 ? gmh / muh : 0.0);
+      int pos = 0;
+      for (int q = 0; q < NP; ++q)
+        pos += (sxh[q] > sxh[lane] || (sxh[q] == sxh[lane] && q < lane)) ? 1 : 0;
+      sorder[pos] = lane;
     }
-  }
-  __syncthreads();
-  // High count: pairs sorted by x_H descending (ties: lower pair first)
-  if (w0 && lane < NP) {
-    int pos = 0;
-    for (int q = 0; q < NP; ++q)
-      pos += (sxh[q] > sxh[lane] || (sxh[q] == sxh[lane] && q < lane)) ? 1 : 0;
-    sorder[pos] = lane;
-  }
-  __syncthreads();
-  if (w0 && lane < NP) svals[lane] = sxh[sorder[lane]];
-  __syncthreads();
-  int nH = 1;
-  if (w0) {
-    if (p.fixed_tiers) {
-      nH = 3;                 // the fixed 9 Low / 4 Medium / 3 High split
-    } else {
-      double best = 0.0;
-      for (int k = 1; k <= 4; ++k) {
-        const double v = split_score(svals, NP, k, lane);
-        if (k == 1 || v > best) { best = v; nH = k; }
-      }
-    }
+    wave_sync();
+    if (lane < NP) svals[lane] = sxh[sorder[lane]];
+    wave_sync();
+    int nH = 3;               // the fixed 9 Low / 4 Medium / 3 High split
+    if (!p.fixed_tiers) nH = best_split(svals, NP, 1, 4, lane);
     if (lane < NP) shigh[lane] = 0;
-  }
-  __syncthreads();
-  if (w0 && lane < nH) shigh[sorder[lane]] = 1;
-  __syncthreads();
-  // Medium count among the remaining pairs, sorted by x_M descending
-  const int nrest = NP - nH;
-  if (w0 && lane < NP && !shigh[lane]) {
-    int pos = 0;
-    for (int q = 0; q < NP; ++q)
-      if (!shigh[q]) pos += (sxm[q] > sxm[lane] || (sxm[q] == sxm[lane] && q < lane)) ? 1 : 0;
-    sorder[pos] = lane;
-  }
-  __syncthreads();
-  if (w0 && lane < nrest) svals[lane] = sxm[sorder[lane]];
-  __syncthreads();
-  if (w0) {
-    int cand[3], ncand;
-    if (nH == 1) { cand[0] = 11; cand[1] = 12; cand[2] = 13; ncand = 3; }
-    else if (nH == 2) { cand[0] = 7; cand[1] = 8; cand[2] = 9; ncand = 3; }
-    else if (nH == 3) { cand[0] = 3; cand[1] = 4; cand[2] = 5; ncand = 3; }
-    else { cand[0] = 0; ncand = 1; }
-    int nM = cand[0];
-    if (p.fixed_tiers) {
-      nM = 4;
-    } else {
-      double best = 0.0;
-      for (int i = 0; i < ncand; ++i) {
-        const double v = split_score(svals, nrest, cand[i], lane);
-        if (i == 0 || v > best) { best = v; nM = cand[i]; }
-      }
+    wave_sync();
+    if (lane < nH) shigh[sorder[lane]] = 1;
+    wave_sync();
+    // Medium count among the remaining pairs, sorted by x_M descending
+    const int nrest = NP - nH;
+    if (lane < NP && !shigh[lane]) {
+      int pos = 0;
+      for (int q = 0; q < NP; ++q)
+        if (!shigh[q]) pos += (sxm[q] > sxm[lane] || (sxm[q] == sxm[lane] && q < lane)) ? 1 : 0;
+      sorder[pos] = lane;
     }
+    wave_sync();
+    if (lane < nrest) svals[lane] = sxm[sorder[lane]];
+    wave_sync();
+    // Medium candidates for the High count (Sec. 2.4.3 table): 11-13, 7-9,
+    // 3-5, or 0 with four High pairs
+    const int m0 = nH == 1 ? 11 : nH == 2 ? 7 : nH == 3 ? 3 : 0;
+    const int nm = nH <= 3 ? 3 : 1;
+    const int nM = p.fixed_tiers ? 4 : best_split(svals, nrest, m0, nm, lane);
     if (lane < NP) {
       int t = 2;
       if (!shigh[lane]) {
@@ -474,49 +535,56 @@ __global__ __launch_bounds__(1024) void select_decide_kernel(SelectArgs p) {
       }
       s_tier[lane] = t;
     }
-  }
-  __syncthreads();
-  // rows: High first, ascending pair within a tier (head-pair order with
-  // pair_order); each row holds the k of its tier events
-  if (w0 && lane < NP) {
-    int row = lane;
-    if (!p.pair_order) {
-      const int t = s_tier[lane];
-      row = 0;
-      for (int q = 0; q < NP; ++q)
-        row += (s_tier[q] > t || (s_tier[q] == t && q < lane)) ? 1 : 0;
-    }
-    s_rowof[lane] = row;
-    s_rowpair[row] = lane;
-  }
-  __syncthreads();
-  if (w0 && lane <= NP) {
-    int e = 0, f = 0;
-    for (int r = 0; r < lane; ++r) {
-      const int q = s_rowpair[r], tq = s_tier[q];
-      e += kk[tq];
-      f += recs[q].nref[tq];
-    }
-    s_rowptr[lane] = e;
-    s_refbase[lane] = f;
-  }
-  __syncthreads();
-  if (w0 && pp == 0) {
+    wave_sync();
+    // rows: High first, ascending pair within a tier (head-pair order with
+    // pair_order); each row holds the k of its tier events
     if (lane < NP) {
-      p.tier[b * NP + lane] = (uint8_t)s_tier[lane];
-      p.row_pair[b * NP + lane] = s_rowpair[lane];
+      int row = lane;
+      if (!p.pair_order) {
+        const int t = s_tier[lane];
+        row = 0;
+        for (int q = 0; q < NP; ++q)
+          row += (s_tier[q] > t || (s_tier[q] == t && q < lane)) ? 1 : 0;
+      }
+      s_rowof[lane] = row;
+      s_rowpair[row] = lane;
     }
-    if (lane <= NP) p.row_ptr[b * (NP + 1) + lane] = s_rowptr[lane];
-    if (lane == 0 && p.stats != nullptr) {
-      int32_t* st = static_cast<int32_t*>(p.stats) + (size_t)b * STATS_INTS;
-      if (p.nf_clear) st[ST_NF_IN] = st[ST_NF_OUT] = 0;
-      int nt[3] = {0, 0, 0};
-      for (int q = 0; q < NP; ++q) nt[s_tier[q]]++;
-      st[0] = s_rowptr[NP];
-      st[1] = p.Emax;
-      st[2] = nt[0]; st[3] = nt[1]; st[4] = nt[2];
-      st[5] = kk[0]; st[6] = kk[1]; st[7] = kk[2];
-      st[8] = s_refbase[NP];
+    wave_sync();
+    {
+      // row offsets: exclusive scans of the events and referenced events per row
+      int e = 0, f = 0;
+      if (lane < NP) {
+        const int q = s_rowpair[lane], tq = s_tier[q];
+        e = kk[tq];
+        f = s_nref[q][tq];
+      }
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int ue = __shfl_up(e, d, 64), uf = __shfl_up(f, d, 64);
+        if (lane >= d) { e += ue; f += uf; }
+      }
+      // lane r now holds the inclusive sums of rows 0 .. r
+      if (lane < NP) { s_rowptr[lane + 1] = e; s_refbase[lane + 1] = f; }
+      if (lane == 0) { s_rowptr[0] = 0; s_refbase[0] = 0; }
+    }
+    wave_sync();
+    if (pp == 0) {
+      if (lane < NP) {
+        p.tier[b * NP + lane] = (uint8_t)s_tier[lane];
+        p.row_pair[b * NP + lane] = s_rowpair[lane];
+      }
+      if (lane <= NP) p.row_ptr[b * (NP + 1) + lane] = s_rowptr[lane];
+      if (lane == 0 && p.stats != nullptr) {
+        int32_t* st = static_cast<int32_t*>(p.stats) + (size_t)b * STATS_INTS;
+        if (p.nf_clear) st[ST_NF_IN] = st[ST_NF_OUT] = 0;
+        int nt[3] = {0, 0, 0};
+        for (int q = 0; q < NP; ++q) nt[s_tier[q]]++;
+        st[0] = s_rowptr[NP];
+        st[1] = p.Emax;
+        st[2] = nt[0]; st[3] = nt[1]; st[4] = nt[2];
+        st[5] = kk[0]; st[6] = kk[1]; st[7] = kk[2];
+        st[8] = s_refbase[NP];
+      }
     }
   }
   __syncthreads();
