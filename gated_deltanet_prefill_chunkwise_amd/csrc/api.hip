@@ -31,7 +31,7 @@ struct Plan {
 };
 
 enum Buf { B_G, B_GAMMA, B_P, B_U, B_W, B_CB, B_KT, B_SNAP, B_S0T, B_SCORE, B_ETA, B_RANK,
-           B_TINFO, B_MASK, B_TIER, B_ROWPAIR, B_ROWPTR, B_COL, B_PRED, B_GSLOT, B_ESLOT,
+           B_PREC, B_MASK, B_TIER, B_ROWPAIR, B_ROWPTR, B_COL, B_PRED, B_GSLOT, B_ESLOT,
            B_WPK, B_STATS, B_FAC, B_REC, B_CHUNKS, B_SPART, B_RANK2, B_ENTRY, B_COLALL,
            B_RPALL, B_ETAP, B_COUNT };
 
@@ -173,7 +173,7 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
     sz[B_ETA] = B * Nv * 4;
     sz[B_ETAP] = B * Nv * GATE_SPLIT * 4;
     sz[B_RANK] = B * NP * C * 4;
-    sz[B_TINFO] = B * NP * PAIRREC_BYTES;
+    sz[B_PREC] = B * NP * PAIRREC_BYTES;
     sz[B_MASK] = B * NP * C;
     sz[B_TIER] = B * NP;
     sz[B_ROWPAIR] = B * NP * 4;
@@ -269,9 +269,9 @@ int debug_copies(const Plan& pl, void* ws, sgdn_debug* dbg, hipStream_t st, int 
   return SGDN_OK;
 }
 
-// Selector scratch: rank tables (q-ranks; caller-key ranks), tier counts,
+// Selector scratch: rank tables (q-ranks; caller-key ranks), pair records,
 // snapshot slot of every event.
-struct SelectScratch { int32_t *rank, *rank_alt, *tierinfo, *event_slot; };
+struct SelectScratch { int32_t *rank, *rank_alt; void* pair_rec; int32_t* event_slot; };
 
 int check_select(const sgdn_problem* prob, const float* score, const float* gamma, const float* eta,
                  const sgdn_sparse_params* params, const uint8_t* mask, const uint8_t* tier,
@@ -299,7 +299,7 @@ int launch_select_call(const Plan& pl, const float* score, const float* gamma, c
   sa.fixed_tiers = params->fixed_tiers; sa.unit_visibility = params->unit_visibility;
   sa.rank_key = params->rank_key;
   sa.rank_alt = sc.rank_alt;
-  sa.rank = sc.rank; sa.tierinfo = sc.tierinfo;
+  sa.rank = sc.rank; sa.pair_rec = sc.pair_rec;
   sa.mask = mask; sa.tier = tier; sa.row_pair = row_pair; sa.row_ptr = row_ptr; sa.col = col;
   sa.pred = pred; sa.group_slot = group_slot; sa.event_slot = sc.event_slot;
   sa.Emax = NP_SPARSE * pl.kH; sa.G = pl.G;
@@ -484,7 +484,7 @@ int sgdn_select(const sgdn_problem* prob, const float* score, const float* gamma
   make_plan(prob, 1, params, pl);
   if (ws_bytes < pl.total) return SGDN_EWORKSPACE;
   SelectScratch sc{at<int32_t>(ws, pl, B_RANK), params->rank_key ? at<int32_t>(ws, pl, B_RANK2) : nullptr,
-                   at<int32_t>(ws, pl, B_TINFO), at<int32_t>(ws, pl, B_ESLOT)};
+                   at<void>(ws, pl, B_PREC), at<int32_t>(ws, pl, B_ESLOT)};
   return launch_select_call(pl, score, gamma, eta, params, mask, tier, row_pair, row_ptr, col, pred,
                             group_slot, stats, sc, static_cast<hipStream_t>(stream));
 }
@@ -505,7 +505,7 @@ int sgdn_select_noalloc(const sgdn_problem* prob, const float* score, const floa
   if ((st = noalloc_scratch(&base)) != SGDN_OK) return st;
   SelectScratch sc{reinterpret_cast<int32_t*>(base + off[0]),
                    params->rank_key ? reinterpret_cast<int32_t*>(base + off[1]) : nullptr,
-                   reinterpret_cast<int32_t*>(base + off[2]), reinterpret_cast<int32_t*>(base + off[3])};
+                   static_cast<void*>(base + off[2]), reinterpret_cast<int32_t*>(base + off[3])};
   return launch_select_call(pl, score, gamma, eta, params, mask, tier, row_pair, row_ptr, col, pred,
                             group_slot, stats, sc, static_cast<hipStream_t>(stream));
 }
@@ -559,7 +559,7 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   sa.pair_order = (pl.ablate & SGDN_ABLATE_TIER_SCHEDULE) != 0;
   sa.rank_key = params->rank_key;
   sa.rank_alt = params->rank_key ? at<int32_t>(ws, pl, B_RANK2) : nullptr;
-  sa.rank = at<int32_t>(ws, pl, B_RANK); sa.tierinfo = at<int32_t>(ws, pl, B_TINFO);
+  sa.rank = at<int32_t>(ws, pl, B_RANK); sa.pair_rec = at<void>(ws, pl, B_PREC);
   sa.mask = at<uint8_t>(ws, pl, B_MASK); sa.tier = at<uint8_t>(ws, pl, B_TIER);
   sa.row_pair = at<int32_t>(ws, pl, B_ROWPAIR); sa.row_ptr = at<int32_t>(ws, pl, B_ROWPTR);
   sa.col = at<int32_t>(ws, pl, B_COL); sa.pred = at<int32_t>(ws, pl, B_PRED);

@@ -186,10 +186,10 @@ struct SelectArgs {
   const float* rank_key;
   int32_t* rank_alt;    // [B][16][C]   workspace: ranks by rank_key
   int32_t* rank;        // [B][16][C]   workspace
-  int32_t* tierinfo;    // [B][16] pair records of PAIRREC_BYTES (gains, referenced events)
+  void* pair_rec;       // [B][16] pair records of PAIRREC_BYTES (gains, referenced events)
   uint8_t* mask; uint8_t* tier;
   int32_t* row_pair; int32_t* row_ptr; int32_t* col; int32_t* pred;
-  int32_t* group_slot; int32_t* event_slot; int32_t* col_row;  // col_row: [B][Emax] row of each event
+  int32_t* group_slot; int32_t* event_slot;
   int Emax, G;
   void* stats;          // sgdn_stats* or null
   int nf_clear;         // also zero the nonfinite fields (sgdn_select)

@@ -437,7 +437,7 @@ __global__ __launch_bounds__(1024) void select_pair_kernel(SelectArgs p) {
   }
   __syncthreads();
   if (tid == 0) {
-    PairRec* rec = reinterpret_cast<PairRec*>(p.tierinfo) + (size_t)b * NP + pp;
+    PairRec* rec = reinterpret_cast<PairRec*>(p.pair_rec) + (size_t)b * NP + pp;
     PairRec q;
     q.glm = (s_L[0] * s_G[0]) * s_sum[0] + (s_L[1] * s_G[1]) * s_sum[1];
     q.gmh = (s_L[0] * s_G[0]) * s_sum[2] + (s_L[1] * s_G[1]) * s_sum[3];
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(1024) void select_decide_kernel(SelectArgs p) {
   const int NW = (C + 63) / 64, NWS = (CS + 63) / 64;
   int kk[3];
   tier_counts(C, p.keep_bp, p.rate_bp, kk);
-  const PairRec* recs = reinterpret_cast<const PairRec*>(p.tierinfo) + (size_t)b * NP;
+  const PairRec* recs = reinterpret_cast<const PairRec*>(p.pair_rec) + (size_t)b * NP;
   // waves 1-15 stage this pair's keep ranks while wave 0 decides the tiers
   // (its steps are ordered by wave-level syncs; one workgroup barrier
   // follows)
@@ -696,13 +696,13 @@ __global__ __launch_bounds__(1024) void select_decide_kernel(SelectArgs p) {
 // Low row, in pair order), kept chunks ascending, predecessor of every output
 // group and compact-snapshot slots numbered over the referenced events in CSR
 // order.  One block of 16 waves per sequence; wave w works on pair w or row w.
-__global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
+__global__ __launch_bounds__(1024) void mask_layout_kernel(SelectArgs p) {
   // Wave w handles head pair w.  Each pair's kept chunks are held as 64-bit
   // words (bit l of word i: chunk 64 i + l), and so are its referenced events,
   // so the CSR columns, the snapshot slots and the group predecessors follow
   // from bit counts without reading back what this kernel writes.
   constexpr int NWMAX = 128;   // 64-chunk words per pair (C <= 8192)
-  __shared__ int s_tier[NP], s_cnt[NP], s_rowpair[NP], s_rowof[NP], s_rowptr[NP + 1];
+  __shared__ int s_cnt[NP], s_rowpair[NP], s_rowof[NP], s_rowptr[NP + 1];
   __shared__ int s_ref[NP], s_refbase[NP + 1];
   __shared__ unsigned long long s_kept[NP][NWMAX], s_refd[NP][NWMAX];
   const int b = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -713,18 +713,11 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
   const int C = valid_chunks(p, b), G = (C + 1) / 2;
   int kk[3];
   tier_counts(C, p.keep_bp, p.rate_bp, kk);
-  const int kL = kk[0], kM = kk[1], kH = kk[2];
   const unsigned long long below = (1ull << lane) - 1ull;
   uint8_t* mask = p.mask + (size_t)b * NP * CS;
-  const bool ovr = p.mask_in != nullptr;
-  const int32_t* rank_src = p.rank_key != nullptr ? p.rank_alt : p.rank;
-  if (tid < NP) s_tier[tid] = ovr ? 0 : p.tier[b * NP + tid];
-  __syncthreads();
   const int pp = w;
   {
-    // mask of pair w (the rank loads of a batch of words are issued together)
-    const int t = s_tier[pp];
-    const int k = t == 2 ? kH : (t == 1 ? kM : kL);
+    // mask of pair w (the loads of a batch of words are issued together)
     int cnt = 0;
     for (int i0 = 0; i0 < NW; i0 += 16) {
       int val[16];
@@ -733,16 +726,14 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
         const int c = 64 * (i0 + u) + lane;
         const size_t idx = (size_t)b * NP * CS + (size_t)pp * CS + c;
         val[u] = 0;
-        if (i0 + u < NW && c < C) val[u] = ovr ? (int)p.mask_in[idx] : rank_src[idx];
+        if (i0 + u < NW && c < C) val[u] = p.mask_in[idx];
       }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int i = i0 + u;
         if (i < NW) {
           const int c = 64 * i + lane;
-          int z = 0;
-          if (c < C)
-            z = ovr ? (val[u] ? 1 : 0) : ((c == 0 || c == C - 1 || (val[u] >= 0 && val[u] < k - 2)) ? 1 : 0);
+          const int z = (c < C && val[u]) ? 1 : 0;
           if (c < CS) mask[(size_t)pp * CS + c] = (uint8_t)z;
           const unsigned long long bal = __ballot(z);
           if (lane == 0) s_kept[pp][i] = bal;
@@ -755,17 +746,13 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
   }
   __syncthreads();
   if (tid == 0) {
-    // CSR rows by tier, High first (in head-pair order with pair_order)
-    int r = 0;
+    // CSR rows in head-pair order
     s_rowptr[0] = 0;
-    for (int t = 2; t >= 0; --t)
-      for (int q = 0; q < NP; ++q)
-        if (p.pair_order ? t == 2 : s_tier[q] == t) {
-          s_rowpair[r] = q;
-          s_rowof[q] = r;
-          s_rowptr[r + 1] = s_rowptr[r] + s_cnt[q];
-          ++r;
-        }
+    for (int q = 0; q < NP; ++q) {
+      s_rowpair[q] = q;
+      s_rowof[q] = q;
+      s_rowptr[q + 1] = s_rowptr[q] + s_cnt[q];
+    }
   }
   __syncthreads();
   if (tid < NP) p.row_pair[b * NP + tid] = s_rowpair[tid];
@@ -842,12 +829,10 @@ __global__ __launch_bounds__(1024) void layout_kernel(SelectArgs p) {
   if (tid == 0 && p.stats != nullptr) {
     int32_t* st = static_cast<int32_t*>(p.stats) + (size_t)b * STATS_INTS;
     if (p.nf_clear) st[ST_NF_IN] = st[ST_NF_OUT] = 0;
-    int nt[3] = {0, 0, 0};
-    for (int q = 0; q < NP; ++q) nt[s_tier[q]]++;
     st[0] = s_rowptr[NP];
     st[1] = p.Emax;
-    st[2] = nt[0]; st[3] = nt[1]; st[4] = nt[2];
-    st[5] = kL; st[6] = kM; st[7] = kH;
+    st[2] = NP; st[3] = 0; st[4] = 0;   // every pair a Low row
+    st[5] = kk[0]; st[6] = kk[1]; st[7] = kk[2];
     st[8] = s_refbase[NP];
   }
 }
@@ -876,7 +861,7 @@ hipError_t launch_fp64_selftest(const double* x, const double* y, double* q, dou
 
 hipError_t launch_select_full(const SelectArgs& a, hipStream_t s) {
   if (a.mask_in != nullptr) {
-    hipLaunchKernelGGL(layout_kernel, dim3(a.B), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(mask_layout_kernel, dim3(a.B), dim3(1024), 0, s, a);
     return hipGetLastError();
   }
   const int nblk = (a.C + RANK_CHUNKS - 1) / RANK_CHUNKS;
