@@ -172,7 +172,8 @@ template <typename I> __device__ __forceinline__ int u_unit(int P) {
 // two halves (in the same order) and form Cb Y, U' and X identically; each
 // then updates its own state rows with K^T X.  The loaders keep two events
 // complete at every barrier (the current and the next).
-template <typename E, bool SPARSE, bool CBP>
+// BA (Cb operand only): the block-adjacent solve, whose Cb has no block (3,0).
+template <typename E, bool SPARSE, bool CBP, bool BA>
 __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanArgs p) {
   using I = inter_t<E>;
   static_assert(!CBP || sizeof(I) == 2, "Cb operand: fp16 intermediates only");
@@ -430,10 +431,12 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
     const int kl = kswz(lane);
 
     // Operands of one event, read from its slot one step ahead: the event
-    // after the current one is complete at every barrier, so its record, Cb
-    // blocks, U slice, factors and this wave's K^T blocks are requested at the
-    // end of the current step and their latency overlaps the barrier.  (For
-    // the row's last event the read slot is stale and the values unused.)
+    // after the current one is complete at every barrier, so each part of its
+    // operands (Cb blocks; record, U slice and factors; this wave's K^T
+    // blocks) is requested as soon as the current step has consumed the same
+    // part, and their latency overlaps the step's remaining products instead
+    // of the wait for LDS completion at the barrier.  (For the row's last
+    // event the read slot is stale and the values unused.)
     struct Ops {
       int4 rc;
       frag_t<I> cb[CB_BLOCKS];
@@ -441,24 +444,26 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
       f32x4 fc[4];
       frag_t<I> kt[4][2];
     };
-    auto load_ops = [&](int slot) __attribute__((always_inline)) {
-      Ops o;
-      const char* sl = ring + slot * R::BYTES;
-      const I* Cs = reinterpret_cast<const I*>(sl + R::W_OFF);
-      const I* Ks = reinterpret_cast<const I*>(sl + R::K_OFF);
-      o.rc = *reinterpret_cast<const int4*>(sl + R::R_OFF);
+    auto load_cb = [&](int slot, Ops& o) __attribute__((always_inline)) {
+      const I* Cs = reinterpret_cast<const I*>(ring + slot * R::BYTES + R::W_OFF);
 #pragma unroll
       for (int b = 0; b < CB_BLOCKS; ++b) o.cb[b] = ld8(Cs + b * 512 + 8 * lane);
+    };
+    auto load_uf = [&](int slot, Ops& o) __attribute__((always_inline)) {
+      const char* sl = ring + slot * R::BYTES;
+      o.rc = *reinterpret_cast<const int4*>(sl + R::R_OFF);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         o.u[i] = *reinterpret_cast<const half_t<I>*>(sl + R::U_OFF + u_off<I>(i, n16, g4));
         o.fc[i] = *reinterpret_cast<const f32x4*>(sl + R::F_OFF + (16 * i + 4 * g4) * 4);
       }
+    };
+    auto load_kt = [&](int slot, Ops& o) __attribute__((always_inline)) {
+      const I* Ks = reinterpret_cast<const I*>(ring + slot * R::BYTES + R::K_OFF);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) o.kt[t][ks] = ld8(Ks + kblk(4 * cw + t, ks) + 8 * kl);
-      return o;
     };
 
     f32x4 y[4], ym[4];
@@ -477,7 +482,9 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
 #pragma unroll
         for (int q = 0; q < 4; ++q) y[i] = mma(kfrag(Ks, q, i), Sf[q], y[i]);
       }
-      op = load_ops(0);
+      load_cb(0, op);
+      load_uf(0, op);
+      load_kt(0, op);
     }
     for (int j = i0; j < i1; ++j) {
       if (j > i0) {
@@ -518,14 +525,15 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
       const f32x4 a0 = mma(cbf(0, 0), Y0, zero4());
       const f32x4 a1 = mma(cbf(1, 0), Y0, zero4());
       const f32x4 a2 = mma(cbf(2, 1), Y1, mma(cbf(2, 0), Y0, zero4()));
-      const f32x4 a3b = mma(cbf(3, 1), Y1, zero4());
-      // (the block-adjacent solve stores no block (3,0): the product of
-      // whatever its slot holds is formed and dropped)
-      const f32x4 a3x = mma(cbf(3, 0), Y0, a3b);
-      const f32x4 a3 = p.blockadj ? a3b : a3x;
+      // (the block-adjacent solve stores no block (3,0))
+      f32x4 a3 = mma(cbf(3, 1), Y1, zero4());
+      if constexpr (!BA) a3 = mma(cbf(3, 0), Y0, a3);
+      Ops nx;
+      load_cb(s1, nx);
 
       // ---- U' = U - F_in W S (Eq. (1)); X = U' 2^(gamma - g); both waves
-      //      stage the same U' values
+      //      form the same U' values, compute wave cw stages token tiles
+      //      2 cw and 2 cw + 1 of it
       auto ux = [&](int i, const f32x4& ai) __attribute__((always_inline)) {
         f32x4 up, x;
 #pragma unroll
@@ -533,30 +541,34 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
           up[jj] = to_f(op.u[i][jj]) - fin * ai[jj];
           x[jj] = up[jj] * op.fc[i][jj];
         }
-        st4<I>(reinterpret_cast<I*>(st + u_off<I>(i, n16, g4)), up);
+        if ((i >> 1) == cw) st4<I>(reinterpret_cast<I*>(st + u_off<I>(i, n16, g4)), up);
         return x;
       };
       const frag_t<I> X0 = pack44<I>(ux(0, a0), ux(1, a1));
       const frag_t<I> X1 = pack44<I>(ux(2, a2), ux(3, a3));
+      load_uf(s1, nx);
       // ---- own rows: S <- 2^gamma F_in S + K^T X (Eq. (2))
 #pragma unroll
       for (int t = 0; t < 4; ++t) So[t] = mma(op.kt[t][0], X0, So[t] * decf);
 #pragma unroll
       for (int t = 0; t < 4; ++t) So[t] = mma(op.kt[t][1], X1, So[t]);
+      load_kt(s1, nx);
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq) Sfo[qq] = pack44<I>(So[2 * qq], So[2 * qq + 1]);
 
       // ---- compact snapshot of S_{c+1}, own key rows (key steps 2 cw + qq);
-      //      staged for every event, copied only where referenced
+      //      staged only where a later output group references it
+      if (snapi >= 0) {
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq)
+        for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
-        for (int hi = 0; hi < 2; ++hi) {
-          const int c8 = 4 * (2 * cw + qq) + 2 * hi + (g4 >> 1);
-          const half_t<I> v = hi ? __builtin_shufflevector(Sfo[qq], Sfo[qq], 4, 5, 6, 7)
-                                 : __builtin_shufflevector(Sfo[qq], Sfo[qq], 0, 1, 2, 3);
-          *reinterpret_cast<half_t<I>*>(st + R::ST_SN + (c8 * 16 + n16) * 16 + 8 * (g4 & 1)) = v;
-        }
+          for (int hi = 0; hi < 2; ++hi) {
+            const int c8 = 4 * (2 * cw + qq) + 2 * hi + (g4 >> 1);
+            const half_t<I> v = hi ? __builtin_shufflevector(Sfo[qq], Sfo[qq], 4, 5, 6, 7)
+                                   : __builtin_shufflevector(Sfo[qq], Sfo[qq], 0, 1, 2, 3);
+            *reinterpret_cast<half_t<I>*>(st + R::ST_SN + (c8 * 16 + n16) * 16 + 8 * (g4 & 1)) = v;
+          }
+      }
       if (lane == 0) *reinterpret_cast<int2*>(st + R::ST_HDR) = make_int2(c, snapi);
 
       // ---- own half of the next event's Y
@@ -566,7 +578,7 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
         ym[i] = mma(kn[1][i], Sfo[1], mma(kn[0][i], Sfo[0], zero4()));
         yw[i * 64 + lane] = ym[i];
       }
-      op = load_ops(s1);
+      op = nx;
       s = s1;
     }
     lds_barrier();   // the last staging entry is complete
@@ -719,20 +731,26 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
   }
 }
 
-template <typename E, bool SPARSE, bool CBP>
+template <typename E, bool SPARSE, bool CBP, bool BA = false>
 hipError_t launch_one(const HScanArgs& a, hipStream_t s) {
   const int nblk = 128 * ((a.B * a.nrows + 7) / 8);
-  hipLaunchKernelGGL((hscan_kernel<E, SPARSE, CBP>), dim3(nblk), dim3(64 * (CBP ? 5 : NWAVE)), 0, s, a);
+  hipLaunchKernelGGL((hscan_kernel<E, SPARSE, CBP, BA>), dim3(nblk), dim3(64 * (CBP ? 5 : NWAVE)), 0, s, a);
   return hipGetLastError();
+}
+
+template <bool SPARSE>
+hipError_t launch_cb(const HScanArgs& a, hipStream_t s) {
+  return a.blockadj ? launch_one<sgdn::bf16, SPARSE, true, true>(a, s)
+                    : launch_one<sgdn::bf16, SPARSE, true, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_hscan(const HScanArgs& a, int bf16, hipStream_t s) {
   if (bf16) {
-    if (!a.sparse) return launch_one<sgdn::bf16, false, true>(a, s);
+    if (!a.sparse) return launch_cb<false>(a, s);
     // W of every chunk (the deferred-W and CSR-off controls) or W S from Cb
-    return a.w_by_chunk ? launch_one<sgdn::bf16, true, false>(a, s) : launch_one<sgdn::bf16, true, true>(a, s);
+    return a.w_by_chunk ? launch_one<sgdn::bf16, true, false>(a, s) : launch_cb<true>(a, s);
   }
   return a.sparse ? launch_one<float, true, false>(a, s) : launch_one<float, false, false>(a, s);
 }
