@@ -42,6 +42,9 @@ path_roofline = the whole layer against HBM with the algorithmic bytes of
 the I/O streams (bf16 Q, K, V; fp16 O; fp32 a; bf16 beta) plus the compact
 snapshots written and read; mfma = the algorithmic flops of the method over
 the same time against the dense bf16 matrix-core peak.
+snapshot_bytes = the group-entry snapshot memory of one layer: allocated (a
+slot for every group boundary of every head) and used (the compact
+snapshots the H scan wrote; all of them in the dense path).
 cpu_baseline = the fp64 numpy oracle as it stands, one worker process per
 host core (up to 16), each on a different layer's first tokens, in both
 modes, in the same unit.
@@ -895,6 +898,15 @@ def main():
                      "stage_ms_per_launch": {k: round(v, 4) for k, v in rr["stage_ms_per_launch"].items()},
                      "roofline": roofline(mode), "path_roofline": pr, "mfma_roofline": mr,
                      "binding_roofline": "hbm" if pr["roofline_ms_per_layer"] >= mr["roofline_ms_per_layer"] else "mfma"}
+    # group-entry snapshot memory per layer: the workspace holds a slot for
+    # every group boundary (fp16, 128 x 128 per head); the compact snapshots
+    # the sparse H scan writes use n_snapshots of the pair slots
+    G = (C + 1) // 2
+    snap_head = 128 * 128 * 2
+    for mode in res:
+        alloc = B * NV * max(G - 1, 1) * snap_head
+        used = alloc if mode == "dense" else int(round(sigma * alloc))
+        out[mode]["snapshot_bytes"] = {"allocated": alloc, "used": used}
     if "sparse" in res:
         out["sparse"]["measured_keep"] = round(keep, 5)
         out["sparse"]["snapshot_fraction"] = round(sigma, 5)
