@@ -649,8 +649,10 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
     // CSR rows 0-3 hold every High-tier pair (at most 4), whose chains are
     // the longest and bound the H scan.  The H scan and O of rows 4-15 run
     // on the caller's second stream beside those of rows 0-3, so O of the
-    // shorter chains overlaps the long ones; rows 4-15 start at XCD 4, rows
-    // 0-3 at XCD 0, which keeps 32 H-scan workgroups on every XCD.
+    // shorter chains overlaps the long ones.  Both H-scan launches spread
+    // each pair group over two XCDs (one head on each): rows 4-15 put 24
+    // workgroups and rows 0-3 put 8 on every XCD, whatever XCD each launch's
+    // round-robin dispatch starts at, so every chain finds a CU at once.
     // (Splitting deferred W and the event records the same way, or moving
     // the gate energy beside the intra kernel, measured no faster: the GPU
     // is busy in those phases.)
@@ -659,14 +661,20 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
     hipEvent_t join = static_cast<hipEvent_t>(params->aux_events[1]);
     SGDN_TRY(hipEventRecord(fork, s));
     SGDN_TRY(hipStreamWaitEvent(aux, fork, 0));
-    ha.row_lo = SPLIT_ROWS; ha.nrows = NP - SPLIT_ROWS; ha.xcd_shift = SPLIT_ROWS;
+    ha.row_lo = SPLIT_ROWS; ha.nrows = NP - SPLIT_ROWS; ha.xcd_shift = SPLIT_ROWS; ha.spread = pl.bf16;
     SGDN_TRY(launch_hscan(ha, pl.bf16, aux));
     SGDN_TRY(expand(SPLIT_ROWS, NP - SPLIT_ROWS, aux));
     oa.row_lo = SPLIT_ROWS; oa.nrows = NP - SPLIT_ROWS;
     SGDN_TRY(launch_ochunk(oa, pl.bf16, aux));
     SGDN_TRY(hipEventRecord(join, aux));
-    ha.row_lo = 0; ha.nrows = SPLIT_ROWS; ha.xcd_shift = 0;
+    // The High-tier chains of rows 0-3 keep CUs busy long after the other
+    // rows' H scan; spread over two XCDs per pair they leave three quarters
+    // of those XCDs' CUs free, so the O launch beside them (whose workgroups
+    // are dealt to the XCDs in equal shares) is not held up by an XCD that
+    // has only half of its CUs.
+    ha.row_lo = 0; ha.nrows = SPLIT_ROWS; ha.xcd_shift = 0; ha.spread = pl.bf16;
     SGDN_TRY(launch_hscan(ha, pl.bf16, s));
+    ha.spread = 0;
     SGDN_TRY(expand(0, SPLIT_ROWS, s));
     mark(dbg, SGDN_EV_HSCAN, s);
     oa.row_lo = 0; oa.nrows = SPLIT_ROWS;

@@ -78,11 +78,12 @@ template <typename I, bool PFON, bool CBP> struct Ring {
   static constexpr int NW = 16 * FB / 1024;          // pieces of K^T
   static constexpr int NUS = U_BYTES / 1024;         // pieces of the U slice
   static constexpr int NX4 = NWA + NW + NUS;
-  // L2 prefetch (fp16 operands): one scattered 4-byte request per
-  // event that touches this workgroup's share of the pair's W and K^T lines
-  // and its own U lines PF_AHEAD events before they are copied (its data lands
-  // in a scratch row).  The 16 workgroups of a pair request each line once
-  // between them, so the copies of the others hit in L2.
+  // L2 prefetch (fp16 operands): one scattered 4-byte request per event that
+  // touches this workgroup's share of the W (Cb) and K^T lines its XCD will
+  // copy, and its own U and factor lines, PF_AHEAD events before they are
+  // copied (its data lands in a scratch row).  The workgroups of a pair on
+  // one XCD request each line once between them, so the copies of the others
+  // hit in L2.
   static constexpr bool PF = PFON;
   static constexpr int PF_AHEAD = 6;
   static constexpr int NU = NX4 + 2 + (PF ? 1 : 0);
@@ -199,14 +200,18 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
   // head pair (2 heads x 8 slices) share K^T tiles and each head's 8 share W,
   // so they are placed on one XCD (workgroups are dealt to the 8 XCDs
   // round-robin): a window of 128 workgroups holds 8 pair groups, group k on
-  // XCD (k + xcd_shift) mod 8.  A launch covers rows row_lo .. row_lo +
-  // nrows - 1 of every sequence; its grid is padded to whole windows and the
-  // padding leaves at once.  Rows are dispatched in order, so the longest
-  // (High-tier) chains start first.
+  // XCD (k + xcd_shift) mod 8.  Spread: group k of a window (k < 4) has its
+  // head 0 on XCD k and its head 1 on XCD k + 4 (group k + 4 likewise), so a
+  // long chain takes a quarter of two XCDs rather than half of one, and the
+  // launches beside it find the XCDs more evenly free.  A launch covers rows
+  // row_lo .. row_lo + nrows - 1 of every sequence; its grid is padded to
+  // whole windows and the padding leaves at once.  Rows are dispatched in
+  // order, so the longest (High-tier) chains start first.
   const int id = blockIdx.x, nr = p.nrows;
-  const int pg = (id >> 7) * 8 + (((id & 7) - p.xcd_shift) & 7);
+  const int xc = id & 7, jx = (id >> 3) & 15;   // XCD (relative) and slot on it
+  const int pg = (id >> 7) * 8 + (p.spread ? (xc & 3) + 4 * (jx >> 3) : ((xc - p.xcd_shift) & 7));
   if (pg >= B * nr) return;
-  const int local = (id >> 3) & 15;
+  const int local = p.spread ? (xc >> 2) * 8 + (jx & 7) : jx;
   // Packed sequences (dense): sequence-major, so the pair groups dispatched
   // together belong to one sequence and their chains are equally long (they
   // start and finish together and keep sharing the pair's lines in L2).
@@ -288,9 +293,10 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
     const I* Cbase = static_cast<const I*>(p.Cb);
     // L2 prefetch of event e (clamped to the row): lanes 0-15 the 16 W lines
     // of this slice's share of the head's tile (CBP: lanes 0-5 the 6 of the
-    // head's 48 Cb lines, 6-15 repeat lane 0), 16-23 this workgroup's 8 of
-    // the pair's 128 K^T lines, 24-39 the 16 lines of its U slice, 40-41 the
-    // factors, the rest repeat lane 0
+    // head's 48 Cb lines, 6-15 repeat lane 0), 16-31 this workgroup's share of
+    // the pair's 128 K^T lines (8 of them with the pair on one XCD, 16 when
+    // spread; the rest repeat lane 16), 32-47 the 16 lines of its U slice,
+    // 48-49 the factors, the rest repeat lane 0
     auto prefetch = [&](int e) __attribute__((always_inline)) {
       e = e < i1 ? e : i1 - 1;
       const int c = col_at(e);
@@ -305,9 +311,11 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
       if (lane < 16) {
         if (!CBP) src = Wt + (slice * 16 + lane) * 128;
         else if (lane < 6) src = Ct + (slice * 6 + lane) * 128;
-      } else if (lane < 24) src = Kt + ((hh * 8 + slice) * 8 + lane - 16) * 128;
-      else if (lane < 40) src = Ut + (lane - 24) * 128;
-      else if (lane < 42) src = reinterpret_cast<const char*>(p.fac + hc * L) + (lane - 40) * 128;
+      } else if (lane < 32) {
+        const int kl = p.spread ? slice * 16 + lane - 16 : (hh * 8 + slice) * 8 + ((lane - 16) & 7);
+        src = Kt + kl * 128;
+      } else if (lane < 48) src = Ut + (lane - 32) * 128;
+      else if (lane < 50) src = reinterpret_cast<const char*>(p.fac + hc * L) + (lane - 48) * 128;
       dma4(src, pf_sink);
     };
     // copy units [u0, u1) of event j (chunk c) into slot s

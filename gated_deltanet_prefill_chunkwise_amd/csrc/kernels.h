@@ -76,8 +76,9 @@ struct HScanArgs {
   const int32_t* cu; int T;  // packed sequences: a dense chain stops at its valid chunks
   int w_by_chunk;           // sparse: W [B][Nv][C][8192] per chunk (deferred-W ablation)
   // rows row_lo .. row_lo + nrows - 1 of every sequence (CSR rows, sparse;
-  // head pairs, dense); pair groups start at XCD xcd_shift
-  int row_lo, nrows, xcd_shift;
+  // head pairs, dense); pair groups start at XCD xcd_shift, or (spread) each
+  // pair group's 16 workgroups are dealt over all 8 XCDs, 2 per XCD
+  int row_lo, nrows, xcd_shift, spread;
   // sparse metadata (per batch)
   const int32_t* row_pair;  // [B][NP]
   const int32_t* row_ptr;   // [B][NP+1]
