@@ -174,13 +174,24 @@ def flops_per_token(mode: str, keep: float) -> float:
     return mac * 2 * NV / 64
 
 
+def code_text(path: str) -> str:
+    """A HIP source with its comments removed and its whitespace collapsed:
+    what the compiler sees of it, so that editing a comment keeps the
+    counters taken on the code valid."""
+    import re
+    src = open(path, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def source_hash(stage: str) -> str:
     f = {"hscan": "hscan.hip", "o": "ochunk.hip", "intra": "intra.hip",
          "decode": "decode.hip"}.get(stage)
     if f is None:
         return ""
     p = os.path.join(ROOT, "gated_deltanet_prefill_chunkwise_amd", "csrc", f)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    return hashlib.sha256(code_text(p).encode()).hexdigest()[:16]
 
 
 def measured_traffic(stage: str, mode: str):

@@ -199,8 +199,9 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
   // Block -> (row, batch, head-in-pair, slice).  The 16 workgroups of one
   // head pair (2 heads x 8 slices) share K^T tiles and each head's 8 share W,
   // so they are placed on one XCD (workgroups are dealt to the 8 XCDs
-  // round-robin): a window of 128 workgroups holds 8 pair groups, group k on
-  // XCD (k + xcd_shift) mod 8.  Spread: group k of a window (k < 4) has its
+  // round-robin, starting at an XCD that varies between launches; XCD k
+  // below counts from it): a window of 128 workgroups holds 8 pair groups,
+  // group k on XCD (k + xcd_shift) mod 8.  Spread: group k of a window (k < 4) has its
   // head 0 on XCD k and its head 1 on XCD k + 4 (group k + 4 likewise), so a
   // long chain takes a quarter of two XCDs rather than half of one, and the
   // launches beside it find the XCDs more evenly free.  A launch covers rows
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
   // whole windows and the padding leaves at once.  Rows are dispatched in
   // order, so the longest (High-tier) chains start first.
   const int id = blockIdx.x, nr = p.nrows;
-  const int xc = id & 7, jx = (id >> 3) & 15;   // XCD (relative) and slot on it
+  const int xc = id & 7, jx = (id >> 3) & 15;   // XCD (counted as above) and slot on it
   const int pg = (id >> 7) * 8 + (p.spread ? (xc & 3) + 4 * (jx >> 3) : ((xc - p.xcd_shift) & 7));
   if (pg >= B * nr) return;
   const int local = p.spread ? (xc >> 2) * 8 + (jx & 7) : jx;
@@ -294,9 +295,9 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
     // L2 prefetch of event e (clamped to the row): lanes 0-15 the 16 W lines
     // of this slice's share of the head's tile (CBP: lanes 0-5 the 6 of the
     // head's 48 Cb lines, 6-15 repeat lane 0), 16-31 this workgroup's share of
-    // the pair's 128 K^T lines (8 of them with the pair on one XCD, 16 when
-    // spread; the rest repeat lane 16), 32-47 the 16 lines of its U slice,
-    // 48-49 the factors, the rest repeat lane 0
+    // the pair's 128 K^T lines (16 when spread; 8 with the pair on one XCD,
+    // lanes 24-31 repeating 16-23), 32-47 the 16 lines of its U slice, 48-49
+    // the factors, the rest repeat lane 0
     auto prefetch = [&](int e) __attribute__((always_inline)) {
       e = e < i1 ? e : i1 - 1;
       const int c = col_at(e);
