@@ -428,9 +428,9 @@ def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
 
     o is fp32 unless ``out_dtype`` (or a given ``o``) says otherwise.  With
     ``cu_seqlens`` the inputs hold packed sequences (see ``batch_shape``).
-    ``aux``: True uses the binding's second stream for the batch-1 schedule
-    (``aux_stream``), False runs every kernel on ``stream``, or a (stream,
-    event, event) triple of the caller's.
+    ``aux``: True uses the binding's second stream (``aux_stream``) for the
+    H scan and O of the shorter chains, False runs every kernel on
+    ``stream``, or a (stream, event, event) triple of the caller's.
     """
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (beta, "beta"), (z, "z")):
@@ -449,7 +449,7 @@ def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
                                                          -(-prob.seqlen // 64)):
         raise ValueError("rank_key must be [B, Nv/2, C]")
     if aux is True:
-        aux = aux_stream(q.device) if prob.batch == 1 else None
+        aux = aux_stream(q.device)
     elif aux is False:
         aux = None
     params = sparse_params(keep_budget, norm_weight, tail=tail, fixed_tiers=fixed_tiers,

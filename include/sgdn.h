@@ -22,7 +22,7 @@
  *   calls (no streams, events or buffers of its own): calls are reentrant,
  *   except that two calls must not share a workspace, a stats array or the
  *   auxiliary events of sgdn_sparse_params concurrently.
- * - sgdn_prefill_sparse with batch 1 can run part of its work on a second,
+ * - sgdn_prefill_sparse can run part of its work on a second,
  *   caller-owned stream (sgdn_sparse_params.aux_stream, forked from and
  *   joined back to `stream` with the caller's two events): later work on
  *   `stream` still sees every output.  Without it, every kernel runs on
@@ -137,11 +137,11 @@ typedef struct {
   int32_t unit_visibility;
   const float* rank_key;
   int32_t ablate;   /* SGDN_ABLATE_* bits, 0 for the method as defined */
-  /* Optional second stream for the batch-1 schedule: a hipStream_t of the
-   * caller's (default priority) and two hipEvent_t of the caller's (created
-   * with hipEventDisableTiming is enough), used to fork the H scan and O of
-   * CSR rows 4-15 onto aux_stream beside those of rows 0-3 on `stream` and
-   * to join them back.  NULL aux_stream: one stream (same outputs).  The
+  /* Optional second stream: a hipStream_t of the caller's (default priority)
+   * and two hipEvent_t of the caller's (created with hipEventDisableTiming is
+   * enough), used to fork the H scan and O of CSR rows 4-15 of every sequence
+   * onto aux_stream beside those of rows 0-3 on `stream` and to join them
+   * back.  NULL aux_stream: one stream (same outputs).  The
    * events must not be used by another call at the same time. */
   void* aux_stream;
   void* aux_events[2];
