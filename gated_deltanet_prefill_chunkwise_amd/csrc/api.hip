@@ -645,14 +645,18 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
     return launch_expand(xa, pl.bf16, q);
   };
 
-  if (!(pl.ablate & SGDN_ABLATE_TIER_SCHEDULE) && params->aux_stream != nullptr) {
+  // (With several sequences and every tier keeping the same count, all
+  // chains are equally long: nothing overlaps, and the O launch of rows 0-3
+  // would cut into the second round of H-scan workgroups; one launch each.)
+  const bool fork_rows = pl.B == 1 || pl.kL != pl.kH;
+  if (!(pl.ablate & SGDN_ABLATE_TIER_SCHEDULE) && params->aux_stream != nullptr && fork_rows) {
     // CSR rows 0-3 of a sequence hold every High-tier pair (at most 4), whose
     // chains are the longest and bound the H scan.  The H scan and O of rows
     // 4-15 of every sequence run on the caller's second stream beside those
     // of rows 0-3, so O of the shorter chains overlaps the long ones (with
     // many sequences the H scan's total work rather than its longest chains
-    // sets its time, and the gain shrinks: -5% at 2 x 32K tokens, -1% at 4,
-    // +1% at 8).  Both H-scan launches spread
+    // sets its time, and the gain shrinks: -5% at 2 x 32K tokens, -1% at 4
+    // and 8).  Both H-scan launches spread
     // each pair group over two XCDs (one head on each): rows 4-15 put 24
     // workgroups and rows 0-3 put 8 on every XCD, whatever XCD each launch's
     // round-robin dispatch starts at, so every chain finds a CU at once.
