@@ -264,18 +264,22 @@ def test_sparse_deterministic():
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
 
 
-def test_one_stream_schedule_equals_two_streams():
+@pytest.mark.parametrize("B,T,budget", [(1, 64 * 23 + 3, 0.29), (3, 64 * 9 + 5, 0.29),
+                                         (2, 64 * 7 + 1, 1.0)])
+def test_one_stream_schedule_equals_two_streams(B, T, budget):
     """Without a second stream every kernel runs on the caller's stream: the
-    same products in the same order per head, so bit-identical outputs."""
+    same products in the same order per head, so bit-identical outputs (one
+    sequence and batches, whose rows 4-15 are forked per sequence; keep 1.0
+    keeps one launch per stage)."""
     import torch
     from gated_deltanet_prefill_chunkwise_amd import ops
-    inp = synth.numpy_inputs(33, 1, 64 * 23 + 3, 16, 32, dtype="bf16", with_z=True,
+    inp = synth.numpy_inputs(33 + B, B, T, 16, 32, dtype="bf16", with_z=True,
                              decay_scale=1 / 16)
     d = to_device(inp)
     outs = []
     for aux in (True, False):
         o, S, st = ops.prefill_sparse(d["q"], d["k"], d["v"], d["a"], d["beta"], z=d["z"],
-                                      keep_budget=0.29, solve="blockadj", aux=aux)
+                                      keep_budget=budget, solve="blockadj", aux=aux)
         torch.cuda.synchronize()
         outs.append((o.cpu(), S.cpu(), st.cpu()))
     assert all(torch.equal(x, y) for x, y in zip(*outs))

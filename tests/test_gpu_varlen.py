@@ -194,3 +194,20 @@ def test_sparse_varlen_matches_each_sequence(with_s0):
         eo, es = rel_max_err(_rows(o, lens, i), o_ref), rel_max_err(S[i:i + 1], S_ref)
         print(f"seq {i} (T={n}, {st[i, 0]} events): err O {eo:.3e} S {es:.3e}")
         assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_sparse_varlen_one_stream_equals_two_streams():
+    """The forked schedule (CSR rows 4-15 of every packed sequence on the
+    second stream) computes the same products in the same order per head as
+    the one-stream schedule: bit-identical outputs and statistics."""
+    import torch
+    from gated_deltanet_prefill_chunkwise_amd import ops
+    lens = SPARSE_LENS
+    d = _packed(_seq_inputs(540, lens, 16, 32, "bf16", with_z=True, decay=1 / 16), "bf16")
+    outs = []
+    for aux in (True, False):
+        r = ops.prefill_sparse(d["q"], d["k"], d["v"], d["a"], d["beta"], z=d["z"],
+                               keep_budget=0.29, solve="blockadj", cu_seqlens=_cu(lens), aux=aux)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in r])
+    assert all(torch.equal(x, y) for x, y in zip(*outs))
