@@ -147,9 +147,13 @@ void make_plan(const sgdn_problem* pr, int sparse, const sgdn_sparse_params* sp,
   sz[B_REC] = B * Nv * C * 16;   // sparse: B * Emax * 2 records, Emax <= NP * C
   sz[B_P] = B * Nv * (C + 1) * 8;
   sz[B_U] = B * Nv * C * L * DV * I;
-  // K^T blocks per chunk (dense, and the sparse ablations with W of every
-  // chunk) or per kept event (sparse: at most E_max = NP C per sequence)
-  sz[B_KT] = B * (size_t)std::max(p.Nq * p.C, sparse ? p.Emax : 0) * DK * L * I;
+  // K^T blocks for the W-operand H scan (fp32 inputs; the sparse controls
+  // with W of every chunk): per chunk (dense, and those controls) or per
+  // kept event (sparse: at most E_max = NP C per sequence).  The Cb-operand
+  // H scan forms them from the key rows.
+  const bool wall_plan = sparse && (p.ablate & (SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_CSR)) != 0;
+  if (I == 4 || wall_plan)
+    sz[B_KT] = B * (size_t)std::max(p.Nq * p.C, sparse ? p.Emax : 0) * DK * L * I;
   sz[B_S0T] = B * Nv * DV * DK * I;
   if (p.cu != nullptr) sz[B_CHUNKS] = (B * C + 1 + B + 1) * 4;   // valid-chunk table
   if (!sparse) {
@@ -425,6 +429,7 @@ int sgdn_prefill_dense(const sgdn_problem* prob, const void* q, const void* k, c
   mark_range(dbg, SGDN_EV_PREFIX, SGDN_EV_DEFERRED, s);
   HScanArgs ha{};
   ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, B_W); ha.U = at<void>(ws, pl, B_U);
+  ha.k = k;
   ha.fac = at<float>(ws, pl, B_FAC); ha.rec = ea.rec; ha.P = nullptr;
   ha.s0 = s0; ha.s_final = s_final; ha.snap = at<void>(ws, pl, B_SNAP);
   ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 0;
@@ -596,9 +601,11 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   auto events = [&](int lo, int hi, hipStream_t q) -> hipError_t {
     if (csr_off) return launch_evrec_all(xa_all, q);   // every chunk an event
     ea.row_lo = lo; ea.row_hi = hi;
-    if (wall) return launch_evrec(ea, q);
+    // fp16 intermediates: the H scan forms W S = Cb (K S) with K^T taken
+    // from the key rows, so the kept events need only their records
+    if (wall || pl.bf16) return launch_evrec(ea, q);
     da.row_lo = lo; da.row_hi = hi;
-    return launch_events(da, ea, pl.bf16, q);          // deferred W and the records
+    return launch_events(da, ea, q);                   // fp32: deferred W and the records
   };
   if (s0 != nullptr) {
     S0PrepArgs s0a{s0, at<void>(ws, pl, B_S0T), pl.B, pl.Nv, stw};
@@ -606,12 +613,13 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   }
   HScanArgs ha{};
   ha.KT = at<void>(ws, pl, B_KT); ha.W = at<void>(ws, pl, wall ? B_W : B_WPK); ha.U = at<void>(ws, pl, B_U);
+  ha.k = k;
   ha.w_by_chunk = wall;
   ha.Cb = at<void>(ws, pl, B_CB); ha.blockadj = pl.solve == SGDN_SOLVE_BLOCKADJ;
   ha.fac = at<float>(ws, pl, B_FAC); ha.rec = ea.rec; ha.P = at<double>(ws, pl, B_P);
   ha.s0 = s0; ha.s_final = s_final; ha.snap = at<void>(ws, pl, B_SNAP);
   ha.B = pl.B; ha.Nq = pl.Nq; ha.Nv = pl.Nv; ha.C = pl.C; ha.sparse = 1;
-  ha.cu = nullptr; ha.T = pl.T;
+  ha.cu = pl.cu; ha.T = pl.T;   // (sequence offsets of the key rows)
   ha.row_pair = sa.row_pair; ha.row_ptr = sa.row_ptr; ha.col = sa.col; ha.event_slot = sa.event_slot;
   ha.Emax = Emax; ha.snap_cap = pl.snap_cap;
   ha.stats = stw;

@@ -20,7 +20,10 @@
 //   two loader waves stream each event's operands (W, K^T, the U slice, the
 //     per-token factors 2^(gamma - g) and a 16-byte event record) straight
 //     from global memory into a ring of LDS slots with the direct
-//     global-to-LDS loads of gfx950, DEPTH events ahead;
+//     global-to-LDS loads of gfx950, DEPTH events ahead (with the Cb
+//     operand three: one for the direct loads of Cb, U, the factors and the
+//     record, and two that form the K^T blocks from the chunk's bf16 key
+//     rows in their registers, so that no K^T copy is written to memory);
 //   a storer wave copies U' and the snapshots, which the compute wave leaves
 //     in a two-entry LDS staging ring, to global memory one event later.
 // One workgroup barrier per event hands a filled slot to the compute wave and
@@ -47,10 +50,13 @@ namespace {
 
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int NLD = 2;          // loader waves
-// waves: compute (one; two with the Cb operand), loaders, storer
+constexpr int NLD = 2;          // loader waves (W operand)
+// waves: compute (one; two with the Cb operand), loaders (two; three with
+// the Cb operand: two for the key rows, one for the direct loads), storer
 constexpr int NWAVE = 2 + NLD;
+constexpr int NWAVE_CB = 6;
 
 // One ring slot per event: W blocks (or, CBP, the six Cb blocks of the head),
 // K^T blocks, the U slice [16 dv][64 t] (rearranged for conflict-free reads),
@@ -63,7 +69,8 @@ template <typename I, bool PFON, bool CBP> struct Ring {
   static constexpr int NWB = CBP ? CB_BLOCKS : 16;   // blocks of W (of Cb)
   static constexpr int W_OFF = 0;
   static constexpr int K_OFF = NWB * FB;
-  static constexpr int U_OFF = (NWB + 16) * FB;
+  // (CBP: the K^T blocks of key tile mt start 16 mt bytes later, see kblk_r)
+  static constexpr int U_OFF = (NWB + 16) * FB + (CBP ? 128 : 0);
   static constexpr int U_BYTES = 16 * L * (int)sizeof(I);
   static constexpr int F_OFF = U_OFF + U_BYTES;
   static constexpr int R_OFF = F_OFF + 256;
@@ -75,7 +82,9 @@ template <typename I, bool PFON, bool CBP> struct Ring {
   // copy units of one event: 1 KB pieces (16 bytes per lane), then the
   // factors and the record (4 bytes per lane)
   static constexpr int NWA = NWB * FB / 1024;       // pieces of W (of Cb)
-  static constexpr int NW = 16 * FB / 1024;          // pieces of K^T
+  // pieces of K^T copied by direct loads (CBP: none; the loader waves form
+  // the K^T blocks from the key rows themselves)
+  static constexpr int NW = CBP ? 0 : 16 * FB / 1024;
   static constexpr int NUS = U_BYTES / 1024;         // pieces of the U slice
   static constexpr int NX4 = NWA + NW + NUS;
   // L2 prefetch (fp16 operands): one scattered 4-byte request per event that
@@ -87,7 +96,9 @@ template <typename I, bool PFON, bool CBP> struct Ring {
   static constexpr bool PF = PFON;
   static constexpr int PF_AHEAD = 6;
   static constexpr int NU = NX4 + 2 + (PF ? 1 : 0);
-  static constexpr int PER = (NU + NLD - 1) / NLD;   // units per loader wave
+  // units per loader wave (CBP: loader 2 issues all of them, loaders 0 and 1
+  // form the K^T blocks)
+  static constexpr int PER = (NU + NLD - 1) / NLD;
   // staging (the fp32 ring leaves no room: there the compute wave stores)
   static constexpr bool STAGE = sizeof(I) == 2;
   static constexpr int SN_BYTES = 16 * DK * (int)sizeof(I);
@@ -96,6 +107,13 @@ template <typename I, bool PFON, bool CBP> struct Ring {
   static constexpr int ST_BYTES = STAGE ? ST_HDR + 16 : 16;
 };
 
+// Element offset of K^T block (mt, ks) in a ring slot of the Cb-operand
+// scan: the fragment-major block of kblk, shifted by 16 mt bytes, so that
+// the loader's stores of one unit per lane into the eight key tiles fall into
+// different LDS banks (the blocks are otherwise a multiple of the bank
+// period apart); reads within one block are unchanged.
+__device__ __forceinline__ int kblk_r(int mt, int ks) { return kblk(mt, ks) + 8 * mt; }
+
 template <int N> __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("" ::: "memory");
@@ -103,11 +121,13 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   asm volatile("" ::: "memory");
 }
 
-// Barrier of the loader waves: they write LDS only through the direct loads,
-// whose completion they have waited for, so no fence (which could also wait
+// Barrier of the loader waves: they write LDS through the direct loads,
+// whose completion they have waited for, and (Cb operand) through their own
+// stores of the K^T blocks, waited for here; no fence (which could also wait
 // for the requests still in flight) is needed.
 __device__ __forceinline__ void loader_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -175,13 +195,15 @@ template <typename I> __device__ __forceinline__ int u_unit(int P) {
 // complete at every barrier (the current and the next).
 // BA (Cb operand only): the block-adjacent solve, whose Cb has no block (3,0).
 template <typename E, bool SPARSE, bool CBP, bool BA>
-__global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanArgs p) {
+__global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel(HScanArgs p) {
   using I = inter_t<E>;
   static_assert(!CBP || sizeof(I) == 2, "Cb operand: fp16 intermediates only");
   using R = Ring<I, sizeof(I) == 2, CBP>;
   constexpr int D = R::DEPTH, NS = R::NS;
   constexpr int NCW = CBP ? 2 : 1;         // compute waves 0 .. NCW - 1
-  constexpr int WST = NCW + NLD;           // storer wave (loaders in between)
+  constexpr int NL = CBP ? 3 : NLD;        // loader waves
+  constexpr int WST = NCW + NL;            // storer wave (loaders in between)
+  static_assert(WST + 1 == (CBP ? NWAVE_CB : NWAVE), "wave roles");
   static_assert(!CBP || D >= 2, "two events complete at each barrier");
   __shared__ __align__(16) char ring[NS * R::BYTES];
   __shared__ __align__(16) char stage[2 * R::ST_BYTES];
@@ -292,6 +314,9 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
     const bool w_ev = SPARSE && !p.w_by_chunk;
     const I* KTbase = static_cast<const I*>(p.KT);
     const I* Cbase = static_cast<const I*>(p.Cb);
+    // Cb operand: the key rows (input type E) of the event's chunk
+    const E* Kin = static_cast<const E*>(p.k);
+    const SeqSpan ksp = seq_span(p.cu, b, p.T);
     // L2 prefetch of event e (clamped to the row): lanes 0-15 the 16 W lines
     // of this slice's share of the head's tile (CBP: lanes 0-5 the 6 of the
     // head's 48 Cb lines, 6-15 repeat lane 0), 16-31 this workgroup's share of
@@ -314,7 +339,13 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
         else if (lane < 6) src = Ct + (slice * 6 + lane) * 128;
       } else if (lane < 32) {
         const int kl = p.spread ? slice * 16 + lane - 16 : (hh * 8 + slice) * 8 + ((lane - 16) & 7);
-        src = Kt + kl * 128;
+        if constexpr (CBP) {
+          // line kl of the chunk's 64 key rows (two 128-byte lines per row)
+          const int tc = min(c * L + (kl >> 1), ksp.len - 1);
+          src = reinterpret_cast<const char*>(Kin + ((size_t)(ksp.tok0 + tc) * p.Nq + pr) * DK) + (kl & 1) * 128;
+        } else {
+          src = Kt + kl * 128;
+        }
       } else if (lane < 48) src = Ut + (lane - 32) * 128;
       else if (lane < 50) src = reinterpret_cast<const char*>(p.fac + hc * L) + (lane - 48) * 128;
       dma4(src, pf_sink);
@@ -351,12 +382,99 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
         }
       }
     };
+    // Cb operand: the K^T blocks of an event come from the chunk's key rows
+    // through the registers of loader waves 0 and 1 (token steps 0 and 1),
+    // which issue no direct loads (their LDS stores then never wait for
+    // direct loads still in flight); loader wave 2 issues every direct load.
+    // Lane (n, g) of key wave ks loads keys 8 n .. 8 n + 7 of the eight
+    // tokens 32 ks + 4 g + r (r < 4) and 32 ks + 16 + 4 g + r - 4 (r >= 4),
+    // i.e. one 16-byte unit of eight tokens for each of its eight keys in the
+    // permuted reduction order of the blocks.  Rows past the end of the
+    // sequence repeat its last token (finite: they meet only exact zeros, the
+    // rows of X and the columns of Cb there, so the products are those of
+    // zero rows).  The requests of event j + 4 go out two steps before their
+    // conversion (bf16 -> fp32 -> fp16, rounded to nearest even) and stores.
+    static_assert(!CBP || std::is_same<E, sgdn::bf16>::value, "key rows are bf16");
+    const int kws = w - NCW;   // token step of a key wave
+    auto ktok = [&](int r) __attribute__((always_inline)) {
+      return 32 * kws + 4 * g4 + (r & 3) + 16 * (r >> 2);
+    };
+    auto kload = [&](int c, u32x4 (&kr)[8]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int tc = min(c * L + ktok(r), ksp.len - 1);
+        kr[r] = *reinterpret_cast<const u32x4*>(Kin + ((size_t)(ksp.tok0 + tc) * p.Nq + pr) * DK + 8 * n16);
+      }
+    };
+    auto kstore = [&](int s, u32x4 (&kv)[8]) __attribute__((always_inline)) {
+      // (the key registers pass through an empty asm here, so that their
+      // conversion is not scheduled ahead of the barrier and of the requests
+      // before this point, whose overlap with the wait it would undo)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) asm volatile("" : "+v"(kv[r]) :: "memory");
+      I* Ks = reinterpret_cast<I*>(ring + s * R::BYTES + R::K_OFF);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // key 8 n + e of each token: bf16 bits in the low half of word e / 2
+        // for even e, the high half for odd e
+        frag_t<I> u;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const uint32_t x = kv[r][e >> 1];
+          u[r] = from_f<I>(__uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16)));
+        }
+        const int key = 8 * n16 + e;
+        *reinterpret_cast<frag_t<I>*>(Ks + kblk_r(key >> 4, kws) + 8 * kswz((key & 15) + 16 * g4)) = u;
+      }
+    };
+    auto run_keys = [&]() __attribute__((always_inline)) {
+      static_assert(!CBP || (D == 4 && NS == 5), "key path: events j + 2 .. j + 4 in flight");
+      // Every step issues the same requests (events past the row's end are
+      // clamped to its last event; their stores land in ring slots no event
+      // uses), so the wait counts are exact and no branch skips a request.
+      const int jlast = i1 - 1;
+      auto ev = [&](int e) __attribute__((always_inline)) { return e < jlast ? e : jlast; };
+      // three register sets: event i0 + m in set m mod 3
+      u32x4 k0[8], k1[8], k2[8];
+      int s2 = 2;   // slot of event j + 2
+      // (the chunk of event j + 4 is read a step early, so that its latency
+      // is not paid between barrier and request)
+      int c4 = 0;
+      // step j: requests of event j + 4's keys (into kl), then event j + 2
+      // (its keys, requested two steps earlier into kc_) converted and stored
+      auto step = [&](int j, u32x4 (&kl)[8], u32x4 (&kc_)[8]) __attribute__((always_inline)) {
+        loader_barrier();   // event j handed over; this wave's stores of j + 1 done
+        kload(c4, kl);
+        c4 = col_at(ev(j + 5));
+        wait_vm<16>();      // the keys of j + 2 (those of j + 3 and j + 4 in flight)
+        kstore(s2, kc_);
+        s2 = (s2 + 1 == NS) ? 0 : s2 + 1;
+      };
+      if (i0 < i1) {
+        kload(col_at(i0), k0);
+        kload(col_at(ev(i0 + 1)), k1);
+        wait_vm<0>();
+        kstore(0, k0);   // events i0 and i0 + 1 before the first barrier
+        kstore(1, k1);
+        kload(col_at(ev(i0 + 2)), k2);
+        kload(col_at(ev(i0 + 3)), k0);
+        c4 = col_at(ev(i0 + 4));
+        int j = i0;
+        for (; j + 2 < i1; j += 3) {
+          step(j, k1, k2);
+          step(j + 1, k2, k0);
+          step(j + 2, k0, k1);
+        }
+        if (j < i1) step(j, k1, k2);
+        if (j + 1 < i1) step(j + 1, k2, k0);
+        wait_vm<0>();   // no request outlives the loop
+      }
+      loader_barrier();
+    };
     // per-loader unit ranges are compile-time constants, so every loop above
     // unrolls into straight-line requests
-    auto run = [&](auto kc) __attribute__((always_inline)) {
-      constexpr int K = decltype(kc)::value;
-      constexpr int U0 = K * R::PER;
-      constexpr int U1 = (K + 1) * R::PER < R::NU ? (K + 1) * R::PER : R::NU;
+    auto run = [&](auto u0c, auto u1c) __attribute__((always_inline)) {
+      constexpr int U0 = decltype(u0c)::value, U1 = decltype(u1c)::value;
       constexpr int CNT = U1 - U0;
       if (i0 < i1) {
         const int npro = (i1 - i0 < D) ? i1 - i0 : D;
@@ -385,9 +503,17 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
       }
       loader_barrier();
     };
-    static_assert(NLD == 2, "one branch per loader wave");
-    if (k == 0) run(std::integral_constant<int, 0>{});
-    else run(std::integral_constant<int, 1>{});
+    static_assert(NL == (CBP ? 3 : 2), "one branch per loader wave");
+    using I0 = std::integral_constant<int, 0>;
+    using IN = std::integral_constant<int, R::NU>;
+    if constexpr (CBP) {
+      if (k < 2) run_keys();
+      else run(I0{}, IN{});
+    } else {
+      constexpr int P1 = R::PER < R::NU ? R::PER : R::NU;
+      if (k == 0) run(I0{}, std::integral_constant<int, P1>{});
+      else run(std::integral_constant<int, P1>{}, IN{});
+    }
     return;
   }
 
@@ -435,7 +561,7 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
     const int koff = 8 * kswz(4 * g4 + (n16 >> 2) + 16 * (n16 & 3));
     auto kfrag = [&](const I* Kb, int q, int i) __attribute__((always_inline)) {
       const int o = koff + 4 * (i & 1);
-      return ld_tr_pair(Kb + kblk(2 * q, i >> 1) + o, Kb + kblk(2 * q + 1, i >> 1) + o);
+      return ld_tr_pair(Kb + kblk_r(2 * q, i >> 1) + o, Kb + kblk_r(2 * q + 1, i >> 1) + o);
     };
     const int kl = kswz(lane);
 
@@ -472,7 +598,7 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) o.kt[t][ks] = ld8(Ks + kblk(4 * cw + t, ks) + 8 * kl);
+        for (int ks = 0; ks < 2; ++ks) o.kt[t][ks] = ld8(Ks + kblk_r(4 * cw + t, ks) + 8 * kl);
     };
 
     f32x4 y[4], ym[4];
@@ -743,7 +869,7 @@ __global__ __launch_bounds__(64 * (CBP ? 5 : NWAVE), 2) void hscan_kernel(HScanA
 template <typename E, bool SPARSE, bool CBP, bool BA = false>
 hipError_t launch_one(const HScanArgs& a, hipStream_t s) {
   const int nblk = 128 * ((a.B * a.nrows + 7) / 8);
-  hipLaunchKernelGGL((hscan_kernel<E, SPARSE, CBP, BA>), dim3(nblk), dim3(64 * (CBP ? 5 : NWAVE)), 0, s, a);
+  hipLaunchKernelGGL((hscan_kernel<E, SPARSE, CBP, BA>), dim3(nblk), dim3(64 * (CBP ? NWAVE_CB : NWAVE)), 0, s, a);
   return hipGetLastError();
 }
 

@@ -274,10 +274,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     load_kv(nxt, kreg, v0reg, 0, true);
     load_ab(nxt);
 
-    // ---- fragment-major key tile (K^T operand blocks) for the H scan; the
-    //      sparse path forms them for the kept events only, in the
-    //      deferred-W stage
-    if constexpr (MODE != 1) {
+    // ---- fragment-major key tile (K^T operand blocks) for the W-operand H
+    //      scan (fp32 inputs, and the sparse controls with W of every
+    //      chunk); the Cb-operand H scan forms them from the key rows itself
+    if constexpr (MODE == 2 || (MODE == 0 && sizeof(E) == 4)) {
       I* kt = static_cast<I*>(p.KT) + ((size_t)(b * Nq + pq) * C + c) * DK * L;
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
@@ -285,10 +285,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
         for (int ks = 0; ks < 2; ++ks) {
           const int mt = 2 * w + mi;
           const frag_t<E> f = ld_tr44(&sK[32 * ks * KS + 16 * mt], KS, lane);
-          // (dense with fp16 intermediates: the Cb-operand H scan reads the
-          // units in the order kswz)
-          *reinterpret_cast<frag_t<I>*>(kt + kblk(mt, ks) + 8 * (MODE == 0 && sizeof(I) == 2 ? kswz(lane) : lane)) =
-              cvt8<I, E>(f);
+          *reinterpret_cast<frag_t<I>*>(kt + kblk(mt, ks) + 8 * lane) = cvt8<I, E>(f);
         }
     }
 

@@ -67,6 +67,7 @@ struct ChunkTableArgs { const int32_t* cu; int32_t* table; int B, T, C; };
 // Sparse: events from the CSR rows, W packed per event.
 struct HScanArgs {
   const void* KT; const void* W; void* U;
+  const void* k;            // key rows [tokens][Nq][dk] (Cb operand: K^T blocks formed in the kernel)
   const float* fac; const int32_t* rec; const double* P;
   const float* s0;          // [B][Nv][dk][dv] or null
   float* s_final;           // [B][Nv][dk][dv] or null
@@ -197,14 +198,13 @@ struct SelectArgs {
   const uint8_t* mask_in;  // override mask [B][16][C] or null
 };
 
+// (fp32 intermediates only: with fp16 the H scan forms W S = Cb (K S) from
+// the staged Cb and the key rows, and the kept events need only records)
 struct DeferredWArgs {
   const void* k;        // keys [tokens][Nq][dk] (the input)
   const void* Cb;
   void* Wpk;            // [B][Emax][2][64 * 128] W per kept event and head
-                        // (fp32 intermediates; null with fp16, where the H
-                        // scan forms W S from Cb)
   void* KTpk;           // [B][Emax][128 * 64] K^T blocks per kept event
-                        // (fp16: 16-byte units in the order kswz)
   const int32_t* row_pair; const int32_t* row_ptr; const int32_t* col;
   int B, Nv, Nq, C, Emax, solve;
   const int32_t* cu; int T;   // packed sequences
@@ -235,9 +235,8 @@ hipError_t launch_prep(const PrefixArgs& pa, const GateArgs* ga, const ScoreArgs
                        hipStream_t s);
 // deferred W + sparse event records of rows ea.row_lo .. ea.row_hi - 1 in one
 // launch (da and ea cover the same rows)
-hipError_t launch_events(const DeferredWArgs& da, const EvRecArgs& ea, int bf16, hipStream_t s);
+hipError_t launch_events(const DeferredWArgs& da, const EvRecArgs& ea, hipStream_t s);   // fp32
 hipError_t launch_select_full(const SelectArgs& a, hipStream_t s);
-hipError_t launch_deferred_w(const DeferredWArgs& a, int bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int bf16, hipStream_t s);
 hipError_t launch_stats_init(const StatsInitArgs& a, hipStream_t s);
 hipError_t launch_fp64_selftest(const double* x, const double* y, double* q, double* r, long long n,

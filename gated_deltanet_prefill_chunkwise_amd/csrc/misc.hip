@@ -251,14 +251,13 @@ __global__ __launch_bounds__(GATE_THREADS) void prep_kernel(PrefixArgs pa, GateA
 }
 
 // Deferred W of kept events only (SparseGDN reading notes, Sec. 2.5,
-// Eq. (15)).  The event's key rows are staged in LDS (zero past the end of
-// the sequence) and turned into the fragment-major K^T blocks the H scan
-// reads, stored per event: only kept chunks get them (with fp16
-// intermediates in the bank-spread unit order kswz).  With fp32
-// intermediates W = Cb K is formed here as well, as W^T = K^T Cb^T, and stored
-// as fragment-major W tiles per event (both heads of the pair); with fp16
-// intermediates (Wpk null) the H scan forms W S = Cb (K S) from Cb and K^T
-// itself, so W is never written.
+// Eq. (15)), fp32 intermediates.  The event's key rows are staged in LDS
+// (zero past the end of the sequence) and turned into the fragment-major K^T
+// blocks the W-operand H scan reads, and W = Cb K is formed as W^T = K^T Cb^T
+// and stored as fragment-major W tiles, both per event (both heads of the
+// pair): only kept chunks get them.  (With fp16 intermediates the H scan
+// forms W S = Cb (K S) from the staged Cb and the key rows itself, and the
+// kept events need only their records.)
 // Each workgroup walks events blockIdx.x, blockIdx.x + gridDim.x, ... of the
 // CSR rows row_lo .. row_hi - 1 (the count is on the device; the grid is
 // sized by the host and does not depend on it).
@@ -303,10 +302,9 @@ __device__ __forceinline__ void deferred_w_body(const DeferredWArgs& p, int bx, 
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int mt = 2 * w + mi;
-        *reinterpret_cast<frag_t<I>*>(KT + kblk(mt, ks) + 8 * (sizeof(I) == 2 ? kswz(lane) : lane)) =
+        *reinterpret_cast<frag_t<I>*>(KT + kblk(mt, ks) + 8 * lane) =
             cvt8<I, E>(ld_tr44(&sK[32 * ks * DW_KS + 16 * mt], DW_KS, lane));
       }
-    // (fp16 intermediates: the H scan forms W S as Cb (K S) itself)
     if (p.Wpk != nullptr) {
       const int ks_lo = (blockadj && w == 3) ? 1 : 0;
       const int ks_hi = (w >= 2) ? 1 : 0;
@@ -334,11 +332,6 @@ __device__ __forceinline__ void deferred_w_body(const DeferredWArgs& p, int bx, 
     }
     __syncthreads();   // the next event rewrites sK
   }
-}
-
-template <typename E>
-__global__ __launch_bounds__(256) void deferred_w_kernel(DeferredWArgs p) {
-  deferred_w_body<E>(p, blockIdx.x, gridDim.x, blockIdx.y);
 }
 
 // Event records of the H scan (SparseGDN reading notes, Sec. 2.1 Eq. (2) and
@@ -388,8 +381,8 @@ __global__ __launch_bounds__(1024) void evrec_sparse_kernel(EvRecArgs p) {
 
 // Deferred W and the event records of the same rows in one launch (both read
 // only the CSR layout and the prefix; one dependent launch fewer):
-// workgroups 0 .. nd - 1 walk the kept events as deferred_w_kernel does, the
-// rest write the records of one row each.
+// workgroups 0 .. nd - 1 walk the kept events (deferred_w_body), the rest
+// write the records of one row each.
 template <typename E>
 __global__ __launch_bounds__(256) void events_kernel(DeferredWArgs da, EvRecArgs ea, int nd) {
   if ((int)blockIdx.x < nd)
@@ -551,22 +544,10 @@ hipError_t launch_prep(const PrefixArgs& pa, const GateArgs* ga, const ScoreArgs
   return hipGetLastError();
 }
 
-hipError_t launch_events(const DeferredWArgs& da, const EvRecArgs& ea, int bf16, hipStream_t s) {
+hipError_t launch_events(const DeferredWArgs& da, const EvRecArgs& ea, hipStream_t s) {
   const int nd = da.Emax < DW_BLOCKS ? da.Emax : DW_BLOCKS;
   const dim3 grid(nd + (ea.row_hi - ea.row_lo), da.B);
-  if (bf16)
-    hipLaunchKernelGGL(events_kernel<sgdn::bf16>, grid, dim3(256), 0, s, da, ea, nd);
-  else
-    hipLaunchKernelGGL(events_kernel<float>, grid, dim3(256), 0, s, da, ea, nd);
-  return hipGetLastError();
-}
-
-hipError_t launch_deferred_w(const DeferredWArgs& a, int bf16, hipStream_t s) {
-  dim3 grid(a.Emax < DW_BLOCKS ? a.Emax : DW_BLOCKS, a.B);
-  if (bf16)
-    hipLaunchKernelGGL(deferred_w_kernel<sgdn::bf16>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(deferred_w_kernel<float>, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(events_kernel<float>, grid, dim3(256), 0, s, da, ea, nd);
   return hipGetLastError();
 }
 
