@@ -521,7 +521,8 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
     // =================== compute waves (Cb operand) ===================
     const int cw = w;
     // the compute waves' chain bounds the step: they win issue arbitration
-    // against the storer wave that shares a SIMD with compute wave 0
+    // against the direct-load and storer waves that share their SIMDs (the
+    // six waves of a workgroup are dealt to the four SIMDs in order)
     __builtin_amdgcn_s_setprio(3);
     const double* P = SPARSE ? p.P + bh * (C + 1) : nullptr;
     // initial state (all rows: the first event's Y is formed from it in
