@@ -655,8 +655,12 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
 
   // (With several sequences and every tier keeping the same count, all
   // chains are equally long: nothing overlaps, and the O launch of rows 0-3
-  // would cut into the second round of H-scan workgroups; one launch each.)
-  const bool fork_rows = pl.B == 1 || pl.kL != pl.kH;
+  // would cut into the second round of H-scan workgroups; one launch each.
+  // Sequences of at most 64 chunks take one launch each as well: there the
+  // stages are short and the fork and join cost more than the overlap
+  // gains, 2.61 vs 2.29 ms per 24 layers of 2048 tokens, even at 4096, and
+  // 5.24 vs 5.77 ms at 8192.)
+  const bool fork_rows = pl.C > 64 && (pl.B == 1 || pl.kL != pl.kH);
   if (!(pl.ablate & SGDN_ABLATE_TIER_SCHEDULE) && params->aux_stream != nullptr && fork_rows) {
     // CSR rows 0-3 of a sequence hold every High-tier pair (at most 4), whose
     // chains are the longest and bound the H scan.  The H scan and O of rows

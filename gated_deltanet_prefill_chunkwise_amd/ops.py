@@ -429,7 +429,8 @@ def prefill_sparse(q, k, v, a, beta, z=None, keep_budget=0.29, solve="blockadj",
     o is fp32 unless ``out_dtype`` (or a given ``o``) says otherwise.  With
     ``cu_seqlens`` the inputs hold packed sequences (see ``batch_shape``).
     ``aux``: True uses the binding's second stream (``aux_stream``) for the
-    H scan and O of the shorter chains, False runs every kernel on
+    H scan and O of the shorter chains (where the library forks: sequences
+    longer than 64 chunks, see include/sgdn.h), False runs every kernel on
     ``stream``, or a (stream, event, event) triple of the caller's.
     """
     import torch

@@ -141,9 +141,11 @@ typedef struct {
    * and two hipEvent_t of the caller's (created with hipEventDisableTiming is
    * enough), used to fork the H scan and O of CSR rows 4-15 of every sequence
    * onto aux_stream beside those of rows 0-3 on `stream` and to join them
-   * back (not with several sequences whose tiers all keep the same count:
-   * there every chain is equally long and the fork cannot gain).  NULL aux_stream: one stream (same outputs).  The
-   * events must not be used by another call at the same time. */
+   * back (not for sequences of at most 64 chunks, where the fork and join
+   * cost more than the overlap gains, nor with several sequences whose tiers
+   * all keep the same count: there every chain is equally long and the fork
+   * cannot gain).  NULL aux_stream: one stream (same outputs).  The events
+   * must not be used by another call at the same time. */
   void* aux_stream;
   void* aux_events[2];
 } sgdn_sparse_params;

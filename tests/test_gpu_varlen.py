@@ -199,10 +199,11 @@ def test_sparse_varlen_matches_each_sequence(with_s0):
 def test_sparse_varlen_one_stream_equals_two_streams():
     """The forked schedule (CSR rows 4-15 of every packed sequence on the
     second stream) computes the same products in the same order per head as
-    the one-stream schedule: bit-identical outputs and statistics."""
+    the one-stream schedule: bit-identical outputs and statistics (the longest
+    sequence has more than 64 chunks, so the fork applies)."""
     import torch
     from gated_deltanet_prefill_chunkwise_amd import ops
-    lens = SPARSE_LENS
+    lens = [64 * 80 + 5, 64 * 13, 1, 0, 64 * 70 + 40, 64, 64 * 2 + 1]
     d = _packed(_seq_inputs(540, lens, 16, 32, "bf16", with_z=True, decay=1 / 16), "bf16")
     outs = []
     for aux in (True, False):
