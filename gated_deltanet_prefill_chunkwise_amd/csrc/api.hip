@@ -572,6 +572,13 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
   sa.Emax = Emax; sa.G = pl.G;
   sa.stats = stw; sa.nf_clear = 0;
   sa.mask_in = mask_override;
+  // the selector's decide kernel also writes the event records (one launch
+  // fewer) on the default path with fp16 intermediates
+  const bool wall = (pl.ablate & (SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_CSR)) != 0;
+  const bool csr_off = (pl.ablate & SGDN_ABLATE_CSR) != 0;
+  const bool rec_in_select = pl.bf16 && !wall && mask_override == nullptr;
+  sa.P = at<double>(ws, pl, B_P);
+  sa.rec = rec_in_select ? at<int32_t>(ws, pl, B_REC) : nullptr;
   SGDN_TRY(launch_select_full(sa, s));
   mark(dbg, SGDN_EV_SELECT, s);
   if (dbg != nullptr) {
@@ -583,8 +590,6 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
 
   // deferred W of the kept events (the deferred-W ablation has W of every
   // chunk from the intra stage instead) and event records
-  const bool wall = (pl.ablate & (SGDN_ABLATE_DEFERRED_W | SGDN_ABLATE_CSR)) != 0;
-  const bool csr_off = (pl.ablate & SGDN_ABLATE_CSR) != 0;
   DeferredWArgs da{};
   da.k = k; da.Cb = at<void>(ws, pl, B_CB); da.Wpk = pl.bf16 ? nullptr : at<void>(ws, pl, B_WPK);
   da.KTpk = at<void>(ws, pl, B_KT); da.cu = pl.cu; da.T = pl.T;
@@ -602,7 +607,9 @@ int sgdn_prefill_sparse(const sgdn_problem* prob, const void* q, const void* k, 
     if (csr_off) return launch_evrec_all(xa_all, q);   // every chunk an event
     ea.row_lo = lo; ea.row_hi = hi;
     // fp16 intermediates: the H scan forms W S = Cb (K S) with K^T taken
-    // from the key rows, so the kept events need only their records
+    // from the key rows, so the kept events need only their records (on the
+    // default path written by the selector already)
+    if (rec_in_select) return hipSuccess;
     if (wall || pl.bf16) return launch_evrec(ea, q);
     da.row_lo = lo; da.row_hi = hi;
     return launch_events(da, ea, q);                   // fp32: deferred W and the records

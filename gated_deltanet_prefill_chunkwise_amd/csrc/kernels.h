@@ -196,6 +196,9 @@ struct SelectArgs {
   void* stats;          // sgdn_stats* or null
   int nf_clear;         // also zero the nonfinite fields (sgdn_select)
   const uint8_t* mask_in;  // override mask [B][16][C] or null
+  // (prefill) the H scan's event records [B][Emax][2] int4 written by the
+  // decide kernel with the layout, from the prefix P [B][Nv][C+1]; or null
+  const double* P; int32_t* rec;
 };
 
 // (fp32 intermediates only: with fp16 the H scan forms W S = Cb (K S) from

@@ -671,8 +671,29 @@ __global__ __launch_bounds__(1024) void select_decide_kernel(SelectArgs p) {
     if (c < CS) mask[c] = kept ? 1 : 0;
     if (kept) {
       const int e = base + s_run[i] + __popcll(bal & below);
+      const int slot = ((rb >> lane) & 1ull) ? rbase + s_rrun[i] + __popcll(rb & below) : -1;
       col[e] = c;
-      eslot[e] = ((rb >> lane) & 1ull) ? rbase + s_rrun[i] + __popcll(rb & below) : -1;
+      eslot[e] = slot;
+      if (p.rec != nullptr) {
+        // the event records of the H scan (Sec. 2.1 Eq. (2), Sec. 2.6
+        // Eq. (21)), as the record kernel forms them: F_in = 2^(P_c -
+        // P_{e'+1}) from the previous kept chunk e' of the row (1 for the
+        // first), 2^gamma F_in, the snapshot slot and the chunk
+        const unsigned long long m = bal & below;
+        const int prev = m ? 64 * i + 63 - (int)__builtin_clzll(m) : s_last[i];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const size_t bh = (size_t)b * NV + 2 * pp + hh;
+          const double* P = p.P + bh * (CS + 1);
+          const float fin = prev >= 0 ? exp2f((float)(P[c] - P[prev + 1])) : 1.f;
+          int4 r;
+          r.x = __float_as_int(fin);
+          r.y = __float_as_int(exp2f(p.gamma[bh * CS + c]) * fin);
+          r.z = slot;
+          r.w = c;
+          reinterpret_cast<int4*>(p.rec)[((size_t)b * p.Emax + e) * 2 + hh] = r;
+        }
+      }
     }
     if ((c & 1) == 0 && c < CS) {
       // group c / 2: the last kept chunk before c and its snapshot slot
