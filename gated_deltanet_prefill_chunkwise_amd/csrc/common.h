@@ -123,7 +123,7 @@ constexpr int CB_BLOCKS = 6;
 // with different g fall into different LDS banks (a permutation: the plain
 // per-lane reads stay conflict-free).
 __device__ __forceinline__ int kswz(int l) { return (l & 48) | ((l & 15) ^ ((l >> 2) & 12)); }
-__device__ __forceinline__ int cb_block(int i, int ks) { return i < 2 ? i : 2 * i - 2 + ks; }
+__host__ __device__ constexpr int cb_block(int i, int ks) { return i < 2 ? i : 2 * i - 2 + ks; }
 
 // Fragment of a row-major LDS tile read along its rows, in the permuted
 // reduction order of the fragment-major tiles: lane (n, g) receives rows

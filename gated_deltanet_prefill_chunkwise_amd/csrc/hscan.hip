@@ -198,8 +198,15 @@ template <typename E, bool SPARSE, bool CBP, bool BA>
 __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel(HScanArgs p) {
   using I = inter_t<E>;
   static_assert(!CBP || sizeof(I) == 2, "Cb operand: fp16 intermediates only");
-  using R = Ring<I, sizeof(I) == 2, CBP>;
+  // (the sparse Cb-operand scan issues no L2 prefetch: its High-tier chains
+  // run on a quarter of the CUs, their loads hit in L2 without one, and the
+  // scattered request only adds to the per-CU memory pipeline that bounds
+  // the step; measured 2% faster without.  The dense scan keeps it.)
+  using R = Ring<I, sizeof(I) == 2 && !(CBP && SPARSE), CBP>;
   constexpr int D = R::DEPTH, NS = R::NS;
+  // copy unit of the Cb block (3,0) (zero with the block-adjacent solve)
+  constexpr int CB_SKIP = 4;
+  static_assert(!CBP || cb_block(3, 0) == CB_SKIP, "Cb block (3,0)");
   constexpr int NCW = CBP ? 2 : 1;         // compute waves 0 .. NCW - 1
   constexpr int NL = CBP ? 3 : NLD;        // loader waves
   constexpr int WST = NCW + NL;            // storer wave (loaders in between)
@@ -362,7 +369,9 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
       char* sl = ring + s * R::BYTES;
 #pragma unroll
       for (int u = u0; u < u1; ++u) {
-        if (u < R::NWA) {
+        if (CBP && BA && u == CB_SKIP) {
+          // the block-adjacent Cb has no block (3,0): nothing to copy
+        } else if (u < R::NWA) {
           if constexpr (CBP)
             dma16(reinterpret_cast<const char*>(Cbase + hc * (CB_BLOCKS * 512)) + u * 1024 + lane * 16,
                   sl + R::W_OFF + u * 1024);
@@ -475,7 +484,8 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
     // unrolls into straight-line requests
     auto run = [&](auto u0c, auto u1c) __attribute__((always_inline)) {
       constexpr int U0 = decltype(u0c)::value, U1 = decltype(u1c)::value;
-      constexpr int CNT = U1 - U0;
+      // requests per event (the block-adjacent Cb operand skips one unit)
+      constexpr int CNT = U1 - U0 - ((CBP && BA && U0 <= CB_SKIP && CB_SKIP < U1) ? 1 : 0);
       if (i0 < i1) {
         const int npro = (i1 - i0 < D) ? i1 - i0 : D;
 #pragma unroll
@@ -520,9 +530,11 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
   if constexpr (CBP) {
     // =================== compute waves (Cb operand) ===================
     const int cw = w;
-    // the compute waves' chain bounds the step: they win issue arbitration
-    // against the direct-load and storer waves that share their SIMDs (the
-    // six waves of a workgroup are dealt to the four SIMDs in order)
+    // the compute waves' chain is one of the step's two limits (the other
+    // is the CU's memory pipeline, shared by the key, direct-load and storer
+    // waves): they win issue arbitration against the direct-load and storer
+    // waves that share their SIMDs (the six waves of a workgroup are dealt
+    // to the four SIMDs in order)
     __builtin_amdgcn_s_setprio(3);
     const double* P = SPARSE ? p.P + bh * (C + 1) : nullptr;
     // initial state (all rows: the first event's Y is formed from it in
