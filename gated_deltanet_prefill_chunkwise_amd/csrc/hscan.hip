@@ -162,19 +162,26 @@ __device__ __forceinline__ void dma4(const void* src, void* lds) {
 }
 
 // Byte offset of lane (n, g)'s 4 values of token tile i in a U slice
-// [16 dv][64 t] as the ring holds it.  fp16: 16-byte unit 32 i + 16 (g >> 1)
-// + n holds tokens 16 i + 8 (g >> 1) .. + 7 of row n; fp32: unit
-// 64 i + 16 g + n holds tokens 16 i + 4 g .. + 3 of row n.
+// [16 dv][64 t] as the ring holds it.  fp16: row n is 8 consecutive 16-byte
+// units (8 tokens each), token unit u at position u ^ (n >> 1) of the row, so
+// that the 16 rows a wave reads at once fall into distinct LDS banks while
+// every 1 KiB copy moves 8 whole rows, i.e. whole 128-byte lines of the
+// slice in global memory; fp32: unit 64 i + 16 g + n holds tokens
+// 16 i + 4 g .. + 3 of row n.
 template <typename I> __device__ __forceinline__ int u_off(int i, int n, int g) {
-  if constexpr (sizeof(I) == 2) return (32 * i + 16 * (g >> 1) + n) * 16 + 8 * (g & 1);
+  if constexpr (sizeof(I) == 2) return (8 * n + ((2 * i + (g >> 1)) ^ (n >> 1))) * 16 + 8 * (g & 1);
   else return (64 * i + 16 * g + n) * 16;
 }
 // Element offset (within the [16 dv][64 t] slice in global memory) of the
 // 16-byte unit P of that arrangement.
 template <typename I> __device__ __forceinline__ int u_unit(int P) {
-  if constexpr (sizeof(I) == 2) return (P & 15) * L + 16 * (P >> 5) + 8 * ((P >> 4) & 1);
+  if constexpr (sizeof(I) == 2) return (P >> 3) * L + 8 * ((P & 7) ^ (P >> 4));
   else return (P & 15) * L + 16 * (P >> 6) + 4 * ((P >> 4) & 3);
 }
+// Staged snapshot slice [16 dv][128 dk]: row n is 16 consecutive 16-byte
+// units (8 keys each), key unit c at position c ^ n of the row (the writers'
+// 16 rows fall into distinct LDS banks; each 1 KiB copy moves 4 whole rows).
+__device__ __forceinline__ int sn_unit(int c, int n) { return 16 * n + (c ^ n); }
 
 // (two waves per SIMD for the register budget: at most 256 registers per
 // lane, so the products accumulate in ordinary vector registers; the LDS ring
@@ -291,8 +298,8 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
         I* sp = snap_at(si) + dv0 * DK;
 #pragma unroll
         for (int r = 0; r < R::SN_BYTES / 1024; ++r) {
-          const int P = 64 * r + lane;   // unit (8 keys c8 = P >> 4, row n = P & 15)
-          stv(sp + (P & 15) * DK + 8 * (P >> 4), ldv(st + R::ST_SN + P * 16));
+          const int P = 64 * r + lane;   // unit of row n = P >> 4 (see sn_unit)
+          stv(sp + (P >> 4) * DK + 8 * ((P & 15) ^ (P >> 4)), ldv(st + R::ST_SN + P * 16));
         }
       }
     };
@@ -714,7 +721,7 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
             const int c8 = 4 * (2 * cw + qq) + 2 * hi + (g4 >> 1);
             const half_t<I> v = hi ? __builtin_shufflevector(Sfo[qq], Sfo[qq], 4, 5, 6, 7)
                                    : __builtin_shufflevector(Sfo[qq], Sfo[qq], 0, 1, 2, 3);
-            *reinterpret_cast<half_t<I>*>(st + R::ST_SN + (c8 * 16 + n16) * 16 + 8 * (g4 & 1)) = v;
+            *reinterpret_cast<half_t<I>*>(st + R::ST_SN + sn_unit(c8, n16) * 16 + 8 * (g4 & 1)) = v;
           }
       }
       if (lane == 0) *reinterpret_cast<int2*>(st + R::ST_HDR) = make_int2(c, snapi);
@@ -844,7 +851,7 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
             const int c8 = 4 * q + 2 * hi + (g4 >> 1);
             const half_t<I> v = hi ? __builtin_shufflevector(Sf[q], Sf[q], 4, 5, 6, 7)
                                    : __builtin_shufflevector(Sf[q], Sf[q], 0, 1, 2, 3);
-            *reinterpret_cast<half_t<I>*>(st + R::ST_SN + (c8 * 16 + n16) * 16 + 8 * (g4 & 1)) = v;
+            *reinterpret_cast<half_t<I>*>(st + R::ST_SN + sn_unit(c8, n16) * 16 + 8 * (g4 & 1)) = v;
           }
       }
       if (lane == 0) *reinterpret_cast<int2*>(st + R::ST_HDR) = make_int2(c, null_ev ? NULL_EVENT : snapi);
