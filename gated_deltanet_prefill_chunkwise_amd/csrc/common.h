@@ -35,6 +35,11 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 constexpr int L = 64;      // chunk length
 constexpr int DK = 128;    // key dimension
 constexpr int DV = 128;    // value dimension
+// U (overwritten in place by U') of one (chunk, head) in global memory: four
+// 16-token tiles, each [128 dv][16 t], so that one 16x16 tile of U a wave
+// writes, and 16 value rows of one token tile, are 512 contiguous bytes
+// (whole lines) in the intermediate type.
+__host__ __device__ constexpr int u_elem(int dv, int t) { return (t >> 4) * (DV * 16) + dv * 16 + (t & 15); }
 
 template <typename E> struct FragOf;
 template <> struct FragOf<bf16> { using T = bf16x8; using H = bf16x4; };

@@ -172,11 +172,12 @@ template <typename I> __device__ __forceinline__ int u_off(int i, int n, int g) 
   if constexpr (sizeof(I) == 2) return (8 * n + ((2 * i + (g >> 1)) ^ (n >> 1))) * 16 + 8 * (g & 1);
   else return (64 * i + 16 * g + n) * 16;
 }
-// Element offset (within the [16 dv][64 t] slice in global memory) of the
-// 16-byte unit P of that arrangement.
+// Element offset (from the slice's first row, u_elem(dv0, 0), in global
+// memory) of the 16-byte unit P of that arrangement: each 1 KiB copy moves
+// whole lines (fp16: 8 rows of all four token tiles; fp32: one token tile).
 template <typename I> __device__ __forceinline__ int u_unit(int P) {
-  if constexpr (sizeof(I) == 2) return (P >> 3) * L + 8 * ((P & 7) ^ (P >> 4));
-  else return (P & 15) * L + 16 * (P >> 6) + 4 * ((P >> 4) & 3);
+  if constexpr (sizeof(I) == 2) return u_elem(P >> 3, 8 * ((P & 7) ^ (P >> 4)));
+  else return u_elem(P & 15, 16 * (P >> 6) + 4 * ((P >> 4) & 3));
 }
 // Staged snapshot slice [16 dv][128 dk]: row n is 16 consecutive 16-byte
 // units (8 keys each), key unit c at position c ^ n of the row (the writers'
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
       const int c = min(max(__builtin_amdgcn_readfirstlane(hd.x), 0), C - 1);
       const int sn = __builtin_amdgcn_readfirstlane(hd.y);
       const int si = (sn >= 0 && sn < snap_cap) ? sn : -1;
-      I* Ug = Ubase + (bh * C + c) * DV * L + dv0 * L;
+      I* Ug = Ubase + (bh * C + c) * DV * L + u_elem(dv0, 0);
       if (sn != NULL_EVENT) {   // a null event keeps U
 #pragma unroll
         for (int r = 0; r < R::U_BYTES / 1024; ++r) {
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
           w_ev ? Wbase + (((size_t)b * p.Emax + e) * 2 + hh) * L * DK : Wbase + hc * L * DK);
       const char* Kt = reinterpret_cast<const char*>(
           w_ev ? KTbase + ((size_t)b * p.Emax + e) * DK * L : KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L);
-      const char* Ut = reinterpret_cast<const char*>(Ubase + hc * DV * L + dv0 * L);
+      const char* Ut = reinterpret_cast<const char*>(Ubase + hc * DV * L + u_elem(dv0, 0));
       const char* Ct = reinterpret_cast<const char*>(Cbase + hc * (CB_BLOCKS * 512));
       const char* src = CBP ? Ct + slice * 6 * 128 : Wt + slice * 16 * 128;
       if (lane < 16) {
@@ -360,8 +361,10 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
         } else {
           src = Kt + kl * 128;
         }
-      } else if (lane < 48) src = Ut + (lane - 32) * 128;
-      else if (lane < 50) src = reinterpret_cast<const char*>(p.fac + hc * L) + (lane - 48) * 128;
+      } else if (lane < 48) {
+        // the slice's 512 bytes of each token tile: four lines per tile
+        src = Ut + ((lane - 32) >> 2) * (DV * 16 * (int)sizeof(I)) + ((lane - 32) & 3) * 128;
+      } else if (lane < 50) src = reinterpret_cast<const char*>(p.fac + hc * L) + (lane - 48) * 128;
       dma4(src, pf_sink);
     };
     // copy units [u0, u1) of event j (chunk c) into slot s
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
           w_ev ? Wbase + (((size_t)b * p.Emax + j) * 2 + hh) * L * DK : Wbase + hc * L * DK);
       const char* Kt = reinterpret_cast<const char*>(
           w_ev ? KTbase + ((size_t)b * p.Emax + j) * DK * L : KTbase + (((size_t)b * p.Nq + pr) * C + c) * DK * L);
-      const I* Ut = Ubase + hc * DV * L + dv0 * L;
+      const I* Ut = Ubase + hc * DV * L + u_elem(dv0, 0);
       const int32_t* rec = SPARSE ? p.rec + (((size_t)b * p.Emax + j) * 2 + hh) * 4 : p.rec + hc * 4;
       char* sl = ring + s * R::BYTES;
 #pragma unroll
@@ -825,7 +828,7 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
       if constexpr (R::STAGE)
         st4<I>(reinterpret_cast<I*>(st + u_off<I>(i, n16, g4)), up);
       else if (!null_ev)
-        st4<I>(Ubase + (bh * C + c) * DV * L + (dv0 + n16) * L + 16 * i + 4 * g4, up);
+        st4<I>(Ubase + (bh * C + c) * DV * L + u_elem(dv0 + n16, 16 * i + 4 * g4), up);
       return x;
     };
     f32x4 a0, a1, a2, a3;

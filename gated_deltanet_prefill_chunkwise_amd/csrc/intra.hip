@@ -451,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
           }
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) {
-            st4<I>(U + (16 * (4 * half + nt) + n16) * L + 16 * w + 4 * g4, acc[nt]);
+            st4<I>(U + u_elem(16 * (4 * half + nt) + n16, 16 * w + 4 * g4), acc[nt]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) ss += acc[nt][j] * acc[nt][j];
           }

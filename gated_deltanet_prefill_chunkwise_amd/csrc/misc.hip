@@ -456,15 +456,15 @@ __global__ __launch_bounds__(1024) void evrec_all_kernel(EvAllArgs p) {
   }
 }
 
-// U tiles [dv][t] (intermediate type) -> token-major fp32 [t][dv] copy for
-// the debug output.
+// U tiles (intermediate type, token-tile-major, see u_elem) -> token-major
+// fp32 [t][dv] copy for the debug output.
 template <typename I>
 __global__ __launch_bounds__(256) void debug_u_kernel(const void* Ut_, float* U) {
   const I* Ut = static_cast<const I*>(Ut_);
   const size_t tile = blockIdx.x;
   for (int q = threadIdx.x; q < L * DV; q += 256) {
     const int t = q >> 7, dv = q & 127;
-    U[tile * L * DV + q] = to_f(Ut[tile * DV * L + dv * L + t]);
+    U[tile * L * DV + q] = to_f(Ut[tile * DV * L + u_elem(dv, t)]);
   }
 }
 

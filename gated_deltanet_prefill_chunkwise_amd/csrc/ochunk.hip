@@ -199,7 +199,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   // they are not live across phase 1; their latency overlaps S^T Q^T)
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    ufr[ks] = ((ks >> 1) == 0 || need1) ? ld8(Up + ((bh * C + c0 + (ks >> 1)) * DV + dvr) * L + 32 * (ks & 1) + 8 * g4)
+    ufr[ks] = ((ks >> 1) == 0 || need1) ? ld8(Up + (bh * C + c0 + (ks >> 1)) * DV * L + u_elem(dvr, 32 * (ks & 1) + 8 * g4))
                                    : zero_frag<I>();
   __syncthreads();
 
