@@ -40,6 +40,11 @@ constexpr int DV = 128;    // value dimension
 // writes, and 16 value rows of one token tile, are 512 contiguous bytes
 // (whole lines) in the intermediate type.
 __host__ __device__ constexpr int u_elem(int dv, int t) { return (t >> 4) * (DV * 16) + dv * 16 + (t & 15); }
+// A state snapshot S^T [dv][dk] (group entry states, the prepared s0) in
+// global memory: four 32-key tiles, each [128 dv][32 dk], so that the
+// 16-row fragment loads of O and the 4-row copies of the H scan's storer are
+// whole 128-byte lines.
+__host__ __device__ constexpr int s_elem(int dv, int dk) { return (dk >> 5) * (DV * 32) + dv * 32 + (dk & 31); }
 
 template <typename E> struct FragOf;
 template <> struct FragOf<bf16> { using T = bf16x8; using H = bf16x4; };

@@ -296,11 +296,11 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
         }
       }
       if (si >= 0) {
-        I* sp = snap_at(si) + dv0 * DK;
+        I* sp = snap_at(si);
 #pragma unroll
         for (int r = 0; r < R::SN_BYTES / 1024; ++r) {
           const int P = 64 * r + lane;   // unit of row n = P >> 4 (see sn_unit)
-          stv(sp + (P >> 4) * DK + 8 * ((P & 15) ^ (P >> 4)), ldv(st + R::ST_SN + P * 16));
+          stv(sp + s_elem(dv0 + (P >> 4), 8 * ((P & 15) ^ (P >> 4))), ldv(st + R::ST_SN + P * 16));
         }
       }
     };
@@ -859,11 +859,11 @@ __global__ __launch_bounds__(64 * (CBP ? NWAVE_CB : NWAVE), 2) void hscan_kernel
       }
       if (lane == 0) *reinterpret_cast<int2*>(st + R::ST_HDR) = make_int2(c, null_ev ? NULL_EVENT : snapi);
     } else if (snapi >= 0) {
-      I* sp = snap_at(snapi) + (dv0 + n16) * DK + 4 * g4;
+      I* sp = snap_at(snapi);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        *reinterpret_cast<half_t<I>*>(sp + 32 * q) = __builtin_shufflevector(Sf[q], Sf[q], 0, 1, 2, 3);
-        *reinterpret_cast<half_t<I>*>(sp + 32 * q + 16) = __builtin_shufflevector(Sf[q], Sf[q], 4, 5, 6, 7);
+        *reinterpret_cast<half_t<I>*>(sp + s_elem(dv0 + n16, 32 * q + 4 * g4)) = __builtin_shufflevector(Sf[q], Sf[q], 0, 1, 2, 3);
+        *reinterpret_cast<half_t<I>*>(sp + s_elem(dv0 + n16, 32 * q + 16 + 4 * g4)) = __builtin_shufflevector(Sf[q], Sf[q], 4, 5, 6, 7);
       }
     }
     s = (s + 1 == NS) ? 0 : s + 1;

@@ -153,8 +153,9 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs p) {
   }
 }
 
-// s0 [dk][dv] -> transposed [dv][dk] in the snapshot element type, the
-// "virtual snapshot" that output groups without a predecessor read.
+// s0 [dk][dv] -> transposed [dv][dk] in the snapshot element type and
+// layout (s_elem), the "virtual snapshot" that output groups without a
+// predecessor read.
 template <typename I>
 __global__ __launch_bounds__(256) void s0prep_kernel(S0PrepArgs p) {
   const size_t bh = blockIdx.x;
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(256) void s0prep_kernel(S0PrepArgs p) {
     const int dv = q >> 7, dk = q & 127;
     const float x = s[dk * DV + dv];
     bad |= nonfinite1(x);
-    o[q] = from_f<I>(x);
+    o[s_elem(dv, dk)] = from_f<I>(x);
   }
   flag_or(p.stats, (int)(bh / p.Nv), ST_NF_IN, bad ? NF_S0 : 0);
 }

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   frag_t<I> sfr[4], ufr[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    sfr[ks] = Ssrc != nullptr ? ld8(Ssrc + (size_t)dvr * DK + 32 * ks + 8 * g4) : zero_frag<I>();
+    sfr[ks] = Ssrc != nullptr ? ld8(Ssrc + s_elem(dvr, 32 * ks + 8 * g4)) : zero_frag<I>();
 
   // ---- stage Q rows of the group and G (a non-finite q is flagged)
   uint32_t nfq = 0;
