@@ -217,6 +217,22 @@ template <> __device__ __forceinline__ void st4o<float>(float* p, f32x4 v) { st4
 template <> __device__ __forceinline__ void st4o<bf16>(bf16* p, f32x4 v) { st4<bf16>(p, v); }
 template <> __device__ __forceinline__ void st4o<fp16>(fp16* p, f32x4 v) { st4<fp16>(p, v); }
 
+// Streaming variants for data that is read or written exactly once (the
+// output rows; U' and the state snapshots read by O): non-temporal, so that
+// they do not displace lines other workgroups still read from L2.
+template <typename E> __device__ __forceinline__ frag_t<E> ld8nt(const E* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const frag_t<E>*>(p));
+}
+template <typename O> __device__ __forceinline__ void st4o_nt(O* p, f32x4 v) {
+  half_t<O> h;
+  h[0] = from_f<O>(v[0]); h[1] = from_f<O>(v[1]);
+  h[2] = from_f<O>(v[2]); h[3] = from_f<O>(v[3]);
+  __builtin_nontemporal_store(h, reinterpret_cast<half_t<O>*>(p));
+}
+template <> __device__ __forceinline__ void st4o_nt<float>(float* p, f32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+
 // 16-byte vector copy helpers (global <-> LDS staging).
 struct alignas(16) V16 { uint32_t w[4]; };
 __device__ __forceinline__ V16 ldv(const void* p) { return *reinterpret_cast<const V16*>(p); }

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   frag_t<I> sfr[4], ufr[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    sfr[ks] = Ssrc != nullptr ? ld8(Ssrc + s_elem(dvr, 32 * ks + 8 * g4)) : zero_frag<I>();
+    sfr[ks] = Ssrc != nullptr ? ld8nt(Ssrc + s_elem(dvr, 32 * ks + 8 * g4)) : zero_frag<I>();
 
   // ---- stage Q rows of the group and G (a non-finite q is flagged)
   uint32_t nfq = 0;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   // they are not live across phase 1; their latency overlaps S^T Q^T)
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    ufr[ks] = ((ks >> 1) == 0 || need1) ? ld8(Up + (bh * C + c0 + (ks >> 1)) * DV * L + u_elem(dvr, 32 * (ks & 1) + 8 * g4))
+    ufr[ks] = ((ks >> 1) == 0 || need1) ? ld8nt(Up + (bh * C + c0 + (ks >> 1)) * DV * L + u_elem(dvr, 32 * (ks & 1) + 8 * g4))
                                    : zero_frag<I>();
   __syncthreads();
 
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
     const int t = q >> 5, c4 = (q & 31) * 4;
     const int tok = c0 * L + 16 * j0 + t;
     if (tok < sp.len)
-      st4o<OT>(O + ((size_t)(sp.tok0 + tok) * Nv + h) * DV + c4, *reinterpret_cast<const f32x4*>(&sO[t * OSTR + c4]));
+      st4o_nt<OT>(O + ((size_t)(sp.tok0 + tok) * Nv + h) * DV + c4, *reinterpret_cast<const f32x4*>(&sO[t * OSTR + c4]));
   }
 }
 
