@@ -142,9 +142,13 @@ __global__ __launch_bounds__(512, 4) void ochunk_kernel(OChunkArgs p) {
   const int dvr = 16 * w + n16;
   const I* Up = static_cast<const I*>(p.U);
   frag_t<I> sfr[4], ufr[4];
+  // a dense group snapshot is read by one group only; a sparse compact
+  // snapshot serves every group up to the next kept event, so it stays cached
+  const bool dense_snap = !p.sparse && p.entry == nullptr && r > 0;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    sfr[ks] = Ssrc != nullptr ? ld8nt(Ssrc + s_elem(dvr, 32 * ks + 8 * g4)) : zero_frag<I>();
+    sfr[ks] = Ssrc == nullptr ? zero_frag<I>()
+              : dense_snap ? ld8nt(Ssrc + s_elem(dvr, 32 * ks + 8 * g4)) : ld8(Ssrc + s_elem(dvr, 32 * ks + 8 * g4));
 
   // ---- stage Q rows of the group and G (a non-finite q is flagged)
   uint32_t nfq = 0;
